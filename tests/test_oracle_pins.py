@@ -1,0 +1,374 @@
+"""Pins for the CPU oracle: each test checks ``oracle`` against something other
+than itself -- values derived by hand from the pages' definitions
+(``tests/golden``), torch's decomposed quantize/dequantize ops (which the
+quantize page says it bit-matches), exact float64 matmul / conv_transpose2d /
+conv2d on integer data, brute force on tiny inputs, identities the pages state,
+and the error bound of the float32 epilogue.  CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from torch.ao.quantization.fx import _decomposed  # noqa: F401  (registers quantized_decomposed ops)
+
+import oracle
+import q8ta_inputs as qi
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U = 2.0 ** -24  # float32 unit roundoff
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _torch_quant(x, scale, zp):
+    return torch.ops.quantized_decomposed.quantize_per_tensor(
+        torch.from_numpy(np.ascontiguousarray(x, np.float32)), scale, zp, -128, 127,
+        torch.int8).numpy()
+
+
+def _torch_dequant(q, scale, zp):
+    return torch.ops.quantized_decomposed.dequantize_per_tensor(
+        torch.from_numpy(np.ascontiguousarray(q, np.int8)), scale, zp, -128, 127,
+        torch.int8).numpy()
+
+
+# --------------------------------------------------------------------------- quantize
+def test_quantize_hand_vectors():
+    g = _gold("quantize_hand.json")
+    for scale, zp, x, q in g["cases"]:
+        xv = np.array([float(x)], np.float32)
+        got = oracle.quantize_per_tensor(xv, scale, zp)
+        assert int(got[0]) == q, (scale, zp, x, q, int(got[0]))
+
+
+SCALES = [0.02, 0.272, 2.176, 0.544, qi.out_scale_for(4096), qi.out_scale_for(576), 1.0 / 3.0, 0.1]
+
+
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("zp", [0, 3, -5, -128, 127])
+def test_quantize_matches_torch_decomposed(scale, zp):
+    g = qi.rng(7)
+    # a spread of values plus values placed on and next to every rounding tie
+    x = np.concatenate([
+        (g.standard_normal(20000) * 80 * scale).astype(np.float32),
+        ((np.arange(-140, 141) + 0.5) * scale).astype(np.float32),
+        np.nextafter(((np.arange(-140, 141) + 0.5) * scale).astype(np.float32), np.float32(np.inf)),
+        np.nextafter(((np.arange(-140, 141) + 0.5) * scale).astype(np.float32), np.float32(-np.inf)),
+        np.array([0.0, -0.0, 1e30, -1e30, np.inf, -np.inf], np.float32),
+    ])
+    np.testing.assert_array_equal(oracle.quantize_per_tensor(x, scale, zp), _torch_quant(x, scale, zp))
+
+
+def test_quantize_reciprocal_is_taken_in_double():
+    """The quantize page says the reciprocal is formed in double and then
+    rounded to float; a float reciprocal differs for the 0.272 output scale and
+    gives different codes on the tie grid, which torch and the oracle agree on."""
+    scale = 0.272
+    inv_double = np.float32(1.0 / scale)
+    inv_float = np.float32(1.0) / np.float32(scale)
+    assert inv_double != inv_float
+    x = np.concatenate([((np.arange(-140, 141) + 0.5) * scale).astype(np.float32)] +
+                       [(g * scale).astype(np.float32) for g in [np.linspace(-140, 140, 200001)]])
+    ref = _torch_quant(x, scale, 0)
+    wrong = np.clip(np.rint(x * inv_float), -128, 127).astype(np.int8)
+    assert (wrong != ref).any()
+    np.testing.assert_array_equal(oracle.quantize_per_tensor(x, scale, 0), ref)
+
+
+def test_quantize_large_workload_matches_torch():
+    c = qi.make_deconv_large()
+    np.testing.assert_array_equal(oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp),
+                                  _torch_quant(c.x_fp32, c.in_scale, c.in_zp))
+
+
+def test_quantize_empty():
+    assert oracle.quantize_per_tensor(np.zeros(0, np.float32), 0.02, 3).shape == (0,)
+
+
+# --------------------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("scale,zp", [(0.02, 3), (0.272, -5), (1.0 / 3.0, 0), (2.176, -128), (0.1, 127)])
+def test_dequantize_matches_torch_decomposed(scale, zp):
+    q = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+    np.testing.assert_array_equal(oracle.dequantize_per_tensor(q, scale, zp), _torch_dequant(q, scale, zp))
+
+
+def test_dequantize_hand():
+    got = oracle.dequantize_per_tensor(np.array([5, -128, 3, 127], np.int8), 0.5, 3)
+    np.testing.assert_array_equal(got, np.array([1.0, -65.5, 0.0, 62.0], np.float32))
+
+
+# --------------------------------------------------------------------------- linear contraction
+def test_linear_acc_bruteforce_tiny():
+    g = qi.rng(11)
+    M, K, N, zp = 3, 5, 4, 3
+    x = qi.x_int8(g, (M, K))
+    w = qi.w_int8(g, (N, K))
+    ref = [[sum((int(x[m, k]) - zp) * int(w[n, k]) for k in range(K)) for n in range(N)]
+           for m in range(M)]
+    np.testing.assert_array_equal(oracle.linear_acc(x, w, zp), np.array(ref, np.int32))
+
+
+@pytest.mark.parametrize("zp", [3, 0, -128, 127])
+@pytest.mark.parametrize("M,K,N", [(37, 300, 53), (1, 4096, 64), (64, 64, 32)])
+def test_linear_acc_matches_f64_matmul(M, K, N, zp):
+    g = qi.rng(M * 1000 + K + N)
+    x = qi.x_int8(g, (M, K))
+    w = g.integers(-128, 128, size=(N, K), dtype=np.int8)
+    ref = (torch.from_numpy(x).double() - zp) @ torch.from_numpy(w).double().T
+    np.testing.assert_array_equal(oracle.linear_acc(x, w, zp), ref.numpy().astype(np.int32))
+
+
+def test_linear_zero_point_fold_identity():
+    g = qi.rng(12)
+    x = qi.x_int8(g, (17, 257))
+    w = qi.w_int8(g, (29, 257))
+    for zp in (3, -128, 127, 0):
+        np.testing.assert_array_equal(oracle.linear_acc(x, w, zp),
+                                      oracle.linear_acc(x, w, zp, folded=True))
+
+
+def test_linear_gemv_is_a_gemm_row():
+    c = qi.linear_case(13, 9, 320, 48)
+    full = oracle.linear(c.x, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale, c.out_zp)
+    for m in range(c.M):
+        row = oracle.linear(c.x[m:m + 1], c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                            c.out_scale, c.out_zp)
+        np.testing.assert_array_equal(row[0], full[m])
+
+
+def test_linear_reads_only_first_K_columns_of_padded_weight():
+    c = qi.linear_case(14, 5, 100, 12, ldw=128)
+    a = oracle.linear_acc(c.x, c.w, c.in_zp)
+    b = oracle.linear_acc(c.x, np.ascontiguousarray(c.w[:, :100]), c.in_zp)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_linear_overflow_is_detected():
+    K = 70000  # (127 + 128) * 127 * 70000 > 2**31 - 1
+    x = np.full((1, K), 127, np.int8)
+    w = np.full((1, K), 127, np.int8)
+    with pytest.raises(OverflowError):
+        oracle.linear_acc(x, w, -128)
+
+
+# --------------------------------------------------------------------------- epilogue
+def test_epilogue_hand_vectors():
+    g = _gold("epilogue_hand.json")
+    for acc, s_in, w_s, b, s_out, ozp, q in g["cases"]:
+        got = oracle.epilogue(np.array([acc], np.int32), 1, 1, s_in, np.array([w_s], np.float32),
+                              None if b is None else np.array([b], np.float32), s_out, ozp)
+        assert int(got[0]) == q, (acc, b, ozp, q, int(got[0]))
+
+
+def _linear_random_acc(seed, M, N, spread):
+    g = qi.rng(seed)
+    return g.integers(-spread, spread + 1, size=(M, N)).astype(np.int32)
+
+
+@pytest.mark.parametrize("out_scale", [qi.out_scale_for(64), qi.out_scale_for(4096), 0.544, 2.176])
+def test_epilogue_requant_matches_torch_quantize(out_scale):
+    """The requantize half of the epilogue is the page's quantize rule applied
+    to the dequantized value v: it must bit-match torch's quantize_per_tensor."""
+    g = qi.rng(21)
+    M, N = 64, 96
+    acc = _linear_random_acc(22, M, N, 400000)
+    ws = qi.scales(g, N)
+    b = qi.bias(g, N)
+    q, pre = oracle.epilogue(acc, N, 1, 0.02, ws, b, out_scale, -5, return_pre=True)
+    np.testing.assert_array_equal(q, _torch_quant(pre, out_scale, -5))
+
+
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_epilogue_dequant_within_float_error_bound(with_bias):
+    g = qi.rng(23)
+    M, N = 50, 70
+    acc = _linear_random_acc(24, M, N, 10 ** 6)
+    ws = qi.scales(g, N)
+    b = qi.bias(g, N) if with_bias else None
+    _, pre = oracle.epilogue(acc, N, 1, 0.02, ws, b, 1.0, 0, return_pre=True)
+    s_in = float(np.float32(0.02))
+    prod = acc.astype(np.float64) * s_in * ws.astype(np.float64)[None, :]
+    exact = prod + (b.astype(np.float64)[None, :] if with_bias else 0.0)
+    bound = 3 * U * (np.abs(prod) + (np.abs(b.astype(np.float64))[None, :] if with_bias else 0)) + 1e-30
+    assert (np.abs(pre.astype(np.float64) - exact) <= bound).all()
+
+
+def test_epilogue_output_within_one_step_of_exact_rounding():
+    """Against the exact (float64) requantization: at most one code apart, and
+    identical wherever the exact value is not within 1e-3 of a rounding tie."""
+    c = qi.linear_case(25, 48, 512, 80)
+    q, acc = oracle.linear(c.x, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                           c.out_zp, return_acc=True)
+    v = acc.astype(np.float64) * c.in_scale * c.weight_scales.astype(np.float64)[None, :] + \
+        c.bias.astype(np.float64)[None, :]
+    t = v / c.out_scale
+    exact = np.clip(np.rint(t) + c.out_zp, -128, 127)
+    d = np.abs(q.astype(np.float64) - exact)
+    assert d.max() <= 1
+    far = np.abs(np.abs(t - np.floor(t)) - 0.5) > 1e-3
+    assert (d[far] == 0).all()
+    # the workload's output scale keeps most outputs inside the int8 range
+    assert (np.abs(q.astype(int)) < 127).mean() > 0.9
+
+
+def test_epilogue_channel_of_nchw_element():
+    """Element e of an NCHW tensor belongs to channel (e // (H*W)) % C."""
+    Nb, C, H, W = 2, 3, 2, 2
+    acc = np.full((Nb, C, H, W), 8, np.int32)
+    ws = np.array([0.25, 0.5, 1.0], np.float32)
+    q = oracle.epilogue(acc, C, H * W, 1.0, ws, None, 1.0, 0)
+    for n in range(Nb):
+        for ch, expect in enumerate([2, 4, 8]):
+            assert (q[n, ch] == expect).all()
+
+
+def test_epilogue_null_bias_equals_zero_bias():
+    c = qi.linear_case(26, 8, 64, 16)
+    a = oracle.linear(c.x, c.w, c.weight_scales, None, c.in_scale, c.in_zp, c.out_scale, c.out_zp)
+    b = oracle.linear(c.x, c.w, c.weight_scales, np.zeros(16, np.float32), c.in_scale, c.in_zp,
+                      c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_chain_small_against_torch_pieces():
+    """quantize -> linear on the small chain workload, with quantize taken from
+    torch and the contraction from float64 matmul."""
+    c = qi.make_chain_small()
+    xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    np.testing.assert_array_equal(xq, _torch_quant(c.x_fp32, c.in_scale, c.in_zp))
+    q, acc = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                           c.out_zp, return_acc=True)
+    ref = (torch.from_numpy(xq).double() - c.in_zp) @ torch.from_numpy(c.w).double().T
+    np.testing.assert_array_equal(acc, ref.numpy().astype(np.int32))
+
+
+# --------------------------------------------------------------------------- deconv
+def _orig_weight(w, OC, Kh, Kw, IC):
+    """Undo the ahead-of-time reshape weight[oc,(kh*Kw+kw)*IC+ic] = orig[ic,oc,kh,kw]."""
+    return torch.from_numpy(np.ascontiguousarray(w[:, :Kh * Kw * IC])).reshape(
+        OC, Kh, Kw, IC).permute(3, 0, 1, 2).contiguous()
+
+
+def _torch_deconv_acc(x, w, zp, Kh, Kw, stride, padding, output_padding, dilation):
+    N, IC, H, W = x.shape
+    OC = w.shape[0]
+    wo = _orig_weight(w, OC, Kh, Kw, IC).double()
+    xs = torch.from_numpy(x).double() - zp
+    return F.conv_transpose2d(xs, wo, stride=stride, padding=padding,
+                              output_padding=output_padding, dilation=dilation).numpy()
+
+
+def test_deconv_hand_cases():
+    for c in _gold("deconv_hand.json")["cases"]:
+        x = np.array(c["x"], np.int8).reshape(c["N"], c["IC"], c["H_in"], c["W_in"])
+        w = np.array(c["w"], np.int8).reshape(c["OC"], -1)
+        for method in ("gather", "scatter", "zpfill"):
+            acc = oracle.deconv_acc(x, w, c["zp"], c["Kh"], c["Kw"], c["stride"], c["pad"], (1, 1),
+                                    c["H_out"], c["W_out"], method=method)
+            np.testing.assert_array_equal(acc.reshape(-1), np.array(c["acc"]), err_msg=c["name"])
+
+
+DECONV_SHAPES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, dil
+    (1, 5, 6, 7, 3, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1)),
+    (2, 4, 5, 5, 6, 4, 4, (2, 2), (1, 1), (0, 0), (1, 1)),
+    (1, 3, 4, 6, 2, 3, 2, (3, 2), (0, 1), (2, 1), (1, 1)),
+    (1, 2, 5, 4, 3, 1, 1, (1, 1), (0, 0), (0, 0), (1, 1)),
+    (1, 3, 4, 4, 2, 5, 3, (2, 3), (2, 1), (1, 0), (1, 1)),
+    (1, 2, 4, 5, 2, 3, 3, (2, 2), (1, 2), (1, 0), (2, 2)),
+    (2, 3, 3, 3, 4, 2, 2, (1, 1), (1, 0), (0, 0), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("shape", DECONV_SHAPES)
+def test_deconv_matches_torch_conv_transpose2d(shape):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, d = shape
+    g = qi.rng(sum(shape[:7]))
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = g.integers(-128, 128, size=(OC, Kh * Kw * IC), dtype=np.int8)
+    ref = _torch_deconv_acc(x, w, 3, Kh, Kw, s, p, op, d)
+    H_out, W_out = ref.shape[2:]
+    assert H_out == qi.deconv_out_size(H, Kh, s[0], p[0], op[0], d[0])
+    assert W_out == qi.deconv_out_size(W, Kw, s[1], p[1], op[1], d[1])
+    for method in ("gather", "scatter", "zpfill"):
+        acc = oracle.deconv_acc(x, w, 3, Kh, Kw, s, p, d, H_out, W_out, method=method)
+        np.testing.assert_array_equal(acc, ref.astype(np.int32), err_msg=method)
+
+
+@pytest.mark.parametrize("H_out,W_out", [(3, 17), (20, 9), (1, 1), (0, 5)])
+def test_deconv_gather_scatter_zpfill_agree_for_any_output_size(H_out, W_out):
+    """The output size is given explicitly; for any size the three
+    formulations of the sum agree."""
+    g = qi.rng(31 + H_out * 7 + W_out)
+    x = qi.x_int8(g, (2, 3, 5, 4))
+    w = qi.w_int8(g, (4, 3 * 3 * 3 + 5))  # padded weight rows
+    a = oracle.deconv_acc(x, w, -7, 3, 3, (2, 2), (1, 1), (1, 1), H_out, W_out, "gather")
+    b = oracle.deconv_acc(x, w, -7, 3, 3, (2, 2), (1, 1), (1, 1), H_out, W_out, "scatter")
+    c = oracle.deconv_acc(x, w, -7, 3, 3, (2, 2), (1, 1), (1, 1), H_out, W_out, "zpfill")
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a, c)
+
+
+def test_deconv_adjoint_identity():
+    """<convT(x'), y> == <x', conv2d(y)> for x' = x - zp (integers, exact in float64)."""
+    g = qi.rng(41)
+    N, IC, H, W, OC, K = 2, 4, 5, 6, 3, 3
+    s, p, op = (2, 2), (1, 1), (1, 1)
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, K * K * IC))
+    Ho, Wo = qi.deconv_out_size(H, K, 2, 1, 1), qi.deconv_out_size(W, K, 2, 1, 1)
+    acc = oracle.deconv_acc(x, w, 3, K, K, s, p, (1, 1), Ho, Wo)
+    y = torch.from_numpy(g.integers(-50, 51, size=(N, OC, Ho, Wo))).double()
+    wo = _orig_weight(w, OC, K, K, IC).double()
+    back = F.conv2d(y, wo, stride=s, padding=p)  # [N, IC, H, W]
+    lhs = float((torch.from_numpy(acc).double() * y).sum())
+    rhs = float(((torch.from_numpy(x).double() - 3) * back[:, :, :H, :W]).sum())
+    assert lhs == rhs
+
+
+def test_deconv_1x1_stride1_is_linear_on_nhwc():
+    g = qi.rng(42)
+    N, IC, H, W, OC = 2, 40, 3, 5, 24
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, IC))
+    acc = oracle.deconv_acc(x, w, 3, 1, 1, (1, 1), (0, 0), (1, 1), H, W)
+    lin = oracle.linear_acc(x.transpose(0, 2, 3, 1).reshape(-1, IC), w, 3)
+    np.testing.assert_array_equal(acc.transpose(0, 2, 3, 1).reshape(-1, OC), lin)
+
+
+def test_deconv_epilogue_channel_is_oc():
+    c = qi.deconv_case(43, 2, 6, 5, 4, 5, 3, 3, (2, 2), (1, 1), (1, 1))
+    q, acc = oracle.conv2d_transposed(c.x, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                      c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding,
+                                      c.dilation, c.H_out, c.W_out, return_acc=True)
+    v = acc.astype(np.float64) * c.in_scale * c.weight_scales.astype(np.float64)[None, :, None, None] \
+        + c.bias.astype(np.float64)[None, :, None, None]
+    t = v / c.out_scale
+    exact = np.clip(np.rint(t) + c.out_zp, -128, 127)
+    d = np.abs(q.astype(np.float64) - exact)
+    assert d.max() <= 1
+    far = np.abs(np.abs(t - np.floor(t)) - 0.5) > 1e-3
+    assert (d[far] == 0).all()
+
+
+def test_deconv_small_workload_matches_torch():
+    c = qi.make_deconv_small()
+    assert (c.H_out, c.W_out) == (64, 64)
+    acc = oracle.deconv_acc(c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation,
+                            c.H_out, c.W_out)
+    ref = _torch_deconv_acc(c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding,
+                            c.output_padding, c.dilation)
+    np.testing.assert_array_equal(acc, ref.astype(np.int32))
+
+
+def test_deconv_large_workload_output_size():
+    c = qi.make_deconv_large()
+    assert (c.H_out, c.W_out) == (128, 128)
+    assert c.w.shape == (128, 9 * 256)
