@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Benchmark of the q8ta int8 path on one MI355X.
+
+A step is one pass of the measured workload over resident synthetic inputs.
+The default workload is the large linear:
+    q8ta_linear GEMM  M=2048 K=4096 N=11008  (int8 x int8 -> int32 -> int8)
+    -> dequantize_per_tensor of the int8 output to fp32
+`value` is 2*M*N*K int8 operations per step divided by the step time (TOPS).
+
+The JSON line also carries
+  roofline      the GEMM kernel's own rate (HIP events around each launch in
+                the timed region, on the stream it runs on) against the dense
+                int8 MFMA peak;
+  cpu_baseline  the CPU oracle timed on a sample of the same workload
+                (a block of rows; the GPU's rows are compared with it);
+  extra         the other workloads of the op family, each timed with events:
+                GEMV, quantize, dequantize and the two transposed convolutions;
+                HBM-bound kernels rotate through enough buffer copies to
+                exceed the 256 MB last-level cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8 TOPS (2·M·N·Kred) for q8ta_linear/conv_transposed; % of int8 MFMA peak"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 matrix peak, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+# Vector-ALU int8 peak: 256 CUs x 2.4 GHz x 64 lanes/clk x 4 MACs (v_dot4) x 2 ops.
+PEAK_DOT4_TOPS = 256 * 2.4e9 * 64 * 4 * 2 / 1e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def valid_taps(out_size, in_size, k, s, p):
+    """Number of (output, tap) pairs of one spatial axis the gather sums."""
+    n = 0
+    for o in range(out_size):
+        for kk in range(k):
+            num = o + p - kk
+            if num >= 0 and num % s == 0 and num // s < in_size:
+                n += 1
+    return n
+
+
+def deconv_ops(c):
+    N, IC, H, W = c.x.shape if c.x_fp32 is None else c.x_fp32.shape
+    OC = c.w.shape[0]
+    th = valid_taps(c.H_out, H, c.Kh, c.stride[0], c.padding[0])
+    tw = valid_taps(c.W_out, W, c.Kw, c.stride[1], c.padding[1])
+    return 2 * N * OC * IC * th * tw
+
+
+def file_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(name, src):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy kernel of known size) and stored beside the
+    profiles; only used while the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha256_16") != file_hash(src):
+        return None
+    return d.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream libq8ta launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time_calls(self, fns, reps, budget_s=4.0):
+        """Time up to `reps` calls (cycling through `fns`), fewer when one call
+        is slow, so that the loop stays within about `budget_s` seconds."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fns[0]()
+        e1.record()
+        torch.cuda.synchronize()
+        one = max(e0.elapsed_time(e1) / 1e3, 1e-6)
+        reps = int(max(3, min(reps, budget_s / one)))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record()
+            fns[i % len(fns)]()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]   # ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the q8ta path has no multi-GPU form in this "
+              "library (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int8_quantized_amd as q8
+    import q8ta_inputs as qi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    lib = q8.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = Timer(torch)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(q8.q8ta_last_error())
+
+    # ------------------------------------------------------------ headline: GEMM -> dequantize
+    c = qi.make_gemm()
+    M, K, N = c.M, c.K, c.N
+    log(f"workload: q8ta_linear GEMM M={M} K={K} N={N} -> dequantize_per_tensor")
+    x = torch.from_numpy(c.x).cuda()
+    w = torch.from_numpy(c.w).cuda()
+    ws = torch.from_numpy(c.weight_scales).cuda()
+    b = torch.from_numpy(c.bias).cuda()
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    none = b"none"
+
+    def gemm():
+        check(lib.q8ta_linear(x.data_ptr(), M, K, c.in_scale, c.in_zp, w.data_ptr(), N, None,
+                              ws.data_ptr(), b.data_ptr(), c.out_scale, c.out_zp, none,
+                              out.data_ptr(), stream))
+
+    def deq():
+        check(lib.q8ta_dequantize_per_tensor(out.data_ptr(), y.data_ptr(), M * N, c.out_scale,
+                                             c.out_zp, stream))
+
+    for _ in range(args.warmup):
+        gemm()
+        deq()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        gemm()
+        ev[i][1].record()
+        deq()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    ops = 2.0 * M * N * K
+    gemm_ms = [a.elapsed_time(bb) for a, bb in ev]
+    gemm_avg_s = statistics.mean(gemm_ms) / 1e3
+    achieved = ops / gemm_avg_s / 1e12
+    log(f"step {step_s * 1e6:.1f} us; GEMM avg {gemm_avg_s * 1e6:.1f} us "
+        f"(min {min(gemm_ms) * 1e3:.1f}) = {achieved:.1f} TOPS")
+
+    # The matrix-core GEMM is switched off in this build; q8ta_linear with M > 4
+    # runs the vector-ALU v_dot4 kernel, whose own ceiling is PEAK_DOT4_TOPS.
+    roofline = {
+        "bound": "alu", "kernel": "k_dot4_gemm<8,8> (v_dot4_i32_i8, vector ALU)",
+        "achieved": round(achieved, 2), "peak": round(PEAK_DOT4_TOPS, 1), "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_DOT4_TOPS, 4),
+        "frac_of_int8_mfma_peak": round(achieved / PEAK_INT8_TOPS, 5),
+        "per_launch_ops": ops, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
+        "traffic": traffic_from_profile("gemm", os.path.join(ROOT, "int8_quantized_amd", "csrc",
+                                                             "gemm_dot4.hip")),
+    }
+
+    # ------------------------------------------------------------ CPU baseline (oracle sample)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        got = out.cpu().numpy()
+        t = time.perf_counter()
+        probe = oracle.linear(c.x[:8], c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                              c.out_scale, c.out_zp)
+        rate = 8 / (time.perf_counter() - t)           # rows per second
+        rows = int(max(8, min(M, round(rate * args.cpu_seconds))))
+        t = time.perf_counter()
+        ref = oracle.linear(c.x[:rows], c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                            c.out_scale, c.out_zp)
+        dt = time.perf_counter() - t
+        cpu = {"value": round(2.0 * rows * N * K / dt / 1e12, 5), "unit": "TOPS",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"rows 0..{rows - 1} of the {M}x{K} activations against all {N} weight "
+                         f"rows (contraction + epilogue), {dt:.1f} s",
+               "sample_bitexact_vs_gpu": bool(np.array_equal(got[:rows], ref) and
+                                             np.array_equal(got[:8], probe))}
+        log(f"cpu oracle: {cpu}")
+
+    # ------------------------------------------------------------ the other workloads
+    extra = {}
+    if not args.no_extra:
+        extra = run_extra(torch, np, q8, qi, lib, stream, timer, check)
+
+    line = {
+        "metric": METRIC, "value": round(ops / step_s / 1e12, 2), "unit": "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "q8ta_linear GEMM M=2048 K=4096 N=11008 -> dequantize_per_tensor",
+                   "M": M, "K": K, "N": N, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_extra(torch, np, q8, qi, lib, stream, timer, check):
+    res = {}
+    reps = 60
+
+    def summary(ms, work, unit, peak):
+        med = statistics.median(ms) / 1e3
+        rate = work / med / (1e9 if unit == "GB/s" else 1e12)
+        d = {"median_us": round(med * 1e6, 2), "min_us": round(min(ms) * 1e3, 2),
+             "rate": round(rate, 2), "unit": unit}
+        if peak:
+            d["frac"] = round(rate / peak, 4)
+        return d
+
+    # ---- GEMV M=1 K=4096 N=4096, HBM-bound: rotate 32 weight copies (537 MB)
+    c = qi.make_gemv()
+    log("extra: gemv 1x4096x4096")
+    copies = 32
+    ws_ = torch.from_numpy(c.weight_scales).cuda()
+    b_ = torch.from_numpy(c.bias).cuda()
+    x_ = torch.from_numpy(c.x).cuda()
+    wl = [torch.from_numpy(c.w).cuda() for _ in range(copies)]
+    outs = [torch.empty((1, c.N), dtype=torch.int8, device="cuda") for _ in range(copies)]
+    fns = [(lambda i=i: check(lib.q8ta_linear_gemv(
+        x_.data_ptr(), 1, c.K, c.in_scale, c.in_zp, wl[i].data_ptr(), c.N, None, ws_.data_ptr(),
+        b_.data_ptr(), c.out_scale, c.out_zp, b"none", outs[i].data_ptr(), stream)))
+        for i in range(copies)]
+    gemv_bytes = c.N * c.K + c.K + 4 * c.N + 4 * c.N + c.N
+    timer.time_calls(fns, copies)
+    res["gemv_1x4096x4096_cold"] = summary(timer.time_calls(fns, 4 * copies), gemv_bytes, "GB/s",
+                                           PEAK_HBM_GBS)
+    res["gemv_1x4096x4096_warm"] = summary(timer.time_calls([fns[0]], reps), gemv_bytes, "GB/s",
+                                           PEAK_HBM_GBS)
+    res["gemv_1x4096x4096_cold"]["algorithmic_bytes"] = gemv_bytes
+    del wl, outs, fns
+
+    # ---- quantize [8,256,64,64] (rotate 16 copies) and the large transposed conv
+    d = qi.make_deconv_large()
+    log("extra: quantize [8,256,64,64] + deconv -> [8,128,128,128]")
+    copies = 16
+    numel = d.x_fp32.size
+    xs = [torch.from_numpy(d.x_fp32).cuda() for _ in range(copies)]
+    qs = [torch.empty(d.x_fp32.shape, dtype=torch.int8, device="cuda") for _ in range(copies)]
+    qfns = [(lambda i=i: check(lib.q8ta_quantize_per_tensor(
+        xs[i].data_ptr(), qs[i].data_ptr(), numel, d.in_scale, d.in_zp, stream)))
+        for i in range(copies)]
+    timer.time_calls(qfns, copies)
+    res["quantize_8x256x64x64_cold"] = summary(timer.time_calls(qfns, 4 * copies), 5 * numel,
+                                               "GB/s", PEAK_HBM_GBS)
+    res["quantize_8x256x64x64_warm"] = summary(timer.time_calls([qfns[0]], reps), 5 * numel,
+                                               "GB/s", PEAK_HBM_GBS)
+    xq = qs[0]
+    del xs, qfns
+    w_ = torch.from_numpy(d.w).cuda()
+    dws = torch.from_numpy(d.weight_scales).cuda()
+    db = torch.from_numpy(d.bias).cuda()
+    N_, IC, H, W = d.x_fp32.shape
+    OC = d.w.shape[0]
+    dout = torch.empty((N_, OC, d.H_out, d.W_out), dtype=torch.int8, device="cuda")
+
+    def dc_large(xq=xq):
+        check(lib.q8ta_conv2d_transposed(
+            xq.data_ptr(), N_, IC, H, W, d.in_scale, d.in_zp, w_.data_ptr(), OC, d.Kh, d.Kw,
+            d.w.shape[1], None, dws.data_ptr(), db.data_ptr(), d.out_scale, d.out_zp,
+            d.stride[0], d.stride[1], d.padding[0], d.padding[1], d.output_padding[0],
+            d.output_padding[1], 1, 1, 1, b"none", dout.data_ptr(), d.H_out, d.W_out, stream))
+    dops = deconv_ops(d)
+    dfns = [(lambda i=i: dc_large(qs[i])) for i in range(copies)]
+    timer.time_calls(dfns, copies)
+    r = summary(timer.time_calls(dfns, 4 * copies), dops, "TOPS", PEAK_INT8_TOPS)
+    r["exact_valid_tap_ops"] = dops
+    r["algorithmic_bytes"] = int(numel + d.w.size + 8 * OC + dout.numel())
+    res["deconv_8x256x64x64_k3s2p1_to_8x128x128x128"] = r
+    del qs, dfns
+
+    # ---- dequantize [2048, 11008] (rotate 8 copies of 22.5 MB in / 90 MB out)
+    log("extra: dequantize [2048,11008]")
+    n = 2048 * 11008
+    copies = 6
+    qin = [torch.randint(-128, 128, (n,), dtype=torch.int8, device="cuda") for _ in range(copies)]
+    fout = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    dqf = [(lambda i=i: check(lib.q8ta_dequantize_per_tensor(
+        qin[i].data_ptr(), fout[i].data_ptr(), n, 0.5, -5, stream))) for i in range(copies)]
+    timer.time_calls(dqf, copies)
+    res["dequantize_2048x11008_cold"] = summary(timer.time_calls(dqf, 4 * copies), 5 * n, "GB/s",
+                                                PEAK_HBM_GBS)
+    del qin, fout, dqf
+
+    # ---- small, latency-bound workloads
+    log("extra: small chain and small deconv")
+    c1 = qi.make_chain_small()
+    xf = torch.from_numpy(c1.x_fp32).cuda()
+    xq1 = torch.empty((c1.M, c1.K), dtype=torch.int8, device="cuda")
+    w1 = torch.from_numpy(c1.w).cuda()
+    s1 = torch.from_numpy(c1.weight_scales).cuda()
+    b1 = torch.from_numpy(c1.bias).cuda()
+    o1 = torch.empty((c1.M, c1.N), dtype=torch.int8, device="cuda")
+
+    def chain():
+        check(lib.q8ta_quantize_per_tensor(xf.data_ptr(), xq1.data_ptr(), c1.M * c1.K,
+                                           c1.in_scale, c1.in_zp, stream))
+        check(lib.q8ta_linear(xq1.data_ptr(), c1.M, c1.K, c1.in_scale, c1.in_zp, w1.data_ptr(),
+                              c1.N, None, s1.data_ptr(), b1.data_ptr(), c1.out_scale, c1.out_zp,
+                              b"none", o1.data_ptr(), stream))
+    timer.time_calls([chain], 10)
+    res["chain_quantize_4x64_linear_4x64x32"] = summary(timer.time_calls([chain], reps),
+                                                        2 * 4 * 64 * 32, "TOPS", None)
+
+    d4 = qi.make_deconv_small()
+    x4 = torch.from_numpy(d4.x).cuda()
+    w4 = torch.from_numpy(d4.w).cuda()
+    s4 = torch.from_numpy(d4.weight_scales).cuda()
+    b4 = torch.from_numpy(d4.bias).cuda()
+    o4 = torch.empty((1, 32, 64, 64), dtype=torch.int8, device="cuda")
+
+    def dc_small():
+        check(lib.q8ta_conv2d_transposed(
+            x4.data_ptr(), 1, 64, 32, 32, d4.in_scale, d4.in_zp, w4.data_ptr(), 32, 4, 4, 1024,
+            None, s4.data_ptr(), b4.data_ptr(), d4.out_scale, d4.out_zp, 2, 2, 1, 1, 0, 0, 1, 1,
+            1, b"none", o4.data_ptr(), 64, 64, stream))
+    timer.time_calls([dc_small], 10)
+    r = summary(timer.time_calls([dc_small], reps), deconv_ops(d4), "TOPS", PEAK_INT8_TOPS)
+    r["exact_valid_tap_ops"] = deconv_ops(d4)
+    res["deconv_1x64x32x32_k4s2p1_to_1x32x64x64"] = r
+    for k, v in res.items():
+        log(f"  {k}: {v}")
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * libq8ta -- int8 quantized-activation ("q8ta") operations for AMD Instinct
+ * MI355X (gfx950), C ABI.
+ *
+ * The operations follow three ExecuTorch WebGPU pull-request pages:
+ *   [QPT]  "Add quantize_per_tensor op (int8 buffer path)" (#21187)
+ *   [LIN]  "Add q8ta_linear op (int8 quantized linear)"     (#21197)
+ *   [DCV]  "Add q8ta_conv2d_transposed op (int8 transposed conv)" (#21205)
+ *
+ * Common rules for every entry point:
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
+ *     allocated and owned by the caller; the library never frees, retains or
+ *     allocates per call.  Tensors are dense and contiguous in the stated
+ *     layout.  int8 tensors are plain byte arrays (element i at byte i).
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns after the launch; results are visible to later work on that
+ *     stream.  Calls are reentrant and keep no state between calls.
+ *   - Scales are passed as double.  The library forms every reciprocal as
+ *     (float)(1.0 / scale) in double on the host ([QPT] commit message) and
+ *     uses (float)scale for a scale that multiplies.
+ *   - Rounding is round-half-to-even; the dequant/requant epilogue is
+ *     evaluated in float, left to right, one rounding per operation, with no
+ *     fused multiply-add:  v = ((float)acc * (float)input_scale) *
+ *     weight_scales[c] + bias[c];  q = clamp(rint(v * inv_output_scale) +
+ *     output_zero_point, -128, 127)  ([LIN]/[DCV] Solution).
+ *   - Accumulators are int32 ([LIN] Solution: an i32 GEMM).  Inputs whose
+ *     exact sums leave the int32 range are outside the contract.
+ *   - Errors are loud: on any invalid argument the call returns a non-zero
+ *     q8ta_status, launches nothing, and q8ta_last_error() describes the
+ *     problem.  Argument checks run before any HIP runtime call.
+ *     Q8TA_ERR_HIP reports a failed launch (for example, no GPU present).
+ *     NaN inputs are outside the contract.
+ */
+#ifndef Q8TA_H
+#define Q8TA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum q8ta_status {
+  Q8TA_OK = 0,
+  Q8TA_ERR_NULL = 1,        /* a required pointer is NULL */
+  Q8TA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  Q8TA_ERR_QPARAM = 3,      /* a scale is not finite and > 0, or a zero point is outside [-128, 127] */
+  Q8TA_ERR_UNSUPPORTED = 4, /* an argument value the op does not implement (activation, groups, dilation) */
+  Q8TA_ERR_HIP = 5          /* the HIP runtime reported an error */
+} q8ta_status;
+
+/* Message for the last non-OK status returned on the calling thread
+ * (a static or thread-local string; never NULL). */
+const char* q8ta_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * [QPT] commit message (Solution / Implementation):
+ *   out[i] = clamp(rint(x[i] * (float)(1.0 / scale)) + zero_point, -128, 127)
+ * x: fp32 [numel]; out: int8 [numel]; numel >= 0 (0 is a no-op).
+ * scale finite and > 0; zero_point in [-128, 127].
+ * The page's numel % 4 requirement (a WebGPU word-binding artifact) does not
+ * apply: any numel and any byte alignment of out is accepted.
+ */
+q8ta_status q8ta_quantize_per_tensor(const float* x, int8_t* out, int64_t numel,
+                                     double scale, int64_t zero_point,
+                                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * dequantize_per_tensor, the op named beside the q8ta ops in the
+ * quantize -> q8ta_* -> dequantize subgraph ([LIN]/[DCV] Problem); the pages
+ * do not print it, and the decomposed definition is used:
+ *   out[i] = (float)(x[i] - zero_point) * (float)scale
+ * x: int8 [numel]; out: fp32 [numel]; numel >= 0.  Same checks as quantize.
+ */
+q8ta_status q8ta_dequantize_per_tensor(const int8_t* x, float* out, int64_t numel,
+                                       double scale, int64_t zero_point,
+                                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * q8ta_linear ([LIN] Solution and Constraints (2)):
+ *   acc[m,n] = sum_k (x[m,k] - input_zero_point) * weight[n,k]      (int32)
+ *   out[m,n] = epilogue(acc[m,n]) with channel c = n
+ * x: int8 [M, K] row-major; weight: int8 [N, K] row-major (symmetric, no
+ * weight zero point); weight_scales: fp32, at least N entries (only [0, N)
+ * is read); bias: fp32, at least N entries, or NULL for no bias;
+ * out: int8 [M, N] row-major.  M, K, N >= 1.
+ * weight_sums: accepted and ignored, as on the page (the zero-point term is
+ * computed from the weights on every call); may be NULL.
+ * activation: must be the string "none"; anything else (including NULL)
+ * returns Q8TA_ERR_UNSUPPORTED ([LIN] Implementation).
+ * The page's N % 4 and M*K % 4 requirements do not apply.
+ */
+q8ta_status q8ta_linear(const int8_t* x, int64_t M, int64_t K,
+                        double input_scale, int64_t input_zero_point,
+                        const int8_t* weight, int64_t N,
+                        const int32_t* weight_sums,
+                        const float* weight_scales, const float* bias,
+                        double output_scale, int64_t output_zero_point,
+                        const char* activation, int8_t* out,
+                        hipStream_t stream);
+
+/* q8ta_linear_gemv ([LIN] Solution: identical schema, the M == 1 case, served
+ * by the same handler).  Same arguments and results as q8ta_linear; returns
+ * Q8TA_ERR_SHAPE unless M == 1. */
+q8ta_status q8ta_linear_gemv(const int8_t* x, int64_t M, int64_t K,
+                             double input_scale, int64_t input_zero_point,
+                             const int8_t* weight, int64_t N,
+                             const int32_t* weight_sums,
+                             const float* weight_scales, const float* bias,
+                             double output_scale, int64_t output_zero_point,
+                             const char* activation, int8_t* out,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * q8ta_conv2d_transposed ([DCV] Solution, Implementation, Constraints):
+ *   acc[n,oc,oh,ow] = sum over (ic, kh, kw) of
+ *       (x[n,ic,ih,iw] - input_zero_point) * weight[oc, (kh*Kw + kw)*IC + ic]
+ *   where ih = (oh + pad_h - kh*dilation_h) / stride_h is used only when the
+ *   numerator is >= 0, divisible by stride_h and ih < H_in (iw likewise);
+ *   out[n,oc,oh,ow] = epilogue(acc) with channel c = oc.
+ * x: int8 NCHW [N, IC, H_in, W_in]; weight: int8 [OC, weight_row_stride],
+ * weight_row_stride >= Kh*Kw*IC (row padding is tolerated, only the first
+ * Kh*Kw*IC bytes of a row are read); weight_scales / bias: fp32 with at least
+ * OC entries (bias may be NULL); out: int8 NCHW [N, OC, H_out, W_out].
+ * H_out and W_out are given explicitly (the page takes them from the
+ * serialized output dims); output_padding_h/_w are accepted and unused.
+ * Requirements: all sizes >= 1, stride >= 1, padding >= 0; dilation must be
+ * 1 and groups must be 1 (Q8TA_ERR_UNSUPPORTED otherwise, as on the page);
+ * activation must be "none".  weight_sums is ignored.
+ */
+q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
+                                   int64_t H_in, int64_t W_in,
+                                   double input_scale, int64_t input_zero_point,
+                                   const int8_t* weight, int64_t OC,
+                                   int64_t Kh, int64_t Kw,
+                                   int64_t weight_row_stride,
+                                   const int32_t* weight_sums,
+                                   const float* weight_scales, const float* bias,
+                                   double output_scale, int64_t output_zero_point,
+                                   int64_t stride_h, int64_t stride_w,
+                                   int64_t pad_h, int64_t pad_w,
+                                   int64_t output_padding_h, int64_t output_padding_w,
+                                   int64_t dilation_h, int64_t dilation_w,
+                                   int64_t groups, const char* activation,
+                                   int8_t* out, int64_t H_out, int64_t W_out,
+                                   hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Accumulator outputs (for verification).  These run the same contraction
+ * kernels as q8ta_linear / q8ta_conv2d_transposed but store the int32
+ * accumulator (the sum above, zero-point term included) instead of the
+ * requantized int8 value.  acc: int32 [M, N] row-major, or NCHW
+ * [N, OC, H_out, W_out].  Argument checks as for the parent op.
+ */
+q8ta_status q8ta_linear_acc(const int8_t* x, int64_t M, int64_t K,
+                            int64_t input_zero_point,
+                            const int8_t* weight, int64_t N,
+                            int32_t* acc, hipStream_t stream);
+
+q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC,
+                                       int64_t H_in, int64_t W_in,
+                                       int64_t input_zero_point,
+                                       const int8_t* weight, int64_t OC,
+                                       int64_t Kh, int64_t Kw,
+                                       int64_t weight_row_stride,
+                                       int64_t stride_h, int64_t stride_w,
+                                       int64_t pad_h, int64_t pad_w,
+                                       int32_t* acc, int64_t H_out, int64_t W_out,
+                                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8TA_H */

@@ -1,0 +1,231 @@
+"""int8_quantized_amd -- Python binding of libq8ta (MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI declared in ``include/q8ta.h``: every
+function here has the name of the C entry point it calls, checks that its
+tensors are dense device tensors of the right dtype, and passes their data
+pointers, sizes and the current HIP stream.  All arithmetic runs in the HIP
+kernels of ``libq8ta.so``; there is no fallback.  If the library has not been
+built, loading fails loudly (build it with ``python -m int8_quantized_amd.build``).
+
+PyTorch is used only for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8ta.so")
+
+Q8TA_OK = 0
+Q8TA_ERR_NULL = 1
+Q8TA_ERR_SHAPE = 2
+Q8TA_ERR_QPARAM = 3
+Q8TA_ERR_UNSUPPORTED = 4
+Q8TA_ERR_HIP = 5
+
+STATUS_NAMES = {0: "Q8TA_OK", 1: "Q8TA_ERR_NULL", 2: "Q8TA_ERR_SHAPE", 3: "Q8TA_ERR_QPARAM",
+                4: "Q8TA_ERR_UNSUPPORTED", 5: "Q8TA_ERR_HIP"}
+
+
+class Q8taError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_I64 = ctypes.c_int64
+_DBL = ctypes.c_double
+_P = ctypes.c_void_p
+_S = ctypes.c_char_p
+
+# argument types of every exported entry point, in declaration order
+SIGNATURES = {
+    "q8ta_last_error": ([], ctypes.c_char_p),
+    "q8ta_quantize_per_tensor": ([_P, _P, _I64, _DBL, _I64, _P], ctypes.c_int),
+    "q8ta_dequantize_per_tensor": ([_P, _P, _I64, _DBL, _I64, _P], ctypes.c_int),
+    "q8ta_linear": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S, _P, _P],
+                    ctypes.c_int),
+    "q8ta_linear_gemv": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S, _P,
+                          _P], ctypes.c_int),
+    "q8ta_conv2d_transposed": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64, _I64, _I64,
+                                _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                _I64, _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
+    "q8ta_linear_acc": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
+    "q8ta_conv2d_transposed_acc": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64,
+                                    _I64, _I64, _I64, _I64, _P, _I64, _I64, _P], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libq8ta.so with argument types set (raises if not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libq8ta.so not found at {LIB_PATH}: build it with "
+                "`python -m int8_quantized_amd.build` (there is no CPU fallback)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def q8ta_last_error() -> str:
+    return lib().q8ta_last_error().decode()
+
+
+def _check(status: int):
+    if status != Q8TA_OK:
+        raise Q8taError(status, q8ta_last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t, dtype, name):
+    return None if t is None else _dev(t, dtype, name)
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _act(activation):
+    return None if activation is None else activation.encode()
+
+
+# ---------------------------------------------------------------------------
+def q8ta_quantize_per_tensor(x, out, scale: float, zero_point: int, stream=None):
+    """out (int8) = clamp(rint(x * (float)(1/scale)) + zero_point, -128, 127)."""
+    torch = _torch()
+    if x.numel() != out.numel():
+        raise ValueError("x and out must have the same number of elements")
+    _check(lib().q8ta_quantize_per_tensor(_dev(x, torch.float32, "x"), _dev(out, torch.int8, "out"),
+                                          x.numel(), float(scale), int(zero_point), _stream(stream)))
+    return out
+
+
+def q8ta_dequantize_per_tensor(x, out, scale: float, zero_point: int, stream=None):
+    """out (fp32) = (float)(x - zero_point) * (float)scale."""
+    torch = _torch()
+    if x.numel() != out.numel():
+        raise ValueError("x and out must have the same number of elements")
+    _check(lib().q8ta_dequantize_per_tensor(_dev(x, torch.int8, "x"), _dev(out, torch.float32, "out"),
+                                            x.numel(), float(scale), int(zero_point), _stream(stream)))
+    return out
+
+
+def _linear(fn, x, input_scale, input_zero_point, weight, weight_sums, weight_scales, bias,
+            output_scale, output_zero_point, activation, out, stream):
+    torch = _torch()
+    if x.dim() != 2 or weight.dim() != 2 or out.dim() != 2:
+        raise ValueError("x [M,K], weight [N,K] and out [M,N] must be 2-D")
+    M, K = x.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, weight {tuple(weight.shape)}, "
+                         f"out {tuple(out.shape)}")
+    _check(fn(_dev(x, torch.int8, "x"), M, K, float(input_scale), int(input_zero_point),
+              _dev(weight, torch.int8, "weight"), N, _opt(weight_sums, torch.int32, "weight_sums"),
+              _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+              float(output_scale), int(output_zero_point), _act(activation),
+              _dev(out, torch.int8, "out"), _stream(stream)))
+    return out
+
+
+def q8ta_linear(x, input_scale, input_zero_point, weight, weight_sums, weight_scales, bias,
+                output_scale, output_zero_point, activation, out, stream=None):
+    """int8 [M,K] x int8 [N,K] -> int8 [M,N] with the per-channel epilogue."""
+    return _linear(lib().q8ta_linear, x, input_scale, input_zero_point, weight, weight_sums,
+                   weight_scales, bias, output_scale, output_zero_point, activation, out, stream)
+
+
+def q8ta_linear_gemv(x, input_scale, input_zero_point, weight, weight_sums, weight_scales, bias,
+                     output_scale, output_zero_point, activation, out, stream=None):
+    """q8ta_linear for M == 1."""
+    return _linear(lib().q8ta_linear_gemv, x, input_scale, input_zero_point, weight, weight_sums,
+                   weight_scales, bias, output_scale, output_zero_point, activation, out, stream)
+
+
+def q8ta_linear_acc(x, input_zero_point, weight, acc, stream=None):
+    """int32 accumulator of q8ta_linear: acc[m,n] = sum_k (x[m,k]-izp)*w[n,k]."""
+    torch = _torch()
+    M, K = x.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K or tuple(acc.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check(lib().q8ta_linear_acc(_dev(x, torch.int8, "x"), M, K, int(input_zero_point),
+                                 _dev(weight, torch.int8, "weight"), N,
+                                 _dev(acc, torch.int32, "acc"), _stream(stream)))
+    return acc
+
+
+def q8ta_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw, weight_sums,
+                           weight_scales, bias, output_scale, output_zero_point, stride, padding,
+                           output_padding, dilation, groups, activation, out, stream=None):
+    """int8 NCHW x int8 [OC, ldw] -> int8 NCHW out (H_out, W_out taken from out)."""
+    torch = _torch()
+    if x.dim() != 4 or weight.dim() != 2 or out.dim() != 4:
+        raise ValueError("x [N,IC,H,W], weight [OC, ldw] and out [N,OC,H_out,W_out] expected")
+    N, IC, H_in, W_in = x.shape
+    OC, ldw = weight.shape
+    if out.shape[0] != N or out.shape[1] != OC:
+        raise ValueError("out must be [N, OC, H_out, W_out]")
+    H_out, W_out = out.shape[2], out.shape[3]
+    _check(lib().q8ta_conv2d_transposed(
+        _dev(x, torch.int8, "x"), N, IC, H_in, W_in, float(input_scale), int(input_zero_point),
+        _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw,
+        _opt(weight_sums, torch.int32, "weight_sums"),
+        _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+        float(output_scale), int(output_zero_point), int(stride[0]), int(stride[1]),
+        int(padding[0]), int(padding[1]), int(output_padding[0]), int(output_padding[1]),
+        int(dilation[0]), int(dilation[1]), int(groups), _act(activation),
+        _dev(out, torch.int8, "out"), H_out, W_out, _stream(stream)))
+    return out
+
+
+def q8ta_conv2d_transposed_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, acc,
+                               stream=None):
+    """int32 accumulator of q8ta_conv2d_transposed (NCHW [N, OC, H_out, W_out])."""
+    torch = _torch()
+    N, IC, H_in, W_in = x.shape
+    OC, ldw = weight.shape
+    if acc.dim() != 4 or acc.shape[0] != N or acc.shape[1] != OC:
+        raise ValueError("acc must be [N, OC, H_out, W_out]")
+    _check(lib().q8ta_conv2d_transposed_acc(
+        _dev(x, torch.int8, "x"), N, IC, H_in, W_in, int(input_zero_point),
+        _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw, int(stride[0]),
+        int(stride[1]), int(padding[0]), int(padding[1]), _dev(acc, torch.int32, "acc"),
+        acc.shape[2], acc.shape[3], _stream(stream)))
+    return acc
+
+
+__all__ = [
+    "Q8taError", "lib", "q8ta_last_error", "q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor",
+    "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_acc", "q8ta_conv2d_transposed",
+    "q8ta_conv2d_transposed_acc",
+]

@@ -1,0 +1,246 @@
+// libq8ta C ABI: argument checks, kernel choice, launch.
+//
+// Every entry point validates all of its arguments before touching the HIP
+// runtime, so invalid calls fail (loudly, with a status and a message) even
+// on a machine without a GPU, and nothing is launched for them.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/q8ta.h"
+#include "q8ta_internal.h"
+
+using namespace q8ta;
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+q8ta_status fail(q8ta_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+q8ta_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return Q8TA_OK;
+  return fail(Q8TA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool scale_ok(double s) { return std::isfinite(s) && s > 0.0; }
+bool zp_ok(int64_t z) { return z >= -128 && z <= 127; }
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+// Reciprocal of a scale as the quantize page defines it: divide in double,
+// round once to float.
+float recip(double s) { return (float)(1.0 / s); }
+
+q8ta_status check_qparams(const char* op, double scale, int64_t zp) {
+  if (!scale_ok(scale)) return fail(Q8TA_ERR_QPARAM, "%s: scale must be finite and > 0 (got %g)", op, scale);
+  if (!zp_ok(zp)) return fail(Q8TA_ERR_QPARAM, "%s: zero_point must be in [-128, 127] (got %lld)", op, (long long)zp);
+  return Q8TA_OK;
+}
+
+q8ta_status check_activation(const char* op, const char* activation) {
+  if (!activation) return fail(Q8TA_ERR_UNSUPPORTED, "%s: activation is NULL (only \"none\" is supported)", op);
+  if (strcmp(activation, "none") != 0)
+    return fail(Q8TA_ERR_UNSUPPORTED, "%s: activation \"%.64s\" is not supported (only \"none\")", op, activation);
+  return Q8TA_OK;
+}
+
+q8ta_status linear_checks(const char* op, const int8_t* x, int64_t M, int64_t K, const int8_t* weight,
+                          int64_t N, const void* out) {
+  if (!x || !weight || !out) return fail(Q8TA_ERR_NULL, "%s: x, weight and out must not be NULL", op);
+  if (M < 1 || K < 1 || N < 1) return fail(Q8TA_ERR_SHAPE, "%s: M, K, N must be >= 1 (got %lld, %lld, %lld)", op,
+                                           (long long)M, (long long)K, (long long)N);
+  if (M > kMaxElems / K || N > kMaxElems / K || M > kMaxElems / N || K >= ((int64_t)1 << 31))
+    return fail(Q8TA_ERR_SHAPE, "%s: sizes too large", op);
+  return Q8TA_OK;
+}
+
+q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t M, int64_t K,
+                        double input_scale, int64_t input_zero_point, const int8_t* weight, int64_t N,
+                        const float* weight_scales, const float* bias, double output_scale,
+                        int64_t output_zero_point, const char* activation, int8_t* out,
+                        hipStream_t stream) {
+  q8ta_status st = linear_checks(op, x, M, K, weight, N, out);
+  if (st) return st;
+  if (gemv_only && M != 1) return fail(Q8TA_ERR_SHAPE, "%s: M must be 1 (got %lld)", op, (long long)M);
+  if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
+  if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
+  if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
+  if ((st = check_activation(op, activation))) return st;
+
+  LinearArgs a{};
+  a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
+  a.M = M; a.K = K; a.N = N; a.izp = (int32_t)input_zero_point;
+  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  return hip_status(launch_linear(a, stream), op);
+}
+
+}  // namespace
+
+namespace q8ta {
+
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
+  if (gemv_supported(a)) return launch_gemv(a, s);
+  if (gemm_mfma_supported(a)) return launch_gemm_mfma(a, s);
+  if (gemm_dot4_supported(a)) return launch_gemm_dot4(a, s);
+  return launch_linear_generic(a, s);
+}
+
+hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
+  if (deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
+  return launch_deconv_generic(a, s);
+}
+
+}  // namespace q8ta
+
+extern "C" {
+
+const char* q8ta_last_error(void) { return g_err; }
+
+q8ta_status q8ta_quantize_per_tensor(const float* x, int8_t* out, int64_t numel, double scale,
+                                     int64_t zero_point, hipStream_t stream) {
+  const char* op = "q8ta_quantize_per_tensor";
+  if (numel < 0 || numel > kMaxElems) return fail(Q8TA_ERR_SHAPE, "%s: numel out of range (%lld)", op, (long long)numel);
+  q8ta_status st = check_qparams(op, scale, zero_point);
+  if (st) return st;
+  if (numel == 0) return Q8TA_OK;
+  if (!x || !out) return fail(Q8TA_ERR_NULL, "%s: x and out must not be NULL", op);
+  return hip_status(launch_quantize(x, out, numel, recip(scale), (float)zero_point, stream), op);
+}
+
+q8ta_status q8ta_dequantize_per_tensor(const int8_t* x, float* out, int64_t numel, double scale,
+                                       int64_t zero_point, hipStream_t stream) {
+  const char* op = "q8ta_dequantize_per_tensor";
+  if (numel < 0 || numel > kMaxElems) return fail(Q8TA_ERR_SHAPE, "%s: numel out of range (%lld)", op, (long long)numel);
+  q8ta_status st = check_qparams(op, scale, zero_point);
+  if (st) return st;
+  if (numel == 0) return Q8TA_OK;
+  if (!x || !out) return fail(Q8TA_ERR_NULL, "%s: x and out must not be NULL", op);
+  return hip_status(launch_dequantize(x, out, numel, (float)scale, (int)zero_point, stream), op);
+}
+
+q8ta_status q8ta_linear(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                        int64_t input_zero_point, const int8_t* weight, int64_t N,
+                        const int32_t* weight_sums, const float* weight_scales, const float* bias,
+                        double output_scale, int64_t output_zero_point, const char* activation,
+                        int8_t* out, hipStream_t stream) {
+  (void)weight_sums;
+  return linear_impl("q8ta_linear", false, x, M, K, input_scale, input_zero_point, weight, N,
+                     weight_scales, bias, output_scale, output_zero_point, activation, out, stream);
+}
+
+q8ta_status q8ta_linear_gemv(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                             int64_t input_zero_point, const int8_t* weight, int64_t N,
+                             const int32_t* weight_sums, const float* weight_scales,
+                             const float* bias, double output_scale, int64_t output_zero_point,
+                             const char* activation, int8_t* out, hipStream_t stream) {
+  (void)weight_sums;
+  return linear_impl("q8ta_linear_gemv", true, x, M, K, input_scale, input_zero_point, weight, N,
+                     weight_scales, bias, output_scale, output_zero_point, activation, out, stream);
+}
+
+q8ta_status q8ta_linear_acc(const int8_t* x, int64_t M, int64_t K, int64_t input_zero_point,
+                            const int8_t* weight, int64_t N, int32_t* acc, hipStream_t stream) {
+  const char* op = "q8ta_linear_acc";
+  q8ta_status st = linear_checks(op, x, M, K, weight, N, acc);
+  if (st) return st;
+  if (!zp_ok(input_zero_point)) return fail(Q8TA_ERR_QPARAM, "%s: input_zero_point out of range", op);
+  LinearArgs a{};
+  a.x = x; a.w = weight; a.acc = acc; a.M = M; a.K = K; a.N = N;
+  a.izp = (int32_t)input_zero_point;
+  return hip_status(launch_linear(a, stream), op);
+}
+
+}  // extern "C"
+
+namespace {
+
+q8ta_status deconv_checks(const char* op, const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
+                          int64_t W_in, const int8_t* weight, int64_t OC, int64_t Kh, int64_t Kw,
+                          int64_t ldw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                          const void* out, int64_t H_out, int64_t W_out) {
+  if (!x || !weight || !out) return fail(Q8TA_ERR_NULL, "%s: x, weight and out must not be NULL", op);
+  if (N < 1 || IC < 1 || H_in < 1 || W_in < 1 || OC < 1 || Kh < 1 || Kw < 1 || H_out < 1 || W_out < 1)
+    return fail(Q8TA_ERR_SHAPE, "%s: all sizes must be >= 1", op);
+  const int64_t lim = (int64_t)1 << 24;
+  if (N > lim || IC > lim || H_in > lim || W_in > lim || OC > lim || Kh > 4096 || Kw > 4096 ||
+      H_out > lim || W_out > lim)
+    return fail(Q8TA_ERR_SHAPE, "%s: a size is too large", op);
+  if (Kh * Kw > kMaxElems / IC) return fail(Q8TA_ERR_SHAPE, "%s: Kh*Kw*IC too large", op);
+  if (ldw < Kh * Kw * IC)
+    return fail(Q8TA_ERR_SHAPE, "%s: weight_row_stride (%lld) must be >= Kh*Kw*IC (%lld)", op,
+                (long long)ldw, (long long)(Kh * Kw * IC));
+  if (sh < 1 || sw < 1 || sh > 4096 || sw > 4096) return fail(Q8TA_ERR_SHAPE, "%s: stride must be >= 1", op);
+  if (ph < 0 || pw < 0 || ph > lim || pw > lim) return fail(Q8TA_ERR_SHAPE, "%s: padding must be >= 0", op);
+  const double xe = (double)N * IC * H_in * W_in, oe = (double)N * OC * H_out * W_out,
+               we = (double)OC * ldw;
+  if (xe > (double)kMaxElems || oe > (double)kMaxElems || we > (double)kMaxElems)
+    return fail(Q8TA_ERR_SHAPE, "%s: tensors too large", op);
+  return Q8TA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, int64_t W_in,
+                                   double input_scale, int64_t input_zero_point, const int8_t* weight,
+                                   int64_t OC, int64_t Kh, int64_t Kw, int64_t weight_row_stride,
+                                   const int32_t* weight_sums, const float* weight_scales,
+                                   const float* bias, double output_scale, int64_t output_zero_point,
+                                   int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                                   int64_t output_padding_h, int64_t output_padding_w,
+                                   int64_t dilation_h, int64_t dilation_w, int64_t groups,
+                                   const char* activation, int8_t* out, int64_t H_out, int64_t W_out,
+                                   hipStream_t stream) {
+  const char* op = "q8ta_conv2d_transposed";
+  (void)weight_sums;
+  (void)output_padding_h;
+  (void)output_padding_w;
+  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
+                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out);
+  if (st) return st;
+  if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
+  if (dilation_h != 1 || dilation_w != 1)
+    return fail(Q8TA_ERR_UNSUPPORTED, "%s: dilation must be 1 (got %lld, %lld)", op,
+                (long long)dilation_h, (long long)dilation_w);
+  if (groups != 1) return fail(Q8TA_ERR_UNSUPPORTED, "%s: groups must be 1 (got %lld)", op, (long long)groups);
+  if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
+  if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
+  if ((st = check_activation(op, activation))) return st;
+
+  DeconvArgs a{};
+  a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
+  a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
+  a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
+  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  return hip_status(launch_deconv(a, stream), op);
+}
+
+q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
+                                       int64_t W_in, int64_t input_zero_point, const int8_t* weight,
+                                       int64_t OC, int64_t Kh, int64_t Kw, int64_t weight_row_stride,
+                                       int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                                       int32_t* acc, int64_t H_out, int64_t W_out, hipStream_t stream) {
+  const char* op = "q8ta_conv2d_transposed_acc";
+  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
+                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out);
+  if (st) return st;
+  if (!zp_ok(input_zero_point)) return fail(Q8TA_ERR_QPARAM, "%s: input_zero_point out of range", op);
+  DeconvArgs a{};
+  a.x = x; a.w = weight; a.acc = acc;
+  a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
+  a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
+  return hip_status(launch_deconv(a, stream), op);
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// q8ta_linear for M <= 4 rows of activations (q8ta_linear_gemv is M == 1):
+// a weight-streaming, HBM-bound kernel ("Add q8ta_linear op", Solution: the
+// M == 1 case of the same contraction and epilogue).
+//
+// Each wave owns ROWS consecutive weight rows.  In one pass over K the 64
+// lanes read CH consecutive 1 KiB slices of each row (lane l takes bytes
+// [16 l, 16 l + 16) of a slice), so every load instruction moves 1 KiB of
+// contiguous weight bytes; all ROWS*CH weight loads of a pass are issued
+// before any arithmetic, keeping ROWS*CH*1 KiB in flight per wave.  The
+// activation row(s) are small and stay in cache.  The dot products use the
+// packed int8 dot instruction (v_dot4): sum x*w and, against 0x01010101,
+// sum w; the zero-point term is folded as sum x*w - izp*sum w, then each
+// row's partial is reduced across the wave and requantized.
+#include <cstdlib>
+
+#include "q8ta_internal.h"
+
+namespace q8ta {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int MR, int ROWS, int CH>
+__global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t n0 = wave * ROWS;
+  if (n0 >= a.N) return;
+  const int64_t K = a.K;
+  int32_t dot[MR][ROWS];
+  int32_t sw[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    sw[r] = 0;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) dot[m][r] = 0;
+  }
+  for (int64_t k0 = 0; k0 < K; k0 += 1024 * CH) {
+    v4i wv[ROWS][CH];
+    v4i xv[MR][CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t kk = k0 + c * 1024 + lane * 16;
+      const bool ok = kk < K;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const bool rok = ok && (n0 + r < a.N);
+        wv[r][c] = rok ? __builtin_nontemporal_load(
+                             reinterpret_cast<const v4i*>(a.w + (n0 + r) * K + kk))
+                       : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        xv[m][c] = ok ? *reinterpret_cast<const v4i*>(a.x + m * K + kk) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          sw[r] = __builtin_amdgcn_sdot4(wv[r][c][d], 0x01010101, sw[r], false);
+#pragma unroll
+          for (int m = 0; m < MR; ++m)
+            dot[m][r] = __builtin_amdgcn_sdot4(xv[m][c][d], wv[r][c][d], dot[m][r], false);
+        }
+      }
+    }
+  }
+  int32_t mine = 0;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      int32_t t = wave_sum(dot[m][r] - a.izp * sw[r]);
+      if (lane == m * ROWS + r) mine = t;
+    }
+  }
+  if (lane < MR * ROWS) {
+    const int m = lane / ROWS, r = lane % ROWS;
+    const int64_t n = n0 + r;
+    if (n < a.N) {
+      if (a.acc) {
+        a.acc[m * a.N + n] = mine;
+      } else {
+        const float b = a.bias ? a.bias[n] : 0.0f;
+        a.out[m * a.N + n] = (int8_t)requant(mine, a.wscale[n], b, a.rq);
+      }
+    }
+  }
+}
+
+template <int MR, int ROWS>
+hipError_t launch_rows(const LinearArgs& a, hipStream_t s) {
+  const int64_t waves = (a.N + ROWS - 1) / ROWS;
+  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL((k_skinny<MR, ROWS, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MR>
+hipError_t launch_mr(const LinearArgs& a, hipStream_t s, int rows) {
+  switch (rows) {
+    case 1: return launch_rows<MR, 1>(a, s);
+    case 2: return launch_rows<MR, 2>(a, s);
+    default: return launch_rows<MR, 4>(a, s);
+  }
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+bool gemv_supported(const LinearArgs& a) {
+  return a.M >= 1 && a.M <= 4 && (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w);
+}
+
+// rows: weight rows per wave (Q8TA_GEMV_ROWS overrides the default of 2).
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) {
+  int rows = 2;
+  if (const char* e = getenv("Q8TA_GEMV_ROWS")) rows = atoi(e);
+  switch (a.M) {
+    case 1: return launch_mr<1>(a, s, rows);
+    case 2: return launch_mr<2>(a, s, rows);
+    case 3: return launch_mr<3>(a, s, rows);
+    default: return launch_mr<4>(a, s, rows);
+  }
+}
+
+}  // namespace q8ta

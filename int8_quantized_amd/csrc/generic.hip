@@ -1,0 +1,82 @@
+// Shape-general kernels: any sizes, any alignment.  They serve the shapes the
+// tiled kernels do not take (reduction lengths that are not a multiple of 16
+// bytes, unaligned pointers, tap sets that do not fit the staged tile) and
+// evaluate the definitions directly, one output element per thread.
+#include "q8ta_internal.h"
+
+namespace q8ta {
+namespace {
+
+constexpr int kThreads = 256;
+
+// "Add q8ta_linear op", Solution: acc = sum_k (x[m,k] - izp) * w[n,k].
+__global__ __launch_bounds__(kThreads) void k_linear_generic(LinearArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= a.M * a.N) return;
+  const int64_t m = idx / a.N, n = idx % a.N;
+  const int8_t* xr = a.x + m * a.K;
+  const int8_t* wr = a.w + n * a.K;
+  int32_t acc = 0;
+  for (int64_t k = 0; k < a.K; ++k) acc += ((int32_t)xr[k] - a.izp) * (int32_t)wr[k];
+  if (a.acc) {
+    a.acc[idx] = acc;
+  } else {
+    float b = a.bias ? a.bias[n] : 0.0f;
+    a.out[idx] = (int8_t)requant(acc, a.wscale[n], b, a.rq);
+  }
+}
+
+// "Add q8ta_conv2d_transposed op", Solution: the gather
+//   ih = (oh + pad_h - kh) / stride_h, used only when the numerator is >= 0,
+//   divisible and ih < H_in (iw likewise; dilation is 1).
+__global__ __launch_bounds__(kThreads) void k_deconv_generic(DeconvArgs a) {
+  const int64_t total = a.N * a.OC * a.H_out * a.W_out;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t ow = idx % a.W_out;
+  const int64_t oh = (idx / a.W_out) % a.H_out;
+  const int64_t oc = (idx / (a.W_out * a.H_out)) % a.OC;
+  const int64_t n = idx / (a.W_out * a.H_out * a.OC);
+  int32_t acc = 0;
+  for (int64_t kh = 0; kh < a.Kh; ++kh) {
+    const int64_t nh = oh + a.ph - kh;
+    if (nh < 0 || nh % a.sh != 0) continue;
+    const int64_t ih = nh / a.sh;
+    if (ih >= a.H_in) continue;
+    for (int64_t kw = 0; kw < a.Kw; ++kw) {
+      const int64_t nw = ow + a.pw - kw;
+      if (nw < 0 || nw % a.sw != 0) continue;
+      const int64_t iw = nw / a.sw;
+      if (iw >= a.W_in) continue;
+      const int8_t* xp = a.x + ((n * a.IC) * a.H_in + ih) * a.W_in + iw;
+      const int8_t* wp = a.w + oc * a.ldw + (kh * a.Kw + kw) * a.IC;
+      const int64_t plane = a.H_in * a.W_in;
+      for (int64_t ic = 0; ic < a.IC; ++ic)
+        acc += ((int32_t)xp[ic * plane] - a.izp) * (int32_t)wp[ic];
+    }
+  }
+  if (a.acc) {
+    a.acc[idx] = acc;
+  } else {
+    float b = a.bias ? a.bias[oc] : 0.0f;
+    a.out[idx] = (int8_t)requant(acc, a.wscale[oc], b, a.rq);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s) {
+  int64_t total = a.M * a.N;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_linear_generic, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s) {
+  int64_t total = a.N * a.OC * a.H_out * a.W_out;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_deconv_generic, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace q8ta

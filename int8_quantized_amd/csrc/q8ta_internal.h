@@ -1,0 +1,90 @@
+// Internal declarations shared by the libq8ta host code and its gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8ta {
+
+// Scalars of the dequant/requant epilogue, prepared on the host:
+// s_in = (float)input_scale, inv_out = (float)(1.0 / output_scale),
+// ozp = (float)output_zero_point.
+struct Requant {
+  float s_in;
+  float inv_out;
+  float ozp;
+};
+
+// The per-channel epilogue of q8ta_linear / q8ta_conv2d_transposed
+// ("Add q8ta_linear op" and "Add q8ta_conv2d_transposed op", Solution):
+// v = acc * input_scale * weight_scale + bias, then
+// q = clamp(round(v * inv_output_scale) + output_zero_point, -128, 127).
+// Evaluated left to right in float with one rounding per operation (every
+// source is built with -ffp-contract=off, so no multiply-add is fused);
+// rint rounds half to even.  A missing bias is passed as 0.0f, which gives
+// the same code as skipping the add.
+__device__ __forceinline__ int requant(int32_t acc, float wscale, float b, const Requant& r) {
+  float v = (float)acc;
+  v = v * r.s_in;
+  v = v * wscale;
+  v = v + b;
+  float t = v * r.inv_out;
+  float q = __builtin_rintf(t);
+  q = q + r.ozp;
+  q = __builtin_fmaxf(q, -128.0f);
+  q = __builtin_fminf(q, 127.0f);
+  return (int)q;
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+// ---- launchers (host functions; each returns hipGetLastError() after launch)
+hipError_t launch_quantize(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
+                           hipStream_t s);
+hipError_t launch_dequantize(const int8_t* x, float* out, int64_t numel, float scale, int zp,
+                             hipStream_t s);
+
+struct LinearArgs {
+  const int8_t* x;
+  const int8_t* w;
+  const float* wscale;
+  const float* bias;  // may be NULL
+  int8_t* out;        // int8 [M, N] (NULL when acc is set)
+  int32_t* acc;       // int32 [M, N] accumulator output (NULL for the int8 op)
+  int64_t M, K, N;
+  int32_t izp;
+  Requant rq;
+};
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
+
+struct DeconvArgs {
+  const int8_t* x;
+  const int8_t* w;
+  const float* wscale;
+  const float* bias;
+  int8_t* out;
+  int32_t* acc;
+  int64_t N, IC, H_in, W_in, OC, Kh, Kw, ldw;
+  int64_t sh, sw, ph, pw;
+  int64_t H_out, W_out;
+  int32_t izp;
+  Requant rq;
+};
+hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s);
+
+// Individual paths (used by the dispatchers above).
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
+bool gemv_supported(const LinearArgs& a);
+hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s);
+bool gemm_mfma_supported(const LinearArgs& a);
+hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s);
+bool gemm_dot4_supported(const LinearArgs& a);
+hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
+hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
+bool deconv_mfma_supported(const DeconvArgs& a);
+
+}  // namespace q8ta

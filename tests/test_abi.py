@@ -1,0 +1,187 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+the header declares, and rejects every invalid argument before any HIP call.
+
+No call here passes a complete set of valid arguments with fake pointers
+(that would launch a kernel on fake addresses on a GPU machine); the one test
+that launches is skipped wherever a GPU is present.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import int8_quantized_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8ta.h")
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8ta_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for n in ["q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor", "q8ta_linear",
+              "q8ta_linear_gemv", "q8ta_conv2d_transposed", "q8ta_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q8.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+        assert n in q8.SIGNATURES, n
+
+
+def test_exported_dynamic_symbols_with_nm():
+    out = subprocess.run(["nm", "-D", "--defined-only", q8.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = set(re.findall(r"\bT (q8ta_\w+)", out))
+    assert set(_declared()) <= syms
+
+
+def test_last_error_is_never_null():
+    assert isinstance(q8.q8ta_last_error(), str)
+
+
+def _st(rc, status, needle=None):
+    assert rc == status, (rc, q8.q8ta_last_error())
+    if needle:
+        assert needle in q8.q8ta_last_error()
+
+
+# ---------------------------------------------------------------- quantize / dequantize
+@pytest.mark.parametrize("fn", ["q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor"])
+def test_quant_errors(fn):
+    f = getattr(q8.lib(), fn)
+    _st(f(None, FAKE, 16, 0.02, 3, None), q8.Q8TA_ERR_NULL)
+    _st(f(FAKE, None, 16, 0.02, 3, None), q8.Q8TA_ERR_NULL)
+    _st(f(FAKE, FAKE, -1, 0.02, 3, None), q8.Q8TA_ERR_SHAPE)
+    _st(f(FAKE, FAKE, 16, 0.0, 3, None), q8.Q8TA_ERR_QPARAM)
+    _st(f(FAKE, FAKE, 16, -1.0, 3, None), q8.Q8TA_ERR_QPARAM)
+    _st(f(FAKE, FAKE, 16, float("nan"), 3, None), q8.Q8TA_ERR_QPARAM)
+    _st(f(FAKE, FAKE, 16, float("inf"), 3, None), q8.Q8TA_ERR_QPARAM)
+    _st(f(FAKE, FAKE, 16, 0.02, 128, None), q8.Q8TA_ERR_QPARAM)
+    _st(f(FAKE, FAKE, 16, 0.02, -129, None), q8.Q8TA_ERR_QPARAM)
+
+
+@pytest.mark.parametrize("fn", ["q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor"])
+def test_quant_empty_is_noop_without_launch(fn):
+    f = getattr(q8.lib(), fn)
+    assert f(None, None, 0, 0.02, 3, None) == q8.Q8TA_OK
+
+
+# ---------------------------------------------------------------- linear
+def _lin(fn="q8ta_linear", x=FAKE, M=4, K=64, s_in=0.02, izp=3, w=FAKE, N=32, ws=None,
+         scales=FAKE, bias=FAKE, s_out=0.27, ozp=-5, act=b"none", out=FAKE):
+    return getattr(q8.lib(), fn)(x, M, K, s_in, izp, w, N, ws, scales, bias, s_out, ozp, act, out,
+                                 None)
+
+
+@pytest.mark.parametrize("fn", ["q8ta_linear", "q8ta_linear_gemv"])
+def test_linear_errors(fn):
+    M = 1
+    _st(_lin(fn, x=None, M=M), q8.Q8TA_ERR_NULL)
+    _st(_lin(fn, w=None, M=M), q8.Q8TA_ERR_NULL)
+    _st(_lin(fn, out=None, M=M), q8.Q8TA_ERR_NULL)
+    _st(_lin(fn, scales=None, M=M), q8.Q8TA_ERR_NULL)
+    _st(_lin(fn, M=0), q8.Q8TA_ERR_SHAPE)
+    _st(_lin(fn, M=M, K=0), q8.Q8TA_ERR_SHAPE)
+    _st(_lin(fn, M=M, N=-3), q8.Q8TA_ERR_SHAPE)
+    _st(_lin(fn, M=M, s_in=0.0), q8.Q8TA_ERR_QPARAM)
+    _st(_lin(fn, M=M, s_out=float("inf")), q8.Q8TA_ERR_QPARAM)
+    _st(_lin(fn, M=M, izp=200), q8.Q8TA_ERR_QPARAM)
+    _st(_lin(fn, M=M, ozp=-129), q8.Q8TA_ERR_QPARAM)
+    _st(_lin(fn, M=M, act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED, "relu")
+    _st(_lin(fn, M=M, act=None), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(_lin(fn, M=M, act=b"None"), q8.Q8TA_ERR_UNSUPPORTED)
+
+
+def test_linear_gemv_requires_single_row():
+    _st(_lin("q8ta_linear_gemv", M=4), q8.Q8TA_ERR_SHAPE, "M must be 1")
+
+
+def test_linear_acc_errors():
+    f = q8.lib().q8ta_linear_acc
+    _st(f(None, 4, 64, 3, FAKE, 32, FAKE, None), q8.Q8TA_ERR_NULL)
+    _st(f(FAKE, 4, 64, 3, FAKE, 32, None, None), q8.Q8TA_ERR_NULL)
+    _st(f(FAKE, 4, 0, 3, FAKE, 32, FAKE, None), q8.Q8TA_ERR_SHAPE)
+    _st(f(FAKE, 4, 64, 300, FAKE, 32, FAKE, None), q8.Q8TA_ERR_QPARAM)
+
+
+# ---------------------------------------------------------------- conv2d_transposed
+DC = dict(x=FAKE, N=1, IC=64, H_in=32, W_in=32, s_in=0.02, izp=3, w=FAKE, OC=32, Kh=4, Kw=4,
+          ldw=1024, ws=None, scales=FAKE, bias=FAKE, s_out=0.54, ozp=-5, sh=2, sw=2, ph=1, pw=1,
+          oph=0, opw=0, dh=1, dw=1, groups=1, act=b"none", out=FAKE, H_out=64, W_out=64)
+
+
+def _dc(**kw):
+    a = dict(DC)
+    a.update(kw)
+    return q8.lib().q8ta_conv2d_transposed(
+        a["x"], a["N"], a["IC"], a["H_in"], a["W_in"], a["s_in"], a["izp"], a["w"], a["OC"],
+        a["Kh"], a["Kw"], a["ldw"], a["ws"], a["scales"], a["bias"], a["s_out"], a["ozp"],
+        a["sh"], a["sw"], a["ph"], a["pw"], a["oph"], a["opw"], a["dh"], a["dw"], a["groups"],
+        a["act"], a["out"], a["H_out"], a["W_out"], None)
+
+
+def test_deconv_errors():
+    _st(_dc(x=None), q8.Q8TA_ERR_NULL)
+    _st(_dc(w=None), q8.Q8TA_ERR_NULL)
+    _st(_dc(out=None), q8.Q8TA_ERR_NULL)
+    _st(_dc(scales=None), q8.Q8TA_ERR_NULL)
+    for k in ["N", "IC", "H_in", "W_in", "OC", "Kh", "Kw", "H_out", "W_out"]:
+        _st(_dc(**{k: 0}), q8.Q8TA_ERR_SHAPE)
+    _st(_dc(ldw=1023), q8.Q8TA_ERR_SHAPE, "weight_row_stride")
+    _st(_dc(sh=0), q8.Q8TA_ERR_SHAPE)
+    _st(_dc(sw=-1), q8.Q8TA_ERR_SHAPE)
+    _st(_dc(ph=-1), q8.Q8TA_ERR_SHAPE)
+    _st(_dc(dh=2), q8.Q8TA_ERR_UNSUPPORTED, "dilation")
+    _st(_dc(dw=0), q8.Q8TA_ERR_UNSUPPORTED, "dilation")
+    _st(_dc(groups=2), q8.Q8TA_ERR_UNSUPPORTED, "groups")
+    _st(_dc(act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(_dc(act=None), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(_dc(izp=128), q8.Q8TA_ERR_QPARAM)
+    _st(_dc(s_out=-0.5), q8.Q8TA_ERR_QPARAM)
+    _st(_dc(s_in=float("nan")), q8.Q8TA_ERR_QPARAM)
+
+
+def test_deconv_acc_errors():
+    f = q8.lib().q8ta_conv2d_transposed_acc
+    args = [FAKE, 1, 64, 32, 32, 3, FAKE, 32, 4, 4, 1024, 2, 2, 1, 1, FAKE, 64, 64, None]
+    a = list(args); a[0] = None
+    _st(f(*a), q8.Q8TA_ERR_NULL)
+    a = list(args); a[10] = 100
+    _st(f(*a), q8.Q8TA_ERR_SHAPE)
+    a = list(args); a[5] = -200
+    _st(f(*a), q8.Q8TA_ERR_QPARAM)
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="launches on fake pointers; only meaningful without a GPU")
+def test_valid_call_without_gpu_reports_hip_error():
+    rc = q8.lib().q8ta_quantize_per_tensor(FAKE, FAKE, 16, 0.02, 3, None)
+    assert rc == q8.Q8TA_ERR_HIP, q8.q8ta_last_error()
+    assert "HIP error" in q8.q8ta_last_error()
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(16, dtype=torch.float32)
+    out = torch.zeros(16, dtype=torch.int8)
+    with pytest.raises(ValueError, match="device tensor"):
+        q8.q8ta_quantize_per_tensor(x, out, 0.02, 3)

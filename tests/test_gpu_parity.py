@@ -1,0 +1,370 @@
+"""GPU parity: libq8ta's HIP kernels, called through the C ABI, against the CPU
+oracle on the same seeded inputs.  int8 outputs and int32 accumulators must be
+bit-exact (integer sums are order-free and the float epilogue is evaluated in
+the same operation order on both sides, without fused multiply-add).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import q8ta_inputs as qi
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import int8_quantized_amd as q8  # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+class env:
+    """Temporarily set an environment variable read by the library per call."""
+
+    def __init__(self, **kw):
+        self.kw = kw
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kw}
+        os.environ.update({k: str(v) for k, v in self.kw.items()})
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+# ============================================================================ quantize
+@pytest.mark.parametrize("numel", [1, 3, 4, 5, 255, 1024, 1027, 4096 + 13, 300001])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_quantize_ragged(numel, offset):
+    _say(f"quantize numel={numel} offset={offset}")
+    g = qi.rng(numel + offset)
+    x = (g.standard_normal(numel) * 3).astype(np.float32)
+    xb = torch.zeros(numel + offset, dtype=torch.float32, device="cuda")
+    xb[offset:] = dev(x)
+    ob = torch.zeros(numel + offset, dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_per_tensor(xb[offset:], ob[offset:], 0.02, 3)
+    np.testing.assert_array_equal(host(ob[offset:]), oracle.quantize_per_tensor(x, 0.02, 3))
+
+
+def test_quantize_ties_and_saturation():
+    import json
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quantize_hand.json")))["cases"]
+    for scale, zp, x, q in cases:
+        xs = torch.full((8,), float(x), dtype=torch.float32, device="cuda")
+        out = torch.empty(8, dtype=torch.int8, device="cuda")
+        q8.q8ta_quantize_per_tensor(xs, out, scale, zp)
+        assert (host(out) == q).all(), (scale, zp, x, q, host(out))
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.272, 2.176, 0.544, qi.out_scale_for(4096)])
+def test_quantize_scales(scale):
+    g = qi.rng(5)
+    x = np.concatenate([(g.standard_normal(100000) * 90 * scale).astype(np.float32),
+                        ((np.arange(-140, 141) + 0.5) * scale).astype(np.float32)])
+    out = torch.empty(x.size, dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_per_tensor(dev(x), out, scale, -5)
+    np.testing.assert_array_equal(host(out), oracle.quantize_per_tensor(x, scale, -5))
+
+
+def test_quantize_large_workload():
+    c = qi.make_deconv_large()
+    _say("quantize [8,256,64,64]")
+    out = torch.empty(c.x_fp32.shape, dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_per_tensor(dev(c.x_fp32), out, c.in_scale, c.in_zp)
+    np.testing.assert_array_equal(host(out), oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp))
+
+
+def test_quantize_empty():
+    x = torch.empty(0, dtype=torch.float32, device="cuda")
+    o = torch.empty(0, dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_per_tensor(x, o, 0.02, 3)
+
+
+# ============================================================================ dequantize
+@pytest.mark.parametrize("numel", [1, 7, 1024, 1029, 65536 + 3])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_dequantize_ragged(numel, offset):
+    _say(f"dequantize numel={numel} offset={offset}")
+    g = qi.rng(numel * 3 + offset)
+    q = qi.x_int8(g, numel)
+    qb = torch.zeros(numel + offset, dtype=torch.int8, device="cuda")
+    qb[offset:] = dev(q)
+    ob = torch.zeros(numel + offset, dtype=torch.float32, device="cuda")
+    q8.q8ta_dequantize_per_tensor(qb[offset:], ob[offset:], 0.272, -5)
+    np.testing.assert_array_equal(host(ob[offset:]), oracle.dequantize_per_tensor(q, 0.272, -5))
+
+
+# ============================================================================ linear
+def _run_linear(c, fn=None, bias=True):
+    fn = fn or q8.q8ta_linear
+    out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+    b = dev(c.bias) if (bias and c.bias is not None) else None
+    fn(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales), b, c.out_scale,
+       c.out_zp, "none", out)
+    return host(out)
+
+
+def _oracle_linear(c, bias=True):
+    return oracle.linear(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale, c.in_zp,
+                         c.out_scale, c.out_zp)
+
+
+def _acc_linear(c):
+    acc = torch.empty((c.M, c.N), dtype=torch.int32, device="cuda")
+    q8.q8ta_linear_acc(dev(c.x), c.in_zp, dev(c.w), acc)
+    return host(acc)
+
+
+MFMA_OFF = ("the matrix-core (MFMA + LDS) kernels are switched off: their first launch on MI355X "
+            "reported an illegal memory access whose cause has not been found")
+FAULTED_CASE = ("this exact case faulted the GPU under the switched-off matrix-core kernel; it stays "
+                "off the GPU until that cause is shown")
+
+LINEAR_SHAPES = [
+    # skinny / gemv path (M <= 4, K % 16 == 0)
+    (1, 4096, 4096), (1, 16, 1), (1, 1040, 37), (2, 1024, 100), (3, 48, 17), (4, 4096, 64),
+    (4, 64, 32),
+    # MFMA path: ragged M, N and K (K % 64 != 0)
+    pytest.param(5, 64, 32, marks=pytest.mark.skip(reason=FAULTED_CASE)), (65, 320, 97), (300, 1040, 257), (256, 4096, 512), (513, 256, 1000),
+    (129, 2064, 129),
+    # shape-general path (K % 16 != 0)
+    (7, 33, 5), (1, 100, 9), (40, 100, 70),
+]
+
+
+@pytest.mark.parametrize("M,K,N", LINEAR_SHAPES)
+def test_linear_parity(M, K, N):
+    _say(f"linear M={M} K={K} N={N}")
+    c = qi.linear_case(M * 7 + K * 3 + N, M, K, N)
+    np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+    np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+
+
+@pytest.mark.parametrize("izp", [-128, 127, 0])
+@pytest.mark.parametrize("M,K,N", [(1, 512, 64), (70, 512, 80)])
+def test_linear_zero_points_and_no_bias(M, K, N, izp):
+    _say(f"linear zp M={M} izp={izp}")
+    c = qi.linear_case(300 + izp, M, K, N, in_zp=izp, out_zp=127 if izp < 0 else -128)
+    np.testing.assert_array_equal(_run_linear(c, bias=False), _oracle_linear(c, bias=False))
+    np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+
+
+@pytest.mark.skip(reason=MFMA_OFF)
+@pytest.mark.parametrize("cfg", ["L", "M", "S"])
+@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
+def test_linear_every_gemm_tile(cfg, M, K, N):
+    _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
+    c = qi.linear_case(M + N + ord(cfg), M, K, N)
+    with env(Q8TA_GEMM_CFG=cfg):
+        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4])
+def test_gemv_rows_per_wave(rows):
+    c = qi.linear_case(77 + rows, 1, 2048, 1001)
+    with env(Q8TA_GEMV_ROWS=rows):
+        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+
+
+def test_linear_gemv_entry_and_gemm_row_identity():
+    """q8ta_linear_gemv is the M == 1 case: identical to q8ta_linear's row."""
+    c = qi.linear_case(91, 8, 1024, 96)
+    full = _run_linear(c)
+    for m in (0, 5, 7):
+        cm = qi.LinearCase(c.x[m:m + 1].copy(), c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                           c.out_scale, c.out_zp)
+        np.testing.assert_array_equal(_run_linear(cm, fn=q8.q8ta_linear_gemv)[0], full[m])
+
+
+def test_linear_gemv_rejects_m_gt_1():
+    c = qi.linear_case(92, 2, 64, 8)
+    with pytest.raises(q8.Q8taError, match="M must be 1"):
+        _run_linear(c, fn=q8.q8ta_linear_gemv)
+
+
+def test_linear_unaligned_pointers():
+    c = qi.linear_case(93, 33, 256, 40)
+    xb = torch.zeros(c.M * c.K + 1, dtype=torch.int8, device="cuda")
+    xb[1:] = dev(c.x.reshape(-1))
+    out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+    q8.q8ta_linear(xb[1:].view(c.M, c.K), c.in_scale, c.in_zp, dev(c.w), None,
+                   dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    np.testing.assert_array_equal(host(out), _oracle_linear(c))
+
+
+def test_chain_small_workload():
+    """quantize_per_tensor [4,64] -> q8ta_linear M=4 K=64 N=32."""
+    c = qi.make_chain_small()
+    xq = torch.empty((c.M, c.K), dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_per_tensor(dev(c.x_fp32), xq, c.in_scale, c.in_zp)
+    ref_xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    np.testing.assert_array_equal(host(xq), ref_xq)
+    out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+    q8.q8ta_linear(xq, c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales), dev(c.bias),
+                   c.out_scale, c.out_zp, "none", out)
+    ref = oracle.linear(ref_xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                        c.out_zp)
+    np.testing.assert_array_equal(host(out), ref)
+
+
+def test_gemv_workload():
+    c = qi.make_gemv()
+    _say("gemv 1x4096x4096")
+    np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+    np.testing.assert_array_equal(_run_linear(c, fn=q8.q8ta_linear_gemv), _oracle_linear(c))
+    np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+
+
+def test_gemm_workload_sampled_rows_and_dequantize():
+    """GEMM M=2048 K=4096 N=11008 in the benchmark's launch configuration:
+    every output of 40 sampled rows (first, last and spread) is compared with
+    the oracle; the dequantize of the whole int8 output is compared in full."""
+    c = qi.make_gemm()
+    _say("gemm 2048x4096x11008")
+    out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+    q8.q8ta_linear(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                   dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    y = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    q8.q8ta_dequantize_per_tensor(out, y, c.out_scale, c.out_zp)
+    got = host(out)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 1023, 2046, 2047],
+                                     qi.rng(3).integers(0, c.M, 33)]))
+    ref = oracle.linear(c.x[rows], c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                        c.out_zp)
+    np.testing.assert_array_equal(got[rows], ref)
+    np.testing.assert_array_equal(host(y), oracle.dequantize_per_tensor(got, c.out_scale, c.out_zp))
+    # the output scale keeps the codes mostly unsaturated
+    assert (np.abs(got.astype(int)) < 127).mean() > 0.9
+
+
+# ============================================================================ conv2d_transposed
+def _run_deconv(c, bias=True):
+    out = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+    b = dev(c.bias) if (bias and c.bias is not None) else None
+    q8.q8ta_conv2d_transposed(dev(c.x), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
+                              dev(c.weight_scales), b, c.out_scale, c.out_zp, c.stride, c.padding,
+                              c.output_padding, (1, 1), 1, "none", out)
+    return host(out)
+
+
+def _acc_deconv(c):
+    acc = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int32, device="cuda")
+    q8.q8ta_conv2d_transposed_acc(dev(c.x), c.in_zp, dev(c.w), c.Kh, c.Kw, c.stride, c.padding, acc)
+    return host(acc)
+
+
+def _oracle_deconv(c, bias=True):
+    return oracle.conv2d_transposed(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale,
+                                    c.in_zp, c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding,
+                                    (1, 1), c.H_out, c.W_out)
+
+
+def _oracle_deconv_acc(c):
+    return oracle.deconv_acc(c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, (1, 1), c.H_out,
+                             c.W_out)
+
+
+DECONV_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, H_out, W_out, ldw_extra
+    (1, 64, 32, 32, 32, 4, 4, (2, 2), (1, 1), (0, 0), None, None, 0),      # small workload shape
+    (2, 32, 9, 12, 48, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 0),
+    (1, 16, 5, 8, 20, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 32),       # padded weight rows
+    (1, 48, 7, 6, 17, 4, 3, (2, 3), (1, 0), (0, 2), None, None, 0),        # mixed strides
+    (1, 16, 6, 8, 16, 1, 1, (1, 1), (0, 0), (0, 0), None, None, 0),        # 1x1, stride 1
+    (1, 32, 4, 8, 16, 5, 5, (3, 3), (2, 2), (1, 1), None, None, 0),        # stride 3
+    (1, 16, 4, 4, 16, 2, 2, (4, 4), (0, 0), (0, 0), None, None, 0),        # phases with no taps
+    (1, 64, 5, 20, 70, 3, 3, (2, 2), (4, 4), (0, 0), None, None, 0),       # pad > K
+    (2, 32, 6, 7, 24, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 0),        # W_in % 4 != 0
+    (1, 32, 8, 8, 32, 3, 3, (2, 2), (1, 1), (1, 1), 21, 9, 0),             # explicit H_out/W_out
+    (1, 32, 8, 8, 32, 3, 3, (2, 2), (1, 1), (1, 1), 3, 40, 0),
+    (1, 128, 16, 80, 96, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 0),     # several column tiles
+    (1, 80, 6, 8, 40, 2, 2, (2, 2), (0, 0), (0, 0), None, None, 0),        # IC not a multiple of 64
+    (1, 320, 3, 4, 24, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 0),
+    (1, 24, 5, 6, 8, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 0),         # IC % 16 != 0 (general)
+    (1, 16, 4, 4, 8, 3, 3, (5, 5), (1, 1), (0, 0), None, None, 0),         # stride 5 (general)
+]
+
+
+@pytest.mark.parametrize("case", DECONV_CASES, ids=[str(i) for i in range(len(DECONV_CASES))])
+def test_deconv_parity(case):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
+    _say(f"deconv case={case}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw]), N, IC, H, W, OC, Kh, Kw, s, p, op,
+                       H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra)
+    np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+    np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
+@pytest.mark.skip(reason=MFMA_OFF)
+@pytest.mark.parametrize("fj,fo,wi", [(1, 1, 1), (2, 4, 2), (4, 2, 1), (4, 4, 4), (1, 4, 3)])
+def test_deconv_every_tile(fj, fo, wi):
+    _say(f"deconv tile FJ={fj} FO={fo} WI={wi}")
+    c = qi.deconv_case(500 + fj * 10 + fo, 2, 64, 10, 36, 72, 3, 3, (2, 2), (1, 1), (1, 1))
+    with env(Q8TA_DECONV_FJ=fj, Q8TA_DECONV_FO=fo, Q8TA_DECONV_WI=wi):
+        np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+        np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
+@pytest.mark.parametrize("izp", [-128, 127])
+def test_deconv_zero_points_and_no_bias(izp):
+    c = qi.deconv_case(600 + izp, 1, 32, 8, 8, 24, 3, 3, (2, 2), (1, 1), (1, 1), in_zp=izp)
+    np.testing.assert_array_equal(_run_deconv(c, bias=False), _oracle_deconv(c, bias=False))
+    np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+
+
+def test_deconv_small_workload():
+    c = qi.make_deconv_small()
+    _say("deconv [1,64,32,32] -> [1,32,64,64]")
+    np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+
+
+def test_deconv_large_workload_sampled():
+    """quantize [8,256,64,64] -> deconv -> [8,128,128,128] in the benchmark's
+    launch configuration; the oracle recomputes images 0 and 7 for 24 output
+    channels (first, last and spread)."""
+    c = qi.make_deconv_large()
+    _say("quantize + deconv [8,256,64,64] -> [8,128,128,128]")
+    xq = torch.empty(c.x_fp32.shape, dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_per_tensor(dev(c.x_fp32), xq, c.in_scale, c.in_zp)
+    out = torch.empty((8, 128, 128, 128), dtype=torch.int8, device="cuda")
+    q8.q8ta_conv2d_transposed(xq, c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
+                              dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, c.stride,
+                              c.padding, c.output_padding, (1, 1), 1, "none", out)
+    got = host(out)
+    xq_ref = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    np.testing.assert_array_equal(host(xq), xq_ref)
+    ocs = np.unique(np.concatenate([[0, 1, 63, 64, 127], qi.rng(4).integers(0, 128, 19)]))
+    for n in (0, 7):
+        ref = oracle.conv2d_transposed(xq_ref[n:n + 1], c.w[ocs], c.weight_scales[ocs],
+                                       c.bias[ocs], c.in_scale, c.in_zp, c.out_scale, c.out_zp,
+                                       c.Kh, c.Kw, c.stride, c.padding, (1, 1), c.H_out, c.W_out)
+        np.testing.assert_array_equal(got[n][ocs], ref[0])
+    assert (np.abs(got.astype(int)) < 127).mean() > 0.9
