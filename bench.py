@@ -89,9 +89,11 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def time_calls(self, fns, reps, budget_s=4.0):
-        """Time up to `reps` calls (cycling through `fns`), fewer when one call
-        is slow, so that the loop stays within about `budget_s` seconds."""
+    def time_calls(self, fns, reps, budget_s=4.0, batches=5):
+        """Average duration (ms) of back-to-back launches, cycling through
+        `fns`: each of `batches` batches of `reps` launches is bracketed by two
+        events; fewer launches when one call is slow, to stay within about
+        `budget_s` seconds.  Returns the per-launch average of every batch."""
         torch = self.torch
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -99,15 +101,16 @@ class Timer:
         e1.record()
         torch.cuda.synchronize()
         one = max(e0.elapsed_time(e1) / 1e3, 1e-6)
-        reps = int(max(3, min(reps, budget_s / one)))
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for i in range(reps):
-            ev[i][0].record()
-            fns[i % len(fns)]()
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in ev]   # ms
+        reps = int(max(1, min(reps, budget_s / batches / one)))
+        out = []
+        for _ in range(batches):
+            e0.record()
+            for i in range(reps):
+                fns[i % len(fns)]()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / reps)
+        return out
 
 
 def main():
@@ -247,7 +250,7 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     def summary(ms, work, unit, peak):
         med = statistics.median(ms) / 1e3
         rate = work / med / (1e9 if unit == "GB/s" else 1e12)
-        d = {"median_us": round(med * 1e6, 2), "min_us": round(min(ms) * 1e3, 2),
+        d = {"avg_launch_us": round(med * 1e6, 2), "best_batch_us": round(min(ms) * 1e3, 2),
              "rate": round(rate, 2), "unit": unit}
         if peak:
             d["frac"] = round(rate / peak, 4)
