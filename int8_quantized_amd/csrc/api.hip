@@ -95,6 +95,7 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
 
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
   if (deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
+  if (deconv_dot4_supported(a)) return launch_deconv_dot4(a, s);
   return launch_deconv_generic(a, s);
 }
 

@@ -1,0 +1,221 @@
+// q8ta_conv2d_transposed on the vector ALU ("Add q8ta_conv2d_transposed op",
+// Solution: acc[n,oc,oh,ow] = sum over (ic, kh, kw) of (x[n,ic,ih,iw] - izp) *
+// w[oc, (kh*Kw + kw)*IC + ic], with ih = (oh + pad_h - kh) / stride_h used only
+// when the numerator is >= 0, divisible and ih < H_in; iw likewise).
+//
+// Stride phases: which taps qualify depends only on rh = oh mod s_h and
+// rw = ow mod s_w.  For oh = rh + s_h*i a qualifying tap kh reads row
+// ih = i + dh with dh = (rh + pad_h - kh) / s_h (exact), and likewise for
+// columns, so a fixed (rh, rw) is a dense stride-1 correlation with its own
+// sub-kernel and no product with a non-qualifying tap is ever formed.
+//
+// A wave owns one output row oh of one image, one column residue rw, 64 phase
+// columns j (one per lane: ow = rw + s_w*j) and OCB output channels; all its
+// lanes share the same taps.  Per tap and 16 input channels a lane loads the 16
+// bytes x[n, ic..ic+15, ih, iw] (each load instruction reads 64 consecutive
+// columns of one channel plane), packs them into 4 dwords, and accumulates
+// v_dot4 against the weights w[oc, tap, ic..ic+15], which are the same for all
+// lanes and come through the scalar unit.  A tap that falls outside the input
+// reads the zero point, so with sum w taken over all of the phase's taps the
+// result sum x*w - izp * sum w equals the gather (the zero-point-filled form of
+// the page's Constraints (1)).  sum w per output channel is formed once per
+// wave, the lanes splitting the (tap, channel) range, then reduced across the
+// wave.  The epilogue requantizes in registers and stores bytes.
+#include <cstdlib>
+
+#include "q8ta_internal.h"
+
+namespace q8ta {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Weights are only read by these kernels: reading them through the constant
+// address space lets the compiler fetch wave-uniform words with scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* cwptr;
+
+constexpr int kMaxS = 8;    // largest stride taken
+constexpr int kMaxT = 16;   // largest number of taps per residue
+
+struct Phases {
+  int nth[kMaxS], thk[kMaxS][kMaxT], thd[kMaxS][kMaxT];
+  int ntw[kMaxS], twk[kMaxS][kMaxT], twd[kMaxS][kMaxT];
+  int jb;     // blocks of 64 phase columns
+  int ocb;    // blocks of OCB output channels
+};
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int OCB>
+__global__ __launch_bounds__(kThreads) void k_deconv_dot4(DeconvArgs a, Phases p) {
+  const int lane = threadIdx.x & 63;
+  // wave index, made explicitly wave-uniform so that everything derived from
+  // it (taps, weight addresses) lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  const int ob = (int)(wid % p.ocb);  wid /= p.ocb;
+  const int jb = (int)(wid % p.jb);   wid /= p.jb;
+  const int sw = (int)a.sw, sh = (int)a.sh;
+  const int rw = (int)(wid % sw);     wid /= sw;
+  const int oh = (int)(wid % a.H_out);
+  const int64_t n = wid / a.H_out;
+  if (n >= a.N) return;
+  const int rh = oh % sh, i = oh / sh;
+  const int j = jb * 64 + lane;
+  const int ow = rw + sw * j;
+  const int oc0 = ob * OCB;
+  const int IC = (int)a.IC, H_in = (int)a.H_in, W_in = (int)a.W_in;
+  const int64_t plane = (int64_t)H_in * W_in;
+  const int8_t* xn = a.x + n * IC * plane;
+  const uint32_t zp4 = 0x01010101u * ((uint32_t)a.izp & 0xffu);
+  const int nth = p.nth[rh], ntw = p.ntw[rw];
+
+  // sum of the phase's weights per output channel (lanes split the channels)
+  int32_t wsum[OCB];
+#pragma unroll
+  for (int o = 0; o < OCB; ++o) wsum[o] = 0;
+  for (int th = 0; th < nth; ++th) {
+    for (int tw = 0; tw < ntw; ++tw) {
+      const int64_t tapoff = (int64_t)(p.thk[rh][th] * a.Kw + p.twk[rw][tw]) * IC;
+      for (int ic = lane * 4; ic < IC; ic += 256) {
+#pragma unroll
+        for (int o = 0; o < OCB; ++o) {
+          const int oc = oc0 + o;
+          const int32_t wv = oc < a.OC
+              ? *reinterpret_cast<const int32_t*>(a.w + (int64_t)oc * a.ldw + tapoff + ic) : 0;
+          wsum[o] = __builtin_amdgcn_sdot4(wv, 0x01010101, wsum[o], false);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 0; o < OCB; ++o) wsum[o] = wave_sum(wsum[o]);
+
+  int32_t acc[OCB];
+#pragma unroll
+  for (int o = 0; o < OCB; ++o) acc[o] = 0;
+  for (int th = 0; th < nth; ++th) {
+    const int kh = p.thk[rh][th];
+    const int ih = i + p.thd[rh][th];
+    const bool row_ok = ih >= 0 && ih < H_in;
+    for (int tw = 0; tw < ntw; ++tw) {
+      const int kw = p.twk[rw][tw];
+      const int iw = j + p.twd[rw][tw];
+      const bool ok = row_ok && iw >= 0 && iw < W_in;
+      const int8_t* xp = xn + (int64_t)(ok ? ih : 0) * W_in + (ok ? iw : 0);
+      const int8_t* wt = a.w + (int64_t)oc0 * a.ldw + (int64_t)(kh * a.Kw + kw) * IC;
+      const int64_t ldw4 = a.ldw / 4;
+      for (int ic = 0; ic < IC; ic += 16) {
+        uint32_t xv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int c = ic + 4 * g + t;
+            const uint32_t by = (c < IC) ? (uint32_t)(uint8_t)xp[(int64_t)c * plane] : 0u;
+            v |= by << (8 * t);
+          }
+          xv[g] = ok ? v : zp4;
+        }
+        const cwptr wc = (cwptr)(wt + ic);
+#pragma unroll
+        for (int o = 0; o < OCB; ++o) {
+          if (oc0 + o < a.OC) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int32_t wv = (ic + 4 * g < IC) ? wc[o * ldw4 + g] : 0;
+              acc[o] = __builtin_amdgcn_sdot4((int)xv[g], wv, acc[o], false);
+            }
+          }
+        }
+      }
+    }
+  }
+  if (ow >= a.W_out) return;
+#pragma unroll
+  for (int o = 0; o < OCB; ++o) {
+    const int oc = oc0 + o;
+    if (oc >= a.OC) break;
+    const int32_t c = acc[o] - a.izp * wsum[o];
+    const int64_t idx = (((int64_t)n * a.OC + oc) * a.H_out + oh) * a.W_out + ow;
+    if (a.acc) {
+      a.acc[idx] = c;
+    } else {
+      const float b = a.bias ? a.bias[oc] : 0.0f;
+      a.out[idx] = (int8_t)requant(c, a.wscale[oc], b, a.rq);
+    }
+  }
+}
+
+int floordiv(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
+
+bool make_phases(const DeconvArgs& a, Phases& p) {
+  if (a.sh > kMaxS || a.sw > kMaxS || a.ph > (1 << 20) || a.pw > (1 << 20)) return false;
+  p = Phases{};
+  for (int r = 0; r < (int)a.sh; ++r) {
+    int cnt = 0;
+    for (int k = 0; k < (int)a.Kh; ++k) {
+      const int num = r + (int)a.ph - k;
+      if (((num % (int)a.sh) + (int)a.sh) % (int)a.sh != 0) continue;
+      if (cnt >= kMaxT) return false;
+      p.thk[r][cnt] = k;
+      p.thd[r][cnt] = floordiv(num, (int)a.sh);
+      ++cnt;
+    }
+    p.nth[r] = cnt;
+  }
+  for (int r = 0; r < (int)a.sw; ++r) {
+    int cnt = 0;
+    for (int k = 0; k < (int)a.Kw; ++k) {
+      const int num = r + (int)a.pw - k;
+      if (((num % (int)a.sw) + (int)a.sw) % (int)a.sw != 0) continue;
+      if (cnt >= kMaxT) return false;
+      p.twk[r][cnt] = k;
+      p.twd[r][cnt] = floordiv(num, (int)a.sw);
+      ++cnt;
+    }
+    p.ntw[r] = cnt;
+  }
+  const int64_t Wp = (a.W_out + a.sw - 1) / a.sw;
+  p.jb = (int)((Wp + 63) / 64);
+  return true;
+}
+
+template <int OCB>
+hipError_t launch_t(const DeconvArgs& a, Phases p, hipStream_t s) {
+  p.ocb = (int)((a.OC + OCB - 1) / OCB);
+  const int64_t waves = (int64_t)p.ocb * p.jb * a.sw * a.H_out * a.N;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((k_deconv_dot4<OCB>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool deconv_dot4_supported(const DeconvArgs& a) {
+  Phases p;
+  if (a.IC % 4 != 0 || a.ldw % 4 != 0 || ((uintptr_t)a.w & 3) != 0) return false;
+  if (a.H_out > (1 << 24) || a.W_out > (1 << 24) || a.H_in > (1 << 24) || a.W_in > (1 << 24) ||
+      a.IC > (1 << 24) || a.OC > (1 << 24))
+    return false;
+  if (!make_phases(a, p)) return false;
+  const int64_t waves = ((a.OC + 7) / 8) * (int64_t)p.jb * a.sw * a.H_out * a.N;
+  return (waves + 3) / 4 < ((int64_t)1 << 31);
+}
+
+// Output channels per wave: 16 (Q8TA_DECONV_OCB = 8 | 16 overrides).
+hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s) {
+  Phases p;
+  if (!make_phases(a, p)) return hipErrorInvalidValue;
+  int ocb = 16;
+  if (const char* e = getenv("Q8TA_DECONV_OCB")) ocb = atoi(e);
+  if (ocb == 8) return launch_t<8>(a, p, s);
+  return launch_t<16>(a, p, s);
+}
+
+}  // namespace q8ta

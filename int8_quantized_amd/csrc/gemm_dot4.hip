@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
   static_assert(RN * RM == 64, "one tile element per lane after the reduction");
   constexpr int64_t SL = 256 * LW;  // bytes of one row covered by one slice
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   // block -> (block-row bm_i along M, block-column bn_i along N), grouped:
   // `group` block-rows are walked together before moving to the next columns.
   const int64_t BM = (tiles_m + 1) / 2, BN = (tiles_n + 1) / 2;

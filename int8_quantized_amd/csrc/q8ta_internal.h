@@ -86,5 +86,7 @@ bool gemm_dot4_supported(const LinearArgs& a);
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);
+hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s);
+bool deconv_dot4_supported(const DeconvArgs& a);
 
 }  // namespace q8ta

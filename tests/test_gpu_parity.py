@@ -187,6 +187,16 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
 
 
+@pytest.mark.parametrize("cfg", ["4S:32", "4S:1", "2S:8", "2P:8", "2P:3"])
+@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (17, 4096, 40), (512, 2048, 768)])
+def test_linear_every_dot4_variant(cfg, M, K, N):
+    _say(f"dot4 gemm cfg={cfg} M={M} K={K} N={N}")
+    c = qi.linear_case(M + N + len(cfg), M, K, N)
+    with env(Q8TA_DOT4_CFG=cfg):
+        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+
+
 @pytest.mark.parametrize("rows", [1, 2, 4])
 def test_gemv_rows_per_wave(rows):
     c = qi.linear_case(77 + rows, 1, 2048, 1001)
@@ -329,6 +339,19 @@ def test_deconv_every_tile(fj, fo, wi):
     _say(f"deconv tile FJ={fj} FO={fo} WI={wi}")
     c = qi.deconv_case(500 + fj * 10 + fo, 2, 64, 10, 36, 72, 3, 3, (2, 2), (1, 1), (1, 1))
     with env(Q8TA_DECONV_FJ=fj, Q8TA_DECONV_FO=fo, Q8TA_DECONV_WI=wi):
+        np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+        np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
+@pytest.mark.parametrize("ocb", [8, 16])
+@pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_CASES[6], DECONV_CASES[11]],
+                         ids=["k3s2", "mixed_strides", "empty_phases", "wide"])
+def test_deconv_every_dot4_variant(ocb, case):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
+    _say(f"deconv dot4 ocb={ocb} case={case}")
+    c = qi.deconv_case(7 + ocb, N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho, W_out=Wo,
+                       ldw=Kh * Kw * IC + extra)
+    with env(Q8TA_DECONV_OCB=ocb):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
