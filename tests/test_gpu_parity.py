@@ -343,15 +343,18 @@ def test_deconv_every_tile(fj, fo, wi):
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
-@pytest.mark.parametrize("ocb", [8, 16])
-@pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_CASES[6], DECONV_CASES[11]],
-                         ids=["k3s2", "mixed_strides", "empty_phases", "wide"])
-def test_deconv_every_dot4_variant(ocb, case):
+@pytest.mark.parametrize("variant", ["blocked:8:1", "blocked:16:1", "nchw:8:1", "nchw:8:2",
+                                     "nchw:8:4", "nchw:16:1", "nchw:16:2"])
+@pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_CASES[6], DECONV_CASES[11],
+                                  DECONV_CASES[13]],
+                         ids=["k3s2", "mixed_strides", "empty_phases", "wide", "ic320"])
+def test_deconv_every_dot4_variant(variant, case):
+    layout, ocb, rq = variant.split(":")
     N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
-    _say(f"deconv dot4 ocb={ocb} case={case}")
-    c = qi.deconv_case(7 + ocb, N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho, W_out=Wo,
-                       ldw=Kh * Kw * IC + extra)
-    with env(Q8TA_DECONV_OCB=ocb):
+    _say(f"deconv dot4 variant={variant} case={case}")
+    c = qi.deconv_case(7 + int(ocb) + int(rq), N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho,
+                       W_out=Wo, ldw=Kh * Kw * IC + extra)
+    with env(Q8TA_DECONV_LAYOUT=layout, Q8TA_DECONV_OCB=ocb, Q8TA_DECONV_RQ=rq):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
