@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--profile-only", choices=["gemm-and-copy"], default=None,
+                    help="for hardware-counter runs: launch the GEMM `--steps` times and the "
+                         "256 MiB calibration copy 3 times, print nothing else")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -168,6 +171,14 @@ def main():
     def deq():
         check(lib.q8ta_dequantize_per_tensor(out.data_ptr(), y.data_ptr(), M * N, c.out_scale,
                                              c.out_zp, stream))
+
+    if args.profile_only == "gemm-and-copy":
+        for _ in range(args.steps):
+            gemm()
+        torch.cuda.synchronize()
+        profile_copy(torch, stream)
+        log(f"profiled {args.steps} GEMM launches and 3 copies of 256 MiB")
+        return
 
     for _ in range(args.warmup):
         gemm()
@@ -230,6 +241,8 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = run_extra(torch, np, q8, qi, lib, stream, timer, check)
+        extra["ceilings"] = run_ceilings(torch, stream, timer)
+        log(f"  ceilings: {extra['ceilings']}")
 
     line = {
         "metric": METRIC, "value": round(ops / step_s / 1e12, 2), "unit": "TOPS",
@@ -241,6 +254,45 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def profile_copy(torch, stream):
+    """Three launches of the 16-byte calibration copy over 256 MiB (reads and
+    writes 268,435,456 bytes each): the reference for scaling HBM counters."""
+    cl = ctypes.CDLL(os.path.join(ROOT, "int8_quantized_amd", "libq8ta_calib.so"))
+    cl.q8ta_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    n = 256 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        cl.q8ta_calib_copy(src.data_ptr(), dst.data_ptr(), n // 16, 256 * 8, stream)
+    torch.cuda.synchronize()
+
+
+def run_ceilings(torch, stream, timer):
+    """Achieved ceilings on this GPU: a register-only v_dot4 loop and a plain
+    16-byte copy (libq8ta_calib.so), next to the published peaks."""
+    path = os.path.join(ROOT, "int8_quantized_amd", "libq8ta_calib.so")
+    if not os.path.exists(path):
+        return None
+    cl = ctypes.CDLL(path)
+    cl.q8ta_calib_dot4.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cl.q8ta_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    blocks, iters = 256 * 16, 1024
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    ms = timer.time_calls([lambda: cl.q8ta_calib_dot4(out.data_ptr(), blocks, iters, stream)], 3,
+                          batches=3)
+    dot4_tops = blocks * 256 * iters * 16 * 8 / (min(ms) / 1e3) / 1e12
+    n = 256 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ms = timer.time_calls([lambda: cl.q8ta_calib_copy(src.data_ptr(), dst.data_ptr(), n // 16,
+                                                      256 * 8, stream)], 10, batches=3)
+    copy_gbs = 2 * n / (min(ms) / 1e3) / 1e9
+    return {"dot4_loop_tops": round(dot4_tops, 1), "dot4_peak_tops_derived": round(PEAK_DOT4_TOPS, 1),
+            "copy_256MiB_gbs": round(copy_gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS}
 
 
 def run_extra(torch, np, q8, qi, lib, stream, timer, check):

@@ -21,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq8ta.so")
+CALIB_SRC = os.path.join(PKG, "calib", "calib.hip")
+CALIB_LIB = os.path.join(PKG, "libq8ta_calib.so")
 ARCH = "gfx950"
 
 
@@ -60,8 +62,15 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # calibration kernels used by the benchmark (not part of libq8ta)
+    tmp = CALIB_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + CFLAGS + extra + ["-shared", "-o", tmp, CALIB_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CALIB_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void k_nchw_to_blocked16(const int8_t* __
 // together through the scalar unit, and the next group's activations are
 // loaded while the current one is multiplied.  ICF: IC is a multiple of 16,
 // so no weight needs masking.
-template <int OCB, bool ICF>
+template <int OCB, bool ICF, int RQ>
 __global__ __launch_bounds__(kThreads) void k_deconv_dot4_blocked(DeconvArgs a, Phases p,
                                                                  const int8_t* __restrict__ xb) {
   typedef int v4i __attribute__((ext_vector_type(4)));
@@ -228,10 +228,11 @@ __global__ __launch_bounds__(kThreads) void k_deconv_dot4_blocked(DeconvArgs a, 
   const int jb = (int)(wid % p.jb);   wid /= p.jb;
   const int sw = (int)a.sw, sh = (int)a.sh;
   const int rw = (int)(wid % sw);     wid /= sw;
-  const int oh = (int)(wid % a.H_out);
-  const int64_t n = wid / a.H_out;
+  const int ib = (int)(wid % p.ib);   wid /= p.ib;
+  const int rh = (int)(wid % sh);     wid /= sh;
+  const int64_t n = wid;
   if (n >= a.N) return;
-  const int rh = oh % sh, i = oh / sh;
+  const int i0 = ib * RQ;               // phase rows i0 .. i0+RQ-1: output rows rh + sh*i
   const int j = jb * 64 + lane;
   const int ow = rw + sw * j;
   const int oc0 = ob * OCB;
@@ -265,23 +266,38 @@ __global__ __launch_bounds__(kThreads) void k_deconv_dot4_blocked(DeconvArgs a, 
 #pragma unroll
   for (int o = 0; o < OCB; ++o) wsum[o] = wave_sum(wsum[o]);
 
-  int32_t acc[OCB];
+  int32_t acc[RQ][OCB];
 #pragma unroll
-  for (int o = 0; o < OCB; ++o) acc[o] = 0;
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int o = 0; o < OCB; ++o) acc[q][o] = 0;
+  const int64_t gstride = (int64_t)W_in * 16;  // bytes between channel groups of a pixel row
   for (int th = 0; th < nth; ++th) {
     const int kh = p.thk[rh][th];
-    const int ih = i + p.thd[rh][th];
-    const bool row_ok = ih >= 0 && ih < H_in;
+    const int dh = p.thd[rh][th];
     for (int tw = 0; tw < ntw; ++tw) {
       const int kw = p.twk[rw][tw];
       const int iw = j + p.twd[rw][tw];
-      const bool ok = row_ok && iw >= 0 && iw < W_in;
-      const int8_t* xp = xb + (((n * H_in + (ok ? ih : 0)) * G) * (int64_t)W_in + (ok ? iw : 0)) * 16;
+      const bool col_ok = iw >= 0 && iw < W_in;
+      const int8_t* xp[RQ];
+      bool ok[RQ];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        const int ih = i0 + q + dh;
+        ok[q] = col_ok && ih >= 0 && ih < H_in;
+        xp[q] = xb + (((n * H_in + (ok[q] ? ih : 0)) * G) * (int64_t)W_in + (ok[q] ? iw : 0)) * 16;
+      }
       const cwptr wt = (cwptr)(a.w + (int64_t)(kh * a.Kw + kw) * IC);
-      v4i xn = *reinterpret_cast<const v4i*>(xp);
+      v4i xn[RQ];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) xn[q] = *reinterpret_cast<const v4i*>(xp[q]);
       for (int g = 0; g < G; ++g) {
-        v4i xv = xn;
-        if (g + 1 < G) xn = *reinterpret_cast<const v4i*>(xp + (int64_t)(g + 1) * W_in * 16);
+        v4i xv[RQ];
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) {
+          xv[q] = xn[q];
+          if (g + 1 < G) xn[q] = *reinterpret_cast<const v4i*>(xp[q] + (int64_t)(g + 1) * gstride);
+        }
         const int ic = 16 * g;
         int32_t wq[OCB][4];
 #pragma unroll
@@ -296,30 +312,41 @@ __global__ __launch_bounds__(kThreads) void k_deconv_dot4_blocked(DeconvArgs a, 
               wq[o][d] = in ? v : 0;
             }
           }
-        if (!ok) {
-          // zero-point fill of an out-of-image tap (channels past IC stay 0)
 #pragma unroll
-          for (int d = 0; d < 4; ++d) xv[d] = (ICF || ic + 4 * d < IC) ? zp4 : 0;
+        for (int q = 0; q < RQ; ++q) {
+          if (!ok[q]) {
+            // zero-point fill of an out-of-image tap (channels past IC stay 0)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) xv[q][d] = (ICF || ic + 4 * d < IC) ? zp4 : 0;
+          }
         }
 #pragma unroll
         for (int o = 0; o < OCB; ++o)
 #pragma unroll
-          for (int d = 0; d < 4; ++d) acc[o] = __builtin_amdgcn_sdot4(xv[d], wq[o][d], acc[o], false);
+          for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int q = 0; q < RQ; ++q)
+              acc[q][o] = __builtin_amdgcn_sdot4(xv[q][d], wq[o][d], acc[q][o], false);
       }
     }
   }
   if (ow >= a.W_out) return;
 #pragma unroll
-  for (int o = 0; o < OCB; ++o) {
-    const int oc = oc0 + o;
-    if (oc >= a.OC) break;
-    const int32_t c = acc[o] - a.izp * wsum[o];
-    const int64_t idx = (((int64_t)n * a.OC + oc) * a.H_out + oh) * a.W_out + ow;
-    if (a.acc) {
-      a.acc[idx] = c;
-    } else {
-      const float b = a.bias ? a.bias[oc] : 0.0f;
-      a.out[idx] = (int8_t)requant(c, a.wscale[oc], b, a.rq);
+  for (int q = 0; q < RQ; ++q) {
+    const int oh = rh + sh * (i0 + q);
+    if (oh >= a.H_out) break;
+#pragma unroll
+    for (int o = 0; o < OCB; ++o) {
+      const int oc = oc0 + o;
+      if (oc >= a.OC) break;
+      const int32_t c = acc[q][o] - a.izp * wsum[o];
+      const int64_t idx = (((int64_t)n * a.OC + oc) * a.H_out + oh) * a.W_out + ow;
+      if (a.acc) {
+        a.acc[idx] = c;
+      } else {
+        const float b = a.bias ? a.bias[oc] : 0.0f;
+        a.out[idx] = (int8_t)requant(c, a.wscale[oc], b, a.rq);
+      }
     }
   }
 }
@@ -369,9 +396,11 @@ hipError_t launch_t(const DeconvArgs& a, Phases p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OCB>
+template <int OCB, int RQ>
 hipError_t launch_blocked(const DeconvArgs& a, Phases p, hipStream_t s) {
   p.ocb = (int)((a.OC + OCB - 1) / OCB);
+  const int64_t Hp = (a.H_out + a.sh - 1) / a.sh;
+  p.ib = (int)((Hp + RQ - 1) / RQ);
   const int G = (int)((a.IC + 15) / 16);
   const size_t bytes = (size_t)a.N * a.H_in * a.W_in * G * 16;
   void* ws = nullptr;
@@ -383,13 +412,14 @@ hipError_t launch_blocked(const DeconvArgs& a, Phases p, hipStream_t s) {
                      (int)a.W_in, G);
   e = hipGetLastError();
   if (e == hipSuccess) {
-    const int64_t waves = (int64_t)p.ocb * p.jb * a.sw * a.H_out * a.N;
+    const int64_t waves = (int64_t)p.ocb * p.jb * a.sw * p.ib * a.sh * a.N;
+    const dim3 grid((unsigned)((waves + 3) / 4));
     if (a.IC % 16 == 0)
-      hipLaunchKernelGGL((k_deconv_dot4_blocked<OCB, true>), dim3((unsigned)((waves + 3) / 4)),
-                         dim3(kThreads), 0, s, a, p, (const int8_t*)ws);
+      hipLaunchKernelGGL((k_deconv_dot4_blocked<OCB, true, RQ>), grid, dim3(kThreads), 0, s, a, p,
+                         (const int8_t*)ws);
     else
-      hipLaunchKernelGGL((k_deconv_dot4_blocked<OCB, false>), dim3((unsigned)((waves + 3) / 4)),
-                         dim3(kThreads), 0, s, a, p, (const int8_t*)ws);
+      hipLaunchKernelGGL((k_deconv_dot4_blocked<OCB, false, RQ>), grid, dim3(kThreads), 0, s, a, p,
+                         (const int8_t*)ws);
     e = hipGetLastError();
   }
   hipError_t f = hipFreeAsync(ws, s);
@@ -410,10 +440,10 @@ bool deconv_dot4_supported(const DeconvArgs& a) {
 }
 
 // Default: the blocked path (input relayout into a stream-ordered workspace,
-// then 8 output channels per wave).  Q8TA_DECONV_LAYOUT=nchw selects the
-// direct path (no workspace); Q8TA_DECONV_OCB = 8 | 16 and, for the direct
-// path, Q8TA_DECONV_RQ = 1 | 2 | 4 choose the tile (16 x 4 is not built: it
-// needs more than 256 vector registers).
+// then 8 output channels x 1 phase row per wave).  Q8TA_DECONV_LAYOUT=nchw
+// selects the direct path (no workspace); Q8TA_DECONV_OCB = 8 | 16 and
+// Q8TA_DECONV_RQ = 1 | 2 | 4 choose the tile (16 x 4 is not built: it needs
+// more than 256 vector registers).
 hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s) {
   Phases p;
   if (!make_phases(a, p)) return hipErrorInvalidValue;
@@ -422,7 +452,12 @@ hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s) {
   if (const char* e = getenv("Q8TA_DECONV_OCB")) ocb = atoi(e);
   if (const char* e = getenv("Q8TA_DECONV_RQ")) rq = atoi(e);
   if (const char* e = getenv("Q8TA_DECONV_LAYOUT")) blocked = (e[0] != 'n');
-  if (blocked) return ocb == 16 ? launch_blocked<16>(a, p, s) : launch_blocked<8>(a, p, s);
+  if (blocked) {
+    if (ocb == 16) return rq == 2 ? launch_blocked<16, 2>(a, p, s) : launch_blocked<16, 1>(a, p, s);
+    if (rq == 2) return launch_blocked<8, 2>(a, p, s);
+    if (rq == 4) return launch_blocked<8, 4>(a, p, s);
+    return launch_blocked<8, 1>(a, p, s);
+  }
   if (ocb == 8) {
     if (rq == 1) return launch_t<8, 1>(a, p, s);
     if (rq == 2) return launch_t<8, 2>(a, p, s);

@@ -343,8 +343,9 @@ def test_deconv_every_tile(fj, fo, wi):
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
-@pytest.mark.parametrize("variant", ["blocked:8:1", "blocked:16:1", "nchw:8:1", "nchw:8:2",
-                                     "nchw:8:4", "nchw:16:1", "nchw:16:2"])
+@pytest.mark.parametrize("variant", ["blocked:8:1", "blocked:8:2", "blocked:8:4", "blocked:16:1",
+                                     "blocked:16:2", "nchw:8:1", "nchw:8:2", "nchw:8:4",
+                                     "nchw:16:1", "nchw:16:2"])
 @pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_CASES[6], DECONV_CASES[11],
                                   DECONV_CASES[13]],
                          ids=["k3s2", "mixed_strides", "empty_phases", "wide", "ic320"])
