@@ -87,7 +87,8 @@ __device__ __forceinline__ void dot_slice(const Slice<RN, RM, LW>& s, int32_t (&
 
 template <int RN, int RM, int LW, bool PIPE>
 __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t tiles_m,
-                                                        int64_t tiles_n, int64_t group) {
+                                                        int64_t tiles_n, int64_t group,
+                                                        int xcd_strips) {
   static_assert(RN * RM == 64, "one tile element per lane after the reduction");
   constexpr int64_t SL = 256 * LW;  // bytes of one row covered by one slice
   const int lane = threadIdx.x & 63;
@@ -95,13 +96,19 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
   // block -> (block-row bm_i along M, block-column bn_i along N), grouped:
   // `group` block-rows are walked together before moving to the next columns.
   const int64_t BM = (tiles_m + 1) / 2, BN = (tiles_n + 1) / 2;
-  const int64_t b = blockIdx.x;
-  const int64_t per_group = group * BN;
+  // With xcd_strips, block b runs on XCD b % 8 (round-robin dispatch) and each
+  // XCD owns a contiguous strip of `width` block-columns, so the weight rows
+  // of a strip are fetched into one L2 only; the grid is padded to 8 strips.
+  const int64_t width = xcd_strips ? (BN + 7) / 8 : BN;
+  const int64_t b = xcd_strips ? (int64_t)blockIdx.x / 8 : (int64_t)blockIdx.x;
+  const int64_t strip0 = xcd_strips ? (int64_t)(blockIdx.x % 8) * width : 0;
+  const int64_t per_group = group * width;
   const int64_t g = b / per_group;
   const int64_t rows_here = (g * group + group <= BM) ? group : BM - g * group;
   const int64_t in_g = b - g * per_group;
   const int64_t bm_i = g * group + in_g % rows_here;
-  const int64_t bn_i = in_g / rows_here;
+  const int64_t bn_i = strip0 + in_g / rows_here;
+  if (bn_i >= BN) return;
   const int64_t tm = bm_i * 2 + (wave & 1);
   const int64_t tn = bn_i * 2 + (wave >> 1);
   if (tm >= tiles_m || tn >= tiles_n) return;
@@ -175,13 +182,14 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
 }
 
 template <int LW, bool PIPE>
-hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group) {
+hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) {
   const int64_t tiles_m = (a.M + 7) / 8;
   const int64_t tiles_n = (a.N + 7) / 8;
-  const int64_t blocks = ((tiles_m + 1) / 2) * ((tiles_n + 1) / 2);
+  const int64_t BM = (tiles_m + 1) / 2, BN = (tiles_n + 1) / 2;
+  const int64_t blocks = BM * (xcd ? (BN + 7) / 8 * 8 : BN);
   if (group < 1) group = 1;
   hipLaunchKernelGGL((k_dot4_gemm<8, 8, LW, PIPE>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     a, tiles_m, tiles_n, group);
+                     a, tiles_m, tiles_n, group, xcd);
   return hipGetLastError();
 }
 
@@ -190,26 +198,32 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 bool gemm_dot4_supported(const LinearArgs& a) {
-  const int64_t blocks = ((a.M + 15) / 16) * ((a.N + 15) / 16);
+  const int64_t blocks = ((a.M + 15) / 16) * (((a.N + 15) / 16 + 7) / 8 * 8);
   return (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w) && blocks < ((int64_t)1 << 31);
 }
 
-// Variant: Q8TA_DOT4_CFG = "<LW><P|S>[:group]" (LW = 2 or 4 dwords per lane per
-// row, P = two-slice pipeline (LW = 2 only), S = single slice; group =
-// block-rows walked together).  Default "4S:32".
+// Variant: Q8TA_DOT4_CFG = "<LW><P|S>[:group[:x]]" (LW = 2 or 4 dwords per
+// lane per row, P = two-slice pipeline (LW = 2 only), S = single slice; group =
+// block-rows walked together; x = one weight strip per XCD).  Default: "4S:32",
+// with XCD strips when there are at least 64 block-columns.
 hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s) {
   int lw = 4;
   bool pipe = false;
   int64_t group = 32;
+  int xcd = ((a.N + 15) / 16) >= 64;
   if (const char* e = getenv("Q8TA_DOT4_CFG")) {
     if (e[0] == '2') lw = 2;
     if (e[0] && e[1] == 'P') pipe = true;
-    if (const char* c = strchr(e, ':')) group = atoll(c + 1);
+    if (const char* c = strchr(e, ':')) {
+      group = atoll(c + 1);
+      xcd = strchr(c + 1, 'x') != nullptr;
+    }
   }
   // The two-slice pipeline is built only with 2 dwords per lane: with 4 it
   // needs more than 256 vector registers.
-  if (lw == 2) return pipe ? launch_t<2, true>(a, s, group) : launch_t<2, false>(a, s, group);
-  return launch_t<4, false>(a, s, group);
+  if (lw == 2)
+    return pipe ? launch_t<2, true>(a, s, group, xcd) : launch_t<2, false>(a, s, group, xcd);
+  return launch_t<4, false>(a, s, group, xcd);
 }
 
 }  // namespace q8ta
