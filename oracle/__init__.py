@@ -27,6 +27,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q8ta_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# Tests that plant a mistake in a copy of the oracle point this at the copy.
+_LIB_OVERRIDE = os.environ.get("Q8TA_ORACLE_LIB")
 
 OK, BAD_ARG, OVERFLOW = 0, 1, 2
 
@@ -35,16 +37,23 @@ _c_dbl = ctypes.c_double
 _c_ptr = ctypes.c_void_p
 
 
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+             "-shared", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc-compile an oracle C source into a shared library at `out`."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc"] + GCC_FLAGS + ["-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = False) -> str:
     """Compile ``q8ta_oracle.c`` with gcc (no FMA contraction, no fast-math)."""
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    return compile_source(_SRC, _LIB)
 
 
 _lib = None
@@ -53,8 +62,11 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_LIB)
         for name in ("oracle_quantize_per_tensor", "oracle_dequantize_per_tensor",
                      "oracle_epilogue", "oracle_linear_acc", "oracle_linear_acc_folded",
                      "oracle_linear", "oracle_deconv_acc_gather", "oracle_deconv_acc_scatter",

@@ -220,6 +220,22 @@ def test_linear_gemv_rejects_m_gt_1():
         _run_linear(c, fn=q8.q8ta_linear_gemv)
 
 
+@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("out_scale", [0.272, 2.176, 1.0 / 3.0])
+def test_linear_epilogue_on_rounding_ties(M, out_scale):
+    """x == input zero point makes every accumulator 0, so the bias alone
+    carries values placed on and beside every rounding tie through the
+    kernel's epilogue (reciprocal in double, round half to even)."""
+    grid = ((np.arange(-140, 141) + 0.5) * out_scale).astype(np.float32)
+    b = np.concatenate([grid, np.nextafter(grid, np.float32(np.inf)),
+                        np.nextafter(grid, np.float32(-np.inf))])
+    N, K = b.size, 64
+    g = qi.rng(17)
+    c = qi.LinearCase(np.full((M, K), 3, np.int8), qi.w_int8(g, (N, K)), qi.scales(g, N), b,
+                      0.02, 3, out_scale, -5)
+    np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+
+
 def test_linear_unaligned_pointers():
     c = qi.linear_case(93, 33, 256, 40)
     xb = torch.zeros(c.M * c.K + 1, dtype=torch.int8, device="cuda")
@@ -358,6 +374,20 @@ def test_deconv_every_dot4_variant(variant, case):
     with env(Q8TA_DECONV_LAYOUT=layout, Q8TA_DECONV_OCB=ocb, Q8TA_DECONV_RQ=rq):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
+def test_deconv_epilogue_on_rounding_ties():
+    """x == input zero point everywhere: the accumulator is 0 and the bias (one
+    value per output channel, on and beside rounding ties) is requantized."""
+    out_scale = 0.272
+    grid = ((np.arange(-140, 141) + 0.5) * out_scale).astype(np.float32)
+    b = np.concatenate([grid, np.nextafter(grid, np.float32(np.inf))])
+    OC = b.size
+    c = qi.deconv_case(23, 1, 16, 4, 4, OC, 3, 3, (2, 2), (1, 1), (1, 1))
+    c.x[...] = 3
+    c.bias = b
+    c.out_scale = out_scale
+    np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
 
 
 @pytest.mark.parametrize("izp", [-128, 127])

@@ -185,6 +185,20 @@ def test_epilogue_requant_matches_torch_quantize(out_scale):
     np.testing.assert_array_equal(q, _torch_quant(pre, out_scale, -5))
 
 
+@pytest.mark.parametrize("out_scale", [0.272, 2.176, 0.544, 1.0 / 3.0])
+def test_epilogue_requant_tie_grid_matches_torch_quantize(out_scale):
+    """With acc = 0 the epilogue's value is the bias exactly, so feeding the
+    quantize tie grid through the bias pins the requantize reciprocal (taken
+    in double, as the quantize page states for its inverse scale) on exactly
+    the values where a float reciprocal would round differently."""
+    grid = ((np.arange(-140, 141) + 0.5) * out_scale).astype(np.float32)
+    v = np.concatenate([grid, np.nextafter(grid, np.float32(np.inf)),
+                        np.nextafter(grid, np.float32(-np.inf))])
+    acc = np.zeros(v.size, np.int32)
+    q = oracle.epilogue(acc, v.size, 1, 1.0, np.ones(v.size, np.float32), v, out_scale, -5)
+    np.testing.assert_array_equal(q, _torch_quant(v, out_scale, -5))
+
+
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_epilogue_dequant_within_float_error_bound(with_bias):
     g = qi.rng(23)
