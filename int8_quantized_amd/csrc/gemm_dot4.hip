@@ -7,8 +7,9 @@
 // 64 lanes split K: in one pass lane l reads LW dwords at byte 4*LW*l of a
 // 256*LW-byte slice of every one of the RN + RM rows (each load instruction
 // moves 256*LW contiguous bytes), and accumulates RN*RM partial dot products
-// plus the RN partial row sums of W (v_dot4 against 0x01010101) in
-// registers.  The zero-point term is folded as sum x*w - izp*sum w.  At the
+// in registers.  The zero-point term is folded as sum x*w - izp*sum w, with
+// the row sums of W formed by a small pass over W before the GEMM (one wave
+// per row, v_dot4 against 0x01010101) into a stream-ordered workspace.  At the
 // end the RN*RM partials are summed over the 64 lanes with a transposing
 // butterfly: at each of the 6 steps a lane keeps half of its values, sends the
 // other half to its partner and adds what it receives, so after 63 exchanges
@@ -71,13 +72,11 @@ __device__ __forceinline__ void load_slice(Slice<RN, RM, LW>& s, const LinearArg
 }
 
 template <int RN, int RM, int LW>
-__device__ __forceinline__ void dot_slice(const Slice<RN, RM, LW>& s, int32_t (&acc)[RN * RM],
-                                          int32_t (&sw)[RN]) {
+__device__ __forceinline__ void dot_slice(const Slice<RN, RM, LW>& s, int32_t (&acc)[RN * RM]) {
 #pragma unroll
   for (int d = 0; d < LW; ++d) {
 #pragma unroll
     for (int r = 0; r < RN; ++r) {
-      sw[r] = __builtin_amdgcn_sdot4(s.w[r][d], 0x01010101, sw[r], false);
 #pragma unroll
       for (int m = 0; m < RM; ++m)
         acc[r * RM + m] = __builtin_amdgcn_sdot4(s.x[m][d], s.w[r][d], acc[r * RM + m], false);
@@ -85,10 +84,30 @@ __device__ __forceinline__ void dot_slice(const Slice<RN, RM, LW>& s, int32_t (&
   }
 }
 
+// sum_k w[n, k] for every weight row: one wave per row, lanes split K, v_dot4
+// against 0x01010101, then a reduction across the wave.
+__global__ __launch_bounds__(kThreads) void k_row_sums(const int8_t* __restrict__ w, int64_t N,
+                                                       int64_t K, int32_t* __restrict__ out) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (n >= N) return;
+  int32_t s = 0;
+  for (int64_t k = (int64_t)lane * 16; k < K; k += 1024) {
+    const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(w + n * K + k));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) s = __builtin_amdgcn_sdot4(v[d], 0x01010101, s, false);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) out[n] = s;
+}
+
 template <int RN, int RM, int LW, bool PIPE>
 __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t tiles_m,
                                                         int64_t tiles_n, int64_t group,
-                                                        int xcd_strips) {
+                                                        int xcd_strips,
+                                                        const int32_t* __restrict__ wsum) {
   static_assert(RN * RM == 64, "one tile element per lane after the reduction");
   constexpr int64_t SL = 256 * LW;  // bytes of one row covered by one slice
   const int lane = threadIdx.x & 63;
@@ -118,11 +137,8 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
   const int8_t* xb = a.x + m0 * a.K;
 
   int32_t acc[RN * RM];
-  int32_t sw[RN];
 #pragma unroll
   for (int i = 0; i < RN * RM; ++i) acc[i] = 0;
-#pragma unroll
-  for (int r = 0; r < RN; ++r) sw[r] = 0;
 
   const int64_t kl = (int64_t)lane * 4 * LW;
   const bool full = (n0 + RN <= a.N) && (m0 + RM <= a.M) && (a.K % SL == 0);
@@ -131,32 +147,27 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
     load_slice<false>(s0, a, wb, xb, n0, m0, kl);
     for (int64_t k0 = 0; k0 < a.K; k0 += 2 * SL) {
       load_slice<false>(s1, a, wb, xb, n0, m0, k0 + SL + kl);
-      dot_slice(s0, acc, sw);
+      dot_slice(s0, acc);
       if (k0 + 2 * SL >= a.K) {
-        dot_slice(s1, acc, sw);
+        dot_slice(s1, acc);
         break;
       }
       load_slice<false>(s0, a, wb, xb, n0, m0, k0 + 2 * SL + kl);
-      dot_slice(s1, acc, sw);
+      dot_slice(s1, acc);
     }
   } else if (full) {
     for (int64_t k0 = 0; k0 < a.K; k0 += SL) {
       Slice<RN, RM, LW> s0;
       load_slice<true>(s0, a, wb, xb, n0, m0, k0 + kl);
-      dot_slice(s0, acc, sw);
+      dot_slice(s0, acc);
     }
   } else {
     for (int64_t k0 = 0; k0 < a.K; k0 += SL) {
       Slice<RN, RM, LW> s0;
       load_slice<false>(s0, a, wb, xb, n0, m0, k0 + kl);
-      dot_slice(s0, acc, sw);
+      dot_slice(s0, acc);
     }
   }
-#pragma unroll
-  for (int r = 0; r < RN; ++r)
-#pragma unroll
-    for (int m = 0; m < RM; ++m) acc[r * RM + m] -= a.izp * sw[r];
-
   // Transposing butterfly over the 64 lanes (element index bit b <- lane bit b).
 #pragma unroll
   for (int half = 32; half >= 1; half >>= 1) {
@@ -172,15 +183,17 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
   const int r = lane / RM, m = lane % RM;
   const int64_t n = n0 + r, mm = m0 + m;
   if (n < a.N && mm < a.M) {
+    const int32_t c = acc[0] - a.izp * wsum[n];
     if (a.acc) {
-      a.acc[mm * a.N + n] = acc[0];
+      a.acc[mm * a.N + n] = c;
     } else {
       const float bv = a.bias ? a.bias[n] : 0.0f;
-      a.out[mm * a.N + n] = (int8_t)requant(acc[0], a.wscale[n], bv, a.rq);
+      a.out[mm * a.N + n] = (int8_t)requant(c, a.wscale[n], bv, a.rq);
     }
   }
 }
 
+// Row sums of W into a stream-ordered workspace, then the GEMM.
 template <int LW, bool PIPE>
 hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) {
   const int64_t tiles_m = (a.M + 7) / 8;
@@ -188,9 +201,19 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
   const int64_t BM = (tiles_m + 1) / 2, BN = (tiles_n + 1) / 2;
   const int64_t blocks = BM * (xcd ? (BN + 7) / 8 * 8 : BN);
   if (group < 1) group = 1;
-  hipLaunchKernelGGL((k_dot4_gemm<8, 8, LW, PIPE>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     a, tiles_m, tiles_n, group, xcd);
-  return hipGetLastError();
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, (size_t)a.N * sizeof(int32_t), s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_row_sums, dim3((unsigned)((a.N + 3) / 4)), dim3(kThreads), 0, s, a.w, a.N,
+                     a.K, (int32_t*)ws);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL((k_dot4_gemm<8, 8, LW, PIPE>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       s, a, tiles_m, tiles_n, group, xcd, (const int32_t*)ws);
+    e = hipGetLastError();
+  }
+  hipError_t f = hipFreeAsync(ws, s);
+  return e != hipSuccess ? e : f;
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
