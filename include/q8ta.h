@@ -9,9 +9,16 @@
  *
  * Common rules for every entry point:
  *   - Every tensor pointer is a DEVICE pointer on the current HIP device,
- *     allocated and owned by the caller; the library never frees, retains or
- *     allocates per call.  Tensors are dense and contiguous in the stated
- *     layout.  int8 tensors are plain byte arrays (element i at byte i).
+ *     allocated and owned by the caller; the library never frees or retains
+ *     it.  Tensors are dense and contiguous in the stated layout.  int8
+ *     tensors are plain byte arrays (element i at byte i).
+ *   - Workspace: on their register-tiled paths, q8ta_linear / q8ta_linear_acc
+ *     with M > 4 (K % 16 == 0, 16-byte aligned x and weight) take 4*N bytes
+ *     (weight row sums), and q8ta_conv2d_transposed(_acc) (IC % 4 == 0) takes
+ *     N*H_in*ceil(IC/16)*W_in*16 bytes (a channel-blocked copy of the input)
+ *     from the stream-ordered allocator (hipMallocAsync on `stream`, released
+ *     with hipFreeAsync on the same stream after the kernels that use it).
+ *     A failed allocation returns Q8TA_ERR_HIP and launches nothing.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns after the launch; results are visible to later work on that
  *     stream.  Calls are reentrant and keep no state between calls.
