@@ -193,6 +193,218 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, int64_t ti
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped variant: the 64 lanes of a wave form 4 groups of 16 (one DPP row
+// each).  Group g owns an 8 x 8 tile (8 activation rows, 8 weight rows) of the
+// wave's 16 x 16 tile; its 16 lanes split K, lane l reading 4*LW bytes at byte
+// 4*LW*l of a 64*LW-byte slice of each of its 16 rows.  The 64 partial sums of
+// a lane are reduced over its 16-lane row only, with a transposing butterfly
+// whose exchanges are DPP lane moves inside the row (mirror of 16, mirror of 8,
+// quad reverse, quad swap: lane masks 15, 7, 3, 1, which span all 16 lanes), so
+// the reduction costs one exchange per four outputs and no LDS traffic.
+// Afterwards lane l of a group holds four consecutive output channels of one
+// activation row: row (l >> 1) & 7, channels 4 * (l & 1) .. +3 of the tile.
+
+// Lane moves inside a row of 16 lanes (DPP controls of the gfx9 encoding).
+constexpr int kDppSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppRev4 = 0x1B;      // quad_perm [3,2,1,0]: lane ^ 3
+constexpr int kDppMirror8 = 0x141;  // row_half_mirror:     lane ^ 7
+constexpr int kDppMirror16 = 0x140; // row_mirror:          lane ^ 15
+
+template <int CTRL>
+__device__ __forceinline__ int32_t row_move(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// One butterfly step over HALF value pairs: keep the upper or lower half by
+// `upper`, receive the partner's copy of the kept half and add it.
+template <int HALF, int CTRL>
+__device__ __forceinline__ void fold(int32_t (&acc)[64], bool upper) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const int32_t lo = acc[i], hi = acc[i + HALF];
+    const int32_t keep = upper ? hi : lo;
+    const int32_t send = upper ? lo : hi;
+    acc[i] = keep + row_move<CTRL>(send);
+  }
+}
+
+// Loads one slice for a group: row r of the weights is read at
+// p.w[r] + (woff + k) and row m of the activations at p.x[m] + (xoff + k):
+// the row pointers are wave-uniform (scalar registers) and the
+// 32-bit lane offset holds the group's row offset, the lane's byte offset in
+// the slice and the slice start k, so every load is one scalar-base plus
+// 32-bit-offset instruction.  k passes through readfirstlane so that the
+// loop does not turn the offsets into per-row 64-bit induction variables.
+// Unless FULL, rows at or past nrem / mrem (counted from the group's first
+// row) and lanes with `kin` false read zeros.
+typedef const __attribute__((address_space(1))) int8_t* gptr;
+
+__device__ __forceinline__ gptr uniform_ptr(const int8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (gptr)(((uint64_t)hi << 32) | lo);
+}
+
+// Row pointers of a wave's 8 weight rows and 8 activation rows (wave-uniform,
+// kept in scalar registers; the empty asm makes each one opaque so that the
+// compiler does not fold the lane offset into a per-row 64-bit vector add).
+struct RowPtrs {
+  gptr w[8], x[8];
+};
+
+__device__ __forceinline__ void row_ptrs(RowPtrs& p, gptr wu, gptr xu, int64_t K) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    p.w[r] = wu + r * K;
+    p.x[r] = xu + r * K;
+    asm volatile("" : "+s"(p.w[r]));
+    asm volatile("" : "+s"(p.x[r]));
+  }
+}
+
+template <bool FULL, int LW>
+__device__ __forceinline__ void load_slice_g(Slice<8, 8, LW>& s, const RowPtrs& p, uint32_t woff,
+                                             uint32_t xoff, int64_t k, bool kin, int64_t nrem,
+                                             int64_t mrem) {
+  typedef typename Vec<LW>::type V;
+  typedef const __attribute__((address_space(1))) V* vptr;
+  const uint32_t ku = __builtin_amdgcn_readfirstlane((uint32_t)k);
+  const uint32_t wo = woff + ku, xo = xoff + ku;
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    s.w[r] = (FULL || (kin && r < nrem)) ? *reinterpret_cast<vptr>(p.w[r] + wo) : V{};
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    s.x[m] = (FULL || (kin && m < mrem)) ? *reinterpret_cast<vptr>(p.x[m] + xo) : V{};
+}
+
+// acc[m * 8 + n] += x row m . w row n over one slice (m, n < 8).
+template <int LW>
+__device__ __forceinline__ void dot_slice_mn(const Slice<8, 8, LW>& s, int32_t (&acc)[64]) {
+#pragma unroll
+  for (int d = 0; d < LW; ++d) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        acc[m * 8 + n] = __builtin_amdgcn_sdot4(s.x[m][d], s.w[n][d], acc[m * 8 + n], false);
+    }
+  }
+}
+
+// Block b covers a 32 x 32 output tile (4 waves, 2 x 2).  Block order as in
+// k_dot4_gemm: `group` block-rows walked together, optionally one strip of
+// block-columns per XCD.
+template <int LW, bool PIPE>
+__global__ __launch_bounds__(kThreads) void k_dot4_gemm_g(LinearArgs a, uint32_t BMb, uint32_t BNb,
+                                                          uint32_t group, int xcd_strips,
+                                                          const int32_t* __restrict__ wsum) {
+  constexpr int64_t SL = 64 * LW;  // bytes of one row covered by one slice of a group
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t width = xcd_strips ? (BNb + 7) / 8 : BNb;
+  const uint32_t b = xcd_strips ? blockIdx.x / 8 : blockIdx.x;
+  const uint32_t strip0 = xcd_strips ? (blockIdx.x % 8) * width : 0;
+  const uint32_t per_group = group * width;
+  const uint32_t g = b / per_group;
+  const uint32_t rows_here = (g * group + group <= BMb) ? group : BMb - g * group;
+  const uint32_t in_g = b - g * per_group;
+  const uint32_t bm_i = g * group + in_g % rows_here;
+  const uint32_t bn_i = strip0 + in_g / rows_here;
+  if (bn_i >= BNb) return;
+  const int64_t m0w = (int64_t)bm_i * 32 + 16 * (wave & 1);
+  const int64_t n0w = (int64_t)bn_i * 32 + 16 * (wave >> 1);
+  if (m0w >= a.M || n0w >= a.N) return;  // wave-uniform
+  const int64_t m0 = m0w + 8 * (grp & 1);
+  const int64_t n0 = n0w + 8 * (grp >> 1);
+  const int64_t nrem = a.N - n0, mrem = a.M - m0;
+  const uint32_t kl = (uint32_t)(l16 * 4 * LW);
+  const uint32_t woff = (uint32_t)(8 * (grp >> 1)) * (uint32_t)a.K + kl;
+  const uint32_t xoff = (uint32_t)(8 * (grp & 1)) * (uint32_t)a.K + kl;
+  const gptr wu = uniform_ptr(a.w + n0w * a.K);
+  const gptr xu = uniform_ptr(a.x + m0w * a.K);
+  RowPtrs rp;
+  row_ptrs(rp, wu, xu, a.K);
+
+  int32_t acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = 0;
+
+  const int64_t Kf = a.K - a.K % SL;  // whole slices; the rest is one masked slice
+  const bool full = (m0w + 16 <= a.M) && (n0w + 16 <= a.N);
+  if constexpr (PIPE) {
+    if (Kf > 0) {
+      Slice<8, 8, LW> s0, s1;
+      load_slice_g<false>(s0, rp, woff, xoff, 0, true, nrem, mrem);
+      for (int64_t k0 = 0; k0 < Kf; k0 += 2 * SL) {
+        if (k0 + SL < Kf)
+          load_slice_g<false>(s1, rp, woff, xoff, k0 + SL, true, nrem, mrem);
+        dot_slice_mn(s0, acc);
+        if (k0 + SL >= Kf) break;
+        if (k0 + 2 * SL < Kf)
+          load_slice_g<false>(s0, rp, woff, xoff, k0 + 2 * SL, true, nrem,
+                              mrem);
+        dot_slice_mn(s1, acc);
+      }
+    }
+  } else if (full) {
+    for (int64_t k0 = 0; k0 < Kf; k0 += SL) {
+      Slice<8, 8, LW> s0;
+      load_slice_g<true>(s0, rp, woff, xoff, k0, true, nrem, mrem);
+      dot_slice_mn(s0, acc);
+    }
+  } else {
+    for (int64_t k0 = 0; k0 < Kf; k0 += SL) {
+      Slice<8, 8, LW> s0;
+      load_slice_g<false>(s0, rp, woff, xoff, k0, true, nrem, mrem);
+      dot_slice_mn(s0, acc);
+    }
+  }
+  if (Kf < a.K) {
+    Slice<8, 8, LW> s0;
+    load_slice_g<false>(s0, rp, woff, xoff, Kf, Kf + kl < a.K, nrem, mrem);
+    dot_slice_mn(s0, acc);
+  }
+  fold<32, kDppMirror16>(acc, (l16 & 8) != 0);
+  fold<16, kDppMirror8>(acc, (l16 & 4) != 0);
+  fold<8, kDppRev4>(acc, (l16 & 2) != 0);
+  fold<4, kDppSwap1>(acc, (l16 & 1) != 0);
+  // acc[t] = tile element e = 32*b3 + 16*b2 + 8*b1 + 4*b0 + t (b = bits of l16),
+  // i.e. row e / 8 = (l16 >> 1) & 7 and channel e % 8 = 4 * (l16 & 1) + t.
+  const int64_t mm = m0 + ((l16 >> 1) & 7);
+  const int64_t nb = n0 + 4 * (l16 & 1);
+  if (mm >= a.M) return;
+  int32_t c[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) c[t] = (nb + t < a.N) ? acc[t] - a.izp * wsum[nb + t] : 0;
+  if (a.acc) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (nb + t < a.N) a.acc[mm * a.N + nb + t] = c[t];
+    return;
+  }
+  int q[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bool ok = nb + t < a.N;
+    const float sc = ok ? a.wscale[nb + t] : 0.0f;
+    const float bv = (ok && a.bias) ? a.bias[nb + t] : 0.0f;
+    q[t] = requant(c[t], sc, bv, a.rq);
+  }
+  int8_t* o = a.out + mm * a.N + nb;
+  if (nb + 3 < a.N && ((uintptr_t)o & 3) == 0) {
+    *reinterpret_cast<uint32_t*>(o) = pack4(q[0], q[1], q[2], q[3]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (nb + t < a.N) o[t] = (int8_t)q[t];
+  }
+}
+
 // Row sums of W into a stream-ordered workspace, then the GEMM.
 template <int LW, bool PIPE>
 hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) {
@@ -216,34 +428,70 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
   return e != hipSuccess ? e : f;
 }
 
+// Row sums of W, then the grouped GEMM.
+template <int LW, bool PIPE>
+hipError_t launch_g(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) {
+  const uint32_t BMb = (uint32_t)((a.M + 31) / 32), BNb = (uint32_t)((a.N + 31) / 32);
+  const int64_t blocks = (int64_t)BMb * (xcd ? ((int64_t)BNb + 7) / 8 * 8 : BNb);
+  if (group < 1) group = 1;
+  if (group > BMb) group = BMb;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, (size_t)a.N * sizeof(int32_t), s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_row_sums, dim3((unsigned)((a.N + 3) / 4)), dim3(kThreads), 0, s, a.w, a.N,
+                     a.K, (int32_t*)ws);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL((k_dot4_gemm_g<LW, PIPE>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a,
+                       BMb, BNb, (uint32_t)group, xcd, (const int32_t*)ws);
+    e = hipGetLastError();
+  }
+  hipError_t f = hipFreeAsync(ws, s);
+  return e != hipSuccess ? e : f;
+}
+
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
 bool gemm_dot4_supported(const LinearArgs& a) {
   const int64_t blocks = ((a.M + 15) / 16) * (((a.N + 15) / 16 + 7) / 8 * 8);
-  return (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w) && blocks < ((int64_t)1 << 31);
+  // K < 2^28 keeps the grouped kernel's 32-bit lane offsets (< 9 K + 256) in range.
+  return (a.K % 16) == 0 && a.K < ((int64_t)1 << 28) && aligned16(a.x) && aligned16(a.w) &&
+         blocks < ((int64_t)1 << 31);
 }
 
-// Variant: Q8TA_DOT4_CFG = "<LW><P|S>[:group[:x]]" (LW = 2 or 4 dwords per
-// lane per row, P = two-slice pipeline (LW = 2 only), S = single slice; group =
-// block-rows walked together; x = one weight strip per XCD).  Default: "4S:32",
-// with XCD strips when there are at least 64 block-columns.
+// Variant: Q8TA_DOT4_CFG = "[G]<LW><P|S>[:group[:x]]".  G = the grouped
+// kernel (16 lanes per K split, 32 x 32 blocks), otherwise the whole-wave K
+// split (16 x 16 blocks); LW = 2 or 4 dwords per lane per row; P = two-slice
+// pipeline (LW = 2 only), S = single slice; group = block-rows walked
+// together; x = one weight strip per XCD.  Default: "G4S:16", with XCD strips
+// when N >= 1024.
 hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s) {
+  bool grouped = true;
   int lw = 4;
   bool pipe = false;
-  int64_t group = 32;
-  int xcd = ((a.N + 15) / 16) >= 64;
+  int64_t group = 16;
+  int xcd = a.N >= 1024;
   if (const char* e = getenv("Q8TA_DOT4_CFG")) {
+    grouped = e[0] == 'G';
+    if (grouped) ++e;
     if (e[0] == '2') lw = 2;
     if (e[0] && e[1] == 'P') pipe = true;
     if (const char* c = strchr(e, ':')) {
       group = atoll(c + 1);
       xcd = strchr(c + 1, 'x') != nullptr;
+    } else if (!grouped) {
+      group = 32;
     }
   }
   // The two-slice pipeline is built only with 2 dwords per lane: with 4 it
   // needs more than 256 vector registers.
+  if (grouped) {
+    if (lw == 2)
+      return pipe ? launch_g<2, true>(a, s, group, xcd) : launch_g<2, false>(a, s, group, xcd);
+    return launch_g<4, false>(a, s, group, xcd);
+  }
   if (lw == 2)
     return pipe ? launch_t<2, true>(a, s, group, xcd) : launch_t<2, false>(a, s, group, xcd);
   return launch_t<4, false>(a, s, group, xcd);

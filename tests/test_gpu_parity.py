@@ -187,7 +187,8 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
 
 
-@pytest.mark.parametrize("cfg", ["4S:32", "4S:32x", "4S:1", "4S:3x", "2S:8", "2P:8", "2P:3x"])
+@pytest.mark.parametrize("cfg", ["G4S:16", "G4S:16x", "G4S:1", "G4S:3x", "G2S:8", "G2P:8", "G2P:3x",
+                                 "4S:32", "4S:32x", "4S:1", "4S:3x", "2S:8", "2P:8", "2P:3x"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (17, 4096, 40), (512, 2048, 768)])
 def test_linear_every_dot4_variant(cfg, M, K, N):
     _say(f"dot4 gemm cfg={cfg} M={M} K={K} N={N}")
