@@ -122,9 +122,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--profile-only", choices=["gemm-and-copy"], default=None,
+    ap.add_argument("--profile-only", choices=["gemm-and-copy", "deconv"], default=None,
                     help="for hardware-counter runs: launch the GEMM `--steps` times and the "
-                         "256 MiB calibration copy 3 times, print nothing else")
+                         "256 MiB calibration copy 3 times (gemm-and-copy), or the large "
+                         "transposed conv `--steps` times (deconv); print nothing else")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -171,6 +172,28 @@ def main():
     def deq():
         check(lib.q8ta_dequantize_per_tensor(out.data_ptr(), y.data_ptr(), M * N, c.out_scale,
                                              c.out_zp, stream))
+
+    if args.profile_only == "deconv":
+        d = qi.make_deconv_large()
+        xq = torch.empty(d.x_fp32.shape, dtype=torch.int8, device="cuda")
+        check(lib.q8ta_quantize_per_tensor(torch.from_numpy(d.x_fp32).cuda().data_ptr(),
+                                           xq.data_ptr(), d.x_fp32.size, d.in_scale, d.in_zp,
+                                           stream))
+        w_ = torch.from_numpy(d.w).cuda()
+        dws = torch.from_numpy(d.weight_scales).cuda()
+        db = torch.from_numpy(d.bias).cuda()
+        N_, IC, H, W = d.x_fp32.shape
+        dout = torch.empty((N_, d.w.shape[0], d.H_out, d.W_out), dtype=torch.int8, device="cuda")
+        for _ in range(args.steps):
+            check(lib.q8ta_conv2d_transposed(
+                xq.data_ptr(), N_, IC, H, W, d.in_scale, d.in_zp, w_.data_ptr(), d.w.shape[0],
+                d.Kh, d.Kw, d.w.shape[1], None, dws.data_ptr(), db.data_ptr(), d.out_scale,
+                d.out_zp, d.stride[0], d.stride[1], d.padding[0], d.padding[1],
+                d.output_padding[0], d.output_padding[1], 1, 1, 1, b"none", dout.data_ptr(),
+                d.H_out, d.W_out, stream))
+        torch.cuda.synchronize()
+        log(f"profiled {args.steps} launches of the large transposed conv")
+        return
 
     if args.profile_only == "gemm-and-copy":
         for _ in range(args.steps):
@@ -291,8 +314,24 @@ def run_ceilings(torch, stream, timer):
     ms = timer.time_calls([lambda: cl.q8ta_calib_copy(src.data_ptr(), dst.data_ptr(), n // 16,
                                                       256 * 8, stream)], 10, batches=3)
     copy_gbs = 2 * n / (min(ms) / 1e3) / 1e9
+    del src, dst
+    # read-only stream of the GEMV's weight size, 32 rotating copies (537 MB) so
+    # that every launch reads from HBM; and an empty launch of the GEMV's grid
+    cl.q8ta_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    cl.q8ta_calib_empty.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    nr = 4096 * 4096
+    bufs = [torch.empty(nr, dtype=torch.uint8, device="cuda") for _ in range(32)]
+    ms = timer.time_calls([lambda b=b: cl.q8ta_calib_read(b.data_ptr(), nr // 16, out.data_ptr(),
+                                                          stream) for b in bufs], 128, batches=3)
+    read_us = min(ms) * 1e3
+    del bufs
+    ms = timer.time_calls([lambda: cl.q8ta_calib_empty(out.data_ptr(), 512, stream)], 200,
+                          batches=3)
     return {"dot4_loop_tops": round(dot4_tops, 1), "dot4_peak_tops_derived": round(PEAK_DOT4_TOPS, 1),
-            "copy_256MiB_gbs": round(copy_gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS}
+            "copy_256MiB_gbs": round(copy_gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS,
+            "read_16MiB_cold_us": round(read_us, 2),
+            "read_16MiB_cold_gbs": round(nr / (read_us / 1e6) / 1e9, 1),
+            "empty_launch_us": round(min(ms) * 1e3, 2)}
 
 
 def run_extra(torch, np, q8, qi, lib, stream, timer, check):

@@ -6,6 +6,11 @@
 //    accumulations on registers (no memory traffic inside the loop) and writes
 //    one int32; ops = threads * iters * 16 * 8.
 //  q8ta_calib_copy: 16-byte grid-stride copy of n16 chunks; bytes = 32 * n16.
+//  q8ta_calib_read: read-only stream of n16 16-byte chunks, 8 per thread in
+//    the access pattern of the GEMV's weight stream (each load instruction of
+//    a wave covers 1 KiB); bytes = 16 * n16.
+//  q8ta_calib_empty: a launch of `blocks` blocks that do no work (the floor
+//    of one launch in a back-to-back sequence).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,6 +43,25 @@ __global__ __launch_bounds__(256) void k_copy16(const v4i* __restrict__ src, v4i
     __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
+__global__ __launch_bounds__(256) void k_read16(const v4i* __restrict__ src, int64_t n16,
+                                                int32_t* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * 256 * 8 + threadIdx.x;
+  v4i v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = base + u * 256;
+    v[u] = i < n16 ? __builtin_nontemporal_load(&src[i]) : v4i{0, 0, 0, 0};
+  }
+  int s = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  if (s == 0x7fffffff) out[0] = s;  // keeps the loads; almost never taken
+}
+
+__global__ __launch_bounds__(256) void k_empty(int32_t* out, int flag) {
+  if (flag) out[threadIdx.x] = 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,6 +77,20 @@ int q8ta_calib_dot4(int32_t* out, int blocks, int iters, hipStream_t s) {
 int q8ta_calib_copy(const void* src, void* dst, int64_t n16, int blocks, hipStream_t s) {
   if (!src || !dst || n16 < 1 || blocks < 1) return 1;
   hipLaunchKernelGGL(k_copy16, dim3(blocks), dim3(256), 0, s, (const v4i*)src, (v4i*)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// src: device buffer of n16 16-byte chunks; out: int32 device scratch (>= 1).
+int q8ta_calib_read(const void* src, int64_t n16, int32_t* out, hipStream_t s) {
+  if (!src || !out || n16 < 1) return 1;
+  const int64_t blocks = (n16 + 256 * 8 - 1) / (256 * 8);
+  hipLaunchKernelGGL(k_read16, dim3((unsigned)blocks), dim3(256), 0, s, (const v4i*)src, n16, out);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int q8ta_calib_empty(int32_t* out, int blocks, hipStream_t s) {
+  if (!out || blocks < 1) return 1;
+  hipLaunchKernelGGL(k_empty, dim3(blocks), dim3(256), 0, s, out, 0);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -46,12 +46,6 @@ struct Phases {
   int ocb;    // blocks of OCB output channels
 };
 
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 template <int OCB, int RQ>
 __global__ __launch_bounds__(kThreads) void k_deconv_dot4(DeconvArgs a, Phases p) {
   const int lane = threadIdx.x & 63;
@@ -96,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void k_deconv_dot4(DeconvArgs a, Phases p
     }
   }
 #pragma unroll
-  for (int o = 0; o < OCB; ++o) wsum[o] = wave_sum(wsum[o]);
+  for (int o = 0; o < OCB; ++o) wsum[o] = wave_total(wsum[o]);
 
   int32_t acc[RQ][OCB];
 #pragma unroll
@@ -264,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_deconv_dot4_blocked(DeconvArgs a, 
     }
   }
 #pragma unroll
-  for (int o = 0; o < OCB; ++o) wsum[o] = wave_sum(wsum[o]);
+  for (int o = 0; o < OCB; ++o) wsum[o] = wave_total(wsum[o]);
 
   int32_t acc[RQ][OCB];
 #pragma unroll

@@ -23,12 +23,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 template <int MR, int ROWS, int CH>
 __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   const int lane = threadIdx.x & 63;
@@ -36,6 +30,16 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   const int64_t n0 = wave * ROWS;
   if (n0 >= a.N) return;
   const int64_t K = a.K;
+  // The epilogue's per-channel scale and bias are fetched before the weight
+  // stream so that their latency overlaps it (lane i < ROWS holds row n0 + i).
+  float sc_pre = 0.0f, b_pre = 0.0f;
+  {
+    const int64_t n = n0 + (lane % ROWS);
+    if (lane < ROWS * MR && n < a.N && !a.acc) {
+      sc_pre = a.wscale[n];
+      b_pre = a.bias ? a.bias[n] : 0.0f;
+    }
+  }
   int32_t dot[MR][ROWS];
   int32_t sw[ROWS];
 #pragma unroll
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   for (int m = 0; m < MR; ++m) {
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      int32_t t = wave_sum(dot[m][r] - a.izp * sw[r]);
+      int32_t t = wave_total(dot[m][r] - a.izp * sw[r]);
       if (lane == m * ROWS + r) mine = t;
     }
   }
@@ -92,8 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
       if (a.acc) {
         a.acc[m * a.N + n] = mine;
       } else {
-        const float b = a.bias ? a.bias[n] : 0.0f;
-        a.out[m * a.N + n] = (int8_t)requant(mine, a.wscale[n], b, a.rq);
+        a.out[m * a.N + n] = (int8_t)requant(mine, sc_pre, b_pre, a.rq);
       }
     }
   }

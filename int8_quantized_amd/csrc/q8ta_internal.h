@@ -41,6 +41,30 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
          ((uint32_t)(d & 0xff) << 24);
 }
 
+// Lane moves inside a row of 16 lanes (DPP controls of the gfx9 encoding).
+constexpr int kDppSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppRev4 = 0x1B;       // quad_perm [3,2,1,0]: lane ^ 3
+constexpr int kDppMirror8 = 0x141;   // row_half_mirror:     lane ^ 7
+constexpr int kDppMirror16 = 0x140;  // row_mirror:          lane ^ 15
+
+template <int CTRL>
+__device__ __forceinline__ int32_t row_move(int32_t v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
+// Sum of v over the 64 lanes of a wave, returned wave-uniform.  Every lane of
+// the wave must be active.  Four DPP steps (lane masks 15, 7, 3, 1 span the 16
+// lanes of a row) leave each row's sum in all of its lanes; the four row sums
+// are then read out with v_readlane.
+__device__ __forceinline__ int32_t wave_total(int32_t v) {
+  v += row_move<kDppMirror16>(v);
+  v += row_move<kDppMirror8>(v);
+  v += row_move<kDppRev4>(v);
+  v += row_move<kDppSwap1>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 // ---- launchers (host functions; each returns hipGetLastError() after launch)
 hipError_t launch_quantize(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
                            hipStream_t s);

@@ -6,11 +6,13 @@
 // dequantize (the decomposed op the q8ta subgraph ends with):
 //   y = (float)(q - zero_point) * (float)scale.
 //
-// Layout: each thread moves UNROLL groups of 4 elements; within one group
+// Layout: each thread moves U groups of 4 elements (U = 4 for dequantize); within one group
 // instruction the 64 lanes of a wave touch 64 consecutive groups, so every
 // global load and store instruction is fully coalesced (1 KiB of fp32 and
 // 256 B of int8 per wave per instruction).  All loads of a thread are issued
-// before any arithmetic so each wave keeps UNROLL requests in flight.
+// before any arithmetic so each wave keeps U requests in flight.
+#include <cstdlib>
+
 #include "q8ta_internal.h"
 
 namespace q8ta {
@@ -20,7 +22,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
-constexpr int64_t kGroupsPerBlock = (int64_t)kThreads * kUnroll;
 
 __device__ __forceinline__ int quant1(float x, float inv, float zp) {
   float t = x * inv;
@@ -33,21 +34,22 @@ __device__ __forceinline__ int quant1(float x, float inv, float zp) {
 
 // x: fp32, 16-byte aligned; out: int8, 4-byte aligned.  n4 = numel / 4 groups;
 // block 0 also converts the numel % 4 trailing elements one by one.
+template <int U>
 __global__ __launch_bounds__(kThreads) void k_quantize_x4(const v4f* __restrict__ x,
                                                           uint32_t* __restrict__ out, int64_t n4,
                                                           int64_t numel, float inv, float zp) {
-  const int64_t base = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x;
-  if (base + (kUnroll - 1) * kThreads < n4) {
-    v4f v[kUnroll];
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U) + threadIdx.x;
+  if (base + (U - 1) * kThreads < n4) {
+    v4f v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(&x[base + u * kThreads]);
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&x[base + u * kThreads]);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       out[base + u * kThreads] = pack4(quant1(v[u].x, inv, zp), quant1(v[u].y, inv, zp),
                                        quant1(v[u].z, inv, zp), quant1(v[u].w, inv, zp));
   } else {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       int64_t c = base + u * kThreads;
       if (c < n4) {
         v4f v = x[c];
@@ -87,6 +89,7 @@ __device__ __forceinline__ v4f dequant4(uint32_t p, float scale, int zp) {
 __global__ __launch_bounds__(kThreads) void k_dequantize_x4(const uint32_t* __restrict__ x,
                                                             v4f* __restrict__ out, int64_t n4,
                                                             int64_t numel, float scale, int zp) {
+  constexpr int64_t kGroupsPerBlock = (int64_t)kThreads * kUnroll;
   const int64_t base = (int64_t)blockIdx.x * kGroupsPerBlock + threadIdx.x;
   if (base + (kUnroll - 1) * kThreads < n4) {
     uint32_t v[kUnroll];
@@ -121,17 +124,28 @@ __global__ __launch_bounds__(kThreads) void k_dequantize_x1(const int8_t* __rest
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+template <int U>
+void launch_quantize_u(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
+                       hipStream_t s) {
+  const int64_t n4 = numel / 4;
+  int64_t blocks = (n4 + (int64_t)kThreads * U - 1) / ((int64_t)kThreads * U);
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_quantize_x4<U>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     reinterpret_cast<const v4f*>(x), reinterpret_cast<uint32_t*>(out), n4, numel,
+                     inv_scale, zp);
+}
+
 }  // namespace
 
+// Q8TA_QUANT_UNROLL = 2 | 4 | 8 groups of 4 elements per thread (default 4).
 hipError_t launch_quantize(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
                            hipStream_t s) {
   if (aligned(x, 16) && aligned(out, 4)) {
-    int64_t n4 = numel / 4;
-    int64_t blocks = (n4 + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(k_quantize_x4, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const v4f*>(x), reinterpret_cast<uint32_t*>(out), n4,
-                       numel, inv_scale, zp);
+    int u = 4;
+    if (const char* e = getenv("Q8TA_QUANT_UNROLL")) u = atoi(e);
+    if (u == 2) launch_quantize_u<2>(x, out, numel, inv_scale, zp, s);
+    else if (u == 8) launch_quantize_u<8>(x, out, numel, inv_scale, zp, s);
+    else launch_quantize_u<4>(x, out, numel, inv_scale, zp, s);
   } else {
     int64_t blocks = (numel + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(k_quantize_x1, dim3((unsigned)blocks), dim3(kThreads), 0, s, x, out, numel,
@@ -144,7 +158,7 @@ hipError_t launch_dequantize(const int8_t* x, float* out, int64_t numel, float s
                              hipStream_t s) {
   if (aligned(x, 4) && aligned(out, 16)) {
     int64_t n4 = numel / 4;
-    int64_t blocks = (n4 + kGroupsPerBlock - 1) / kGroupsPerBlock;
+    int64_t blocks = (n4 + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(k_dequantize_x4, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        reinterpret_cast<const uint32_t*>(x), reinterpret_cast<v4f*>(out), n4,

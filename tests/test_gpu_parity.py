@@ -73,6 +73,17 @@ def test_quantize_ragged(numel, offset):
     np.testing.assert_array_equal(host(ob[offset:]), oracle.quantize_per_tensor(x, 0.02, 3))
 
 
+@pytest.mark.parametrize("unroll", ["2", "4", "8"])
+@pytest.mark.parametrize("numel", [5, 4096 + 13, 300001, 2 * 256 * 8 * 4 + 7])
+def test_quantize_every_unroll(unroll, numel):
+    _say(f"quantize unroll={unroll} numel={numel}")
+    x = (qi.rng(numel + 17).standard_normal(numel) * 3).astype(np.float32)
+    ob = torch.zeros(numel, dtype=torch.int8, device="cuda")
+    with env(Q8TA_QUANT_UNROLL=unroll):
+        q8.q8ta_quantize_per_tensor(dev(x), ob, 0.02, 3)
+    np.testing.assert_array_equal(host(ob), oracle.quantize_per_tensor(x, 0.02, 3))
+
+
 def test_quantize_ties_and_saturation():
     import json
     cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quantize_hand.json")))["cases"]
@@ -187,8 +198,9 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
 
 
-@pytest.mark.parametrize("cfg", ["G4S:16", "G4S:16x", "G4S:1", "G4S:3x", "G2S:8", "G2P:8", "G2P:3x",
-                                 "4S:32", "4S:32x", "4S:1", "4S:3x", "2S:8", "2P:8", "2P:3x"])
+@pytest.mark.parametrize("cfg", ["4S.16x2:16", "4S.16x2:16x", "4S.16x2:1", "4S.16x2:3x",
+                                 "4S.8x2:16x", "4S.8x2:1", "4S.8x4:3x", "4S.4x4:8x", "4S.4x4:1",
+                                 "2S.16x2:8", "2P.16x2:3x", "2S.8x2:8x", "2P.8x2:1"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (17, 4096, 40), (512, 2048, 768)])
 def test_linear_every_dot4_variant(cfg, M, K, N):
     _say(f"dot4 gemm cfg={cfg} M={M} K={K} N={N}")
