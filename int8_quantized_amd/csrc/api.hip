@@ -8,7 +8,10 @@
 #include <cstdio>
 #include <cstring>
 
+#include <cstdlib>
+
 #include "../../include/q8ta.h"
+
 #include "q8ta_internal.h"
 
 using namespace q8ta;
@@ -93,8 +96,17 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   return launch_linear_generic(a, s);
 }
 
+// The implicit GEMM (three launches' worth of fixed cost: input copy, then the
+// GEMM) pays off from about 2^28 multiply-adds; smaller problems take the
+// direct tiled kernel.  Q8TA_DECONV_PATH = igemm | dot4 forces either one
+// where the shape allows it (used by the tests).
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
   if (deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
+  const char* e = getenv("Q8TA_DECONV_PATH");
+  const double macs = (double)a.N * a.OC * a.H_out * a.W_out * a.IC * a.Kh * a.Kw /
+                      ((double)a.sh * a.sw);
+  const bool want_igemm = e ? e[0] == 'i' : macs >= (double)(1 << 28);
+  if (want_igemm && deconv_igemm_supported(a)) return launch_deconv_igemm(a, s);
   if (deconv_dot4_supported(a)) return launch_deconv_dot4(a, s);
   return launch_deconv_generic(a, s);
 }

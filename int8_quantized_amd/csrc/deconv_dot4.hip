@@ -35,17 +35,6 @@ constexpr int kThreads = 256;
 // address space lets the compiler fetch wave-uniform words with scalar loads.
 typedef const __attribute__((address_space(4))) int32_t* cwptr;
 
-constexpr int kMaxS = 8;    // largest stride taken
-constexpr int kMaxT = 16;   // largest number of taps per residue
-
-struct Phases {
-  int nth[kMaxS], thk[kMaxS][kMaxT], thd[kMaxS][kMaxT];
-  int ntw[kMaxS], twk[kMaxS][kMaxT], twd[kMaxS][kMaxT];
-  int jb;     // blocks of 64 phase columns
-  int ib;     // blocks of RQ phase rows
-  int ocb;    // blocks of OCB output channels
-};
-
 template <int OCB, int RQ>
 __global__ __launch_bounds__(kThreads) void k_deconv_dot4(DeconvArgs a, Phases p) {
   const int lane = threadIdx.x & 63;
@@ -347,6 +336,8 @@ __global__ __launch_bounds__(kThreads) void k_deconv_dot4_blocked(DeconvArgs a, 
 
 int floordiv(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
 
+}  // namespace
+
 bool make_phases(const DeconvArgs& a, Phases& p) {
   if (a.sh > kMaxS || a.sw > kMaxS || a.ph > (1 << 20) || a.pw > (1 << 20)) return false;
   p = Phases{};
@@ -378,6 +369,8 @@ bool make_phases(const DeconvArgs& a, Phases& p) {
   p.jb = (int)((Wp + 63) / 64);
   return true;
 }
+
+namespace {
 
 template <int OCB, int RQ>
 hipError_t launch_t(const DeconvArgs& a, Phases p, hipStream_t s) {

@@ -78,19 +78,6 @@ __global__ __launch_bounds__(kThreads) void k_row_sums(const int8_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// One butterfly step over HALF value pairs: keep the upper or lower half by
-// `upper`, receive the partner's copy of the kept half and add it.
-template <int HALF, int CTRL>
-__device__ __forceinline__ void fold(int32_t (&acc)[64], bool upper) {
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    const int32_t lo = acc[i], hi = acc[i + HALF];
-    const int32_t keep = upper ? hi : lo;
-    const int32_t send = upper ? lo : hi;
-    acc[i] = keep + row_move<CTRL>(send);
-  }
-}
-
 // Loads one slice for a group: row r of the weights is read at
 // p.w[r] + (woff + k) and row m of the activations at p.x[m] + (xoff + k):
 // the row pointers are wave-uniform (scalar registers) and the
@@ -100,15 +87,6 @@ __device__ __forceinline__ void fold(int32_t (&acc)[64], bool upper) {
 // loop does not turn the offsets into per-row 64-bit induction variables.
 // Unless FULL, rows at or past nrem / mrem (counted from the group's first
 // row) and lanes with `kin` false read zeros.
-typedef const __attribute__((address_space(1))) int8_t* gptr;
-
-__device__ __forceinline__ gptr uniform_ptr(const int8_t* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (gptr)(((uint64_t)hi << 32) | lo);
-}
-
 // Row pointers of a wave's 8 weight rows and 8 activation rows (wave-uniform,
 // kept in scalar registers; the empty asm makes each one opaque so that the
 // compiler does not fold the lane offset into a per-row 64-bit vector add).
@@ -153,25 +131,6 @@ __device__ __forceinline__ void dot_slice_mn(const Slice<LW>& s, int32_t (&acc)[
       for (int n = 0; n < 8; ++n)
         acc[m * 8 + n] = __builtin_amdgcn_sdot4(s.x[m][d], s.w[n][d], acc[m * 8 + n], false);
     }
-  }
-}
-
-// Butterfly over the LPG lanes of a group: 64 values -> 64/LPG values.
-template <int LPG>
-__device__ __forceinline__ void reduce_group(int32_t (&acc)[64], int lg) {
-  if constexpr (LPG == 16) {
-    fold<32, kDppMirror16>(acc, (lg & 8) != 0);
-    fold<16, kDppMirror8>(acc, (lg & 4) != 0);
-    fold<8, kDppRev4>(acc, (lg & 2) != 0);
-    fold<4, kDppSwap1>(acc, (lg & 1) != 0);
-  } else if constexpr (LPG == 8) {
-    fold<32, kDppMirror8>(acc, (lg & 4) != 0);
-    fold<16, kDppRev4>(acc, (lg & 2) != 0);
-    fold<8, kDppSwap1>(acc, (lg & 1) != 0);
-  } else {
-    static_assert(LPG == 4, "LPG");
-    fold<32, kDppRev4>(acc, (lg & 2) != 0);
-    fold<16, kDppSwap1>(acc, (lg & 1) != 0);
   }
 }
 

@@ -65,6 +65,51 @@ __device__ __forceinline__ int32_t wave_total(int32_t v) {
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
+// Transposing butterfly of the register-tiled contractions: a lane holds 64
+// partial sums of an 8 x 8 tile and the LPG lanes of a group (inside one DPP
+// row) together cover the whole K range.  One step over HALF value pairs: keep
+// the upper or lower half by `upper`, receive the partner's copy of the kept
+// half and add it.
+template <int HALF, int CTRL>
+__device__ __forceinline__ void fold(int32_t (&acc)[64], bool upper) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const int32_t lo = acc[i], hi = acc[i + HALF];
+    const int32_t keep = upper ? hi : lo;
+    const int32_t send = upper ? lo : hi;
+    acc[i] = keep + row_move<CTRL>(send);
+  }
+}
+
+// Butterfly over the LPG lanes of a group: 64 values -> 64/LPG values.
+template <int LPG>
+__device__ __forceinline__ void reduce_group(int32_t (&acc)[64], int lg) {
+  if constexpr (LPG == 16) {
+    fold<32, kDppMirror16>(acc, (lg & 8) != 0);
+    fold<16, kDppMirror8>(acc, (lg & 4) != 0);
+    fold<8, kDppRev4>(acc, (lg & 2) != 0);
+    fold<4, kDppSwap1>(acc, (lg & 1) != 0);
+  } else if constexpr (LPG == 8) {
+    fold<32, kDppMirror8>(acc, (lg & 4) != 0);
+    fold<16, kDppRev4>(acc, (lg & 2) != 0);
+    fold<8, kDppSwap1>(acc, (lg & 1) != 0);
+  } else {
+    static_assert(LPG == 4, "LPG");
+    fold<32, kDppRev4>(acc, (lg & 2) != 0);
+    fold<16, kDppSwap1>(acc, (lg & 1) != 0);
+  }
+}
+
+// Global pointer kept in scalar registers (wave-uniform).
+typedef const __attribute__((address_space(1))) int8_t* gptr;
+
+__device__ __forceinline__ gptr uniform_ptr(const int8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (gptr)(((uint64_t)hi << 32) | lo);
+}
+
 // ---- launchers (host functions; each returns hipGetLastError() after launch)
 hipError_t launch_quantize(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
                            hipStream_t s);
@@ -99,6 +144,22 @@ struct DeconvArgs {
 };
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s);
 
+// Stride phases of a transposed conv, built on the host: for row residue r
+// (output rows oh = r + s_h*i) the nth[r] qualifying kernel rows thk[r][t] read
+// input rows ih = i + thd[r][t]; likewise for columns.  jb, ib and ocb are tile
+// counts filled in by the launchers that use them.
+constexpr int kMaxS = 8;    // largest stride taken
+constexpr int kMaxT = 16;   // largest number of taps per residue
+struct Phases {
+  int nth[kMaxS], thk[kMaxS][kMaxT], thd[kMaxS][kMaxT];
+  int ntw[kMaxS], twk[kMaxS][kMaxT], twd[kMaxS][kMaxT];
+  int jb;     // blocks of 64 phase columns
+  int ib;     // blocks of phase rows
+  int ocb;    // blocks of output channels
+};
+// False when a stride or a residue's tap count exceeds the limits above.
+bool make_phases(const DeconvArgs& a, Phases& p);
+
 // Individual paths (used by the dispatchers above).
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
@@ -112,5 +173,7 @@ hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);
 hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s);
 bool deconv_dot4_supported(const DeconvArgs& a);
+hipError_t launch_deconv_igemm(const DeconvArgs& a, hipStream_t s);
+bool deconv_igemm_supported(const DeconvArgs& a);
 
 }  // namespace q8ta

@@ -362,6 +362,38 @@ def test_deconv_parity(case):
     np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
+# Shapes for the implicit-GEMM path (IC a multiple of 64): zero-point border on
+# every side, output channels not a multiple of 32, phases without taps, tall
+# and wide inputs, explicit (cropped) output sizes.
+DECONV_IGEMM_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, H_out, W_out, ldw_extra
+    (1, 64, 5, 7, 32, 4, 4, (2, 2), (1, 1), (0, 0), None, None, 0),
+    (2, 64, 6, 5, 40, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 16),
+    (1, 128, 4, 9, 64, 3, 3, (1, 1), (1, 1), (0, 0), None, None, 0),
+    (1, 64, 3, 4, 96, 5, 3, (3, 2), (2, 0), (0, 0), None, None, 0),
+    (1, 64, 7, 3, 8, 3, 5, (2, 3), (0, 2), (1, 1), None, None, 0),
+    (1, 64, 33, 5, 33, 4, 4, (2, 2), (1, 1), (0, 0), None, None, 0),
+    (1, 64, 4, 40, 32, 2, 2, (2, 2), (0, 0), (0, 0), None, None, 0),
+    (1, 64, 3, 3, 16, 1, 1, (4, 4), (0, 0), (3, 3), None, None, 0),
+    (1, 64, 5, 5, 32, 3, 3, (2, 2), (1, 1), (1, 1), 7, 6, 0),
+    (3, 192, 9, 70, 130, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 64),
+]
+
+
+@pytest.mark.parametrize("case", DECONV_IGEMM_CASES,
+                         ids=[str(i) for i in range(len(DECONV_IGEMM_CASES))])
+@pytest.mark.parametrize("path", ["igemm:4x4", "igemm:4x8", "dot4:"])
+def test_deconv_igemm_parity(case, path):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
+    _say(f"deconv {path} case={case}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 1, N, IC, H, W, OC, Kh, Kw, s, p, op,
+                       H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra)
+    kind, layout = path.split(":")
+    with env(Q8TA_DECONV_PATH=kind, Q8TA_IGEMM_CFG=layout or "4x4"):
+        np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+        np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
 @pytest.mark.skip(reason=MFMA_OFF)
 @pytest.mark.parametrize("fj,fo,wi", [(1, 1, 1), (2, 4, 2), (4, 2, 1), (4, 4, 4), (1, 4, 3)])
 def test_deconv_every_tile(fj, fo, wi):
@@ -384,7 +416,8 @@ def test_deconv_every_dot4_variant(variant, case):
     _say(f"deconv dot4 variant={variant} case={case}")
     c = qi.deconv_case(7 + int(ocb) + int(rq), N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho,
                        W_out=Wo, ldw=Kh * Kw * IC + extra)
-    with env(Q8TA_DECONV_LAYOUT=layout, Q8TA_DECONV_OCB=ocb, Q8TA_DECONV_RQ=rq):
+    with env(Q8TA_DECONV_PATH="dot4", Q8TA_DECONV_LAYOUT=layout, Q8TA_DECONV_OCB=ocb,
+             Q8TA_DECONV_RQ=rq):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
