@@ -8,9 +8,10 @@ The default workload is the large linear:
 `value` is 2*M*N*K int8 operations per step divided by the step time (TOPS).
 
 The JSON line also carries
-  roofline      the GEMM kernel's own rate (HIP events around each launch in
-                the timed region, on the stream it runs on) against the dense
-                int8 MFMA peak;
+  roofline      the GEMM call's own rate (HIP events around each call in the
+                timed region, on the stream it runs on) against the v_dot4
+                vector-ALU peak it is bound by (and, beside it, the fraction
+                of the dense int8 MFMA peak);
   cpu_baseline  the CPU oracle timed on a sample of the same workload
                 (a block of rows; the GPU's rows are compared with it);
   extra         the other workloads of the op family, each timed with events:
@@ -18,7 +19,8 @@ The JSON line also carries
                 HBM-bound kernels rotate through enough buffer copies to
                 exceed the 256 MB last-level cache.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                       [--profile-only gemm-and-copy|deconv]
 """
 from __future__ import annotations
 
@@ -226,10 +228,11 @@ def main():
     log(f"step {step_s * 1e6:.1f} us; GEMM avg {gemm_avg_s * 1e6:.1f} us "
         f"(min {min(gemm_ms) * 1e3:.1f}) = {achieved:.1f} TOPS")
 
-    # The matrix-core GEMM is switched off in this build; q8ta_linear with M > 4
-    # runs the vector-ALU v_dot4 kernel, whose own ceiling is PEAK_DOT4_TOPS.
+    # The matrix-core GEMM is switched off; q8ta_linear with M > 4 runs the
+    # vector-ALU v_dot4 kernel, whose own ceiling is PEAK_DOT4_TOPS.
     roofline = {
-        "bound": "alu", "kernel": "k_dot4_gemm<8,8> (v_dot4_i32_i8, vector ALU)",
+        "bound": "alu",
+        "kernel": "k_row_sums + k_dot4_gemm<4,false,4,4> (v_dot4_i32_i8, vector ALU)",
         "achieved": round(achieved, 2), "peak": round(PEAK_DOT4_TOPS, 1), "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_DOT4_TOPS, 4),
         "frac_of_int8_mfma_peak": round(achieved / PEAK_INT8_TOPS, 5),
