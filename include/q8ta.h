@@ -14,11 +14,15 @@
  *     tensors are plain byte arrays (element i at byte i).
  *   - Workspace: on their register-tiled paths, q8ta_linear / q8ta_linear_acc
  *     with M > 4 (K % 16 == 0, 16-byte aligned x and weight) take 4*N bytes
- *     (weight row sums), and q8ta_conv2d_transposed(_acc) (IC % 4 == 0) takes
- *     N*H_in*ceil(IC/16)*W_in*16 bytes (a channel-blocked copy of the input)
- *     from the stream-ordered allocator (hipMallocAsync on `stream`, released
- *     with hipFreeAsync on the same stream after the kernels that use it).
- *     A failed allocation returns Q8TA_ERR_HIP and launches nothing.
+ *     (weight row sums); q8ta_conv2d_transposed(_acc) takes, on its
+ *     implicit-GEMM path (IC % 64 == 0), an NHWC copy of the input inside a
+ *     zero-point border (N * IC * (H_in + a few rows) * (W_in + a few
+ *     columns) bytes) plus 4 * stride_h * stride_w * OC bytes of weight sums,
+ *     and on its direct tiled path (other IC % 4 == 0) a channel-blocked copy
+ *     of the input (N * H_in * ceil(IC/16) * W_in * 16 bytes).  Workspaces
+ *     come from the stream-ordered allocator (hipMallocAsync on `stream`,
+ *     released with hipFreeAsync on the same stream after the kernels that
+ *     use them); a failed allocation returns Q8TA_ERR_HIP.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns after the launch; results are visible to later work on that
  *     stream.  Calls are reentrant and keep no state between calls.
