@@ -8,7 +8,8 @@
  *   - "[WebGPU] Add q8ta_linear op (int8 quantized linear)" (#21197),
  *     Solution and Constraints sections;
  *   - "[WebGPU] Add q8ta_conv2d_transposed op (int8 transposed conv)" (#21205),
- *     Solution, Implementation and Constraints sections.
+ *     Solution, Implementation and Constraints sections (and the forward
+ *     q8ta_conv2d whose scaffold that page says the transposed op reuses).
  *
  * Only tests, the smoke check and the benchmark's CPU-baseline leg load this
  * library.  It shares no code, header or constant with the GPU library.
@@ -345,6 +346,75 @@ int oracle_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
   if (rc == ORACLE_OK && total > 0)
     rc = oracle_epilogue(acc, total, OC, H_out * W_out, input_scale, weight_scales,
                          bias, output_scale, output_zero_point, out, NULL);
+  if (!acc_out) free(acc);
+  return rc;
+}
+
+/* ---- forward q8ta_conv2d (the general int8 conv whose scaffold and
+ * [OC, Kh*Kw*IC] weight layout the transposed op reuses, #21205 Solution; the
+ * pages print only the transposed index relation, so the forward one is the
+ * standard convolution index):
+ * acc[n, oc, oh, ow] = sum over (ic, kh, kw) of
+ *     (x[n, ic, ih, iw] - input_zero_point) * w[oc, (kh*Kw + kw)*IC + ic]
+ * with ih = oh*stride_h - pad_h + kh*dil_h, used only when 0 <= ih < H_in
+ * (iw likewise).  x is NCHW [N, IC, H_in, W_in]; w is [OC, ldw]; acc is NCHW
+ * [N, OC, H_out, W_out] int32.  groups == 1. */
+int oracle_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
+                      int64_t W_in, int64_t input_zero_point, const int8_t* w,
+                      int64_t OC, int64_t Kh, int64_t Kw, int64_t ldw,
+                      int64_t stride_h, int64_t stride_w, int64_t pad_h,
+                      int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                      int64_t H_out, int64_t W_out, int32_t* acc) {
+  if (N < 0 || IC <= 0 || OC <= 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * IC ||
+      stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || H_out < 0 || W_out < 0)
+    return ORACLE_BAD_ARG;
+  int overflow = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : overflow)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t oc = 0; oc < OC; ++oc) {
+      for (int64_t oh = 0; oh < H_out; ++oh) {
+        for (int64_t ow = 0; ow < W_out; ++ow) {
+          int64_t s = 0;
+          for (int64_t ic = 0; ic < IC; ++ic) {
+            for (int64_t kh = 0; kh < Kh; ++kh) {
+              const int64_t ih = oh * stride_h - pad_h + kh * dil_h;
+              if (ih < 0 || ih >= H_in) continue;
+              for (int64_t kw = 0; kw < Kw; ++kw) {
+                const int64_t iw = ow * stride_w - pad_w + kw * dil_w;
+                if (iw < 0 || iw >= W_in) continue;
+                int64_t xv = x[((n * IC + ic) * H_in + ih) * W_in + iw];
+                int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];
+                s += (xv - input_zero_point) * wv;
+              }
+            }
+          }
+          if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+          acc[((n * OC + oc) * H_out + oh) * W_out + ow] = (int32_t)s;
+        }
+      }
+    }
+  }
+  return overflow ? ORACLE_OVERFLOW : ORACLE_OK;
+}
+
+/* Full q8ta_conv2d: contraction then the per-channel epilogue, channel = oc. */
+int oracle_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
+                  int64_t W_in, double input_scale, int64_t input_zero_point,
+                  const int8_t* w, int64_t OC, int64_t Kh, int64_t Kw, int64_t ldw,
+                  const float* weight_scales, const float* bias, double output_scale,
+                  int64_t output_zero_point, int64_t stride_h, int64_t stride_w,
+                  int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                  int64_t H_out, int64_t W_out, int8_t* out, int32_t* acc_out) {
+  if (N < 0 || OC <= 0 || H_out < 0 || W_out < 0) return ORACLE_BAD_ARG;
+  int64_t total = N * OC * H_out * W_out;
+  int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(total + 1));
+  if (!acc) return ORACLE_BAD_ARG;
+  int rc = oracle_conv2d_acc(x, N, IC, H_in, W_in, input_zero_point, w, OC, Kh, Kw, ldw,
+                             stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, H_out, W_out,
+                             acc);
+  if (rc == ORACLE_OK && total > 0)
+    rc = oracle_epilogue(acc, total, OC, H_out * W_out, input_scale, weight_scales, bias,
+                         output_scale, output_zero_point, out, NULL);
   if (!acc_out) free(acc);
   return rc;
 }

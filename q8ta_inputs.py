@@ -140,6 +140,38 @@ def deconv_case(seed: int, N: int, IC: int, H_in: int, W_in: int, OC: int, Kh: i
                       H_out, W_out, xf)
 
 
+def conv_out_size(in_size, k, s, p, d=1):
+    """Conventional convolution output size (PyTorch's formula)."""
+    return (in_size + 2 * p - d * (k - 1) - 1) // s + 1
+
+
+def conv_case(seed: int, N: int, IC: int, H_in: int, W_in: int, OC: int, Kh: int, Kw: int,
+              stride=(1, 1), padding=(1, 1), dilation=(1, 1), H_out=None, W_out=None, ldw=None,
+              with_bias=True, in_zp=IN_ZP, out_zp=OUT_ZP, x_from_fp32: bool = False,
+              in_scale: float = IN_SCALE) -> DeconvCase:
+    """Forward conv inputs, in the same container as the transposed conv's
+    (output_padding unused, (0, 0))."""
+    g = rng(seed)
+    if H_out is None:
+        H_out = conv_out_size(H_in, Kh, stride[0], padding[0], dilation[0])
+    if W_out is None:
+        W_out = conv_out_size(W_in, Kw, stride[1], padding[1], dilation[1])
+    ldw = Kh * Kw * IC if ldw is None else ldw
+    xf = None
+    if x_from_fp32:
+        xf = x_fp32(g, (N, IC, H_in, W_in))
+        x = np.zeros((N, IC, H_in, W_in), np.int8)   # filled by the caller's quantize
+    else:
+        x = x_int8(g, (N, IC, H_in, W_in))
+    w = w_int8(g, (OC, ldw))
+    ws = scales(g, OC)
+    b = bias(g, OC) if with_bias else None
+    kred = IC * Kh * Kw
+    return DeconvCase(x, w, ws, b, in_scale, in_zp, out_scale_for(kred, in_scale), out_zp,
+                      Kh, Kw, tuple(stride), tuple(padding), (0, 0), tuple(dilation),
+                      H_out, W_out, xf)
+
+
 # --- the five named workloads -------------------------------------------------
 @dataclass
 class Workload:

@@ -60,6 +60,17 @@ MUTANTS = [
     ("deconv_zp_sign", "s += (xv - input_zero_point) * wv;", "s += (xv + input_zero_point) * wv;", 0),
     ("deconv_pad_sign", "int64_t num = o + pad - k * dil;\n  if (num < 0)",
      "int64_t num = o - pad - k * dil;\n  if (num < 0)", 0),
+    ("conv_pad_sign", "const int64_t ih = oh * stride_h - pad_h + kh * dil_h;",
+     "const int64_t ih = oh * stride_h + pad_h + kh * dil_h;", 0),
+    ("conv_dilation_dropped", "const int64_t iw = ow * stride_w - pad_w + kw * dil_w;",
+     "const int64_t iw = ow * stride_w - pad_w + kw;", 0),
+    ("conv_stride_axis", "const int64_t iw = ow * stride_w - pad_w + kw * dil_w;",
+     "const int64_t iw = ow * stride_h - pad_w + kw * dil_w;", 0),
+    ("conv_last_column_dropped", "if (iw < 0 || iw >= W_in) continue;",
+     "if (iw < 0 || iw >= W_in - 1) continue;", 0),
+    ("conv_tap_order", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];\n                s +=",
+     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * IC + ic];\n                s +=", 1),
+    ("conv_zp_sign", "s += (xv - input_zero_point) * wv;", "s += (xv + input_zero_point) * wv;", 1),
 ]
 
 

@@ -386,3 +386,111 @@ def test_deconv_large_workload_output_size():
     c = qi.make_deconv_large()
     assert (c.H_out, c.W_out) == (128, 128)
     assert c.w.shape == (128, 9 * 256)
+
+
+# --------------------------------------------------------------------------- forward conv2d
+def _torch_conv2d_acc(x, w, zp, Kh, Kw, stride, padding, dilation):
+    """Exact float64 torch conv2d of (x - zp) with the weight reshape
+    w[oc, (kh*Kw+kw)*IC + ic] = orig[oc, ic, kh, kw] undone."""
+    N, IC, H, W = x.shape
+    OC = w.shape[0]
+    wo = torch.from_numpy(np.ascontiguousarray(w[:, :Kh * Kw * IC])).reshape(
+        OC, Kh, Kw, IC).permute(0, 3, 1, 2).contiguous().double()
+    xs = torch.from_numpy(x).double() - zp
+    return F.conv2d(xs, wo, stride=stride, padding=padding, dilation=dilation).numpy()
+
+
+def test_conv2d_hand_cases():
+    for c in _gold("conv2d_hand.json")["cases"]:
+        x = np.array(c["x"], np.int8).reshape(c["N"], c["IC"], c["H_in"], c["W_in"])
+        w = np.array(c["w"], np.int8).reshape(c["OC"], -1)
+        acc = oracle.conv2d_acc(x, w, c["zp"], c["Kh"], c["Kw"], c["stride"], c["pad"], c["dil"],
+                                c["H_out"], c["W_out"])
+        np.testing.assert_array_equal(acc.reshape(-1), np.array(c["acc"]), err_msg=c["name"])
+
+
+CONV2D_SHAPES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, dil
+    (1, 5, 7, 6, 3, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (2, 4, 9, 8, 5, 3, 3, (2, 2), (1, 1), (1, 1)),
+    (1, 3, 8, 9, 2, 5, 3, (2, 3), (2, 0), (1, 1)),
+    (1, 3, 9, 7, 4, 3, 2, (1, 2), (0, 1), (2, 3)),
+    (1, 2, 5, 5, 3, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 2, 4, 5, 2, 3, 3, (1, 1), (4, 3), (1, 1)),      # pad larger than the kernel
+    (2, 3, 6, 6, 2, 4, 4, (3, 3), (1, 2), (1, 1)),
+]
+
+
+@pytest.mark.parametrize("shape", CONV2D_SHAPES)
+def test_conv2d_matches_torch_conv2d(shape):
+    N, IC, H, W, OC, Kh, Kw, s, p, d = shape
+    g = qi.rng(sum(shape[:7]) + 1)
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = g.integers(-128, 128, size=(OC, Kh * Kw * IC), dtype=np.int8)
+    ref = _torch_conv2d_acc(x, w, -5, Kh, Kw, s, p, d)
+    H_out, W_out = ref.shape[2:]
+    assert H_out == qi.conv_out_size(H, Kh, s[0], p[0], d[0])
+    assert W_out == qi.conv_out_size(W, Kw, s[1], p[1], d[1])
+    acc = oracle.conv2d_acc(x, w, -5, Kh, Kw, s, p, d, H_out, W_out)
+    np.testing.assert_array_equal(acc, ref.astype(np.int32))
+
+
+def test_conv2d_brute_force_tiny():
+    """Pure-Python loops over the definition on a tiny input."""
+    g = qi.rng(77)
+    N, IC, H, W, OC, Kh, Kw, s, p, d, zp = 1, 2, 4, 5, 2, 2, 3, (2, 1), (1, 1), (1, 2), 7
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, Kh * Kw * IC + 3))
+    Ho, Wo = qi.conv_out_size(H, Kh, s[0], p[0], d[0]), qi.conv_out_size(W, Kw, s[1], p[1], d[1])
+    ref = np.zeros((N, OC, Ho, Wo), np.int64)
+    for n in range(N):
+        for oc in range(OC):
+            for oh in range(Ho):
+                for ow in range(Wo):
+                    t = 0
+                    for ic in range(IC):
+                        for kh in range(Kh):
+                            for kw in range(Kw):
+                                ih, iw = oh * s[0] - p[0] + kh * d[0], ow * s[1] - p[1] + kw * d[1]
+                                if 0 <= ih < H and 0 <= iw < W:
+                                    t += (int(x[n, ic, ih, iw]) - zp) * int(w[oc, (kh * Kw + kw) * IC + ic])
+                    ref[n, oc, oh, ow] = t
+    np.testing.assert_array_equal(oracle.conv2d_acc(x, w, zp, Kh, Kw, s, p, d, Ho, Wo), ref)
+
+
+def test_conv2d_is_the_adjoint_of_the_transposed_conv():
+    """<conv2d(x - zp), y> == <x - zp, conv_transpose(y)> with the channel axes
+    of the weight swapped: ties the forward oracle to the (separately pinned)
+    transposed one; integers, exact in int64."""
+    g = qi.rng(78)
+    N, IC, H, W, OC, Kh, Kw, s, p, d = 2, 5, 9, 8, 4, 3, 2, (2, 3), (1, 1), (1, 2)
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, Kh * Kw * IC))
+    Ho, Wo = qi.conv_out_size(H, Kh, s[0], p[0], d[0]), qi.conv_out_size(W, Kw, s[1], p[1], d[1])
+    acc = oracle.conv2d_acc(x, w, 3, Kh, Kw, s, p, d, Ho, Wo).astype(np.int64)
+    y = qi.x_int8(g, (N, OC, Ho, Wo))
+    wt = w.reshape(OC, Kh * Kw, IC).transpose(2, 1, 0).reshape(IC, Kh * Kw * OC)
+    back = oracle.deconv_acc(y, wt, 0, Kh, Kw, s, p, d, H, W).astype(np.int64)
+    lhs = int((acc * y.astype(np.int64)).sum())
+    rhs = int(((x.astype(np.int64) - 3) * back).sum())
+    assert lhs == rhs
+
+
+def test_conv2d_1x1_stride1_is_linear_on_nhwc():
+    g = qi.rng(79)
+    N, IC, H, W, OC = 2, 40, 3, 5, 24
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, IC))
+    acc = oracle.conv2d_acc(x, w, 3, 1, 1, (1, 1), (0, 0), (1, 1), H, W)
+    lin = oracle.linear_acc(x.transpose(0, 2, 3, 1).reshape(-1, IC), w, 3)
+    np.testing.assert_array_equal(acc.transpose(0, 2, 3, 1).reshape(-1, OC), lin)
+
+
+def test_conv2d_epilogue_matches_the_shared_epilogue():
+    c = qi.conv_case(80, 2, 6, 7, 5, 5, 3, 3, (2, 2), (1, 1), (1, 1))
+    q, acc = oracle.conv2d(c.x, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                           c.out_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out,
+                           return_acc=True)
+    ref = oracle.epilogue(acc, c.w.shape[0], c.H_out * c.W_out, c.in_scale, c.weight_scales,
+                          c.bias, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(q, ref)
