@@ -67,6 +67,17 @@ def deconv_ops(c):
     return 2 * N * OC * IC * th * tw
 
 
+def conv_ops(c):
+    """Exact int8 ops of the forward conv: taps inside the input only."""
+    N, IC, H, W = c.x.shape
+    OC = c.w.shape[0]
+    th = sum(1 for oh in range(c.H_out) for k in range(c.Kh)
+             if 0 <= oh * c.stride[0] - c.padding[0] + k * c.dilation[0] < H)
+    tw = sum(1 for ow in range(c.W_out) for k in range(c.Kw)
+             if 0 <= ow * c.stride[1] - c.padding[1] + k * c.dilation[1] < W)
+    return 2 * N * OC * IC * th * tw
+
+
 def file_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -408,6 +419,7 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     r = summary(timer.time_calls(dfns, 4 * copies), dops, "TOPS", PEAK_INT8_TOPS)
     r["exact_valid_tap_ops"] = dops
     r["algorithmic_bytes"] = int(numel + d.w.size + 8 * OC + dout.numel())
+    r["frac_of_dot4_peak"] = round(r["rate"] / PEAK_DOT4_TOPS, 4)
     res["deconv_8x256x64x64_k3s2p1_to_8x128x128x128"] = r
     del qs, dfns
 
@@ -460,6 +472,28 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     r = summary(timer.time_calls([dc_small], reps), deconv_ops(d4), "TOPS", PEAK_INT8_TOPS)
     r["exact_valid_tap_ops"] = deconv_ops(d4)
     res["deconv_1x64x32x32_k4s2p1_to_1x32x64x64"] = r
+
+    # ---- forward conv [8,256,64,64] K3 s1 p1 -> [8,128,64,64] (implicit GEMM)
+    log("extra: conv2d [8,256,64,64] -> [8,128,64,64]")
+    cc = qi.make_conv2d_large()
+    cx, cw = torch.from_numpy(cc.x).cuda(), torch.from_numpy(cc.w).cuda()
+    cs, cb = torch.from_numpy(cc.weight_scales).cuda(), torch.from_numpy(cc.bias).cuda()
+    cN, cIC, cH, cW = cc.x.shape
+    cOC = cc.w.shape[0]
+    cout = torch.empty((cN, cOC, cc.H_out, cc.W_out), dtype=torch.int8, device="cuda")
+
+    def conv():
+        check(lib.q8ta_conv2d(
+            cx.data_ptr(), cN, cIC, cH, cW, cc.in_scale, cc.in_zp, cw.data_ptr(), cOC, cc.Kh,
+            cc.Kw, cc.w.shape[1], None, cs.data_ptr(), cb.data_ptr(), cc.out_scale, cc.out_zp,
+            cc.stride[0], cc.stride[1], cc.padding[0], cc.padding[1], cc.dilation[0],
+            cc.dilation[1], 1, b"none", cout.data_ptr(), cc.H_out, cc.W_out, stream))
+    timer.time_calls([conv], 5)
+    cops = conv_ops(cc)
+    r = summary(timer.time_calls([conv], reps), cops, "TOPS", PEAK_INT8_TOPS)
+    r["exact_valid_tap_ops"] = cops
+    r["frac_of_dot4_peak"] = round(r["rate"] / PEAK_DOT4_TOPS, 4)
+    res["conv2d_8x256x64x64_k3s1p1_to_8x128x64x64"] = r
     for k, v in res.items():
         log(f"  {k}: {v}")
     return res

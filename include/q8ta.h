@@ -158,8 +158,39 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
                                    hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * q8ta_conv2d: the forward int8 convolution whose scaffold and weight layout
+ * the transposed op reuses ([DCV] Solution).  The pages print only the
+ * transposed index relation; the forward one is the standard convolution's:
+ *   acc[n,oc,oh,ow] = sum over (ic, kh, kw) of
+ *       (x[n,ic,ih,iw] - input_zero_point) * weight[oc, (kh*Kw + kw)*IC + ic]
+ *   with ih = oh*stride_h - pad_h + kh*dilation_h used only when
+ *   0 <= ih < H_in (iw likewise);  out[n,oc,oh,ow] = epilogue(acc), c = oc.
+ * Layouts, scales, bias, weight_row_stride and the epilogue as for
+ * q8ta_conv2d_transposed; H_out / W_out are given explicitly (any sizes >= 1).
+ * Requirements: all sizes >= 1, stride >= 1, padding >= 0, dilation in
+ * [1, 4096]; groups must be 1 (grouped and depthwise convolutions are not
+ * implemented: Q8TA_ERR_UNSUPPORTED); activation must be "none".
+ * weight_sums is ignored.  Workspace on the implicit-GEMM path (IC % 64 ==
+ * 0): an NHWC copy of the input inside a zero-point border plus 4 * OC bytes.
+ */
+q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC,
+                        int64_t H_in, int64_t W_in,
+                        double input_scale, int64_t input_zero_point,
+                        const int8_t* weight, int64_t OC,
+                        int64_t Kh, int64_t Kw, int64_t weight_row_stride,
+                        const int32_t* weight_sums,
+                        const float* weight_scales, const float* bias,
+                        double output_scale, int64_t output_zero_point,
+                        int64_t stride_h, int64_t stride_w,
+                        int64_t pad_h, int64_t pad_w,
+                        int64_t dilation_h, int64_t dilation_w,
+                        int64_t groups, const char* activation,
+                        int8_t* out, int64_t H_out, int64_t W_out,
+                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Accumulator outputs (for verification).  These run the same contraction
- * kernels as q8ta_linear / q8ta_conv2d_transposed but store the int32
+ * kernels as q8ta_linear / q8ta_conv2d_transposed / q8ta_conv2d but store the int32
  * accumulator (the sum above, zero-point term included) instead of the
  * requantized int8 value.  acc: int32 [M, N] row-major, or NCHW
  * [N, OC, H_out, W_out].  Argument checks as for the parent op.
@@ -179,6 +210,17 @@ q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC,
                                        int64_t pad_h, int64_t pad_w,
                                        int32_t* acc, int64_t H_out, int64_t W_out,
                                        hipStream_t stream);
+
+q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC,
+                            int64_t H_in, int64_t W_in,
+                            int64_t input_zero_point,
+                            const int8_t* weight, int64_t OC,
+                            int64_t Kh, int64_t Kw, int64_t weight_row_stride,
+                            int64_t stride_h, int64_t stride_w,
+                            int64_t pad_h, int64_t pad_w,
+                            int64_t dilation_h, int64_t dilation_w,
+                            int32_t* acc, int64_t H_out, int64_t W_out,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -55,6 +55,11 @@ SIGNATURES = {
     "q8ta_linear_acc": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
     "q8ta_conv2d_transposed_acc": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64,
                                     _I64, _I64, _I64, _I64, _P, _I64, _I64, _P], ctypes.c_int),
+    "q8ta_conv2d": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64, _I64, _I64,
+                     _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                     _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
+    "q8ta_conv2d_acc": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64,
+                         _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P], ctypes.c_int),
 }
 
 _lib = None
@@ -224,8 +229,48 @@ def q8ta_conv2d_transposed_acc(x, input_zero_point, weight, Kh, Kw, stride, padd
     return acc
 
 
+def q8ta_conv2d(x, input_scale, input_zero_point, weight, Kh, Kw, weight_sums, weight_scales,
+                bias, output_scale, output_zero_point, stride, padding, dilation, groups,
+                activation, out, stream=None):
+    """Forward conv: int8 NCHW x int8 [OC, ldw] -> int8 NCHW out (H_out, W_out
+    taken from out)."""
+    torch = _torch()
+    if x.dim() != 4 or weight.dim() != 2 or out.dim() != 4:
+        raise ValueError("x [N,IC,H,W], weight [OC, ldw] and out [N,OC,H_out,W_out] expected")
+    N, IC, H_in, W_in = x.shape
+    OC, ldw = weight.shape
+    if out.shape[0] != N or out.shape[1] != OC:
+        raise ValueError("out must be [N, OC, H_out, W_out]")
+    _check(lib().q8ta_conv2d(
+        _dev(x, torch.int8, "x"), N, IC, H_in, W_in, float(input_scale), int(input_zero_point),
+        _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw,
+        _opt(weight_sums, torch.int32, "weight_sums"),
+        _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+        float(output_scale), int(output_zero_point), int(stride[0]), int(stride[1]),
+        int(padding[0]), int(padding[1]), int(dilation[0]), int(dilation[1]), int(groups),
+        _act(activation), _dev(out, torch.int8, "out"), out.shape[2], out.shape[3],
+        _stream(stream)))
+    return out
+
+
+def q8ta_conv2d_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, dilation, acc,
+                    stream=None):
+    """int32 accumulator of q8ta_conv2d (NCHW [N, OC, H_out, W_out])."""
+    torch = _torch()
+    N, IC, H_in, W_in = x.shape
+    OC, ldw = weight.shape
+    if acc.dim() != 4 or acc.shape[0] != N or acc.shape[1] != OC:
+        raise ValueError("acc must be [N, OC, H_out, W_out]")
+    _check(lib().q8ta_conv2d_acc(
+        _dev(x, torch.int8, "x"), N, IC, H_in, W_in, int(input_zero_point),
+        _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw, int(stride[0]),
+        int(stride[1]), int(padding[0]), int(padding[1]), int(dilation[0]), int(dilation[1]),
+        _dev(acc, torch.int32, "acc"), acc.shape[2], acc.shape[3], _stream(stream)))
+    return acc
+
+
 __all__ = [
     "Q8taError", "lib", "q8ta_last_error", "q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor",
     "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_acc", "q8ta_conv2d_transposed",
-    "q8ta_conv2d_transposed_acc",
+    "q8ta_conv2d_transposed_acc", "q8ta_conv2d", "q8ta_conv2d_acc",
 ]

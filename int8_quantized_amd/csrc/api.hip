@@ -111,6 +111,12 @@ hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
   return launch_deconv_generic(a, s);
 }
 
+// Forward conv: the implicit GEMM (IC % 64 == 0) or the shape-general kernel.
+hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s) {
+  if (conv_igemm_supported(a)) return launch_conv_igemm(a, s);
+  return launch_conv2d_generic(a, s);
+}
+
 }  // namespace q8ta
 
 extern "C" {
@@ -254,6 +260,61 @@ q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC, i
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
   return hip_status(launch_deconv(a, stream), op);
+}
+
+
+q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, int64_t W_in,
+                        double input_scale, int64_t input_zero_point, const int8_t* weight,
+                        int64_t OC, int64_t Kh, int64_t Kw, int64_t weight_row_stride,
+                        const int32_t* weight_sums, const float* weight_scales, const float* bias,
+                        double output_scale, int64_t output_zero_point, int64_t stride_h,
+                        int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dilation_h,
+                        int64_t dilation_w, int64_t groups, const char* activation, int8_t* out,
+                        int64_t H_out, int64_t W_out, hipStream_t stream) {
+  const char* op = "q8ta_conv2d";
+  (void)weight_sums;
+  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
+                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out);
+  if (st) return st;
+  if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
+  if (dilation_h < 1 || dilation_w < 1 || dilation_h > 4096 || dilation_w > 4096)
+    return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
+  if (groups != 1)
+    return fail(Q8TA_ERR_UNSUPPORTED, "%s: groups must be 1 (got %lld)", op, (long long)groups);
+  if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
+  if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
+  if ((st = check_activation(op, activation))) return st;
+
+  DeconvArgs a{};
+  a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
+  a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
+  a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w;
+  a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
+  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  return hip_status(launch_conv2d(a, stream), op);
+}
+
+q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, int64_t W_in,
+                            int64_t input_zero_point, const int8_t* weight, int64_t OC, int64_t Kh,
+                            int64_t Kw, int64_t weight_row_stride, int64_t stride_h,
+                            int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dilation_h,
+                            int64_t dilation_w, int32_t* acc, int64_t H_out, int64_t W_out,
+                            hipStream_t stream) {
+  const char* op = "q8ta_conv2d_acc";
+  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
+                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out);
+  if (st) return st;
+  if (dilation_h < 1 || dilation_w < 1 || dilation_h > 4096 || dilation_w > 4096)
+    return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
+  if (!zp_ok(input_zero_point)) return fail(Q8TA_ERR_QPARAM, "%s: input_zero_point out of range", op);
+  DeconvArgs a{};
+  a.x = x; a.w = weight; a.acc = acc;
+  a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
+  a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w;
+  a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
+  return hip_status(launch_conv2d(a, stream), op);
 }
 
 }  // extern "C"

@@ -52,6 +52,11 @@ struct Plan {
   int nph;
   int pt, pl;               // zero-point border above / left of the input
   int Hpad, Wpad;           // padded NHWC height / width
+  // Geometry: phase (rh, rw) holds output pixels (rh + osh*i, rw + osw*j), and
+  // tap t of its row list reads input row i*ish + thd[rh][t] (columns
+  // likewise).  Transposed conv: osh/osw = stride, ish/isw = 1; forward conv:
+  // one phase, osh/osw = 1, ish/isw = stride.
+  int osh, osw, ish, isw;
 };
 
 // x NCHW -> xp, NHWC inside a zero-point border: xp[n][hp][wp][c] =
@@ -92,13 +97,14 @@ __device__ __forceinline__ void relayout_one(const int8_t* __restrict__ x, int8_
 
 // wsum[ph * OC + oc] = sum over the phase's taps and all ic of w[oc, tap, ic]:
 // one wave per (phase, channel), lanes split the (tap, ic) words.
-__device__ __forceinline__ void phase_wsum_one(const DeconvArgs& a, const Phases& p, int nph,
-                                               int32_t* __restrict__ wsum, int64_t id) {
+__device__ __forceinline__ void phase_wsum_one(const DeconvArgs& a, const Phases& p,
+                                               const Plan& plan, int32_t* __restrict__ wsum,
+                                               int64_t id) {
   const int lane = threadIdx.x & 63;
-  if (id >= (int64_t)nph * a.OC) return;
+  if (id >= (int64_t)plan.nph * a.OC) return;
   const int ph = (int)(id / a.OC);
   const int64_t oc = id % a.OC;
-  const int rh = ph / (int)a.sw, rw = ph % (int)a.sw;
+  const int rh = ph / plan.osw, rw = ph % plan.osw;
   const int IC = (int)a.IC;
   int32_t s = 0;
   for (int th = 0; th < p.nth[rh]; ++th)
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(DeconvArgs a, Phases p, Plan 
                  b * kThreads + threadIdx.x);
   } else {
     const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    phase_wsum_one(a, p, plan.nph, wsum, (b - relayout_blocks) * (kThreads / 64) + wave);
+    phase_wsum_one(a, p, plan, wsum, (b - relayout_blocks) * (kThreads / 64) + wave);
   }
 }
 
@@ -152,10 +158,10 @@ __global__ __launch_bounds__(kThreads) void k_deconv_igemm(DeconvArgs a, Phases 
   const int b = (int)blockIdx.x;
   int ph = 0;
   while (ph + 1 < plan.nph && plan.off[ph + 1] <= b) ++ph;
-  const int sh = (int)a.sh, sw = (int)a.sw;
-  const int rh = ph / sw, rw = ph % sw;
-  const int Hp = ((int)a.H_out - rh + sh - 1) / sh;
-  const int Wp = ((int)a.W_out - rw + sw - 1) / sw;
+  const int osh = plan.osh, osw = plan.osw;
+  const int rh = ph / osw, rw = ph % osw;
+  const int Hp = ((int)a.H_out - rh + osh - 1) / osh;
+  const int Wp = ((int)a.W_out - rw + osw - 1) / osw;
   const int OB = ((int)a.OC + 2 * WO - 1) / (2 * WO);
   const int JB = (Wp + WJ - 1) / WJ;
   const int IB = (Hp + 1) / 2;
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_deconv_igemm(DeconvArgs a, Phases 
   // lane offset of pixel row r inside the tap's window of WJ pixels
   uint32_t xoff[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) xoff[r] = (uint32_t)((8 * gm + r) * IC + 16 * lg);
+  for (int r = 0; r < 8; ++r) xoff[r] = (uint32_t)((8 * gm + r) * plan.isw * IC + 16 * lg);
   const uint32_t woff = (uint32_t)(8 * gn) * (uint32_t)a.ldw + (uint32_t)(16 * lg);
 
   int32_t acc[64];
@@ -187,10 +193,10 @@ __global__ __launch_bounds__(kThreads) void k_deconv_igemm(DeconvArgs a, Phases 
 
   for (int th = 0; th < p.nth[rh]; ++th) {
     const int kh = p.thk[rh][th];
-    const int64_t hp = i + p.thd[rh][th] + plan.pt;  // padded input row, in range
+    const int64_t hp = (int64_t)i * plan.ish + p.thd[rh][th] + plan.pt;  // padded row, in range
     for (int tw = 0; tw < p.ntw[rw]; ++tw) {
       const int kw = p.twk[rw][tw];
-      const int64_t wp0 = j0w + p.twd[rw][tw] + plan.pl;  // padded column of pixel j0w
+      const int64_t wp0 = (int64_t)j0w * plan.isw + p.twd[rw][tw] + plan.pl;  // of pixel j0w
       const gptr xr = uniform_ptr(xp + ((n * plan.Hpad + hp) * plan.Wpad + wp0) * IC);
       const int8_t* wu = a.w + (int64_t)oc0w * a.ldw + (int64_t)(kh * a.Kw + kw) * IC;
       gptr wr[8];
@@ -228,14 +234,14 @@ __global__ __launch_bounds__(kThreads) void k_deconv_igemm(DeconvArgs a, Phases 
   constexpr int C = V >= 8 ? 8 : V;
   const int m0l = (V * lg) >> 3, c0l = (V * lg) & 7;
   const int64_t plane = a.H_out * a.W_out;
-  const int64_t oh = rh + (int64_t)sh * i;
+  const int64_t oh = rh + (int64_t)osh * i;
   const int32_t* wsp = wsum + (int64_t)ph * a.OC;
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     const int j = jg + m0l + h;
     if (j >= Wp) continue;
     // output index of (n, channel, oh, ow); the next channel is one plane further
-    int64_t o = ((n * a.OC + oc0 + c0l) * a.H_out + oh) * a.W_out + rw + (int64_t)sw * j;
+    int64_t o = ((n * a.OC + oc0 + c0l) * a.H_out + oh) * a.W_out + rw + (int64_t)osw * j;
 #pragma unroll
     for (int t = 0; t < C; ++t, o += plane) {
       const int oc = oc0 + c0l + t;
@@ -251,29 +257,37 @@ __global__ __launch_bounds__(kThreads) void k_deconv_igemm(DeconvArgs a, Phases 
   }
 }
 
-// Tile counts per phase, block offsets and the zero-point border.
-bool make_plan(const DeconvArgs& a, const Phases& p, int WJ, int WO, Plan& plan,
-               int64_t& blocks) {
+// Tile counts per phase, block offsets and the zero-point border, for the
+// geometry (osh, osw, ish, isw) described at Plan.
+bool make_plan(const DeconvArgs& a, const Phases& p, int osh, int osw, int ish, int isw, int WJ,
+               int WO, Plan& plan, int64_t& blocks) {
   plan = Plan{};
-  plan.nph = (int)(a.sh * a.sw);
+  plan.osh = osh;
+  plan.osw = osw;
+  plan.ish = ish;
+  plan.isw = isw;
+  plan.nph = osh * osw;
+  if (plan.nph > kMaxPhases) return false;
   blocks = 0;
   int64_t lo_h = 0, hi_h = a.H_in - 1, lo_w = 0, hi_w = a.W_in - 1;
   for (int ph = 0; ph < plan.nph; ++ph) {
-    const int rh = ph / (int)a.sw, rw = ph % (int)a.sw;
-    const int64_t Hp = (a.H_out - rh + a.sh - 1) / a.sh, Wp = (a.W_out - rw + a.sw - 1) / a.sw;
+    const int rh = ph / osw, rw = ph % osw;
+    const int64_t Hp = (a.H_out - rh + osh - 1) / osh, Wp = (a.W_out - rw + osw - 1) / osw;
     const int64_t JB = (Wp + WJ - 1) / WJ;
     plan.off[ph] = (int)blocks;
     blocks += a.N * ((Hp + 1) / 2) * JB * ((a.OC + 2 * WO - 1) / (2 * WO));
     if (blocks >= ((int64_t)1 << 31) - 1) return false;
     if (Hp > 0)
       for (int th = 0; th < p.nth[rh]; ++th) {
-        lo_h = lo_h < p.thd[rh][th] ? lo_h : p.thd[rh][th];
-        hi_h = hi_h > Hp - 1 + p.thd[rh][th] ? hi_h : Hp - 1 + p.thd[rh][th];
+        const int64_t d = p.thd[rh][th], last = (Hp - 1) * ish + d;
+        lo_h = lo_h < d ? lo_h : d;
+        hi_h = hi_h > last ? hi_h : last;
       }
     if (Wp > 0)
       for (int tw = 0; tw < p.ntw[rw]; ++tw) {
-        lo_w = lo_w < p.twd[rw][tw] ? lo_w : p.twd[rw][tw];
-        hi_w = hi_w > JB * WJ - 1 + p.twd[rw][tw] ? hi_w : JB * WJ - 1 + p.twd[rw][tw];
+        const int64_t d = p.twd[rw][tw], last = (JB * WJ - 1) * isw + d;
+        lo_w = lo_w < d ? lo_w : d;
+        hi_w = hi_w > last ? hi_w : last;
       }
   }
   plan.off[plan.nph] = (int)blocks;
@@ -282,7 +296,34 @@ bool make_plan(const DeconvArgs& a, const Phases& p, int WJ, int WO, Plan& plan,
   plan.pl = (int)-lo_w;
   plan.Hpad = (int)(hi_h - lo_h + 1);
   plan.Wpad = (int)(hi_w - lo_w + 1);
+  // 32-bit lane offsets: pixel rows reach (WJ - 1) * isw * IC + IC bytes
+  if ((double)WJ * isw * a.IC >= (double)((int64_t)1 << 31)) return false;
   return true;
+}
+
+// Forward conv as one phase: every tap qualifies; tap kh reads input row
+// oh*stride_h + kh*dil_h - pad_h.
+bool make_conv_phases(const DeconvArgs& a, Phases& p) {
+  if (a.Kh > kMaxT || a.Kw > kMaxT) return false;
+  p = Phases{};
+  p.nth[0] = (int)a.Kh;
+  for (int k = 0; k < (int)a.Kh; ++k) {
+    p.thk[0][k] = k;
+    p.thd[0][k] = (int)(k * a.dil_h - a.ph);
+  }
+  p.ntw[0] = (int)a.Kw;
+  for (int k = 0; k < (int)a.Kw; ++k) {
+    p.twk[0][k] = k;
+    p.twd[0][k] = (int)(k * a.dil_w - a.pw);
+  }
+  return true;
+}
+
+bool igemm_shape_ok(const DeconvArgs& a) {
+  if (a.IC % kSlice != 0 || a.ldw % 16 != 0 || ((uintptr_t)a.w & 15) != 0) return false;
+  // 32-bit lane offsets (< 32 * ldw) and 32-bit tile counters
+  return a.IC < (1 << 25) && a.ldw < (1 << 25) && a.H_out < (1 << 30) && a.W_out < (1 << 30) &&
+         a.H_in < (1 << 30) && a.W_in < (1 << 30) && a.OC < (1 << 30);
 }
 
 }  // namespace
@@ -291,24 +332,33 @@ bool deconv_igemm_supported(const DeconvArgs& a) {
   Phases p;
   Plan plan;
   int64_t blocks;
-  if (a.IC % kSlice != 0 || a.ldw % 16 != 0 || ((uintptr_t)a.w & 15) != 0) return false;
-  // 32-bit lane offsets (< 32 * IC and < 32 * ldw) and 32-bit tile counters
-  if (a.IC >= (1 << 25) || a.ldw >= (1 << 25) || a.H_out >= (1 << 30) || a.W_out >= (1 << 30) ||
-      a.H_in >= (1 << 30) || a.W_in >= (1 << 30) || a.OC >= (1 << 30))
-    return false;
-  return make_phases(a, p) && make_plan(a, p, 32, 32, plan, blocks) &&
-         make_plan(a, p, 64, 16, plan, blocks);
+  const int sh = (int)a.sh, sw = (int)a.sw;
+  return igemm_shape_ok(a) && make_phases(a, p) &&
+         make_plan(a, p, sh, sw, 1, 1, 32, 32, plan, blocks) &&
+         make_plan(a, p, sh, sw, 1, 1, 64, 16, plan, blocks);
+}
+
+bool conv_igemm_supported(const DeconvArgs& a) {
+  Phases p;
+  Plan plan;
+  int64_t blocks;
+  if (a.sh > 4096 || a.sw > 4096 || a.dil_h > 4096 || a.dil_w > 4096) return false;
+  const int sh = (int)a.sh, sw = (int)a.sw;
+  return igemm_shape_ok(a) && make_conv_phases(a, p) &&
+         make_plan(a, p, 1, 1, sh, sw, 32, 32, plan, blocks) &&
+         make_plan(a, p, 1, 1, sh, sw, 64, 16, plan, blocks);
 }
 
 namespace {
 
 template <int LPG, int GM>
-hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, hipStream_t s) {
+hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, int osh, int osw, int ish,
+                          int isw, hipStream_t s) {
   constexpr int GN = 64 / LPG / GM;
   constexpr int WJ = 8 * GM, WO = 8 * GN;
   Plan plan;
   int64_t blocks;
-  if (!make_plan(a, p, WJ, WO, plan, blocks)) return hipErrorInvalidValue;
+  if (!make_plan(a, p, osh, osw, ish, isw, WJ, WO, plan, blocks)) return hipErrorInvalidValue;
   const size_t xbytes = (size_t)a.N * plan.Hpad * plan.Wpad * a.IC;
   const size_t xpad = (xbytes + 255) / 256 * 256;
   const size_t wsbytes = (size_t)plan.nph * (size_t)a.OC * sizeof(int32_t);
@@ -336,6 +386,13 @@ hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, hipStream_t s) {
   return e != hipSuccess ? e : f;
 }
 
+int igemm_layout() {
+  int gm = 4;
+  if (const char* e = getenv("Q8TA_IGEMM_CFG"))
+    if (const char* xx = strchr(e, 'x')) gm = atoi(xx + 1);
+  return gm;
+}
+
 }  // namespace
 
 // NHWC copy of the input inside its zero-point border and sum w per (phase,
@@ -345,10 +402,18 @@ hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, hipStream_t s) {
 hipError_t launch_deconv_igemm(const DeconvArgs& a, hipStream_t s) {
   Phases p;
   if (!make_phases(a, p)) return hipErrorInvalidValue;
-  int gm = 4;
-  if (const char* e = getenv("Q8TA_IGEMM_CFG"))
-    if (const char* xx = strchr(e, 'x')) gm = atoi(xx + 1);
-  return gm == 8 ? launch_igemm_t<4, 8>(a, p, s) : launch_igemm_t<4, 4>(a, p, s);
+  const int sh = (int)a.sh, sw = (int)a.sw;
+  return igemm_layout() == 8 ? launch_igemm_t<4, 8>(a, p, sh, sw, 1, 1, s)
+                             : launch_igemm_t<4, 4>(a, p, sh, sw, 1, 1, s);
+}
+
+// The forward conv through the same kernels: one phase, every tap.
+hipError_t launch_conv_igemm(const DeconvArgs& a, hipStream_t s) {
+  Phases p;
+  if (!make_conv_phases(a, p)) return hipErrorInvalidValue;
+  const int sh = (int)a.sh, sw = (int)a.sw;
+  return igemm_layout() == 8 ? launch_igemm_t<4, 8>(a, p, 1, 1, sh, sw, s)
+                             : launch_igemm_t<4, 4>(a, p, 1, 1, sh, sw, s);
 }
 
 }  // namespace q8ta

@@ -63,6 +63,40 @@ __global__ __launch_bounds__(kThreads) void k_deconv_generic(DeconvArgs a) {
   }
 }
 
+// Forward q8ta_conv2d, one output per thread: ih = oh*stride_h - pad_h +
+// kh*dil_h, taps outside the input skipped.
+__global__ __launch_bounds__(kThreads) void k_conv2d_generic(DeconvArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t total = a.N * a.OC * a.H_out * a.W_out;
+  if (idx >= total) return;
+  const int64_t ow = idx % a.W_out;
+  int64_t r = idx / a.W_out;
+  const int64_t oh = r % a.H_out;
+  r /= a.H_out;
+  const int64_t oc = r % a.OC;
+  const int64_t n = r / a.OC;
+  const int64_t plane = a.H_in * a.W_in;
+  int32_t acc = 0;
+  for (int64_t kh = 0; kh < a.Kh; ++kh) {
+    const int64_t ih = oh * a.sh - a.ph + kh * a.dil_h;
+    if (ih < 0 || ih >= a.H_in) continue;
+    for (int64_t kw = 0; kw < a.Kw; ++kw) {
+      const int64_t iw = ow * a.sw - a.pw + kw * a.dil_w;
+      if (iw < 0 || iw >= a.W_in) continue;
+      const int8_t* xp = a.x + ((n * a.IC) * a.H_in + ih) * a.W_in + iw;
+      const int8_t* wp = a.w + oc * a.ldw + (kh * a.Kw + kw) * a.IC;
+      for (int64_t ic = 0; ic < a.IC; ++ic)
+        acc += ((int32_t)xp[ic * plane] - a.izp) * (int32_t)wp[ic];
+    }
+  }
+  if (a.acc) {
+    a.acc[idx] = acc;
+  } else {
+    float b = a.bias ? a.bias[oc] : 0.0f;
+    a.out[idx] = (int8_t)requant(acc, a.wscale[oc], b, a.rq);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s) {
@@ -76,6 +110,13 @@ hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s) {
   int64_t total = a.N * a.OC * a.H_out * a.W_out;
   int64_t blocks = (total + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(k_deconv_generic, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv2d_generic(const DeconvArgs& a, hipStream_t s) {
+  int64_t total = a.N * a.OC * a.H_out * a.W_out;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_conv2d_generic, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

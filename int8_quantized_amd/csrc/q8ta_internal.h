@@ -141,8 +141,12 @@ struct DeconvArgs {
   int64_t H_out, W_out;
   int32_t izp;
   Requant rq;
+  int64_t dil_h = 1, dil_w = 1;  // forward conv only (the transposed op takes 1)
 };
+// The same arguments describe the forward q8ta_conv2d (stride, padding and
+// dilation of the forward index relation).
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s);
+hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s);
 
 // Stride phases of a transposed conv, built on the host: for row residue r
 // (output rows oh = r + s_h*i) the nth[r] qualifying kernel rows thk[r][t] read
@@ -175,5 +179,8 @@ hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s);
 bool deconv_dot4_supported(const DeconvArgs& a);
 hipError_t launch_deconv_igemm(const DeconvArgs& a, hipStream_t s);
 bool deconv_igemm_supported(const DeconvArgs& a);
+hipError_t launch_conv_igemm(const DeconvArgs& a, hipStream_t s);
+bool conv_igemm_supported(const DeconvArgs& a);
+hipError_t launch_conv2d_generic(const DeconvArgs& a, hipStream_t s);
 
 }  // namespace q8ta

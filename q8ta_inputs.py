@@ -200,6 +200,13 @@ WORKLOADS = {
         "[8,128,128,128]", 1005,
         dict(N=8, IC=256, H_in=64, W_in=64, OC=128, Kh=3, Kw=3, stride=(2, 2),
              padding=(1, 1), output_padding=(1, 1))),
+    # Not a workload of the pages (they measure none for the forward conv): the
+    # same-size 3x3 conv on the large transposed conv's input, for the forward
+    # op's measurement.
+    "conv2d_large": Workload(
+        "conv2d_large", "q8ta_conv2d [8,256,64,64] K3 s1 p1 -> [8,128,64,64]", 1006,
+        dict(N=8, IC=256, H_in=64, W_in=64, OC=128, Kh=3, Kw=3, stride=(1, 1),
+             padding=(1, 1), dilation=(1, 1))),
 }
 
 
@@ -234,3 +241,8 @@ def make_deconv_small():
 def make_deconv_large():
     wl = WORKLOADS["deconv_large"]
     return deconv_case(wl.seed, x_from_fp32=True, **wl.params)
+
+
+def make_conv2d_large():
+    wl = WORKLOADS["conv2d_large"]
+    return conv_case(wl.seed, **wl.params)

@@ -29,7 +29,8 @@ def _declared():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for n in ["q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor", "q8ta_linear",
-              "q8ta_linear_gemv", "q8ta_conv2d_transposed", "q8ta_last_error"]:
+              "q8ta_linear_gemv", "q8ta_conv2d_transposed", "q8ta_conv2d", "q8ta_conv2d_acc",
+              "q8ta_last_error"]:
         assert n in names
 
 
@@ -161,6 +162,52 @@ def test_deconv_acc_errors():
     a = list(args); a[10] = 100
     _st(f(*a), q8.Q8TA_ERR_SHAPE)
     a = list(args); a[5] = -200
+    _st(f(*a), q8.Q8TA_ERR_QPARAM)
+
+
+# ---------------------------------------------------------------- forward conv2d
+CV = dict(x=FAKE, N=1, IC=64, H_in=32, W_in=32, s_in=0.02, izp=3, w=FAKE, OC=32, Kh=3, Kw=3,
+          ldw=576, ws=None, scales=FAKE, bias=FAKE, s_out=0.54, ozp=-5, sh=1, sw=1, ph=1, pw=1,
+          dh=1, dw=1, groups=1, act=b"none", out=FAKE, H_out=32, W_out=32)
+
+
+def _cv(**kw):
+    a = dict(CV)
+    a.update(kw)
+    return q8.lib().q8ta_conv2d(
+        a["x"], a["N"], a["IC"], a["H_in"], a["W_in"], a["s_in"], a["izp"], a["w"], a["OC"],
+        a["Kh"], a["Kw"], a["ldw"], a["ws"], a["scales"], a["bias"], a["s_out"], a["ozp"],
+        a["sh"], a["sw"], a["ph"], a["pw"], a["dh"], a["dw"], a["groups"], a["act"], a["out"],
+        a["H_out"], a["W_out"], None)
+
+
+def test_conv2d_errors():
+    _st(_cv(x=None), q8.Q8TA_ERR_NULL)
+    _st(_cv(w=None), q8.Q8TA_ERR_NULL)
+    _st(_cv(out=None), q8.Q8TA_ERR_NULL)
+    _st(_cv(scales=None), q8.Q8TA_ERR_NULL)
+    for k in ["N", "IC", "H_in", "W_in", "OC", "Kh", "Kw", "H_out", "W_out"]:
+        _st(_cv(**{k: 0}), q8.Q8TA_ERR_SHAPE)
+    _st(_cv(ldw=575), q8.Q8TA_ERR_SHAPE, "weight_row_stride")
+    _st(_cv(sh=0), q8.Q8TA_ERR_SHAPE)
+    _st(_cv(ph=-1), q8.Q8TA_ERR_SHAPE)
+    _st(_cv(dh=0), q8.Q8TA_ERR_SHAPE, "dilation")
+    _st(_cv(dw=5000), q8.Q8TA_ERR_SHAPE, "dilation")
+    _st(_cv(groups=2), q8.Q8TA_ERR_UNSUPPORTED, "groups")
+    _st(_cv(groups=64), q8.Q8TA_ERR_UNSUPPORTED, "groups")
+    _st(_cv(act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(_cv(izp=-129), q8.Q8TA_ERR_QPARAM)
+    _st(_cv(s_out=0.0), q8.Q8TA_ERR_QPARAM)
+
+
+def test_conv2d_acc_errors():
+    f = q8.lib().q8ta_conv2d_acc
+    args = [FAKE, 1, 64, 32, 32, 3, FAKE, 32, 3, 3, 576, 1, 1, 1, 1, 1, 1, FAKE, 32, 32, None]
+    a = list(args); a[17] = None
+    _st(f(*a), q8.Q8TA_ERR_NULL)
+    a = list(args); a[15] = 0
+    _st(f(*a), q8.Q8TA_ERR_SHAPE)
+    a = list(args); a[5] = 200
     _st(f(*a), q8.Q8TA_ERR_QPARAM)
 
 

@@ -471,3 +471,76 @@ def test_deconv_large_workload_sampled():
                                        c.Kh, c.Kw, c.stride, c.padding, (1, 1), c.H_out, c.W_out)
         np.testing.assert_array_equal(got[n][ocs], ref[0])
     assert (np.abs(got.astype(int)) < 127).mean() > 0.9
+
+
+# ============================================================================ forward conv2d
+def _run_conv(c, bias=True):
+    out = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+    b = dev(c.bias) if (bias and c.bias is not None) else None
+    q8.q8ta_conv2d(dev(c.x), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
+                   dev(c.weight_scales), b, c.out_scale, c.out_zp, c.stride, c.padding,
+                   c.dilation, 1, "none", out)
+    return host(out)
+
+
+def _acc_conv(c):
+    acc = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int32, device="cuda")
+    q8.q8ta_conv2d_acc(dev(c.x), c.in_zp, dev(c.w), c.Kh, c.Kw, c.stride, c.padding, c.dilation,
+                       acc)
+    return host(acc)
+
+
+def _oracle_conv(c, bias=True):
+    return oracle.conv2d(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale, c.in_zp,
+                         c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation,
+                         c.H_out, c.W_out)
+
+
+CONV2D_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, dil, H_out, W_out, ldw_extra
+    (1, 64, 9, 11, 32, 3, 3, (1, 1), (1, 1), (1, 1), None, None, 0),
+    (2, 64, 10, 9, 40, 3, 3, (2, 2), (1, 1), (1, 1), None, None, 16),     # OC % 32 != 0
+    (1, 128, 7, 40, 64, 1, 1, (1, 1), (0, 0), (1, 1), None, None, 0),     # pointwise
+    (1, 64, 9, 9, 16, 3, 2, (1, 2), (2, 0), (2, 3), None, None, 0),       # dilation, mixed strides
+    (1, 64, 12, 70, 33, 5, 5, (3, 2), (2, 2), (1, 1), None, None, 0),     # several column tiles
+    (1, 64, 4, 5, 32, 3, 3, (1, 1), (4, 3), (1, 1), None, None, 0),       # pad larger than K
+    (1, 64, 6, 6, 32, 3, 3, (1, 1), (1, 1), (1, 1), 4, 9, 0),             # explicit output size
+    (3, 192, 17, 33, 130, 3, 3, (1, 1), (1, 1), (1, 1), None, None, 64),
+    (1, 24, 7, 7, 8, 3, 3, (1, 1), (1, 1), (1, 1), None, None, 0),        # IC % 64 != 0 (general)
+    (1, 3, 16, 16, 16, 7, 7, (2, 2), (3, 3), (1, 1), None, None, 0),      # stem-like (general)
+]
+
+
+@pytest.mark.parametrize("case", CONV2D_CASES, ids=[str(i) for i in range(len(CONV2D_CASES))])
+@pytest.mark.parametrize("layout", ["4x4", "4x8"])
+def test_conv2d_parity(case, layout):
+    N, IC, H, W, OC, Kh, Kw, s, p, d, Ho, Wo, extra = case
+    _say(f"conv2d layout={layout} case={case}")
+    c = qi.conv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 2, N, IC, H, W, OC, Kh, Kw, s, p, d,
+                     H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra)
+    with env(Q8TA_IGEMM_CFG=layout):
+        np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
+        np.testing.assert_array_equal(_acc_conv(c), oracle.conv2d_acc(
+            c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out))
+
+
+@pytest.mark.parametrize("izp", [-128, 127, 0])
+def test_conv2d_zero_points_and_no_bias(izp):
+    c = qi.conv_case(700 + izp, 1, 64, 8, 8, 24, 3, 3, (1, 1), (1, 1), (1, 1), in_zp=izp)
+    np.testing.assert_array_equal(_run_conv(c, bias=False), _oracle_conv(c, bias=False))
+    np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
+
+
+def test_conv2d_large_workload_sampled():
+    """[8,256,64,64] K3 s1 p1 -> [8,128,64,64] in the benchmark's launch
+    configuration; the oracle recomputes images 0 and 7 for 24 output channels."""
+    c = qi.make_conv2d_large()
+    _say("conv2d [8,256,64,64] -> [8,128,64,64]")
+    got = _run_conv(c)
+    chans = np.array(sorted(set([0, 1, 2, 63, 64, 65, 126, 127] + list(range(5, 128, 8)))))[:24]
+    for n in (0, 7):
+        ref = oracle.conv2d(c.x[n:n + 1], c.w[chans], c.weight_scales[chans], c.bias[chans],
+                            c.in_scale, c.in_zp, c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride,
+                            c.padding, c.dilation, c.H_out, c.W_out)
+        np.testing.assert_array_equal(got[n:n + 1, chans], ref)
+
