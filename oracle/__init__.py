@@ -218,24 +218,25 @@ def conv2d_transposed(x, w, weight_scales, bias, input_scale: float, input_zero_
 
 
 def conv2d_acc(x, w, input_zero_point: int, Kh: int, Kw: int, stride, padding, dilation,
-               H_out: int, W_out: int) -> np.ndarray:
+               H_out: int, W_out: int, groups: int = 1) -> np.ndarray:
     """Forward q8ta_conv2d contraction (the general conv whose scaffold #21205
     Solution says the transposed op reuses): ih = oh*stride - pad + kh*dil,
-    taken only inside the input."""
+    taken only inside the input; with groups, output channel oc sums over the
+    input channels of its group only, w[oc, (kh*Kw+kw)*(IC/groups) + icg]."""
     x, w, (N, IC, H_in, W_in, OC, ldw, sh, sw, ph, pw, dh, dw) = _deconv_args(
         x, w, Kh, Kw, stride, padding, dilation)
     acc = np.empty((N, OC, H_out, W_out), np.int32)
     _chk(_load().oracle_conv2d_acc(
         _p(x), _c_i64(N), _c_i64(IC), _c_i64(H_in), _c_i64(W_in), _c_i64(input_zero_point),
         _p(w), _c_i64(OC), _c_i64(Kh), _c_i64(Kw), _c_i64(ldw), _c_i64(sh), _c_i64(sw),
-        _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(H_out), _c_i64(W_out),
-        _p(acc)), "conv2d_acc")
+        _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(groups), _c_i64(H_out),
+        _c_i64(W_out), _p(acc)), "conv2d_acc")
     return acc
 
 
 def conv2d(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
            output_scale: float, output_zero_point: int, Kh: int, Kw: int, stride, padding,
-           dilation, H_out: int, W_out: int, return_acc: bool = False):
+           dilation, H_out: int, W_out: int, return_acc: bool = False, groups: int = 1):
     """Forward q8ta_conv2d: contraction then the per-channel epilogue with
     channel = oc.  x int8 NCHW, w int8 [OC, ldw] with w[oc, (kh*Kw+kw)*IC + ic];
     output int8 NCHW [N, OC, H_out, W_out]."""
@@ -249,6 +250,6 @@ def conv2d(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
         _p(x), _c_i64(N), _c_i64(IC), _c_i64(H_in), _c_i64(W_in), _c_dbl(input_scale),
         _c_i64(input_zero_point), _p(w), _c_i64(OC), _c_i64(Kh), _c_i64(Kw), _c_i64(ldw),
         _p(ws), _p(b), _c_dbl(output_scale), _c_i64(output_zero_point), _c_i64(sh),
-        _c_i64(sw), _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(H_out),
-        _c_i64(W_out), _p(out), _p(acc)), "conv2d")
+        _c_i64(sw), _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(groups),
+        _c_i64(H_out), _c_i64(W_out), _p(out), _p(acc)), "conv2d")
     return (out, acc) if return_acc else out

@@ -358,14 +358,21 @@ int oracle_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
  *     (x[n, ic, ih, iw] - input_zero_point) * w[oc, (kh*Kw + kw)*IC + ic]
  * with ih = oh*stride_h - pad_h + kh*dil_h, used only when 0 <= ih < H_in
  * (iw likewise).  x is NCHW [N, IC, H_in, W_in]; w is [OC, ldw]; acc is NCHW
- * [N, OC, H_out, W_out] int32.  groups == 1. */
+ * [N, OC, H_out, W_out] int32.
+ * Groups (not on the pages; the usual grouped convolution on the same layout):
+ * the channels split into `groups` equal groups, output channel oc belongs to
+ * group g = oc / (OC/groups) and sums only over the IC/groups input channels
+ * ic = g*(IC/groups) + icg, with w[oc, (kh*Kw + kw)*(IC/groups) + icg].
+ * groups == IC == OC is the depthwise convolution. */
 int oracle_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
                       int64_t W_in, int64_t input_zero_point, const int8_t* w,
                       int64_t OC, int64_t Kh, int64_t Kw, int64_t ldw,
                       int64_t stride_h, int64_t stride_w, int64_t pad_h,
-                      int64_t pad_w, int64_t dil_h, int64_t dil_w,
+                      int64_t pad_w, int64_t dil_h, int64_t dil_w, int64_t groups,
                       int64_t H_out, int64_t W_out, int32_t* acc) {
-  if (N < 0 || IC <= 0 || OC <= 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * IC ||
+  if (groups < 1 || IC % groups != 0 || OC % groups != 0) return ORACLE_BAD_ARG;
+  const int64_t ICg = IC / groups, OCg = OC / groups;
+  if (N < 0 || IC <= 0 || OC <= 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * ICg ||
       stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || H_out < 0 || W_out < 0)
     return ORACLE_BAD_ARG;
   int overflow = 0;
@@ -375,7 +382,9 @@ int oracle_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
       for (int64_t oh = 0; oh < H_out; ++oh) {
         for (int64_t ow = 0; ow < W_out; ++ow) {
           int64_t s = 0;
-          for (int64_t ic = 0; ic < IC; ++ic) {
+          const int64_t g = oc / OCg;
+          for (int64_t icg = 0; icg < ICg; ++icg) {
+            const int64_t ic = g * ICg + icg;
             for (int64_t kh = 0; kh < Kh; ++kh) {
               const int64_t ih = oh * stride_h - pad_h + kh * dil_h;
               if (ih < 0 || ih >= H_in) continue;
@@ -383,7 +392,7 @@ int oracle_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
                 const int64_t iw = ow * stride_w - pad_w + kw * dil_w;
                 if (iw < 0 || iw >= W_in) continue;
                 int64_t xv = x[((n * IC + ic) * H_in + ih) * W_in + iw];
-                int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];
+                int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];
                 s += (xv - input_zero_point) * wv;
               }
             }
@@ -404,14 +413,15 @@ int oracle_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
                   const float* weight_scales, const float* bias, double output_scale,
                   int64_t output_zero_point, int64_t stride_h, int64_t stride_w,
                   int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
-                  int64_t H_out, int64_t W_out, int8_t* out, int32_t* acc_out) {
+                  int64_t groups, int64_t H_out, int64_t W_out, int8_t* out,
+                  int32_t* acc_out) {
   if (N < 0 || OC <= 0 || H_out < 0 || W_out < 0) return ORACLE_BAD_ARG;
   int64_t total = N * OC * H_out * W_out;
   int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(total + 1));
   if (!acc) return ORACLE_BAD_ARG;
   int rc = oracle_conv2d_acc(x, N, IC, H_in, W_in, input_zero_point, w, OC, Kh, Kw, ldw,
-                             stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, H_out, W_out,
-                             acc);
+                             stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, groups, H_out,
+                             W_out, acc);
   if (rc == ORACLE_OK && total > 0)
     rc = oracle_epilogue(acc, total, OC, H_out * W_out, input_scale, weight_scales, bias,
                          output_scale, output_zero_point, out, NULL);

@@ -68,9 +68,14 @@ MUTANTS = [
      "const int64_t iw = ow * stride_h - pad_w + kw * dil_w;", 0),
     ("conv_last_column_dropped", "if (iw < 0 || iw >= W_in) continue;",
      "if (iw < 0 || iw >= W_in - 1) continue;", 0),
-    ("conv_tap_order", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];\n                s +=",
-     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * IC + ic];\n                s +=", 1),
+    ("conv_tap_order", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];",
+     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * ICg + icg];", 0),
     ("conv_zp_sign", "s += (xv - input_zero_point) * wv;", "s += (xv + input_zero_point) * wv;", 1),
+    ("conv_group_of_channel", "const int64_t g = oc / OCg;", "const int64_t g = oc % groups;", 0),
+    ("conv_group_channels_interleaved", "const int64_t ic = g * ICg + icg;",
+     "const int64_t ic = icg * groups + g;", 0),
+    ("conv_group_weight_stride", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];",
+     "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + icg];", 0),
 ]
 
 

@@ -389,15 +389,17 @@ def test_deconv_large_workload_output_size():
 
 
 # --------------------------------------------------------------------------- forward conv2d
-def _torch_conv2d_acc(x, w, zp, Kh, Kw, stride, padding, dilation):
+def _torch_conv2d_acc(x, w, zp, Kh, Kw, stride, padding, dilation, groups=1):
     """Exact float64 torch conv2d of (x - zp) with the weight reshape
-    w[oc, (kh*Kw+kw)*IC + ic] = orig[oc, ic, kh, kw] undone."""
+    w[oc, (kh*Kw+kw)*ICg + icg] = orig[oc, icg, kh, kw] undone (ICg = IC/groups)."""
     N, IC, H, W = x.shape
     OC = w.shape[0]
-    wo = torch.from_numpy(np.ascontiguousarray(w[:, :Kh * Kw * IC])).reshape(
-        OC, Kh, Kw, IC).permute(0, 3, 1, 2).contiguous().double()
+    ICg = IC // groups
+    wo = torch.from_numpy(np.ascontiguousarray(w[:, :Kh * Kw * ICg])).reshape(
+        OC, Kh, Kw, ICg).permute(0, 3, 1, 2).contiguous().double()
     xs = torch.from_numpy(x).double() - zp
-    return F.conv2d(xs, wo, stride=stride, padding=padding, dilation=dilation).numpy()
+    return F.conv2d(xs, wo, stride=stride, padding=padding, dilation=dilation,
+                    groups=groups).numpy()
 
 
 def test_conv2d_hand_cases():
@@ -405,7 +407,7 @@ def test_conv2d_hand_cases():
         x = np.array(c["x"], np.int8).reshape(c["N"], c["IC"], c["H_in"], c["W_in"])
         w = np.array(c["w"], np.int8).reshape(c["OC"], -1)
         acc = oracle.conv2d_acc(x, w, c["zp"], c["Kh"], c["Kw"], c["stride"], c["pad"], c["dil"],
-                                c["H_out"], c["W_out"])
+                                c["H_out"], c["W_out"], groups=c["groups"])
         np.testing.assert_array_equal(acc.reshape(-1), np.array(c["acc"]), err_msg=c["name"])
 
 
@@ -494,3 +496,60 @@ def test_conv2d_epilogue_matches_the_shared_epilogue():
     ref = oracle.epilogue(acc, c.w.shape[0], c.H_out * c.W_out, c.in_scale, c.weight_scales,
                           c.bias, c.out_scale, c.out_zp)
     np.testing.assert_array_equal(q, ref)
+
+
+GROUPED_SHAPES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, dil, groups
+    (1, 6, 7, 6, 4, 3, 3, (1, 1), (1, 1), (1, 1), 2),
+    (2, 8, 9, 8, 12, 3, 2, (2, 1), (1, 0), (1, 2), 4),
+    (1, 5, 8, 9, 5, 3, 3, (1, 1), (1, 1), (1, 1), 5),      # depthwise
+    (1, 4, 9, 7, 8, 5, 3, (2, 2), (2, 1), (1, 1), 4),      # depthwise, channel multiplier 2
+    (2, 6, 6, 6, 6, 3, 3, (2, 2), (1, 1), (2, 2), 6),      # depthwise, dilated, strided
+]
+
+
+@pytest.mark.parametrize("shape", GROUPED_SHAPES)
+def test_grouped_conv2d_matches_torch(shape):
+    N, IC, H, W, OC, Kh, Kw, s, p, d, G = shape
+    g = qi.rng(sum(shape[:7]) + 3)
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = g.integers(-128, 128, size=(OC, Kh * Kw * (IC // G)), dtype=np.int8)
+    ref = _torch_conv2d_acc(x, w, 9, Kh, Kw, s, p, d, groups=G)
+    H_out, W_out = ref.shape[2:]
+    acc = oracle.conv2d_acc(x, w, 9, Kh, Kw, s, p, d, H_out, W_out, groups=G)
+    np.testing.assert_array_equal(acc, ref.astype(np.int32))
+
+
+def test_grouped_conv2d_is_per_group_ungrouped_conv():
+    """A grouped conv equals the ungrouped conv of each group's channel slice."""
+    g = qi.rng(81)
+    N, IC, H, W, OC, K, G = 2, 6, 7, 5, 9, 3, 3
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, K * K * (IC // G) + 4))
+    acc = oracle.conv2d_acc(x, w, -3, K, K, (1, 2), (1, 1), (1, 1), 7, 3, groups=G)
+    for gi in range(G):
+        xs = x[:, gi * (IC // G):(gi + 1) * (IC // G)]
+        ws = w[gi * (OC // G):(gi + 1) * (OC // G)]
+        part = oracle.conv2d_acc(xs, ws, -3, K, K, (1, 2), (1, 1), (1, 1), 7, 3)
+        np.testing.assert_array_equal(acc[:, gi * (OC // G):(gi + 1) * (OC // G)], part)
+
+
+def test_depthwise_brute_force_tiny():
+    g = qi.rng(82)
+    N, C, H, W, Kh, Kw, s, p, d, zp = 1, 3, 5, 4, 3, 2, (2, 1), (1, 1), (1, 1), 5
+    x = qi.x_int8(g, (N, C, H, W))
+    w = qi.w_int8(g, (C, Kh * Kw))
+    Ho, Wo = qi.conv_out_size(H, Kh, s[0], p[0], d[0]), qi.conv_out_size(W, Kw, s[1], p[1], d[1])
+    ref = np.zeros((N, C, Ho, Wo), np.int64)
+    for c in range(C):
+        for oh in range(Ho):
+            for ow in range(Wo):
+                t = 0
+                for kh in range(Kh):
+                    for kw in range(Kw):
+                        ih, iw = oh * s[0] - p[0] + kh * d[0], ow * s[1] - p[1] + kw * d[1]
+                        if 0 <= ih < H and 0 <= iw < W:
+                            t += (int(x[0, c, ih, iw]) - zp) * int(w[c, kh * Kw + kw])
+                ref[0, c, oh, ow] = t
+    np.testing.assert_array_equal(oracle.conv2d_acc(x, w, zp, Kh, Kw, s, p, d, Ho, Wo, groups=C),
+                                  ref)
