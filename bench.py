@@ -494,6 +494,29 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     r["exact_valid_tap_ops"] = cops
     r["frac_of_dot4_peak"] = round(r["rate"] / PEAK_DOT4_TOPS, 4)
     res["conv2d_8x256x64x64_k3s1p1_to_8x128x64x64"] = r
+    del cx, cout
+
+    # ---- depthwise [8,256,64,64] K3 s1 p1, HBM-bound: rotate 40 input copies (335 MB)
+    log("extra: depthwise conv [8,256,64,64]")
+    dc = qi.make_depthwise_large()
+    copies = 40
+    dxs = [torch.from_numpy(dc.x).cuda() for _ in range(copies)]
+    dw_, ds_, db_ = (torch.from_numpy(a).cuda() for a in (dc.w, dc.weight_scales, dc.bias))
+    dN, dC, dH, dW = dc.x.shape
+    dout2 = torch.empty((dN, dC, dc.H_out, dc.W_out), dtype=torch.int8, device="cuda")
+
+    def dw_call(i):
+        check(lib.q8ta_conv2d(
+            dxs[i].data_ptr(), dN, dC, dH, dW, dc.in_scale, dc.in_zp, dw_.data_ptr(), dC, dc.Kh,
+            dc.Kw, dc.w.shape[1], None, ds_.data_ptr(), db_.data_ptr(), dc.out_scale, dc.out_zp,
+            1, 1, 1, 1, 1, 1, dC, b"none", dout2.data_ptr(), dc.H_out, dc.W_out, stream))
+    dwf = [(lambda i=i: dw_call(i)) for i in range(copies)]
+    dbytes = int(dc.x.size + dout2.numel() + dc.w.size + 8 * dC)
+    timer.time_calls(dwf, copies)
+    r = summary(timer.time_calls(dwf, 4 * copies), dbytes, "GB/s", PEAK_HBM_GBS)
+    r["algorithmic_bytes"] = dbytes
+    res["depthwise_8x256x64x64_k3s1p1_cold"] = r
+    del dxs, dout2
     for k, v in res.items():
         log(f"  {k}: {v}")
     return res

@@ -57,7 +57,7 @@ typedef enum q8ta_status {
   Q8TA_ERR_NULL = 1,        /* a required pointer is NULL */
   Q8TA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   Q8TA_ERR_QPARAM = 3,      /* a scale is not finite and > 0, or a zero point is outside [-128, 127] */
-  Q8TA_ERR_UNSUPPORTED = 4, /* an argument value the op does not implement (activation, groups, dilation) */
+  Q8TA_ERR_UNSUPPORTED = 4, /* an argument value the op does not implement (activation; groups and dilation of the transposed conv) */
   Q8TA_ERR_HIP = 5          /* the HIP runtime reported an error */
 } q8ta_status;
 
@@ -165,13 +165,17 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
  *       (x[n,ic,ih,iw] - input_zero_point) * weight[oc, (kh*Kw + kw)*IC + ic]
  *   with ih = oh*stride_h - pad_h + kh*dilation_h used only when
  *   0 <= ih < H_in (iw likewise);  out[n,oc,oh,ow] = epilogue(acc), c = oc.
+ * Groups (not on the pages; the usual grouped convolution on the same
+ * layout): groups must divide IC and OC; output channel oc belongs to group
+ * g = oc / (OC/groups) and sums only over input channels g*(IC/groups) + icg,
+ * with weight[oc, (kh*Kw + kw)*(IC/groups) + icg] (weight_row_stride >=
+ * Kh*Kw*IC/groups).  groups == IC == OC is the depthwise convolution.
  * Layouts, scales, bias, weight_row_stride and the epilogue as for
  * q8ta_conv2d_transposed; H_out / W_out are given explicitly (any sizes >= 1).
  * Requirements: all sizes >= 1, stride >= 1, padding >= 0, dilation in
- * [1, 4096]; groups must be 1 (grouped and depthwise convolutions are not
- * implemented: Q8TA_ERR_UNSUPPORTED); activation must be "none".
- * weight_sums is ignored.  Workspace on the implicit-GEMM path (IC % 64 ==
- * 0): an NHWC copy of the input inside a zero-point border plus 4 * OC bytes.
+ * [1, 4096]; activation must be "none".  weight_sums is ignored.  Workspace
+ * on the implicit-GEMM path (groups 1, IC % 64 == 0): an NHWC copy of the
+ * input inside a zero-point border plus 4 * OC bytes; none otherwise.
  */
 q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC,
                         int64_t H_in, int64_t W_in,
@@ -218,7 +222,7 @@ q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC,
                             int64_t Kh, int64_t Kw, int64_t weight_row_stride,
                             int64_t stride_h, int64_t stride_w,
                             int64_t pad_h, int64_t pad_w,
-                            int64_t dilation_h, int64_t dilation_w,
+                            int64_t dilation_h, int64_t dilation_w, int64_t groups,
                             int32_t* acc, int64_t H_out, int64_t W_out,
                             hipStream_t stream);
 

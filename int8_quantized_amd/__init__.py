@@ -59,7 +59,8 @@ SIGNATURES = {
                      _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                      _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
     "q8ta_conv2d_acc": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64,
-                         _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P], ctypes.c_int),
+                         _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P],
+                        ctypes.c_int),
 }
 
 _lib = None
@@ -254,7 +255,7 @@ def q8ta_conv2d(x, input_scale, input_zero_point, weight, Kh, Kw, weight_sums, w
 
 
 def q8ta_conv2d_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, dilation, acc,
-                    stream=None):
+                    groups=1, stream=None):
     """int32 accumulator of q8ta_conv2d (NCHW [N, OC, H_out, W_out])."""
     torch = _torch()
     N, IC, H_in, W_in = x.shape
@@ -265,7 +266,8 @@ def q8ta_conv2d_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, dilati
         _dev(x, torch.int8, "x"), N, IC, H_in, W_in, int(input_zero_point),
         _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw, int(stride[0]),
         int(stride[1]), int(padding[0]), int(padding[1]), int(dilation[0]), int(dilation[1]),
-        _dev(acc, torch.int32, "acc"), acc.shape[2], acc.shape[3], _stream(stream)))
+        int(groups), _dev(acc, torch.int32, "acc"), acc.shape[2], acc.shape[3],
+        _stream(stream)))
     return acc
 
 

@@ -111,9 +111,11 @@ hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
   return launch_deconv_generic(a, s);
 }
 
-// Forward conv: the implicit GEMM (IC % 64 == 0) or the shape-general kernel.
+// Forward conv: the implicit GEMM (groups 1, IC % 64 == 0), the depthwise
+// kernel (groups == IC == OC), or the shape-general kernel.
 hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s) {
   if (conv_igemm_supported(a)) return launch_conv_igemm(a, s);
+  if (depthwise_supported(a)) return launch_depthwise(a, s);
   return launch_conv2d_generic(a, s);
 }
 
@@ -181,10 +183,11 @@ q8ta_status q8ta_linear_acc(const int8_t* x, int64_t M, int64_t K, int64_t input
 
 namespace {
 
+// icg: input channels per weight row (IC, or IC / groups for a grouped conv).
 q8ta_status deconv_checks(const char* op, const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
                           int64_t W_in, const int8_t* weight, int64_t OC, int64_t Kh, int64_t Kw,
                           int64_t ldw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
-                          const void* out, int64_t H_out, int64_t W_out) {
+                          const void* out, int64_t H_out, int64_t W_out, int64_t icg) {
   if (!x || !weight || !out) return fail(Q8TA_ERR_NULL, "%s: x, weight and out must not be NULL", op);
   if (N < 1 || IC < 1 || H_in < 1 || W_in < 1 || OC < 1 || Kh < 1 || Kw < 1 || H_out < 1 || W_out < 1)
     return fail(Q8TA_ERR_SHAPE, "%s: all sizes must be >= 1", op);
@@ -193,9 +196,9 @@ q8ta_status deconv_checks(const char* op, const int8_t* x, int64_t N, int64_t IC
       H_out > lim || W_out > lim)
     return fail(Q8TA_ERR_SHAPE, "%s: a size is too large", op);
   if (Kh * Kw > kMaxElems / IC) return fail(Q8TA_ERR_SHAPE, "%s: Kh*Kw*IC too large", op);
-  if (ldw < Kh * Kw * IC)
-    return fail(Q8TA_ERR_SHAPE, "%s: weight_row_stride (%lld) must be >= Kh*Kw*IC (%lld)", op,
-                (long long)ldw, (long long)(Kh * Kw * IC));
+  if (ldw < Kh * Kw * icg)
+    return fail(Q8TA_ERR_SHAPE, "%s: weight_row_stride (%lld) must be >= Kh*Kw*%s (%lld)", op,
+                (long long)ldw, icg == IC ? "IC" : "IC/groups", (long long)(Kh * Kw * icg));
   if (sh < 1 || sw < 1 || sh > 4096 || sw > 4096) return fail(Q8TA_ERR_SHAPE, "%s: stride must be >= 1", op);
   if (ph < 0 || pw < 0 || ph > lim || pw > lim) return fail(Q8TA_ERR_SHAPE, "%s: padding must be >= 0", op);
   const double xe = (double)N * IC * H_in * W_in, oe = (double)N * OC * H_out * W_out,
@@ -224,7 +227,7 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC, int64
   (void)output_padding_h;
   (void)output_padding_w;
   q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out);
+                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out, IC);
   if (st) return st;
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
   if (dilation_h != 1 || dilation_w != 1)
@@ -251,7 +254,7 @@ q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC, i
                                        int32_t* acc, int64_t H_out, int64_t W_out, hipStream_t stream) {
   const char* op = "q8ta_conv2d_transposed_acc";
   q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out);
+                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out, IC);
   if (st) return st;
   if (!zp_ok(input_zero_point)) return fail(Q8TA_ERR_QPARAM, "%s: input_zero_point out of range", op);
   DeconvArgs a{};
@@ -273,14 +276,15 @@ q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, in
                         int64_t H_out, int64_t W_out, hipStream_t stream) {
   const char* op = "q8ta_conv2d";
   (void)weight_sums;
+  if (groups < 1 || IC < 1 || OC < 1 || IC % groups != 0 || OC % groups != 0)
+    return fail(Q8TA_ERR_SHAPE, "%s: groups (%lld) must divide IC and OC", op, (long long)groups);
   q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out);
+                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out,
+                                 IC / groups);
   if (st) return st;
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
   if (dilation_h < 1 || dilation_w < 1 || dilation_h > 4096 || dilation_w > 4096)
     return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
-  if (groups != 1)
-    return fail(Q8TA_ERR_UNSUPPORTED, "%s: groups must be 1 (got %lld)", op, (long long)groups);
   if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
   if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
   if ((st = check_activation(op, activation))) return st;
@@ -289,7 +293,7 @@ q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, in
   a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
   a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
-  a.dil_h = dilation_h; a.dil_w = dilation_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
   a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
   return hip_status(launch_conv2d(a, stream), op);
@@ -299,11 +303,14 @@ q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in
                             int64_t input_zero_point, const int8_t* weight, int64_t OC, int64_t Kh,
                             int64_t Kw, int64_t weight_row_stride, int64_t stride_h,
                             int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t dilation_h,
-                            int64_t dilation_w, int32_t* acc, int64_t H_out, int64_t W_out,
-                            hipStream_t stream) {
+                            int64_t dilation_w, int64_t groups, int32_t* acc, int64_t H_out,
+                            int64_t W_out, hipStream_t stream) {
   const char* op = "q8ta_conv2d_acc";
+  if (groups < 1 || IC < 1 || OC < 1 || IC % groups != 0 || OC % groups != 0)
+    return fail(Q8TA_ERR_SHAPE, "%s: groups (%lld) must divide IC and OC", op, (long long)groups);
   q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out);
+                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out,
+                                 IC / groups);
   if (st) return st;
   if (dilation_h < 1 || dilation_w < 1 || dilation_h > 4096 || dilation_w > 4096)
     return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
@@ -312,7 +319,7 @@ q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in
   a.x = x; a.w = weight; a.acc = acc;
   a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
-  a.dil_h = dilation_h; a.dil_w = dilation_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
   return hip_status(launch_conv2d(a, stream), op);
 }

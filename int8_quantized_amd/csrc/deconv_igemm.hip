@@ -342,7 +342,7 @@ bool conv_igemm_supported(const DeconvArgs& a) {
   Phases p;
   Plan plan;
   int64_t blocks;
-  if (a.sh > 4096 || a.sw > 4096 || a.dil_h > 4096 || a.dil_w > 4096) return false;
+  if (a.groups != 1 || a.sh > 4096 || a.sw > 4096 || a.dil_h > 4096 || a.dil_w > 4096) return false;
   const int sh = (int)a.sh, sw = (int)a.sw;
   return igemm_shape_ok(a) && make_conv_phases(a, p) &&
          make_plan(a, p, 1, 1, sh, sw, 32, 32, plan, blocks) &&

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kThreads) void k_deconv_generic(DeconvArgs a) {
 }
 
 // Forward q8ta_conv2d, one output per thread: ih = oh*stride_h - pad_h +
-// kh*dil_h, taps outside the input skipped.
+// kh*dil_h, taps outside the input skipped; with groups, output channel oc
+// sums over the IC/groups input channels of its group.
 __global__ __launch_bounds__(kThreads) void k_conv2d_generic(DeconvArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t total = a.N * a.OC * a.H_out * a.W_out;
@@ -76,6 +77,8 @@ __global__ __launch_bounds__(kThreads) void k_conv2d_generic(DeconvArgs a) {
   const int64_t oc = r % a.OC;
   const int64_t n = r / a.OC;
   const int64_t plane = a.H_in * a.W_in;
+  const int64_t ICg = a.IC / a.groups, OCg = a.OC / a.groups;
+  const int64_t ic0 = (oc / OCg) * ICg;  // first input channel of oc's group
   int32_t acc = 0;
   for (int64_t kh = 0; kh < a.Kh; ++kh) {
     const int64_t ih = oh * a.sh - a.ph + kh * a.dil_h;
@@ -83,9 +86,9 @@ __global__ __launch_bounds__(kThreads) void k_conv2d_generic(DeconvArgs a) {
     for (int64_t kw = 0; kw < a.Kw; ++kw) {
       const int64_t iw = ow * a.sw - a.pw + kw * a.dil_w;
       if (iw < 0 || iw >= a.W_in) continue;
-      const int8_t* xp = a.x + ((n * a.IC) * a.H_in + ih) * a.W_in + iw;
-      const int8_t* wp = a.w + oc * a.ldw + (kh * a.Kw + kw) * a.IC;
-      for (int64_t ic = 0; ic < a.IC; ++ic)
+      const int8_t* xp = a.x + ((n * a.IC + ic0) * a.H_in + ih) * a.W_in + iw;
+      const int8_t* wp = a.w + oc * a.ldw + (kh * a.Kw + kw) * ICg;
+      for (int64_t ic = 0; ic < ICg; ++ic)
         acc += ((int32_t)xp[ic * plane] - a.izp) * (int32_t)wp[ic];
     }
   }

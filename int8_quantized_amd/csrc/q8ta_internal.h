@@ -142,6 +142,7 @@ struct DeconvArgs {
   int32_t izp;
   Requant rq;
   int64_t dil_h = 1, dil_w = 1;  // forward conv only (the transposed op takes 1)
+  int64_t groups = 1;            // forward conv only: IC and OC split into equal groups
 };
 // The same arguments describe the forward q8ta_conv2d (stride, padding and
 // dilation of the forward index relation).
@@ -182,5 +183,7 @@ bool deconv_igemm_supported(const DeconvArgs& a);
 hipError_t launch_conv_igemm(const DeconvArgs& a, hipStream_t s);
 bool conv_igemm_supported(const DeconvArgs& a);
 hipError_t launch_conv2d_generic(const DeconvArgs& a, hipStream_t s);
+hipError_t launch_depthwise(const DeconvArgs& a, hipStream_t s);
+bool depthwise_supported(const DeconvArgs& a);
 
 }  // namespace q8ta

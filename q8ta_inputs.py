@@ -148,15 +148,15 @@ def conv_out_size(in_size, k, s, p, d=1):
 def conv_case(seed: int, N: int, IC: int, H_in: int, W_in: int, OC: int, Kh: int, Kw: int,
               stride=(1, 1), padding=(1, 1), dilation=(1, 1), H_out=None, W_out=None, ldw=None,
               with_bias=True, in_zp=IN_ZP, out_zp=OUT_ZP, x_from_fp32: bool = False,
-              in_scale: float = IN_SCALE) -> DeconvCase:
+              in_scale: float = IN_SCALE, groups: int = 1) -> DeconvCase:
     """Forward conv inputs, in the same container as the transposed conv's
-    (output_padding unused, (0, 0))."""
+    (output_padding unused, (0, 0)); the weight has Kh*Kw*IC/groups columns."""
     g = rng(seed)
     if H_out is None:
         H_out = conv_out_size(H_in, Kh, stride[0], padding[0], dilation[0])
     if W_out is None:
         W_out = conv_out_size(W_in, Kw, stride[1], padding[1], dilation[1])
-    ldw = Kh * Kw * IC if ldw is None else ldw
+    ldw = Kh * Kw * (IC // groups) if ldw is None else ldw
     xf = None
     if x_from_fp32:
         xf = x_fp32(g, (N, IC, H_in, W_in))
@@ -166,10 +166,12 @@ def conv_case(seed: int, N: int, IC: int, H_in: int, W_in: int, OC: int, Kh: int
     w = w_int8(g, (OC, ldw))
     ws = scales(g, OC)
     b = bias(g, OC) if with_bias else None
-    kred = IC * Kh * Kw
-    return DeconvCase(x, w, ws, b, in_scale, in_zp, out_scale_for(kred, in_scale), out_zp,
-                      Kh, Kw, tuple(stride), tuple(padding), (0, 0), tuple(dilation),
-                      H_out, W_out, xf)
+    kred = (IC // groups) * Kh * Kw
+    c = DeconvCase(x, w, ws, b, in_scale, in_zp, out_scale_for(kred, in_scale), out_zp,
+                   Kh, Kw, tuple(stride), tuple(padding), (0, 0), tuple(dilation),
+                   H_out, W_out, xf)
+    c.groups = groups
+    return c
 
 
 # --- the five named workloads -------------------------------------------------
@@ -207,6 +209,11 @@ WORKLOADS = {
         "conv2d_large", "q8ta_conv2d [8,256,64,64] K3 s1 p1 -> [8,128,64,64]", 1006,
         dict(N=8, IC=256, H_in=64, W_in=64, OC=128, Kh=3, Kw=3, stride=(1, 1),
              padding=(1, 1), dilation=(1, 1))),
+    # Likewise ours: the depthwise 3x3 conv on the same input.
+    "depthwise_large": Workload(
+        "depthwise_large", "q8ta_conv2d depthwise [8,256,64,64] K3 s1 p1 -> [8,256,64,64]", 1007,
+        dict(N=8, IC=256, H_in=64, W_in=64, OC=256, Kh=3, Kw=3, stride=(1, 1),
+             padding=(1, 1), dilation=(1, 1), groups=256)),
 }
 
 
@@ -245,4 +252,9 @@ def make_deconv_large():
 
 def make_conv2d_large():
     wl = WORKLOADS["conv2d_large"]
+    return conv_case(wl.seed, **wl.params)
+
+
+def make_depthwise_large():
+    wl = WORKLOADS["depthwise_large"]
     return conv_case(wl.seed, **wl.params)

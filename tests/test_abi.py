@@ -193,8 +193,10 @@ def test_conv2d_errors():
     _st(_cv(ph=-1), q8.Q8TA_ERR_SHAPE)
     _st(_cv(dh=0), q8.Q8TA_ERR_SHAPE, "dilation")
     _st(_cv(dw=5000), q8.Q8TA_ERR_SHAPE, "dilation")
-    _st(_cv(groups=2), q8.Q8TA_ERR_UNSUPPORTED, "groups")
-    _st(_cv(groups=64), q8.Q8TA_ERR_UNSUPPORTED, "groups")
+    _st(_cv(groups=0), q8.Q8TA_ERR_SHAPE, "groups")
+    _st(_cv(groups=3), q8.Q8TA_ERR_SHAPE, "groups")          # does not divide IC = 64
+    _st(_cv(groups=64), q8.Q8TA_ERR_SHAPE, "groups")         # does not divide OC = 32
+    _st(_cv(groups=2, ldw=287), q8.Q8TA_ERR_SHAPE, "weight_row_stride")
     _st(_cv(act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED)
     _st(_cv(izp=-129), q8.Q8TA_ERR_QPARAM)
     _st(_cv(s_out=0.0), q8.Q8TA_ERR_QPARAM)
@@ -202,9 +204,11 @@ def test_conv2d_errors():
 
 def test_conv2d_acc_errors():
     f = q8.lib().q8ta_conv2d_acc
-    args = [FAKE, 1, 64, 32, 32, 3, FAKE, 32, 3, 3, 576, 1, 1, 1, 1, 1, 1, FAKE, 32, 32, None]
-    a = list(args); a[17] = None
+    args = [FAKE, 1, 64, 32, 32, 3, FAKE, 32, 3, 3, 576, 1, 1, 1, 1, 1, 1, 1, FAKE, 32, 32, None]
+    a = list(args); a[18] = None
     _st(f(*a), q8.Q8TA_ERR_NULL)
+    a = list(args); a[17] = 5
+    _st(f(*a), q8.Q8TA_ERR_SHAPE)
     a = list(args); a[15] = 0
     _st(f(*a), q8.Q8TA_ERR_SHAPE)
     a = list(args); a[5] = 200

@@ -479,21 +479,21 @@ def _run_conv(c, bias=True):
     b = dev(c.bias) if (bias and c.bias is not None) else None
     q8.q8ta_conv2d(dev(c.x), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
                    dev(c.weight_scales), b, c.out_scale, c.out_zp, c.stride, c.padding,
-                   c.dilation, 1, "none", out)
+                   c.dilation, getattr(c, "groups", 1), "none", out)
     return host(out)
 
 
 def _acc_conv(c):
     acc = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int32, device="cuda")
     q8.q8ta_conv2d_acc(dev(c.x), c.in_zp, dev(c.w), c.Kh, c.Kw, c.stride, c.padding, c.dilation,
-                       acc)
+                       acc, groups=getattr(c, "groups", 1))
     return host(acc)
 
 
 def _oracle_conv(c, bias=True):
     return oracle.conv2d(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale, c.in_zp,
                          c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation,
-                         c.H_out, c.W_out)
+                         c.H_out, c.W_out, groups=getattr(c, "groups", 1))
 
 
 CONV2D_CASES = [
@@ -543,4 +543,39 @@ def test_conv2d_large_workload_sampled():
                             c.in_scale, c.in_zp, c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride,
                             c.padding, c.dilation, c.H_out, c.W_out)
         np.testing.assert_array_equal(got[n:n + 1, chans], ref)
+
+
+GROUPED_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, dil, groups, H_out, W_out
+    (1, 64, 9, 11, 64, 3, 3, (1, 1), (1, 1), (1, 1), 64, None, None),    # depthwise
+    (2, 32, 10, 9, 32, 3, 3, (2, 2), (1, 1), (1, 1), 32, None, None),    # depthwise, strided
+    (1, 16, 9, 9, 16, 5, 5, (1, 2), (2, 2), (2, 1), 16, None, None),     # depthwise, dilated
+    (1, 12, 13, 5, 12, 3, 2, (1, 1), (0, 1), (1, 1), 12, None, None),    # W_out % 4 != 0
+    (1, 16, 6, 6, 16, 3, 3, (1, 1), (1, 1), (1, 1), 16, 4, 9),           # explicit output size
+    (1, 16, 11, 13, 16, 5, 5, (1, 1), (2, 2), (1, 1), 16, None, None),   # depthwise 5x5
+    (1, 16, 12, 9, 16, 5, 5, (2, 2), (2, 2), (1, 1), 16, None, None),    # depthwise 5x5 s2
+    (2, 8, 7, 10, 8, 3, 3, (2, 2), (0, 0), (1, 1), 8, None, None),       # depthwise 3x3 s2 p0
+    (1, 8, 9, 9, 8, 3, 3, (1, 1), (1, 1), (1, 1), 8, 11, 5),             # output past the input
+    (1, 8, 7, 6, 16, 3, 3, (1, 1), (1, 1), (1, 1), 8, None, None),       # channel multiplier 2
+    (2, 64, 8, 8, 32, 3, 3, (1, 1), (1, 1), (1, 1), 4, None, None),      # grouped
+]
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES, ids=[str(i) for i in range(len(GROUPED_CASES))])
+def test_grouped_conv2d_parity(case):
+    N, IC, H, W, OC, Kh, Kw, s, p, d, G, Ho, Wo = case
+    _say(f"grouped conv2d case={case}")
+    c = qi.conv_case(sum([N, IC, H, W, OC, Kh, Kw, G]), N, IC, H, W, OC, Kh, Kw, s, p, d,
+                     H_out=Ho, W_out=Wo, groups=G)
+    np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
+    np.testing.assert_array_equal(_acc_conv(c), oracle.conv2d_acc(
+        c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out,
+        groups=G))
+
+
+def test_depthwise_large_workload():
+    """[8,256,64,64] depthwise 3x3 s1 p1, every output against the oracle."""
+    c = qi.make_depthwise_large()
+    _say("depthwise [8,256,64,64]")
+    np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
 
