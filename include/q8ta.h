@@ -124,6 +124,24 @@ q8ta_status q8ta_linear_gemv(const int8_t* x, int64_t M, int64_t K,
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * q8ta_linear followed by dequantize_per_tensor of its output, in one call
+ * (the q8ta_linear -> dequantize chain the [LIN] Problem section describes,
+ * with the dequantize folded into the epilogue):
+ *   out[m, n] = (float)(q[m, n] - output_zero_point) * (float)output_scale,
+ *   q = the int8 result q8ta_linear would produce for the same arguments.
+ * Bit-identical to the two calls; the int8 tensor is never written.
+ * out: fp32 [M, N] row-major.  Other arguments as for q8ta_linear.
+ */
+q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K,
+                           double input_scale, int64_t input_zero_point,
+                           const int8_t* weight, int64_t N,
+                           const int32_t* weight_sums,
+                           const float* weight_scales, const float* bias,
+                           double output_scale, int64_t output_zero_point,
+                           const char* activation, float* out,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * q8ta_conv2d_transposed ([DCV] Solution, Implementation, Constraints):
  *   acc[n,oc,oh,ow] = sum over (ic, kh, kw) of
  *       (x[n,ic,ih,iw] - input_zero_point) * weight[oc, (kh*Kw + kw)*IC + ic]
@@ -156,6 +174,33 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
                                    int64_t groups, const char* activation,
                                    int8_t* out, int64_t H_out, int64_t W_out,
                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * quantize_per_tensor followed by q8ta_conv2d_transposed, in one call (the
+ * chain the [DCV] Problem section describes, with the quantize folded into
+ * the transposed conv's input read): x is fp32 NCHW [N, IC, H_in, W_in] and is
+ * quantized with input_scale / input_zero_point exactly as
+ * q8ta_quantize_per_tensor would; the result is bit-identical to the two
+ * calls.  Other arguments, requirements and workspaces as for
+ * q8ta_conv2d_transposed (plus, off the implicit-GEMM path, an int8 copy of
+ * the quantized input).
+ */
+q8ta_status q8ta_quantize_conv2d_transposed(const float* x, int64_t N, int64_t IC,
+                                            int64_t H_in, int64_t W_in,
+                                            double input_scale, int64_t input_zero_point,
+                                            const int8_t* weight, int64_t OC,
+                                            int64_t Kh, int64_t Kw,
+                                            int64_t weight_row_stride,
+                                            const int32_t* weight_sums,
+                                            const float* weight_scales, const float* bias,
+                                            double output_scale, int64_t output_zero_point,
+                                            int64_t stride_h, int64_t stride_w,
+                                            int64_t pad_h, int64_t pad_w,
+                                            int64_t output_padding_h, int64_t output_padding_w,
+                                            int64_t dilation_h, int64_t dilation_w,
+                                            int64_t groups, const char* activation,
+                                            int8_t* out, int64_t H_out, int64_t W_out,
+                                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * q8ta_conv2d: the forward int8 convolution whose scaffold and weight layout

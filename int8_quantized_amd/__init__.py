@@ -52,6 +52,12 @@ SIGNATURES = {
     "q8ta_conv2d_transposed": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64, _I64, _I64,
                                 _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                 _I64, _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
+    "q8ta_linear_dq": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S, _P, _P],
+                       ctypes.c_int),
+    "q8ta_quantize_conv2d_transposed": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64,
+                                         _I64, _I64, _P, _P, _P, _DBL, _I64, _I64, _I64, _I64,
+                                         _I64, _I64, _I64, _I64, _I64, _I64, _S, _P, _I64, _I64,
+                                         _P], ctypes.c_int),
     "q8ta_linear_acc": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
     "q8ta_conv2d_transposed_acc": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64,
                                     _I64, _I64, _I64, _I64, _P, _I64, _I64, _P], ctypes.c_int),
@@ -190,6 +196,24 @@ def q8ta_linear_acc(x, input_zero_point, weight, acc, stream=None):
     return acc
 
 
+def q8ta_linear_dq(x, input_scale, input_zero_point, weight, weight_sums, weight_scales, bias,
+                   output_scale, output_zero_point, activation, out, stream=None):
+    """q8ta_linear then dequantize_per_tensor of its output, in one call:
+    fp32 out [M, N]."""
+    torch = _torch()
+    M, K = x.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("weight [N, K] and out [M, N] expected")
+    _check(lib().q8ta_linear_dq(
+        _dev(x, torch.int8, "x"), M, K, float(input_scale), int(input_zero_point),
+        _dev(weight, torch.int8, "weight"), N, _opt(weight_sums, torch.int32, "weight_sums"),
+        _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+        float(output_scale), int(output_zero_point), _act(activation),
+        _dev(out, torch.float32, "out"), _stream(stream)))
+    return out
+
+
 def q8ta_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw, weight_sums,
                            weight_scales, bias, output_scale, output_zero_point, stride, padding,
                            output_padding, dilation, groups, activation, out, stream=None):
@@ -211,6 +235,31 @@ def q8ta_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw, wei
         int(padding[0]), int(padding[1]), int(output_padding[0]), int(output_padding[1]),
         int(dilation[0]), int(dilation[1]), int(groups), _act(activation),
         _dev(out, torch.int8, "out"), H_out, W_out, _stream(stream)))
+    return out
+
+
+def q8ta_quantize_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw,
+                                    weight_sums, weight_scales, bias, output_scale,
+                                    output_zero_point, stride, padding, output_padding, dilation,
+                                    groups, activation, out, stream=None):
+    """quantize_per_tensor of the fp32 NCHW x, then q8ta_conv2d_transposed, in
+    one call (H_out, W_out taken from out)."""
+    torch = _torch()
+    if x.dim() != 4 or weight.dim() != 2 or out.dim() != 4:
+        raise ValueError("x [N,IC,H,W], weight [OC, ldw] and out [N,OC,H_out,W_out] expected")
+    N, IC, H_in, W_in = x.shape
+    OC, ldw = weight.shape
+    if out.shape[0] != N or out.shape[1] != OC:
+        raise ValueError("out must be [N, OC, H_out, W_out]")
+    _check(lib().q8ta_quantize_conv2d_transposed(
+        _dev(x, torch.float32, "x"), N, IC, H_in, W_in, float(input_scale),
+        int(input_zero_point), _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw,
+        _opt(weight_sums, torch.int32, "weight_sums"),
+        _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+        float(output_scale), int(output_zero_point), int(stride[0]), int(stride[1]),
+        int(padding[0]), int(padding[1]), int(output_padding[0]), int(output_padding[1]),
+        int(dilation[0]), int(dilation[1]), int(groups), _act(activation),
+        _dev(out, torch.int8, "out"), out.shape[2], out.shape[3], _stream(stream)))
     return out
 
 
@@ -273,6 +322,7 @@ def q8ta_conv2d_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, dilati
 
 __all__ = [
     "Q8taError", "lib", "q8ta_last_error", "q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor",
-    "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_acc", "q8ta_conv2d_transposed",
-    "q8ta_conv2d_transposed_acc", "q8ta_conv2d", "q8ta_conv2d_acc",
+    "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_dq", "q8ta_linear_acc", "q8ta_conv2d_transposed",
+    "q8ta_conv2d_transposed_acc", "q8ta_quantize_conv2d_transposed", "q8ta_conv2d",
+    "q8ta_conv2d_acc",
 ]

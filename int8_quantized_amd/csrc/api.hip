@@ -65,12 +65,15 @@ q8ta_status linear_checks(const char* op, const int8_t* x, int64_t M, int64_t K,
   return Q8TA_OK;
 }
 
+// out: int8 [M, N]; or, with outf set (out NULL), fp32 [M, N] = the
+// dequantized int8 result (fused dequantize_per_tensor with the output's own
+// scale and zero point).
 q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t M, int64_t K,
                         double input_scale, int64_t input_zero_point, const int8_t* weight, int64_t N,
                         const float* weight_scales, const float* bias, double output_scale,
                         int64_t output_zero_point, const char* activation, int8_t* out,
-                        hipStream_t stream) {
-  q8ta_status st = linear_checks(op, x, M, K, weight, N, out);
+                        hipStream_t stream, float* outf = nullptr) {
+  q8ta_status st = linear_checks(op, x, M, K, weight, N, outf ? (const void*)outf : out);
   if (st) return st;
   if (gemv_only && M != 1) return fail(Q8TA_ERR_SHAPE, "%s: M must be 1 (got %lld)", op, (long long)M);
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
@@ -82,6 +85,9 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
   a.M = M; a.K = K; a.N = N; a.izp = (int32_t)input_zero_point;
   a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  a.outf = outf;
+  a.dq_scale = (float)output_scale;
+  a.dq_zp = (int32_t)output_zero_point;
   return hip_status(launch_linear(a, stream), op);
 }
 
@@ -100,15 +106,37 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
 // GEMM) pays off from about 2^28 multiply-adds; smaller problems take the
 // direct tiled kernel.  Q8TA_DECONV_PATH = igemm | dot4 forces either one
 // where the shape allows it (used by the tests).
-hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
-  if (deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
+static bool deconv_wants_igemm(const DeconvArgs& a) {
   const char* e = getenv("Q8TA_DECONV_PATH");
   const double macs = (double)a.N * a.OC * a.H_out * a.W_out * a.IC * a.Kh * a.Kw /
                       ((double)a.sh * a.sw);
-  const bool want_igemm = e ? e[0] == 'i' : macs >= (double)(1 << 28);
-  if (want_igemm && deconv_igemm_supported(a)) return launch_deconv_igemm(a, s);
+  return (e ? e[0] == 'i' : macs >= (double)(1 << 28)) && deconv_igemm_supported(a);
+}
+
+hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
+  if (deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
+  if (deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
   if (deconv_dot4_supported(a)) return launch_deconv_dot4(a, s);
   return launch_deconv_generic(a, s);
+}
+
+// quantize_per_tensor -> transposed conv with an fp32 input (a.xf): the
+// implicit GEMM quantizes while it copies the input; the other paths quantize
+// into a stream-ordered int8 workspace first.
+hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
+  if (deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
+  const int64_t numel = a.N * a.IC * a.H_in * a.W_in;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, (size_t)numel, s);
+  if (e != hipSuccess) return e;
+  e = launch_quantize(a.xf, (int8_t*)ws, numel, a.inv_in, (float)a.izp, s);
+  if (e == hipSuccess) {
+    a.x = (const int8_t*)ws;
+    a.xf = nullptr;
+    e = launch_deconv(a, s);
+  }
+  hipError_t f = hipFreeAsync(ws, s);
+  return e != hipSuccess ? e : f;
 }
 
 // Forward conv: the implicit GEMM (groups 1, IC % 64 == 0), the depthwise
@@ -165,6 +193,17 @@ q8ta_status q8ta_linear_gemv(const int8_t* x, int64_t M, int64_t K, double input
   (void)weight_sums;
   return linear_impl("q8ta_linear_gemv", true, x, M, K, input_scale, input_zero_point, weight, N,
                      weight_scales, bias, output_scale, output_zero_point, activation, out, stream);
+}
+
+q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                           int64_t input_zero_point, const int8_t* weight, int64_t N,
+                           const int32_t* weight_sums, const float* weight_scales,
+                           const float* bias, double output_scale, int64_t output_zero_point,
+                           const char* activation, float* out, hipStream_t stream) {
+  (void)weight_sums;
+  return linear_impl("q8ta_linear_dq", false, x, M, K, input_scale, input_zero_point, weight, N,
+                     weight_scales, bias, output_scale, output_zero_point, activation, nullptr,
+                     stream, out);
 }
 
 q8ta_status q8ta_linear_acc(const int8_t* x, int64_t M, int64_t K, int64_t input_zero_point,
@@ -322,6 +361,42 @@ q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in
   a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
   return hip_status(launch_conv2d(a, stream), op);
+}
+
+
+q8ta_status q8ta_quantize_conv2d_transposed(
+    const float* x, int64_t N, int64_t IC, int64_t H_in, int64_t W_in, double input_scale,
+    int64_t input_zero_point, const int8_t* weight, int64_t OC, int64_t Kh, int64_t Kw,
+    int64_t weight_row_stride, const int32_t* weight_sums, const float* weight_scales,
+    const float* bias, double output_scale, int64_t output_zero_point, int64_t stride_h,
+    int64_t stride_w, int64_t pad_h, int64_t pad_w, int64_t output_padding_h,
+    int64_t output_padding_w, int64_t dilation_h, int64_t dilation_w, int64_t groups,
+    const char* activation, int8_t* out, int64_t H_out, int64_t W_out, hipStream_t stream) {
+  const char* op = "q8ta_quantize_conv2d_transposed";
+  (void)weight_sums;
+  (void)output_padding_h;
+  (void)output_padding_w;
+  q8ta_status st = deconv_checks(op, (const int8_t*)x, N, IC, H_in, W_in, weight, OC, Kh, Kw,
+                                 weight_row_stride, stride_h, stride_w, pad_h, pad_w, out, H_out,
+                                 W_out, IC);
+  if (st) return st;
+  if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
+  if (dilation_h != 1 || dilation_w != 1)
+    return fail(Q8TA_ERR_UNSUPPORTED, "%s: dilation must be 1 (got %lld, %lld)", op,
+                (long long)dilation_h, (long long)dilation_w);
+  if (groups != 1) return fail(Q8TA_ERR_UNSUPPORTED, "%s: groups must be 1 (got %lld)", op, (long long)groups);
+  if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
+  if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
+  if ((st = check_activation(op, activation))) return st;
+
+  DeconvArgs a{};
+  a.x = nullptr; a.xf = x; a.inv_in = recip(input_scale);
+  a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
+  a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
+  a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
+  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  return hip_status(launch_quantize_deconv(a, stream), op);
 }
 
 }  // extern "C"

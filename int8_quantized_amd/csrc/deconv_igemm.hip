@@ -60,13 +60,15 @@ struct Plan {
 };
 
 // x NCHW -> xp, NHWC inside a zero-point border: xp[n][hp][wp][c] =
-// x[n][c][hp - pt][wp - pl] inside the input, the zero-point byte outside.  16
+// x[n][c][hp - pt][wp - pl] inside the input, the zero-point byte outside (with
+// xf set, the fp32 input quantized on the way: quantize_per_tensor fused).  16
 // channels per thread: 16 byte loads (each load instruction reads 64
 // consecutive columns of one channel plane) packed into one 16-byte store.  t
 // enumerates (n, hp, g, wp) with wp fastest.
-__device__ __forceinline__ void relayout_one(const int8_t* __restrict__ x, int8_t* __restrict__ xp,
-                                             int64_t N, int C, int H, int W, const Plan& plan,
-                                             int zp, int64_t t) {
+__device__ __forceinline__ void relayout_one(const int8_t* __restrict__ x,
+                                             const float* __restrict__ xf, float inv_in,
+                                             int8_t* __restrict__ xp, int64_t N, int C, int H,
+                                             int W, const Plan& plan, int zp, int64_t t) {
   const int G = C / 16;
   if (t >= N * plan.Hpad * G * plan.Wpad) return;
   const int wp = (int)(t % plan.Wpad);
@@ -79,13 +81,26 @@ __device__ __forceinline__ void relayout_one(const int8_t* __restrict__ x, int8_
   uint32_t d[4];
   if (h >= 0 && h < H && w >= 0 && w < W) {
     const int64_t plane = (int64_t)H * W;
-    const int8_t* src = x + (n * C + g * 16) * plane + (int64_t)h * W + w;
+    const int64_t off = (n * C + g * 16) * plane + (int64_t)h * W + w;
+    if (xf) {  // fused quantize of the fp32 input
+      const float* src = xf + off;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t v = 0;
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) v |= (uint32_t)(uint8_t)src[(q * 4 + b) * plane] << (8 * b);
-      d[q] = v;
+        for (int b = 0; b < 4; ++b)
+          v |= (uint32_t)(quantize1(src[(q * 4 + b) * plane], inv_in, (float)zp) & 0xff) << (8 * b);
+        d[q] = v;
+      }
+    } else {
+      const int8_t* src = x + off;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v |= (uint32_t)(uint8_t)src[(q * 4 + b) * plane] << (8 * b);
+        d[q] = v;
+      }
     }
   } else {
 #pragma unroll
@@ -126,8 +141,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(DeconvArgs a, Phases p, Plan 
                                                    int64_t relayout_blocks) {
   const int64_t b = blockIdx.x;
   if (b < relayout_blocks) {
-    relayout_one(a.x, xp, a.N, (int)a.IC, (int)a.H_in, (int)a.W_in, plan, (int)a.izp,
-                 b * kThreads + threadIdx.x);
+    relayout_one(a.x, a.xf, a.inv_in, xp, a.N, (int)a.IC, (int)a.H_in, (int)a.W_in, plan,
+                 (int)a.izp, b * kThreads + threadIdx.x);
   } else {
     const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     phase_wsum_one(a, p, plan, wsum, (b - relayout_blocks) * (kThreads / 64) + wave);

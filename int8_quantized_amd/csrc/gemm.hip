@@ -245,7 +245,7 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 constexpr bool kMfmaGemmEnabled = false;
 
 bool gemm_mfma_supported(const LinearArgs& a) {
-  return kMfmaGemmEnabled && (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w) &&
+  return kMfmaGemmEnabled && !a.outf && (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w) &&
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 

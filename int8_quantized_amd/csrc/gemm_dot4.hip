@@ -236,6 +236,22 @@ __global__ __launch_bounds__(kThreads) void k_dot4_gemm(LinearArgs a, uint32_t B
       const float bv = (ok && a.bias) ? a.bias[nb + t] : 0.0f;
       q[t] = requant(cv[t], sc, bv, a.rq);
     }
+    if (a.outf) {
+      float* of = a.outf + mm * a.N + nb;
+      if (nb + C <= a.N && ((uintptr_t)of & 15) == 0) {
+        typedef float v4f __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int t = 0; t < C; t += 4)
+          *reinterpret_cast<v4f*>(of + t) =
+              v4f{dequant1(q[t], a.dq_zp, a.dq_scale), dequant1(q[t + 1], a.dq_zp, a.dq_scale),
+                  dequant1(q[t + 2], a.dq_zp, a.dq_scale), dequant1(q[t + 3], a.dq_zp, a.dq_scale)};
+      } else {
+#pragma unroll
+        for (int t = 0; t < C; ++t)
+          if (nb + t < a.N) of[t] = dequant1(q[t], a.dq_zp, a.dq_scale);
+      }
+      continue;
+    }
     int8_t* o = a.out + mm * a.N + nb;
     if (nb + C <= a.N && ((uintptr_t)o & 3) == 0) {
 #pragma unroll

@@ -96,7 +96,11 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
       if (a.acc) {
         a.acc[m * a.N + n] = mine;
       } else {
-        a.out[m * a.N + n] = (int8_t)requant(mine, sc_pre, b_pre, a.rq);
+        const int q = requant(mine, sc_pre, b_pre, a.rq);
+        if (a.outf)
+          a.outf[m * a.N + n] = dequant1(q, a.dq_zp, a.dq_scale);
+        else
+          a.out[m * a.N + n] = (int8_t)q;
       }
     }
   }

@@ -22,7 +22,11 @@ __global__ __launch_bounds__(kThreads) void k_linear_generic(LinearArgs a) {
     a.acc[idx] = acc;
   } else {
     float b = a.bias ? a.bias[n] : 0.0f;
-    a.out[idx] = (int8_t)requant(acc, a.wscale[n], b, a.rq);
+    const int q = requant(acc, a.wscale[n], b, a.rq);
+    if (a.outf)
+      a.outf[idx] = dequant1(q, a.dq_zp, a.dq_scale);
+    else
+      a.out[idx] = (int8_t)q;
   }
 }
 

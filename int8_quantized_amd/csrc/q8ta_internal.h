@@ -36,6 +36,23 @@ __device__ __forceinline__ int requant(int32_t acc, float wscale, float b, const
   return (int)q;
 }
 
+// quantize_per_tensor of one value ("Add quantize_per_tensor op (int8 buffer
+// path)", commit message): clamp(rint(x * inv) + zp, -128, 127), inv formed on
+// the host as (float)(1.0 / scale).
+__device__ __forceinline__ int quantize1(float x, float inv, float zp) {
+  float t = x * inv;
+  float r = __builtin_rintf(t);
+  float u = r + zp;
+  u = __builtin_fmaxf(u, -128.0f);
+  u = __builtin_fminf(u, 127.0f);
+  return (int)u;
+}
+
+// dequantize_per_tensor of one int8 value: (float)(q - zp) * scale.
+__device__ __forceinline__ float dequant1(int q, int zp, float scale) {
+  return (float)(q - zp) * scale;
+}
+
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
          ((uint32_t)(d & 0xff) << 24);
@@ -121,11 +138,16 @@ struct LinearArgs {
   const int8_t* w;
   const float* wscale;
   const float* bias;  // may be NULL
-  int8_t* out;        // int8 [M, N] (NULL when acc is set)
+  int8_t* out;        // int8 [M, N] (NULL when acc or outf is set)
   int32_t* acc;       // int32 [M, N] accumulator output (NULL for the int8 op)
   int64_t M, K, N;
   int32_t izp;
   Requant rq;
+  // Fused dequantize: when set, the kernels write fp32 [M, N] =
+  // (float)(q - dq_zp) * dq_scale of the requantized q instead of q itself.
+  float* outf = nullptr;
+  float dq_scale = 0.0f;
+  int32_t dq_zp = 0;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
@@ -143,11 +165,17 @@ struct DeconvArgs {
   Requant rq;
   int64_t dil_h = 1, dil_w = 1;  // forward conv only (the transposed op takes 1)
   int64_t groups = 1;            // forward conv only: IC and OC split into equal groups
+  // Fused quantize: when xf is set (x NULL), the input is fp32 NCHW and is
+  // quantized on the fly with inv_in = (float)(1/input_scale) and the input
+  // zero point, exactly as quantize_per_tensor would.
+  const float* xf = nullptr;
+  float inv_in = 0.0f;
 };
 // The same arguments describe the forward q8ta_conv2d (stride, padding and
 // dilation of the forward index relation).
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s);
+hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s);
 
 // Stride phases of a transposed conv, built on the host: for row residue r
 // (output rows oh = r + s_h*i) the nth[r] qualifying kernel rows thk[r][t] read

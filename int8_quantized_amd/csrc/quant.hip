@@ -23,14 +23,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
-__device__ __forceinline__ int quant1(float x, float inv, float zp) {
-  float t = x * inv;
-  float r = __builtin_rintf(t);
-  float u = r + zp;
-  u = __builtin_fmaxf(u, -128.0f);
-  u = __builtin_fminf(u, 127.0f);
-  return (int)u;
-}
+__device__ __forceinline__ int quant1(float x, float inv, float zp) { return quantize1(x, inv, zp); }
 
 // x: fp32, 16-byte aligned; out: int8, 4-byte aligned.  n4 = numel / 4 groups;
 // block 0 also converts the numel % 4 trailing elements one by one.

@@ -215,6 +215,26 @@ def test_conv2d_acc_errors():
     _st(f(*a), q8.Q8TA_ERR_QPARAM)
 
 
+def test_fused_entry_points_errors():
+    l = q8.lib()
+    # q8ta_linear_dq: same checks as q8ta_linear
+    _st(l.q8ta_linear_dq(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", None,
+                         None), q8.Q8TA_ERR_NULL)
+    _st(l.q8ta_linear_dq(FAKE, 0, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE,
+                         None), q8.Q8TA_ERR_SHAPE)
+    _st(l.q8ta_linear_dq(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"relu", FAKE,
+                         None), q8.Q8TA_ERR_UNSUPPORTED)
+    # q8ta_quantize_conv2d_transposed: same checks as q8ta_conv2d_transposed
+    args = [FAKE, 1, 64, 32, 32, 0.02, 3, FAKE, 32, 4, 4, 1024, None, FAKE, FAKE, 0.54, -5, 2, 2,
+            1, 1, 0, 0, 1, 1, 1, b"none", FAKE, 64, 64, None]
+    a = list(args); a[0] = None
+    _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_NULL)
+    a = list(args); a[23] = 2
+    _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_UNSUPPORTED, "dilation")
+    a = list(args); a[5] = -1.0
+    _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_QPARAM)
+
+
 def _gpu_present():
     try:
         import torch

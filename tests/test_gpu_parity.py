@@ -579,3 +579,74 @@ def test_depthwise_large_workload():
     _say("depthwise [8,256,64,64]")
     np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
 
+
+# ============================================================================ fused chains
+DQ_SHAPES = [(1, 4096, 4096), (3, 48, 17), (4, 64, 32), (65, 320, 97), (300, 1040, 257),
+             (129, 2064, 129), (7, 33, 5), (40, 100, 70), (64, 128, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", DQ_SHAPES)
+def test_linear_dq_equals_linear_then_dequantize(M, K, N):
+    """q8ta_linear_dq == dequantize_per_tensor(q8ta_linear(...)) bit for bit,
+    against the oracle's two steps."""
+    _say(f"linear_dq M={M} K={K} N={N}")
+    c = qi.linear_case(M * 3 + K + N, M, K, N)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                      dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    ref = oracle.dequantize_per_tensor(_oracle_linear(c), c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+
+
+def test_linear_dq_gemm_workload_sampled():
+    c = qi.make_gemm()
+    _say("linear_dq 2048x4096x11008")
+    out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                      dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    got = host(out)
+    rows = np.array([0, 1, 2, 511, 1024, 1025, 2046, 2047])
+    q = oracle.linear(c.x[rows], c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                      c.out_zp)
+    ref = oracle.dequantize_per_tensor(q, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(got[rows].view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_IGEMM_CASES[1],
+                                  DECONV_IGEMM_CASES[5], DECONV_CASES[14]],
+                         ids=["k3s2", "mixed", "igemm_oc40", "igemm_tall", "general"])
+@pytest.mark.parametrize("path", ["igemm", "dot4"])
+def test_quantize_conv2d_transposed_equals_the_chain(case, path):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
+    _say(f"quantize+deconv {path} case={case}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC]) + 5, N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho,
+                       W_out=Wo, ldw=Kh * Kw * IC + extra, x_from_fp32=True)
+    out = torch.empty((N, OC, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+    with env(Q8TA_DECONV_PATH=path):
+        q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh,
+                                           c.Kw, None, dev(c.weight_scales), dev(c.bias),
+                                           c.out_scale, c.out_zp, c.stride, c.padding,
+                                           c.output_padding, (1, 1), 1, "none", out)
+    xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    ref = oracle.conv2d_transposed(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                   c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding, (1, 1),
+                                   c.H_out, c.W_out)
+    np.testing.assert_array_equal(host(out), ref)
+
+
+def test_quantize_conv2d_transposed_large_workload_sampled():
+    c = qi.make_deconv_large()
+    _say("quantize+deconv fused [8,256,64,64] -> [8,128,128,128]")
+    out = torch.empty((8, 128, 128, 128), dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw,
+                                       None, dev(c.weight_scales), dev(c.bias), c.out_scale,
+                                       c.out_zp, c.stride, c.padding, c.output_padding, (1, 1), 1,
+                                       "none", out)
+    got = host(out)
+    xq = oracle.quantize_per_tensor(c.x_fp32[7:8], c.in_scale, c.in_zp)
+    chans = np.array([0, 1, 64, 127, 33, 98])
+    ref = oracle.conv2d_transposed(xq, c.w[chans], c.weight_scales[chans], c.bias[chans],
+                                   c.in_scale, c.in_zp, c.out_scale, c.out_zp, c.Kh, c.Kw,
+                                   c.stride, c.padding, (1, 1), c.H_out, c.W_out)
+    np.testing.assert_array_equal(got[7:8, chans], ref)
+
