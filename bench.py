@@ -129,16 +129,20 @@ class Timer:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first: the GPU clock settles over the first tens of ms")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--step", choices=["fused", "chain"], default="fused",
+                    help="fused: one q8ta_linear_dq call (the dequantize folded into the GEMM "
+                         "epilogue); chain: q8ta_linear then q8ta_dequantize_per_tensor")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--profile-only", choices=["gemm-and-copy", "deconv"], default=None,
-                    help="for hardware-counter runs: launch the GEMM `--steps` times and the "
-                         "256 MiB calibration copy 3 times (gemm-and-copy), or the large "
-                         "transposed conv `--steps` times (deconv); print nothing else")
+                    help="for hardware-counter runs: run `--steps` steps of the GEMM workload "
+                         "and the 256 MiB calibration copy 3 times (gemm-and-copy), or the "
+                         "large transposed conv `--steps` times (deconv); print nothing else")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -186,6 +190,18 @@ def main():
         check(lib.q8ta_dequantize_per_tensor(out.data_ptr(), y.data_ptr(), M * N, c.out_scale,
                                              c.out_zp, stream))
 
+    def gemm_dq():
+        check(lib.q8ta_linear_dq(x.data_ptr(), M, K, c.in_scale, c.in_zp, w.data_ptr(), N, None,
+                                 ws.data_ptr(), b.data_ptr(), c.out_scale, c.out_zp, none,
+                                 y.data_ptr(), stream))
+
+    # A step is the whole workload, q8ta_linear -> dequantize_per_tensor; `call`
+    # is the GEMM call the roofline times (the fused call is the whole step).
+    if args.step == "fused":
+        call, rest = gemm_dq, (lambda: None)
+    else:
+        call, rest = gemm, deq
+
     if args.profile_only == "deconv":
         d = qi.make_deconv_large()
         xq = torch.empty(d.x_fp32.shape, dtype=torch.int8, device="cuda")
@@ -210,15 +226,16 @@ def main():
 
     if args.profile_only == "gemm-and-copy":
         for _ in range(args.steps):
-            gemm()
+            call()
+            rest()
         torch.cuda.synchronize()
         profile_copy(torch, stream)
-        log(f"profiled {args.steps} GEMM launches and 3 copies of 256 MiB")
+        log(f"profiled {args.steps} steps ({args.step}) and 3 copies of 256 MiB")
         return
 
     for _ in range(args.warmup):
-        gemm()
-        deq()
+        call()
+        rest()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -226,9 +243,9 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record()
-        gemm()
+        call()
         ev[i][1].record()
-        deq()
+        rest()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
@@ -238,6 +255,19 @@ def main():
     achieved = ops / gemm_avg_s / 1e12
     log(f"step {step_s * 1e6:.1f} us; GEMM avg {gemm_avg_s * 1e6:.1f} us "
         f"(min {min(gemm_ms) * 1e3:.1f}) = {achieved:.1f} TOPS")
+
+    # The int8 result for the checks below (outside the timed region); in the
+    # fused form the step's fp32 output must equal dequantize(int8 result).
+    gemm()
+    torch.cuda.synchronize()
+    fused_ok = None
+    if args.step == "fused":
+        deq_ref = torch.empty_like(y)
+        check(lib.q8ta_dequantize_per_tensor(out.data_ptr(), deq_ref.data_ptr(), M * N,
+                                             c.out_scale, c.out_zp, stream))
+        torch.cuda.synchronize()
+        fused_ok = bool(torch.equal(y.view(torch.int32), deq_ref.view(torch.int32)))
+        del deq_ref
 
     # The matrix-core GEMM is switched off; q8ta_linear with M > 4 runs the
     # vector-ALU v_dot4 kernel, whose own ceiling is PEAK_DOT4_TOPS.
@@ -277,7 +307,14 @@ def main():
     # ------------------------------------------------------------ the other workloads
     extra = {}
     if not args.no_extra:
-        extra = run_extra(torch, np, q8, qi, lib, stream, timer, check)
+        def chain():
+            gemm()
+            deq()
+        for name, fn in (("gemm_step_chain_us", chain), ("gemm_step_fused_us", gemm_dq)):
+            extra[name] = round(min(timer.time_calls([fn], 10, batches=3)) * 1e3, 1)
+        log(f"  step forms: chain {extra['gemm_step_chain_us']} us, "
+            f"fused {extra['gemm_step_fused_us']} us")
+        extra.update(run_extra(torch, np, q8, qi, lib, stream, timer, check))
         extra["ceilings"] = run_ceilings(torch, stream, timer)
         log(f"  ceilings: {extra['ceilings']}")
 
@@ -287,7 +324,10 @@ def main():
         "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": "q8ta_linear GEMM M=2048 K=4096 N=11008 -> dequantize_per_tensor",
-                   "M": M, "K": K, "N": N, "parallelism": "none (1 GPU)"},
+                   "M": M, "K": K, "N": N, "parallelism": "none (1 GPU)",
+                   "step": ("one q8ta_linear_dq call (dequantize folded into the GEMM epilogue; "
+                            "output equal to the two-call chain: %s)" % fused_ok)
+                   if args.step == "fused" else "q8ta_linear, then q8ta_dequantize_per_tensor"},
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
@@ -422,6 +462,23 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     r["frac_of_dot4_peak"] = round(r["rate"] / PEAK_DOT4_TOPS, 4)
     res["deconv_8x256x64x64_k3s2p1_to_8x128x128x128"] = r
     del qs, dfns
+
+    # quantize -> transposed conv as one call (quantize folded into the input copy)
+    xs = [torch.from_numpy(d.x_fp32).cuda() for _ in range(copies)]
+
+    def qdc(xf):
+        check(lib.q8ta_quantize_conv2d_transposed(
+            xf.data_ptr(), N_, IC, H, W, d.in_scale, d.in_zp, w_.data_ptr(), OC, d.Kh, d.Kw,
+            d.w.shape[1], None, dws.data_ptr(), db.data_ptr(), d.out_scale, d.out_zp,
+            d.stride[0], d.stride[1], d.padding[0], d.padding[1], d.output_padding[0],
+            d.output_padding[1], 1, 1, 1, b"none", dout.data_ptr(), d.H_out, d.W_out, stream))
+    qfns = [(lambda i=i: qdc(xs[i])) for i in range(copies)]
+    timer.time_calls(qfns, copies)
+    r = summary(timer.time_calls(qfns, 4 * copies), dops, "TOPS", PEAK_INT8_TOPS)
+    r["exact_valid_tap_ops"] = dops
+    r["note"] = "one call: quantize [8,256,64,64] fp32 (cold) + transposed conv"
+    res["quantize_deconv_fused_8x256x64x64"] = r
+    del xs, qfns
 
     # ---- dequantize [2048, 11008] (rotate 8 copies of 22.5 MB in / 90 MB out)
     log("extra: dequantize [2048,11008]")
