@@ -70,7 +70,8 @@ __global__ __launch_bounds__(kThreads) void k_depthwise(DeconvArgs a) {
   }
 }
 
-template <int K, int S>
+// DW: rows are read as 32-bit words (W_in % 4 == 0 and 4-byte aligned input).
+template <int K, int S, bool DW>
 __global__ __launch_bounds__(kThreads) void k_depthwise_patch(DeconvArgs a) {
   constexpr int P = 4;                   // outputs per patch side
   constexpr int WN = (P - 1) * S + K;    // input window side
@@ -84,27 +85,61 @@ __global__ __launch_bounds__(kThreads) void k_depthwise_patch(DeconvArgs a) {
   const int ih0 = oh0 * S - (int)a.ph, iw0 = ow0 * S - (int)a.pw;
   const int8_t* xp = a.x + plane_id * (int64_t)H_in * W_in;
   const int izp = a.izp;
-  // Every load reads a clamped, in-range address (no branch around it); the
-  // select afterwards zeroes the pixels outside the input.
-  int iwc[WN];
+  int win[WN][WN];  // x - izp inside the input, 0 outside
   bool cok[WN];
 #pragma unroll
-  for (int q = 0; q < WN; ++q) {
-    const int iw = iw0 + q;
-    cok[q] = iw >= 0 && iw < W_in;
-    iwc[q] = iw < 0 ? 0 : (iw >= W_in ? W_in - 1 : iw);
-  }
-  int win[WN][WN];  // x - izp inside the input, 0 outside
+  for (int q = 0; q < WN; ++q) cok[q] = iw0 + q >= 0 && iw0 + q < W_in;
+  if constexpr (DW) {
+    // Rows as 32-bit words (W_in % 4 == 0, 4-byte aligned planes): the window
+    // starts `shift` bytes into word dq0 (shift is the same for every thread:
+    // iw0 = ow0*S - pad_w with ow0*S a multiple of 4); ND clamped word loads
+    // per row, realigned with v_alignbyte, then one signed byte per column.
+    constexpr int ND = (WN + 3) / 4 + 1;
+    const int shift = (4 - ((int)a.pw & 3)) & 3;
+    const int dq0 = (iw0 - shift) / 4;
+    const int nwords = W_in / 4;
 #pragma unroll
-  for (int r = 0; r < WN; ++r) {
-    const int ih = ih0 + r;
-    const bool rok = ih >= 0 && ih < H_in;
-    const int8_t* row = xp + (int64_t)(ih < 0 ? 0 : (ih >= H_in ? H_in - 1 : ih)) * W_in;
+    for (int r = 0; r < WN; ++r) {
+      const int ih = ih0 + r;
+      const bool rok = ih >= 0 && ih < H_in;
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(
+          xp + (int64_t)(ih < 0 ? 0 : (ih >= H_in ? H_in - 1 : ih)) * W_in);
+      uint32_t d[ND];
+#pragma unroll
+      for (int k = 0; k < ND; ++k) {
+        const int dk = dq0 + k;
+        d[k] = row[dk < 0 ? 0 : (dk >= nwords ? nwords - 1 : dk)];
+        asm volatile("" : "+v"(d[k]));  // unconditional load (no branch around it)
+      }
+      uint32_t e[ND - 1];
+#pragma unroll
+      for (int k = 0; k < ND - 1; ++k) e[k] = __builtin_amdgcn_alignbyte(d[k + 1], d[k], shift);
+#pragma unroll
+      for (int q = 0; q < WN; ++q) {
+        const int v = (int)(int8_t)(e[q / 4] >> (8 * (q % 4))) - izp;
+        win[r][q] = v & -(int)(rok && cok[q]);  // arithmetic select, no branch
+      }
+    }
+  } else {
+    // Byte loads from clamped, in-range addresses (no branch around them); the
+    // select afterwards zeroes the pixels outside the input.
+    int iwc[WN];
 #pragma unroll
     for (int q = 0; q < WN; ++q) {
-      int v = (int)row[iwc[q]] - izp;
-      asm volatile("" : "+v"(v));  // keep the load unconditional (no branch around it)
-      win[r][q] = (rok && cok[q]) ? v : 0;
+      const int iw = iw0 + q;
+      iwc[q] = iw < 0 ? 0 : (iw >= W_in ? W_in - 1 : iw);
+    }
+#pragma unroll
+    for (int r = 0; r < WN; ++r) {
+      const int ih = ih0 + r;
+      const bool rok = ih >= 0 && ih < H_in;
+      const int8_t* row = xp + (int64_t)(ih < 0 ? 0 : (ih >= H_in ? H_in - 1 : ih)) * W_in;
+#pragma unroll
+      for (int q = 0; q < WN; ++q) {
+        int v = (int)row[iwc[q]] - izp;
+        asm volatile("" : "+v"(v));  // keep the load unconditional (no branch around it)
+        win[r][q] = (rok && cok[q]) ? v : 0;
+      }
     }
   }
   const cbptr wc = (cbptr)(a.w + c * a.ldw);
@@ -155,7 +190,11 @@ template <int K, int S>
 hipError_t launch_patch(const DeconvArgs& a, hipStream_t s) {
   const int64_t items = ((a.H_out + 3) / 4) * ((a.W_out + 3) / 4);
   const dim3 grid((unsigned)((items + kThreads - 1) / kThreads), (unsigned)(a.N * a.OC));
-  hipLaunchKernelGGL((k_depthwise_patch<K, S>), grid, dim3(kThreads), 0, s, a);
+  const bool dw = a.W_in % 4 == 0 && ((uintptr_t)a.x & 3) == 0;
+  if (dw)
+    hipLaunchKernelGGL((k_depthwise_patch<K, S, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_depthwise_patch<K, S, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
