@@ -97,6 +97,13 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
+def _relu_flag(activation: str) -> int:
+    """"none" -> 0, "relu" -> 1 (the relu-fused follow-up of #21197/#21205)."""
+    if activation not in ("none", "relu"):
+        raise ValueError(f"unknown activation {activation!r}")
+    return 1 if activation == "relu" else 0
+
+
 # ---------------------------------------------------------------------------
 def quantize_per_tensor(x, scale: float, zero_point: int) -> np.ndarray:
     """#21187 Solution/Implementation: clamp(round(x*inv_scale)+zp, -128, 127),
@@ -119,10 +126,13 @@ def dequantize_per_tensor(q, scale: float, zero_point: int) -> np.ndarray:
 
 
 def epilogue(acc, channels: int, inner: int, input_scale: float, weight_scales, bias,
-             output_scale: float, output_zero_point: int, return_pre: bool = False):
+             output_scale: float, output_zero_point: int, return_pre: bool = False,
+             activation: str = "none"):
     """#21197/#21205 Solution: v = acc*input_scale*weight_scales[c] + bias[c];
     q = clamp(round(v*inv_output_scale) + output_zero_point, -128, 127).
-    Element e belongs to channel (e // inner) % channels."""
+    Element e belongs to channel (e // inner) % channels.  activation="relu"
+    (the pages' relu-fused follow-up) requantizes max(v, 0) instead of v;
+    return_pre gives v before the rectifier."""
     acc = _c(acc, np.int32)
     ws = _c(weight_scales, np.float32)
     b = None if bias is None else _c(bias, np.float32)
@@ -130,7 +140,8 @@ def epilogue(acc, channels: int, inner: int, input_scale: float, weight_scales, 
     pre = np.empty(acc.shape, np.float32) if return_pre else None
     _chk(_load().oracle_epilogue(_p(acc), _c_i64(acc.size), _c_i64(channels), _c_i64(inner),
                                  _c_dbl(input_scale), _p(ws), _p(b), _c_dbl(output_scale),
-                                 _c_i64(output_zero_point), _p(out), _p(pre)), "epilogue")
+                                 _c_i64(output_zero_point), _c_i64(_relu_flag(activation)),
+                                 _p(out), _p(pre)), "epilogue")
     return (out, pre) if return_pre else out
 
 
@@ -149,7 +160,8 @@ def linear_acc(x, w, input_zero_point: int, folded: bool = False) -> np.ndarray:
 
 
 def linear(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
-           output_scale: float, output_zero_point: int, return_acc: bool = False):
+           output_scale: float, output_zero_point: int, return_acc: bool = False,
+           activation: str = "none"):
     """q8ta_linear (#21197 Solution): contraction then per-channel epilogue.
     x int8 [M,K] row-major, w int8 [N,ldw] row-major (only [:, :K] is read)."""
     x = _c(x, np.int8)
@@ -163,7 +175,7 @@ def linear(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
     _chk(_load().oracle_linear(_p(x), _c_i64(M), _c_i64(K), _c_dbl(input_scale),
                                _c_i64(input_zero_point), _p(w), _c_i64(N), _c_i64(ldw),
                                _p(ws), _p(b), _c_dbl(output_scale), _c_i64(output_zero_point),
-                               _p(out), _p(acc)), "linear")
+                               _c_i64(_relu_flag(activation)), _p(out), _p(acc)), "linear")
     return (out, acc) if return_acc else out
 
 
@@ -179,9 +191,11 @@ def _deconv_args(x, w, Kh, Kw, stride, padding, dilation):
 
 
 def deconv_acc(x, w, input_zero_point: int, Kh: int, Kw: int, stride, padding, dilation,
-               H_out: int, W_out: int, method: str = "gather") -> np.ndarray:
+               H_out: int, W_out: int, method: str = "gather", groups: int = 1) -> np.ndarray:
     """#21205 Solution gather (method="gather"); the scatter and zero-point-fill
-    formulations ("scatter", "zpfill") exist only to check it."""
+    formulations ("scatter", "zpfill") exist only to check it.  With groups,
+    output channel oc sums over the input channels of its group only,
+    w[oc, (kh*Kw+kw)*(IC/groups) + icg]."""
     x, w, (N, IC, H_in, W_in, OC, ldw, sh, sw, ph, pw, dh, dw) = _deconv_args(
         x, w, Kh, Kw, stride, padding, dilation)
     acc = np.empty((N, OC, H_out, W_out), np.int32)
@@ -190,18 +204,19 @@ def deconv_acc(x, w, input_zero_point: int, Kh: int, Kw: int, stride, padding, d
           "zpfill": _load().oracle_deconv_acc_zpfill}[method]
     _chk(fn(_p(x), _c_i64(N), _c_i64(IC), _c_i64(H_in), _c_i64(W_in), _c_i64(input_zero_point),
             _p(w), _c_i64(OC), _c_i64(Kh), _c_i64(Kw), _c_i64(ldw), _c_i64(sh), _c_i64(sw),
-            _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(H_out), _c_i64(W_out),
-            _p(acc)), "deconv_acc")
+            _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(groups), _c_i64(H_out),
+            _c_i64(W_out), _p(acc)), "deconv_acc")
     return acc
 
 
 def conv2d_transposed(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
                       output_scale: float, output_zero_point: int, Kh: int, Kw: int,
                       stride, padding, dilation, H_out: int, W_out: int,
-                      return_acc: bool = False):
+                      return_acc: bool = False, groups: int = 1, activation: str = "none"):
     """q8ta_conv2d_transposed (#21205 Solution): gather contraction then the
     per-channel epilogue with channel = oc.  x int8 NCHW, w int8 [OC, ldw] with
-    w[oc, (kh*Kw+kw)*IC + ic]; output int8 NCHW [N, OC, H_out, W_out]."""
+    w[oc, (kh*Kw+kw)*IC + ic] (IC/groups per row when grouped); output int8 NCHW
+    [N, OC, H_out, W_out]."""
     x, w, (N, IC, H_in, W_in, OC, ldw, sh, sw, ph, pw, dh, dw) = _deconv_args(
         x, w, Kh, Kw, stride, padding, dilation)
     ws = _c(weight_scales, np.float32)
@@ -212,8 +227,9 @@ def conv2d_transposed(x, w, weight_scales, bias, input_scale: float, input_zero_
         _p(x), _c_i64(N), _c_i64(IC), _c_i64(H_in), _c_i64(W_in), _c_dbl(input_scale),
         _c_i64(input_zero_point), _p(w), _c_i64(OC), _c_i64(Kh), _c_i64(Kw), _c_i64(ldw),
         _p(ws), _p(b), _c_dbl(output_scale), _c_i64(output_zero_point), _c_i64(sh),
-        _c_i64(sw), _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(H_out),
-        _c_i64(W_out), _p(out), _p(acc)), "conv2d_transposed")
+        _c_i64(sw), _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(groups),
+        _c_i64(H_out), _c_i64(W_out), _c_i64(_relu_flag(activation)), _p(out), _p(acc)),
+        "conv2d_transposed")
     return (out, acc) if return_acc else out
 
 
@@ -236,7 +252,8 @@ def conv2d_acc(x, w, input_zero_point: int, Kh: int, Kw: int, stride, padding, d
 
 def conv2d(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
            output_scale: float, output_zero_point: int, Kh: int, Kw: int, stride, padding,
-           dilation, H_out: int, W_out: int, return_acc: bool = False, groups: int = 1):
+           dilation, H_out: int, W_out: int, return_acc: bool = False, groups: int = 1,
+           activation: str = "none"):
     """Forward q8ta_conv2d: contraction then the per-channel epilogue with
     channel = oc.  x int8 NCHW, w int8 [OC, ldw] with w[oc, (kh*Kw+kw)*IC + ic];
     output int8 NCHW [N, OC, H_out, W_out]."""
@@ -251,5 +268,6 @@ def conv2d(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
         _c_i64(input_zero_point), _p(w), _c_i64(OC), _c_i64(Kh), _c_i64(Kw), _c_i64(ldw),
         _p(ws), _p(b), _c_dbl(output_scale), _c_i64(output_zero_point), _c_i64(sh),
         _c_i64(sw), _c_i64(ph), _c_i64(pw), _c_i64(dh), _c_i64(dw), _c_i64(groups),
-        _c_i64(H_out), _c_i64(W_out), _p(out), _p(acc)), "conv2d")
+        _c_i64(H_out), _c_i64(W_out), _c_i64(_relu_flag(activation)), _p(out), _p(acc)),
+        "conv2d")
     return (out, acc) if return_acc else out

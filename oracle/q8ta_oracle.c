@@ -26,6 +26,8 @@
  *     rounding per operation: ((float(acc) * s_in) * w_scale[c]) + bias[c],
  *     then * inv_out, round, + zero_point, clamp to [-128, 127];
  *   - a NULL bias means no bias term;
+ *   - the relu-fused activation (a follow-up the pages keep fail-loud) is
+ *     max(v, 0) on the real-valued output v, before it is requantized;
  *   - dequantize is float(q - zp) * float(scale).
  * Integer sums are formed in int64 and each result is checked to fit int32;
  * the functions return a non-zero code if not (or on a bad argument).
@@ -78,12 +80,16 @@ int oracle_dequantize_per_tensor(const int8_t* q, float* out, int64_t numel,
  * v = acc * input_scale * weight_scales[c] + bias[c];
  * q = clamp(round(v * inv_output_scale) + output_zero_point, -128, 127).
  * The element at flat index e belongs to channel (e / inner) % channels.
- * pre (optional) receives v, the value just before the requantize multiply. */
+ * pre (optional) receives v, the value just before the requantize multiply.
+ * relu != 0 is the relu-fused activation, which the pages leave as a fail-loud
+ * follow-up (#21197 Implementation and Constraints, #21205 Constraints): the
+ * rectifier acts on the real-valued output, v = max(v, 0), before it is
+ * requantized. */
 int oracle_epilogue(const int32_t* acc, int64_t numel, int64_t channels,
                     int64_t inner, double input_scale,
                     const float* weight_scales, const float* bias,
                     double output_scale, int64_t output_zero_point,
-                    int8_t* out, float* pre) {
+                    int64_t relu, int8_t* out, float* pre) {
   if (numel < 0 || channels <= 0 || inner <= 0) return ORACLE_BAD_ARG;
   if (numel > 0 && (!acc || !out || !weight_scales)) return ORACLE_BAD_ARG;
   const float s_in = (float)input_scale;
@@ -97,6 +103,7 @@ int oracle_epilogue(const int32_t* acc, int64_t numel, int64_t channels,
     v = v * weight_scales[c];
     if (bias) v = v + bias[c];
     if (pre) pre[e] = v;
+    if (relu && v < 0.0f) v = 0.0f;
     float t = v * inv_out;
     float r = nearbyintf(t);
     float u = r + ozp;
@@ -155,15 +162,15 @@ int oracle_linear_acc_folded(const int8_t* x, int64_t M, int64_t K,
 int oracle_linear(const int8_t* x, int64_t M, int64_t K, double input_scale,
                   int64_t input_zero_point, const int8_t* w, int64_t N,
                   int64_t ldw, const float* weight_scales, const float* bias,
-                  double output_scale, int64_t output_zero_point, int8_t* out,
-                  int32_t* acc_out) {
+                  double output_scale, int64_t output_zero_point, int64_t relu,
+                  int8_t* out, int32_t* acc_out) {
   if (M < 0 || N <= 0 || K < 0) return ORACLE_BAD_ARG;
   int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * N + 1));
   if (!acc) return ORACLE_BAD_ARG;
   int rc = oracle_linear_acc(x, M, K, input_zero_point, w, N, ldw, acc);
   if (rc == ORACLE_OK)
     rc = oracle_epilogue(acc, M * N, N, 1, input_scale, weight_scales, bias,
-                         output_scale, output_zero_point, out, NULL);
+                         output_scale, output_zero_point, relu, out, NULL);
   if (!acc_out) free(acc);
   return rc;
 }
@@ -175,7 +182,14 @@ int oracle_linear(const int8_t* x, int64_t M, int64_t K, double input_scale,
  * numerator is >= 0, divisible by stride_h and ih < H_in (iw likewise).
  * x is NCHW [N, IC, H_in, W_in]; w is [OC, ldw], ldw >= Kh*Kw*IC
  * (#21205 Implementation: the row stride tolerates padding); acc is NCHW
- * [N, OC, H_out, W_out] with H_out/W_out given by the caller. */
+ * [N, OC, H_out, W_out] with H_out/W_out given by the caller.
+ * Dilation and groups are the pages' fail-loud follow-ups (#21205
+ * Implementation and Constraints); dil_h enters the numerator as printed.
+ * Groups (not on the pages) split IC and OC into `groups` equal groups as in
+ * the forward conv below: output channel oc of group g = oc / (OC/groups) sums
+ * over ic = g*(IC/groups) + icg only, with w[oc, (kh*Kw + kw)*(IC/groups) + icg]
+ * (the reshape of #21205 Constraints (2) applied to each group's
+ * [IC/groups, OC/groups, Kh, Kw] block of the original weight). */
 static int tap_index(int64_t o, int64_t pad, int64_t k, int64_t dil,
                      int64_t stride, int64_t in_size, int64_t* i_out) {
   int64_t num = o + pad - k * dil;
@@ -187,14 +201,21 @@ static int tap_index(int64_t o, int64_t pad, int64_t k, int64_t dil,
   return 1;
 }
 
+static int groups_ok(int64_t IC, int64_t OC, int64_t groups) {
+  return groups >= 1 && IC > 0 && OC > 0 && IC % groups == 0 && OC % groups == 0;
+}
+
 int oracle_deconv_acc_gather(const int8_t* x, int64_t N, int64_t IC,
                              int64_t H_in, int64_t W_in,
                              int64_t input_zero_point, const int8_t* w,
                              int64_t OC, int64_t Kh, int64_t Kw, int64_t ldw,
                              int64_t stride_h, int64_t stride_w, int64_t pad_h,
                              int64_t pad_w, int64_t dil_h, int64_t dil_w,
-                             int64_t H_out, int64_t W_out, int32_t* acc) {
-  if (N < 0 || IC <= 0 || OC <= 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * IC ||
+                             int64_t groups, int64_t H_out, int64_t W_out,
+                             int32_t* acc) {
+  if (!groups_ok(IC, OC, groups)) return ORACLE_BAD_ARG;
+  const int64_t ICg = IC / groups, OCg = OC / groups;
+  if (N < 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * ICg ||
       stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || H_out < 0 || W_out < 0)
     return ORACLE_BAD_ARG;
   int overflow = 0;
@@ -204,7 +225,9 @@ int oracle_deconv_acc_gather(const int8_t* x, int64_t N, int64_t IC,
       for (int64_t oh = 0; oh < H_out; ++oh) {
         for (int64_t ow = 0; ow < W_out; ++ow) {
           int64_t s = 0;
-          for (int64_t ic = 0; ic < IC; ++ic) {
+          const int64_t g = oc / OCg;
+          for (int64_t icg = 0; icg < ICg; ++icg) {
+            const int64_t ic = g * ICg + icg;
             for (int64_t kh = 0; kh < Kh; ++kh) {
               int64_t ih;
               if (!tap_index(oh, pad_h, kh, dil_h, stride_h, H_in, &ih)) continue;
@@ -212,7 +235,7 @@ int oracle_deconv_acc_gather(const int8_t* x, int64_t N, int64_t IC,
                 int64_t iw;
                 if (!tap_index(ow, pad_w, kw, dil_w, stride_w, W_in, &iw)) continue;
                 int64_t xv = x[((n * IC + ic) * H_in + ih) * W_in + iw];
-                int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];
+                int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];
                 s += (xv - input_zero_point) * wv;
               }
             }
@@ -235,8 +258,11 @@ int oracle_deconv_acc_scatter(const int8_t* x, int64_t N, int64_t IC,
                               int64_t OC, int64_t Kh, int64_t Kw, int64_t ldw,
                               int64_t stride_h, int64_t stride_w, int64_t pad_h,
                               int64_t pad_w, int64_t dil_h, int64_t dil_w,
-                              int64_t H_out, int64_t W_out, int32_t* acc) {
-  if (N < 0 || IC <= 0 || OC <= 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * IC ||
+                              int64_t groups, int64_t H_out, int64_t W_out,
+                              int32_t* acc) {
+  if (!groups_ok(IC, OC, groups)) return ORACLE_BAD_ARG;
+  const int64_t ICg = IC / groups, OCg = OC / groups;
+  if (N < 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * ICg ||
       stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || H_out < 0 || W_out < 0)
     return ORACLE_BAD_ARG;
   int64_t plane = H_out * W_out;
@@ -254,9 +280,10 @@ int oracle_deconv_acc_scatter(const int8_t* x, int64_t N, int64_t IC,
             for (int64_t kw = 0; kw < Kw; ++kw) {
               int64_t ow = iw * stride_w - pad_w + kw * dil_w;
               if (ow < 0 || ow >= W_out) continue;
-              for (int64_t oc = 0; oc < OC; ++oc)
+              const int64_t g = ic / ICg, icg = ic % ICg;
+              for (int64_t oc = g * OCg; oc < (g + 1) * OCg; ++oc)
                 s[((n * OC + oc) * H_out + oh) * W_out + ow] +=
-                    xv * (int64_t)w[oc * ldw + (kh * Kw + kw) * IC + ic];
+                    xv * (int64_t)w[oc * ldw + (kh * Kw + kw) * ICg + icg];
             }
           }
         }
@@ -288,8 +315,11 @@ int oracle_deconv_acc_zpfill(const int8_t* x, int64_t N, int64_t IC,
                              int64_t OC, int64_t Kh, int64_t Kw, int64_t ldw,
                              int64_t stride_h, int64_t stride_w, int64_t pad_h,
                              int64_t pad_w, int64_t dil_h, int64_t dil_w,
-                             int64_t H_out, int64_t W_out, int32_t* acc) {
-  if (N < 0 || IC <= 0 || OC <= 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * IC ||
+                             int64_t groups, int64_t H_out, int64_t W_out,
+                             int32_t* acc) {
+  if (!groups_ok(IC, OC, groups)) return ORACLE_BAD_ARG;
+  const int64_t ICg = IC / groups, OCg = OC / groups;
+  if (N < 0 || Kh <= 0 || Kw <= 0 || ldw < Kh * Kw * ICg ||
       stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || H_out < 0 || W_out < 0)
     return ORACLE_BAD_ARG;
   int overflow = 0;
@@ -299,17 +329,19 @@ int oracle_deconv_acc_zpfill(const int8_t* x, int64_t N, int64_t IC,
       for (int64_t oh = 0; oh < H_out; ++oh) {
         for (int64_t ow = 0; ow < W_out; ++ow) {
           int64_t xw = 0, ws = 0;
+          const int64_t g = oc / OCg;
           for (int64_t kh = 0; kh < Kh; ++kh) {
             int64_t ih;
             if (!tap_divisible(oh, pad_h, kh, dil_h, stride_h, &ih)) continue;
             for (int64_t kw = 0; kw < Kw; ++kw) {
               int64_t iw;
               if (!tap_divisible(ow, pad_w, kw, dil_w, stride_w, &iw)) continue;
-              for (int64_t ic = 0; ic < IC; ++ic) {
+              for (int64_t icg = 0; icg < ICg; ++icg) {
+                const int64_t ic = g * ICg + icg;
                 int64_t xv = input_zero_point;
                 if (ih >= 0 && ih < H_in && iw >= 0 && iw < W_in)
                   xv = x[((n * IC + ic) * H_in + ih) * W_in + iw];
-                int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];
+                int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];
                 xw += xv * wv;
                 ws += wv;
               }
@@ -334,18 +366,18 @@ int oracle_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
                              double output_scale, int64_t output_zero_point,
                              int64_t stride_h, int64_t stride_w, int64_t pad_h,
                              int64_t pad_w, int64_t dil_h, int64_t dil_w,
-                             int64_t H_out, int64_t W_out, int8_t* out,
-                             int32_t* acc_out) {
+                             int64_t groups, int64_t H_out, int64_t W_out,
+                             int64_t relu, int8_t* out, int32_t* acc_out) {
   if (N < 0 || OC <= 0 || H_out < 0 || W_out < 0) return ORACLE_BAD_ARG;
   int64_t total = N * OC * H_out * W_out;
   int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(total + 1));
   if (!acc) return ORACLE_BAD_ARG;
   int rc = oracle_deconv_acc_gather(x, N, IC, H_in, W_in, input_zero_point, w, OC,
                                     Kh, Kw, ldw, stride_h, stride_w, pad_h, pad_w,
-                                    dil_h, dil_w, H_out, W_out, acc);
+                                    dil_h, dil_w, groups, H_out, W_out, acc);
   if (rc == ORACLE_OK && total > 0)
     rc = oracle_epilogue(acc, total, OC, H_out * W_out, input_scale, weight_scales,
-                         bias, output_scale, output_zero_point, out, NULL);
+                         bias, output_scale, output_zero_point, relu, out, NULL);
   if (!acc_out) free(acc);
   return rc;
 }
@@ -413,8 +445,8 @@ int oracle_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
                   const float* weight_scales, const float* bias, double output_scale,
                   int64_t output_zero_point, int64_t stride_h, int64_t stride_w,
                   int64_t pad_h, int64_t pad_w, int64_t dil_h, int64_t dil_w,
-                  int64_t groups, int64_t H_out, int64_t W_out, int8_t* out,
-                  int32_t* acc_out) {
+                  int64_t groups, int64_t H_out, int64_t W_out, int64_t relu,
+                  int8_t* out, int32_t* acc_out) {
   if (N < 0 || OC <= 0 || H_out < 0 || W_out < 0) return ORACLE_BAD_ARG;
   int64_t total = N * OC * H_out * W_out;
   int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(total + 1));
@@ -424,7 +456,7 @@ int oracle_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in,
                              W_out, acc);
   if (rc == ORACLE_OK && total > 0)
     rc = oracle_epilogue(acc, total, OC, H_out * W_out, input_scale, weight_scales, bias,
-                         output_scale, output_zero_point, out, NULL);
+                         output_scale, output_zero_point, relu, out, NULL);
   if (!acc_out) free(acc);
   return rc;
 }

@@ -49,11 +49,26 @@ MUTANTS = [
      0),
     ("linear_transposed_weight", "* (int64_t)w[n * ldw + k];\n      if (s > INT32_MAX",
      "* (int64_t)w[(k % N) * ldw + (n % K)];\n      if (s > INT32_MAX", 0),
-    ("deconv_tap_order", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];\n                s +=",
-     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * IC + ic];\n                s +=", 0),
-    ("deconv_channel_major_weight", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + ic];\n"
-     "                s +=", "int64_t wv = w[oc * ldw + ic * Kh * Kw + kh * Kw + kw];\n"
+    ("deconv_tap_order", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];\n                s +=",
+     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * ICg + icg];\n                s +=", 0),
+    ("deconv_channel_major_weight", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];\n"
+     "                s +=", "int64_t wv = w[oc * ldw + icg * Kh * Kw + kh * Kw + kw];\n"
      "                s +=", 0),
+    ("deconv_dilation_dropped", "int64_t num = o + pad - k * dil;\n  if (num < 0)",
+     "int64_t num = o + pad - k;\n  if (num < 0)", 0),
+    ("deconv_group_of_channel", "const int64_t g = oc / OCg;", "const int64_t g = oc % groups;", 0),
+    ("deconv_group_channels_interleaved", "const int64_t ic = g * ICg + icg;",
+     "const int64_t ic = icg * groups + g;", 0),
+    ("deconv_group_weight_stride", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];",
+     "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + icg];", 0),
+    ("relu_dropped", "if (relu && v < 0.0f) v = 0.0f;", "", 0),
+    ("relu_on_the_code", "if (relu && v < 0.0f) v = 0.0f;\n    float t = v * inv_out;\n"
+     "    float r = nearbyintf(t);\n    float u = r + ozp;",
+     "float t = v * inv_out;\n    float r = nearbyintf(t);\n    float u = r + ozp;\n"
+     "    if (relu && u < 0.0f) u = 0.0f;", 0),
+    ("relu_before_bias", "if (bias) v = v + bias[c];\n    if (pre) pre[e] = v;\n"
+     "    if (relu && v < 0.0f) v = 0.0f;", "if (relu && v < 0.0f) v = 0.0f;\n"
+     "    if (bias) v = v + bias[c];\n    if (pre) pre[e] = v;", 0),
     ("deconv_negative_numerator_allowed", "if (num < 0) return 0;            /* checked before dividing */",
      "", 0),
     ("deconv_last_row_dropped", "if (i >= in_size) return 0;", "if (i >= in_size - 1) return 0;", 0),
@@ -69,13 +84,13 @@ MUTANTS = [
     ("conv_last_column_dropped", "if (iw < 0 || iw >= W_in) continue;",
      "if (iw < 0 || iw >= W_in - 1) continue;", 0),
     ("conv_tap_order", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];",
-     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * ICg + icg];", 0),
+     "int64_t wv = w[oc * ldw + (kw * Kh + kh) * ICg + icg];", 2),
     ("conv_zp_sign", "s += (xv - input_zero_point) * wv;", "s += (xv + input_zero_point) * wv;", 1),
-    ("conv_group_of_channel", "const int64_t g = oc / OCg;", "const int64_t g = oc % groups;", 0),
+    ("conv_group_of_channel", "const int64_t g = oc / OCg;", "const int64_t g = oc % groups;", 2),
     ("conv_group_channels_interleaved", "const int64_t ic = g * ICg + icg;",
-     "const int64_t ic = icg * groups + g;", 0),
+     "const int64_t ic = icg * groups + g;", 2),
     ("conv_group_weight_stride", "int64_t wv = w[oc * ldw + (kh * Kw + kw) * ICg + icg];",
-     "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + icg];", 0),
+     "int64_t wv = w[oc * ldw + (kh * Kw + kw) * IC + icg];", 2),
 ]
 
 

@@ -553,3 +553,157 @@ def test_depthwise_brute_force_tiny():
                 ref[0, c, oh, ow] = t
     np.testing.assert_array_equal(oracle.conv2d_acc(x, w, zp, Kh, Kw, s, p, d, Ho, Wo, groups=C),
                                   ref)
+
+
+# --------------------------------------------------------------------------- relu-fused epilogue
+def test_relu_epilogue_hand_vectors():
+    g = _gold("epilogue_relu_hand.json")
+    for acc, s_in, w_s, b, s_out, ozp, q_relu, q_none in g["cases"]:
+        args = (np.array([acc], np.int32), 1, 1, s_in, np.array([w_s], np.float32),
+                None if b is None else np.array([b], np.float32), s_out, ozp)
+        assert int(oracle.epilogue(*args, activation="relu")[0]) == q_relu, (acc, b, ozp)
+        assert int(oracle.epilogue(*args)[0]) == q_none, (acc, b, ozp)
+
+
+@pytest.mark.parametrize("ozp", [-128, -5, 0, 3, 127])
+def test_relu_epilogue_is_torch_quantize_of_relu(ozp):
+    """Relu-fused output == torch's decomposed quantize of torch.relu(v), v the
+    real-valued output before requantization; and == max(plain output, zp)."""
+    g = qi.rng(1091 + ozp)
+    acc = _linear_random_acc(1092 + ozp, 64, 48, 300000)
+    ws = g.uniform(0.005, 0.02, 48).astype(np.float32)
+    b = g.normal(0, 0.1, 48).astype(np.float32)
+    s_out = qi.out_scale_for(4096)
+    q_none, pre = oracle.epilogue(acc, 48, 1, 0.02, ws, b, s_out, ozp, return_pre=True)
+    q_relu = oracle.epilogue(acc, 48, 1, 0.02, ws, b, s_out, ozp, activation="relu")
+    assert (pre < 0).mean() > 0.3 and (pre > 0).mean() > 0.3
+    ref = _torch_quant(torch.relu(torch.from_numpy(pre)).numpy(), s_out, ozp)
+    np.testing.assert_array_equal(q_relu, ref)
+    np.testing.assert_array_equal(q_relu, np.maximum(q_none, ozp))
+
+
+def test_relu_reaches_every_op():
+    """linear, the transposed conv and the forward conv pass the activation to
+    the epilogue: their relu outputs are max(plain output, zp)."""
+    c = qi.linear_case(93, 5, 64, 24)
+    for act_out, plain in [
+        (oracle.linear(c.x, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                       c.out_zp, activation="relu"),
+         oracle.linear(c.x, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                       c.out_zp))]:
+        np.testing.assert_array_equal(act_out, np.maximum(plain, c.out_zp))
+    d = qi.deconv_case(94, 1, 4, 5, 5, 6, 3, 3, (2, 2), (1, 1), (1, 1))
+    args = (d.x, d.w, d.weight_scales, d.bias, d.in_scale, d.in_zp, d.out_scale, d.out_zp, d.Kh,
+            d.Kw, d.stride, d.padding, d.dilation, d.H_out, d.W_out)
+    np.testing.assert_array_equal(oracle.conv2d_transposed(*args, activation="relu"),
+                                  np.maximum(oracle.conv2d_transposed(*args), d.out_zp))
+    f = qi.conv_case(95, 1, 4, 7, 6, 5, 3, 3, (1, 1), (1, 1), (1, 1))
+    args = (f.x, f.w, f.weight_scales, f.bias, f.in_scale, f.in_zp, f.out_scale, f.out_zp, f.Kh,
+            f.Kw, f.stride, f.padding, f.dilation, f.H_out, f.W_out)
+    relu = oracle.conv2d(*args, activation="relu")
+    np.testing.assert_array_equal(relu, np.maximum(oracle.conv2d(*args), f.out_zp))
+    assert (relu == f.out_zp).mean() > 0.2
+
+
+# --------------------------------------------------------------------------- transposed conv: dilation, groups
+def _torch_deconv_acc_grouped(x, w, zp, Kh, Kw, stride, padding, output_padding, dilation, groups):
+    """Exact float64 torch conv_transpose2d of (x - zp) with the grouped reshape
+    w[oc, (kh*Kw+kw)*ICg + icg] = orig[g*ICg + icg, oc - g*OCg, kh, kw] undone."""
+    N, IC, H, W = x.shape
+    OC = w.shape[0]
+    ICg, OCg = IC // groups, OC // groups
+    wo = torch.from_numpy(np.ascontiguousarray(w[:, :Kh * Kw * ICg])).reshape(
+        groups, OCg, Kh, Kw, ICg).permute(0, 4, 1, 2, 3).reshape(IC, OCg, Kh, Kw)
+    xs = torch.from_numpy(x).double() - zp
+    return F.conv_transpose2d(xs, wo.contiguous().double(), stride=stride, padding=padding,
+                              output_padding=output_padding, dilation=dilation,
+                              groups=groups).numpy()
+
+
+DECONV_GROUPED_SHAPES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, dil, groups
+    (1, 4, 5, 6, 6, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), 2),
+    (2, 6, 4, 5, 3, 4, 4, (2, 2), (1, 1), (0, 0), (1, 1), 3),
+    (1, 5, 5, 4, 5, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), 5),      # depthwise
+    (1, 3, 4, 5, 6, 3, 2, (2, 1), (1, 0), (1, 0), (1, 1), 3),      # depthwise, multiplier 2
+    (1, 4, 5, 5, 4, 3, 3, (2, 2), (2, 2), (1, 1), (2, 2), 2),      # grouped and dilated
+    (1, 3, 6, 5, 2, 3, 3, (1, 1), (2, 1), (0, 0), (2, 3), 1),      # dilated, stride 1
+    (2, 2, 4, 4, 3, 3, 3, (3, 2), (2, 1), (2, 1), (2, 2), 1),      # dilated, stride 3 x 2
+]
+
+
+@pytest.mark.parametrize("shape", DECONV_GROUPED_SHAPES)
+def test_grouped_dilated_deconv_matches_torch(shape):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, d, G = shape
+    g = qi.rng(sum(shape[:7]) + 5)
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = g.integers(-128, 128, size=(OC, Kh * Kw * (IC // G)), dtype=np.int8)
+    ref = _torch_deconv_acc_grouped(x, w, -6, Kh, Kw, s, p, op, d, G)
+    H_out, W_out = ref.shape[2:]
+    assert H_out == qi.deconv_out_size(H, Kh, s[0], p[0], op[0], d[0])
+    for method in ("gather", "scatter", "zpfill"):
+        acc = oracle.deconv_acc(x, w, -6, Kh, Kw, s, p, d, H_out, W_out, method=method, groups=G)
+        np.testing.assert_array_equal(acc, ref.astype(np.int32), err_msg=method)
+
+
+def test_grouped_deconv_is_per_group_ungrouped_deconv():
+    g = qi.rng(96)
+    N, IC, H, W, OC, K, G = 2, 6, 5, 4, 9, 3, 3
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, K * K * (IC // G) + 3))
+    acc = oracle.deconv_acc(x, w, 4, K, K, (2, 2), (1, 1), (1, 2), 10, 9, groups=G)
+    for gi in range(G):
+        xs = x[:, gi * (IC // G):(gi + 1) * (IC // G)]
+        ws = w[gi * (OC // G):(gi + 1) * (OC // G)]
+        part = oracle.deconv_acc(xs, ws, 4, K, K, (2, 2), (1, 1), (1, 2), 10, 9)
+        np.testing.assert_array_equal(acc[:, gi * (OC // G):(gi + 1) * (OC // G)], part)
+
+
+def test_grouped_dilated_deconv_is_the_adjoint_of_the_grouped_conv():
+    """<conv2d_g(x - zp), y> == <x - zp, convT_g(y)>, the transposed weight
+    holding each group's block with its channel axes swapped; exact in int64."""
+    g = qi.rng(97)
+    N, IC, H, W, OC, Kh, Kw, s, p, d, G = 2, 6, 9, 8, 4, 3, 2, (2, 3), (1, 1), (2, 2), 2
+    ICg, OCg, T = IC // G, OC // G, Kh * Kw
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, T * ICg))
+    Ho, Wo = qi.conv_out_size(H, Kh, s[0], p[0], d[0]), qi.conv_out_size(W, Kw, s[1], p[1], d[1])
+    acc = oracle.conv2d_acc(x, w, 3, Kh, Kw, s, p, d, Ho, Wo, groups=G).astype(np.int64)
+    y = qi.x_int8(g, (N, OC, Ho, Wo))
+    wt = w.reshape(G, OCg, T, ICg).transpose(0, 3, 2, 1).reshape(IC, T * OCg)
+    back = oracle.deconv_acc(y, wt, 0, Kh, Kw, s, p, d, H, W, groups=G).astype(np.int64)
+    lhs = int((acc * y.astype(np.int64)).sum())
+    rhs = int(((x.astype(np.int64) - 3) * back).sum())
+    assert lhs == rhs
+
+
+def test_grouped_dilated_deconv_brute_force_tiny():
+    """Pure-Python loops over the gather as the page states it (numerator
+    checked for sign and divisibility before dividing), per group."""
+    g = qi.rng(98)
+    N, IC, H, W, OC, Kh, Kw, s, p, d, G, zp = 1, 4, 3, 4, 6, 3, 2, (2, 3), (1, 2), (2, 1), 2, -9
+    ICg, OCg = IC // G, OC // G
+    x = qi.x_int8(g, (N, IC, H, W))
+    w = qi.w_int8(g, (OC, Kh * Kw * ICg + 2))
+    Ho, Wo = 8, 11
+    ref = np.zeros((N, OC, Ho, Wo), np.int64)
+    for oc in range(OC):
+        gi = oc // OCg
+        for oh in range(Ho):
+            for ow in range(Wo):
+                t = 0
+                for icg in range(ICg):
+                    for kh in range(Kh):
+                        nh = oh + p[0] - kh * d[0]
+                        if nh < 0 or nh % s[0] or nh // s[0] >= H:
+                            continue
+                        for kw in range(Kw):
+                            nw = ow + p[1] - kw * d[1]
+                            if nw < 0 or nw % s[1] or nw // s[1] >= W:
+                                continue
+                            t += (int(x[0, gi * ICg + icg, nh // s[0], nw // s[1]]) - zp) * \
+                                int(w[oc, (kh * Kw + kw) * ICg + icg])
+                ref[0, oc, oh, ow] = t
+    for method in ("gather", "scatter", "zpfill"):
+        np.testing.assert_array_equal(
+            oracle.deconv_acc(x, w, zp, Kh, Kw, s, p, d, Ho, Wo, method=method, groups=G), ref)
