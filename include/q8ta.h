@@ -57,7 +57,7 @@ typedef enum q8ta_status {
   Q8TA_ERR_NULL = 1,        /* a required pointer is NULL */
   Q8TA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   Q8TA_ERR_QPARAM = 3,      /* a scale is not finite and > 0, or a zero point is outside [-128, 127] */
-  Q8TA_ERR_UNSUPPORTED = 4, /* an argument value the op does not implement (activation; groups and dilation of the transposed conv) */
+  Q8TA_ERR_UNSUPPORTED = 4, /* an argument value the op does not implement (an activation other than "none" / "relu") */
   Q8TA_ERR_HIP = 5          /* the HIP runtime reported an error */
 } q8ta_status;
 
@@ -98,8 +98,10 @@ q8ta_status q8ta_dequantize_per_tensor(const int8_t* x, float* out, int64_t nume
  * out: int8 [M, N] row-major.  M, K, N >= 1.
  * weight_sums: accepted and ignored, as on the page (the zero-point term is
  * computed from the weights on every call); may be NULL.
- * activation: must be the string "none"; anything else (including NULL)
- * returns Q8TA_ERR_UNSUPPORTED ([LIN] Implementation).
+ * activation: "none", or "relu" for the relu-fused variant that [LIN]
+ * Implementation names as a follow-up: the epilogue then requantizes
+ * max(v, 0), so every code is at least output_zero_point.  Anything else
+ * (including NULL) returns Q8TA_ERR_UNSUPPORTED.
  * The page's N % 4 and M*K % 4 requirements do not apply.
  */
 q8ta_status q8ta_linear(const int8_t* x, int64_t M, int64_t K,
@@ -154,9 +156,17 @@ q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K,
  * OC entries (bias may be NULL); out: int8 NCHW [N, OC, H_out, W_out].
  * H_out and W_out are given explicitly (the page takes them from the
  * serialized output dims); output_padding_h/_w are accepted and unused.
- * Requirements: all sizes >= 1, stride >= 1, padding >= 0; dilation must be
- * 1 and groups must be 1 (Q8TA_ERR_UNSUPPORTED otherwise, as on the page);
- * activation must be "none".  weight_sums is ignored.
+ * Requirements: all sizes >= 1, stride >= 1, padding >= 0, dilation in
+ * [1, 4096], groups dividing IC and OC; activation "none" or "relu" (as for
+ * q8ta_linear).  weight_sums is ignored.
+ * Dilation, groups and relu are the follow-ups the page keeps fail-loud.
+ * Dilation enters the gather's numerator as printed.  Groups (not on the
+ * page): output channel oc of group g = oc / (OC/groups) sums only over input
+ * channels g*(IC/groups) + icg, with weight[oc, (kh*Kw + kw)*(IC/groups) + icg]
+ * (weight_row_stride >= Kh*Kw*IC/groups) -- the page's reshape of the
+ * original [IC, OC, Kh, Kw] weight applied to each group's block.
+ * Kernels: groups 1 take the implicit GEMM or the tiled direct kernel;
+ * grouped shapes take a one-output-per-thread kernel.
  */
 q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
                                    int64_t H_in, int64_t W_in,
@@ -218,7 +228,7 @@ q8ta_status q8ta_quantize_conv2d_transposed(const float* x, int64_t N, int64_t I
  * Layouts, scales, bias, weight_row_stride and the epilogue as for
  * q8ta_conv2d_transposed; H_out / W_out are given explicitly (any sizes >= 1).
  * Requirements: all sizes >= 1, stride >= 1, padding >= 0, dilation in
- * [1, 4096]; activation must be "none".  weight_sums is ignored.  Workspace
+ * [1, 4096]; activation "none" or "relu".  weight_sums is ignored.  Workspace
  * on the implicit-GEMM path (groups 1, IC % 64 == 0): an NHWC copy of the
  * input inside a zero-point border plus 4 * OC bytes; none otherwise.
  */
@@ -257,6 +267,8 @@ q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC,
                                        int64_t weight_row_stride,
                                        int64_t stride_h, int64_t stride_w,
                                        int64_t pad_h, int64_t pad_w,
+                                       int64_t dilation_h, int64_t dilation_w,
+                                       int64_t groups,
                                        int32_t* acc, int64_t H_out, int64_t W_out,
                                        hipStream_t stream);
 

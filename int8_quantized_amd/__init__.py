@@ -60,7 +60,8 @@ SIGNATURES = {
                                          _P], ctypes.c_int),
     "q8ta_linear_acc": ([_P, _I64, _I64, _I64, _P, _I64, _P, _P], ctypes.c_int),
     "q8ta_conv2d_transposed_acc": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _I64, _I64,
-                                    _I64, _I64, _I64, _I64, _P, _I64, _I64, _P], ctypes.c_int),
+                                    _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P],
+                                   ctypes.c_int),
     "q8ta_conv2d": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64, _I64, _I64,
                      _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                      _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
@@ -264,7 +265,7 @@ def q8ta_quantize_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh
 
 
 def q8ta_conv2d_transposed_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, acc,
-                               stream=None):
+                               stream=None, dilation=(1, 1), groups=1):
     """int32 accumulator of q8ta_conv2d_transposed (NCHW [N, OC, H_out, W_out])."""
     torch = _torch()
     N, IC, H_in, W_in = x.shape
@@ -274,8 +275,9 @@ def q8ta_conv2d_transposed_acc(x, input_zero_point, weight, Kh, Kw, stride, padd
     _check(lib().q8ta_conv2d_transposed_acc(
         _dev(x, torch.int8, "x"), N, IC, H_in, W_in, int(input_zero_point),
         _dev(weight, torch.int8, "weight"), OC, int(Kh), int(Kw), ldw, int(stride[0]),
-        int(stride[1]), int(padding[0]), int(padding[1]), _dev(acc, torch.int32, "acc"),
-        acc.shape[2], acc.shape[3], _stream(stream)))
+        int(stride[1]), int(padding[0]), int(padding[1]), int(dilation[0]), int(dilation[1]),
+        int(groups), _dev(acc, torch.int32, "acc"), acc.shape[2], acc.shape[3],
+        _stream(stream)))
     return acc
 
 

@@ -48,10 +48,35 @@ q8ta_status check_qparams(const char* op, double scale, int64_t zp) {
   return Q8TA_OK;
 }
 
-q8ta_status check_activation(const char* op, const char* activation) {
-  if (!activation) return fail(Q8TA_ERR_UNSUPPORTED, "%s: activation is NULL (only \"none\" is supported)", op);
-  if (strcmp(activation, "none") != 0)
-    return fail(Q8TA_ERR_UNSUPPORTED, "%s: activation \"%.64s\" is not supported (only \"none\")", op, activation);
+// "none" or "relu" (the relu-fused variant the pages name as a follow-up);
+// anything else, NULL included, fails.
+q8ta_status check_activation(const char* op, const char* activation, bool* relu) {
+  if (!activation)
+    return fail(Q8TA_ERR_UNSUPPORTED, "%s: activation is NULL (\"none\" or \"relu\")", op);
+  if (strcmp(activation, "none") == 0) {
+    *relu = false;
+  } else if (strcmp(activation, "relu") == 0) {
+    *relu = true;
+  } else {
+    return fail(Q8TA_ERR_UNSUPPORTED, "%s: activation \"%.64s\" is not supported (\"none\" or \"relu\")",
+                op, activation);
+  }
+  return Q8TA_OK;
+}
+
+Requant make_requant(double input_scale, double output_scale, int64_t output_zero_point, bool relu) {
+  const float ozp = (float)output_zero_point;
+  return Requant{(float)input_scale, recip(output_scale), ozp, relu ? ozp : -128.0f};
+}
+
+// Dilation and groups of the convolutions: dilation >= 1, groups dividing IC
+// and OC.
+q8ta_status check_dil_groups(const char* op, int64_t IC, int64_t OC, int64_t dh, int64_t dw,
+                             int64_t groups) {
+  if (groups < 1 || IC < 1 || OC < 1 || IC % groups != 0 || OC % groups != 0)
+    return fail(Q8TA_ERR_SHAPE, "%s: groups (%lld) must divide IC and OC", op, (long long)groups);
+  if (dh < 1 || dw < 1 || dh > 4096 || dw > 4096)
+    return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
   return Q8TA_OK;
 }
 
@@ -79,12 +104,13 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
   if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
   if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
-  if ((st = check_activation(op, activation))) return st;
+  bool relu = false;
+  if ((st = check_activation(op, activation, &relu))) return st;
 
   LinearArgs a{};
   a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
   a.M = M; a.K = K; a.N = N; a.izp = (int32_t)input_zero_point;
-  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  a.rq = make_requant(input_scale, output_scale, output_zero_point, relu);
   a.outf = outf;
   a.dq_scale = (float)output_scale;
   a.dq_zp = (int32_t)output_zero_point;
@@ -265,24 +291,24 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC, int64
   (void)weight_sums;
   (void)output_padding_h;
   (void)output_padding_w;
-  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out, IC);
+  q8ta_status st = check_dil_groups(op, IC, OC, dilation_h, dilation_w, groups);
+  if (st) return st;
+  st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride, stride_h,
+                     stride_w, pad_h, pad_w, out, H_out, W_out, IC / groups);
   if (st) return st;
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
-  if (dilation_h != 1 || dilation_w != 1)
-    return fail(Q8TA_ERR_UNSUPPORTED, "%s: dilation must be 1 (got %lld, %lld)", op,
-                (long long)dilation_h, (long long)dilation_w);
-  if (groups != 1) return fail(Q8TA_ERR_UNSUPPORTED, "%s: groups must be 1 (got %lld)", op, (long long)groups);
   if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
   if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
-  if ((st = check_activation(op, activation))) return st;
+  bool relu = false;
+  if ((st = check_activation(op, activation, &relu))) return st;
 
   DeconvArgs a{};
   a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
   a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
-  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  a.rq = make_requant(input_scale, output_scale, output_zero_point, relu);
   return hip_status(launch_deconv(a, stream), op);
 }
 
@@ -290,16 +316,20 @@ q8ta_status q8ta_conv2d_transposed_acc(const int8_t* x, int64_t N, int64_t IC, i
                                        int64_t W_in, int64_t input_zero_point, const int8_t* weight,
                                        int64_t OC, int64_t Kh, int64_t Kw, int64_t weight_row_stride,
                                        int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+                                       int64_t dilation_h, int64_t dilation_w, int64_t groups,
                                        int32_t* acc, int64_t H_out, int64_t W_out, hipStream_t stream) {
   const char* op = "q8ta_conv2d_transposed_acc";
-  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out, IC);
+  q8ta_status st = check_dil_groups(op, IC, OC, dilation_h, dilation_w, groups);
+  if (st) return st;
+  st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride, stride_h,
+                     stride_w, pad_h, pad_w, acc, H_out, W_out, IC / groups);
   if (st) return st;
   if (!zp_ok(input_zero_point)) return fail(Q8TA_ERR_QPARAM, "%s: input_zero_point out of range", op);
   DeconvArgs a{};
   a.x = x; a.w = weight; a.acc = acc;
   a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
   return hip_status(launch_deconv(a, stream), op);
 }
@@ -315,18 +345,16 @@ q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, in
                         int64_t H_out, int64_t W_out, hipStream_t stream) {
   const char* op = "q8ta_conv2d";
   (void)weight_sums;
-  if (groups < 1 || IC < 1 || OC < 1 || IC % groups != 0 || OC % groups != 0)
-    return fail(Q8TA_ERR_SHAPE, "%s: groups (%lld) must divide IC and OC", op, (long long)groups);
-  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, out, H_out, W_out,
-                                 IC / groups);
+  q8ta_status st = check_dil_groups(op, IC, OC, dilation_h, dilation_w, groups);
+  if (st) return st;
+  st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride, stride_h,
+                     stride_w, pad_h, pad_w, out, H_out, W_out, IC / groups);
   if (st) return st;
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
-  if (dilation_h < 1 || dilation_w < 1 || dilation_h > 4096 || dilation_w > 4096)
-    return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
   if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
   if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
-  if ((st = check_activation(op, activation))) return st;
+  bool relu = false;
+  if ((st = check_activation(op, activation, &relu))) return st;
 
   DeconvArgs a{};
   a.x = x; a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
@@ -334,7 +362,7 @@ q8ta_status q8ta_conv2d(const int8_t* x, int64_t N, int64_t IC, int64_t H_in, in
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
   a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
-  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  a.rq = make_requant(input_scale, output_scale, output_zero_point, relu);
   return hip_status(launch_conv2d(a, stream), op);
 }
 
@@ -345,14 +373,11 @@ q8ta_status q8ta_conv2d_acc(const int8_t* x, int64_t N, int64_t IC, int64_t H_in
                             int64_t dilation_w, int64_t groups, int32_t* acc, int64_t H_out,
                             int64_t W_out, hipStream_t stream) {
   const char* op = "q8ta_conv2d_acc";
-  if (groups < 1 || IC < 1 || OC < 1 || IC % groups != 0 || OC % groups != 0)
-    return fail(Q8TA_ERR_SHAPE, "%s: groups (%lld) must divide IC and OC", op, (long long)groups);
-  q8ta_status st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride,
-                                 stride_h, stride_w, pad_h, pad_w, acc, H_out, W_out,
-                                 IC / groups);
+  q8ta_status st = check_dil_groups(op, IC, OC, dilation_h, dilation_w, groups);
   if (st) return st;
-  if (dilation_h < 1 || dilation_w < 1 || dilation_h > 4096 || dilation_w > 4096)
-    return fail(Q8TA_ERR_SHAPE, "%s: dilation must be in [1, 4096]", op);
+  st = deconv_checks(op, x, N, IC, H_in, W_in, weight, OC, Kh, Kw, weight_row_stride, stride_h,
+                     stride_w, pad_h, pad_w, acc, H_out, W_out, IC / groups);
+  if (st) return st;
   if (!zp_ok(input_zero_point)) return fail(Q8TA_ERR_QPARAM, "%s: input_zero_point out of range", op);
   DeconvArgs a{};
   a.x = x; a.w = weight; a.acc = acc;
@@ -376,26 +401,26 @@ q8ta_status q8ta_quantize_conv2d_transposed(
   (void)weight_sums;
   (void)output_padding_h;
   (void)output_padding_w;
-  q8ta_status st = deconv_checks(op, (const int8_t*)x, N, IC, H_in, W_in, weight, OC, Kh, Kw,
-                                 weight_row_stride, stride_h, stride_w, pad_h, pad_w, out, H_out,
-                                 W_out, IC);
+  q8ta_status st = check_dil_groups(op, IC, OC, dilation_h, dilation_w, groups);
+  if (st) return st;
+  st = deconv_checks(op, (const int8_t*)x, N, IC, H_in, W_in, weight, OC, Kh, Kw,
+                     weight_row_stride, stride_h, stride_w, pad_h, pad_w, out, H_out, W_out,
+                     IC / groups);
   if (st) return st;
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
-  if (dilation_h != 1 || dilation_w != 1)
-    return fail(Q8TA_ERR_UNSUPPORTED, "%s: dilation must be 1 (got %lld, %lld)", op,
-                (long long)dilation_h, (long long)dilation_w);
-  if (groups != 1) return fail(Q8TA_ERR_UNSUPPORTED, "%s: groups must be 1 (got %lld)", op, (long long)groups);
   if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
   if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
-  if ((st = check_activation(op, activation))) return st;
+  bool relu = false;
+  if ((st = check_activation(op, activation, &relu))) return st;
 
   DeconvArgs a{};
   a.x = nullptr; a.xf = x; a.inv_in = recip(input_scale);
   a.w = weight; a.wscale = weight_scales; a.bias = bias; a.out = out; a.acc = nullptr;
   a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
   a.ldw = weight_row_stride; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
   a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
-  a.rq = Requant{(float)input_scale, recip(output_scale), (float)output_zero_point};
+  a.rq = make_requant(input_scale, output_scale, output_zero_point, relu);
   return hip_status(launch_quantize_deconv(a, stream), op);
 }
 

@@ -405,7 +405,7 @@ hipError_t launch_t(const DeconvArgs& a, const Plan& p, hipStream_t s) {
 constexpr bool kMfmaDeconvEnabled = false;
 
 bool deconv_mfma_supported(const DeconvArgs& a) {
-  if (!kMfmaDeconvEnabled) return false;
+  if (!kMfmaDeconvEnabled || a.groups != 1 || a.dil_h != 1 || a.dil_w != 1) return false;
   Plan p;
   int FJ, FO;
   return make_plan(a, p, FJ, FO);

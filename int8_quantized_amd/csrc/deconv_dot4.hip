@@ -339,12 +339,14 @@ int floordiv(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
 }  // namespace
 
 bool make_phases(const DeconvArgs& a, Phases& p) {
-  if (a.sh > kMaxS || a.sw > kMaxS || a.ph > (1 << 20) || a.pw > (1 << 20)) return false;
+  if (a.sh > kMaxS || a.sw > kMaxS || a.ph > (1 << 20) || a.pw > (1 << 20) || a.dil_h > 4096 ||
+      a.dil_w > 4096 || a.Kh > 4096 || a.Kw > 4096)
+    return false;
   p = Phases{};
   for (int r = 0; r < (int)a.sh; ++r) {
     int cnt = 0;
     for (int k = 0; k < (int)a.Kh; ++k) {
-      const int num = r + (int)a.ph - k;
+      const int num = r + (int)a.ph - k * (int)a.dil_h;
       if (((num % (int)a.sh) + (int)a.sh) % (int)a.sh != 0) continue;
       if (cnt >= kMaxT) return false;
       p.thk[r][cnt] = k;
@@ -356,7 +358,7 @@ bool make_phases(const DeconvArgs& a, Phases& p) {
   for (int r = 0; r < (int)a.sw; ++r) {
     int cnt = 0;
     for (int k = 0; k < (int)a.Kw; ++k) {
-      const int num = r + (int)a.pw - k;
+      const int num = r + (int)a.pw - k * (int)a.dil_w;
       if (((num % (int)a.sw) + (int)a.sw) % (int)a.sw != 0) continue;
       if (cnt >= kMaxT) return false;
       p.twk[r][cnt] = k;
@@ -417,7 +419,7 @@ hipError_t launch_blocked(const DeconvArgs& a, Phases p, hipStream_t s) {
 
 bool deconv_dot4_supported(const DeconvArgs& a) {
   Phases p;
-  if (a.IC % 4 != 0 || a.ldw % 4 != 0 || ((uintptr_t)a.w & 3) != 0) return false;
+  if (a.groups != 1 || a.IC % 4 != 0 || a.ldw % 4 != 0 || ((uintptr_t)a.w & 3) != 0) return false;
   if (a.H_out > (1 << 24) || a.W_out > (1 << 24) || a.H_in > (1 << 24) || a.W_in > (1 << 24) ||
       a.IC > (1 << 24) || a.OC > (1 << 24))
     return false;

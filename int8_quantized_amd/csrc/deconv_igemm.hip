@@ -311,6 +311,10 @@ bool make_plan(const DeconvArgs& a, const Phases& p, int osh, int osw, int ish, 
   plan.pl = (int)-lo_w;
   plan.Hpad = (int)(hi_h - lo_h + 1);
   plan.Wpad = (int)(hi_w - lo_w + 1);
+  // the bordered copy stays within a few times the input (large padding or
+  // dilation takes the other kernels)
+  if ((double)plan.Hpad * plan.Wpad > 4.0 * ((double)a.H_in + 64) * ((double)a.W_in + 64))
+    return false;
   // 32-bit lane offsets: pixel rows reach (WJ - 1) * isw * IC + IC bytes
   if ((double)WJ * isw * a.IC >= (double)((int64_t)1 << 31)) return false;
   return true;
@@ -348,7 +352,7 @@ bool deconv_igemm_supported(const DeconvArgs& a) {
   Plan plan;
   int64_t blocks;
   const int sh = (int)a.sh, sw = (int)a.sw;
-  return igemm_shape_ok(a) && make_phases(a, p) &&
+  return a.groups == 1 && igemm_shape_ok(a) && make_phases(a, p) &&
          make_plan(a, p, sh, sw, 1, 1, 32, 32, plan, blocks) &&
          make_plan(a, p, sh, sw, 1, 1, 64, 16, plan, blocks);
 }

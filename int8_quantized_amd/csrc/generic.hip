@@ -31,8 +31,10 @@ __global__ __launch_bounds__(kThreads) void k_linear_generic(LinearArgs a) {
 }
 
 // "Add q8ta_conv2d_transposed op", Solution: the gather
-//   ih = (oh + pad_h - kh) / stride_h, used only when the numerator is >= 0,
-//   divisible and ih < H_in (iw likewise; dilation is 1).
+//   ih = (oh + pad_h - kh*dil_h) / stride_h, used only when the numerator is
+//   >= 0, divisible and ih < H_in (iw likewise).  With groups, output channel
+//   oc sums over the IC/groups input channels of its group, weight row
+//   w[oc, (kh*Kw + kw)*(IC/groups) + icg].
 __global__ __launch_bounds__(kThreads) void k_deconv_generic(DeconvArgs a) {
   const int64_t total = a.N * a.OC * a.H_out * a.W_out;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -41,22 +43,24 @@ __global__ __launch_bounds__(kThreads) void k_deconv_generic(DeconvArgs a) {
   const int64_t oh = (idx / a.W_out) % a.H_out;
   const int64_t oc = (idx / (a.W_out * a.H_out)) % a.OC;
   const int64_t n = idx / (a.W_out * a.H_out * a.OC);
+  const int64_t ICg = a.IC / a.groups, OCg = a.OC / a.groups;
+  const int64_t ic0 = (oc / OCg) * ICg;  // first input channel of oc's group
+  const int64_t plane = a.H_in * a.W_in;
   int32_t acc = 0;
   for (int64_t kh = 0; kh < a.Kh; ++kh) {
-    const int64_t nh = oh + a.ph - kh;
+    const int64_t nh = oh + a.ph - kh * a.dil_h;
     if (nh < 0 || nh % a.sh != 0) continue;
     const int64_t ih = nh / a.sh;
     if (ih >= a.H_in) continue;
     for (int64_t kw = 0; kw < a.Kw; ++kw) {
-      const int64_t nw = ow + a.pw - kw;
+      const int64_t nw = ow + a.pw - kw * a.dil_w;
       if (nw < 0 || nw % a.sw != 0) continue;
       const int64_t iw = nw / a.sw;
       if (iw >= a.W_in) continue;
-      const int8_t* xp = a.x + ((n * a.IC) * a.H_in + ih) * a.W_in + iw;
-      const int8_t* wp = a.w + oc * a.ldw + (kh * a.Kw + kw) * a.IC;
-      const int64_t plane = a.H_in * a.W_in;
-      for (int64_t ic = 0; ic < a.IC; ++ic)
-        acc += ((int32_t)xp[ic * plane] - a.izp) * (int32_t)wp[ic];
+      const int8_t* xp = a.x + ((n * a.IC + ic0) * a.H_in + ih) * a.W_in + iw;
+      const int8_t* wp = a.w + oc * a.ldw + (kh * a.Kw + kw) * ICg;
+      for (int64_t icg = 0; icg < ICg; ++icg)
+        acc += ((int32_t)xp[icg * plane] - a.izp) * (int32_t)wp[icg];
     }
   }
   if (a.acc) {

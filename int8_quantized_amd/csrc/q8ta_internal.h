@@ -8,11 +8,13 @@ namespace q8ta {
 
 // Scalars of the dequant/requant epilogue, prepared on the host:
 // s_in = (float)input_scale, inv_out = (float)(1.0 / output_scale),
-// ozp = (float)output_zero_point.
+// ozp = (float)output_zero_point, qmin = the lowest code: -128, or the output
+// zero point for the relu-fused activation.
 struct Requant {
   float s_in;
   float inv_out;
   float ozp;
+  float qmin;
 };
 
 // The per-channel epilogue of q8ta_linear / q8ta_conv2d_transposed
@@ -22,7 +24,11 @@ struct Requant {
 // Evaluated left to right in float with one rounding per operation (every
 // source is built with -ffp-contract=off, so no multiply-add is fused);
 // rint rounds half to even.  A missing bias is passed as 0.0f, which gives
-// the same code as skipping the add.
+// the same code as skipping the add.  Relu fused (the follow-up both pages
+// leave fail-loud) requantizes max(v, 0): for v <= 0 that code is the output
+// zero point and the plain code is at most the zero point, for v > 0 the plain
+// code is already at least the zero point, so it equals clamping the plain
+// code from below at the zero point (r.qmin) for every finite v.
 __device__ __forceinline__ int requant(int32_t acc, float wscale, float b, const Requant& r) {
   float v = (float)acc;
   v = v * r.s_in;
@@ -31,7 +37,7 @@ __device__ __forceinline__ int requant(int32_t acc, float wscale, float b, const
   float t = v * r.inv_out;
   float q = __builtin_rintf(t);
   q = q + r.ozp;
-  q = __builtin_fmaxf(q, -128.0f);
+  q = __builtin_fmaxf(q, r.qmin);
   q = __builtin_fminf(q, 127.0f);
   return (int)q;
 }
@@ -163,8 +169,8 @@ struct DeconvArgs {
   int64_t H_out, W_out;
   int32_t izp;
   Requant rq;
-  int64_t dil_h = 1, dil_w = 1;  // forward conv only (the transposed op takes 1)
-  int64_t groups = 1;            // forward conv only: IC and OC split into equal groups
+  int64_t dil_h = 1, dil_w = 1;
+  int64_t groups = 1;  // IC and OC split into equal groups (weight rows hold IC/groups channels)
   // Fused quantize: when xf is set (x NULL), the input is fp32 NCHW and is
   // quantized on the fly with inv_in = (float)(1/input_scale) and the input
   // zero point, exactly as quantize_per_tensor would.

@@ -118,13 +118,15 @@ def deconv_out_size(in_size, k, s, p, op, d=1):
 def deconv_case(seed: int, N: int, IC: int, H_in: int, W_in: int, OC: int, Kh: int, Kw: int,
                 stride=(2, 2), padding=(1, 1), output_padding=(0, 0), H_out=None, W_out=None,
                 ldw=None, with_bias=True, in_zp=IN_ZP, out_zp=OUT_ZP,
-                x_from_fp32: bool = False, in_scale: float = IN_SCALE) -> DeconvCase:
+                x_from_fp32: bool = False, in_scale: float = IN_SCALE, dilation=(1, 1),
+                groups: int = 1) -> DeconvCase:
+    """Transposed-conv inputs; the weight has Kh*Kw*IC/groups columns."""
     g = rng(seed)
     if H_out is None:
-        H_out = deconv_out_size(H_in, Kh, stride[0], padding[0], output_padding[0])
+        H_out = deconv_out_size(H_in, Kh, stride[0], padding[0], output_padding[0], dilation[0])
     if W_out is None:
-        W_out = deconv_out_size(W_in, Kw, stride[1], padding[1], output_padding[1])
-    ldw = Kh * Kw * IC if ldw is None else ldw
+        W_out = deconv_out_size(W_in, Kw, stride[1], padding[1], output_padding[1], dilation[1])
+    ldw = Kh * Kw * (IC // groups) if ldw is None else ldw
     xf = None
     if x_from_fp32:
         xf = x_fp32(g, (N, IC, H_in, W_in))
@@ -134,10 +136,12 @@ def deconv_case(seed: int, N: int, IC: int, H_in: int, W_in: int, OC: int, Kh: i
     w = w_int8(g, (OC, ldw))
     ws = scales(g, OC)
     b = bias(g, OC) if with_bias else None
-    kred = IC * Kh * Kw / (stride[0] * stride[1])
-    return DeconvCase(x, w, ws, b, in_scale, in_zp, out_scale_for(kred, in_scale), out_zp,
-                      Kh, Kw, tuple(stride), tuple(padding), tuple(output_padding), (1, 1),
-                      H_out, W_out, xf)
+    kred = (IC // groups) * Kh * Kw / (stride[0] * stride[1])
+    c = DeconvCase(x, w, ws, b, in_scale, in_zp, out_scale_for(kred, in_scale), out_zp,
+                   Kh, Kw, tuple(stride), tuple(padding), tuple(output_padding), tuple(dilation),
+                   H_out, W_out, xf)
+    c.groups = groups
+    return c
 
 
 def conv_out_size(in_size, k, s, p, d=1):

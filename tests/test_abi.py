@@ -100,7 +100,8 @@ def test_linear_errors(fn):
     _st(_lin(fn, M=M, s_out=float("inf")), q8.Q8TA_ERR_QPARAM)
     _st(_lin(fn, M=M, izp=200), q8.Q8TA_ERR_QPARAM)
     _st(_lin(fn, M=M, ozp=-129), q8.Q8TA_ERR_QPARAM)
-    _st(_lin(fn, M=M, act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED, "relu")
+    _st(_lin(fn, M=M, act=b"gelu"), q8.Q8TA_ERR_UNSUPPORTED, "gelu")
+    _st(_lin(fn, M=M, act=b"RELU"), q8.Q8TA_ERR_UNSUPPORTED)
     _st(_lin(fn, M=M, act=None), q8.Q8TA_ERR_UNSUPPORTED)
     _st(_lin(fn, M=M, act=b"None"), q8.Q8TA_ERR_UNSUPPORTED)
 
@@ -144,10 +145,13 @@ def test_deconv_errors():
     _st(_dc(sh=0), q8.Q8TA_ERR_SHAPE)
     _st(_dc(sw=-1), q8.Q8TA_ERR_SHAPE)
     _st(_dc(ph=-1), q8.Q8TA_ERR_SHAPE)
-    _st(_dc(dh=2), q8.Q8TA_ERR_UNSUPPORTED, "dilation")
-    _st(_dc(dw=0), q8.Q8TA_ERR_UNSUPPORTED, "dilation")
-    _st(_dc(groups=2), q8.Q8TA_ERR_UNSUPPORTED, "groups")
-    _st(_dc(act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(_dc(dw=0), q8.Q8TA_ERR_SHAPE, "dilation")
+    _st(_dc(dh=5000), q8.Q8TA_ERR_SHAPE, "dilation")
+    _st(_dc(groups=0), q8.Q8TA_ERR_SHAPE, "groups")
+    _st(_dc(groups=3), q8.Q8TA_ERR_SHAPE, "groups")          # does not divide IC = 64
+    _st(_dc(groups=64), q8.Q8TA_ERR_SHAPE, "groups")         # does not divide OC = 32
+    _st(_dc(groups=2, ldw=511), q8.Q8TA_ERR_SHAPE, "weight_row_stride")
+    _st(_dc(act=b"sigmoid"), q8.Q8TA_ERR_UNSUPPORTED)
     _st(_dc(act=None), q8.Q8TA_ERR_UNSUPPORTED)
     _st(_dc(izp=128), q8.Q8TA_ERR_QPARAM)
     _st(_dc(s_out=-0.5), q8.Q8TA_ERR_QPARAM)
@@ -156,11 +160,17 @@ def test_deconv_errors():
 
 def test_deconv_acc_errors():
     f = q8.lib().q8ta_conv2d_transposed_acc
-    args = [FAKE, 1, 64, 32, 32, 3, FAKE, 32, 4, 4, 1024, 2, 2, 1, 1, FAKE, 64, 64, None]
+    args = [FAKE, 1, 64, 32, 32, 3, FAKE, 32, 4, 4, 1024, 2, 2, 1, 1, 1, 1, 1, FAKE, 64, 64, None]
     a = list(args); a[0] = None
+    _st(f(*a), q8.Q8TA_ERR_NULL)
+    a = list(args); a[18] = None
     _st(f(*a), q8.Q8TA_ERR_NULL)
     a = list(args); a[10] = 100
     _st(f(*a), q8.Q8TA_ERR_SHAPE)
+    a = list(args); a[15] = 0
+    _st(f(*a), q8.Q8TA_ERR_SHAPE, "dilation")
+    a = list(args); a[17] = 3
+    _st(f(*a), q8.Q8TA_ERR_SHAPE, "groups")
     a = list(args); a[5] = -200
     _st(f(*a), q8.Q8TA_ERR_QPARAM)
 
@@ -197,7 +207,7 @@ def test_conv2d_errors():
     _st(_cv(groups=3), q8.Q8TA_ERR_SHAPE, "groups")          # does not divide IC = 64
     _st(_cv(groups=64), q8.Q8TA_ERR_SHAPE, "groups")         # does not divide OC = 32
     _st(_cv(groups=2, ldw=287), q8.Q8TA_ERR_SHAPE, "weight_row_stride")
-    _st(_cv(act=b"relu"), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(_cv(act=b"tanh"), q8.Q8TA_ERR_UNSUPPORTED)
     _st(_cv(izp=-129), q8.Q8TA_ERR_QPARAM)
     _st(_cv(s_out=0.0), q8.Q8TA_ERR_QPARAM)
 
@@ -222,15 +232,17 @@ def test_fused_entry_points_errors():
                          None), q8.Q8TA_ERR_NULL)
     _st(l.q8ta_linear_dq(FAKE, 0, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE,
                          None), q8.Q8TA_ERR_SHAPE)
-    _st(l.q8ta_linear_dq(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"relu", FAKE,
+    _st(l.q8ta_linear_dq(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"relu6", FAKE,
                          None), q8.Q8TA_ERR_UNSUPPORTED)
     # q8ta_quantize_conv2d_transposed: same checks as q8ta_conv2d_transposed
     args = [FAKE, 1, 64, 32, 32, 0.02, 3, FAKE, 32, 4, 4, 1024, None, FAKE, FAKE, 0.54, -5, 2, 2,
             1, 1, 0, 0, 1, 1, 1, b"none", FAKE, 64, 64, None]
     a = list(args); a[0] = None
     _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_NULL)
-    a = list(args); a[23] = 2
-    _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_UNSUPPORTED, "dilation")
+    a = list(args); a[23] = 0
+    _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_SHAPE, "dilation")
+    a = list(args); a[25] = 5
+    _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_SHAPE, "groups")
     a = list(args); a[5] = -1.0
     _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_QPARAM)
 
@@ -248,6 +260,19 @@ def test_valid_call_without_gpu_reports_hip_error():
     rc = q8.lib().q8ta_quantize_per_tensor(FAKE, FAKE, 16, 0.02, 3, None)
     assert rc == q8.Q8TA_ERR_HIP, q8.q8ta_last_error()
     assert "HIP error" in q8.q8ta_last_error()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="launches on fake pointers; only meaningful without a GPU")
+def test_relu_dilation_and_groups_pass_validation():
+    """relu on every op, dilation and groups on the transposed conv are
+    accepted: without a GPU such calls get as far as the HIP runtime."""
+    for fn in ("q8ta_linear", "q8ta_linear_gemv"):
+        _st(_lin(fn, M=1, act=b"relu"), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(_dc(act=b"relu"), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(_dc(dh=2, dw=3), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(_dc(groups=2, ldw=512), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(_dc(groups=32, ldw=32), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(_cv(act=b"relu"), q8.Q8TA_ERR_HIP, "HIP error")
 
 
 def test_binding_rejects_host_tensors():

@@ -133,18 +133,18 @@ def test_dequantize_ragged(numel, offset):
 
 
 # ============================================================================ linear
-def _run_linear(c, fn=None, bias=True):
+def _run_linear(c, fn=None, bias=True, activation="none"):
     fn = fn or q8.q8ta_linear
     out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
     b = dev(c.bias) if (bias and c.bias is not None) else None
     fn(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales), b, c.out_scale,
-       c.out_zp, "none", out)
+       c.out_zp, activation, out)
     return host(out)
 
 
-def _oracle_linear(c, bias=True):
+def _oracle_linear(c, bias=True, activation="none"):
     return oracle.linear(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale, c.in_zp,
-                         c.out_scale, c.out_zp)
+                         c.out_scale, c.out_zp, activation=activation)
 
 
 def _acc_linear(c):
@@ -305,30 +305,32 @@ def test_gemm_workload_sampled_rows_and_dequantize():
 
 
 # ============================================================================ conv2d_transposed
-def _run_deconv(c, bias=True):
+def _run_deconv(c, bias=True, activation="none"):
     out = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int8, device="cuda")
     b = dev(c.bias) if (bias and c.bias is not None) else None
     q8.q8ta_conv2d_transposed(dev(c.x), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
                               dev(c.weight_scales), b, c.out_scale, c.out_zp, c.stride, c.padding,
-                              c.output_padding, (1, 1), 1, "none", out)
+                              c.output_padding, c.dilation, c.groups, activation, out)
     return host(out)
 
 
 def _acc_deconv(c):
     acc = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int32, device="cuda")
-    q8.q8ta_conv2d_transposed_acc(dev(c.x), c.in_zp, dev(c.w), c.Kh, c.Kw, c.stride, c.padding, acc)
+    q8.q8ta_conv2d_transposed_acc(dev(c.x), c.in_zp, dev(c.w), c.Kh, c.Kw, c.stride, c.padding, acc,
+                                  dilation=c.dilation, groups=c.groups)
     return host(acc)
 
 
-def _oracle_deconv(c, bias=True):
+def _oracle_deconv(c, bias=True, activation="none"):
     return oracle.conv2d_transposed(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale,
                                     c.in_zp, c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding,
-                                    (1, 1), c.H_out, c.W_out)
+                                    c.dilation, c.H_out, c.W_out, groups=c.groups,
+                                    activation=activation)
 
 
 def _oracle_deconv_acc(c):
-    return oracle.deconv_acc(c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, (1, 1), c.H_out,
-                             c.W_out)
+    return oracle.deconv_acc(c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation,
+                             c.H_out, c.W_out, groups=c.groups)
 
 
 DECONV_CASES = [
@@ -474,12 +476,12 @@ def test_deconv_large_workload_sampled():
 
 
 # ============================================================================ forward conv2d
-def _run_conv(c, bias=True):
+def _run_conv(c, bias=True, activation="none"):
     out = torch.empty((c.x.shape[0], c.w.shape[0], c.H_out, c.W_out), dtype=torch.int8, device="cuda")
     b = dev(c.bias) if (bias and c.bias is not None) else None
     q8.q8ta_conv2d(dev(c.x), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
                    dev(c.weight_scales), b, c.out_scale, c.out_zp, c.stride, c.padding,
-                   c.dilation, getattr(c, "groups", 1), "none", out)
+                   c.dilation, getattr(c, "groups", 1), activation, out)
     return host(out)
 
 
@@ -490,10 +492,10 @@ def _acc_conv(c):
     return host(acc)
 
 
-def _oracle_conv(c, bias=True):
+def _oracle_conv(c, bias=True, activation="none"):
     return oracle.conv2d(c.x, c.w, c.weight_scales, c.bias if bias else None, c.in_scale, c.in_zp,
                          c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation,
-                         c.H_out, c.W_out, groups=getattr(c, "groups", 1))
+                         c.H_out, c.W_out, groups=getattr(c, "groups", 1), activation=activation)
 
 
 CONV2D_CASES = [
@@ -650,3 +652,120 @@ def test_quantize_conv2d_transposed_large_workload_sampled():
                                    c.stride, c.padding, (1, 1), c.H_out, c.W_out)
     np.testing.assert_array_equal(got[7:8, chans], ref)
 
+
+
+# ============================================================================ relu, transposed-conv dilation and groups
+@pytest.mark.parametrize("M,K,N", [(1, 512, 64), (1, 4096, 4096), (3, 48, 17), (300, 1040, 257),
+                                   (7, 33, 5), (64, 128, 64)])
+def test_linear_relu(M, K, N):
+    """activation "relu" on every linear kernel (GEMV, skinny, grouped GEMM,
+    shape-general) and on the fused dequantize."""
+    _say(f"linear relu M={M} K={K} N={N}")
+    c = qi.linear_case(M * 5 + K + N + 11, M, K, N)
+    ref = _oracle_linear(c, activation="relu")
+    assert (ref == c.out_zp).mean() > 0.2
+    np.testing.assert_array_equal(_run_linear(c, activation="relu"), ref)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                      dev(c.bias), c.out_scale, c.out_zp, "relu", out)
+    dq = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(host(out).view(np.uint32), dq.view(np.uint32))
+    if M == 1:
+        np.testing.assert_array_equal(_run_linear(c, fn=q8.q8ta_linear_gemv, activation="relu"), ref)
+
+
+@pytest.mark.parametrize("path", ["igemm", "dot4", "generic"])
+def test_deconv_relu(path):
+    _say(f"deconv relu path={path}")
+    IC = 6 if path == "generic" else 64   # IC % 4 != 0 takes the one-output-per-thread kernel
+    c = qi.deconv_case(811 + IC, 2, IC, 6, 7, 40, 3, 3, (2, 2), (1, 1), (1, 1))
+    with env(Q8TA_DECONV_PATH=path):
+        np.testing.assert_array_equal(_run_deconv(c, activation="relu"),
+                                      _oracle_deconv(c, activation="relu"))
+
+
+@pytest.mark.parametrize("case", ["igemm", "depthwise", "generic"])
+def test_conv2d_relu(case):
+    _say(f"conv2d relu {case}")
+    if case == "igemm":
+        c = qi.conv_case(821, 1, 64, 9, 11, 32, 3, 3, (1, 1), (1, 1), (1, 1))
+    elif case == "depthwise":
+        c = qi.conv_case(822, 2, 16, 12, 16, 16, 3, 3, (1, 1), (1, 1), (1, 1), groups=16)
+    else:
+        c = qi.conv_case(823, 1, 24, 7, 7, 8, 3, 3, (1, 1), (1, 1), (1, 1))
+    np.testing.assert_array_equal(_run_conv(c, activation="relu"),
+                                  _oracle_conv(c, activation="relu"))
+
+
+def test_quantize_conv2d_transposed_relu():
+    _say("quantize+deconv relu")
+    c = qi.deconv_case(831, 1, 64, 5, 7, 32, 4, 4, (2, 2), (1, 1), (0, 0), x_from_fp32=True)
+    for path in ("igemm", "dot4"):
+        out = torch.empty((1, 32, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+        with env(Q8TA_DECONV_PATH=path):
+            q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh,
+                                               c.Kw, None, dev(c.weight_scales), dev(c.bias),
+                                               c.out_scale, c.out_zp, c.stride, c.padding,
+                                               c.output_padding, (1, 1), 1, "relu", out)
+        xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+        ref = oracle.conv2d_transposed(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                       c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding,
+                                       (1, 1), c.H_out, c.W_out, activation="relu")
+        np.testing.assert_array_equal(host(out), ref, err_msg=path)
+
+
+# Dilated transposed convs: the stride phases take the dilated taps
+# (num = r + pad - kh*dil); some phases get every tap, some none.
+DECONV_DILATED_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, dil
+    (1, 64, 6, 7, 32, 3, 3, (2, 2), (2, 2), (1, 1), (2, 2)),
+    (1, 64, 5, 5, 40, 3, 3, (1, 1), (2, 2), (0, 0), (2, 2)),
+    (2, 128, 4, 9, 64, 3, 3, (2, 2), (1, 1), (1, 1), (2, 1)),
+    (1, 64, 5, 4, 16, 4, 4, (3, 2), (3, 2), (0, 0), (2, 3)),
+    (1, 64, 4, 4, 16, 3, 3, (2, 2), (0, 0), (0, 0), (4, 4)),
+    (1, 64, 3, 6, 24, 2, 3, (2, 2), (1, 2), (1, 1), (3, 3)),
+]
+
+
+@pytest.mark.parametrize("case", DECONV_DILATED_CASES,
+                         ids=[str(i) for i in range(len(DECONV_DILATED_CASES))])
+@pytest.mark.parametrize("path", ["igemm", "dot4"])
+def test_deconv_dilated_parity(case, path):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, d = case
+    _say(f"deconv dilated {path} case={case}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 13, N, IC, H, W, OC, Kh, Kw, s, p, op,
+                       dilation=d)
+    with env(Q8TA_DECONV_PATH=path):
+        np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+        np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
+def test_deconv_dilated_general_kernel():
+    """IC % 4 != 0: the one-output-per-thread kernel with dilation."""
+    _say("deconv dilated general")
+    c = qi.deconv_case(841, 1, 6, 5, 6, 8, 3, 3, (2, 2), (1, 1), (1, 1), dilation=(2, 3))
+    np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+    np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+
+
+DECONV_GROUPED_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, dil, groups
+    (1, 16, 5, 6, 16, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), 16),     # depthwise
+    (2, 32, 4, 5, 16, 4, 4, (2, 2), (1, 1), (0, 0), (1, 1), 4),
+    (1, 8, 6, 5, 16, 3, 3, (2, 2), (1, 1), (1, 1), (2, 2), 8),       # multiplier 2, dilated
+    (1, 128, 4, 4, 64, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), 2),     # IC % 64 == 0, grouped
+    (1, 12, 7, 3, 6, 2, 3, (3, 1), (0, 1), (2, 0), (1, 2), 3),
+]
+
+
+@pytest.mark.parametrize("case", DECONV_GROUPED_CASES,
+                         ids=[str(i) for i in range(len(DECONV_GROUPED_CASES))])
+def test_deconv_grouped_parity(case):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, d, G = case
+    _say(f"deconv grouped case={case}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw, G]) + 17, N, IC, H, W, OC, Kh, Kw, s, p, op,
+                       dilation=d, groups=G)
+    np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
+    np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+    np.testing.assert_array_equal(_run_deconv(c, activation="relu"),
+                                  _oracle_deconv(c, activation="relu"))
