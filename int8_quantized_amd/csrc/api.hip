@@ -121,9 +121,13 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
 
 namespace q8ta {
 
+// Q8TA_GEMM_PATH = dot4 skips the matrix-core GEMM where both apply (used by
+// the tests to reach the v_dot4 kernel).
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (gemv_supported(a)) return launch_gemv(a, s);
-  if (gemm_mfma_supported(a)) return launch_gemm_mfma(a, s);
+  const char* e = getenv("Q8TA_GEMM_PATH");
+  const bool no_mfma = e && e[0] == 'd';
+  if (!no_mfma && gemm_mfma_supported(a)) return launch_gemm_mfma(a, s);
   if (gemm_dot4_supported(a)) return launch_gemm_dot4(a, s);
   return launch_linear_generic(a, s);
 }

@@ -161,11 +161,13 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
     const int sh = (int)a.sh, sw = (int)a.sw;
     const int NQ64 = p.ICP >> 6;
 
+    // Scales and bias only for the requantizing call (the accumulator entry
+    // point passes no weight_scales).
     float sc[FO], bi[FO];
 #pragma unroll
     for (int f = 0; f < FO; ++f) {
       const int oc = ocw + f * 16 + lrow;
-      const bool ok = oc < a.OC;
+      const bool ok = oc < a.OC && !a.acc;
       sc[f] = ok ? a.wscale[oc] : 0.0f;
       bi[f] = (ok && a.bias) ? a.bias[oc] : 0.0f;
     }

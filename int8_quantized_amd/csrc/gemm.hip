@@ -183,16 +183,20 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
     for (int r = 0; r < 4; ++r) ws4[i][r] = __shfl(v, 4 * lgrp + r, 64);
   }
 
-  const bool vec_store = (N % 4) == 0;
+  const bool vec_store = (N % 4) == 0 && ((uintptr_t)a.out & 3) == 0;
 #pragma unroll
   for (int i = 0; i < C::FN; ++i) {
     const int64_t nb = bn0 + wn * C::WN + i * 16 + 4 * lgrp;
-    float sc[4], bi[4];
+    // Scales and bias exist only for the requantizing calls: the accumulator
+    // entry point passes no weight_scales (NULL), so nothing is read then.
+    float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (!a.acc) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = nb + r < N;
-      sc[r] = ok ? a.wscale[nb + r] : 0.0f;
-      bi[r] = (ok && a.bias) ? a.bias[nb + r] : 0.0f;
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = nb + r < N;
+        sc[r] = ok ? a.wscale[nb + r] : 0.0f;
+        bi[r] = (ok && a.bias) ? a.bias[nb + r] : 0.0f;
+      }
     }
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) {
@@ -209,7 +213,20 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
         int q[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) q[r] = requant(cacc[r], sc[r], bi[r], a.rq);
-        if (vec_store && nb + 3 < N) {
+        if (a.outf) {
+          // fused dequantize: fp32 out[m, n] = (q - zp) * scale of the output
+          float* of = a.outf + m * N + nb;
+          if (nb + 3 < N && ((uintptr_t)of & 15) == 0) {
+            typedef float v4f __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<v4f*>(of) =
+                v4f{dequant1(q[0], a.dq_zp, a.dq_scale), dequant1(q[1], a.dq_zp, a.dq_scale),
+                    dequant1(q[2], a.dq_zp, a.dq_scale), dequant1(q[3], a.dq_zp, a.dq_scale)};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (nb + r < N) of[r] = dequant1(q[r], a.dq_zp, a.dq_scale);
+          }
+        } else if (vec_store && nb + 3 < N) {
           *reinterpret_cast<uint32_t*>(a.out + m * N + nb) = pack4(q[0], q[1], q[2], q[3]);
         } else {
 #pragma unroll
@@ -238,14 +255,14 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-// Switched off: the first launch of this kernel on an MI355X reported an
-// illegal memory access whose cause has not been identified (the index
-// arithmetic and the generated code check out in-bounds).  The kernel stays
-// compiled but is never dispatched until that is resolved.
-constexpr bool kMfmaGemmEnabled = false;
+// The epilogue once read weight_scales[n] also for the accumulator entry
+// point, which passes NULL there: a read near address 0, the illegal memory
+// access of the first launch.  Scales and bias are now read only when the
+// call requantizes.
+constexpr bool kMfmaGemmEnabled = true;
 
 bool gemm_mfma_supported(const LinearArgs& a) {
-  return kMfmaGemmEnabled && !a.outf && (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w) &&
+  return kMfmaGemmEnabled && (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w) &&
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
