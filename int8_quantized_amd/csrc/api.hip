@@ -132,21 +132,28 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   return launch_linear_generic(a, s);
 }
 
-// The implicit GEMM (three launches' worth of fixed cost: input copy, then the
-// GEMM) pays off from about 2^28 multiply-adds; smaller problems take the
-// direct tiled kernel.  Q8TA_DECONV_PATH = igemm | dot4 forces either one
-// where the shape allows it (used by the tests).
-static bool deconv_wants_igemm(const DeconvArgs& a) {
+// Q8TA_DECONV_PATH = mfma | igemm | dot4 | generic forces one kernel family
+// where the shape allows it (used by the tests); unset, the matrix-core kernel
+// takes every shape it supports, then the implicit GEMM (three launches' worth
+// of fixed cost: input copy, then the GEMM) from about 2^28 multiply-adds,
+// then the direct tiled kernel.
+static char deconv_path() {
   const char* e = getenv("Q8TA_DECONV_PATH");
+  return e ? e[0] : 0;
+}
+
+static bool deconv_wants_igemm(const DeconvArgs& a) {
+  const char k = deconv_path();
   const double macs = (double)a.N * a.OC * a.H_out * a.W_out * a.IC * a.Kh * a.Kw /
                       ((double)a.sh * a.sw);
-  return (e ? e[0] == 'i' : macs >= (double)(1 << 28)) && deconv_igemm_supported(a);
+  return (k ? k == 'i' : macs >= (double)(1 << 28)) && deconv_igemm_supported(a);
 }
 
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
-  if (deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
+  const char k = deconv_path();
+  if ((k == 0 || k == 'm') && deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
   if (deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
-  if (deconv_dot4_supported(a)) return launch_deconv_dot4(a, s);
+  if (k != 'g' && deconv_dot4_supported(a)) return launch_deconv_dot4(a, s);
   return launch_deconv_generic(a, s);
 }
 
@@ -154,7 +161,7 @@ hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
 // implicit GEMM quantizes while it copies the input; the other paths quantize
 // into a stream-ordered int8 workspace first.
 hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
-  if (deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
+  if (deconv_path() != 'm' && deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
   const int64_t numel = a.N * a.IC * a.H_in * a.W_in;
   void* ws = nullptr;
   hipError_t e = hipMallocAsync(&ws, (size_t)numel, s);

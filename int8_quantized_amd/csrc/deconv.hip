@@ -400,11 +400,10 @@ hipError_t launch_t(const DeconvArgs& a, const Plan& p, hipStream_t s) {
 
 }  // namespace
 
-// Switched off together with the matrix-core GEMM, which shares this
-// kernel's instruction mix (LDS tiles, barriers, int8 MFMA with accumulator
-// registers) and whose first launch on an MI355X reported an illegal memory
-// access of unidentified cause.  Never dispatched until that is resolved.
-constexpr bool kMfmaDeconvEnabled = false;
+// Scales and bias are read only by requantizing calls (the accumulator entry
+// point passes no weight_scales); the same NULL read once faulted the
+// matrix-core GEMM.
+constexpr bool kMfmaDeconvEnabled = true;
 
 bool deconv_mfma_supported(const DeconvArgs& a) {
   if (!kMfmaDeconvEnabled || a.groups != 1 || a.dil_h != 1 || a.dil_w != 1) return false;

@@ -153,11 +153,6 @@ def _acc_linear(c):
     return host(acc)
 
 
-MFMA_OFF = ("the matrix-core (MFMA + LDS) kernels are switched off: their first launch on MI355X "
-            "reported an illegal memory access whose cause has not been found")
-FAULTED_CASE = ("this exact case faulted the GPU under the switched-off matrix-core kernel; it stays "
-                "off the GPU until that cause is shown")
-
 LINEAR_SHAPES = [
     # skinny / gemv path (M <= 4, K % 16 == 0)
     (1, 4096, 4096), (1, 16, 1), (1, 1040, 37), (2, 1024, 100), (3, 48, 17), (4, 4096, 64),
@@ -384,7 +379,7 @@ DECONV_IGEMM_CASES = [
 
 @pytest.mark.parametrize("case", DECONV_IGEMM_CASES,
                          ids=[str(i) for i in range(len(DECONV_IGEMM_CASES))])
-@pytest.mark.parametrize("path", ["igemm:4x4", "igemm:4x8", "dot4:"])
+@pytest.mark.parametrize("path", ["igemm:4x4", "igemm:4x8", "dot4:", "mfma:"])
 def test_deconv_igemm_parity(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
     _say(f"deconv {path} case={case}")
@@ -396,7 +391,6 @@ def test_deconv_igemm_parity(case, path):
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
-@pytest.mark.skip(reason=MFMA_OFF)
 @pytest.mark.parametrize("fj,fo,wi", [(1, 1, 1), (2, 4, 2), (4, 2, 1), (4, 4, 4), (1, 4, 3)])
 def test_deconv_every_tile(fj, fo, wi):
     _say(f"deconv tile FJ={fj} FO={fo} WI={wi}")
@@ -619,7 +613,7 @@ def test_linear_dq_gemm_workload_sampled():
 @pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_IGEMM_CASES[1],
                                   DECONV_IGEMM_CASES[5], DECONV_CASES[14]],
                          ids=["k3s2", "mixed", "igemm_oc40", "igemm_tall", "general"])
-@pytest.mark.parametrize("path", ["igemm", "dot4"])
+@pytest.mark.parametrize("path", ["igemm", "dot4", "mfma"])
 def test_quantize_conv2d_transposed_equals_the_chain(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
     _say(f"quantize+deconv {path} case={case}")
@@ -678,7 +672,7 @@ def test_linear_relu(M, K, N):
         np.testing.assert_array_equal(_run_linear(c, fn=q8.q8ta_linear_gemv, activation="relu"), ref)
 
 
-@pytest.mark.parametrize("path", ["igemm", "dot4", "generic"])
+@pytest.mark.parametrize("path", ["mfma", "igemm", "dot4", "generic"])
 def test_deconv_relu(path):
     _say(f"deconv relu path={path}")
     IC = 6 if path == "generic" else 64   # IC % 4 != 0 takes the one-output-per-thread kernel
