@@ -269,18 +269,29 @@ def main():
         fused_ok = bool(torch.equal(y.view(torch.int32), deq_ref.view(torch.int32)))
         del deq_ref
 
-    # The matrix-core GEMM is switched off; q8ta_linear with M > 4 runs the
-    # vector-ALU v_dot4 kernel, whose own ceiling is PEAK_DOT4_TOPS.
-    roofline = {
-        "bound": "alu",
-        "kernel": "k_row_sums + k_dot4_gemm<4,false,4,4> (v_dot4_i32_i8, vector ALU)",
-        "achieved": round(achieved, 2), "peak": round(PEAK_DOT4_TOPS, 1), "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_DOT4_TOPS, 4),
-        "frac_of_int8_mfma_peak": round(achieved / PEAK_INT8_TOPS, 5),
-        "per_launch_ops": ops, "avg_launch_us": round(gemm_avg_s * 1e6, 2),
-        "traffic": traffic_from_profile("gemm", os.path.join(ROOT, "int8_quantized_amd", "csrc",
-                                                             "gemm_dot4.hip")),
-    }
+    # q8ta_linear with M > 4 runs the matrix-core GEMM (bound by the dense int8
+    # MFMA peak); Q8TA_GEMM_PATH=dot4 selects the vector-ALU v_dot4 kernel,
+    # whose own ceiling is PEAK_DOT4_TOPS.
+    if os.environ.get("Q8TA_GEMM_PATH", "").startswith("d"):
+        roofline = {
+            "bound": "alu",
+            "kernel": "k_row_sums + k_dot4_gemm<4,false,4,4> (v_dot4_i32_i8, vector ALU)",
+            "achieved": round(achieved, 2), "peak": round(PEAK_DOT4_TOPS, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_DOT4_TOPS, 4),
+            "frac_of_int8_mfma_peak": round(achieved / PEAK_INT8_TOPS, 5),
+            "traffic": traffic_from_profile("gemm_dot4", os.path.join(
+                ROOT, "int8_quantized_amd", "csrc", "gemm_dot4.hip")),
+        }
+    else:
+        roofline = {
+            "bound": "mfma",
+            "kernel": "k_gemm<128x128x64 tile, 2x2 waves> (v_mfma_i32_16x16x64_i8)",
+            "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic_from_profile("gemm", os.path.join(
+                ROOT, "int8_quantized_amd", "csrc", "gemm.hip")),
+        }
+    roofline.update({"per_launch_ops": ops, "avg_launch_us": round(gemm_avg_s * 1e6, 2)})
 
     # ------------------------------------------------------------ CPU baseline (oracle sample)
     cpu = None

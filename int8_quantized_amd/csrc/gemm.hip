@@ -266,16 +266,18 @@ bool gemm_mfma_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-// Tile choice: the large tile when it still gives at least one tile per CU,
-// otherwise the medium or small one.  Q8TA_GEMM_CFG=L|M|S overrides.
+// Tile choice: the medium tile, or the small one for few rows.  The large
+// tile (128 x 128 per wave) needs 256 accumulator registers per lane and the
+// compiler then keeps the accumulators in scratch memory (7x slower than the
+// medium tile on 2048 x 4096 x 11008); it is reachable only through
+// Q8TA_GEMM_CFG=L|M|S, which overrides the choice.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
   if (e && (e[0] == 'L' || e[0] == 'M' || e[0] == 'S')) pick = e[0];
   if (!pick) {
-    const int64_t tl = ((a.M + 255) / 256) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    pick = tl >= 256 ? 'L' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
+    pick = (tm >= 256 || a.M > 64) ? 'M' : 'S';
   }
   switch (pick) {
     case 'L': return launch_cfg<CfgL>(a, s);
