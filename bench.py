@@ -285,7 +285,7 @@ def main():
     else:
         roofline = {
             "bound": "mfma",
-            "kernel": "k_gemm<128x128x64 tile, 2x2 waves> (v_mfma_i32_16x16x64_i8)",
+            "kernel": "k_gemm<256x128x128 tile, 4x2 waves> (v_mfma_i32_16x16x64_i8)",
             "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic_from_profile("gemm", os.path.join(
@@ -392,11 +392,24 @@ def run_ceilings(torch, stream, timer):
     del bufs
     ms = timer.time_calls([lambda: cl.q8ta_calib_empty(out.data_ptr(), 512, stream)], 200,
                           batches=3)
+    empty_us = min(ms) * 1e3
+    # register-only loops of independent int8 MFMAs, one wave per SIMD (512
+    # workgroups of 4 waves): the matrix cores' issue ceiling per instruction
+    cl.q8ta_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    mfma = {}
+    for kind, name, per in ((0, "mfma_16x16x64_i8_loop_tops", 16 * 32768),
+                            (1, "mfma_32x32x32_i8_loop_tops", 8 * 65536)):
+        mb, mi = 512, 2000
+        ms = timer.time_calls([lambda k=kind: cl.q8ta_calib_mfma(out.data_ptr(), mb, mi, k, stream)],
+                              3, batches=3)
+        mfma[name] = round(mb * 4 * mi * per / (min(ms) / 1e3) / 1e12, 1)
     return {"dot4_loop_tops": round(dot4_tops, 1), "dot4_peak_tops_derived": round(PEAK_DOT4_TOPS, 1),
+            **mfma, "int8_mfma_peak_tops": PEAK_INT8_TOPS,
             "copy_256MiB_gbs": round(copy_gbs, 1), "hbm_peak_gbs": PEAK_HBM_GBS,
             "read_16MiB_cold_us": round(read_us, 2),
             "read_16MiB_cold_gbs": round(nr / (read_us / 1e6) / 1e9, 1),
-            "empty_launch_us": round(min(ms) * 1e3, 2)}
+            "empty_launch_us": round(empty_us, 2)}
 
 
 def run_extra(torch, np, q8, qi, lib, stream, timer, check):

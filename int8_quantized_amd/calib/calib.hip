@@ -5,6 +5,8 @@
 //  q8ta_calib_dot4: each thread runs `iters` rounds of 16 independent v_dot4
 //    accumulations on registers (no memory traffic inside the loop) and writes
 //    one int32; ops = threads * iters * 16 * 8.
+//  q8ta_calib_mfma: a register-only loop of independent int8 MFMAs per wave
+//    (the matrix-core issue ceiling).
 //  q8ta_calib_copy: 16-byte grid-stride copy of n16 chunks; bytes = 32 * n16.
 //  q8ta_calib_read: read-only stream of n16 16-byte chunks, 8 per thread in
 //    the access pattern of the GEMV's weight stream (each load instruction of
@@ -33,6 +35,44 @@ __global__ __launch_bounds__(256) void k_dot4_loop(int32_t* out, int iters, int 
   int s = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) s ^= acc[k];
+  out[t] = s;
+}
+
+// MFMA issue ceiling: each wave runs `iters` rounds of 16 independent int8
+// matrix products into 16 accumulators held in registers.  kind 0:
+// v_mfma_i32_16x16x64_i8 (32768 ops each), kind 1: v_mfma_i32_32x32x32_i8
+// (65536 ops each).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_mfma_loop(int32_t* out, int iters, int seed) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const v4i a = v4i{(int)(t * 0x9E3779B1u) ^ seed, t, seed, 7};
+  const v4i b = v4i{t ^ 0x5a5a5a5a, seed, (int)(t * 0x85EBCA6Bu), 3};
+  int s = 0;
+  if constexpr (KIND == 0) {
+    v4i acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = v4i{k, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) acc[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[k], 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s ^= acc[k][0] ^ acc[k][3];
+  } else {
+    typedef int v16i __attribute__((ext_vector_type(16)));
+    v16i acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc[k] = v16i{};
+      acc[k][0] = k;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[k], 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s ^= acc[k][0] ^ acc[k][15];
+  }
   out[t] = s;
 }
 
@@ -67,6 +107,15 @@ __global__ __launch_bounds__(256) void k_empty(int32_t* out, int flag) {
 extern "C" {
 
 // out: int32 device buffer of blocks * 256 entries.
+// ops = blocks * 4 waves * iters * (16 * 32768 for kind 0, 8 * 65536 for kind 1)
+int q8ta_calib_mfma(int32_t* out, int blocks, int iters, int kind, hipStream_t s) {
+  if (kind == 0)
+    hipLaunchKernelGGL(k_mfma_loop<0>, dim3(blocks), dim3(256), 0, s, out, iters, 12345);
+  else
+    hipLaunchKernelGGL(k_mfma_loop<1>, dim3(blocks), dim3(256), 0, s, out, iters, 12345);
+  return (int)hipGetLastError();
+}
+
 int q8ta_calib_dot4(int32_t* out, int blocks, int iters, hipStream_t s) {
   if (!out || blocks < 1 || iters < 1) return 1;
   hipLaunchKernelGGL(k_dot4_loop, dim3(blocks), dim3(256), 0, s, out, iters, 12345);

@@ -241,6 +241,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
 using CfgL = Cfg<256, 256, 64, 2, 2>;   // 128x128 per wave
 using CfgM = Cfg<128, 128, 64, 2, 2>;   // 64x64 per wave
 using CfgS = Cfg<128, 64, 64, 2, 1>;    // 64x64 per wave, 2 waves
+using CfgK = Cfg<128, 128, 128, 2, 2>;  // 64x64 per wave, 128-byte K steps
+using CfgW = Cfg<256, 128, 64, 4, 2>;   // 64x64 per wave, 8 waves
+using CfgV = Cfg<256, 128, 128, 4, 2>;  // 64x64 per wave, 8 waves, 128-byte K steps
+using CfgU = Cfg<128, 256, 64, 2, 4>;   // 64x64 per wave, 8 waves
+using CfgQ = Cfg<256, 128, 64, 2, 2>;   // 128x64 per wave
+using CfgR = Cfg<128, 128, 64, 2, 1>;   // 64x128 per wave, 2 waves
 
 template <class C>
 hipError_t launch_cfg(const LinearArgs& a, hipStream_t s) {
@@ -266,22 +272,32 @@ bool gemm_mfma_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-// Tile choice: the medium tile, or the small one for few rows.  The large
-// tile (128 x 128 per wave) needs 256 accumulator registers per lane and the
-// compiler then keeps the accumulators in scratch memory (7x slower than the
-// medium tile on 2048 x 4096 x 11008); it is reachable only through
-// Q8TA_GEMM_CFG=L|M|S, which overrides the choice.
+// Tile choice (measured on 2048 x 4096 x 11008): 256 x 128 tiles with
+// 128-byte K steps and 8 waves when they fill the GPU at least once and K is
+// long, otherwise the medium tile, or the small one for few rows.  The large
+// tile of this file (128 x 128 per wave, loops the compiler leaves rolled)
+// keeps its accumulators in scratch memory; the 32x32x32 kernels of
+// gemm_big.hip ('B') measured slower on that shape.  Q8TA_GEMM_CFG (one letter
+// of LMSKWVUQRB) overrides the choice.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
-  if (e && (e[0] == 'L' || e[0] == 'M' || e[0] == 'S')) pick = e[0];
+  if (e && strchr("LMSKWVUQRB", e[0])) pick = e[0];
   if (!pick) {
+    const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    pick = (tm >= 256 || a.M > 64) ? 'M' : 'S';
+    pick = (tv >= 256 && a.K >= 1024) ? 'V' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
   }
+  if (pick == 'B') return gemm_big_supported(a) ? launch_gemm_big(a, s) : launch_cfg<CfgM>(a, s);
   switch (pick) {
     case 'L': return launch_cfg<CfgL>(a, s);
     case 'M': return launch_cfg<CfgM>(a, s);
+    case 'K': return launch_cfg<CfgK>(a, s);
+    case 'W': return launch_cfg<CfgW>(a, s);
+    case 'V': return launch_cfg<CfgV>(a, s);
+    case 'U': return launch_cfg<CfgU>(a, s);
+    case 'Q': return launch_cfg<CfgQ>(a, s);
+    case 'R': return launch_cfg<CfgR>(a, s);
     default: return launch_cfg<CfgS>(a, s);
   }
 }

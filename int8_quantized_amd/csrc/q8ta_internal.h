@@ -207,6 +207,8 @@ hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s);
 bool gemm_mfma_supported(const LinearArgs& a);
 hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s);
 bool gemm_dot4_supported(const LinearArgs& a);
+hipError_t launch_gemm_big(const LinearArgs& a, hipStream_t s);
+bool gemm_big_supported(const LinearArgs& a);
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);

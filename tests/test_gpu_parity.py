@@ -183,7 +183,7 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
 
 
-@pytest.mark.parametrize("cfg", ["L", "M", "S"])
+@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "B"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
 def test_linear_every_gemm_tile(cfg, M, K, N):
     _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
@@ -191,6 +191,23 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
     with env(Q8TA_GEMM_CFG=cfg):
         np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+
+
+@pytest.mark.parametrize("cfg", ["B", "D", "T", "Q", "K", "M"])
+@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768), (700, 272, 1100)])
+def test_linear_every_gemm32_tile(cfg, M, K, N):
+    """The 32x32x32 matrix-core GEMM in each of its tile shapes."""
+    _say(f"gemm32 cfg={cfg} M={M} K={K} N={N}")
+    c = qi.linear_case(M + N + ord(cfg) + 1, M, K, N)
+    with env(Q8TA_GEMM_CFG="B", Q8TA_GEMM32_CFG=cfg):
+        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                          dev(c.bias), c.out_scale, c.out_zp, "relu", out)
+        ref = oracle.dequantize_per_tensor(_oracle_linear(c, activation="relu"), c.out_scale,
+                                           c.out_zp)
+        np.testing.assert_array_equal(host(out).view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("cfg", ["4S.16x2:16", "4S.16x2:16x", "4S.16x2:1", "4S.16x2:3x",
