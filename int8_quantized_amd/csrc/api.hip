@@ -158,10 +158,12 @@ hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
 }
 
 // quantize_per_tensor -> transposed conv with an fp32 input (a.xf): the
-// implicit GEMM quantizes while it copies the input; the other paths quantize
-// into a stream-ordered int8 workspace first.
+// implicit GEMM quantizes while it copies the input; the other paths (the
+// matrix-core kernel first) quantize into a stream-ordered int8 workspace.
 hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
-  if (deconv_path() != 'm' && deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
+  const char k = deconv_path();
+  const bool mfma = (k == 0 || k == 'm') && deconv_mfma_supported(a);
+  if (!mfma && k != 'm' && deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
   const int64_t numel = a.N * a.IC * a.H_in * a.W_in;
   void* ws = nullptr;
   hipError_t e = hipMallocAsync(&ws, (size_t)numel, s);
@@ -176,10 +178,16 @@ hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
   return e != hipSuccess ? e : f;
 }
 
-// Forward conv: the implicit GEMM (groups 1, IC % 64 == 0), the depthwise
-// kernel (groups == IC == OC), or the shape-general kernel.
+// Forward conv: the matrix-core kernel (groups 1, stride 1, IC % 16 == 0),
+// the implicit GEMM on v_dot4 (groups 1, IC % 64 == 0), the depthwise kernel
+// (groups == IC == OC), or the shape-general kernel.  Q8TA_CONV_PATH = mfma |
+// igemm | generic forces one where the shape allows it (used by the tests).
 hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s) {
-  if (conv_igemm_supported(a)) return launch_conv_igemm(a, s);
+  const char* e = getenv("Q8TA_CONV_PATH");
+  const char k = e ? e[0] : 0;
+  if ((k == 0 || k == 'm') && conv_mfma_supported(a)) return launch_conv_mfma(a, s);
+  if ((k == 0 || k == 'i') && conv_igemm_supported(a)) return launch_conv_igemm(a, s);
+  if (k == 'g') return launch_conv2d_generic(a, s);
   if (depthwise_supported(a)) return launch_depthwise(a, s);
   return launch_conv2d_generic(a, s);
 }

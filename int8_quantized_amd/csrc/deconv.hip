@@ -296,9 +296,15 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
 int floordiv(int a, int b) { return (a >= 0) ? a / b : -((-a + b - 1) / b); }
 
 // Builds the phase/tap tables and the tile geometry; returns false when the
-// tiled kernel cannot take the shape.
-bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO) {
+// tiled kernel cannot take the shape.  forward: the stride-1 forward conv,
+// one phase whose taps kh read input rows oh + kh*dil_h - pad_h (a dense
+// correlation like every phase of the transposed conv).
+bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = false) {
   if (a.sh > kMaxS || a.sw > kMaxS) return false;
+  if (forward && (a.sh != 1 || a.sw != 1)) return false;
+  if (a.groups != 1 || a.dil_h < 1 || a.dil_w < 1 || a.dil_h > 4096 || a.dil_w > 4096 ||
+      a.Kh > 4096 || a.Kw > 4096)
+    return false;
   if (a.IC % 16 != 0 || a.ldw % 16 != 0 || ((uintptr_t)a.w & 15) != 0) return false;
   if (a.IC > 4096 || a.OC > (1 << 20) || a.H_out > (1 << 20) || a.W_out > (1 << 20) ||
       a.H_in > (1 << 20) || a.W_in > (1 << 20) || a.N > (1 << 20) || a.ph > 4096 || a.pw > 4096)
@@ -309,11 +315,11 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO) {
   for (int r = 0; r < sh; ++r) {
     int cnt = 0;
     for (int k = 0; k < (int)a.Kh; ++k) {
-      const int num = r + ph - k;
-      if (((num % sh) + sh) % sh != 0) continue;
+      const int num = r + ph - k * (int)a.dil_h;
+      if (!forward && ((num % sh) + sh) % sh != 0) continue;
       if (cnt >= kMaxT) return false;
       p.thk[r][cnt] = k;
-      p.thd[r][cnt] = floordiv(num, sh);
+      p.thd[r][cnt] = forward ? k * (int)a.dil_h - ph : floordiv(num, sh);
       dhmin = p.thd[r][cnt] < dhmin ? p.thd[r][cnt] : dhmin;
       dhmax = p.thd[r][cnt] > dhmax ? p.thd[r][cnt] : dhmax;
       ++cnt;
@@ -323,11 +329,11 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO) {
   for (int r = 0; r < sw; ++r) {
     int cnt = 0;
     for (int k = 0; k < (int)a.Kw; ++k) {
-      const int num = r + pw - k;
-      if (((num % sw) + sw) % sw != 0) continue;
+      const int num = r + pw - k * (int)a.dil_w;
+      if (!forward && ((num % sw) + sw) % sw != 0) continue;
       if (cnt >= kMaxT) return false;
       p.twk[r][cnt] = k;
-      p.twd[r][cnt] = floordiv(num, sw);
+      p.twd[r][cnt] = forward ? k * (int)a.dil_w - pw : floordiv(num, sw);
       dwmin = p.twd[r][cnt] < dwmin ? p.twd[r][cnt] : dwmin;
       dwmax = p.twd[r][cnt] > dwmax ? p.twd[r][cnt] : dwmax;
       ++cnt;
@@ -406,16 +412,24 @@ hipError_t launch_t(const DeconvArgs& a, const Plan& p, hipStream_t s) {
 constexpr bool kMfmaDeconvEnabled = true;
 
 bool deconv_mfma_supported(const DeconvArgs& a) {
-  if (!kMfmaDeconvEnabled || a.groups != 1 || a.dil_h != 1 || a.dil_w != 1) return false;
+  if (!kMfmaDeconvEnabled) return false;
   Plan p;
   int FJ, FO;
   return make_plan(a, p, FJ, FO);
 }
 
-hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s) {
+bool conv_mfma_supported(const DeconvArgs& a) {
+  if (!kMfmaDeconvEnabled) return false;
   Plan p;
   int FJ, FO;
-  if (!make_plan(a, p, FJ, FO)) return hipErrorInvalidValue;
+  return make_plan(a, p, FJ, FO, true);
+}
+
+namespace {
+hipError_t launch_mfma(const DeconvArgs& a, hipStream_t s, bool forward) {
+  Plan p;
+  int FJ, FO;
+  if (!make_plan(a, p, FJ, FO, forward)) return hipErrorInvalidValue;
 #define Q8TA_DC(fj, fo) \
   if (FJ == fj && FO == fo) return launch_t<fj, fo>(a, p, s);
   Q8TA_DC(1, 1) Q8TA_DC(1, 2) Q8TA_DC(1, 4)
@@ -424,5 +438,9 @@ hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s) {
 #undef Q8TA_DC
   return hipErrorInvalidValue;
 }
+}  // namespace
+
+hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s) { return launch_mfma(a, s, false); }
+hipError_t launch_conv_mfma(const DeconvArgs& a, hipStream_t s) { return launch_mfma(a, s, true); }
 
 }  // namespace q8ta

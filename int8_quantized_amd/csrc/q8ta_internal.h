@@ -212,6 +212,8 @@ bool gemm_big_supported(const LinearArgs& a);
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);
+hipError_t launch_conv_mfma(const DeconvArgs& a, hipStream_t s);
+bool conv_mfma_supported(const DeconvArgs& a);
 hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s);
 bool deconv_dot4_supported(const DeconvArgs& a);
 hipError_t launch_deconv_igemm(const DeconvArgs& a, hipStream_t s);

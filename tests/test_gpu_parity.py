@@ -525,13 +525,14 @@ CONV2D_CASES = [
 
 
 @pytest.mark.parametrize("case", CONV2D_CASES, ids=[str(i) for i in range(len(CONV2D_CASES))])
-@pytest.mark.parametrize("layout", ["4x4", "4x8"])
-def test_conv2d_parity(case, layout):
+@pytest.mark.parametrize("path", ["mfma:4x4", "igemm:4x4", "igemm:4x8"])
+def test_conv2d_parity(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, d, Ho, Wo, extra = case
-    _say(f"conv2d layout={layout} case={case}")
+    kind, layout = path.split(":")
+    _say(f"conv2d path={path} case={case}")
     c = qi.conv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 2, N, IC, H, W, OC, Kh, Kw, s, p, d,
                      H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra)
-    with env(Q8TA_IGEMM_CFG=layout):
+    with env(Q8TA_IGEMM_CFG=layout, Q8TA_CONV_PATH=kind):
         np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
         np.testing.assert_array_equal(_acc_conv(c), oracle.conv2d_acc(
             c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out))
@@ -699,17 +700,18 @@ def test_deconv_relu(path):
                                       _oracle_deconv(c, activation="relu"))
 
 
-@pytest.mark.parametrize("case", ["igemm", "depthwise", "generic"])
+@pytest.mark.parametrize("case", ["mfma", "igemm", "depthwise", "generic"])
 def test_conv2d_relu(case):
     _say(f"conv2d relu {case}")
-    if case == "igemm":
+    if case in ("mfma", "igemm"):
         c = qi.conv_case(821, 1, 64, 9, 11, 32, 3, 3, (1, 1), (1, 1), (1, 1))
     elif case == "depthwise":
         c = qi.conv_case(822, 2, 16, 12, 16, 16, 3, 3, (1, 1), (1, 1), (1, 1), groups=16)
     else:
         c = qi.conv_case(823, 1, 24, 7, 7, 8, 3, 3, (1, 1), (1, 1), (1, 1))
-    np.testing.assert_array_equal(_run_conv(c, activation="relu"),
-                                  _oracle_conv(c, activation="relu"))
+    with env(Q8TA_CONV_PATH=case[0] if case in ("mfma", "igemm") else ""):
+        np.testing.assert_array_equal(_run_conv(c, activation="relu"),
+                                      _oracle_conv(c, activation="relu"))
 
 
 def test_quantize_conv2d_transposed_relu():
@@ -744,7 +746,7 @@ DECONV_DILATED_CASES = [
 
 @pytest.mark.parametrize("case", DECONV_DILATED_CASES,
                          ids=[str(i) for i in range(len(DECONV_DILATED_CASES))])
-@pytest.mark.parametrize("path", ["igemm", "dot4"])
+@pytest.mark.parametrize("path", ["mfma", "igemm", "dot4"])
 def test_deconv_dilated_parity(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, op, d = case
     _say(f"deconv dilated {path} case={case}")
