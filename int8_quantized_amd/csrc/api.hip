@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include <atomic>
 #include <cstdlib>
 
 #include "../../include/q8ta.h"
@@ -121,6 +122,22 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
 
 namespace q8ta {
 
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s) {
+  static std::atomic<uint64_t> pools_set{0};   // one bit per device
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && !(pools_set.load() & (1ull << dev))) {
+    hipMemPool_t pool;
+    e = hipDeviceGetDefaultMemPool(&pool, dev);
+    uint64_t keep = (uint64_t)1 << 30;
+    if (e == hipSuccess) e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    pools_set.fetch_or(1ull << dev);
+  }
+  return hipMallocAsync(p, bytes, s);
+}
+
 // Q8TA_GEMM_PATH = dot4 skips the matrix-core GEMM where both apply (used by
 // the tests to reach the v_dot4 kernel).
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
@@ -166,7 +183,7 @@ hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
   if (!mfma && k != 'm' && deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
   const int64_t numel = a.N * a.IC * a.H_in * a.W_in;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, (size_t)numel, s);
+  hipError_t e = workspace_alloc(&ws, (size_t)numel, s);
   if (e != hipSuccess) return e;
   e = launch_quantize(a.xf, (int8_t*)ws, numel, a.inv_in, (float)a.izp, s);
   if (e == hipSuccess) {

@@ -59,6 +59,7 @@ __device__ __forceinline__ int swz(int row, int c) {
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t smem[2 * C::STAGE];
+  __shared__ float epi[2 * C::BN];   // per-channel scale and bias of the tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,6 +129,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
 #pragma unroll
   for (int i = 0; i < C::FN; ++i) wsum[i] = 0;
 
+  // The epilogue's per-channel scale and bias (tile row tid), fetched before
+  // the K loop so that their latency hides behind it; handed over through LDS
+  // after the loop.
+  static_assert(C::BN <= C::NT, "one channel per thread");
+  float e_sc = 0.0f, e_bi = 0.0f;
+  if (tid < C::BN && !a.acc && bn0 + tid < N) {
+    e_sc = a.wscale[bn0 + tid];
+    e_bi = a.bias ? a.bias[bn0 + tid] : 0.0f;
+  }
+
   load_global(0);
   store_lds(0);
   __syncthreads();
@@ -170,6 +181,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
     __syncthreads();
   }
 
+  if (tid < C::BN) {
+    epi[tid] = e_sc;
+    epi[C::BN + tid] = e_bi;
+  }
+  __syncthreads();
+
   // Row sums of W: lane l holds a partial for row (l & 15) of each fragment;
   // add the four k-groups, then fetch the sums of the four rows this lane's
   // accumulators belong to (rows 4*(l>>4) .. +3 of the fragment).
@@ -186,17 +203,15 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
   const bool vec_store = (N % 4) == 0 && ((uintptr_t)a.out & 3) == 0;
 #pragma unroll
   for (int i = 0; i < C::FN; ++i) {
-    const int64_t nb = bn0 + wn * C::WN + i * 16 + 4 * lgrp;
+    const int lr = wn * C::WN + i * 16 + 4 * lgrp;   // tile row of this lane's registers
+    const int64_t nb = bn0 + lr;
     // Scales and bias exist only for the requantizing calls: the accumulator
-    // entry point passes no weight_scales (NULL), so nothing is read then.
-    float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (!a.acc) {
+    // entry point passes no weight_scales (NULL), so none was read then.
+    float sc[4], bi[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = nb + r < N;
-        sc[r] = ok ? a.wscale[nb + r] : 0.0f;
-        bi[r] = (ok && a.bias) ? a.bias[nb + r] : 0.0f;
-      }
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = epi[lr + r];
+      bi[r] = epi[C::BN + lr + r];
     }
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) {
@@ -276,19 +291,19 @@ bool gemm_mfma_supported(const LinearArgs& a) {
 // 128-byte K steps and 8 waves when they fill the GPU at least once and K is
 // long, otherwise the medium tile, or the small one for few rows.  The large
 // tile of this file (128 x 128 per wave, loops the compiler leaves rolled)
-// keeps its accumulators in scratch memory; the 32x32x32 kernels of
-// gemm_big.hip ('B') measured slower on that shape.  Q8TA_GEMM_CFG (one letter
-// of LMSKWVUQRB) overrides the choice.
+// keeps its accumulators in scratch memory; the direct-to-LDS 32x32x32 kernel
+// of gemm_dl.hip ('G') measured slower on that shape.  Q8TA_GEMM_CFG (one
+// letter of LMSKWVUQRG) overrides the choice.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
-  if (e && strchr("LMSKWVUQRB", e[0])) pick = e[0];
+  if (e && strchr("LMSKWVUQRG", e[0])) pick = e[0];
   if (!pick) {
     const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
     pick = (tv >= 256 && a.K >= 1024) ? 'V' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
   }
-  if (pick == 'B') return gemm_big_supported(a) ? launch_gemm_big(a, s) : launch_cfg<CfgM>(a, s);
+  if (pick == 'G') return gemm_dl_supported(a) ? launch_gemm_dl(a, s) : launch_cfg<CfgM>(a, s);
   switch (pick) {
     case 'L': return launch_cfg<CfgL>(a, s);
     case 'M': return launch_cfg<CfgM>(a, s);

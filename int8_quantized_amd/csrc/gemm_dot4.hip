@@ -275,7 +275,7 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
   if (group < 1) group = 1;
   if (group > BMb) group = BMb;
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, (size_t)a.N * sizeof(int32_t), s);
+  hipError_t e = workspace_alloc(&ws, (size_t)a.N * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_row_sums, dim3((unsigned)((a.N + 3) / 4)), dim3(kThreads), 0, s, a.w, a.N,
                      a.K, (int32_t*)ws);
@@ -292,6 +292,11 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
+
+hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_sums, dim3((unsigned)((N + 3) / 4)), dim3(kThreads), 0, s, w, N, K, out);
+  return hipGetLastError();
+}
 
 bool gemm_dot4_supported(const LinearArgs& a) {
   // The smallest block tile is 32 x 32; the grid must stay below 2^31 blocks.

@@ -133,6 +133,13 @@ __device__ __forceinline__ gptr uniform_ptr(const int8_t* p) {
   return (gptr)(((uint64_t)hi << 32) | lo);
 }
 
+// Stream-ordered workspace from the current device's default memory pool
+// (hipMallocAsync; release with hipFreeAsync on the same stream).  On first use
+// per device the pool is told to keep up to 1 GiB after frees: by default it
+// returns freed memory at every synchronization and each call maps memory
+// afresh.
+hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s);
+
 // ---- launchers (host functions; each returns hipGetLastError() after launch)
 hipError_t launch_quantize(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
                            hipStream_t s);
@@ -207,8 +214,10 @@ hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s);
 bool gemm_mfma_supported(const LinearArgs& a);
 hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s);
 bool gemm_dot4_supported(const LinearArgs& a);
-hipError_t launch_gemm_big(const LinearArgs& a, hipStream_t s);
-bool gemm_big_supported(const LinearArgs& a);
+hipError_t launch_gemm_dl(const LinearArgs& a, hipStream_t s);
+bool gemm_dl_supported(const LinearArgs& a);
+// out[n] = sum_k w[n, k] for an [N, K] int8 matrix (K % 16 == 0, w 16-byte aligned).
+hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t s);
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);

@@ -183,7 +183,7 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
 
 
-@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "B"])
+@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
 def test_linear_every_gemm_tile(cfg, M, K, N):
     _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
@@ -193,13 +193,13 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
 
 
-@pytest.mark.parametrize("cfg", ["B", "D", "T", "Q", "K", "M"])
-@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768), (700, 272, 1100)])
-def test_linear_every_gemm32_tile(cfg, M, K, N):
-    """The 32x32x32 matrix-core GEMM in each of its tile shapes."""
-    _say(f"gemm32 cfg={cfg} M={M} K={K} N={N}")
-    c = qi.linear_case(M + N + ord(cfg) + 1, M, K, N)
-    with env(Q8TA_GEMM_CFG="B", Q8TA_GEMM32_CFG=cfg):
+@pytest.mark.parametrize("cfg", ["B", "D", "Q"])
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 257), (64, 128, 64), (512, 4096, 768), (700, 256, 1100)])
+def test_linear_every_gemm_dl_tile(cfg, M, K, N):
+    """The direct-to-LDS 32x32x32 matrix-core GEMM in each of its tile shapes."""
+    _say(f"gemm dl cfg={cfg} M={M} K={K} N={N}")
+    c = qi.linear_case(M + N + ord(cfg) + 2, M, K, N)
+    with env(Q8TA_GEMM_CFG="G", Q8TA_GEMM_DL_CFG=cfg):
         np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
         out = torch.empty((M, N), dtype=torch.float32, device="cuda")
