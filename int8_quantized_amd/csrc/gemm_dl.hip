@@ -77,10 +77,13 @@ struct CfgDL {
   static_assert(STAGES >= 2 && LOADS * (STAGES - 1) <= 63, "vmcnt range");
 };
 
+// Chunk swizzle: distinct positions for the rows one LDS cycle serves under
+// both an 8-lanes-per-cycle / 32-bank and a 16-lanes-per-cycle / 64-bank
+// reading of ds_read_b128; depends on row bits 0..4 only.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (CPR == 8) return row & 7;
-  else return (row >> 1) & 3;
+  if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
+  else return ((row >> 1) ^ (row >> 3)) & 3;
 }
 
 // s_waitcnt with vmcnt <= N and the other counters left alone (gfx9 encoding:
