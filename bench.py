@@ -321,10 +321,22 @@ def main():
         def chain():
             gemm()
             deq()
-        for name, fn in (("gemm_step_chain_us", chain), ("gemm_step_fused_us", gemm_dq)):
+        sums = torch.empty(N, dtype=torch.int32, device="cuda")
+        check(lib.q8ta_weight_sums(w.data_ptr(), N, K, sums.data_ptr(), stream))
+
+        def gemm_dq_presummed():
+            check(lib.q8ta_linear_dq_presummed(x.data_ptr(), M, K, c.in_scale, c.in_zp, w.data_ptr(),
+                                               N, sums.data_ptr(), ws.data_ptr(), b.data_ptr(),
+                                               c.out_scale, c.out_zp, none, y.data_ptr(), stream))
+        for name, fn in (("gemm_step_chain_us", chain), ("gemm_step_fused_us", gemm_dq),
+                         ("gemm_step_fused_presummed_us", gemm_dq_presummed)):
             extra[name] = round(min(timer.time_calls([fn], 10, batches=3)) * 1e3, 1)
+        extra["weight_sums_us"] = round(min(timer.time_calls(
+            [lambda: check(lib.q8ta_weight_sums(w.data_ptr(), N, K, sums.data_ptr(), stream))], 20,
+            batches=3)) * 1e3, 1)
         log(f"  step forms: chain {extra['gemm_step_chain_us']} us, "
-            f"fused {extra['gemm_step_fused_us']} us")
+            f"fused {extra['gemm_step_fused_us']} us, fused with precomputed weight sums "
+            f"{extra['gemm_step_fused_presummed_us']} us (+ {extra['weight_sums_us']} us once per weight)")
         extra.update(run_extra(torch, np, q8, qi, lib, stream, timer, check))
         extra["ceilings"] = run_ceilings(torch, stream, timer)
         log(f"  ceilings: {extra['ceilings']}")

@@ -144,6 +144,43 @@ q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K,
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Precomputed weight sums (opt-in).  [LIN] Constraints (1): the zero-point
+ * term needs sum_k weight[n, k]; the pages' op ignores its weight_sums
+ * argument and folds the term per call, while the Vulkan op it mirrors takes
+ * the sums precomputed.  These entry points offer the latter for weights that
+ * are reused across calls:
+ *   q8ta_weight_sums:  sums[n] = sum_{k<K} weight[n*K + k] (int32 [N]; exact
+ *     for K < 2^24).  weight: int8 [N, K] row-major.  Any K and alignment.
+ *   q8ta_linear_presummed / q8ta_linear_dq_presummed: q8ta_linear /
+ *     q8ta_linear_dq with weight_sums REQUIRED (NULL -> Q8TA_ERR_NULL) and
+ *     TRUSTED: the kernels subtract input_zero_point * weight_sums[n] instead of
+ *     forming the sums themselves.  With the sums q8ta_weight_sums returns the
+ *     results are bit-identical to q8ta_linear / q8ta_linear_dq; other sums
+ *     give other results (the library cannot check them).  All other
+ *     arguments, requirements and errors as for q8ta_linear / q8ta_linear_dq.
+ */
+q8ta_status q8ta_weight_sums(const int8_t* weight, int64_t N, int64_t K, int32_t* sums,
+                             hipStream_t stream);
+
+q8ta_status q8ta_linear_presummed(const int8_t* x, int64_t M, int64_t K,
+                                  double input_scale, int64_t input_zero_point,
+                                  const int8_t* weight, int64_t N,
+                                  const int32_t* weight_sums,
+                                  const float* weight_scales, const float* bias,
+                                  double output_scale, int64_t output_zero_point,
+                                  const char* activation, int8_t* out,
+                                  hipStream_t stream);
+
+q8ta_status q8ta_linear_dq_presummed(const int8_t* x, int64_t M, int64_t K,
+                                     double input_scale, int64_t input_zero_point,
+                                     const int8_t* weight, int64_t N,
+                                     const int32_t* weight_sums,
+                                     const float* weight_scales, const float* bias,
+                                     double output_scale, int64_t output_zero_point,
+                                     const char* activation, float* out,
+                                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * q8ta_conv2d_transposed ([DCV] Solution, Implementation, Constraints):
  *   acc[n,oc,oh,ow] = sum over (ic, kh, kw) of
  *       (x[n,ic,ih,iw] - input_zero_point) * weight[oc, (kh*Kw + kw)*IC + ic]

@@ -54,6 +54,11 @@ SIGNATURES = {
                                 _I64, _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
     "q8ta_linear_dq": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S, _P, _P],
                        ctypes.c_int),
+    "q8ta_weight_sums": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
+    "q8ta_linear_presummed": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
+                               _P, _P], ctypes.c_int),
+    "q8ta_linear_dq_presummed": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64,
+                                  _S, _P, _P], ctypes.c_int),
     "q8ta_quantize_conv2d_transposed": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64,
                                          _I64, _I64, _P, _P, _P, _DBL, _I64, _I64, _I64, _I64,
                                          _I64, _I64, _I64, _I64, _I64, _I64, _S, _P, _I64, _I64,
@@ -182,6 +187,46 @@ def q8ta_linear_gemv(x, input_scale, input_zero_point, weight, weight_sums, weig
     """q8ta_linear for M == 1."""
     return _linear(lib().q8ta_linear_gemv, x, input_scale, input_zero_point, weight, weight_sums,
                    weight_scales, bias, output_scale, output_zero_point, activation, out, stream)
+
+
+def q8ta_weight_sums(weight, sums, stream=None):
+    """sums[n] = sum_k weight[n, k] (int32 [N]) for int8 weight [N, K]."""
+    torch = _torch()
+    if weight.dim() != 2 or tuple(sums.shape) != (weight.shape[0],):
+        raise ValueError("weight [N, K] and sums [N] expected")
+    _check(lib().q8ta_weight_sums(_dev(weight, torch.int8, "weight"), weight.shape[0],
+                                  weight.shape[1], _dev(sums, torch.int32, "sums"),
+                                  _stream(stream)))
+    return sums
+
+
+def q8ta_linear_presummed(x, input_scale, input_zero_point, weight, weight_sums, weight_scales,
+                          bias, output_scale, output_zero_point, activation, out, stream=None):
+    """q8ta_linear with the caller's (trusted) weight_sums."""
+    if weight_sums is None:
+        raise ValueError("weight_sums is required")
+    return _linear(lib().q8ta_linear_presummed, x, input_scale, input_zero_point, weight,
+                   weight_sums, weight_scales, bias, output_scale, output_zero_point, activation,
+                   out, stream)
+
+
+def q8ta_linear_dq_presummed(x, input_scale, input_zero_point, weight, weight_sums, weight_scales,
+                             bias, output_scale, output_zero_point, activation, out, stream=None):
+    """q8ta_linear_dq with the caller's (trusted) weight_sums: fp32 out [M, N]."""
+    torch = _torch()
+    if weight_sums is None:
+        raise ValueError("weight_sums is required")
+    M, K = x.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError("weight [N, K] and out [M, N] expected")
+    _check(lib().q8ta_linear_dq_presummed(
+        _dev(x, torch.int8, "x"), M, K, float(input_scale), int(input_zero_point),
+        _dev(weight, torch.int8, "weight"), N, _dev(weight_sums, torch.int32, "weight_sums"),
+        _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+        float(output_scale), int(output_zero_point), _act(activation),
+        _dev(out, torch.float32, "out"), _stream(stream)))
+    return out
 
 
 def q8ta_linear_acc(x, input_zero_point, weight, acc, stream=None):
@@ -325,6 +370,7 @@ def q8ta_conv2d_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, dilati
 __all__ = [
     "Q8taError", "lib", "q8ta_last_error", "q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor",
     "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_dq", "q8ta_linear_acc", "q8ta_conv2d_transposed",
+    "q8ta_weight_sums", "q8ta_linear_presummed", "q8ta_linear_dq_presummed",
     "q8ta_conv2d_transposed_acc", "q8ta_quantize_conv2d_transposed", "q8ta_conv2d",
     "q8ta_conv2d_acc",
 ]

@@ -98,7 +98,8 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
                         double input_scale, int64_t input_zero_point, const int8_t* weight, int64_t N,
                         const float* weight_scales, const float* bias, double output_scale,
                         int64_t output_zero_point, const char* activation, int8_t* out,
-                        hipStream_t stream, float* outf = nullptr) {
+                        hipStream_t stream, float* outf = nullptr,
+                        const int32_t* wsum_pre = nullptr) {
   q8ta_status st = linear_checks(op, x, M, K, weight, N, outf ? (const void*)outf : out);
   if (st) return st;
   if (gemv_only && M != 1) return fail(Q8TA_ERR_SHAPE, "%s: M must be 1 (got %lld)", op, (long long)M);
@@ -115,6 +116,7 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   a.outf = outf;
   a.dq_scale = (float)output_scale;
   a.dq_zp = (int32_t)output_zero_point;
+  a.wsum_pre = wsum_pre;
   return hip_status(launch_linear(a, stream), op);
 }
 
@@ -266,6 +268,44 @@ q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K, double input_s
   return linear_impl("q8ta_linear_dq", false, x, M, K, input_scale, input_zero_point, weight, N,
                      weight_scales, bias, output_scale, output_zero_point, activation, nullptr,
                      stream, out);
+}
+
+q8ta_status q8ta_weight_sums(const int8_t* weight, int64_t N, int64_t K, int32_t* sums,
+                             hipStream_t stream) {
+  const char* op = "q8ta_weight_sums";
+  if (!weight || !sums) return fail(Q8TA_ERR_NULL, "%s: weight and sums must not be NULL", op);
+  if (N < 1 || K < 1 || N > kMaxElems / K || K >= ((int64_t)1 << 31))
+    return fail(Q8TA_ERR_SHAPE, "%s: N and K must be >= 1 (got %lld, %lld)", op, (long long)N,
+                (long long)K);
+  if (K % 16 == 0 && ((uintptr_t)weight & 15) == 0)
+    return hip_status(launch_row_sums(weight, N, K, sums, stream), op);
+  return hip_status(launch_row_sums_generic(weight, N, K, K, sums, stream), op);
+}
+
+q8ta_status q8ta_linear_presummed(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                                  int64_t input_zero_point, const int8_t* weight, int64_t N,
+                                  const int32_t* weight_sums, const float* weight_scales,
+                                  const float* bias, double output_scale,
+                                  int64_t output_zero_point, const char* activation, int8_t* out,
+                                  hipStream_t stream) {
+  const char* op = "q8ta_linear_presummed";
+  if (!weight_sums) return fail(Q8TA_ERR_NULL, "%s: weight_sums must not be NULL", op);
+  return linear_impl(op, false, x, M, K, input_scale, input_zero_point, weight, N, weight_scales,
+                     bias, output_scale, output_zero_point, activation, out, stream, nullptr,
+                     weight_sums);
+}
+
+q8ta_status q8ta_linear_dq_presummed(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                                     int64_t input_zero_point, const int8_t* weight, int64_t N,
+                                     const int32_t* weight_sums, const float* weight_scales,
+                                     const float* bias, double output_scale,
+                                     int64_t output_zero_point, const char* activation, float* out,
+                                     hipStream_t stream) {
+  const char* op = "q8ta_linear_dq_presummed";
+  if (!weight_sums) return fail(Q8TA_ERR_NULL, "%s: weight_sums must not be NULL", op);
+  return linear_impl(op, false, x, M, K, input_scale, input_zero_point, weight, N, weight_scales,
+                     bias, output_scale, output_zero_point, activation, nullptr, stream, out,
+                     weight_sums);
 }
 
 q8ta_status q8ta_linear_acc(const int8_t* x, int64_t M, int64_t K, int64_t input_zero_point,

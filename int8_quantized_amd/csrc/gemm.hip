@@ -26,6 +26,7 @@
 //    which share W and X slabs in that XCD's L2.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "q8ta_internal.h"
 
@@ -56,10 +57,13 @@ __device__ __forceinline__ int swz(int row, int c) {
   else return c ^ ((row >> 1) & 3);
 }
 
-template <class C>
+// PRE: the row sums of W come from a.wsum_pre (trusted, precomputed by the
+// caller) instead of v_dot4 over the W fragments.
+template <class C, bool PRE>
 __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t smem[2 * C::STAGE];
   __shared__ float epi[2 * C::BN];   // per-channel scale and bias of the tile
+  __shared__ int32_t epi_ws[PRE ? C::BN : 1];   // per-channel row sums (PRE)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,10 +138,12 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
   // after the loop.
   static_assert(C::BN <= C::NT, "one channel per thread");
   float e_sc = 0.0f, e_bi = 0.0f;
+  int32_t e_ws = 0;
   if (tid < C::BN && !a.acc && bn0 + tid < N) {
     e_sc = a.wscale[bn0 + tid];
     e_bi = a.bias ? a.bias[bn0 + tid] : 0.0f;
   }
+  if (PRE && tid < C::BN && bn0 + tid < N) e_ws = a.wsum_pre[bn0 + tid];
 
   load_global(0);
   store_lds(0);
@@ -164,12 +170,14 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
         const int row = wm * C::WM + j * 16 + lrow;
         bf[j] = *reinterpret_cast<const v4i*>(Bs + row * C::BK + 16 * swz<C::CPR>(row, c));
       }
+      if constexpr (!PRE) {
 #pragma unroll
-      for (int i = 0; i < C::FN; ++i) {
-        wsum[i] = __builtin_amdgcn_sdot4(af[i][0], 0x01010101, wsum[i], false);
-        wsum[i] = __builtin_amdgcn_sdot4(af[i][1], 0x01010101, wsum[i], false);
-        wsum[i] = __builtin_amdgcn_sdot4(af[i][2], 0x01010101, wsum[i], false);
-        wsum[i] = __builtin_amdgcn_sdot4(af[i][3], 0x01010101, wsum[i], false);
+        for (int i = 0; i < C::FN; ++i) {
+          wsum[i] = __builtin_amdgcn_sdot4(af[i][0], 0x01010101, wsum[i], false);
+          wsum[i] = __builtin_amdgcn_sdot4(af[i][1], 0x01010101, wsum[i], false);
+          wsum[i] = __builtin_amdgcn_sdot4(af[i][2], 0x01010101, wsum[i], false);
+          wsum[i] = __builtin_amdgcn_sdot4(af[i][3], 0x01010101, wsum[i], false);
+        }
       }
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
@@ -184,6 +192,7 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
   if (tid < C::BN) {
     epi[tid] = e_sc;
     epi[C::BN + tid] = e_bi;
+    if constexpr (PRE) epi_ws[tid] = e_ws;
   }
   __syncthreads();
 
@@ -193,11 +202,16 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
   int32_t ws4[C::FN][4];
 #pragma unroll
   for (int i = 0; i < C::FN; ++i) {
-    int32_t v = wsum[i];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    if constexpr (PRE) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ws4[i][r] = __shfl(v, 4 * lgrp + r, 64);
+      for (int r = 0; r < 4; ++r) ws4[i][r] = epi_ws[wn * C::WN + i * 16 + 4 * lgrp + r];
+    } else {
+      int32_t v = wsum[i];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ws4[i][r] = __shfl(v, 4 * lgrp + r, 64);
+    }
   }
 
   const bool vec_store = (N % 4) == 0 && ((uintptr_t)a.out & 3) == 0;
@@ -268,7 +282,18 @@ hipError_t launch_cfg(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
   const int T = tiles_m * tiles_n;
-  hipLaunchKernelGGL(k_gemm<C>, dim3((unsigned)T), dim3(C::NT), 0, s, a, tiles_m, tiles_n);
+  // The tiles the default choice uses also come in a form that takes the
+  // caller's row sums; the others form their own (same result).
+  constexpr bool pre_built = std::is_same<C, CfgV>::value || std::is_same<C, CfgM>::value ||
+                             std::is_same<C, CfgS>::value;
+  if constexpr (pre_built) {
+    if (a.wsum_pre) {
+      hipLaunchKernelGGL((k_gemm<C, true>), dim3((unsigned)T), dim3(C::NT), 0, s, a, tiles_m,
+                         tiles_n);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_gemm<C, false>), dim3((unsigned)T), dim3(C::NT), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -296,13 +296,18 @@ hipError_t launch_dl(const LinearArgs& a, hipStream_t s) {
       attr_set = true;
     }
   }
+  const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
+  const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
+  if (a.wsum_pre) {   // the caller's row sums: no pre-pass, no workspace
+    hipLaunchKernelGGL(k_gemm_dl<C>, dim3((unsigned)(tiles_m * tiles_n)), dim3(C::NT), C::LDS, s,
+                       a, tiles_m, tiles_n, a.wsum_pre);
+    return hipGetLastError();
+  }
   void* ws = nullptr;
   hipError_t e = workspace_alloc(&ws, (size_t)a.N * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
   e = launch_row_sums(a.w, a.N, a.K, (int32_t*)ws, s);
   if (e == hipSuccess) {
-    const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
-    const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
     hipLaunchKernelGGL(k_gemm_dl<C>, dim3((unsigned)(tiles_m * tiles_n)), dim3(C::NT), C::LDS, s,
                        a, tiles_m, tiles_n, (const int32_t*)ws);
     e = hipGetLastError();

@@ -274,6 +274,11 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
   const int64_t blocks = (int64_t)BMb * (xcd ? ((int64_t)BNb + 7) / 8 * 8 : BNb);
   if (group < 1) group = 1;
   if (group > BMb) group = BMb;
+  if (a.wsum_pre) {   // the caller's row sums: no pre-pass, no workspace
+    hipLaunchKernelGGL((k_dot4_gemm<LW, PIPE, LPG, GM>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       s, a, BMb, BNb, (uint32_t)group, xcd, a.wsum_pre);
+    return hipGetLastError();
+  }
   void* ws = nullptr;
   hipError_t e = workspace_alloc(&ws, (size_t)a.N * sizeof(int32_t), s);
   if (e != hipSuccess) return e;

@@ -117,6 +117,24 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// sum_k w[n, k] for any K and alignment: one thread per row.
+__global__ __launch_bounds__(kThreads) void k_row_sums_generic(const int8_t* w, int64_t N, int64_t K,
+                                                               int64_t ldw, int32_t* out) {
+  const int64_t n = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (n >= N) return;
+  const int8_t* r = w + n * ldw;
+  int32_t s = 0;
+  for (int64_t k = 0; k < K; ++k) s += r[k];
+  out[n] = s;
+}
+
+hipError_t launch_row_sums_generic(const int8_t* w, int64_t N, int64_t K, int64_t ldw, int32_t* out,
+                                   hipStream_t s) {
+  hipLaunchKernelGGL(k_row_sums_generic, dim3((unsigned)((N + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, w, N, K, ldw, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s) {
   int64_t total = a.N * a.OC * a.H_out * a.W_out;
   int64_t blocks = (total + kThreads - 1) / kThreads;

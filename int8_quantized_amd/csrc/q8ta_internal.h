@@ -161,6 +161,10 @@ struct LinearArgs {
   float* outf = nullptr;
   float dq_scale = 0.0f;
   int32_t dq_zp = 0;
+  // Trusted per-row sums sum_k w[n, k] supplied by the caller (the
+  // precomputed weight_sums of the presummed entry points); NULL: the kernels
+  // form them.
+  const int32_t* wsum_pre = nullptr;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
@@ -218,6 +222,9 @@ hipError_t launch_gemm_dl(const LinearArgs& a, hipStream_t s);
 bool gemm_dl_supported(const LinearArgs& a);
 // out[n] = sum_k w[n, k] for an [N, K] int8 matrix (K % 16 == 0, w 16-byte aligned).
 hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t s);
+// Same for any K and alignment, rows ldw bytes apart (one thread per row).
+hipError_t launch_row_sums_generic(const int8_t* w, int64_t N, int64_t K, int64_t ldw, int32_t* out,
+                                   hipStream_t s);
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);

@@ -159,6 +159,18 @@ def linear_acc(x, w, input_zero_point: int, folded: bool = False) -> np.ndarray:
     return acc
 
 
+def weight_sums(w, K: int | None = None) -> np.ndarray:
+    """sum_k w[n, k] over the first K columns (all by default), int32: the
+    zero-point term's factor of #21197 Constraints (1) (sum(x-zp)w = sum xw -
+    zp * sum w).  Formed in int64 and checked to fit int32."""
+    w = _c(w, np.int8)
+    K = w.shape[1] if K is None else K
+    s = w[:, :K].astype(np.int64).sum(axis=1)
+    if s.size and (s.max() > np.iinfo(np.int32).max or s.min() < np.iinfo(np.int32).min):
+        raise OverflowError("weight_sums: a sum left the int32 range")
+    return s.astype(np.int32)
+
+
 def linear(x, w, weight_scales, bias, input_scale: float, input_zero_point: int,
            output_scale: float, output_zero_point: int, return_acc: bool = False,
            activation: str = "none"):

@@ -247,6 +247,25 @@ def test_fused_entry_points_errors():
     _st(l.q8ta_quantize_conv2d_transposed(*a), q8.Q8TA_ERR_QPARAM)
 
 
+def test_presummed_entry_points_errors():
+    l = q8.lib()
+    _st(l.q8ta_weight_sums(None, 32, 64, FAKE, None), q8.Q8TA_ERR_NULL)
+    _st(l.q8ta_weight_sums(FAKE, 32, 64, None, None), q8.Q8TA_ERR_NULL)
+    _st(l.q8ta_weight_sums(FAKE, 0, 64, FAKE, None), q8.Q8TA_ERR_SHAPE)
+    _st(l.q8ta_weight_sums(FAKE, 32, 0, FAKE, None), q8.Q8TA_ERR_SHAPE)
+    for fn in (l.q8ta_linear_presummed, l.q8ta_linear_dq_presummed):
+        # weight_sums is required
+        _st(fn(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_NULL, "weight_sums")
+        # the rest as for q8ta_linear
+        _st(fn(FAKE, 0, 64, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_SHAPE)
+        _st(fn(FAKE, 4, 64, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"gelu", FAKE, None),
+            q8.Q8TA_ERR_UNSUPPORTED)
+        _st(fn(FAKE, 4, 64, 0.02, 300, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_QPARAM)
+
+
 def _gpu_present():
     try:
         import torch
@@ -273,6 +292,9 @@ def test_relu_dilation_and_groups_pass_validation():
     _st(_dc(groups=2, ldw=512), q8.Q8TA_ERR_HIP, "HIP error")
     _st(_dc(groups=32, ldw=32), q8.Q8TA_ERR_HIP, "HIP error")
     _st(_cv(act=b"relu"), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(q8.lib().q8ta_weight_sums(FAKE, 32, 64, FAKE, None), q8.Q8TA_ERR_HIP, "HIP error")
+    _st(q8.lib().q8ta_linear_presummed(FAKE, 4, 64, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5,
+                                       b"none", FAKE, None), q8.Q8TA_ERR_HIP, "HIP error")
 
 
 def test_binding_rejects_host_tensors():

@@ -786,3 +786,51 @@ def test_deconv_grouped_parity(case):
     np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
     np.testing.assert_array_equal(_run_deconv(c, activation="relu"),
                                   _oracle_deconv(c, activation="relu"))
+
+
+# ============================================================================ precomputed weight sums (opt-in)
+@pytest.mark.parametrize("N,K,offset", [(4096, 4096, 0), (257, 1040, 0), (37, 33, 0), (5, 64, 1),
+                                        (11008, 4096, 0)])
+def test_weight_sums(N, K, offset):
+    _say(f"weight sums N={N} K={K} offset={offset}")
+    g = qi.rng(N + K + offset)
+    w = qi.w_int8(g, (N, K))
+    buf = torch.zeros(N * K + offset, dtype=torch.int8, device="cuda")
+    buf[offset:] = dev(w.reshape(-1))
+    sums = torch.empty(N, dtype=torch.int32, device="cuda")
+    q8.q8ta_weight_sums(buf[offset:].view(N, K), sums)
+    np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
+
+
+@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "dot4", "generic"])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
+                                   (7, 33, 5)])
+def test_linear_presummed_equals_linear(path, M, K, N):
+    """With the sums q8ta_weight_sums returns, the presummed calls give the
+    same bits as q8ta_linear / q8ta_linear_dq on every kernel; with other sums
+    the results move (the sums are used, not recomputed)."""
+    _say(f"presummed {path} M={M} K={K} N={N}")
+    c = qi.linear_case(M * 11 + K + N + len(path), M, K, N)
+    kind, cfg = (path.split(":") + [""])[:2]
+    envs = {"default": {}, "mfma": {"Q8TA_GEMM_CFG": cfg}, "dot4": {"Q8TA_GEMM_PATH": "dot4"},
+            "generic": {}}[kind]
+    wd = dev(c.w)
+    sums = torch.empty(N, dtype=torch.int32, device="cuda")
+    q8.q8ta_weight_sums(wd, sums)
+    ref = _oracle_linear(c)
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    outf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    with env(**envs):
+        q8.q8ta_linear_presummed(dev(c.x), c.in_scale, c.in_zp, wd, sums, dev(c.weight_scales),
+                                 dev(c.bias), c.out_scale, c.out_zp, "none", out)
+        np.testing.assert_array_equal(host(out), ref)
+        q8.q8ta_linear_dq_presummed(dev(c.x), c.in_scale, c.in_zp, wd, sums, dev(c.weight_scales),
+                                    dev(c.bias), c.out_scale, c.out_zp, "none", outf)
+        dq = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
+        np.testing.assert_array_equal(host(outf).view(np.uint32), dq.view(np.uint32))
+        if M > 4 and K % 16 == 0:
+            # kernels that take the sums: shifted sums shift the accumulator
+            wrong = sums + 1000
+            q8.q8ta_linear_presummed(dev(c.x), c.in_scale, c.in_zp, wd, wrong, dev(c.weight_scales),
+                                     dev(c.bias), c.out_scale, c.out_zp, "none", out)
+            assert not np.array_equal(host(out), ref)

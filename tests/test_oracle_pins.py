@@ -707,3 +707,17 @@ def test_grouped_dilated_deconv_brute_force_tiny():
     for method in ("gather", "scatter", "zpfill"):
         np.testing.assert_array_equal(
             oracle.deconv_acc(x, w, zp, Kh, Kw, s, p, d, Ho, Wo, method=method, groups=G), ref)
+
+
+# --------------------------------------------------------------------------- weight sums (precomputed, opt-in)
+def test_weight_sums_brute_force_and_zero_point_identity():
+    """sum_k w[n,k] by pure-Python loops on a tiny matrix, and through the
+    contraction: acc(zp = 0) - acc(zp) == zp * sum_k w (the page's fold)."""
+    g = qi.rng(99)
+    w = qi.w_int8(g, (5, 37))
+    ref = [sum(int(v) for v in row) for row in w]
+    np.testing.assert_array_equal(oracle.weight_sums(w), np.array(ref, np.int32))
+    np.testing.assert_array_equal(oracle.weight_sums(w, K=20), np.array([sum(int(v) for v in row[:20]) for row in w], np.int32))
+    x = qi.x_int8(g, (3, 37))
+    d = oracle.linear_acc(x, w, 0).astype(np.int64) - oracle.linear_acc(x, w, 7).astype(np.int64)
+    np.testing.assert_array_equal(d, 7 * np.broadcast_to(oracle.weight_sums(w).astype(np.int64), d.shape))
