@@ -12,20 +12,24 @@
  *     allocated and owned by the caller; the library never frees or retains
  *     it.  Tensors are dense and contiguous in the stated layout.  int8
  *     tensors are plain byte arrays (element i at byte i).
- *   - Workspace: on their register-tiled paths, q8ta_linear / q8ta_linear_acc
- *     with M > 4 (K % 16 == 0, 16-byte aligned x and weight) take 4*N bytes
- *     (weight row sums); q8ta_conv2d_transposed(_acc) takes, on its
- *     implicit-GEMM path (IC % 64 == 0), an NHWC copy of the input inside a
- *     zero-point border (N * IC * (H_in + a few rows) * (W_in + a few
- *     columns) bytes) plus 4 * stride_h * stride_w * OC bytes of weight sums,
- *     and on its direct tiled path (other IC % 4 == 0) a channel-blocked copy
- *     of the input (N * H_in * ceil(IC/16) * W_in * 16 bytes).  Workspaces
- *     come from the stream-ordered allocator (hipMallocAsync on `stream`,
- *     released with hipFreeAsync on the same stream after the kernels that
- *     use them); a failed allocation returns Q8TA_ERR_HIP.
+ *   - Workspace: some paths need device scratch memory: q8ta_linear(_acc,
+ *     _dq) on the v_dot4 and direct-to-LDS GEMMs take 4*N bytes of weight
+ *     row sums (the default matrix-core GEMM and the presummed calls take
+ *     none); q8ta_quantize_conv2d_transposed takes the int8 copy of its input
+ *     (N * IC * H_in * W_in bytes); q8ta_conv2d_transposed(_acc) takes, on
+ *     its implicit-GEMM path, an NHWC copy of the input inside a zero-point
+ *     border plus 4 * stride_h * stride_w * OC bytes of weight sums, and on
+ *     its v_dot4 tiled path a channel-blocked copy of the input
+ *     (N * H_in * ceil(IC/16) * W_in * 16 bytes).  The library keeps one
+ *     buffer per (device, stream, nesting depth), grows it on demand after
+ *     synchronizing that stream, and holds it until the process ends; under
+ *     graph capture, above 256 MiB or deeper than 4 nested uses it takes
+ *     stream-ordered memory (hipMallocAsync / hipFreeAsync on `stream`)
+ *     instead.  A failed allocation returns Q8TA_ERR_HIP.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns after the launch; results are visible to later work on that
- *     stream.  Calls are reentrant and keep no state between calls.
+ *     stream.  Calls are reentrant (several host threads may call at once)
+ *     and keep no state between calls except the cached workspaces.
  *   - Scales are passed as double.  The library forms every reciprocal as
  *     (float)(1.0 / scale) in double on the host ([QPT] commit message) and
  *     uses (float)scale for a scale that multiplies.

@@ -9,6 +9,9 @@
 #include <cstring>
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <cstdlib>
 
 #include "../../include/q8ta.h"
@@ -124,7 +127,9 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
 
 namespace q8ta {
 
-hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s) {
+namespace {
+
+hipError_t pool_alloc(void** p, size_t bytes, hipStream_t s) {
   static std::atomic<uint64_t> pools_set{0};   // one bit per device
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -138,6 +143,84 @@ hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s) {
     pools_set.fetch_or(1ull << dev);
   }
   return hipMallocAsync(p, bytes, s);
+}
+
+constexpr int kWsDepth = 4;                          // nested acquisitions per stream
+constexpr size_t kWsCachedMax = (size_t)256 << 20;   // larger requests use the pool
+constexpr size_t kWsGrain = (size_t)1 << 20;
+
+struct WsSlot {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+struct WsStream {
+  WsSlot slot[kWsDepth];
+  int depth = 0;
+};
+
+// Held from a cached acquisition to its release, so that no other thread
+// regrows a buffer between a call's launches.
+std::recursive_mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, WsStream> g_ws;
+
+}  // namespace
+
+hipError_t workspace_acquire(void** p, size_t bytes, hipStream_t s) {
+  *p = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) return e;
+  if (cap != hipStreamCaptureStatusNone || bytes > kWsCachedMax) return pool_alloc(p, bytes, s);
+  g_ws_mu.lock();
+  WsStream& ws = g_ws[{dev, (uintptr_t)s}];
+  if (ws.depth >= kWsDepth) {
+    g_ws_mu.unlock();
+    return pool_alloc(p, bytes, s);
+  }
+  WsSlot& sl = ws.slot[ws.depth];
+  if (sl.bytes < bytes) {
+    if (sl.ptr) {
+      // earlier calls on this stream may still read the old buffer
+      e = hipStreamSynchronize(s);
+      if (e == hipSuccess) e = hipFree(sl.ptr);
+      if (e != hipSuccess) {
+        g_ws_mu.unlock();
+        return e;
+      }
+      sl = WsSlot{};
+    }
+    const size_t want = (bytes + kWsGrain - 1) / kWsGrain * kWsGrain;
+    e = hipMalloc(&sl.ptr, want);
+    if (e != hipSuccess) {
+      sl = WsSlot{};
+      g_ws_mu.unlock();
+      return e;
+    }
+    sl.bytes = want;
+  }
+  ++ws.depth;
+  *p = sl.ptr;
+  return hipSuccess;   // g_ws_mu stays locked until workspace_release
+}
+
+hipError_t workspace_release(void* p, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::recursive_mutex> g(g_ws_mu);
+    auto it = g_ws.find({dev, (uintptr_t)s});
+    if (it != g_ws.end() && it->second.depth > 0 &&
+        it->second.slot[it->second.depth - 1].ptr == p) {
+      --it->second.depth;
+      g_ws_mu.unlock();   // the lock taken by workspace_acquire
+      return hipSuccess;
+    }
+  }
+  return hipFreeAsync(p, s);
 }
 
 // Q8TA_GEMM_PATH = dot4 skips the matrix-core GEMM where both apply (used by
@@ -185,7 +268,7 @@ hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
   if (!mfma && k != 'm' && deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
   const int64_t numel = a.N * a.IC * a.H_in * a.W_in;
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(&ws, (size_t)numel, s);
+  hipError_t e = workspace_acquire(&ws, (size_t)numel, s);
   if (e != hipSuccess) return e;
   e = launch_quantize(a.xf, (int8_t*)ws, numel, a.inv_in, (float)a.izp, s);
   if (e == hipSuccess) {
@@ -193,7 +276,7 @@ hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
     a.xf = nullptr;
     e = launch_deconv(a, s);
   }
-  hipError_t f = hipFreeAsync(ws, s);
+  hipError_t f = workspace_release(ws, s);
   return e != hipSuccess ? e : f;
 }
 

@@ -393,7 +393,7 @@ hipError_t launch_blocked(const DeconvArgs& a, Phases p, hipStream_t s) {
   const int G = (int)((a.IC + 15) / 16);
   const size_t bytes = (size_t)a.N * a.H_in * a.W_in * G * 16;
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(&ws, bytes, s);
+  hipError_t e = workspace_acquire(&ws, bytes, s);
   if (e != hipSuccess) return e;
   const int64_t t = (int64_t)a.N * a.H_in * G * a.W_in;
   hipLaunchKernelGGL(k_nchw_to_blocked16, dim3((unsigned)((t + kThreads - 1) / kThreads)),
@@ -411,7 +411,7 @@ hipError_t launch_blocked(const DeconvArgs& a, Phases p, hipStream_t s) {
                          (const int8_t*)ws);
     e = hipGetLastError();
   }
-  hipError_t f = hipFreeAsync(ws, s);
+  hipError_t f = workspace_release(ws, s);
   return e != hipSuccess ? e : f;
 }
 

@@ -382,7 +382,7 @@ hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, int osh, int osw
   const size_t xpad = (xbytes + 255) / 256 * 256;
   const size_t wsbytes = (size_t)plan.nph * (size_t)a.OC * sizeof(int32_t);
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(&ws, xpad + wsbytes, s);
+  hipError_t e = workspace_acquire(&ws, xpad + wsbytes, s);
   if (e != hipSuccess) return e;
   int8_t* xp = (int8_t*)ws;
   int32_t* wsum = (int32_t*)((char*)ws + xpad);
@@ -401,7 +401,7 @@ hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, int osh, int osw
                          0, s, a, p, plan, (const int8_t*)xp, (const int32_t*)wsum);
     e = hipGetLastError();
   }
-  hipError_t f = hipFreeAsync(ws, s);
+  hipError_t f = workspace_release(ws, s);
   return e != hipSuccess ? e : f;
 }
 

@@ -317,18 +317,20 @@ bool gemm_mfma_supported(const LinearArgs& a) {
 // long, otherwise the medium tile, or the small one for few rows.  The large
 // tile of this file (128 x 128 per wave, loops the compiler leaves rolled)
 // keeps its accumulators in scratch memory; the direct-to-LDS 32x32x32 kernel
-// of gemm_dl.hip ('G') measured slower on that shape.  Q8TA_GEMM_CFG (one
-// letter of LMSKWVUQRG) overrides the choice.
+// of gemm_dl.hip ('G') measured slower on that shape, as did the 32x32x32
+// variant of the 256 x 128 tile in gemm32.hip ('X').  Q8TA_GEMM_CFG (one
+// letter of LMSKWVUQRGX) overrides the choice.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
-  if (e && strchr("LMSKWVUQRG", e[0])) pick = e[0];
+  if (e && strchr("LMSKWVUQRGX", e[0])) pick = e[0];
   if (!pick) {
     const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
     pick = (tv >= 256 && a.K >= 1024) ? 'V' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
   }
   if (pick == 'G') return gemm_dl_supported(a) ? launch_gemm_dl(a, s) : launch_cfg<CfgM>(a, s);
+  if (pick == 'X') return launch_gemm32(a, s);
   switch (pick) {
     case 'L': return launch_cfg<CfgL>(a, s);
     case 'M': return launch_cfg<CfgM>(a, s);

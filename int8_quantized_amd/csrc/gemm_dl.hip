@@ -304,7 +304,7 @@ hipError_t launch_dl(const LinearArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(&ws, (size_t)a.N * sizeof(int32_t), s);
+  hipError_t e = workspace_acquire(&ws, (size_t)a.N * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
   e = launch_row_sums(a.w, a.N, a.K, (int32_t*)ws, s);
   if (e == hipSuccess) {
@@ -312,7 +312,7 @@ hipError_t launch_dl(const LinearArgs& a, hipStream_t s) {
                        a, tiles_m, tiles_n, (const int32_t*)ws);
     e = hipGetLastError();
   }
-  hipError_t f = hipFreeAsync(ws, s);
+  hipError_t f = workspace_release(ws, s);
   return e != hipSuccess ? e : f;
 }
 

@@ -280,7 +280,7 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
     return hipGetLastError();
   }
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(&ws, (size_t)a.N * sizeof(int32_t), s);
+  hipError_t e = workspace_acquire(&ws, (size_t)a.N * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_row_sums, dim3((unsigned)((a.N + 3) / 4)), dim3(kThreads), 0, s, a.w, a.N,
                      a.K, (int32_t*)ws);
@@ -290,7 +290,7 @@ hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t group, int xcd) 
                        s, a, BMb, BNb, (uint32_t)group, xcd, (const int32_t*)ws);
     e = hipGetLastError();
   }
-  hipError_t f = hipFreeAsync(ws, s);
+  hipError_t f = workspace_release(ws, s);
   return e != hipSuccess ? e : f;
 }
 

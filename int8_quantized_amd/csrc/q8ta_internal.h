@@ -133,12 +133,16 @@ __device__ __forceinline__ gptr uniform_ptr(const int8_t* p) {
   return (gptr)(((uint64_t)hi << 32) | lo);
 }
 
-// Stream-ordered workspace from the current device's default memory pool
-// (hipMallocAsync; release with hipFreeAsync on the same stream).  On first use
-// per device the pool is told to keep up to 1 GiB after frees: by default it
-// returns freed memory at every synchronization and each call maps memory
-// afresh.
-hipError_t workspace_alloc(void** p, size_t bytes, hipStream_t s);
+// Scratch device memory ordered on stream s, released with workspace_release
+// on the same stream and thread once the call's kernels are launched.  The
+// library keeps one buffer per (device, stream) and nesting depth, grown on
+// demand (after a synchronization of s) and held until the process ends:
+// a per-call hipMallocAsync / hipFreeAsync pair costs ~15 us of stream time.
+// Requests above 256 MiB, deeper nesting and streams under graph capture take
+// stream-ordered memory from the device's default pool instead (kept up to
+// 1 GiB after frees).  Between acquire and release the library holds a lock.
+hipError_t workspace_acquire(void** p, size_t bytes, hipStream_t s);
+hipError_t workspace_release(void* p, hipStream_t s);
 
 // ---- launchers (host functions; each returns hipGetLastError() after launch)
 hipError_t launch_quantize(const float* x, int8_t* out, int64_t numel, float inv_scale, float zp,
@@ -220,6 +224,8 @@ hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s);
 bool gemm_dot4_supported(const LinearArgs& a);
 hipError_t launch_gemm_dl(const LinearArgs& a, hipStream_t s);
 bool gemm_dl_supported(const LinearArgs& a);
+// 32x32x32 matrix-core GEMM (same operand requirements as launch_gemm_mfma).
+hipError_t launch_gemm32(const LinearArgs& a, hipStream_t s);
 // out[n] = sum_k w[n, k] for an [N, K] int8 matrix (K % 16 == 0, w 16-byte aligned).
 hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t s);
 // Same for any K and alignment, rows ldw bytes apart (one thread per row).

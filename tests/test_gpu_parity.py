@@ -3,6 +3,7 @@ oracle on the same seeded inputs.  int8 outputs and int32 accumulators must be
 bit-exact (integer sums are order-free and the float epilogue is evaluated in
 the same operation order on both sides, without fused multiply-add).
 """
+import contextlib
 import os
 import sys
 
@@ -183,7 +184,7 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
 
 
-@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R"])
+@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
 def test_linear_every_gemm_tile(cfg, M, K, N):
     _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
@@ -668,6 +669,42 @@ def test_quantize_conv2d_transposed_large_workload_sampled():
 
 
 
+@pytest.mark.parametrize("path", ["mfma", "igemm", "dot4"])
+def test_workspace_reuse_across_calls_and_streams(path):
+    """Calls that need scratch memory, queued back to back without a host
+    synchronization: small, larger (the stream's buffer grows), small again,
+    and one on a second stream.  Every result is checked after one final
+    synchronization."""
+    _say(f"workspace reuse {path}")
+    shapes = [(1, 32, 6, 5, 16), (2, 64, 13, 11, 32), (1, 16, 4, 9, 16)]
+    cases = [qi.deconv_case(940 + i, n, ic, h, w, oc, 3, 3, (2, 2), (1, 1), (1, 1),
+                            x_from_fp32=True) for i, (n, ic, h, w, oc) in enumerate(shapes)]
+    side = torch.cuda.Stream()
+    keep, outs = [], []
+    with env(Q8TA_DECONV_PATH=path):
+        for i, c in enumerate(cases + cases[1:2]):
+            args = (dev(c.x_fp32), dev(c.w), dev(c.weight_scales), dev(c.bias))
+            out = torch.empty((c.x_fp32.shape[0], c.w.shape[0], c.H_out, c.W_out),
+                              dtype=torch.int8, device="cuda")
+            keep.append(args)
+            outs.append(out)
+            ctx = torch.cuda.stream(side) if i == 3 else contextlib.nullcontext()
+            if i == 3:
+                side.wait_stream(torch.cuda.current_stream())
+            with ctx:
+                q8.q8ta_quantize_conv2d_transposed(args[0], c.in_scale, c.in_zp, args[1], c.Kh,
+                                                   c.Kw, None, args[2], args[3], c.out_scale,
+                                                   c.out_zp, c.stride, c.padding,
+                                                   c.output_padding, (1, 1), 1, "none", out)
+    torch.cuda.synchronize()
+    for c, out in zip(cases + cases[1:2], outs):
+        xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+        ref = oracle.conv2d_transposed(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                       c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding,
+                                       (1, 1), c.H_out, c.W_out)
+        np.testing.assert_array_equal(host(out), ref)
+
+
 # ============================================================================ relu, transposed-conv dilation and groups
 @pytest.mark.parametrize("M,K,N", [(1, 512, 64), (1, 4096, 4096), (3, 48, 17), (300, 1040, 257),
                                    (7, 33, 5), (64, 128, 64)])
@@ -802,7 +839,7 @@ def test_weight_sums(N, K, offset):
     np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
 
 
-@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "dot4", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "mfma:X", "dot4", "generic"])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
                                    (7, 33, 5)])
 def test_linear_presummed_equals_linear(path, M, K, N):
