@@ -35,6 +35,7 @@
 //     of the workgroup's NCHW output block (phases interleaved there), which
 //     is then written to global memory in whole rows.
 #include <cstdlib>
+#include <type_traits>
 
 #include "q8ta_internal.h"
 
@@ -46,10 +47,29 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kMaxS = 4;   // largest stride the tiled kernel takes
 constexpr int kMaxT = 8;   // largest number of taps per residue
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kDepth = 2;  // weight-fragment prefetch distance (iterations)
+
+template <int B, int E>
+struct Static {
+  template <class F>
+  __device__ __forceinline__ static void each(F&& f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>{});
+      Static<B + 1, E>::each(f);
+    }
+  }
+};
 
 struct Plan {
   int nth[kMaxS], thk[kMaxS][kMaxT], thd[kMaxS][kMaxT];
   int ntw[kMaxS], twk[kMaxS][kMaxT], twd[kMaxS][kMaxT];
+  // The qualifying taps of a residue form an arithmetic progression in both
+  // the kernel index and the input offset (solutions of one linear
+  // congruence): tap t of row residue r is kernel row hk0[r] + t*hks[r],
+  // input row offset hd0[r] + t*hds[r]; likewise for columns.  The kernel
+  // uses these (scalar arithmetic) instead of indexing the tables.
+  int hk0[kMaxS], hks[kMaxS], hd0[kMaxS], hds[kMaxS];
+  int wk0[kMaxS], wks[kMaxS], wd0[kMaxS], wds[kMaxS];
   int dhmin, dwmin;
   int Hp, Wp;                 // phase rows / columns: ceil(H_out/s_h), ceil(W_out/s_w)
   int WI, WO, TJ, OCB;        // workgroup tile
@@ -111,19 +131,38 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
       const int iw = col0 + 4 * cg;
       const bool row_ok = ih >= 0 && ih < H_in;
       uint32_t d[16];
+      if (p.x_dword) {
+        // All 16 loads are unconditional, from addresses clamped into the
+        // image (an exec-masked load per channel would make the compiler
+        // wait for each one before the next); out-of-image words and
+        // channels past IC are then replaced.  W_in % 4 == 0 and iw is a
+        // multiple of 4, so the clamped column stays word-aligned.
+        const bool in_img = row_ok && iw >= 0 && iw < W_in;
+        const int ihc = ih < 0 ? 0 : (ih >= H_in ? H_in - 1 : ih);
+        const int iwc = iw < 0 ? 0 : (iw > W_in - 4 ? W_in - 4 : iw);
+        const int8_t* src0 = xn + (int64_t)ihc * W_in + iwc;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int ic = q * 16 + t;
-        uint32_t v;
-        if (ic >= IC) {
-          v = 0u;
-        } else if (!row_ok) {
-          v = zp4;
-        } else {
-          const int8_t* src = xn + (int64_t)ic * plane + (int64_t)ih * W_in;
-          if (p.x_dword) {
-            v = (iw >= 0 && iw < W_in) ? *reinterpret_cast<const uint32_t*>(src + iw) : zp4;
+        for (int t = 0; t < 16; ++t) {
+          const int ic = q * 16 + t;
+          const int icc = ic < IC ? ic : IC - 1;
+          d[t] = *reinterpret_cast<const uint32_t*>(src0 + (int64_t)icc * plane);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int ic = q * 16 + t;
+          d[t] = ic >= IC ? 0u : (in_img ? d[t] : zp4);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int ic = q * 16 + t;
+          uint32_t v;
+          if (ic >= IC) {
+            v = 0u;
+          } else if (!row_ok) {
+            v = zp4;
           } else {
+            const int8_t* src = xn + (int64_t)ic * plane + (int64_t)ih * W_in;
             v = 0u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -133,8 +172,8 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
               v |= by << (8 * e);
             }
           }
+          d[t] = v;
         }
-        d[t] = v;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {   // pixel 4*cg + e of this row
@@ -184,45 +223,92 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
 #pragma unroll
           for (int g = 0; g < FJ; ++g) acc[g][f] = v4i{0, 0, 0, 0};
         }
-        for (int th = 0; th < p.nth[rh]; ++th) {
-          const int kh = p.thk[rh][th];
-          const int lr = wi + p.thd[rh][th] - p.dhmin;
-          for (int tw = 0; tw < p.ntw[rw]; ++tw) {
-            const int kw = p.twk[rw][tw];
-            const int dw = p.twd[rw][tw];
-            const int64_t tapoff = (int64_t)(kh * a.Kw + kw) * IC;
-            for (int c64 = 0; c64 < NQ64; ++c64) {
-              const int q = c64 * 4 + lgrp;
-              const int icb = q * 16;
-              v4i bf[FO];
+        // The phase's (tap row, tap column, 64-channel slice) iterations in
+        // one flat sequence; the weight fragments of iteration it + kDepth
+        // are requested while iteration it computes (ring of kDepth + 1
+        // register buffers), so their global/L2 latency overlaps the MFMAs.
+        const int nth = p.nth[rh], ntw = p.ntw[rw];
+        const int nit = nth * ntw * NQ64;
+        const int hk0 = p.hk0[rh], hks = p.hks[rh], hd0 = p.hd0[rh] - p.dhmin, hds = p.hds[rh];
+        const int wk0 = p.wk0[rw], wks = p.wks[rw], wd0 = p.wd0[rw], wds = p.wds[rw];
+        constexpr int R = kDepth + 1;
+        v4i bb[R][FO];
+        int pth = 0, ptw = 0, pc = 0;   // prefetch cursor
+        // The loads are unconditional (an exec-masked load would make the
+        // compiler wait for every outstanding load before the next MFMA):
+        // rows past OC read row OC - 1 (their accumulators are never
+        // stored) and channel chunks past IC read the row's last chunk
+        // (their activations are zero in LDS; their weight sums are dropped
+        // in `compute`).  tapoff + icb + 16 <= Kh*Kw*IC <= ldw.
+        auto load_b = [&](v4i (&dst)[FO]) {
+          const int64_t tapoff = (int64_t)((hk0 + pth * hks) * (int)a.Kw + wk0 + ptw * wks) * IC;
+          const int icb = (pc * 4 + lgrp) * 16;
+          const int icc = icb < IC ? icb : IC - 16;
 #pragma unroll
-              for (int f = 0; f < FO; ++f) {
-                const int oc = ocw + f * 16 + lrow;
-                bf[f] = (oc < a.OC && icb < IC)
-                            ? *reinterpret_cast<const v4i*>(a.w + (int64_t)oc * a.ldw + tapoff + icb)
-                            : v4i{0, 0, 0, 0};
-              }
-              v4i af[FJ];
-#pragma unroll
-              for (int g = 0; g < FJ; ++g) {
-                const int c = j0 + g * 16 + lrow + dw - col0;
-                af[g] = *reinterpret_cast<const v4i*>(xs + ((int64_t)(lr * p.HC + c) * p.ICP) +
-                                                      16 * xswz(c, q, p.ICP));
-              }
-#pragma unroll
-              for (int f = 0; f < FO; ++f) {
-                wsum[f] = __builtin_amdgcn_sdot4(bf[f][0], 0x01010101, wsum[f], false);
-                wsum[f] = __builtin_amdgcn_sdot4(bf[f][1], 0x01010101, wsum[f], false);
-                wsum[f] = __builtin_amdgcn_sdot4(bf[f][2], 0x01010101, wsum[f], false);
-                wsum[f] = __builtin_amdgcn_sdot4(bf[f][3], 0x01010101, wsum[f], false);
-              }
-#pragma unroll
-              for (int g = 0; g < FJ; ++g)
-#pragma unroll
-                for (int f = 0; f < FO; ++f)
-                  acc[g][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[g], bf[f], acc[g][f], 0, 0, 0);
-            }
+          for (int f = 0; f < FO; ++f) {
+            const int oc = ocw + f * 16 + lrow;
+            const int occ = oc < a.OC ? oc : (int)a.OC - 1;
+            dst[f] = *reinterpret_cast<const v4i*>(a.w + (int64_t)occ * a.ldw + tapoff + icc);
           }
+          // advance, saturating at the phase's last iteration (prefetches
+          // past the end re-read it and are never consumed)
+          if (++pc == NQ64) {
+            pc = 0;
+            if (++ptw == ntw) { ptw = 0; ++pth; }
+          }
+          if (pth >= nth) { pth = nth - 1; ptw = ntw - 1; pc = NQ64 - 1; }
+        };
+        int cth = 0, ctw = 0, cc = 0;   // compute cursor
+        auto compute = [&](const v4i (&bf)[FO]) {
+          const int lr = wi + hd0 + cth * hds;
+          const int dw = wd0 + ctw * wds;
+          const int q = cc * 4 + lgrp;
+          v4i af[FJ];
+#pragma unroll
+          for (int g = 0; g < FJ; ++g) {
+            const int c = j0 + g * 16 + lrow + dw - col0;
+            af[g] = *reinterpret_cast<const v4i*>(xs + ((int64_t)(lr * p.HC + c) * p.ICP) +
+                                                  16 * xswz(c, q, p.ICP));
+          }
+          const bool in_ic = q * 16 < IC;
+#pragma unroll
+          for (int f = 0; f < FO; ++f) {
+            int32_t t = __builtin_amdgcn_sdot4(bf[f][0], 0x01010101, 0, false);
+            t = __builtin_amdgcn_sdot4(bf[f][1], 0x01010101, t, false);
+            t = __builtin_amdgcn_sdot4(bf[f][2], 0x01010101, t, false);
+            t = __builtin_amdgcn_sdot4(bf[f][3], 0x01010101, t, false);
+            wsum[f] += in_ic ? t : 0;
+          }
+#pragma unroll
+          for (int g = 0; g < FJ; ++g)
+#pragma unroll
+            for (int f = 0; f < FO; ++f)
+              acc[g][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[g], bf[f], acc[g][f], 0, 0, 0);
+          if (++cc == NQ64) {
+            cc = 0;
+            if (++ctw == ntw) { ctw = 0; ++cth; }
+          }
+        };
+        // Whole groups of R iterations run without guards, so the compiler
+        // sees every load of the ring and waits only for the oldest; the
+        // remaining nit % R iterations follow.
+        if (nit > 0) {
+          Static<0, kDepth>::each([&](auto U) { load_b(bb[decltype(U)::value]); });
+          const int nfull = nit - nit % R;
+          for (int base = 0; base < nfull; base += R) {
+            Static<0, R>::each([&](auto U) {
+              constexpr int u = decltype(U)::value;
+              load_b(bb[(u + kDepth) % R]);
+              compute(bb[u]);
+            });
+          }
+          Static<0, R - 1>::each([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            if (nfull + u < nit) {
+              load_b(bb[(u + kDepth) % R]);
+              compute(bb[u]);
+            }
+          });
         }
         // epilogue of phase (rh, rw): lane holds pixels j = j0+16g+4*lgrp+e of
         // output channel ocw + 16f + lrow.
@@ -340,6 +426,27 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
     }
     p.ntw[r] = cnt;
   }
+  // progressions (checked against the scanned tables)
+  for (int r = 0; r < sh; ++r) {
+    const int n = p.nth[r];
+    p.hk0[r] = n ? p.thk[r][0] : 0;
+    p.hd0[r] = n ? p.thd[r][0] : 0;
+    p.hks[r] = n > 1 ? p.thk[r][1] - p.thk[r][0] : 0;
+    p.hds[r] = n > 1 ? p.thd[r][1] - p.thd[r][0] : 0;
+    for (int t = 0; t < n; ++t)
+      if (p.thk[r][t] != p.hk0[r] + t * p.hks[r] || p.thd[r][t] != p.hd0[r] + t * p.hds[r])
+        return false;
+  }
+  for (int r = 0; r < sw; ++r) {
+    const int n = p.ntw[r];
+    p.wk0[r] = n ? p.twk[r][0] : 0;
+    p.wd0[r] = n ? p.twd[r][0] : 0;
+    p.wks[r] = n > 1 ? p.twk[r][1] - p.twk[r][0] : 0;
+    p.wds[r] = n > 1 ? p.twd[r][1] - p.twd[r][0] : 0;
+    for (int t = 0; t < n; ++t)
+      if (p.twk[r][t] != p.wk0[r] + t * p.wks[r] || p.twd[r][t] != p.wd0[r] + t * p.wds[r])
+        return false;
+  }
   if (dhmin > dhmax) { dhmin = dhmax = 0; }   // no row taps at all
   if (dwmin > dwmax) { dwmin = dwmax = 0; }
   p.dhmin = dhmin;
@@ -347,16 +454,22 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
   p.Hp = (int)((a.H_out + sh - 1) / sh);
   p.Wp = (int)((a.W_out + sw - 1) / sw);
 
+  // Two 16-channel fragments per wave and up to four phase rows per
+  // workgroup: 8 waves (two per SIMD) where the LDS tiles allow, which
+  // measured faster than four fragments per wave with one wave per SIMD
+  // ([8,256,64,64] K3 s2: 45.6 -> 36.7 us; forward K3 s1: 30.5 -> 29.2 us).
   FJ = p.Wp >= 64 ? 4 : p.Wp >= 32 ? 2 : 1;
-  FO = a.OC >= 64 ? 4 : a.OC >= 32 ? 2 : 1;
+  FO = a.OC >= 32 ? 2 : 1;
+  bool small = false;
   {
     // Small problems are latency-bound: when the default tile leaves the chip
     // mostly idle (fewer than 256 workgroups), take one 16-channel fragment
     // per wave (measured on [1,64,32,32] K4 s2: 18.3 -> 12.7 us).
     const int64_t ocb = 2 * 16 * FO;
-    const int64_t est = a.N * ((p.Hp + 1) / 2) * ((p.Wp + 16 * FJ - 1) / (16 * FJ)) *
+    const int64_t est = a.N * ((p.Hp + 3) / 4) * ((p.Wp + 16 * FJ - 1) / (16 * FJ)) *
                         ((a.OC + ocb - 1) / ocb);
-    if (est < 256) FO = 1;
+    small = est < 256;
+    if (small) FO = 1;
   }
   if (const char* e = getenv("Q8TA_DECONV_FJ")) FJ = atoi(e);
   if (const char* e = getenv("Q8TA_DECONV_FO")) FO = atoi(e);
@@ -372,7 +485,7 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
   const int c_hi = p.TJ - 1 + dwmax + 1;
   p.HC = ((c_hi - c_lo) + 3) / 4 * 4;
   p.OCols = sw * p.TJ;
-  int wi_pref = 2;
+  int wi_pref = small ? 2 : 4;   // small problems: more, smaller workgroups
   if (const char* e = getenv("Q8TA_DECONV_WI")) wi_pref = atoi(e);
   if (wi_pref < 1) wi_pref = 1;
   if (wi_pref * p.WO > 8) wi_pref = 8 / p.WO;
