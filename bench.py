@@ -301,11 +301,12 @@ def main():
     else:
         roofline = {
             "bound": "mfma",
-            "kernel": "k_gemm<256x128x128 tile, 4x2 waves> (v_mfma_i32_16x16x64_i8)",
+            "kernel": "k_gemm_mx<256x128x64 tile, 2x2 waves of 128x64, 2 workgroups/CU, loads 2 "
+                      "K steps ahead> (v_mfma_i32_32x32x32_i8)",
             "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
-            "traffic": traffic_from_profile("gemm", os.path.join(
-                ROOT, "int8_quantized_amd", "csrc", "gemm.hip")),
+            "traffic": traffic_from_profile("gemm_mx", os.path.join(
+                ROOT, "int8_quantized_amd", "csrc", "gemm_mx.hip")),
         }
     roofline.update({"per_launch_ops": ops, "avg_launch_us": round(gemm_avg_s * 1e6, 2)})
 

@@ -312,25 +312,28 @@ bool gemm_mfma_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-// Tile choice (measured on 2048 x 4096 x 11008): 256 x 128 tiles with
-// 128-byte K steps and 8 waves when they fill the GPU at least once and K is
-// long, otherwise the medium tile, or the small one for few rows.  The large
-// tile of this file (128 x 128 per wave, loops the compiler leaves rolled)
-// keeps its accumulators in scratch memory; the direct-to-LDS 32x32x32 kernel
-// of gemm_dl.hip ('G') measured slower on that shape, as did the 32x32x32
-// variant of the 256 x 128 tile in gemm32.hip ('X').  Q8TA_GEMM_CFG (one
-// letter of LMSKWVUQRGX) overrides the choice.
+// Tile choice (measured on 2048 x 4096 x 11008, fused dequantize): for
+// problems that fill the GPU at least once with 256 x 128 tiles and have a
+// long K, the 32x32x32 kernel of gemm_mx.hip with two workgroups per CU and
+// loads two K steps ahead ('y': 129 us against 132 us for this file's
+// 256 x 128 tile 'V'); otherwise the medium tile, or the small one for few
+// rows.  The large tile of this file (128 x 128 per wave, loops the compiler
+// leaves rolled) keeps its accumulators in scratch memory; the
+// direct-to-LDS 32x32x32 kernel of gemm_dl.hip ('G') measured 156-182 us,
+// the 32x32x32 variant of the 256 x 128 tile in gemm32.hip ('X') 146 us.
+// Q8TA_GEMM_CFG (one letter of LMSKWVUQRGXYZPyz) overrides the choice.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
-  if (e && strchr("LMSKWVUQRGX", e[0])) pick = e[0];
+  if (e && strchr("LMSKWVUQRGXYZPyz", e[0])) pick = e[0];
   if (!pick) {
     const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    pick = (tv >= 256 && a.K >= 1024) ? 'V' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
+    pick = (tv >= 256 && a.K >= 1024) ? 'y' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
   }
   if (pick == 'G') return gemm_dl_supported(a) ? launch_gemm_dl(a, s) : launch_cfg<CfgM>(a, s);
   if (pick == 'X') return launch_gemm32(a, s);
+  if (pick == 'Y' || pick == 'Z' || pick == 'P' || pick == 'y' || pick == 'z') return launch_gemm_mx(a, pick, s);
   switch (pick) {
     case 'L': return launch_cfg<CfgL>(a, s);
     case 'M': return launch_cfg<CfgM>(a, s);

@@ -226,6 +226,7 @@ hipError_t launch_gemm_dl(const LinearArgs& a, hipStream_t s);
 bool gemm_dl_supported(const LinearArgs& a);
 // 32x32x32 matrix-core GEMM (same operand requirements as launch_gemm_mfma).
 hipError_t launch_gemm32(const LinearArgs& a, hipStream_t s);
+hipError_t launch_gemm_mx(const LinearArgs& a, char cfg, hipStream_t s);
 // out[n] = sum_k w[n, k] for an [N, K] int8 matrix (K % 16 == 0, w 16-byte aligned).
 hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t s);
 // Same for any K and alignment, rows ldw bytes apart (one thread per row).

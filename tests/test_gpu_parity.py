@@ -184,7 +184,7 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
 
 
-@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X"])
+@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X", "Y", "Z", "P", "y", "z"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
 def test_linear_every_gemm_tile(cfg, M, K, N):
     _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
@@ -839,7 +839,7 @@ def test_weight_sums(N, K, offset):
     np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
 
 
-@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "mfma:X", "dot4", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "mfma:X", "mfma:Y", "mfma:Z", "mfma:P", "mfma:y", "mfma:z", "dot4", "generic"])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
                                    (7, 33, 5)])
 def test_linear_presummed_equals_linear(path, M, K, N):
