@@ -23,8 +23,8 @@
 //    slab is fetched into registers (16 B per load, rows past M/N/K
 //    zero-filled) while the matrix cores work on the current buffer, then
 //    written to the other buffer; one barrier per step.  The 16-byte chunk c
-//    of LDS row r sits at chunk position c ^ f(r), f chosen so that the lanes
-//    one ds_read_b128 phase serves hit distinct banks.
+//    of LDS row r sits at chunk position c ^ f(r), f chosen so that the 16
+//    lanes one ds_read_b128 cycle serves hit distinct banks.
 //  * W is the A operand and X the B operand: lane l supplies row l % 32 of
 //    each operand with K bytes 16 * (l / 32) .. +15 of each 32-byte slice;
 //    accumulator register r of lane l holds row 8 * (r / 4) + 4 * (l / 32) +
@@ -83,20 +83,22 @@ struct MxCfg {
   static_assert(KS % WAVES_M == 0 || WAVES_M == 1, "row-sum split");
 };
 
-// Chunk position of chunk c in LDS row r: c ^ f(r), each bit of f the parity
-// of a subset of row bits 0..4, so rows 32 apart (the fragments of one wave)
-// share the pattern.  A ds_read_b128 is served in groups of 8 lanes that are
-// not 8 consecutive lanes (lanes 0-3 go with 20-23, 4-7 with 16-19, 8-11 with
-// 28-31, 12-15 with 24-27, likewise in the upper half); with the 32x32x32
-// operand pattern (lane l reads row l % 32) the row-parity masks below give
-// every such group distinct banks for both 32-bank and 64-bank readings, and
-// also for groups of 8 or 16 consecutive lanes, and they keep the loader's
-// ds_write_b128 (4 or 8 lanes per row) conflict-free.
-__device__ __forceinline__ int par(int v) { return __builtin_popcount(v) & 1; }
+// Chunk position of chunk c in LDS row r: c ^ f(r), f from row bits 1..4
+// only, so rows 32 apart (the fragments of one wave) share the pattern.
+// Measured on gfx950 with an LDS probe (SQ_LDS_BANK_CONFLICT over 29 lane
+// patterns): a ds_read_b128 serves 16 lanes per cycle over 64 banks, and the
+// 16 lanes of a cycle are the lane quads (lanes 4q .. 4q+3) of one half-wave
+// whose quad index q has even parity, or those with odd parity.  For the
+// 32x32x32 pattern (lane l reads row l % 32 at one chunk per half-wave) the
+// 16 rows of a cycle are then 4 rows in each residue class r % 4 (64-byte
+// rows) or r % 2 (128-byte rows); f = (r >> 2) & 3, resp. (r >> 1) & 7,
+// sends them to distinct chunk positions.  The earlier swizzles measured 4
+// conflict cycles per read.  The loader's ds_write_b128 (CPR lanes per row)
+// measured conflict-free with any of them.
 template <int CPR>
 __device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (CPR == 4) return c ^ (par(r & 30) | (par(r & 26) << 1));
-  else return c ^ (par(r & 31) | (par(r & 29) << 1) | (par(r & 25) << 2));
+  if constexpr (CPR == 4) return c ^ ((r >> 2) & 3);
+  else return c ^ ((r >> 1) & 7);
 }
 
 // The requantized code as a float in [qmin, 127] (the steps of requant()).
