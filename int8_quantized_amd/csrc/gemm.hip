@@ -325,7 +325,7 @@ bool gemm_mfma_supported(const LinearArgs& a) {
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
-  if (e && strchr("LMSKWVUQRGXYZPyz", e[0])) pick = e[0];
+  if (e && strchr("LMSKWVUQRGXYZPyzw", e[0])) pick = e[0];
   if (!pick) {
     const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
@@ -333,7 +333,7 @@ hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   }
   if (pick == 'G') return gemm_dl_supported(a) ? launch_gemm_dl(a, s) : launch_cfg<CfgM>(a, s);
   if (pick == 'X') return launch_gemm32(a, s);
-  if (pick == 'Y' || pick == 'Z' || pick == 'P' || pick == 'y' || pick == 'z') return launch_gemm_mx(a, pick, s);
+  if (strchr("YZPyzw", pick)) return launch_gemm_mx(a, pick, s);
   switch (pick) {
     case 'L': return launch_cfg<CfgL>(a, s);
     case 'M': return launch_cfg<CfgM>(a, s);

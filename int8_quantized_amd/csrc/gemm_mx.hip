@@ -62,7 +62,10 @@ struct Static {
 
 template <int BN_, int BM_, int BK_, int WAVES_N_, int WAVES_M_, int BLOCKS_PER_CU_, int PD_ = 1>
 struct MxCfg {
-  static constexpr int PD = PD_;                 // prefetch distance in K steps
+  // 1: one register set, loads one step ahead; 2: two sets, loads two steps
+  // ahead; 3: two sets, the LDS write of step k + 1 moved to the top of
+  // step k (see the K loop)
+  static constexpr int PD = PD_;
   static constexpr int BN = BN_, BM = BM_, BK = BK_;
   static constexpr int WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
   static constexpr int BLOCKS_PER_CU = BLOCKS_PER_CU_;
@@ -75,7 +78,7 @@ struct MxCfg {
   static constexpr int B_LD = BM * CPR / NT;     // X chunks per thread per step
   static constexpr int STAGE = (BN + BM) * BK;   // bytes per LDS buffer
   static_assert(BK == 64 || BK == 128, "BK");
-  static_assert(PD == 1 || PD == 2, "prefetch distance");
+  static_assert(PD >= 1 && PD <= 3, "prefetch mode");
   static_assert(WN % 32 == 0 && WM % 32 == 0, "wave tile");
   static_assert((BN * CPR) % NT == 0 && (BM * CPR) % NT == 0, "loader");
   static_assert(NT % CPR == 0, "a thread keeps its chunk column");
@@ -176,7 +179,8 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   // PD register sets of staged chunks: with PD = 2 the loads of step kt + 2
   // are issued while step kt is computed and step kt + 1 waits in the other
   // set, so each load has two steps to arrive.
-  v4i ra[C::PD][C::A_LD], rb[C::PD][C::B_LD];
+  constexpr int SETS = C::PD == 1 ? 1 : 2;
+  v4i ra[SETS][C::A_LD], rb[SETS][C::B_LD];
   auto load_global = [&](int kt, auto SET) {
     constexpr int st = decltype(SET)::value;
     int64_t ko = (int64_t)kt * C::BK;
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
       store_lds(cur ^ 1, S0);
       __syncthreads();
     }
-  } else {
+  } else if constexpr (C::PD == 2) {
     constexpr std::integral_constant<int, 1> S1{};
     load_global(min(1, KT - 1), S1);
     __syncthreads();
@@ -302,6 +306,29 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
       load_global(min(kt + 3, KT - 1), S1);
       compute(1);
       store_lds(0, S0);
+      __syncthreads();
+    }
+    if (kt < KT) compute(0);   // odd KT: the last step sits in buffer 0
+  } else {
+    // Store first: at the top of step kt the set holding step kt + 1 (loaded
+    // two steps earlier) is written to buffer (kt + 1) % 2 -- read last in
+    // step kt - 1, before the barrier that ended it -- and immediately
+    // refilled with step kt + 3; then step kt is computed from buffer
+    // kt % 2.  The LDS writes overlap the step's matrix-core work instead of
+    // delaying the barrier, and each load still has two steps to arrive.
+    constexpr std::integral_constant<int, 1> S1{};
+    load_global(min(1, KT - 1), S1);
+    load_global(min(2, KT - 1), S0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      store_lds(1, S1);
+      load_global(min(kt + 3, KT - 1), S1);
+      compute(0);
+      __syncthreads();
+      store_lds(0, S0);
+      load_global(min(kt + 4, KT - 1), S0);
+      compute(1);
       __syncthreads();
     }
     if (kt < KT) compute(0);   // odd KT: the last step sits in buffer 0
@@ -402,6 +429,8 @@ using MxP = MxCfg<128, 256, 64, 2, 2, 2>;
 // Loads issued two K steps ahead.
 using MxY2 = MxCfg<256, 128, 64, 2, 2, 2, 2>;
 using MxZ2 = MxCfg<256, 128, 128, 2, 2, 1, 2>;
+// Store-first K loop.
+using MxY3 = MxCfg<256, 128, 64, 2, 2, 2, 3>;
 
 template <class C, bool PRE>
 hipError_t launch_mx2(const LinearArgs& a, int tiles_m, int tiles_n, hipStream_t s) {
@@ -429,6 +458,7 @@ hipError_t launch_gemm_mx(const LinearArgs& a, char cfg, hipStream_t s) {
   if (cfg == 'Z') return launch_mx<MxZ>(a, s);
   if (cfg == 'y') return launch_mx<MxY2>(a, s);
   if (cfg == 'z') return launch_mx<MxZ2>(a, s);
+  if (cfg == 'w') return launch_mx<MxY3>(a, s);
   if (cfg == 'P') return launch_mx<MxP>(a, s);
   return launch_mx<MxY>(a, s);
 }

@@ -184,7 +184,7 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
 
 
-@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X", "Y", "Z", "P", "y", "z"])
+@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X", "Y", "Z", "P", "y", "z", "w"])
 @pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
 def test_linear_every_gemm_tile(cfg, M, K, N):
     _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
@@ -224,10 +224,15 @@ def test_linear_every_dot4_variant(cfg, M, K, N):
 
 
 @pytest.mark.parametrize("rows", [1, 2, 4])
-def test_gemv_rows_per_wave(rows):
-    c = qi.linear_case(77 + rows, 1, 2048, 1001)
+@pytest.mark.parametrize("M,K", [(1, 2048), (3, 4096), (1, 5136), (4, 48)])
+def test_gemv_rows_per_wave(rows, M, K):
+    """Every skinny-GEMM layout (ROWS weight rows per wave); K spans partial
+    1 KiB slices and several passes."""
+    _say(f"gemv rows={rows} M={M} K={K}")
+    c = qi.linear_case(77 + rows + M + K, M, K, 1001)
     with env(Q8TA_GEMV_ROWS=rows):
         np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
 
 
 def test_linear_gemv_entry_and_gemm_row_identity():
@@ -839,7 +844,7 @@ def test_weight_sums(N, K, offset):
     np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
 
 
-@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "mfma:X", "mfma:Y", "mfma:Z", "mfma:P", "mfma:y", "mfma:z", "dot4", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "mfma:X", "mfma:Y", "mfma:Z", "mfma:P", "mfma:y", "mfma:z", "mfma:w", "dot4", "generic"])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
                                    (7, 33, 5)])
 def test_linear_presummed_equals_linear(path, M, K, N):
