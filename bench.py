@@ -345,17 +345,40 @@ def main():
             check(lib.q8ta_linear_dq_presummed(x.data_ptr(), M, K, c.in_scale, c.in_zp, w.data_ptr(),
                                                N, sums.data_ptr(), ws.data_ptr(), b.data_ptr(),
                                                c.out_scale, c.out_zp, none, y.data_ptr(), stream))
+        packed = torch.empty(lib.q8ta_weight_prepacked_bytes(N, K), dtype=torch.int8, device="cuda")
+        check(lib.q8ta_weight_prepack(w.data_ptr(), N, K, packed.data_ptr(), stream))
+        yp = torch.empty_like(y)
+
+        def gemm_dq_prepacked():
+            check(lib.q8ta_linear_dq_prepacked(x.data_ptr(), M, K, c.in_scale, c.in_zp,
+                                               packed.data_ptr(), N, sums.data_ptr(), ws.data_ptr(),
+                                               b.data_ptr(), c.out_scale, c.out_zp, none,
+                                               yp.data_ptr(), stream))
+        gemm_dq_prepacked()
+        gemm_dq()
+        torch.cuda.synchronize()
+        extra["prepacked_output_equal"] = bool(torch.equal(yp.view(torch.int32),
+                                                           y.view(torch.int32)))
         # the CPU leg leaves the GPU idle and its clock low: warm it again
         timer.time_calls([gemm_dq], args.warmup, budget_s=0.2, batches=1)
         for name, fn in (("gemm_step_chain_us", chain), ("gemm_step_fused_us", gemm_dq),
-                         ("gemm_step_fused_presummed_us", gemm_dq_presummed)):
+                         ("gemm_step_fused_presummed_us", gemm_dq_presummed),
+                         ("gemm_step_fused_prepacked_us", gemm_dq_prepacked)):
             extra[name] = round(min(timer.time_calls([fn], 50, batches=3)) * 1e3, 1)
+        extra["gemm_prepacked_tops"] = round(2.0 * M * N * K / extra["gemm_step_fused_prepacked_us"]
+                                             / 1e6, 1)
+        extra["weight_prepack_us"] = round(min(timer.time_calls(
+            [lambda: check(lib.q8ta_weight_prepack(w.data_ptr(), N, K, packed.data_ptr(), stream))],
+            20, batches=3)) * 1e3, 1)
+        del yp
         extra["weight_sums_us"] = round(min(timer.time_calls(
             [lambda: check(lib.q8ta_weight_sums(w.data_ptr(), N, K, sums.data_ptr(), stream))], 20,
             batches=3)) * 1e3, 1)
         log(f"  step forms: chain {extra['gemm_step_chain_us']} us, "
             f"fused {extra['gemm_step_fused_us']} us, fused with precomputed weight sums "
-            f"{extra['gemm_step_fused_presummed_us']} us (+ {extra['weight_sums_us']} us once per weight)")
+            f"{extra['gemm_step_fused_presummed_us']} us (+ {extra['weight_sums_us']} us once per weight), "
+            f"prepacked weight {extra['gemm_step_fused_prepacked_us']} us (+ {extra['weight_prepack_us']} us "
+            f"once per weight; output equal: {extra['prepacked_output_equal']})")
         extra.update(run_extra(torch, np, q8, qi, lib, stream, timer, check))
         extra["ceilings"] = run_ceilings(torch, stream, timer)
         log(f"  ceilings: {extra['ceilings']}")

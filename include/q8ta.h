@@ -185,6 +185,55 @@ q8ta_status q8ta_linear_dq_presummed(const int8_t* x, int64_t M, int64_t K,
                                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Prepacked weights (opt-in; the prepacked-layout half of the weight
+ * preparation the Vulkan op behind [LIN] does ahead of time, Constraints
+ * (1)/(2)).  A weight reused across calls is rearranged once into the operand
+ * order of the int8 matrix-core instruction, so the GEMM streams it without
+ * staging:
+ *   packed layout: fragments of 32 rows x 32 K bytes; byte 16*l + j of
+ *     fragment (nb, s) is weight[32*nb + l % 32][32*s + 16*(l / 32) + j]
+ *     (l = 0..63, j = 0..15), zero past N or K; fragment (nb, s) starts at
+ *     byte (nb * KS + s) * 1024 with KS = 2 * ceil(K / 64).
+ *   q8ta_weight_prepacked_bytes: size of that buffer,
+ *     ceil(N/32)*32 * ceil(K/64)*64 bytes; -1 for N < 1, K < 1 or sizes past
+ *     2^31 elements.  Host-only, no HIP call.
+ *   q8ta_weight_prepack: weight int8 [N, K] row-major -> packed (device,
+ *     caller-allocated, q8ta_weight_prepacked_bytes(N, K) bytes).  Needs
+ *     K % 16 == 0 and 16-byte aligned weight and packed
+ *     (else Q8TA_ERR_UNSUPPORTED).
+ *   q8ta_linear_prepacked / q8ta_linear_dq_prepacked: q8ta_linear_presummed /
+ *     q8ta_linear_dq_presummed with packed_weight in place of weight (N is the
+ *     weight's row count, K its row length).  weight_sums is REQUIRED and
+ *     TRUSTED (sum over the unpacked rows, as q8ta_weight_sums returns).
+ *     Needs K % 16 == 0 and 16-byte aligned x and packed_weight
+ *     (else Q8TA_ERR_UNSUPPORTED).  With the weight's own sums the results are
+ *     bit-identical to q8ta_linear / q8ta_linear_dq.  Other arguments and
+ *     errors as for q8ta_linear / q8ta_linear_dq.
+ */
+int64_t q8ta_weight_prepacked_bytes(int64_t N, int64_t K);
+
+q8ta_status q8ta_weight_prepack(const int8_t* weight, int64_t N, int64_t K, int8_t* packed,
+                                hipStream_t stream);
+
+q8ta_status q8ta_linear_prepacked(const int8_t* x, int64_t M, int64_t K,
+                                  double input_scale, int64_t input_zero_point,
+                                  const int8_t* packed_weight, int64_t N,
+                                  const int32_t* weight_sums,
+                                  const float* weight_scales, const float* bias,
+                                  double output_scale, int64_t output_zero_point,
+                                  const char* activation, int8_t* out,
+                                  hipStream_t stream);
+
+q8ta_status q8ta_linear_dq_prepacked(const int8_t* x, int64_t M, int64_t K,
+                                     double input_scale, int64_t input_zero_point,
+                                     const int8_t* packed_weight, int64_t N,
+                                     const int32_t* weight_sums,
+                                     const float* weight_scales, const float* bias,
+                                     double output_scale, int64_t output_zero_point,
+                                     const char* activation, float* out,
+                                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * q8ta_conv2d_transposed ([DCV] Solution, Implementation, Constraints):
  *   acc[n,oc,oh,ow] = sum over (ic, kh, kw) of
  *       (x[n,ic,ih,iw] - input_zero_point) * weight[oc, (kh*Kw + kw)*IC + ic]

@@ -59,6 +59,12 @@ SIGNATURES = {
                                _P, _P], ctypes.c_int),
     "q8ta_linear_dq_presummed": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64,
                                   _S, _P, _P], ctypes.c_int),
+    "q8ta_weight_prepacked_bytes": ([_I64, _I64], ctypes.c_int64),
+    "q8ta_weight_prepack": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
+    "q8ta_linear_prepacked": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
+                               _P, _P], ctypes.c_int),
+    "q8ta_linear_dq_prepacked": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64,
+                                  _S, _P, _P], ctypes.c_int),
     "q8ta_quantize_conv2d_transposed": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64,
                                          _I64, _I64, _P, _P, _P, _DBL, _I64, _I64, _I64, _I64,
                                          _I64, _I64, _I64, _I64, _I64, _I64, _S, _P, _I64, _I64,
@@ -229,6 +235,61 @@ def q8ta_linear_dq_presummed(x, input_scale, input_zero_point, weight, weight_su
     return out
 
 
+def q8ta_weight_prepacked_bytes(N: int, K: int) -> int:
+    """Size in bytes of the prepacked layout of an int8 [N, K] weight (-1 if invalid)."""
+    return int(lib().q8ta_weight_prepacked_bytes(int(N), int(K)))
+
+
+def q8ta_weight_prepack(weight, packed, stream=None):
+    """Rearrange int8 weight [N, K] into the matrix-core fragment layout
+    (packed: int8 device tensor of q8ta_weight_prepacked_bytes(N, K) bytes)."""
+    torch = _torch()
+    if weight.dim() != 2:
+        raise ValueError("weight [N, K] expected")
+    N, K = weight.shape
+    if packed.numel() != q8ta_weight_prepacked_bytes(N, K):
+        raise ValueError(f"packed must hold {q8ta_weight_prepacked_bytes(N, K)} bytes")
+    _check(lib().q8ta_weight_prepack(_dev(weight, torch.int8, "weight"), N, K,
+                                     _dev(packed, torch.int8, "packed"), _stream(stream)))
+    return packed
+
+
+def _linear_pk(fn, out_dtype, x, input_scale, input_zero_point, packed, N, weight_sums,
+               weight_scales, bias, output_scale, output_zero_point, activation, out, stream):
+    torch = _torch()
+    if weight_sums is None:
+        raise ValueError("weight_sums is required")
+    if x.dim() != 2 or tuple(out.shape) != (x.shape[0], N):
+        raise ValueError("x [M, K] and out [M, N] expected")
+    M, K = x.shape
+    if packed.numel() != q8ta_weight_prepacked_bytes(N, K):
+        raise ValueError("packed does not hold an [N, K] prepacked weight")
+    _check(fn(_dev(x, torch.int8, "x"), M, K, float(input_scale), int(input_zero_point),
+              _dev(packed, torch.int8, "packed"), int(N),
+              _dev(weight_sums, torch.int32, "weight_sums"),
+              _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+              float(output_scale), int(output_zero_point), _act(activation),
+              _dev(out, out_dtype, "out"), _stream(stream)))
+    return out
+
+
+def q8ta_linear_prepacked(x, input_scale, input_zero_point, packed, N, weight_sums, weight_scales,
+                          bias, output_scale, output_zero_point, activation, out, stream=None):
+    """q8ta_linear_presummed on a prepacked weight of N rows: int8 out [M, N]."""
+    return _linear_pk(lib().q8ta_linear_prepacked, _torch().int8, x, input_scale,
+                      input_zero_point, packed, N, weight_sums, weight_scales, bias, output_scale,
+                      output_zero_point, activation, out, stream)
+
+
+def q8ta_linear_dq_prepacked(x, input_scale, input_zero_point, packed, N, weight_sums,
+                             weight_scales, bias, output_scale, output_zero_point, activation, out,
+                             stream=None):
+    """q8ta_linear_dq_presummed on a prepacked weight of N rows: fp32 out [M, N]."""
+    return _linear_pk(lib().q8ta_linear_dq_prepacked, _torch().float32, x, input_scale,
+                      input_zero_point, packed, N, weight_sums, weight_scales, bias, output_scale,
+                      output_zero_point, activation, out, stream)
+
+
 def q8ta_linear_acc(x, input_zero_point, weight, acc, stream=None):
     """int32 accumulator of q8ta_linear: acc[m,n] = sum_k (x[m,k]-izp)*w[n,k]."""
     torch = _torch()
@@ -371,6 +432,8 @@ __all__ = [
     "Q8taError", "lib", "q8ta_last_error", "q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor",
     "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_dq", "q8ta_linear_acc", "q8ta_conv2d_transposed",
     "q8ta_weight_sums", "q8ta_linear_presummed", "q8ta_linear_dq_presummed",
+    "q8ta_weight_prepacked_bytes", "q8ta_weight_prepack", "q8ta_linear_prepacked",
+    "q8ta_linear_dq_prepacked",
     "q8ta_conv2d_transposed_acc", "q8ta_quantize_conv2d_transposed", "q8ta_conv2d",
     "q8ta_conv2d_acc",
 ]

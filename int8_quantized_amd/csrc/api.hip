@@ -102,9 +102,13 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
                         const float* weight_scales, const float* bias, double output_scale,
                         int64_t output_zero_point, const char* activation, int8_t* out,
                         hipStream_t stream, float* outf = nullptr,
-                        const int32_t* wsum_pre = nullptr) {
+                        const int32_t* wsum_pre = nullptr, bool packed = false) {
   q8ta_status st = linear_checks(op, x, M, K, weight, N, outf ? (const void*)outf : out);
   if (st) return st;
+  if (packed && (K % 16 != 0 || ((uintptr_t)x & 15) != 0 || ((uintptr_t)weight & 15) != 0))
+    return fail(Q8TA_ERR_UNSUPPORTED,
+                "%s: needs K %% 16 == 0 and 16-byte aligned x and packed weight (K = %lld)", op,
+                (long long)K);
   if (gemv_only && M != 1) return fail(Q8TA_ERR_SHAPE, "%s: M must be 1 (got %lld)", op, (long long)M);
   if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
   if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
@@ -120,6 +124,10 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   a.dq_scale = (float)output_scale;
   a.dq_zp = (int32_t)output_zero_point;
   a.wsum_pre = wsum_pre;
+  if (packed) {
+    a.wpk = weight;
+    return hip_status(launch_gemm_pk(a, stream), op);
+  }
   return hip_status(launch_linear(a, stream), op);
 }
 
@@ -389,6 +397,51 @@ q8ta_status q8ta_linear_dq_presummed(const int8_t* x, int64_t M, int64_t K, doub
   return linear_impl(op, false, x, M, K, input_scale, input_zero_point, weight, N, weight_scales,
                      bias, output_scale, output_zero_point, activation, nullptr, stream, out,
                      weight_sums);
+}
+
+int64_t q8ta_weight_prepacked_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N > kMaxElems / K || K >= ((int64_t)1 << 31)) return -1;
+  return prepacked_bytes(N, K);
+}
+
+q8ta_status q8ta_weight_prepack(const int8_t* weight, int64_t N, int64_t K, int8_t* packed,
+                                hipStream_t stream) {
+  const char* op = "q8ta_weight_prepack";
+  if (!weight || !packed) return fail(Q8TA_ERR_NULL, "%s: weight and packed must not be NULL", op);
+  if (q8ta_weight_prepacked_bytes(N, K) < 0)
+    return fail(Q8TA_ERR_SHAPE, "%s: N and K must be >= 1 (got %lld, %lld)", op, (long long)N,
+                (long long)K);
+  if (K % 16 != 0 || ((uintptr_t)weight & 15) != 0 || ((uintptr_t)packed & 15) != 0)
+    return fail(Q8TA_ERR_UNSUPPORTED,
+                "%s: needs K %% 16 == 0 and 16-byte aligned weight and packed (K = %lld)", op,
+                (long long)K);
+  return hip_status(launch_prepack(weight, N, K, packed, stream), op);
+}
+
+q8ta_status q8ta_linear_prepacked(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                                  int64_t input_zero_point, const int8_t* packed_weight, int64_t N,
+                                  const int32_t* weight_sums, const float* weight_scales,
+                                  const float* bias, double output_scale,
+                                  int64_t output_zero_point, const char* activation, int8_t* out,
+                                  hipStream_t stream) {
+  const char* op = "q8ta_linear_prepacked";
+  if (!weight_sums) return fail(Q8TA_ERR_NULL, "%s: weight_sums must not be NULL", op);
+  return linear_impl(op, false, x, M, K, input_scale, input_zero_point, packed_weight, N,
+                     weight_scales, bias, output_scale, output_zero_point, activation, out, stream,
+                     nullptr, weight_sums, true);
+}
+
+q8ta_status q8ta_linear_dq_prepacked(const int8_t* x, int64_t M, int64_t K, double input_scale,
+                                     int64_t input_zero_point, const int8_t* packed_weight,
+                                     int64_t N, const int32_t* weight_sums,
+                                     const float* weight_scales, const float* bias,
+                                     double output_scale, int64_t output_zero_point,
+                                     const char* activation, float* out, hipStream_t stream) {
+  const char* op = "q8ta_linear_dq_prepacked";
+  if (!weight_sums) return fail(Q8TA_ERR_NULL, "%s: weight_sums must not be NULL", op);
+  return linear_impl(op, false, x, M, K, input_scale, input_zero_point, packed_weight, N,
+                     weight_scales, bias, output_scale, output_zero_point, activation, nullptr,
+                     stream, out, weight_sums, true);
 }
 
 q8ta_status q8ta_linear_acc(const int8_t* x, int64_t M, int64_t K, int64_t input_zero_point,

@@ -169,6 +169,9 @@ struct LinearArgs {
   // precomputed weight_sums of the presummed entry points); NULL: the kernels
   // form them.
   const int32_t* wsum_pre = nullptr;
+  // Prepacked weight (the MFMA-fragment layout of q8ta_weight_prepack); set
+  // only by the prepacked entry points, which also supply wsum_pre.
+  const int8_t* wpk = nullptr;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
@@ -227,6 +230,9 @@ bool gemm_dl_supported(const LinearArgs& a);
 // 32x32x32 matrix-core GEMM (same operand requirements as launch_gemm_mfma).
 hipError_t launch_gemm32(const LinearArgs& a, hipStream_t s);
 hipError_t launch_gemm_mx(const LinearArgs& a, char cfg, hipStream_t s);
+int64_t prepacked_bytes(int64_t N, int64_t K);
+hipError_t launch_prepack(const int8_t* w, int64_t N, int64_t K, int8_t* packed, hipStream_t s);
+hipError_t launch_gemm_pk(const LinearArgs& a, hipStream_t s);
 // out[n] = sum_k w[n, k] for an [N, K] int8 matrix (K % 16 == 0, w 16-byte aligned).
 hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t s);
 // Same for any K and alignment, rows ldw bytes apart (one thread per row).

@@ -266,6 +266,42 @@ def test_presummed_entry_points_errors():
             q8.Q8TA_ERR_QPARAM)
 
 
+def test_prepacked_size_formula():
+    """ceil(N/32)*32 rows of ceil(K/64)*64 bytes; -1 for invalid sizes."""
+    l = q8.lib()
+    for N, K in [(1, 1), (32, 64), (33, 64), (11008, 4096), (100, 1040), (7, 48)]:
+        assert l.q8ta_weight_prepacked_bytes(N, K) == -(-N // 32) * 32 * (-(-K // 64) * 64)
+    assert l.q8ta_weight_prepacked_bytes(0, 64) == -1
+    assert l.q8ta_weight_prepacked_bytes(32, 0) == -1
+    assert l.q8ta_weight_prepacked_bytes(32, 1 << 31) == -1
+
+
+def test_prepacked_entry_points_errors():
+    l = q8.lib()
+    odd = ctypes.c_void_p(4096 + 8)   # not 16-byte aligned
+    _st(l.q8ta_weight_prepack(None, 32, 64, FAKE, None), q8.Q8TA_ERR_NULL)
+    _st(l.q8ta_weight_prepack(FAKE, 32, 64, None, None), q8.Q8TA_ERR_NULL)
+    _st(l.q8ta_weight_prepack(FAKE, 0, 64, FAKE, None), q8.Q8TA_ERR_SHAPE)
+    _st(l.q8ta_weight_prepack(FAKE, 32, 40, FAKE, None), q8.Q8TA_ERR_UNSUPPORTED, "K % 16")
+    _st(l.q8ta_weight_prepack(odd, 32, 64, FAKE, None), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(l.q8ta_weight_prepack(FAKE, 32, 64, odd, None), q8.Q8TA_ERR_UNSUPPORTED)
+    for fn in (l.q8ta_linear_prepacked, l.q8ta_linear_dq_prepacked):
+        _st(fn(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_NULL, "weight_sums")
+        _st(fn(FAKE, 4, 40, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_UNSUPPORTED, "K % 16")
+        _st(fn(odd, 4, 64, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_UNSUPPORTED)
+        _st(fn(FAKE, 4, 64, 0.02, 3, odd, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_UNSUPPORTED)
+        _st(fn(FAKE, 0, 64, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_SHAPE)
+        _st(fn(FAKE, 4, 64, 0.02, 3, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"gelu", FAKE, None),
+            q8.Q8TA_ERR_UNSUPPORTED)
+        _st(fn(FAKE, 4, 64, 0.02, 300, FAKE, 32, FAKE, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_QPARAM)
+
+
 def _gpu_present():
     try:
         import torch

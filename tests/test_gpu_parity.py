@@ -876,3 +876,102 @@ def test_linear_presummed_equals_linear(path, M, K, N):
             q8.q8ta_linear_presummed(dev(c.x), c.in_scale, c.in_zp, wd, wrong, dev(c.weight_scales),
                                      dev(c.bias), c.out_scale, c.out_zp, "none", out)
             assert not np.array_equal(host(out), ref)
+
+
+# ============================================================================ prepacked weights
+def _pack_reference(w):
+    """The packed layout as the header defines it, built with numpy indexing:
+    byte 16*l + j of fragment (nb, s) = w[32*nb + l % 32][32*s + 16*(l // 32) + j],
+    zero past N or K; fragment (nb, s) at (nb * KS + s) * 1024, KS = 2*ceil(K/64)."""
+    N, K = w.shape
+    NB, KP = -(-N // 32), -(-K // 64) * 64
+    wp = np.zeros((NB * 32, KP), dtype=np.int8)
+    wp[:N, :K] = w
+    KS = KP // 32
+    out = np.zeros(NB * 32 * KP, dtype=np.int8)
+    for nb in range(NB):
+        for s in range(KS):
+            frag = np.empty((64, 16), dtype=np.int8)
+            for l in range(64):
+                frag[l] = wp[32 * nb + l % 32, 32 * s + 16 * (l // 32): 32 * s + 16 * (l // 32) + 16]
+            out[(nb * KS + s) * 1024:(nb * KS + s + 1) * 1024] = frag.reshape(-1)
+    return out
+
+
+def _prepack(w):
+    N, K = w.shape
+    packed = torch.empty(q8.q8ta_weight_prepacked_bytes(N, K), dtype=torch.int8, device="cuda")
+    q8.q8ta_weight_prepack(dev(w), packed)
+    sums = torch.empty(N, dtype=torch.int32, device="cuda")
+    q8.q8ta_weight_sums(dev(w), sums)
+    return packed, sums
+
+
+@pytest.mark.parametrize("N,K", [(32, 64), (33, 80), (100, 1040), (257, 4096), (7, 16)])
+def test_weight_prepack_layout(N, K):
+    _say(f"prepack N={N} K={K}")
+    w = qi.linear_case(N + K, 1, K, N).w
+    packed, _ = _prepack(w)
+    np.testing.assert_array_equal(host(packed), _pack_reference(w))
+
+
+PK_SHAPES = [(300, 1040, 257), (64, 128, 64), (512, 4096, 768), (5, 64, 32), (129, 2064, 129),
+             (1, 4096, 512), (700, 256, 1100), (256, 192, 256)]
+
+
+@pytest.mark.parametrize("M,K,N", PK_SHAPES)
+def test_linear_prepacked_parity(M, K, N):
+    """q8ta_linear_prepacked / _dq_prepacked with the weight's own sums: equal
+    to the oracle (int8 codes, and their dequantized fp32 values bit for bit)."""
+    _say(f"linear prepacked M={M} K={K} N={N}")
+    c = qi.linear_case(M * 5 + K + N + 11, M, K, N)
+    packed, sums = _prepack(c.w)
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    q8.q8ta_linear_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
+                             dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    ref = _oracle_linear(c)
+    np.testing.assert_array_equal(host(out), ref)
+    outf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    q8.q8ta_linear_dq_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
+                                dev(c.weight_scales), None, c.out_scale, c.out_zp, "relu", outf)
+    refr = oracle.dequantize_per_tensor(_oracle_linear(c, bias=False, activation="relu"),
+                                        c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(host(outf).view(np.uint32), refr.view(np.uint32))
+
+
+@pytest.mark.parametrize("izp", [-128, 127])
+def test_linear_prepacked_zero_points_and_shifted_sums(izp):
+    """Extreme input zero points; sums other than the weight's move the result
+    (the sums are used, not recomputed)."""
+    M, K, N = 200, 512, 300
+    c = qi.linear_case(900 + izp, M, K, N, in_zp=izp, out_zp=127 if izp < 0 else -128)
+    packed, sums = _prepack(c.w)
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    q8.q8ta_linear_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
+                             dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    np.testing.assert_array_equal(host(out), _oracle_linear(c))
+    q8.q8ta_linear_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums + 1000,
+                             dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    assert not np.array_equal(host(out), _oracle_linear(c))
+
+
+def test_linear_dq_prepacked_gemm_workload_sampled():
+    """The 2048 x 4096 x 11008 workload: fp32 rows checked against the oracle
+    one by one, and the whole output against q8ta_linear_dq."""
+    c = qi.make_gemm()
+    _say("linear_dq prepacked 2048x4096x11008")
+    packed, sums = _prepack(c.w)
+    out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    x, sc, bi = dev(c.x), dev(c.weight_scales), dev(c.bias)
+    q8.q8ta_linear_dq_prepacked(x, c.in_scale, c.in_zp, packed, c.N, sums, sc, bi, c.out_scale,
+                                c.out_zp, "none", out)
+    ref_full = torch.empty_like(out)
+    q8.q8ta_linear_dq(x, c.in_scale, c.in_zp, dev(c.w), None, sc, bi, c.out_scale, c.out_zp,
+                      "none", ref_full)
+    assert torch.equal(out.view(torch.int32), ref_full.view(torch.int32))
+    got = host(out)
+    rows = np.array([0, 1, 127, 128, 1000, 2047])
+    q = oracle.linear(c.x[rows], c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                      c.out_zp)
+    ref = oracle.dequantize_per_tensor(q, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(got[rows].view(np.uint32), ref.view(np.uint32))
