@@ -128,7 +128,12 @@ __device__ __forceinline__ int cslot(int r) { return (r & 3) * (BN / 4) + (r >> 
 
 // PRE: the row sums of W come from a.wsum_pre (trusted, precomputed by the
 // caller) instead of v_dot4 over the W fragments.
-template <class C, bool PRE, bool KFULL>
+// TR (fp32 output only): X is the A operand and W the B operand, so lane l
+// holds output channel l % 32 of its fragments and the 32 lanes of a
+// half-wave store 32 consecutive floats (one whole 128-byte line) of one
+// output row per register; in the other form each store instruction writes
+// 16-byte pieces of 32 rows, which the L2 has to merge.
+template <class C, bool PRE, bool KFULL, bool TR>
 __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs a, int tiles_m,
                                                                       int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t smem[2 * C::STAGE];
@@ -268,7 +273,10 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
         constexpr int i = decltype(I)::value;
         Static<0, C::FM>::each([&](auto J) {
           constexpr int j = decltype(J)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+          if constexpr (TR)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
         });
       });
     });
@@ -354,9 +362,37 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   __syncthreads();
 
   constexpr int NWS = PRE ? 1 : C::WAVES_M;
+  if constexpr (TR) {
+    // lane l: channel n of tile row wn*WN + i*32 + l % 32; register r: output
+    // row m of fragment j at 8 * (r / 4) + 4 * (l / 32) + r % 4
+    const float dq_zpf = (float)a.dq_zp;
+    Static<0, C::FN>::each([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int rr = wn * C::WN + i * 32 + lrow;
+      const int sl = cslot<C::BN>(rr);
+      int32_t ws = epi_ws[0][sl];
+      Static<1, NWS>::each([&](auto W) { ws += epi_ws[decltype(W)::value][sl]; });
+      const int32_t zc = a.izp * ws;
+      const float sc = epi_sc[sl], bi = epi_bi[sl];
+      const int64_t n = bn0 + rr;
+      if (n < N) {
+        Static<0, C::FM>::each([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Static<0, 16>::each([&](auto R) {
+            constexpr int r = decltype(R)::value;
+            const int64_t m = bm0 + wm * C::WM + j * 32 + 8 * (r / 4) + 4 * kg + r % 4;
+            if (m < M) {
+              const float q = requant_code(acc[i][j][r] - zc, sc, bi, a.rq);
+              a.outf[m * N + n] = (q - dq_zpf) * a.dq_scale;
+            }
+          });
+        });
+      }
+    });
+    return;
+  }
+  // int8 (or int32 accumulator) output
   const bool vec_out = (N % 4) == 0 && ((uintptr_t)a.out & 3) == 0;
-  const bool vec_outf = (N % 4) == 0 && ((uintptr_t)a.outf & 15) == 0;
-  const float dq_zpf = (float)a.dq_zp;
   Static<0, C::FN>::each([&](auto I) {
     constexpr int i = decltype(I)::value;
     Static<0, 4>::each([&](auto G) {
@@ -391,21 +427,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
             float q[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) q[r] = requant_code(c[r], sc[r], bi[r], a.rq);
-            if (a.outf) {
-              // fused dequantize: (q - zp) * scale; q and zp are small
-              // integers, so the float subtraction is exact
-              float* of = a.outf + m * N + nb;
-              v4f y;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) y[r] = (q[r] - dq_zpf) * a.dq_scale;
-              if (vec_outf && nb + 3 < N) {
-                *reinterpret_cast<v4f*>(of) = y;
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (nb + r < N) of[r] = y[r];
-              }
-            } else if (vec_out && nb + 3 < N) {
+            if (vec_out && nb + 3 < N) {
               *reinterpret_cast<uint32_t*>(a.out + m * N + nb) =
                   pack4((int)q[0], (int)q[1], (int)q[2], (int)q[3]);
             } else {
@@ -435,10 +457,22 @@ using MxY3 = MxCfg<256, 128, 64, 2, 2, 2, 3>;
 template <class C, bool PRE>
 hipError_t launch_mx2(const LinearArgs& a, int tiles_m, int tiles_n, hipStream_t s) {
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  if (a.K % C::BK == 0)
-    hipLaunchKernelGGL((k_gemm_mx<C, PRE, true>), grid, dim3(C::NT), 0, s, a, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((k_gemm_mx<C, PRE, false>), grid, dim3(C::NT), 0, s, a, tiles_m, tiles_n);
+  // fp32 output (fused dequantize): the transposed form, whole-line stores
+  const bool tr = a.outf != nullptr && a.acc == nullptr;
+  if (a.K % C::BK == 0) {
+    if (tr)
+      hipLaunchKernelGGL((k_gemm_mx<C, PRE, true, true>), grid, dim3(C::NT), 0, s, a, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((k_gemm_mx<C, PRE, true, false>), grid, dim3(C::NT), 0, s, a, tiles_m,
+                         tiles_n);
+  } else {
+    if (tr)
+      hipLaunchKernelGGL((k_gemm_mx<C, PRE, false, true>), grid, dim3(C::NT), 0, s, a, tiles_m,
+                         tiles_n);
+    else
+      hipLaunchKernelGGL((k_gemm_mx<C, PRE, false, false>), grid, dim3(C::NT), 0, s, a, tiles_m,
+                         tiles_n);
+  }
   return hipGetLastError();
 }
 

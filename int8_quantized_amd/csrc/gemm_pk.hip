@@ -95,7 +95,11 @@ __global__ __launch_bounds__(256) void k_prepack(const int8_t* __restrict__ w, i
   packed[c] = v;
 }
 
-template <bool KFULL>
+// TR (fp32 output): X is the A operand and W the B operand, so the 32 lanes of
+// a half-wave hold 32 consecutive output channels of one row and each store
+// writes a whole 128-byte line (measured 2-2.5 us faster per call on
+// 2048 x 4096 x 11008 than 16-byte pieces of 32 rows per store).
+template <bool KFULL, bool TR>
 __global__ __launch_bounds__(kNT, 2) void k_gemm_pk(LinearArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t smem[2 * kStage];
   __shared__ __attribute__((aligned(16))) float epi_sc[kBN];
@@ -211,8 +215,12 @@ __global__ __launch_bounds__(kNT, 2) void k_gemm_pk(LinearArgs a, int tiles_m, i
         constexpr int i = decltype(I)::value;
         Static<0, kFM>::each([&](auto J) {
           constexpr int j = decltype(J)::value;
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wv[p][ks][i], bf[j], acc[i][j], 0, 0,
-                                                            0);
+          if constexpr (TR)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], wv[p][ks][i], acc[i][j], 0,
+                                                              0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wv[p][ks][i], bf[j], acc[i][j], 0,
+                                                              0, 0);
         });
       });
       if constexpr (decltype(LOAD)::value) load_w(next, P, KSI);
@@ -252,9 +260,35 @@ __global__ __launch_bounds__(kNT, 2) void k_gemm_pk(LinearArgs a, int tiles_m, i
   epi_bi[cslot(tid)] = e_bi;
   __syncthreads();
 
+  if constexpr (TR) {
+    // lane l: channel of tile row wn*64 + i*32 + l % 32; register r: output
+    // row m of fragment j at 8 * (r / 4) + 4 * (l / 32) + r % 4
+    const float dq_zpf = (float)a.dq_zp;
+    Static<0, kFN>::each([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      const int rr = wn * kWN + i * 32 + lrow;
+      const int sl = cslot(rr);
+      const int32_t zc = a.izp * epi_ws[sl];
+      const float sc = epi_sc[sl], bi = epi_bi[sl];
+      const int64_t n = bn0 + rr;
+      if (n < N) {
+        Static<0, kFM>::each([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Static<0, 16>::each([&](auto R) {
+            constexpr int r = decltype(R)::value;
+            const int64_t m = bm0 + j * 32 + 8 * (r / 4) + 4 * kg + r % 4;
+            if (m < M) {
+              const float q = requant_code(acc[i][j][r] - zc, sc, bi, a.rq);
+              a.outf[m * N + n] = (q - dq_zpf) * a.dq_scale;
+            }
+          });
+        });
+      }
+    });
+    return;
+  }
+  // int8 (or int32 accumulator) output
   const bool vec_out = (N % 4) == 0 && ((uintptr_t)a.out & 3) == 0;
-  const bool vec_outf = (N % 4) == 0 && ((uintptr_t)a.outf & 15) == 0;
-  const float dq_zpf = (float)a.dq_zp;
   Static<0, kFN>::each([&](auto I) {
     constexpr int i = decltype(I)::value;
     Static<0, 4>::each([&](auto G) {
@@ -285,20 +319,7 @@ __global__ __launch_bounds__(kNT, 2) void k_gemm_pk(LinearArgs a, int tiles_m, i
             float q[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) q[r] = requant_code(c[r], sc[r], bi[r], a.rq);
-            if (a.outf) {
-              // fused dequantize: (q - zp) * scale, q and zp small integers
-              float* of = a.outf + m * N + nb;
-              v4f y;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) y[r] = (q[r] - dq_zpf) * a.dq_scale;
-              if (vec_outf && nb + 3 < N) {
-                *reinterpret_cast<v4f*>(of) = y;
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (nb + r < N) of[r] = y[r];
-              }
-            } else if (vec_out && nb + 3 < N) {
+            if (vec_out && nb + 3 < N) {
               *reinterpret_cast<uint32_t*>(a.out + m * N + nb) =
                   pack4((int)q[0], (int)q[1], (int)q[2], (int)q[3]);
             } else {
@@ -333,10 +354,14 @@ hipError_t launch_gemm_pk(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + kBM - 1) / kBM);
   const int tiles_n = (int)((a.N + kBN - 1) / kBN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  if (a.K % kBK == 0)
-    hipLaunchKernelGGL(k_gemm_pk<true>, grid, dim3(kNT), 0, s, a, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL(k_gemm_pk<false>, grid, dim3(kNT), 0, s, a, tiles_m, tiles_n);
+  const bool tr = a.outf != nullptr && a.acc == nullptr;
+  if (a.K % kBK == 0) {
+    if (tr) hipLaunchKernelGGL((k_gemm_pk<true, true>), grid, dim3(kNT), 0, s, a, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((k_gemm_pk<true, false>), grid, dim3(kNT), 0, s, a, tiles_m, tiles_n);
+  } else {
+    if (tr) hipLaunchKernelGGL((k_gemm_pk<false, true>), grid, dim3(kNT), 0, s, a, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((k_gemm_pk<false, false>), grid, dim3(kNT), 0, s, a, tiles_m, tiles_n);
+  }
   return hipGetLastError();
 }
 

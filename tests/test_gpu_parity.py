@@ -192,6 +192,14 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
     with env(Q8TA_GEMM_CFG=cfg):
         np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+        # fp32 output (fused dequantize; the 32x32x32 kernels store it in their
+        # transposed form)
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                          dev(c.bias), c.out_scale, c.out_zp, "relu", out)
+        ref = oracle.dequantize_per_tensor(_oracle_linear(c, activation="relu"), c.out_scale,
+                                           c.out_zp)
+        np.testing.assert_array_equal(host(out).view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("cfg", ["B", "D", "Q"])
