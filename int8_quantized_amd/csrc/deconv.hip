@@ -464,12 +464,18 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
   {
     // Small problems are latency-bound: when the default tile leaves the chip
     // mostly idle (fewer than 256 workgroups), take one 16-channel fragment
-    // per wave (measured on [1,64,32,32] K4 s2: 18.3 -> 12.7 us).
+    // and one 16-column phase fragment per wave and one phase row per
+    // workgroup, for as many workgroups as the problem allows (measured on
+    // [1,64,32,32] K4 s2: 18.3 -> 12.7 us with one channel fragment, 10.8 ->
+    // 9.3 us with one column fragment and one row: 16 -> 64 workgroups).
     const int64_t ocb = 2 * 16 * FO;
     const int64_t est = a.N * ((p.Hp + 3) / 4) * ((p.Wp + 16 * FJ - 1) / (16 * FJ)) *
                         ((a.OC + ocb - 1) / ocb);
     small = est < 256;
-    if (small) FO = 1;
+    if (small) {
+      FO = 1;
+      FJ = 1;
+    }
   }
   if (const char* e = getenv("Q8TA_DECONV_FJ")) FJ = atoi(e);
   if (const char* e = getenv("Q8TA_DECONV_FO")) FO = atoi(e);
@@ -485,7 +491,7 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
   const int c_hi = p.TJ - 1 + dwmax + 1;
   p.HC = ((c_hi - c_lo) + 3) / 4 * 4;
   p.OCols = sw * p.TJ;
-  int wi_pref = small ? 2 : 4;   // small problems: more, smaller workgroups
+  int wi_pref = small ? 1 : 4;   // small problems: more, smaller workgroups
   if (const char* e = getenv("Q8TA_DECONV_WI")) wi_pref = atoi(e);
   if (wi_pref < 1) wi_pref = 1;
   if (wi_pref * p.WO > 8) wi_pref = 8 / p.WO;
