@@ -301,8 +301,8 @@ def main():
     else:
         roofline = {
             "bound": "mfma",
-            "kernel": "k_gemm_mx<256x128x64 tile, 2x2 waves of 128x64, 2 workgroups/CU, loads 2 "
-                      "K steps ahead> (v_mfma_i32_32x32x32_i8)",
+            "kernel": "k_gemm_mx<256x128x64 tile, 2x2 waves of 128x64, 2 workgroups/CU, "
+                      "store-first K loop, transposed fp32 stores> (v_mfma_i32_32x32x32_i8)",
             "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic_from_profile("gemm_mx", os.path.join(

@@ -315,13 +315,15 @@ bool gemm_mfma_supported(const LinearArgs& a) {
 // Tile choice (measured on 2048 x 4096 x 11008, fused dequantize): for
 // problems that fill the GPU at least once with 256 x 128 tiles and have a
 // long K, the 32x32x32 kernel of gemm_mx.hip with two workgroups per CU and
-// loads two K steps ahead ('y': 129 us against 132 us for this file's
-// 256 x 128 tile 'V'); otherwise the medium tile, or the small one for few
-// rows.  The large tile of this file (128 x 128 per wave, loops the compiler
-// leaves rolled) keeps its accumulators in scratch memory; the
-// direct-to-LDS 32x32x32 kernel of gemm_dl.hip ('G') measured 156-182 us,
-// the 32x32x32 variant of the 256 x 128 tile in gemm32.hip ('X') 146 us.
-// Q8TA_GEMM_CFG (one letter of LMSKWVUQRGXYZPyz) overrides the choice.
+// the store-first K loop ('w': 125.7-126.4 us against 129.5-130.5 us for
+// 'y', loads two steps ahead with the LDS write at the end of each step, and
+// 131-135 us for this file's 256 x 128 tile 'V'); otherwise the medium tile,
+// or the small one for few rows.  The large tile of this file (128 x 128 per
+// wave, loops the compiler leaves rolled) keeps its accumulators in scratch
+// memory; the direct-to-LDS 32x32x32 kernel of gemm_dl.hip ('G') measured
+// 150 us, the 32x32x32 variant of the 256 x 128 tile in gemm32.hip ('X')
+// 146 us.  Q8TA_GEMM_CFG (one letter of LMSKWVUQRGXYZPyzw) overrides the
+// choice.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   const char* e = getenv("Q8TA_GEMM_CFG");
   char pick = 0;
@@ -329,7 +331,7 @@ hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
   if (!pick) {
     const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
     const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    pick = (tv >= 256 && a.K >= 1024) ? 'y' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
+    pick = (tv >= 256 && a.K >= 1024) ? 'w' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
   }
   if (pick == 'G') return gemm_dl_supported(a) ? launch_gemm_dl(a, s) : launch_cfg<CfgM>(a, s);
   if (pick == 'X') return launch_gemm32(a, s);
