@@ -185,7 +185,8 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
 
 
 @pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X", "Y", "Z", "P", "y", "z", "w"])
-@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768)])
+@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768),
+                                   (70, 48, 300)])
 def test_linear_every_gemm_tile(cfg, M, K, N):
     _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
     c = qi.linear_case(M + N + ord(cfg), M, K, N)
