@@ -5,32 +5,37 @@
 // sum x*w - izp * sum w; Constraints (2): x [M,K] and w [N,K] K-contiguous).
 //
 // Why this shape on gfx950:
-//  * A register-only loop of v_mfma_i32_32x32x32_i8 issues at ~4.4 POP/s,
-//    one of v_mfma_i32_16x16x64_i8 at ~2.4 POP/s, so only the 32x32x32 form
-//    can approach the 5.0 POP/s dense int8 peak.
+//  * A register-only loop of v_mfma_i32_32x32x32_i8 issues at ~4.3 POP/s
+//    (3.7-3.9 with one or two waves per SIMD), one of v_mfma_i32_16x16x64_i8
+//    at ~2.4-3.0, so only the 32x32x32 form can approach the 5.0 POP/s dense
+//    int8 peak.
 //  * Each wave owns a WN x WM = 128 x 64 (or 64 x 128) sub-tile: 8
 //    accumulator fragments of 16 registers.  Every K byte then costs the wave
 //    WN + WM = 192 bytes of LDS fragment reads for 2 * WN * WM = 16384
 //    operations, 85 operations per LDS byte; the 64 x 64 wave tile of the
 //    16x16x64 kernel reads 128 bytes for 8192 (64 per byte), which puts the
 //    LDS port at the matrix cores' speed.
-//  * Two workgroups of four waves share a CU (256 registers per wave, two
-//    waves per SIMD, 2 x 48 KiB of LDS): their barriers and epilogues are
-//    independent, so one workgroup's requantize and stores run while the
-//    other keeps the matrix cores busy.  (The one-workgroup variant keeps a
-//    whole SIMD per wave and 128-byte K steps.)
-//  * K advances BK bytes per step through two LDS buffers: the next step's
-//    slab is fetched into registers (16 B per load, rows past M/N/K
-//    zero-filled) while the matrix cores work on the current buffer, then
-//    written to the other buffer; one barrier per step.  The 16-byte chunk c
-//    of LDS row r sits at chunk position c ^ f(r), f chosen so that the 16
-//    lanes one ds_read_b128 cycle serves hit distinct banks.
-//  * W is the A operand and X the B operand: lane l supplies row l % 32 of
-//    each operand with K bytes 16 * (l / 32) .. +15 of each 32-byte slice;
-//    accumulator register r of lane l holds row 8 * (r / 4) + 4 * (l / 32) +
-//    r % 4 and column l % 32, so registers 4g .. 4g+3 are four consecutive
-//    output channels n of one row m: one 32-bit int8 store or one 16-byte
-//    fp32 store per group in the epilogue.
+//  * Two workgroups of four waves share a CU (up to 256 registers per wave,
+//    two waves per SIMD, 2 x 24 KiB of LDS buffers): their barriers and
+//    epilogues are independent, so one workgroup's requantize and stores run
+//    while the other keeps the matrix cores busy.  (The one-workgroup
+//    variant keeps a whole SIMD per wave and 128-byte K steps.)
+//  * K advances BK bytes per step through two LDS buffers; the slabs are
+//    staged in registers (16 B per load; rows past M/N read the last row,
+//    chunks past K are zeroed) and written to the buffer the matrix cores are
+//    not reading; one barrier per step.  The default loop (PD = 3) writes
+//    step k + 1's registers to LDS at the top of step k and refills them with
+//    step k + 3 at once.  The 16-byte chunk c of LDS row r sits at chunk
+//    position c ^ f(r), f chosen so that the 16 lanes one ds_read_b128 cycle
+//    serves hit distinct banks.
+//  * Lane l supplies row l % 32 of each operand with K bytes 16 * (l / 32)
+//    .. +15 of each 32-byte slice; accumulator register r of lane l holds row
+//    8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the product.
+//    For int8 output W is the A operand and X the B operand, so registers
+//    4g .. 4g+3 are four consecutive output channels of one row (one 32-bit
+//    store); for fp32 output (fused dequantize) the operands swap, so lane l
+//    holds one channel and each half-wave store writes 32 consecutive floats
+//    of one row, a whole 128-byte line.
 //  * sum w comes from v_dot4 against 0x01010101 over the W fragments while
 //    they are in registers; the waves sharing a W strip split the K slices
 //    between them and add their partial sums through LDS after the loop.
