@@ -499,7 +499,36 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     res["gemv_1x4096x4096_warm"] = summary(timer.time_calls([fns[0]], reps), gemv_bytes, "GB/s",
                                            PEAK_HBM_GBS)
     res["gemv_1x4096x4096_cold"]["algorithmic_bytes"] = gemv_bytes
-    del wl, outs, fns
+    # fp32 activations: quantize folded into the weight-streaming kernel
+    # against the two calls (quantize_per_tensor, then the int8 GEMV)
+    xf_ = torch.from_numpy(qi.x_fp32(qi.rng(c.K), (1, c.K))).cuda()
+    xq_ = torch.empty((1, c.K), dtype=torch.int8, device="cuda")
+    qfns = [(lambda i=i: check(lib.q8ta_quantize_linear(
+        xf_.data_ptr(), 1, c.K, c.in_scale, c.in_zp, wl[i].data_ptr(), c.N, None,
+        ws_.data_ptr(), b_.data_ptr(), c.out_scale, c.out_zp, b"none", outs[i].data_ptr(),
+        stream))) for i in range(copies)]
+
+    def _chain(i):
+        check(lib.q8ta_quantize_per_tensor(xf_.data_ptr(), xq_.data_ptr(), c.K, c.in_scale,
+                                           c.in_zp, stream))
+        check(lib.q8ta_linear_gemv(xq_.data_ptr(), 1, c.K, c.in_scale, c.in_zp, wl[i].data_ptr(),
+                                   c.N, None, ws_.data_ptr(), b_.data_ptr(), c.out_scale, c.out_zp,
+                                   b"none", outs[i].data_ptr(), stream))
+    cfns = [(lambda i=i: _chain(i)) for i in range(copies)]
+    qgemv_bytes = c.N * c.K + 4 * c.K + 4 * c.N + 4 * c.N + c.N
+    timer.time_calls(qfns, copies)
+    res["quantize_gemv_1x4096x4096_fused_cold"] = summary(
+        timer.time_calls(qfns, 4 * copies), qgemv_bytes, "GB/s", PEAK_HBM_GBS)
+    timer.time_calls(cfns, copies)
+    res["quantize_gemv_1x4096x4096_two_calls_cold"] = summary(
+        timer.time_calls(cfns, 4 * copies), qgemv_bytes, "GB/s", PEAK_HBM_GBS)
+    qfns[0]()
+    fused_q = outs[0].clone()
+    cfns[0]()
+    torch.cuda.synchronize()
+    res["quantize_gemv_1x4096x4096_fused_cold"]["output_equal_to_two_calls"] = bool(
+        torch.equal(fused_q, outs[0]))
+    del wl, outs, fns, qfns, cfns
 
     # ---- quantize [8,256,64,64] (rotate 16 copies) and the large transposed conv
     d = qi.make_deconv_large()
@@ -590,6 +619,14 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     timer.time_calls([chain], 10)
     res["chain_quantize_4x64_linear_4x64x32"] = summary(timer.time_calls([chain], reps),
                                                         2 * 4 * 64 * 32, "TOPS", None)
+
+    def chain_fused():
+        check(lib.q8ta_quantize_linear(xf.data_ptr(), c1.M, c1.K, c1.in_scale, c1.in_zp,
+                                       w1.data_ptr(), c1.N, None, s1.data_ptr(), b1.data_ptr(),
+                                       c1.out_scale, c1.out_zp, b"none", o1.data_ptr(), stream))
+    timer.time_calls([chain_fused], 10)
+    res["chain_quantize_4x64_linear_4x64x32_one_call"] = summary(
+        timer.time_calls([chain_fused], reps), 2 * 4 * 64 * 32, "TOPS", None)
 
     d4 = qi.make_deconv_small()
     x4 = torch.from_numpy(d4.x).cuda()

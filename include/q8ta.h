@@ -148,6 +148,40 @@ q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K,
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * quantize_per_tensor of fp32 activations followed by q8ta_linear (and, for
+ * the _dq form, by dequantize_per_tensor of its output), in one call: the
+ * whole quantize -> q8ta_linear -> dequantize chain of the [LIN] Problem
+ * section.
+ *   xq[m, k] = clamp(rint(x[m, k] * (float)(1/input_scale)) + input_zero_point,
+ *                    -128, 127)   (the q8ta_quantize_per_tensor formula)
+ *   q8ta_quantize_linear:    out = q8ta_linear(xq, ...)            int8 [M, N]
+ *   q8ta_quantize_linear_dq: out = q8ta_linear_dq(xq, ...)          fp32 [M, N]
+ * Bit-identical to the two (three) separate calls with the same scales and
+ * zero points.  x: fp32 [M, K] row-major, device.  For M <= 4 with K % 16 == 0
+ * and 16-byte aligned x and weight the activations are quantized inside the
+ * weight-streaming kernel and xq is never stored; otherwise the library
+ * quantizes into its own stream-ordered workspace (M * K bytes) and runs the
+ * q8ta_linear path.  Other arguments, requirements and errors as for
+ * q8ta_linear / q8ta_linear_dq (x NULL -> Q8TA_ERR_NULL).
+ */
+q8ta_status q8ta_quantize_linear(const float* x, int64_t M, int64_t K,
+                                 double input_scale, int64_t input_zero_point,
+                                 const int8_t* weight, int64_t N,
+                                 const int32_t* weight_sums,
+                                 const float* weight_scales, const float* bias,
+                                 double output_scale, int64_t output_zero_point,
+                                 const char* activation, int8_t* out,
+                                 hipStream_t stream);
+q8ta_status q8ta_quantize_linear_dq(const float* x, int64_t M, int64_t K,
+                                    double input_scale, int64_t input_zero_point,
+                                    const int8_t* weight, int64_t N,
+                                    const int32_t* weight_sums,
+                                    const float* weight_scales, const float* bias,
+                                    double output_scale, int64_t output_zero_point,
+                                    const char* activation, float* out,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Precomputed weight sums (opt-in).  [LIN] Constraints (1): the zero-point
  * term needs sum_k weight[n, k]; the pages' op ignores its weight_sums
  * argument and folds the term per call, while the Vulkan op it mirrors takes

@@ -54,6 +54,10 @@ SIGNATURES = {
                                 _I64, _I64, _S, _P, _I64, _I64, _P], ctypes.c_int),
     "q8ta_linear_dq": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S, _P, _P],
                        ctypes.c_int),
+    "q8ta_quantize_linear": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
+                              _P, _P], ctypes.c_int),
+    "q8ta_quantize_linear_dq": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64,
+                                 _S, _P, _P], ctypes.c_int),
     "q8ta_weight_sums": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "q8ta_linear_presummed": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
                                _P, _P], ctypes.c_int),
@@ -321,6 +325,42 @@ def q8ta_linear_dq(x, input_scale, input_zero_point, weight, weight_sums, weight
     return out
 
 
+def _quantize_linear(fn, out_dtype, x, input_scale, input_zero_point, weight, weight_sums,
+                     weight_scales, bias, output_scale, output_zero_point, activation, out, stream):
+    torch = _torch()
+    if x.dim() != 2 or weight.dim() != 2 or out.dim() != 2:
+        raise ValueError("x [M,K], weight [N,K] and out [M,N] must be 2-D")
+    M, K = x.shape
+    N = weight.shape[0]
+    if weight.shape[1] != K or tuple(out.shape) != (M, N):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, weight {tuple(weight.shape)}, "
+                         f"out {tuple(out.shape)}")
+    _check(fn(_dev(x, torch.float32, "x"), M, K, float(input_scale), int(input_zero_point),
+              _dev(weight, torch.int8, "weight"), N, _opt(weight_sums, torch.int32, "weight_sums"),
+              _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+              float(output_scale), int(output_zero_point), _act(activation),
+              _dev(out, out_dtype, "out"), _stream(stream)))
+    return out
+
+
+def q8ta_quantize_linear(x, input_scale, input_zero_point, weight, weight_sums, weight_scales,
+                         bias, output_scale, output_zero_point, activation, out, stream=None):
+    """quantize_per_tensor of fp32 x [M, K] (input_scale, input_zero_point), then
+    q8ta_linear, in one call: int8 out [M, N]."""
+    return _quantize_linear(lib().q8ta_quantize_linear, _torch().int8, x, input_scale,
+                            input_zero_point, weight, weight_sums, weight_scales, bias,
+                            output_scale, output_zero_point, activation, out, stream)
+
+
+def q8ta_quantize_linear_dq(x, input_scale, input_zero_point, weight, weight_sums, weight_scales,
+                            bias, output_scale, output_zero_point, activation, out, stream=None):
+    """quantize_per_tensor -> q8ta_linear -> dequantize_per_tensor of fp32 x [M, K]
+    in one call: fp32 out [M, N]."""
+    return _quantize_linear(lib().q8ta_quantize_linear_dq, _torch().float32, x, input_scale,
+                            input_zero_point, weight, weight_sums, weight_scales, bias,
+                            output_scale, output_zero_point, activation, out, stream)
+
+
 def q8ta_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw, weight_sums,
                            weight_scales, bias, output_scale, output_zero_point, stride, padding,
                            output_padding, dilation, groups, activation, out, stream=None):
@@ -431,6 +471,7 @@ def q8ta_conv2d_acc(x, input_zero_point, weight, Kh, Kw, stride, padding, dilati
 __all__ = [
     "Q8taError", "lib", "q8ta_last_error", "q8ta_quantize_per_tensor", "q8ta_dequantize_per_tensor",
     "q8ta_linear", "q8ta_linear_gemv", "q8ta_linear_dq", "q8ta_linear_acc", "q8ta_conv2d_transposed",
+    "q8ta_quantize_linear", "q8ta_quantize_linear_dq",
     "q8ta_weight_sums", "q8ta_linear_presummed", "q8ta_linear_dq_presummed",
     "q8ta_weight_prepacked_bytes", "q8ta_weight_prepack", "q8ta_linear_prepacked",
     "q8ta_linear_dq_prepacked",

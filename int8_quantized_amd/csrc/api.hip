@@ -84,7 +84,7 @@ q8ta_status check_dil_groups(const char* op, int64_t IC, int64_t OC, int64_t dh,
   return Q8TA_OK;
 }
 
-q8ta_status linear_checks(const char* op, const int8_t* x, int64_t M, int64_t K, const int8_t* weight,
+q8ta_status linear_checks(const char* op, const void* x, int64_t M, int64_t K, const int8_t* weight,
                           int64_t N, const void* out) {
   if (!x || !weight || !out) return fail(Q8TA_ERR_NULL, "%s: x, weight and out must not be NULL", op);
   if (M < 1 || K < 1 || N < 1) return fail(Q8TA_ERR_SHAPE, "%s: M, K, N must be >= 1 (got %lld, %lld, %lld)", op,
@@ -102,8 +102,10 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
                         const float* weight_scales, const float* bias, double output_scale,
                         int64_t output_zero_point, const char* activation, int8_t* out,
                         hipStream_t stream, float* outf = nullptr,
-                        const int32_t* wsum_pre = nullptr, bool packed = false) {
-  q8ta_status st = linear_checks(op, x, M, K, weight, N, outf ? (const void*)outf : out);
+                        const int32_t* wsum_pre = nullptr, bool packed = false,
+                        const float* xf = nullptr) {
+  q8ta_status st = linear_checks(op, xf ? (const void*)xf : x, M, K, weight, N,
+                                 outf ? (const void*)outf : out);
   if (st) return st;
   if (packed && (K % 16 != 0 || ((uintptr_t)x & 15) != 0 || ((uintptr_t)weight & 15) != 0))
     return fail(Q8TA_ERR_UNSUPPORTED,
@@ -127,6 +129,11 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   if (packed) {
     a.wpk = weight;
     return hip_status(launch_gemm_pk(a, stream), op);
+  }
+  if (xf) {
+    a.xf = xf;
+    a.inv_in = recip(input_scale);
+    return hip_status(launch_quantize_linear(a, stream), op);
   }
   return hip_status(launch_linear(a, stream), op);
 }
@@ -240,6 +247,25 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   if (!no_mfma && gemm_mfma_supported(a)) return launch_gemm_mfma(a, s);
   if (gemm_dot4_supported(a)) return launch_gemm_dot4(a, s);
   return launch_linear_generic(a, s);
+}
+
+// quantize_per_tensor -> linear with fp32 activations (a.xf): the M <= 4
+// kernel quantizes while it loads them; other shapes quantize into a
+// stream-ordered int8 workspace and take the usual path.
+hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s) {
+  if (gemv_supported(a)) return launch_gemv(a, s);
+  const int64_t numel = a.M * a.K;
+  void* ws = nullptr;
+  hipError_t e = workspace_acquire(&ws, (size_t)numel, s);
+  if (e != hipSuccess) return e;
+  e = launch_quantize(a.xf, (int8_t*)ws, numel, a.inv_in, (float)a.izp, s);
+  if (e == hipSuccess) {
+    a.x = (const int8_t*)ws;
+    a.xf = nullptr;
+    e = launch_linear(a, s);
+  }
+  hipError_t f = workspace_release(ws, s);
+  return e != hipSuccess ? e : f;
 }
 
 // Q8TA_DECONV_PATH = mfma | igemm | dot4 | generic forces one kernel family
@@ -359,6 +385,30 @@ q8ta_status q8ta_linear_dq(const int8_t* x, int64_t M, int64_t K, double input_s
   return linear_impl("q8ta_linear_dq", false, x, M, K, input_scale, input_zero_point, weight, N,
                      weight_scales, bias, output_scale, output_zero_point, activation, nullptr,
                      stream, out);
+}
+
+q8ta_status q8ta_quantize_linear(const float* x, int64_t M, int64_t K, double input_scale,
+                                 int64_t input_zero_point, const int8_t* weight, int64_t N,
+                                 const int32_t* weight_sums, const float* weight_scales,
+                                 const float* bias, double output_scale,
+                                 int64_t output_zero_point, const char* activation, int8_t* out,
+                                 hipStream_t stream) {
+  (void)weight_sums;
+  return linear_impl("q8ta_quantize_linear", false, nullptr, M, K, input_scale, input_zero_point,
+                     weight, N, weight_scales, bias, output_scale, output_zero_point, activation,
+                     out, stream, nullptr, nullptr, false, x);
+}
+
+q8ta_status q8ta_quantize_linear_dq(const float* x, int64_t M, int64_t K, double input_scale,
+                                    int64_t input_zero_point, const int8_t* weight, int64_t N,
+                                    const int32_t* weight_sums, const float* weight_scales,
+                                    const float* bias, double output_scale,
+                                    int64_t output_zero_point, const char* activation, float* out,
+                                    hipStream_t stream) {
+  (void)weight_sums;
+  return linear_impl("q8ta_quantize_linear_dq", false, nullptr, M, K, input_scale,
+                     input_zero_point, weight, N, weight_scales, bias, output_scale,
+                     output_zero_point, activation, nullptr, stream, out, nullptr, false, x);
 }
 
 q8ta_status q8ta_weight_sums(const int8_t* weight, int64_t N, int64_t K, int32_t* sums,

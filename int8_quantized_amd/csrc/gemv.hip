@@ -10,7 +10,11 @@
 // activation row(s) are small and stay in cache.  The dot products use the
 // packed int8 dot instruction (v_dot4): sum x*w and, against 0x01010101,
 // sum w; the zero-point term is folded as sum x*w - izp*sum w, then each
-// row's partial is reduced across the wave and requantized.
+// row's partial is reduced across the wave and requantized.  With fp32
+// activations (the fused quantize -> linear chain) each lane loads its 16
+// values as four float4 and quantizes them with the quantize_per_tensor
+// formula into LDS, once per workgroup and chunk (the four waves share it),
+// before the dot products, so the int8 activations never go to HBM.
 #include <cstdlib>
 
 #include "q8ta_internal.h"
@@ -19,17 +23,22 @@ namespace q8ta {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-template <int MR, int ROWS, int CH>
+template <int MR, int ROWS, int CH, bool XF>
 __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t n0 = wave * ROWS;
-  if (n0 >= a.N) return;
+  // The fp32 form shares each chunk's codes through LDS and meets barriers,
+  // so there a wave past the last row stays (its loads are masked to zero
+  // and it stores nothing).
+  if (!XF && n0 >= a.N) return;
   const int64_t K = a.K;
+  __shared__ v4i xs[XF ? MR * CH * 64 : 1];
   // The epilogue's per-channel scale and bias are fetched before the weight
   // stream so that their latency overlaps it (lane i < ROWS holds row n0 + i).
   float sc_pre = 0.0f, b_pre = 0.0f;
@@ -51,20 +60,76 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   for (int64_t k0 = 0; k0 < K; k0 += 1024 * CH) {
     v4i wv[ROWS][CH];
     v4i xv[MR][CH];
+    int ones[CH];  // 0x01010101 where the lane's slice is inside K, else 0
+    if constexpr (XF) {
+      // The chunk's fp32 activations are loaded first (the quantize below
+      // waits only for them), then the weight stream, with every load
+      // unconditional: rows past N read row N - 1 (never stored), slices past
+      // K read the row's first bytes and are cancelled by zero activation
+      // codes and a zero ones-vector in sum w.  The workgroup quantizes the
+      // MR x 1024*CH activations once: slot i = (m, c, lane) of the register
+      // layout, 16 values each.
+      static_assert((MR * CH * 64) % kThreads == 0, "whole slots per thread");
+      constexpr int SL = MR * CH * 64 / kThreads;
+      v4f xr[SL][4];
+      bool xok[SL];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t kk = k0 + c * 1024 + lane * 16;
-      const bool ok = kk < K;
+      for (int j = 0; j < SL; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        const int m = i / (CH * 64);
+        const int64_t kk = k0 + (int64_t)(i % (CH * 64)) * 16;
+        xok[j] = kk < K;
+        const v4f* p = reinterpret_cast<const v4f*>(a.xf + m * K + (xok[j] ? kk : 0));
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        const bool rok = ok && (n0 + r < a.N);
-        wv[r][c] = rok ? __builtin_nontemporal_load(
-                             reinterpret_cast<const v4i*>(a.w + (n0 + r) * K + kk))
-                       : v4i{0, 0, 0, 0};
+        for (int d = 0; d < 4; ++d) xr[j][d] = p[d];
       }
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-        xv[m][c] = ok ? *reinterpret_cast<const v4i*>(a.x + m * K + kk) : v4i{0, 0, 0, 0};
+      for (int c = 0; c < CH; ++c) {
+        const int64_t kk = k0 + c * 1024 + lane * 16;
+        const bool ok = kk < K;
+        ones[c] = ok ? 0x01010101 : 0;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const int64_t n = n0 + r < a.N ? n0 + r : a.N - 1;
+          wv[r][c] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4i*>(a.w + n * K + (ok ? kk : 0)));
+        }
+      }
+      if (k0 != 0) __syncthreads();  // every wave has read the last chunk
+#pragma unroll
+      for (int j = 0; j < SL; ++j) {
+        v4i q;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          q[d] = (int)pack4(quantize1(xr[j][d][0], a.inv_in, (float)a.izp),
+                            quantize1(xr[j][d][1], a.inv_in, (float)a.izp),
+                            quantize1(xr[j][d][2], a.inv_in, (float)a.izp),
+                            quantize1(xr[j][d][3], a.inv_in, (float)a.izp));
+        xs[threadIdx.x + j * kThreads] = xok[j] ? q : v4i{0, 0, 0, 0};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) xv[m][c] = xs[(m * CH + c) * 64 + lane];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int64_t kk = k0 + c * 1024 + lane * 16;
+        const bool ok = kk < K;
+        ones[c] = 0x01010101;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const bool rok = ok && (n0 + r < a.N);
+          wv[r][c] = rok ? __builtin_nontemporal_load(
+                               reinterpret_cast<const v4i*>(a.w + (n0 + r) * K + kk))
+                         : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+          xv[m][c] = ok ? *reinterpret_cast<const v4i*>(a.x + m * K + kk) : v4i{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -72,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
       for (int r = 0; r < ROWS; ++r) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          sw[r] = __builtin_amdgcn_sdot4(wv[r][c][d], 0x01010101, sw[r], false);
+          sw[r] = __builtin_amdgcn_sdot4(wv[r][c][d], ones[c], sw[r], false);
 #pragma unroll
           for (int m = 0; m < MR; ++m)
             dot[m][r] = __builtin_amdgcn_sdot4(xv[m][c][d], wv[r][c][d], dot[m][r], false);
@@ -110,7 +175,10 @@ template <int MR, int ROWS>
 hipError_t launch_rows(const LinearArgs& a, hipStream_t s) {
   const int64_t waves = (a.N + ROWS - 1) / ROWS;
   const int64_t blocks = (waves + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL((k_skinny<MR, ROWS, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  if (a.xf)
+    hipLaunchKernelGGL((k_skinny<MR, ROWS, 4, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_skinny<MR, ROWS, 4, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -128,13 +196,17 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 bool gemv_supported(const LinearArgs& a) {
-  return a.M >= 1 && a.M <= 4 && (a.K % 16) == 0 && aligned16(a.x) && aligned16(a.w);
+  return a.M >= 1 && a.M <= 4 && (a.K % 16) == 0 && aligned16(a.xf ? (const void*)a.xf : a.x) &&
+         aligned16(a.w);
 }
 
 // rows: weight rows per wave (Q8TA_GEMV_ROWS overrides the default of 1: on
 // 1 x 4096 x 4096, 4.7-4.9 us against 4.9-5.2 us for 2 rows and 6.1 for 4).
+// The fp32 form takes 4 rows for M > 1, where each workgroup's quantize pass
+// grows with M: on 4 x 4096 x 4096, 7.1 us against 7.2 for 2 rows and 9.7
+// for 1 (M = 1: 5.3 us with 1 row, 6.0 with 4).
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) {
-  int rows = 1;
+  int rows = (a.xf && a.M > 1) ? 4 : 1;
   if (const char* e = getenv("Q8TA_GEMV_ROWS")) rows = atoi(e);
   switch (a.M) {
     case 1: return launch_mr<1>(a, s, rows);

@@ -172,8 +172,15 @@ struct LinearArgs {
   // Prepacked weight (the MFMA-fragment layout of q8ta_weight_prepack); set
   // only by the prepacked entry points, which also supply wsum_pre.
   const int8_t* wpk = nullptr;
+  // Fused quantize: when xf is set (x NULL), the activations are fp32 [M, K]
+  // and are quantized with inv_in = (float)(1/input_scale) and the input zero
+  // point before the contraction (the M <= 4 kernel does it while it loads
+  // them; launch_quantize_linear sends the other shapes through a workspace).
+  const float* xf = nullptr;
+  float inv_in = 0.0f;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
+hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s);
 
 struct DeconvArgs {
   const int8_t* x;

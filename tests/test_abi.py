@@ -234,6 +234,20 @@ def test_fused_entry_points_errors():
                          None), q8.Q8TA_ERR_SHAPE)
     _st(l.q8ta_linear_dq(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"relu6", FAKE,
                          None), q8.Q8TA_ERR_UNSUPPORTED)
+    # q8ta_quantize_linear(_dq): same checks as q8ta_linear, x fp32
+    for fn in (l.q8ta_quantize_linear, l.q8ta_quantize_linear_dq):
+        _st(fn(None, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_NULL)
+        _st(fn(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, None, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_NULL)
+        _st(fn(FAKE, 4, 0, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_SHAPE)
+        _st(fn(FAKE, 4, 64, 0.0, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_QPARAM)
+        _st(fn(FAKE, 4, 64, 0.02, 300, FAKE, 32, None, FAKE, None, 0.5, -5, b"none", FAKE, None),
+            q8.Q8TA_ERR_QPARAM)
+        _st(fn(FAKE, 4, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5, b"gelu", FAKE, None),
+            q8.Q8TA_ERR_UNSUPPORTED)
     # q8ta_quantize_conv2d_transposed: same checks as q8ta_conv2d_transposed
     args = [FAKE, 1, 64, 32, 32, 0.02, 3, FAKE, 32, 4, 4, 1024, None, FAKE, FAKE, 0.54, -5, 2, 2,
             1, 1, 0, 0, 1, 1, 1, b"none", FAKE, 64, 64, None]

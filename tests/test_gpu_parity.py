@@ -643,6 +643,89 @@ def test_linear_dq_gemm_workload_sampled():
     np.testing.assert_array_equal(got[rows].view(np.uint32), ref.view(np.uint32))
 
 
+# M <= 4 with K % 16 == 0: quantized inside the weight-streaming kernel; the
+# rest (ragged K, M > 4, the GEMM shapes) through the int8 workspace.
+QLIN_SHAPES = [(1, 4096, 4096), (4, 5136, 33), (2, 48, 17), (3, 1040, 300), (1, 4112, 7),
+               (4, 36, 9), (5, 64, 32), (65, 320, 97), (300, 1040, 257), (7, 33, 5)]
+
+
+@pytest.mark.parametrize("M,K,N", QLIN_SHAPES)
+@pytest.mark.parametrize("act", ["none", "relu"])
+def test_quantize_linear_equals_the_chain(M, K, N, act):
+    """q8ta_quantize_linear == q8ta_linear(quantize_per_tensor(x)) and
+    q8ta_quantize_linear_dq == dequantize of it, bit for bit, against the
+    oracle's steps; fp32 inputs include values beyond the int8 range so that
+    the quantize clamps."""
+    _say(f"quantize+linear M={M} K={K} N={N} act={act}")
+    g = qi.rng(M * 7 + K + N)
+    c = qi.linear_case(M * 5 + K + N, M, K, N)
+    xf = (qi.x_fp32(g, (M, K)) * 1.5).astype(np.float32)
+    xf.flat[:: 7] *= 3.0
+    xq = oracle.quantize_per_tensor(xf, c.in_scale, c.in_zp)
+    ref = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                        c.out_zp, activation=act)
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_linear(dev(xf), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                            dev(c.bias), c.out_scale, c.out_zp, act, out)
+    np.testing.assert_array_equal(host(out), ref)
+    outf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    q8.q8ta_quantize_linear_dq(dev(xf), c.in_scale, c.in_zp, dev(c.w), None,
+                               dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, act, outf)
+    refd = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(host(outf).view(np.uint32), refd.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows", ["1", "2", "4"])
+@pytest.mark.parametrize("M,K,N", [(1, 5136, 33), (2, 4112, 7), (3, 48, 301), (4, 8192, 65)])
+def test_quantize_linear_rows_per_wave(rows, M, K, N):
+    """Every rows-per-wave form of the fp32-activation kernel (ragged N, K
+    chunks with masked slices) against the oracle's quantize -> linear."""
+    _say(f"quantize+linear rows={rows} M={M} K={K} N={N}")
+    c = qi.linear_case(M * 11 + K + N, M, K, N)
+    xf = (qi.x_fp32(qi.rng(K + N), (M, K)) * 2.0).astype(np.float32)
+    xq = oracle.quantize_per_tensor(xf, c.in_scale, c.in_zp)
+    ref = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                        c.out_zp)
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    with env(Q8TA_GEMV_ROWS=rows):
+        q8.q8ta_quantize_linear(dev(xf), c.in_scale, c.in_zp, dev(c.w), None,
+                                dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none",
+                                out)
+    np.testing.assert_array_equal(host(out), ref)
+
+
+def test_quantize_linear_chain_small_workload():
+    """The small chain workload (quantize [4,64] -> linear 4x64x32) in one call."""
+    c = qi.make_chain_small()
+    _say("quantize+linear chain_small")
+    xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    ref = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                        c.out_zp)
+    out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+    q8.q8ta_quantize_linear(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), None,
+                            dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    np.testing.assert_array_equal(host(out), ref)
+
+
+def test_quantize_linear_dq_gemm_workload_sampled():
+    """fp32 [2048, 4096] -> quantize -> 2048 x 4096 x 11008 GEMM -> dequantize,
+    sampled rows against the oracle."""
+    c = qi.make_gemm()
+    _say("quantize+linear_dq 2048x4096x11008")
+    xf = qi.x_fp32(qi.rng(2024), (c.M, c.K))
+    out = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    q8.q8ta_quantize_linear_dq(dev(xf), c.in_scale, c.in_zp, dev(c.w), None,
+                               dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none",
+                               out)
+    got = host(out)
+    rows = np.array([0, 1, 1023, 2047])
+    xq = oracle.quantize_per_tensor(xf[rows], c.in_scale, c.in_zp)
+    q = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                      c.out_zp)
+    ref = oracle.dequantize_per_tensor(q, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(got[rows].view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_IGEMM_CASES[1],
                                   DECONV_IGEMM_CASES[5], DECONV_CASES[14]],
                          ids=["k3s2", "mixed", "igemm_oc40", "igemm_tall", "general"])
