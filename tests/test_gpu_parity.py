@@ -587,6 +587,14 @@ GROUPED_CASES = [
     (1, 8, 9, 9, 8, 3, 3, (1, 1), (1, 1), (1, 1), 8, 11, 5),             # output past the input
     (1, 8, 7, 6, 16, 3, 3, (1, 1), (1, 1), (1, 1), 8, None, None),       # channel multiplier 2
     (2, 64, 8, 8, 32, 3, 3, (1, 1), (1, 1), (1, 1), 4, None, None),      # grouped
+    # wide rows (W % 16 == 0), large planes, outputs past the input
+    (2, 8, 9, 16, 8, 3, 3, (1, 1), (1, 1), (1, 1), 8, None, None),       # ragged last block
+    (1, 4, 5, 32, 4, 5, 5, (1, 1), (2, 2), (1, 1), 4, None, None),       # 5x5, W 32
+    (1, 4, 8, 16, 4, 3, 3, (1, 1), (1, 1), (1, 1), 4, 11, 20),           # output past the input
+    (1, 4, 4, 16, 4, 3, 3, (1, 1), (3, 3), (1, 1), 4, None, None),       # pad larger than K
+    (1, 2, 128, 128, 2, 3, 3, (1, 1), (1, 1), (1, 1), 2, None, None),    # 128 x 128 plane
+    (1, 2, 129, 128, 2, 3, 3, (1, 1), (1, 1), (1, 1), 2, None, None),    # 129 x 128 plane
+    (1, 3, 16, 48, 3, 3, 3, (1, 1), (0, 0), (1, 1), 3, None, None),      # p0, W_out % 4 != 0
 ]
 
 
