@@ -810,6 +810,38 @@ def test_workspace_reuse_across_calls_and_streams(path):
         np.testing.assert_array_equal(host(out), ref)
 
 
+def test_quantize_linear_workspace_across_calls_and_streams():
+    """q8ta_quantize_linear calls that quantize through the workspace (M > 4,
+    and K % 16 != 0 at M <= 4) mixed with in-kernel ones, queued back to back:
+    small, larger (the buffer grows), small again, and one on a second
+    stream; every result checked after one final synchronization."""
+    _say("quantize+linear workspace reuse")
+    shapes = [(8, 64, 32), (300, 1040, 257), (2, 36, 9), (1, 4096, 64), (65, 320, 97)]
+    cases = []
+    for i, (M, K, N) in enumerate(shapes):
+        c = qi.linear_case(960 + i, M, K, N)
+        cases.append((c, (qi.x_fp32(qi.rng(970 + i), (M, K)) * 1.5).astype(np.float32)))
+    side = torch.cuda.Stream()
+    keep, outs = [], []
+    for i, (c, xf) in enumerate(cases + cases[1:2]):
+        args = (dev(xf), dev(c.w), dev(c.weight_scales), dev(c.bias))
+        out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+        keep.append(args)
+        outs.append(out)
+        on_side = i == len(cases)
+        if on_side:
+            side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side) if on_side else contextlib.nullcontext():
+            q8.q8ta_quantize_linear(args[0], c.in_scale, c.in_zp, args[1], None, args[2], args[3],
+                                    c.out_scale, c.out_zp, "none", out)
+    torch.cuda.synchronize()
+    for (c, xf), out in zip(cases + cases[1:2], outs):
+        xq = oracle.quantize_per_tensor(xf, c.in_scale, c.in_zp)
+        ref = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
+                            c.out_zp)
+        np.testing.assert_array_equal(host(out), ref)
+
+
 # ============================================================================ relu, transposed-conv dilation and groups
 @pytest.mark.parametrize("M,K,N", [(1, 512, 64), (1, 4096, 4096), (3, 48, 17), (300, 1040, 257),
                                    (7, 33, 5), (64, 128, 64)])
