@@ -371,6 +371,36 @@ def main():
             [lambda: check(lib.q8ta_weight_prepack(w.data_ptr(), N, K, packed.data_ptr(), stream))],
             20, batches=3)) * 1e3, 1)
         del yp
+        # fp32 activations in, fp32 out: the whole quantize -> linear -> dequantize
+        # chain in one call (its quantize goes through the library's workspace at
+        # this M) against the three separate calls
+        xf32 = torch.from_numpy(qi.x_fp32(qi.rng(2024), (M, K))).cuda()
+        xq32 = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        yq = torch.empty_like(y)
+
+        def qchain_one_call():
+            check(lib.q8ta_quantize_linear_dq(xf32.data_ptr(), M, K, c.in_scale, c.in_zp,
+                                              w.data_ptr(), N, None, ws.data_ptr(), b.data_ptr(),
+                                              c.out_scale, c.out_zp, none, yq.data_ptr(), stream))
+
+        def qchain_three_calls():
+            check(lib.q8ta_quantize_per_tensor(xf32.data_ptr(), xq32.data_ptr(), M * K,
+                                               c.in_scale, c.in_zp, stream))
+            check(lib.q8ta_linear(xq32.data_ptr(), M, K, c.in_scale, c.in_zp, w.data_ptr(), N,
+                                  None, ws.data_ptr(), b.data_ptr(), c.out_scale, c.out_zp, none,
+                                  q8out.data_ptr(), stream))
+            check(lib.q8ta_dequantize_per_tensor(q8out.data_ptr(), y.data_ptr(), M * N,
+                                                 c.out_scale, c.out_zp, stream))
+        q8out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+        qchain_one_call()
+        qchain_three_calls()
+        torch.cuda.synchronize()
+        extra["quantize_gemm_dq_output_equal"] = bool(torch.equal(yq.view(torch.int32),
+                                                                  y.view(torch.int32)))
+        for name, fn in (("quantize_gemm_dq_one_call_us", qchain_one_call),
+                         ("quantize_gemm_dq_three_calls_us", qchain_three_calls)):
+            extra[name] = round(min(timer.time_calls([fn], 50, batches=3)) * 1e3, 1)
+        del xf32, xq32, yq, q8out
         extra["weight_sums_us"] = round(min(timer.time_calls(
             [lambda: check(lib.q8ta_weight_sums(w.data_ptr(), N, K, sums.data_ptr(), stream))], 20,
             batches=3)) * 1e3, 1)
