@@ -353,3 +353,21 @@ def test_binding_rejects_host_tensors():
     out = torch.zeros(16, dtype=torch.int8)
     with pytest.raises(ValueError, match="device tensor"):
         q8.q8ta_quantize_per_tensor(x, out, 0.02, 3)
+
+
+def test_quantize_linear_binding_checks_shapes_before_the_call():
+    """The fused quantize -> linear bindings reject mismatched shapes and host
+    tensors before anything reaches the library."""
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float32)
+    w = torch.zeros((32, 64), dtype=torch.int8)
+    s = torch.ones(32, dtype=torch.float32)
+    for fn, dt in ((q8.q8ta_quantize_linear, torch.int8),
+                   (q8.q8ta_quantize_linear_dq, torch.float32)):
+        with pytest.raises(ValueError, match="shape mismatch"):
+            fn(x, 0.02, 3, w, None, s, None, 0.5, -5, "none", torch.zeros((4, 31), dtype=dt))
+        with pytest.raises(ValueError, match="2-D"):
+            fn(x.view(-1), 0.02, 3, w, None, s, None, 0.5, -5, "none",
+               torch.zeros((4, 32), dtype=dt))
+        with pytest.raises(ValueError, match="device tensor"):
+            fn(x, 0.02, 3, w, None, s, None, 0.5, -5, "none", torch.zeros((4, 32), dtype=dt))
