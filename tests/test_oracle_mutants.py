@@ -36,6 +36,18 @@ MUTANTS = [
     ("epilogue_bias_sign", "if (bias) v = v + bias[c];", "if (bias) v = v - bias[c];", 0),
     ("epilogue_bias_dropped", "if (bias) v = v + bias[c];", "if (bias) v = v;", 0),
     ("epilogue_input_scale_dropped", "v = v * s_in;", "v = v * 1.0f;", 0),
+    # the operation order of acc * input_scale * weight_scales[c] + bias[c]
+    ("epilogue_prefolded_scales", "v = v * s_in;\n    v = v * weight_scales[c];",
+     "v = v * (s_in * weight_scales[c]);", 0),
+    ("epilogue_fma_weight_scale_bias", "v = v * weight_scales[c];\n    if (bias) v = v + bias[c];",
+     "if (bias) v = fmaf(v, weight_scales[c], bias[c]);\n    else v = v * weight_scales[c];", 0),
+    ("epilogue_scales_swapped", "v = v * s_in;\n    v = v * weight_scales[c];",
+     "v = v * weight_scales[c];\n    v = v * s_in;", 0),
+    ("epilogue_input_scale_in_double", "v = v * s_in;", "v = (float)((double)v * input_scale);", 0),
+    ("epilogue_dequant_in_double", "v = v * s_in;\n    v = v * weight_scales[c];\n"
+     "    if (bias) v = v + bias[c];",
+     "v = (float)((double)v * (double)s_in * (double)weight_scales[c]"
+     " + (bias ? (double)bias[c] : 0.0));", 0),
     ("epilogue_out_zp_sign", "float u = r + ozp;", "float u = r - ozp;", 0),
     ("epilogue_round_half_away", "float r = nearbyintf(t);", "float r = roundf(t);", 1),
     ("epilogue_float_reciprocal", "const float inv_out = (float)(1.0 / output_scale);",

@@ -167,6 +167,120 @@ def test_epilogue_hand_vectors():
         assert int(got[0]) == q, (acc, b, ozp, q, int(got[0]))
 
 
+def _round_binary(x, mant, emin):
+    """Nearest value of a binary floating-point format (``mant`` fraction
+    bits, smallest normal exponent ``emin``) to the rational x, ties to even:
+    the IEEE 754 default rounding written out from its definition."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, emin) - mant)
+    n = a / quantum
+    k = n.numerator // n.denominator
+    if n - k > Fraction(1, 2) or (n - k == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    return (k if x > 0 else -k) * quantum
+
+
+def _r32(x):
+    return _round_binary(x, 23, -126)
+
+
+def _r64(x):
+    return _round_binary(x, 52, -1022)
+
+
+def _rne_int(t):
+    k = t.numerator // t.denominator
+    if t - k > 0.5 or (t - k == 0.5 and k % 2 == 1):
+        k += 1
+    return k
+
+
+def test_epilogue_order_derivation_is_exact():
+    """Checks the hand derivation in epilogue_order_hand.json step by step in
+    exact rational arithmetic (each stated intermediate is the correctly
+    rounded binary32 result of the exact operation on the previous ones), and
+    that each of the four other readings of the expression lands on a
+    different code on at least two rows -- so the codes pin the order."""
+    from fractions import Fraction as Fr
+    g = _gold("epilogue_order_hand.json")
+    caught = {}
+    for row in g["rows"]:
+        h = lambda key: Fr(float.fromhex(row[key]))
+        s_in_d = _r64(Fr(row["input_scale"]))
+        assert h("s_in_f32") == _r32(s_in_d)
+        assert h("weight_scale_f32") == _r32(Fr(row["weight_scale"]))
+        assert h("bias_f32") == _r32(Fr(row["bias"]))
+        assert h("inv_out_f32") == _r32(1 / _r64(Fr(row["output_scale"])))
+        a = _r32(Fr(row["acc"]))
+        assert a == row["acc"]  # |acc| < 2**24: exact
+        assert h("p1") == _r32(a * h("s_in_f32"))
+        assert h("p2") == _r32(h("p1") * h("weight_scale_f32"))
+        assert h("v") == _r32(h("p2") + h("bias_f32"))
+        assert h("t") == _r32(h("v") * h("inv_out_f32"))
+        q = max(-128, min(127, _rne_int(h("t")) + row["output_zero_point"]))
+        assert q == row["q"]
+        ws, b, inv, s_in = h("weight_scale_f32"), h("bias_f32"), h("inv_out_f32"), h("s_in_f32")
+        others = {
+            "prefolded_scales": _r32(_r32(a * _r32(s_in * ws)) + b),
+            "fma_weight_scale_bias": _r32(h("p1") * ws + b),
+            "scales_swapped": _r32(_r32(_r32(a * ws) * s_in) + b),
+            "input_scale_in_double": _r32(_r32(_r32(_r64(a * s_in_d)) * ws) + b),
+        }
+        for name, vm in others.items():
+            st = row["other_orders"][name]
+            assert Fr(float.fromhex(st["v"])) == vm, (row["acc"], name)
+            tm = _r32(vm * inv)
+            assert Fr(float.fromhex(st["t"])) == tm
+            qm = max(-128, min(127, _rne_int(tm) + row["output_zero_point"]))
+            assert qm == st["q"]
+            if qm != q:
+                caught[name] = caught.get(name, 0) + 1
+    assert set(caught) == {"prefolded_scales", "fma_weight_scale_bias", "scales_swapped",
+                           "input_scale_in_double"}
+    assert min(caught.values()) >= 2, caught
+
+
+def test_epilogue_order_hand_vectors():
+    """The oracle's epilogue reproduces every hand-derived code, alone and at
+    the end of the full linear (a 1x1 contraction that yields the row's acc)."""
+    g = _gold("epilogue_order_hand.json")
+    for row in g["rows"]:
+        args = (row["input_scale"], row["weight_scale"], row["bias"], row["output_scale"],
+                row["output_zero_point"])
+        s_in, w_s, b, s_out, ozp = (float(args[0]), np.float32(args[1]), np.float32(args[2]),
+                                    float(args[3]), args[4])
+        got = oracle.epilogue(np.array([row["acc"]], np.int32), 1, 1, s_in,
+                              np.array([w_s], np.float32), np.array([b], np.float32), s_out, ozp)
+        assert int(got[0]) == row["q"], (row["acc"], row["q"], int(got[0]))
+        # the same value through oracle.linear: acc = 127 * S + r with 0 <= r < 127,
+        # S spread over terms x * 127 with |x| <= 127, then one term r * 1
+        acc = row["acc"]
+        r = acc % 127
+        S = (acc - r) // 127
+        xs_l, ws_l = [], []
+        while S != 0:
+            step = max(-127, min(127, S))
+            xs_l.append(step)
+            ws_l.append(127)
+            S -= step
+        xs_l.append(r)
+        ws_l.append(1)
+        xs = np.array([xs_l], np.int8)
+        wv = np.array([ws_l], np.int8)
+        assert int((xs.astype(np.int64) * wv).sum()) == acc
+        ql = oracle.linear(xs, wv, np.array([w_s], np.float32), np.array([b], np.float32), s_in,
+                           0, s_out, ozp)
+        assert int(ql[0, 0]) == row["q"]
+
+
 def _linear_random_acc(seed, M, N, spread):
     g = qi.rng(seed)
     return g.integers(-spread, spread + 1, size=(M, N)).astype(np.int32)
