@@ -285,29 +285,15 @@ def main():
         fused_ok = bool(torch.equal(y.view(torch.int32), deq_ref.view(torch.int32)))
         del deq_ref
 
-    # q8ta_linear with M > 4 runs the matrix-core GEMM (bound by the dense int8
-    # MFMA peak); Q8TA_GEMM_PATH=dot4 selects the vector-ALU v_dot4 kernel,
-    # whose own ceiling is PEAK_DOT4_TOPS.
-    if os.environ.get("Q8TA_GEMM_PATH", "").startswith("d"):
-        roofline = {
-            "bound": "alu",
-            "kernel": "k_row_sums + k_dot4_gemm<4,false,4,4> (v_dot4_i32_i8, vector ALU)",
-            "achieved": round(achieved, 2), "peak": round(PEAK_DOT4_TOPS, 1), "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_DOT4_TOPS, 4),
-            "frac_of_int8_mfma_peak": round(achieved / PEAK_INT8_TOPS, 5),
-            "traffic": traffic_from_profile("gemm_dot4", os.path.join(
-                ROOT, "int8_quantized_amd", "csrc", "gemm_dot4.hip")),
-        }
-    else:
-        roofline = {
-            "bound": "mfma",
-            "kernel": "k_gemm_mx<256x128x64 tile, 2x2 waves of 128x64, 2 workgroups/CU, "
-                      "store-first K loop, transposed fp32 stores> (v_mfma_i32_32x32x32_i8)",
-            "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_INT8_TOPS, 4),
-            "traffic": traffic_from_profile("gemm_mx", os.path.join(
-                ROOT, "int8_quantized_amd", "csrc", "gemm_mx.hip")),
-        }
+    roofline = {
+        "bound": "mfma",
+        "kernel": "k_gemm_mx<256x128x64 tile, 2x2 waves of 128x64, 2 workgroups/CU, "
+                  "store-first K loop, transposed fp32 stores> (v_mfma_i32_32x32x32_i8)",
+        "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_INT8_TOPS, 4),
+        "traffic": traffic_from_profile("gemm_mx", os.path.join(
+            ROOT, "int8_quantized_amd", "csrc", "gemm_mx.hip")),
+    }
     roofline.update({"per_launch_ops": ops, "avg_launch_us": round(gemm_avg_s * 1e6, 2)})
 
     # ------------------------------------------------------------ CPU baseline (oracle sample)
@@ -596,7 +582,6 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     r = summary(timer.time_calls(dfns, 4 * copies), dops, "TOPS", PEAK_INT8_TOPS)
     r["exact_valid_tap_ops"] = dops
     r["algorithmic_bytes"] = int(numel + d.w.size + 8 * OC + dout.numel())
-    r["frac_of_dot4_peak"] = round(r["rate"] / PEAK_DOT4_TOPS, 4)
     res["deconv_8x256x64x64_k3s2p1_to_8x128x128x128"] = r
     del qs, dfns
 
@@ -694,7 +679,6 @@ def run_extra(torch, np, q8, qi, lib, stream, timer, check):
     cops = conv_ops(cc)
     r = summary(timer.time_calls([conv], reps), cops, "TOPS", PEAK_INT8_TOPS)
     r["exact_valid_tap_ops"] = cops
-    r["frac_of_dot4_peak"] = round(r["rate"] / PEAK_DOT4_TOPS, 4)
     res["conv2d_8x256x64x64_k3s1p1_to_8x128x64x64"] = r
     del cx, cout
 

@@ -12,24 +12,31 @@
  *     allocated and owned by the caller; the library never frees or retains
  *     it.  Tensors are dense and contiguous in the stated layout.  int8
  *     tensors are plain byte arrays (element i at byte i).
- *   - Workspace: some paths need device scratch memory: q8ta_linear(_acc,
- *     _dq) on the v_dot4 and direct-to-LDS GEMMs take 4*N bytes of weight
- *     row sums (the default matrix-core GEMM and the presummed calls take
- *     none); q8ta_quantize_conv2d_transposed takes the int8 copy of its input
- *     (N * IC * H_in * W_in bytes); q8ta_conv2d_transposed(_acc) takes, on
- *     its implicit-GEMM path, an NHWC copy of the input inside a zero-point
- *     border plus 4 * stride_h * stride_w * OC bytes of weight sums, and on
- *     its v_dot4 tiled path a channel-blocked copy of the input
- *     (N * H_in * ceil(IC/16) * W_in * 16 bytes).  The library keeps one
- *     buffer per (device, stream, nesting depth), grows it on demand after
- *     synchronizing that stream, and holds it until the process ends; under
- *     graph capture, above 256 MiB or deeper than 4 nested uses it takes
- *     stream-ordered memory (hipMallocAsync / hipFreeAsync on `stream`)
- *     instead.  A failed allocation returns Q8TA_ERR_HIP.
+ *   - Workspace: some paths need device scratch memory: the fused
+ *     quantize entry points take an int8 copy of their input
+ *     (q8ta_quantize_linear(_dq) with M > 4 or a shape the M <= 4 kernel
+ *     refuses: M * K bytes; q8ta_quantize_conv2d_transposed:
+ *     N * IC * H_in * W_in bytes); q8ta_conv2d_transposed(_acc) and
+ *     q8ta_conv2d(_acc) take, on their implicit-GEMM path, an NHWC copy of
+ *     the input inside a zero-point border plus 4 * stride_h * stride_w * OC
+ *     bytes of weight sums, and on the transposed conv's tiled path a
+ *     channel-blocked copy of the input (N * H_in * ceil(IC/16) * W_in * 16
+ *     bytes).  The default matrix-core kernels of q8ta_linear and
+ *     q8ta_conv2d_transposed take none.  The library keeps up to 4 such
+ *     buffers per device and holds them until the process ends.  Taking one
+ *     never blocks the host: a buffer last used on another stream is ordered
+ *     after that use with hipStreamWaitEvent, and one that is too small is
+ *     replaced in stream order (hipFreeAsync / hipMallocAsync on `stream`).
+ *     When all 4 are in use, under graph capture and above 256 MiB a call
+ *     takes its own stream-ordered allocation instead.  A failed allocation
+ *     returns Q8TA_ERR_HIP.
+ *   - Sizes: element counts up to 2^40 per tensor (the kernels address in
+ *     64 bits; a row length K of the linear below 2^31).
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns after the launch; results are visible to later work on that
  *     stream.  Calls are reentrant (several host threads may call at once)
- *     and keep no state between calls except the cached workspaces.
+ *     and keep no state between calls except the cached workspaces and the
+ *     kernel choice of q8ta_select_kernel.
  *   - Scales are passed as double.  The library forms every reciprocal as
  *     (float)(1.0 / scale) in double on the host ([QPT] commit message) and
  *     uses (float)scale for a scale that multiplies.
@@ -68,6 +75,18 @@ typedef enum q8ta_status {
 /* Message for the last non-OK status returned on the calling thread
  * (a static or thread-local string; never NULL). */
 const char* q8ta_last_error(void);
+
+/* Kernel-family choice, for testing and tuning; callers of the ops never need
+ * it.  Forces one kernel family of an op where the shape allows it (shapes
+ * that family cannot take keep the default choice); results are bit-identical
+ * whichever kernel runs.  Process-wide: applies to calls made after it returns.
+ *   op "linear":            kernel "default" | "generic" (the shape-general
+ *                           kernel instead of the GEMV / matrix-core GEMM)
+ *   op "conv2d_transposed": "default" | "mfma" | "igemm" | "tiled" | "generic"
+ *   op "conv2d":            "default" | "mfma" | "igemm" | "generic"
+ * Returns Q8TA_ERR_NULL for a NULL name and Q8TA_ERR_UNSUPPORTED for an unknown
+ * op or kernel name (the choice is then unchanged).  Host-only, no HIP call. */
+q8ta_status q8ta_select_kernel(const char* op, const char* kernel);
 
 /* ---------------------------------------------------------------------------
  * [QPT] commit message (Solution / Implementation):
@@ -180,6 +199,7 @@ q8ta_status q8ta_quantize_linear_dq(const float* x, int64_t M, int64_t K,
                                     double output_scale, int64_t output_zero_point,
                                     const char* activation, float* out,
                                     hipStream_t stream);
+
 
 /* ---------------------------------------------------------------------------
  * Precomputed weight sums (opt-in).  [LIN] Constraints (1): the zero-point

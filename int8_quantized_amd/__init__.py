@@ -43,6 +43,7 @@ _S = ctypes.c_char_p
 # argument types of every exported entry point, in declaration order
 SIGNATURES = {
     "q8ta_last_error": ([], ctypes.c_char_p),
+    "q8ta_select_kernel": ([_S, _S], ctypes.c_int),
     "q8ta_quantize_per_tensor": ([_P, _P, _I64, _DBL, _I64, _P], ctypes.c_int),
     "q8ta_dequantize_per_tensor": ([_P, _P, _I64, _DBL, _I64, _P], ctypes.c_int),
     "q8ta_linear": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S, _P, _P],
@@ -112,6 +113,12 @@ def q8ta_last_error() -> str:
 def _check(status: int):
     if status != Q8TA_OK:
         raise Q8taError(status, q8ta_last_error())
+
+
+def q8ta_select_kernel(op: str, kernel: str) -> None:
+    """Force one kernel family of ``op`` ("linear", "conv2d_transposed",
+    "conv2d") where the shape allows it; "default" restores the normal choice."""
+    _check(lib().q8ta_select_kernel(op.encode(), kernel.encode()))
 
 
 def _torch():

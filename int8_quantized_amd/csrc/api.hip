@@ -40,6 +40,7 @@ q8ta_status hip_status(hipError_t e, const char* what) {
 bool scale_ok(double s) { return std::isfinite(s) && s > 0.0; }
 bool zp_ok(int64_t z) { return z >= -128 && z <= 127; }
 
+// Tensors up to 2^40 elements: every kernel forms its addresses in 64 bits.
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
 // Reciprocal of a scale as the quantize page defines it: divide in double,
@@ -160,26 +161,38 @@ hipError_t pool_alloc(void** p, size_t bytes, hipStream_t s) {
   return hipMallocAsync(p, bytes, s);
 }
 
-constexpr int kWsDepth = 4;                          // nested acquisitions per stream
+constexpr int kWsSlots = 4;                          // cached buffers per device
 constexpr size_t kWsCachedMax = (size_t)256 << 20;   // larger requests use the pool
 constexpr size_t kWsGrain = (size_t)1 << 20;
 
+// A cached workspace buffer.  While `busy` it belongs to one call (between its
+// workspace_acquire and workspace_release); `done` is recorded on that call's
+// stream at release, after the call's kernels, so that the next holder --
+// on any stream -- is ordered after them.
 struct WsSlot {
   void* ptr = nullptr;
   size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  bool busy = false;
 };
-struct WsStream {
-  WsSlot slot[kWsDepth];
-  int depth = 0;
+struct WsDevice {
+  WsSlot slot[kWsSlots];
 };
 
-// Held from a cached acquisition to its release, so that no other thread
-// regrows a buffer between a call's launches.
-std::recursive_mutex g_ws_mu;
-std::map<std::pair<int, uintptr_t>, WsStream> g_ws;
+// Guards the slot tables only (lookups and flag updates); never held across
+// a HIP call that waits or launches.
+std::mutex g_ws_mu;
+std::map<int, WsDevice> g_ws;
 
 }  // namespace
 
+// Takes a cached buffer of at least `bytes` for stream s without blocking the
+// host: a buffer last used on another stream (or by a stream since destroyed)
+// is ordered after that use with hipStreamWaitEvent; one that is too small is
+// freed and replaced in stream order (hipFreeAsync / hipMallocAsync on s, after
+// that wait), so work already queued keeps the memory it was given.  When every
+// slot is taken, under graph capture and for requests above 256 MiB the call
+// gets its own stream-ordered allocation, freed by workspace_release.
 hipError_t workspace_acquire(void** p, size_t bytes, hipStream_t s) {
   *p = nullptr;
   int dev = 0;
@@ -189,74 +202,101 @@ hipError_t workspace_acquire(void** p, size_t bytes, hipStream_t s) {
   e = hipStreamIsCapturing(s, &cap);
   if (e != hipSuccess) return e;
   if (cap != hipStreamCaptureStatusNone || bytes > kWsCachedMax) return pool_alloc(p, bytes, s);
-  g_ws_mu.lock();
-  WsStream& ws = g_ws[{dev, (uintptr_t)s}];
-  if (ws.depth >= kWsDepth) {
-    g_ws_mu.unlock();
-    return pool_alloc(p, bytes, s);
-  }
-  WsSlot& sl = ws.slot[ws.depth];
-  if (sl.bytes < bytes) {
-    if (sl.ptr) {
-      // earlier calls on this stream may still read the old buffer
-      e = hipStreamSynchronize(s);
-      if (e == hipSuccess) e = hipFree(sl.ptr);
-      if (e != hipSuccess) {
-        g_ws_mu.unlock();
-        return e;
-      }
-      sl = WsSlot{};
+
+  WsSlot* sl = nullptr;
+  WsSlot mine;
+  {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    WsDevice& d = g_ws[dev];
+    // the smallest free buffer that fits, else the largest free one (to grow)
+    for (WsSlot& c : d.slot) {
+      if (c.busy) continue;
+      if (!sl) { sl = &c; continue; }
+      const bool c_fits = c.bytes >= bytes, s_fits = sl->bytes >= bytes;
+      if (c_fits ? (!s_fits || c.bytes < sl->bytes) : (!s_fits && c.bytes > sl->bytes)) sl = &c;
     }
-    const size_t want = (bytes + kWsGrain - 1) / kWsGrain * kWsGrain;
-    e = hipMalloc(&sl.ptr, want);
-    if (e != hipSuccess) {
-      sl = WsSlot{};
-      g_ws_mu.unlock();
-      return e;
+    if (sl) {
+      sl->busy = true;
+      mine = *sl;
     }
-    sl.bytes = want;
   }
-  ++ws.depth;
-  *p = sl.ptr;
-  return hipSuccess;   // g_ws_mu stays locked until workspace_release
+  if (!sl) return pool_alloc(p, bytes, s);
+
+  if (!mine.done) e = hipEventCreateWithFlags(&mine.done, hipEventDisableTiming);
+  if (e == hipSuccess && mine.ptr) {
+    const hipError_t q = hipEventQuery(mine.done);   // never recorded: hipSuccess
+    if (q == hipErrorNotReady) e = hipStreamWaitEvent(s, mine.done, 0);
+    else if (q != hipSuccess) e = q;
+  }
+  if (e == hipSuccess && mine.bytes < bytes) {
+    if (mine.ptr) e = hipFreeAsync(mine.ptr, s);
+    mine.ptr = nullptr;
+    mine.bytes = 0;
+    if (e == hipSuccess) {
+      const size_t want = (bytes + kWsGrain - 1) / kWsGrain * kWsGrain;
+      e = pool_alloc(&mine.ptr, want, s);
+      if (e == hipSuccess) mine.bytes = want;
+      else mine.ptr = nullptr;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    sl->ptr = mine.ptr;
+    sl->bytes = mine.bytes;
+    sl->done = mine.done;
+    if (e != hipSuccess) sl->busy = false;
+  }
+  if (e != hipSuccess) return e;
+  *p = mine.ptr;
+  return hipSuccess;
 }
 
+// Returns a buffer from workspace_acquire once the call's kernels are queued
+// on s: a cached one is marked free after its event is recorded on s, any
+// other is freed in stream order.
 hipError_t workspace_release(void* p, hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  WsSlot* sl = nullptr;
+  hipEvent_t done = nullptr;
   {
-    std::lock_guard<std::recursive_mutex> g(g_ws_mu);
-    auto it = g_ws.find({dev, (uintptr_t)s});
-    if (it != g_ws.end() && it->second.depth > 0 &&
-        it->second.slot[it->second.depth - 1].ptr == p) {
-      --it->second.depth;
-      g_ws_mu.unlock();   // the lock taken by workspace_acquire
-      return hipSuccess;
-    }
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    auto it = g_ws.find(dev);
+    if (it != g_ws.end())
+      for (WsSlot& c : it->second.slot)
+        if (c.busy && c.ptr == p) {
+          sl = &c;
+          done = c.done;
+          break;
+        }
   }
-  return hipFreeAsync(p, s);
+  if (!sl) return p ? hipFreeAsync(p, s) : hipSuccess;
+  e = hipEventRecord(done, s);
+  std::lock_guard<std::mutex> g(g_ws_mu);
+  sl->busy = false;
+  return e;
 }
 
-// Q8TA_GEMM_PATH = dot4 skips the matrix-core GEMM where both apply (used by
-// the tests to reach the v_dot4 kernel).
+// Kernel-family choice forced through q8ta_select_kernel (0 = default).
+std::atomic<char> g_sel_linear{0}, g_sel_deconv{0}, g_sel_conv{0};
+
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
+  if (g_sel_linear.load(std::memory_order_relaxed) == 'g') return launch_linear_generic(a, s);
   if (gemv_supported(a)) return launch_gemv(a, s);
-  const char* e = getenv("Q8TA_GEMM_PATH");
-  const bool no_mfma = e && e[0] == 'd';
-  if (!no_mfma && gemm_mfma_supported(a)) return launch_gemm_mfma(a, s);
-  if (gemm_dot4_supported(a)) return launch_gemm_dot4(a, s);
+  if (gemm_mfma_supported(a)) return launch_gemm_mfma(a, s);
   return launch_linear_generic(a, s);
 }
 
 // quantize_per_tensor -> linear with fp32 activations (a.xf): the M <= 4
-// kernel quantizes while it loads them; other shapes quantize into a
-// stream-ordered int8 workspace and take the usual path.
-hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s) {
+// kernel quantizes while it loads them; other shapes quantize into an int8
+// buffer of M * K bytes -- `staging` when given, else a workspace -- and
+// take the usual path.
+hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s, int8_t* staging) {
   if (gemv_supported(a)) return launch_gemv(a, s);
   const int64_t numel = a.M * a.K;
-  void* ws = nullptr;
-  hipError_t e = workspace_acquire(&ws, (size_t)numel, s);
+  void* ws = staging;
+  hipError_t e = staging ? hipSuccess : workspace_acquire(&ws, (size_t)numel, s);
   if (e != hipSuccess) return e;
   e = launch_quantize(a.xf, (int8_t*)ws, numel, a.inv_in, (float)a.izp, s);
   if (e == hipSuccess) {
@@ -264,19 +304,17 @@ hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s) {
     a.xf = nullptr;
     e = launch_linear(a, s);
   }
+  if (staging) return e;
   hipError_t f = workspace_release(ws, s);
   return e != hipSuccess ? e : f;
 }
 
-// Q8TA_DECONV_PATH = mfma | igemm | dot4 | generic forces one kernel family
-// where the shape allows it (used by the tests); unset, the matrix-core kernel
-// takes every shape it supports, then the implicit GEMM (three launches' worth
-// of fixed cost: input copy, then the GEMM) from about 2^28 multiply-adds,
-// then the direct tiled kernel.
-static char deconv_path() {
-  const char* e = getenv("Q8TA_DECONV_PATH");
-  return e ? e[0] : 0;
-}
+// Transposed conv: the matrix-core kernel takes every shape it supports, then
+// the implicit GEMM (three launches' worth of fixed cost: input copy, then the
+// GEMM) from about 2^28 multiply-adds, then the direct tiled kernel, then the
+// shape-general one.  q8ta_select_kernel can force one family ('m' matrix
+// cores, 'i' implicit GEMM, 't' tiled, 'g' generic) where the shape allows it.
+static char deconv_path() { return g_sel_deconv.load(std::memory_order_relaxed); }
 
 static bool deconv_wants_igemm(const DeconvArgs& a) {
   const char k = deconv_path();
@@ -316,11 +354,10 @@ hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
 
 // Forward conv: the matrix-core kernel (groups 1, stride 1, IC % 16 == 0),
 // the implicit GEMM on v_dot4 (groups 1, IC % 64 == 0), the depthwise kernel
-// (groups == IC == OC), or the shape-general kernel.  Q8TA_CONV_PATH = mfma |
-// igemm | generic forces one where the shape allows it (used by the tests).
+// (groups == IC == OC), or the shape-general kernel.  q8ta_select_kernel can
+// force one ('m', 'i', 'g') where the shape allows it.
 hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s) {
-  const char* e = getenv("Q8TA_CONV_PATH");
-  const char k = e ? e[0] : 0;
+  const char k = g_sel_conv.load(std::memory_order_relaxed);
   if ((k == 0 || k == 'm') && conv_mfma_supported(a)) return launch_conv_mfma(a, s);
   if ((k == 0 || k == 'i') && conv_igemm_supported(a)) return launch_conv_igemm(a, s);
   if (k == 'g') return launch_conv2d_generic(a, s);
@@ -333,6 +370,28 @@ hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s) {
 extern "C" {
 
 const char* q8ta_last_error(void) { return g_err; }
+
+q8ta_status q8ta_select_kernel(const char* op, const char* kernel) {
+  if (!op || !kernel) return fail(Q8TA_ERR_NULL, "q8ta_select_kernel: op and kernel must not be NULL");
+  struct Name { const char* name; char code; };
+  static const Name linear[] = {{"default", 0}, {"generic", 'g'}};
+  static const Name deconv[] = {{"default", 0}, {"mfma", 'm'}, {"igemm", 'i'}, {"tiled", 't'},
+                                {"generic", 'g'}};
+  static const Name conv[] = {{"default", 0}, {"mfma", 'm'}, {"igemm", 'i'}, {"generic", 'g'}};
+  const Name* tab = nullptr;
+  size_t n = 0;
+  std::atomic<char>* dst = nullptr;
+  if (strcmp(op, "linear") == 0) { tab = linear; n = 2; dst = &g_sel_linear; }
+  else if (strcmp(op, "conv2d_transposed") == 0) { tab = deconv; n = 5; dst = &g_sel_deconv; }
+  else if (strcmp(op, "conv2d") == 0) { tab = conv; n = 4; dst = &g_sel_conv; }
+  else return fail(Q8TA_ERR_UNSUPPORTED, "q8ta_select_kernel: unknown op \"%.64s\"", op);
+  for (size_t i = 0; i < n; ++i)
+    if (strcmp(kernel, tab[i].name) == 0) {
+      dst->store(tab[i].code, std::memory_order_relaxed);
+      return Q8TA_OK;
+    }
+  return fail(Q8TA_ERR_UNSUPPORTED, "q8ta_select_kernel: unknown kernel \"%.64s\" for %s", kernel, op);
+}
 
 q8ta_status q8ta_quantize_per_tensor(const float* x, int8_t* out, int64_t numel, double scale,
                                      int64_t zero_point, hipStream_t stream) {

@@ -477,10 +477,6 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
       FJ = 1;
     }
   }
-  if (const char* e = getenv("Q8TA_DECONV_FJ")) FJ = atoi(e);
-  if (const char* e = getenv("Q8TA_DECONV_FO")) FO = atoi(e);
-  if (FJ != 1 && FJ != 2 && FJ != 4) FJ = 4;
-  if (FO != 1 && FO != 2 && FO != 4) FO = 4;
   p.TJ = 16 * FJ;
   const int ocf = 16 * FO;
   p.WO = (int)((a.OC + ocf - 1) / ocf);
@@ -492,8 +488,6 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
   p.HC = ((c_hi - c_lo) + 3) / 4 * 4;
   p.OCols = sw * p.TJ;
   int wi_pref = small ? 1 : 4;   // small problems: more, smaller workgroups
-  if (const char* e = getenv("Q8TA_DECONV_WI")) wi_pref = atoi(e);
-  if (wi_pref < 1) wi_pref = 1;
   if (wi_pref * p.WO > 8) wi_pref = 8 / p.WO;
   for (int WI = wi_pref; WI >= 1; --WI) {
     p.WI = WI;
@@ -560,9 +554,9 @@ hipError_t launch_mfma(const DeconvArgs& a, hipStream_t s, bool forward) {
   if (!make_plan(a, p, FJ, FO, forward)) return hipErrorInvalidValue;
 #define Q8TA_DC(fj, fo) \
   if (FJ == fj && FO == fo) return launch_t<fj, fo>(a, p, s);
-  Q8TA_DC(1, 1) Q8TA_DC(1, 2) Q8TA_DC(1, 4)
-  Q8TA_DC(2, 1) Q8TA_DC(2, 2) Q8TA_DC(2, 4)
-  Q8TA_DC(4, 1) Q8TA_DC(4, 2) Q8TA_DC(4, 4)
+  Q8TA_DC(1, 1) Q8TA_DC(1, 2)
+  Q8TA_DC(2, 1) Q8TA_DC(2, 2)
+  Q8TA_DC(4, 1) Q8TA_DC(4, 2)
 #undef Q8TA_DC
   return hipErrorInvalidValue;
 }

@@ -12,10 +12,10 @@
 // A wave owns one image, one row residue rh with RQ consecutive phase rows
 // (output rows oh = rh + s_h*i), one column residue rw, 64 phase columns j
 // (one per lane: ow = rw + s_w*j) and OCB output channels; all its lanes share
-// the same taps.  Per tap and 16 input channels a lane loads, for each of its
-// RQ rows, the 16 bytes x[n, ic..ic+15, ih, iw] (each load instruction reads
-// 64 consecutive columns of one channel plane), packs them into 4 dwords, and
-// accumulates v_dot4 against the weights w[oc, tap, ic..ic+15], which are the
+// the same taps.  The input is first relaid out into blocks of 16 channels per
+// pixel (k_nchw_to_blocked16); per tap and 16 input channels a lane then loads,
+// for each of its RQ rows, the 16 bytes x[n, ic..ic+15, ih, iw] in one 16-byte
+// load and accumulates v_dot4 against the weights w[oc, tap, ic..ic+15], which are the
 // same for all lanes, come through the scalar unit and are reused RQ times.  A tap that falls outside the input
 // reads the zero point, so with sum w taken over all of the phase's taps the
 // result sum x*w - izp * sum w equals the gather (the zero-point-filled form of
@@ -34,127 +34,6 @@ constexpr int kThreads = 256;
 // Weights are only read by these kernels: reading them through the constant
 // address space lets the compiler fetch wave-uniform words with scalar loads.
 typedef const __attribute__((address_space(4))) int32_t* cwptr;
-
-template <int OCB, int RQ>
-__global__ __launch_bounds__(kThreads) void k_deconv_dot4(DeconvArgs a, Phases p) {
-  const int lane = threadIdx.x & 63;
-  // wave index, made explicitly wave-uniform so that everything derived from
-  // it (taps, weight addresses) lives in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-  const int ob = (int)(wid % p.ocb);  wid /= p.ocb;
-  const int jb = (int)(wid % p.jb);   wid /= p.jb;
-  const int sw = (int)a.sw, sh = (int)a.sh;
-  const int rw = (int)(wid % sw);     wid /= sw;
-  const int ib = (int)(wid % p.ib);   wid /= p.ib;
-  const int rh = (int)(wid % sh);     wid /= sh;
-  const int64_t n = wid;
-  if (n >= a.N) return;
-  const int i0 = ib * RQ;               // first phase row; output rows rh + sh*(i0 + q)
-  const int j = jb * 64 + lane;
-  const int ow = rw + sw * j;
-  const int oc0 = ob * OCB;
-  const int IC = (int)a.IC, H_in = (int)a.H_in, W_in = (int)a.W_in;
-  const int64_t plane = (int64_t)H_in * W_in;
-  const int8_t* xn = a.x + n * IC * plane;
-  const uint32_t zp4 = 0x01010101u * ((uint32_t)a.izp & 0xffu);
-  const int nth = p.nth[rh], ntw = p.ntw[rw];
-
-  // sum of the phase's weights per output channel (lanes split the channels)
-  int32_t wsum[OCB];
-#pragma unroll
-  for (int o = 0; o < OCB; ++o) wsum[o] = 0;
-  for (int th = 0; th < nth; ++th) {
-    for (int tw = 0; tw < ntw; ++tw) {
-      const int64_t tapoff = (int64_t)(p.thk[rh][th] * a.Kw + p.twk[rw][tw]) * IC;
-      for (int ic = lane * 4; ic < IC; ic += 256) {
-#pragma unroll
-        for (int o = 0; o < OCB; ++o) {
-          const int oc = oc0 + o;
-          const int32_t wv = oc < a.OC
-              ? *reinterpret_cast<const int32_t*>(a.w + (int64_t)oc * a.ldw + tapoff + ic) : 0;
-          wsum[o] = __builtin_amdgcn_sdot4(wv, 0x01010101, wsum[o], false);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 0; o < OCB; ++o) wsum[o] = wave_total(wsum[o]);
-
-  int32_t acc[RQ][OCB];
-#pragma unroll
-  for (int q = 0; q < RQ; ++q)
-#pragma unroll
-    for (int o = 0; o < OCB; ++o) acc[q][o] = 0;
-  const int64_t ldw4 = a.ldw / 4;
-  for (int th = 0; th < nth; ++th) {
-    const int kh = p.thk[rh][th];
-    const int dh = p.thd[rh][th];
-    for (int tw = 0; tw < ntw; ++tw) {
-      const int kw = p.twk[rw][tw];
-      const int iw = j + p.twd[rw][tw];
-      const bool col_ok = iw >= 0 && iw < W_in;
-      const int8_t* xq[RQ];
-      bool ok[RQ];
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        const int ih = i0 + q + dh;
-        ok[q] = col_ok && ih >= 0 && ih < H_in;
-        xq[q] = xn + (int64_t)(ok[q] ? ih : 0) * W_in + (ok[q] ? iw : 0);
-      }
-      const int8_t* wt = a.w + (int64_t)oc0 * a.ldw + (int64_t)(kh * a.Kw + kw) * IC;
-      for (int ic = 0; ic < IC; ic += 16) {
-        uint32_t xv[RQ][4];
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int c = ic + 4 * g + t;
-              const uint32_t by = (c < IC) ? (uint32_t)(uint8_t)xq[q][(int64_t)c * plane] : 0u;
-              v |= by << (8 * t);
-            }
-            xv[q][g] = ok[q] ? v : zp4;
-          }
-        }
-        const cwptr wc = (cwptr)(wt + ic);
-#pragma unroll
-        for (int o = 0; o < OCB; ++o) {
-          if (oc0 + o < a.OC) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int32_t wv = (ic + 4 * g < IC) ? wc[o * ldw4 + g] : 0;
-#pragma unroll
-              for (int q = 0; q < RQ; ++q)
-                acc[q][o] = __builtin_amdgcn_sdot4((int)xv[q][g], wv, acc[q][o], false);
-            }
-          }
-        }
-      }
-    }
-  }
-  if (ow >= a.W_out) return;
-#pragma unroll
-  for (int q = 0; q < RQ; ++q) {
-    const int oh = rh + sh * (i0 + q);
-    if (oh >= a.H_out) break;
-#pragma unroll
-    for (int o = 0; o < OCB; ++o) {
-      const int oc = oc0 + o;
-      if (oc >= a.OC) break;
-      const int32_t c = acc[q][o] - a.izp * wsum[o];
-      const int64_t idx = (((int64_t)n * a.OC + oc) * a.H_out + oh) * a.W_out + ow;
-      if (a.acc) {
-        a.acc[idx] = c;
-      } else {
-        const float b = a.bias ? a.bias[oc] : 0.0f;
-        a.out[idx] = (int8_t)requant(c, a.wscale[oc], b, a.rq);
-      }
-    }
-  }
-}
 
 // Input relayout for the blocked path: x NCHW -> xb[n][h][g][w][16] with
 // g = ic / 16 (channels past IC are zero).  One thread per (n, h, g, w): it
@@ -192,9 +71,9 @@ __global__ __launch_bounds__(kThreads) void k_nchw_to_blocked16(const int8_t* __
   *reinterpret_cast<v4i*>(xb + t * 16) = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
 }
 
-// Main kernel of the blocked path: same wave layout as k_deconv_dot4 with one
-// phase row per wave, but the 16 channels of a pixel come in one 16-byte load
-// from xb (lanes read consecutive 16-byte chunks).  The inner loop is
+// Main kernel: the wave layout above with RQ phase rows per wave; the 16
+// channels of a pixel come in one 16-byte load from xb (lanes read
+// consecutive 16-byte chunks).  The inner loop is
 // branch-free: weight rows past OC are clamped to OC - 1 (their results are
 // never stored), the OCB weight quads of a 16-channel group are requested
 // together through the scalar unit, and the next group's activations are
@@ -375,17 +254,6 @@ bool make_phases(const DeconvArgs& a, Phases& p) {
 namespace {
 
 template <int OCB, int RQ>
-hipError_t launch_t(const DeconvArgs& a, Phases p, hipStream_t s) {
-  p.ocb = (int)((a.OC + OCB - 1) / OCB);
-  const int64_t Hp = (a.H_out + a.sh - 1) / a.sh;
-  p.ib = (int)((Hp + RQ - 1) / RQ);
-  const int64_t waves = (int64_t)p.ocb * p.jb * a.sw * p.ib * a.sh * a.N;
-  const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((k_deconv_dot4<OCB, RQ>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a, p);
-  return hipGetLastError();
-}
-
-template <int OCB, int RQ>
 hipError_t launch_blocked(const DeconvArgs& a, Phases p, hipStream_t s) {
   p.ocb = (int)((a.OC + OCB - 1) / OCB);
   const int64_t Hp = (a.H_out + a.sh - 1) / a.sh;
@@ -428,32 +296,14 @@ bool deconv_dot4_supported(const DeconvArgs& a) {
   return (waves + 3) / 4 < ((int64_t)1 << 31);
 }
 
-// Default: the blocked path (input relayout into a stream-ordered workspace,
-// then 8 output channels x 1 phase row per wave).  Q8TA_DECONV_LAYOUT=nchw
-// selects the direct path (no workspace); Q8TA_DECONV_OCB = 8 | 16 and
-// Q8TA_DECONV_RQ = 1 | 2 | 4 choose the tile (16 x 4 is not built: it needs
-// more than 256 vector registers).
+// The blocked path: the input relaid out into channel blocks of 16 in a
+// stream-ordered workspace, then 8 output channels x 1 phase row per wave.
+// (The direct NCHW path without a workspace and tiles of 16 channels or 2-4
+// phase rows per wave measured no faster and were removed.)
 hipError_t launch_deconv_dot4(const DeconvArgs& a, hipStream_t s) {
   Phases p;
   if (!make_phases(a, p)) return hipErrorInvalidValue;
-  int ocb = 8, rq = 1;
-  bool blocked = true;
-  if (const char* e = getenv("Q8TA_DECONV_OCB")) ocb = atoi(e);
-  if (const char* e = getenv("Q8TA_DECONV_RQ")) rq = atoi(e);
-  if (const char* e = getenv("Q8TA_DECONV_LAYOUT")) blocked = (e[0] != 'n');
-  if (blocked) {
-    if (ocb == 16) return rq == 2 ? launch_blocked<16, 2>(a, p, s) : launch_blocked<16, 1>(a, p, s);
-    if (rq == 2) return launch_blocked<8, 2>(a, p, s);
-    if (rq == 4) return launch_blocked<8, 4>(a, p, s);
-    return launch_blocked<8, 1>(a, p, s);
-  }
-  if (ocb == 8) {
-    if (rq == 1) return launch_t<8, 1>(a, p, s);
-    if (rq == 2) return launch_t<8, 2>(a, p, s);
-    return launch_t<8, 4>(a, p, s);
-  }
-  if (rq == 1) return launch_t<16, 1>(a, p, s);
-  return launch_t<16, 2>(a, p, s);
+  return launch_blocked<8, 1>(a, p, s);
 }
 
 }  // namespace q8ta

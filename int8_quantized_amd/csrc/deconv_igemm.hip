@@ -405,25 +405,16 @@ hipError_t launch_igemm_t(const DeconvArgs& a, const Phases& p, int osh, int osw
   return e != hipSuccess ? e : f;
 }
 
-int igemm_layout() {
-  int gm = 4;
-  if (const char* e = getenv("Q8TA_IGEMM_CFG"))
-    if (const char* xx = strchr(e, 'x')) gm = atoi(xx + 1);
-  return gm;
-}
-
 }  // namespace
 
 // NHWC copy of the input inside its zero-point border and sum w per (phase,
 // channel) in one stream-ordered workspace, then the implicit GEMM over every
-// phase.  Q8TA_IGEMM_CFG = "4x4" (32 x 32 wave tile, default) or "4x8" (64
-// pixels x 16 channels).
+// phase (4 x 4 groups of 4 lanes: a 32 x 32 wave tile).
 hipError_t launch_deconv_igemm(const DeconvArgs& a, hipStream_t s) {
   Phases p;
   if (!make_phases(a, p)) return hipErrorInvalidValue;
   const int sh = (int)a.sh, sw = (int)a.sw;
-  return igemm_layout() == 8 ? launch_igemm_t<4, 8>(a, p, sh, sw, 1, 1, s)
-                             : launch_igemm_t<4, 4>(a, p, sh, sw, 1, 1, s);
+  return launch_igemm_t<4, 4>(a, p, sh, sw, 1, 1, s);
 }
 
 // The forward conv through the same kernels: one phase, every tap.
@@ -431,8 +422,7 @@ hipError_t launch_conv_igemm(const DeconvArgs& a, hipStream_t s) {
   Phases p;
   if (!make_conv_phases(a, p)) return hipErrorInvalidValue;
   const int sh = (int)a.sh, sw = (int)a.sw;
-  return igemm_layout() == 8 ? launch_igemm_t<4, 8>(a, p, 1, 1, sh, sw, s)
-                             : launch_igemm_t<4, 4>(a, p, 1, 1, sh, sw, s);
+  return launch_igemm_t<4, 4>(a, p, 1, 1, sh, sw, s);
 }
 
 }  // namespace q8ta

@@ -267,31 +267,19 @@ __global__ __launch_bounds__(C::NT, 1) void k_gemm(LinearArgs a, int tiles_m, in
   }
 }
 
-using CfgL = Cfg<256, 256, 64, 2, 2>;   // 128x128 per wave
 using CfgM = Cfg<128, 128, 64, 2, 2>;   // 64x64 per wave
 using CfgS = Cfg<128, 64, 64, 2, 1>;    // 64x64 per wave, 2 waves
-using CfgK = Cfg<128, 128, 128, 2, 2>;  // 64x64 per wave, 128-byte K steps
-using CfgW = Cfg<256, 128, 64, 4, 2>;   // 64x64 per wave, 8 waves
-using CfgV = Cfg<256, 128, 128, 4, 2>;  // 64x64 per wave, 8 waves, 128-byte K steps
-using CfgU = Cfg<128, 256, 64, 2, 4>;   // 64x64 per wave, 8 waves
-using CfgQ = Cfg<256, 128, 64, 2, 2>;   // 128x64 per wave
-using CfgR = Cfg<128, 128, 64, 2, 1>;   // 64x128 per wave, 2 waves
 
 template <class C>
 hipError_t launch_cfg(const LinearArgs& a, hipStream_t s) {
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
   const int T = tiles_m * tiles_n;
-  // The tiles the default choice uses also come in a form that takes the
-  // caller's row sums; the others form their own (same result).
-  constexpr bool pre_built = std::is_same<C, CfgV>::value || std::is_same<C, CfgM>::value ||
-                             std::is_same<C, CfgS>::value;
-  if constexpr (pre_built) {
-    if (a.wsum_pre) {
-      hipLaunchKernelGGL((k_gemm<C, true>), dim3((unsigned)T), dim3(C::NT), 0, s, a, tiles_m,
-                         tiles_n);
-      return hipGetLastError();
-    }
+  // With the caller's row sums the K loop drops its v_dot4 (same result).
+  if (a.wsum_pre) {
+    hipLaunchKernelGGL((k_gemm<C, true>), dim3((unsigned)T), dim3(C::NT), 0, s, a, tiles_m,
+                       tiles_n);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((k_gemm<C, false>), dim3((unsigned)T), dim3(C::NT), 0, s, a, tiles_m, tiles_n);
   return hipGetLastError();
@@ -312,41 +300,17 @@ bool gemm_mfma_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-// Tile choice (measured on 2048 x 4096 x 11008, fused dequantize): for
-// problems that fill the GPU at least once with 256 x 128 tiles and have a
-// long K, the 32x32x32 kernel of gemm_mx.hip with two workgroups per CU and
-// the store-first K loop ('w': 125.7-126.4 us against 129.5-130.5 us for
-// 'y', loads two steps ahead with the LDS write at the end of each step, and
-// 131-135 us for this file's 256 x 128 tile 'V'); otherwise the medium tile,
-// or the small one for few rows.  The large tile of this file (128 x 128 per
-// wave, loops the compiler leaves rolled) keeps its accumulators in scratch
-// memory; the direct-to-LDS 32x32x32 kernel of gemm_dl.hip ('G') measured
-// 150 us, the 32x32x32 variant of the 256 x 128 tile in gemm32.hip ('X')
-// 146 us.  Q8TA_GEMM_CFG (one letter of LMSKWVUQRGXYZPyzw) overrides the
-// choice.
+// Tile choice: problems that fill the GPU at least once with 256 x 128 tiles
+// and have a long K take the 32x32x32 kernel of gemm_mx.hip (two workgroups
+// per CU, store-first K loop: 125.7-126.4 us on 2048 x 4096 x 11008 with the
+// fused dequantize, against 131-135 us for a 256 x 128 tile of this file);
+// the rest the 128 x 128 tile, or the 128 x 64 tile for few rows.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
-  const char* e = getenv("Q8TA_GEMM_CFG");
-  char pick = 0;
-  if (e && strchr("LMSKWVUQRGXYZPyzw", e[0])) pick = e[0];
-  if (!pick) {
-    const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
-    const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    pick = (tv >= 256 && a.K >= 1024) ? 'w' : (tm >= 256 || a.M > 64) ? 'M' : 'S';
-  }
-  if (pick == 'G') return gemm_dl_supported(a) ? launch_gemm_dl(a, s) : launch_cfg<CfgM>(a, s);
-  if (pick == 'X') return launch_gemm32(a, s);
-  if (strchr("YZPyzw", pick)) return launch_gemm_mx(a, pick, s);
-  switch (pick) {
-    case 'L': return launch_cfg<CfgL>(a, s);
-    case 'M': return launch_cfg<CfgM>(a, s);
-    case 'K': return launch_cfg<CfgK>(a, s);
-    case 'W': return launch_cfg<CfgW>(a, s);
-    case 'V': return launch_cfg<CfgV>(a, s);
-    case 'U': return launch_cfg<CfgU>(a, s);
-    case 'Q': return launch_cfg<CfgQ>(a, s);
-    case 'R': return launch_cfg<CfgR>(a, s);
-    default: return launch_cfg<CfgS>(a, s);
-  }
+  const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
+  const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (tv >= 256 && a.K >= 1024) return launch_gemm_mx(a, s);
+  if (tm >= 256 || a.M > 64) return launch_cfg<CfgM>(a, s);
+  return launch_cfg<CfgS>(a, s);
 }
 
 }  // namespace q8ta

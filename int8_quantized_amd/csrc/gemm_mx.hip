@@ -447,16 +447,8 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   });
 }
 
-// Two workgroups per CU: 256 x 128 tiles, 128 x 64 per wave, 64-byte K steps.
-using MxY = MxCfg<256, 128, 64, 2, 2, 2>;
-// One workgroup per CU: same tile, 128-byte K steps.
-using MxZ = MxCfg<256, 128, 128, 2, 2, 1>;
-// Two workgroups per CU, 64 x 128 per wave (X-heavy wave tile).
-using MxP = MxCfg<128, 256, 64, 2, 2, 2>;
-// Loads issued two K steps ahead.
-using MxY2 = MxCfg<256, 128, 64, 2, 2, 2, 2>;
-using MxZ2 = MxCfg<256, 128, 128, 2, 2, 1, 2>;
-// Store-first K loop.
+// Two workgroups per CU: 256 x 128 tiles, 128 x 64 per wave, 64-byte K steps,
+// store-first K loop (loads three steps ahead).
 using MxY3 = MxCfg<256, 128, 64, 2, 2, 2, 3>;
 
 template <class C, bool PRE>
@@ -491,15 +483,6 @@ hipError_t launch_mx(const LinearArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// cfg: 'Y' (two workgroups per CU, 64-byte K steps), 'Z' (one workgroup per
-// CU, 128-byte K steps), 'P' (64 x 128 per wave).
-hipError_t launch_gemm_mx(const LinearArgs& a, char cfg, hipStream_t s) {
-  if (cfg == 'Z') return launch_mx<MxZ>(a, s);
-  if (cfg == 'y') return launch_mx<MxY2>(a, s);
-  if (cfg == 'z') return launch_mx<MxZ2>(a, s);
-  if (cfg == 'w') return launch_mx<MxY3>(a, s);
-  if (cfg == 'P') return launch_mx<MxP>(a, s);
-  return launch_mx<MxY>(a, s);
-}
+hipError_t launch_gemm_mx(const LinearArgs& a, hipStream_t s) { return launch_mx<MxY3>(a, s); }
 
 }  // namespace q8ta

@@ -186,7 +186,6 @@ template <int MR>
 hipError_t launch_mr(const LinearArgs& a, hipStream_t s, int rows) {
   switch (rows) {
     case 1: return launch_rows<MR, 1>(a, s);
-    case 2: return launch_rows<MR, 2>(a, s);
     default: return launch_rows<MR, 4>(a, s);
   }
 }
@@ -200,14 +199,13 @@ bool gemv_supported(const LinearArgs& a) {
          aligned16(a.w);
 }
 
-// rows: weight rows per wave (Q8TA_GEMV_ROWS overrides the default of 1: on
-// 1 x 4096 x 4096, 4.7-4.9 us against 4.9-5.2 us for 2 rows and 6.1 for 4).
-// The fp32 form takes 4 rows for M > 1, where each workgroup's quantize pass
-// grows with M: on 4 x 4096 x 4096, 7.1 us against 7.2 for 2 rows and 9.7
-// for 1 (M = 1: 5.3 us with 1 row, 6.0 with 4).
+// rows: weight rows per wave.  One for int8 activations (1 x 4096 x 4096:
+// 4.7-4.9 us against 4.9-5.2 us for 2 rows and 6.1 for 4).  The fp32 form
+// takes 4 rows for M > 1, where each workgroup's quantize pass grows with M:
+// on 4 x 4096 x 4096, 7.1 us against 7.2 for 2 rows and 9.7 for 1 (M = 1:
+// 5.3 us with 1 row, 6.0 with 4).
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) {
-  int rows = (a.xf && a.M > 1) ? 4 : 1;
-  if (const char* e = getenv("Q8TA_GEMV_ROWS")) rows = atoi(e);
+  const int rows = (a.xf && a.M > 1) ? 4 : 1;
   switch (a.M) {
     case 1: return launch_mr<1>(a, s, rows);
     case 2: return launch_mr<2>(a, s, rows);

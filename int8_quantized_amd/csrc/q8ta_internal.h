@@ -180,7 +180,7 @@ struct LinearArgs {
   float inv_in = 0.0f;
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
-hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s);
+hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s, int8_t* staging = nullptr);
 
 struct DeconvArgs {
   const int8_t* x;
@@ -230,13 +230,9 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 bool gemv_supported(const LinearArgs& a);
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s);
 bool gemm_mfma_supported(const LinearArgs& a);
-hipError_t launch_gemm_dot4(const LinearArgs& a, hipStream_t s);
-bool gemm_dot4_supported(const LinearArgs& a);
-hipError_t launch_gemm_dl(const LinearArgs& a, hipStream_t s);
-bool gemm_dl_supported(const LinearArgs& a);
-// 32x32x32 matrix-core GEMM (same operand requirements as launch_gemm_mfma).
-hipError_t launch_gemm32(const LinearArgs& a, hipStream_t s);
-hipError_t launch_gemm_mx(const LinearArgs& a, char cfg, hipStream_t s);
+// 32x32x32 matrix-core GEMM for large problems (same operand requirements as
+// launch_gemm_mfma, which chooses it).
+hipError_t launch_gemm_mx(const LinearArgs& a, hipStream_t s);
 int64_t prepacked_bytes(int64_t N, int64_t K);
 hipError_t launch_prepack(const int8_t* w, int64_t N, int64_t K, int8_t* packed, hipStream_t s);
 hipError_t launch_gemm_pk(const LinearArgs& a, hipStream_t s);

@@ -371,3 +371,21 @@ def test_quantize_linear_binding_checks_shapes_before_the_call():
                torch.zeros((4, 32), dtype=dt))
         with pytest.raises(ValueError, match="device tensor"):
             fn(x, 0.02, 3, w, None, s, None, 0.5, -5, "none", torch.zeros((4, 32), dtype=dt))
+
+
+def test_select_kernel_names():
+    """q8ta_select_kernel accepts the documented op and kernel names, rejects
+    others (leaving the choice unchanged) and makes no HIP call."""
+    lib = q8.lib()
+    for op, kernels in (("linear", ("generic",)),
+                        ("conv2d_transposed", ("mfma", "igemm", "tiled", "generic")),
+                        ("conv2d", ("mfma", "igemm", "generic"))):
+        for k in kernels + ("default",):
+            _st(lib.q8ta_select_kernel(op.encode(), k.encode()), q8.Q8TA_OK)
+        _st(lib.q8ta_select_kernel(op.encode(), b"dot4"), q8.Q8TA_ERR_UNSUPPORTED, "unknown kernel")
+    _st(lib.q8ta_select_kernel(b"gemm", b"default"), q8.Q8TA_ERR_UNSUPPORTED, "unknown op")
+    _st(lib.q8ta_select_kernel(None, b"default"), q8.Q8TA_ERR_NULL)
+    _st(lib.q8ta_select_kernel(b"linear", None), q8.Q8TA_ERR_NULL)
+    q8.q8ta_select_kernel("linear", "default")
+    with pytest.raises(q8.Q8taError, match="unknown kernel"):
+        q8.q8ta_select_kernel("conv2d", "tiled")

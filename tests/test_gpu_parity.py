@@ -42,22 +42,18 @@ def host(t):
     return t.cpu().numpy()
 
 
-class env:
-    """Temporarily set an environment variable read by the library per call."""
+class kernel:
+    """Force one kernel family of an op (q8ta_select_kernel) inside a block;
+    "default" (or "") keeps the library's own choice."""
 
-    def __init__(self, **kw):
-        self.kw = kw
+    def __init__(self, op, name):
+        self.op, self.name = op, name or "default"
 
     def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.kw}
-        os.environ.update({k: str(v) for k, v in self.kw.items()})
+        q8.q8ta_select_kernel(self.op, self.name)
 
     def __exit__(self, *exc):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        q8.q8ta_select_kernel(self.op, "default")
 
 
 # ============================================================================ quantize
@@ -74,14 +70,13 @@ def test_quantize_ragged(numel, offset):
     np.testing.assert_array_equal(host(ob[offset:]), oracle.quantize_per_tensor(x, 0.02, 3))
 
 
-@pytest.mark.parametrize("unroll", ["2", "4", "8"])
-@pytest.mark.parametrize("numel", [5, 4096 + 13, 300001, 2 * 256 * 8 * 4 + 7])
-def test_quantize_every_unroll(unroll, numel):
-    _say(f"quantize unroll={unroll} numel={numel}")
+@pytest.mark.parametrize("numel", [5, 4096 + 13, 300001, 2 * 256 * 8 * 4 + 7, 256 * 16 * 3 + 4])
+def test_quantize_grid_tails(numel):
+    """Sizes around the vector kernel's per-thread and per-block strides."""
+    _say(f"quantize numel={numel}")
     x = (qi.rng(numel + 17).standard_normal(numel) * 3).astype(np.float32)
     ob = torch.zeros(numel, dtype=torch.int8, device="cuda")
-    with env(Q8TA_QUANT_UNROLL=unroll):
-        q8.q8ta_quantize_per_tensor(dev(x), ob, 0.02, 3)
+    q8.q8ta_quantize_per_tensor(dev(x), ob, 0.02, 3)
     np.testing.assert_array_equal(host(ob), oracle.quantize_per_tensor(x, 0.02, 3))
 
 
@@ -184,16 +179,26 @@ def test_linear_zero_points_and_no_bias(M, K, N, izp):
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
 
 
-@pytest.mark.parametrize("cfg", ["L", "M", "S", "K", "W", "V", "U", "Q", "R", "X", "Y", "Z", "P", "y", "z", "w"])
-@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (512, 4096, 768),
-                                   (70, 48, 300)])
-def test_linear_every_gemm_tile(cfg, M, K, N):
-    _say(f"gemm cfg={cfg} M={M} K={K} N={N}")
-    c = qi.linear_case(M + N + ord(cfg), M, K, N)
-    with env(Q8TA_GEMM_CFG=cfg):
+# Shapes that reach each GEMM tile of the default dispatch: the 128 x 64 tile
+# (M <= 64 with few tiles), the 128 x 128 tile, the 32x32x32 256 x 128 tile
+# (>= 256 such tiles and K >= 1024; one of them with ragged M, N and K tail),
+# and the shape-general kernel (K % 16 != 0); plus every shape forced onto the
+# shape-general kernel.
+GEMM_TILE_SHAPES = [(64, 128, 64), (70, 48, 300), (300, 1040, 257), (512, 4096, 768),
+                    (1024, 1024, 8192), (1000, 1040, 8100), (33, 100, 70)]
+
+
+@pytest.mark.parametrize("path", ["default", "generic"])
+@pytest.mark.parametrize("M,K,N", GEMM_TILE_SHAPES)
+def test_linear_every_gemm_tile(path, M, K, N):
+    _say(f"gemm {path} M={M} K={K} N={N}")
+    if path == "generic" and M * K * N > 1 << 31:
+        pytest.skip("the shape-general kernel is checked on the smaller shapes")
+    c = qi.linear_case(M + N + len(path), M, K, N)
+    with kernel("linear", path):
         np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
         np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
-        # fp32 output (fused dequantize; the 32x32x32 kernels store it in their
+        # fp32 output (fused dequantize; the 32x32x32 kernel stores it in its
         # transposed form)
         out = torch.empty((M, N), dtype=torch.float32, device="cuda")
         q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
@@ -203,45 +208,14 @@ def test_linear_every_gemm_tile(cfg, M, K, N):
         np.testing.assert_array_equal(host(out).view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("cfg", ["B", "D", "Q"])
-@pytest.mark.parametrize("M,K,N", [(300, 1024, 257), (64, 128, 64), (512, 4096, 768), (700, 256, 1100)])
-def test_linear_every_gemm_dl_tile(cfg, M, K, N):
-    """The direct-to-LDS 32x32x32 matrix-core GEMM in each of its tile shapes."""
-    _say(f"gemm dl cfg={cfg} M={M} K={K} N={N}")
-    c = qi.linear_case(M + N + ord(cfg) + 2, M, K, N)
-    with env(Q8TA_GEMM_CFG="G", Q8TA_GEMM_DL_CFG=cfg):
-        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
-        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
-        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
-                          dev(c.bias), c.out_scale, c.out_zp, "relu", out)
-        ref = oracle.dequantize_per_tensor(_oracle_linear(c, activation="relu"), c.out_scale,
-                                           c.out_zp)
-        np.testing.assert_array_equal(host(out).view(np.uint32), ref.view(np.uint32))
-
-
-@pytest.mark.parametrize("cfg", ["4S.16x2:16", "4S.16x2:16x", "4S.16x2:1", "4S.16x2:3x",
-                                 "4S.8x2:16x", "4S.8x2:1", "4S.8x4:3x", "4S.4x4:8x", "4S.4x4:1",
-                                 "2S.16x2:8", "2P.16x2:3x", "2S.8x2:8x", "2P.8x2:1"])
-@pytest.mark.parametrize("M,K,N", [(300, 1040, 257), (64, 128, 64), (17, 4096, 40), (512, 2048, 768)])
-def test_linear_every_dot4_variant(cfg, M, K, N):
-    _say(f"dot4 gemm cfg={cfg} M={M} K={K} N={N}")
-    c = qi.linear_case(M + N + len(cfg), M, K, N)
-    with env(Q8TA_DOT4_CFG=cfg, Q8TA_GEMM_PATH="dot4"):
-        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
-        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
-
-
-@pytest.mark.parametrize("rows", [1, 2, 4])
-@pytest.mark.parametrize("M,K", [(1, 2048), (3, 4096), (1, 5136), (4, 48)])
-def test_gemv_rows_per_wave(rows, M, K):
-    """Every skinny-GEMM layout (ROWS weight rows per wave); K spans partial
-    1 KiB slices and several passes."""
-    _say(f"gemv rows={rows} M={M} K={K}")
-    c = qi.linear_case(77 + rows + M + K, M, K, 1001)
-    with env(Q8TA_GEMV_ROWS=rows):
-        np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
-        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+@pytest.mark.parametrize("M,K", [(1, 2048), (3, 4096), (1, 5136), (4, 48), (2, 16)])
+def test_gemv_k_slices(M, K):
+    """The skinny GEMM (M <= 4); K spans partial 1 KiB slices and several
+    passes."""
+    _say(f"gemv M={M} K={K}")
+    c = qi.linear_case(78 + M + K, M, K, 1001)
+    np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
+    np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
 
 
 def test_linear_gemv_entry_and_gemm_row_identity():
@@ -411,41 +385,48 @@ DECONV_IGEMM_CASES = [
 
 @pytest.mark.parametrize("case", DECONV_IGEMM_CASES,
                          ids=[str(i) for i in range(len(DECONV_IGEMM_CASES))])
-@pytest.mark.parametrize("path", ["igemm:4x4", "igemm:4x8", "dot4:", "mfma:"])
+@pytest.mark.parametrize("path", ["igemm", "tiled", "mfma"])
 def test_deconv_igemm_parity(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
     _say(f"deconv {path} case={case}")
     c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 1, N, IC, H, W, OC, Kh, Kw, s, p, op,
                        H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra)
-    kind, layout = path.split(":")
-    with env(Q8TA_DECONV_PATH=kind, Q8TA_IGEMM_CFG=layout or "4x4"):
+    with kernel("conv2d_transposed", path):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
-@pytest.mark.parametrize("fj,fo,wi", [(1, 1, 1), (2, 4, 2), (4, 2, 1), (4, 4, 4), (1, 4, 3)])
-def test_deconv_every_tile(fj, fo, wi):
-    _say(f"deconv tile FJ={fj} FO={fo} WI={wi}")
-    c = qi.deconv_case(500 + fj * 10 + fo, 2, 64, 10, 36, 72, 3, 3, (2, 2), (1, 1), (1, 1))
-    with env(Q8TA_DECONV_FJ=fj, Q8TA_DECONV_FO=fo, Q8TA_DECONV_WI=wi):
+# Shapes that reach each tile plan of the matrix-core transposed conv: phase
+# columns per wave (16, 32, 64: W_out / stride below 32, below 64, at least
+# 64), output-channel fragments per wave (OC below 32 or not), and the
+# one-fragment plan for problems that leave the chip mostly idle.
+DECONV_PLAN_SHAPES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad   (256 workgroups or more unless noted)
+    (8, 32, 64, 24, 16, 3, 3, (2, 2), (1, 1), (1, 1)),    # 24 phase columns, OC 16
+    (8, 32, 64, 40, 48, 3, 3, (2, 2), (1, 1), (1, 1)),    # 40 phase columns, 2 fragments
+    (8, 32, 64, 70, 40, 3, 3, (2, 2), (1, 1), (1, 1)),    # 70 phase columns
+    (2, 64, 10, 36, 72, 3, 3, (2, 2), (1, 1), (1, 1)),    # 24 workgroups: one-fragment plan
+]
+
+
+@pytest.mark.parametrize("shape", DECONV_PLAN_SHAPES, ids=[str(i) for i in range(4)])
+def test_deconv_every_tile(shape):
+    _say(f"deconv tile plan shape={shape}")
+    c = qi.deconv_case(500 + sum(shape[:5]), *shape)
+    with kernel("conv2d_transposed", "mfma"):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
-@pytest.mark.parametrize("variant", ["blocked:8:1", "blocked:8:2", "blocked:8:4", "blocked:16:1",
-                                     "blocked:16:2", "nchw:8:1", "nchw:8:2", "nchw:8:4",
-                                     "nchw:16:1", "nchw:16:2"])
 @pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_CASES[6], DECONV_CASES[11],
                                   DECONV_CASES[13]],
                          ids=["k3s2", "mixed_strides", "empty_phases", "wide", "ic320"])
-def test_deconv_every_dot4_variant(variant, case):
-    layout, ocb, rq = variant.split(":")
+def test_deconv_tiled_kernel(case):
     N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
-    _say(f"deconv dot4 variant={variant} case={case}")
-    c = qi.deconv_case(7 + int(ocb) + int(rq), N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho,
+    _say(f"deconv tiled case={case}")
+    c = qi.deconv_case(7 + 8 + 1, N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho,
                        W_out=Wo, ldw=Kh * Kw * IC + extra)
-    with env(Q8TA_DECONV_PATH="dot4", Q8TA_DECONV_LAYOUT=layout, Q8TA_DECONV_OCB=ocb,
-             Q8TA_DECONV_RQ=rq):
+    with kernel("conv2d_transposed", "tiled"):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
@@ -477,27 +458,36 @@ def test_deconv_small_workload():
     np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
 
 
-def test_deconv_large_workload_sampled():
+_C5_REF = {}
+
+
+def _c5_reference():
+    """The oracle's quantize and transposed conv of the large workload, over
+    every output (computed once per test session)."""
+    if not _C5_REF:
+        c = qi.make_deconv_large()
+        xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+        ref = oracle.conv2d_transposed(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                       c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding,
+                                       (1, 1), c.H_out, c.W_out)
+        _C5_REF.update(c=c, xq=xq, ref=ref)
+    return _C5_REF["c"], _C5_REF["xq"], _C5_REF["ref"]
+
+
+def test_deconv_large_workload_full():
     """quantize [8,256,64,64] -> deconv -> [8,128,128,128] in the benchmark's
-    launch configuration; the oracle recomputes images 0 and 7 for 24 output
-    channels (first, last and spread)."""
-    c = qi.make_deconv_large()
-    _say("quantize + deconv [8,256,64,64] -> [8,128,128,128]")
+    launch configuration, every output compared with the oracle."""
+    c, xq_ref, ref = _c5_reference()
+    _say("quantize + deconv [8,256,64,64] -> [8,128,128,128], full output")
     xq = torch.empty(c.x_fp32.shape, dtype=torch.int8, device="cuda")
     q8.q8ta_quantize_per_tensor(dev(c.x_fp32), xq, c.in_scale, c.in_zp)
     out = torch.empty((8, 128, 128, 128), dtype=torch.int8, device="cuda")
     q8.q8ta_conv2d_transposed(xq, c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw, None,
                               dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, c.stride,
                               c.padding, c.output_padding, (1, 1), 1, "none", out)
-    got = host(out)
-    xq_ref = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
     np.testing.assert_array_equal(host(xq), xq_ref)
-    ocs = np.unique(np.concatenate([[0, 1, 63, 64, 127], qi.rng(4).integers(0, 128, 19)]))
-    for n in (0, 7):
-        ref = oracle.conv2d_transposed(xq_ref[n:n + 1], c.w[ocs], c.weight_scales[ocs],
-                                       c.bias[ocs], c.in_scale, c.in_zp, c.out_scale, c.out_zp,
-                                       c.Kh, c.Kw, c.stride, c.padding, (1, 1), c.H_out, c.W_out)
-        np.testing.assert_array_equal(got[n][ocs], ref[0])
+    got = host(out)
+    np.testing.assert_array_equal(got, ref)
     assert (np.abs(got.astype(int)) < 127).mean() > 0.9
 
 
@@ -540,14 +530,13 @@ CONV2D_CASES = [
 
 
 @pytest.mark.parametrize("case", CONV2D_CASES, ids=[str(i) for i in range(len(CONV2D_CASES))])
-@pytest.mark.parametrize("path", ["mfma:4x4", "igemm:4x4", "igemm:4x8"])
+@pytest.mark.parametrize("path", ["mfma", "igemm"])
 def test_conv2d_parity(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, d, Ho, Wo, extra = case
-    kind, layout = path.split(":")
     _say(f"conv2d path={path} case={case}")
     c = qi.conv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 2, N, IC, H, W, OC, Kh, Kw, s, p, d,
                      H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra)
-    with env(Q8TA_IGEMM_CFG=layout, Q8TA_CONV_PATH=kind):
+    with kernel("conv2d", path):
         np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
         np.testing.assert_array_equal(_acc_conv(c), oracle.conv2d_acc(
             c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out))
@@ -623,14 +612,14 @@ DQ_SHAPES = [(1, 4096, 4096), (3, 48, 17), (4, 64, 32), (65, 320, 97), (300, 104
 
 
 @pytest.mark.parametrize("M,K,N", DQ_SHAPES)
-@pytest.mark.parametrize("path", ["mfma", "dot4"])
+@pytest.mark.parametrize("path", ["default", "generic"])
 def test_linear_dq_equals_linear_then_dequantize(M, K, N, path):
     """q8ta_linear_dq == dequantize_per_tensor(q8ta_linear(...)) bit for bit,
-    against the oracle's two steps (matrix-core and v_dot4 GEMMs)."""
+    against the oracle's two steps (default and shape-general kernels)."""
     _say(f"linear_dq {path} M={M} K={K} N={N}")
     c = qi.linear_case(M * 3 + K + N, M, K, N)
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    with env(Q8TA_GEMM_PATH=path):
+    with kernel("linear", path):
         q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
                           dev(c.bias), c.out_scale, c.out_zp, "none", out)
     ref = oracle.dequantize_per_tensor(_oracle_linear(c), c.out_scale, c.out_zp)
@@ -683,22 +672,20 @@ def test_quantize_linear_equals_the_chain(M, K, N, act):
     np.testing.assert_array_equal(host(outf).view(np.uint32), refd.view(np.uint32))
 
 
-@pytest.mark.parametrize("rows", ["1", "2", "4"])
 @pytest.mark.parametrize("M,K,N", [(1, 5136, 33), (2, 4112, 7), (3, 48, 301), (4, 8192, 65)])
-def test_quantize_linear_rows_per_wave(rows, M, K, N):
-    """Every rows-per-wave form of the fp32-activation kernel (ragged N, K
-    chunks with masked slices) against the oracle's quantize -> linear."""
-    _say(f"quantize+linear rows={rows} M={M} K={K} N={N}")
+def test_quantize_linear_skinny_shapes(M, K, N):
+    """The fp32-activation skinny kernel (one weight row per wave for M = 1,
+    four for M > 1; ragged N, K chunks with masked slices) against the
+    oracle's quantize -> linear."""
+    _say(f"quantize+linear M={M} K={K} N={N}")
     c = qi.linear_case(M * 11 + K + N, M, K, N)
     xf = (qi.x_fp32(qi.rng(K + N), (M, K)) * 2.0).astype(np.float32)
     xq = oracle.quantize_per_tensor(xf, c.in_scale, c.in_zp)
     ref = oracle.linear(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp, c.out_scale,
                         c.out_zp)
     out = torch.empty((M, N), dtype=torch.int8, device="cuda")
-    with env(Q8TA_GEMV_ROWS=rows):
-        q8.q8ta_quantize_linear(dev(xf), c.in_scale, c.in_zp, dev(c.w), None,
-                                dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none",
-                                out)
+    q8.q8ta_quantize_linear(dev(xf), c.in_scale, c.in_zp, dev(c.w), None,
+                            dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
     np.testing.assert_array_equal(host(out), ref)
 
 
@@ -737,14 +724,14 @@ def test_quantize_linear_dq_gemm_workload_sampled():
 @pytest.mark.parametrize("case", [DECONV_CASES[1], DECONV_CASES[3], DECONV_IGEMM_CASES[1],
                                   DECONV_IGEMM_CASES[5], DECONV_CASES[14]],
                          ids=["k3s2", "mixed", "igemm_oc40", "igemm_tall", "general"])
-@pytest.mark.parametrize("path", ["igemm", "dot4", "mfma"])
+@pytest.mark.parametrize("path", ["igemm", "tiled", "mfma"])
 def test_quantize_conv2d_transposed_equals_the_chain(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, op, Ho, Wo, extra = case
     _say(f"quantize+deconv {path} case={case}")
     c = qi.deconv_case(sum([N, IC, H, W, OC]) + 5, N, IC, H, W, OC, Kh, Kw, s, p, op, H_out=Ho,
                        W_out=Wo, ldw=Kh * Kw * IC + extra, x_from_fp32=True)
     out = torch.empty((N, OC, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
-    with env(Q8TA_DECONV_PATH=path):
+    with kernel("conv2d_transposed", path):
         q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh,
                                            c.Kw, None, dev(c.weight_scales), dev(c.bias),
                                            c.out_scale, c.out_zp, c.stride, c.padding,
@@ -756,25 +743,20 @@ def test_quantize_conv2d_transposed_equals_the_chain(case, path):
     np.testing.assert_array_equal(host(out), ref)
 
 
-def test_quantize_conv2d_transposed_large_workload_sampled():
-    c = qi.make_deconv_large()
-    _say("quantize+deconv fused [8,256,64,64] -> [8,128,128,128]")
+def test_quantize_conv2d_transposed_large_workload_full():
+    """The fused quantize -> transposed conv on the large workload, every
+    output compared with the oracle's quantize then transposed conv."""
+    c, _, ref = _c5_reference()
+    _say("quantize+deconv fused [8,256,64,64] -> [8,128,128,128], full output")
     out = torch.empty((8, 128, 128, 128), dtype=torch.int8, device="cuda")
     q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh, c.Kw,
                                        None, dev(c.weight_scales), dev(c.bias), c.out_scale,
                                        c.out_zp, c.stride, c.padding, c.output_padding, (1, 1), 1,
                                        "none", out)
-    got = host(out)
-    xq = oracle.quantize_per_tensor(c.x_fp32[7:8], c.in_scale, c.in_zp)
-    chans = np.array([0, 1, 64, 127, 33, 98])
-    ref = oracle.conv2d_transposed(xq, c.w[chans], c.weight_scales[chans], c.bias[chans],
-                                   c.in_scale, c.in_zp, c.out_scale, c.out_zp, c.Kh, c.Kw,
-                                   c.stride, c.padding, (1, 1), c.H_out, c.W_out)
-    np.testing.assert_array_equal(got[7:8, chans], ref)
+    np.testing.assert_array_equal(host(out), ref)
 
 
-
-@pytest.mark.parametrize("path", ["mfma", "igemm", "dot4"])
+@pytest.mark.parametrize("path", ["mfma", "igemm", "tiled"])
 def test_workspace_reuse_across_calls_and_streams(path):
     """Calls that need scratch memory, queued back to back without a host
     synchronization: small, larger (the stream's buffer grows), small again,
@@ -786,7 +768,7 @@ def test_workspace_reuse_across_calls_and_streams(path):
                             x_from_fp32=True) for i, (n, ic, h, w, oc) in enumerate(shapes)]
     side = torch.cuda.Stream()
     keep, outs = [], []
-    with env(Q8TA_DECONV_PATH=path):
+    with kernel("conv2d_transposed", path):
         for i, c in enumerate(cases + cases[1:2]):
             args = (dev(c.x_fp32), dev(c.w), dev(c.weight_scales), dev(c.bias))
             out = torch.empty((c.x_fp32.shape[0], c.w.shape[0], c.H_out, c.W_out),
@@ -853,7 +835,7 @@ def test_linear_relu(M, K, N):
     ref = _oracle_linear(c, activation="relu")
     assert (ref == c.out_zp).mean() > 0.2
     np.testing.assert_array_equal(_run_linear(c, activation="relu"), ref)
-    with env(Q8TA_GEMM_PATH="dot4"):
+    with kernel("linear", "generic"):
         np.testing.assert_array_equal(_run_linear(c, activation="relu"), ref)
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
     q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
@@ -864,12 +846,12 @@ def test_linear_relu(M, K, N):
         np.testing.assert_array_equal(_run_linear(c, fn=q8.q8ta_linear_gemv, activation="relu"), ref)
 
 
-@pytest.mark.parametrize("path", ["mfma", "igemm", "dot4", "generic"])
+@pytest.mark.parametrize("path", ["mfma", "igemm", "tiled", "generic"])
 def test_deconv_relu(path):
     _say(f"deconv relu path={path}")
     IC = 6 if path == "generic" else 64   # IC % 4 != 0 takes the one-output-per-thread kernel
     c = qi.deconv_case(811 + IC, 2, IC, 6, 7, 40, 3, 3, (2, 2), (1, 1), (1, 1))
-    with env(Q8TA_DECONV_PATH=path):
+    with kernel("conv2d_transposed", path):
         np.testing.assert_array_equal(_run_deconv(c, activation="relu"),
                                       _oracle_deconv(c, activation="relu"))
 
@@ -883,7 +865,7 @@ def test_conv2d_relu(case):
         c = qi.conv_case(822, 2, 16, 12, 16, 16, 3, 3, (1, 1), (1, 1), (1, 1), groups=16)
     else:
         c = qi.conv_case(823, 1, 24, 7, 7, 8, 3, 3, (1, 1), (1, 1), (1, 1))
-    with env(Q8TA_CONV_PATH=case[0] if case in ("mfma", "igemm") else ""):
+    with kernel("conv2d", case if case in ("mfma", "igemm") else "default"):
         np.testing.assert_array_equal(_run_conv(c, activation="relu"),
                                       _oracle_conv(c, activation="relu"))
 
@@ -891,9 +873,9 @@ def test_conv2d_relu(case):
 def test_quantize_conv2d_transposed_relu():
     _say("quantize+deconv relu")
     c = qi.deconv_case(831, 1, 64, 5, 7, 32, 4, 4, (2, 2), (1, 1), (0, 0), x_from_fp32=True)
-    for path in ("igemm", "dot4"):
+    for path in ("igemm", "tiled"):
         out = torch.empty((1, 32, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
-        with env(Q8TA_DECONV_PATH=path):
+        with kernel("conv2d_transposed", path):
             q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh,
                                                c.Kw, None, dev(c.weight_scales), dev(c.bias),
                                                c.out_scale, c.out_zp, c.stride, c.padding,
@@ -920,13 +902,13 @@ DECONV_DILATED_CASES = [
 
 @pytest.mark.parametrize("case", DECONV_DILATED_CASES,
                          ids=[str(i) for i in range(len(DECONV_DILATED_CASES))])
-@pytest.mark.parametrize("path", ["mfma", "igemm", "dot4"])
+@pytest.mark.parametrize("path", ["mfma", "igemm", "tiled"])
 def test_deconv_dilated_parity(case, path):
     N, IC, H, W, OC, Kh, Kw, s, p, op, d = case
     _say(f"deconv dilated {path} case={case}")
     c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 13, N, IC, H, W, OC, Kh, Kw, s, p, op,
                        dilation=d)
-    with env(Q8TA_DECONV_PATH=path):
+    with kernel("conv2d_transposed", path):
         np.testing.assert_array_equal(_run_deconv(c), _oracle_deconv(c))
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
@@ -976,25 +958,22 @@ def test_weight_sums(N, K, offset):
     np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
 
 
-@pytest.mark.parametrize("path", ["default", "mfma:V", "mfma:M", "mfma:S", "mfma:G", "mfma:X", "mfma:Y", "mfma:Z", "mfma:P", "mfma:y", "mfma:z", "mfma:w", "dot4", "generic"])
+@pytest.mark.parametrize("path", ["default", "generic"])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
-                                   (7, 33, 5)])
+                                   (7, 33, 5), (40, 256, 64), (1024, 1024, 8192)])
 def test_linear_presummed_equals_linear(path, M, K, N):
     """With the sums q8ta_weight_sums returns, the presummed calls give the
     same bits as q8ta_linear / q8ta_linear_dq on every kernel; with other sums
     the results move (the sums are used, not recomputed)."""
     _say(f"presummed {path} M={M} K={K} N={N}")
     c = qi.linear_case(M * 11 + K + N + len(path), M, K, N)
-    kind, cfg = (path.split(":") + [""])[:2]
-    envs = {"default": {}, "mfma": {"Q8TA_GEMM_CFG": cfg}, "dot4": {"Q8TA_GEMM_PATH": "dot4"},
-            "generic": {}}[kind]
     wd = dev(c.w)
     sums = torch.empty(N, dtype=torch.int32, device="cuda")
     q8.q8ta_weight_sums(wd, sums)
     ref = _oracle_linear(c)
     out = torch.empty((M, N), dtype=torch.int8, device="cuda")
     outf = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    with env(**envs):
+    with kernel("linear", path):
         q8.q8ta_linear_presummed(dev(c.x), c.in_scale, c.in_zp, wd, sums, dev(c.weight_scales),
                                  dev(c.bias), c.out_scale, c.out_zp, "none", out)
         np.testing.assert_array_equal(host(out), ref)
@@ -1002,8 +981,9 @@ def test_linear_presummed_equals_linear(path, M, K, N):
                                     dev(c.bias), c.out_scale, c.out_zp, "none", outf)
         dq = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
         np.testing.assert_array_equal(host(outf).view(np.uint32), dq.view(np.uint32))
-        if M > 4 and K % 16 == 0:
-            # kernels that take the sums: shifted sums shift the accumulator
+        if M > 4 and K % 16 == 0 and path == "default":
+            # the matrix-core GEMM takes the sums (the shape-general kernel forms
+            # (x - zp) * w directly): shifted sums shift the accumulator
             wrong = sums + 1000
             q8.q8ta_linear_presummed(dev(c.x), c.in_scale, c.in_zp, wd, wrong, dev(c.weight_scales),
                                      dev(c.bias), c.out_scale, c.out_zp, "none", out)
