@@ -200,6 +200,29 @@ q8ta_status q8ta_quantize_linear_dq(const float* x, int64_t M, int64_t K,
                                     const char* activation, float* out,
                                     hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as q8ta_quantize_linear, bit-identical results, but the call never
+ * allocates.  Shapes the M <= 4 kernel takes need no staging; every other
+ * shape stages its quantized activations (M * K bytes) in a static device
+ * array of 16 MiB (16,777,216 bytes) that the library holds on each GPU it runs
+ * on until the process ends, and a call with M * K above that size returns
+ * Q8TA_ERR_SHAPE before any HIP call.  All calls on one GPU share that array
+ * and it keeps the last call's contents (every call writes the bytes it reads
+ * first): calls that overlap in time on one GPU -- on different streams or
+ * from different threads -- race, and the caller must order them.  The array's
+ * device address is looked up once per device on the first call.  Arguments,
+ * requirements and other errors as for q8ta_quantize_linear.
+ */
+q8ta_status q8ta_quantize_linear_noalloc(const float* x, int64_t M, int64_t K,
+                                         double input_scale, int64_t input_zero_point,
+                                         const int8_t* weight, int64_t N,
+                                         const int32_t* weight_sums,
+                                         const float* weight_scales, const float* bias,
+                                         double output_scale, int64_t output_zero_point,
+                                         const char* activation, int8_t* out,
+                                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Precomputed weight sums (opt-in).  [LIN] Constraints (1): the zero-point

@@ -59,6 +59,8 @@ SIGNATURES = {
                               _P, _P], ctypes.c_int),
     "q8ta_quantize_linear_dq": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64,
                                  _S, _P, _P], ctypes.c_int),
+    "q8ta_quantize_linear_noalloc": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL,
+                                      _I64, _S, _P, _P], ctypes.c_int),
     "q8ta_weight_sums": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "q8ta_linear_presummed": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
                                _P, _P], ctypes.c_int),
@@ -355,6 +357,16 @@ def q8ta_quantize_linear(x, input_scale, input_zero_point, weight, weight_sums, 
     """quantize_per_tensor of fp32 x [M, K] (input_scale, input_zero_point), then
     q8ta_linear, in one call: int8 out [M, N]."""
     return _quantize_linear(lib().q8ta_quantize_linear, _torch().int8, x, input_scale,
+                            input_zero_point, weight, weight_sums, weight_scales, bias,
+                            output_scale, output_zero_point, activation, out, stream)
+
+
+def q8ta_quantize_linear_noalloc(x, input_scale, input_zero_point, weight, weight_sums,
+                                 weight_scales, bias, output_scale, output_zero_point, activation,
+                                 out, stream=None):
+    """q8ta_quantize_linear without any device allocation (the quantized
+    activations go through the library's static scratch; M * K <= 16 MiB)."""
+    return _quantize_linear(lib().q8ta_quantize_linear_noalloc, _torch().int8, x, input_scale,
                             input_zero_point, weight, weight_sums, weight_scales, bias,
                             output_scale, output_zero_point, activation, out, stream)
 

@@ -95,6 +95,42 @@ q8ta_status linear_checks(const char* op, const void* x, int64_t M, int64_t K, c
   return Q8TA_OK;
 }
 
+// Scratch of the allocation-free entry point q8ta_quantize_linear_noalloc:
+// the quantized activations of one call (M * K bytes) before its GEMM.  A
+// file-scope device array, so each GPU the library runs on holds its own copy
+// from module load until the process ends.  In host code `scratch` names a
+// host-side stand-in: kernels get the device address noalloc_scratch returns.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) int8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept.
+hipError_t noalloc_scratch(void** p) {
+  *p = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!q) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = q;
+  }
+  *p = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // out: int8 [M, N]; or, with outf set (out NULL), fp32 [M, N] = the
 // dequantized int8 result (fused dequantize_per_tensor with the output's own
 // scale and zero point).
@@ -104,7 +140,7 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
                         int64_t output_zero_point, const char* activation, int8_t* out,
                         hipStream_t stream, float* outf = nullptr,
                         const int32_t* wsum_pre = nullptr, bool packed = false,
-                        const float* xf = nullptr) {
+                        const float* xf = nullptr, bool noalloc = false) {
   q8ta_status st = linear_checks(op, xf ? (const void*)xf : x, M, K, weight, N,
                                  outf ? (const void*)outf : out);
   if (st) return st;
@@ -134,6 +170,17 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   if (xf) {
     a.xf = xf;
     a.inv_in = recip(input_scale);
+    if (noalloc) {
+      // Only the shapes the M <= 4 kernel refuses stage the quantized
+      // activations (M * K bytes); they must fit the static scratch array.
+      if (!gemv_supported(a) && (uint64_t)M * (uint64_t)K > kNoAllocScratchBytes)
+        return fail(Q8TA_ERR_SHAPE,
+                    "%s: M * K = %lld bytes of quantized activations exceed the static scratch "
+                    "of %llu bytes", op, (long long)(M * K), (unsigned long long)kNoAllocScratchBytes);
+      void* scratch_ptr = nullptr;
+      if ((st = hip_status(noalloc_scratch(&scratch_ptr), op))) return st;
+      return hip_status(launch_quantize_linear(a, stream, (int8_t*)scratch_ptr), op);
+    }
     return hip_status(launch_quantize_linear(a, stream), op);
   }
   return hip_status(launch_linear(a, stream), op);
@@ -290,8 +337,8 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
 
 // quantize_per_tensor -> linear with fp32 activations (a.xf): the M <= 4
 // kernel quantizes while it loads them; other shapes quantize into an int8
-// buffer of M * K bytes -- `staging` when given, else a workspace -- and
-// take the usual path.
+// buffer of M * K bytes -- `staging` when given (the allocation-free entry
+// point's static scratch), else a workspace -- and take the usual path.
 hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s, int8_t* staging) {
   if (gemv_supported(a)) return launch_gemv(a, s);
   const int64_t numel = a.M * a.K;
@@ -468,6 +515,19 @@ q8ta_status q8ta_quantize_linear_dq(const float* x, int64_t M, int64_t K, double
   return linear_impl("q8ta_quantize_linear_dq", false, nullptr, M, K, input_scale,
                      input_zero_point, weight, N, weight_scales, bias, output_scale,
                      output_zero_point, activation, nullptr, stream, out, nullptr, false, x);
+}
+
+q8ta_status q8ta_quantize_linear_noalloc(const float* x, int64_t M, int64_t K,
+                                         double input_scale, int64_t input_zero_point,
+                                         const int8_t* weight, int64_t N,
+                                         const int32_t* weight_sums, const float* weight_scales,
+                                         const float* bias, double output_scale,
+                                         int64_t output_zero_point, const char* activation,
+                                         int8_t* out, hipStream_t stream) {
+  (void)weight_sums;
+  return linear_impl("q8ta_quantize_linear_noalloc", false, nullptr, M, K, input_scale,
+                     input_zero_point, weight, N, weight_scales, bias, output_scale,
+                     output_zero_point, activation, out, stream, nullptr, nullptr, false, x, true);
 }
 
 q8ta_status q8ta_weight_sums(const int8_t* weight, int64_t N, int64_t K, int32_t* sums,

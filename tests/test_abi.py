@@ -389,3 +389,18 @@ def test_select_kernel_names():
     q8.q8ta_select_kernel("linear", "default")
     with pytest.raises(q8.Q8taError, match="unknown kernel"):
         q8.q8ta_select_kernel("conv2d", "tiled")
+
+
+def test_noalloc_rejects_staging_beyond_the_static_scratch():
+    """q8ta_quantize_linear_noalloc refuses, before any HIP call, a shape whose
+    staged activations (M * K bytes) exceed its 16 MiB static scratch."""
+    lib = q8.lib()
+    M, K = 4097, 4096
+    rc = lib.q8ta_quantize_linear_noalloc(FAKE, M, K, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5,
+                                          b"none", FAKE, None)
+    _st(rc, q8.Q8TA_ERR_SHAPE, "static scratch")
+    # the usual argument checks come first
+    _st(lib.q8ta_quantize_linear_noalloc(None, 8, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5,
+                                         b"none", FAKE, None), q8.Q8TA_ERR_NULL)
+    _st(lib.q8ta_quantize_linear_noalloc(FAKE, 8, 64, 0.02, 3, FAKE, 32, None, FAKE, None, 0.5, -5,
+                                         b"gelu", FAKE, None), q8.Q8TA_ERR_UNSUPPORTED)
