@@ -82,8 +82,10 @@ const char* q8ta_last_error(void);
  * whichever kernel runs.  Process-wide: applies to calls made after it returns.
  *   op "linear":            kernel "default" | "generic" (the shape-general
  *                           kernel instead of the GEMV / matrix-core GEMM)
- *   op "conv2d_transposed": "default" | "mfma" | "igemm" | "tiled" | "generic"
- *   op "conv2d":            "default" | "mfma" | "igemm" | "generic"
+ *   op "conv2d_transposed": "default" | "fixed" | "mfma32" | "mfma" | "igemm" |
+ *                           "tiled" | "generic"
+ *   op "conv2d":            "default" | "fixed" | "mfma32" | "mfma" | "igemm" |
+ *                           "generic"
  * Returns Q8TA_ERR_NULL for a NULL name and Q8TA_ERR_UNSUPPORTED for an unknown
  * op or kernel name (the choice is then unchanged).  Host-only, no HIP call. */
 q8ta_status q8ta_select_kernel(const char* op, const char* kernel);

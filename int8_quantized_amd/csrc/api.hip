@@ -356,22 +356,39 @@ hipError_t launch_quantize_linear(LinearArgs a, hipStream_t s, int8_t* staging) 
   return e != hipSuccess ? e : f;
 }
 
-// Transposed conv: the matrix-core kernel takes every shape it supports, then
-// the implicit GEMM (three launches' worth of fixed cost: input copy, then the
-// GEMM) from about 2^28 multiply-adds, then the direct tiled kernel, then the
-// shape-general one.  q8ta_select_kernel can force one family ('m' matrix
-// cores, 'i' implicit GEMM, 't' tiled, 'g' generic) where the shape allows it.
-static char deconv_path() { return g_sel_deconv.load(std::memory_order_relaxed); }
+// Transposed conv: the compile-time-pattern 32x32x32 kernel for 3x3 and 4x4
+// stride-2 shapes with at least one workgroup per CU, then the tiled
+// 16x16x64 matrix-core kernel for every shape it supports, then the implicit
+// GEMM (three launches' worth of fixed cost: input copy, then the GEMM) from
+// about 2^28 multiply-adds, then the direct tiled kernel, then the
+// shape-general one.  q8ta_select_kernel can force one family ('f' pattern,
+// 'x' 32x32x32, 'm' 16x16x64, 'i' implicit GEMM, 't' tiled, 'g' generic)
+// where the shape allows it.
+// The forced family when it takes the shape, else 0 (the default choice).
+static char deconv_family(const DeconvArgs& a) {
+  const char k = g_sel_deconv.load(std::memory_order_relaxed);
+  switch (k) {
+    case 'f': return deconv_fixed_supported(a) ? k : 0;
+    case 'x': return deconv_mx_supported(a) ? k : 0;
+    case 'm': return deconv_mfma_supported(a) ? k : 0;
+    case 'i': return deconv_igemm_supported(a) ? k : 0;
+    case 't': return deconv_dot4_supported(a) ? k : 0;
+    default: return k;   // 0 or 'g' (the generic kernel takes every shape)
+  }
+}
 
 static bool deconv_wants_igemm(const DeconvArgs& a) {
-  const char k = deconv_path();
+  const char k = deconv_family(a);
   const double macs = (double)a.N * a.OC * a.H_out * a.W_out * a.IC * a.Kh * a.Kw /
                       ((double)a.sh * a.sw);
   return (k ? k == 'i' : macs >= (double)(1 << 28)) && deconv_igemm_supported(a);
 }
 
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
-  const char k = deconv_path();
+  const char k = deconv_family(a);
+  if ((k == 0 && deconv_fixed_preferred(a)) || (k == 'f' && deconv_fixed_supported(a)))
+    return launch_deconv_fixed(a, s);
+  if (k == 'x' && deconv_mx_supported(a)) return launch_deconv_mx(a, s);
   if ((k == 0 || k == 'm') && deconv_mfma_supported(a)) return launch_deconv_mfma(a, s);
   if (deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
   if (k != 'g' && deconv_dot4_supported(a)) return launch_deconv_dot4(a, s);
@@ -382,9 +399,13 @@ hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
 // implicit GEMM quantizes while it copies the input; the other paths (the
 // matrix-core kernel first) quantize into a stream-ordered int8 workspace.
 hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
-  const char k = deconv_path();
-  const bool mfma = (k == 0 || k == 'm') && deconv_mfma_supported(a);
-  if (!mfma && k != 'm' && deconv_wants_igemm(a)) return launch_deconv_igemm(a, s);
+  const char k = deconv_family(a);
+  const bool mfma = ((k == 0 || k == 'm') && deconv_mfma_supported(a)) ||
+                    (k == 0 && deconv_fixed_preferred(a)) ||
+                    (k == 'x' && deconv_mx_supported(a)) ||
+                    (k == 'f' && deconv_fixed_supported(a));
+  if (!mfma && k != 'm' && k != 'x' && k != 'f' && deconv_wants_igemm(a))
+    return launch_deconv_igemm(a, s);
   const int64_t numel = a.N * a.IC * a.H_in * a.W_in;
   void* ws = nullptr;
   hipError_t e = workspace_acquire(&ws, (size_t)numel, s);
@@ -399,12 +420,20 @@ hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
   return e != hipSuccess ? e : f;
 }
 
-// Forward conv: the matrix-core kernel (groups 1, stride 1, IC % 16 == 0),
+// Forward conv: the 32x32x32 kernel for large stride-1 shapes (IC % 32 == 0,
+// W_in % 4 == 0), the 16x16x64 matrix-core kernel (groups 1, stride 1, IC % 16 == 0),
 // the implicit GEMM on v_dot4 (groups 1, IC % 64 == 0), the depthwise kernel
 // (groups == IC == OC), or the shape-general kernel.  q8ta_select_kernel can
 // force one ('m', 'i', 'g') where the shape allows it.
 hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s) {
-  const char k = g_sel_conv.load(std::memory_order_relaxed);
+  char k = g_sel_conv.load(std::memory_order_relaxed);
+  // a forced family that does not take the shape falls back to the default
+  if ((k == 'f' && !conv_fixed_supported(a)) || (k == 'x' && !conv_mx_supported(a)) ||
+      (k == 'm' && !conv_mfma_supported(a)) || (k == 'i' && !conv_igemm_supported(a)))
+    k = 0;
+  if (k == 'f' && conv_fixed_supported(a)) return launch_conv_fixed(a, s);
+  if ((k == 0 && conv_mx_preferred(a)) || (k == 'x' && conv_mx_supported(a)))
+    return launch_conv_mx(a, s);
   if ((k == 0 || k == 'm') && conv_mfma_supported(a)) return launch_conv_mfma(a, s);
   if ((k == 0 || k == 'i') && conv_igemm_supported(a)) return launch_conv_igemm(a, s);
   if (k == 'g') return launch_conv2d_generic(a, s);
@@ -422,15 +451,16 @@ q8ta_status q8ta_select_kernel(const char* op, const char* kernel) {
   if (!op || !kernel) return fail(Q8TA_ERR_NULL, "q8ta_select_kernel: op and kernel must not be NULL");
   struct Name { const char* name; char code; };
   static const Name linear[] = {{"default", 0}, {"generic", 'g'}};
-  static const Name deconv[] = {{"default", 0}, {"mfma", 'm'}, {"igemm", 'i'}, {"tiled", 't'},
-                                {"generic", 'g'}};
-  static const Name conv[] = {{"default", 0}, {"mfma", 'm'}, {"igemm", 'i'}, {"generic", 'g'}};
+  static const Name deconv[] = {{"default", 0}, {"fixed", 'f'}, {"mfma32", 'x'}, {"mfma", 'm'},
+                                {"igemm", 'i'}, {"tiled", 't'}, {"generic", 'g'}};
+  static const Name conv[] = {{"default", 0}, {"fixed", 'f'}, {"mfma32", 'x'}, {"mfma", 'm'},
+                              {"igemm", 'i'}, {"generic", 'g'}};
   const Name* tab = nullptr;
   size_t n = 0;
   std::atomic<char>* dst = nullptr;
   if (strcmp(op, "linear") == 0) { tab = linear; n = 2; dst = &g_sel_linear; }
-  else if (strcmp(op, "conv2d_transposed") == 0) { tab = deconv; n = 5; dst = &g_sel_deconv; }
-  else if (strcmp(op, "conv2d") == 0) { tab = conv; n = 4; dst = &g_sel_conv; }
+  else if (strcmp(op, "conv2d_transposed") == 0) { tab = deconv; n = 7; dst = &g_sel_deconv; }
+  else if (strcmp(op, "conv2d") == 0) { tab = conv; n = 6; dst = &g_sel_conv; }
   else return fail(Q8TA_ERR_UNSUPPORTED, "q8ta_select_kernel: unknown op \"%.64s\"", op);
   for (size_t i = 0; i < n; ++i)
     if (strcmp(kernel, tab[i].name) == 0) {

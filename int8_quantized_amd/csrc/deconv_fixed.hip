@@ -1,0 +1,490 @@
+// q8ta_conv2d_transposed for a kernel size and stride known at compile time
+// (the 3x3 and 4x4 stride-2 convolutions, and the 3x3 stride-1 forward conv),
+// as an implicit GEMM on v_mfma_i32_32x32x32_i8.
+//
+// The gather of "Add q8ta_conv2d_transposed op" (Solution) sums, for output
+// (oh, ow), the taps (kh, kw) whose numerators oh + pad_h - kh and
+// ow + pad_w - kw are non-negative multiples of the stride and land inside the
+// input.  With oh = s*i + rh the qualifying kernel rows of residue rh are the
+// kh with kh = rh + pad_h (mod s), and each reads input row i + dh(rh, kh),
+// dh = (rh + pad_h - kh) / s; columns likewise.  So phase (rh, rw) is a dense
+// correlation of the input with its sub-kernel, and every (phase, tap) pair
+// reads the input at one of a few shifts (dh, dw): for 3x3 stride 2 the 9
+// taps of the 4 phases use only 4 shifts, for 4x4 the 16 taps 9 shifts.  All
+// of this is fixed by (K, s, pad mod s) and is built at compile time.  Taps
+// that fall outside the input read the zero point, so with the weight sum
+// taken over the phase's taps, sum x*w - zp * sum w is the gather (the page's
+// Constraints (1), zero-point-filled form).
+//
+// Workgroup: one image, two phase rows, 64 phase columns and 128 output
+// channels (4 waves of 32 channels, one wave per SIMD).  Each wave computes
+// all phases of the tile for its channels: per phase 4 fragments of 32
+// pixels (2 rows x 2 column halves), the accumulators of every phase live
+// together in the accumulation registers.
+// Steps:
+//  * the whole input halo of the tile (all channels) is staged in LDS once,
+//    in the operand's K-contiguous order: 32-bit words of 16 channel planes,
+//    transposed in registers with byte permutes; out-of-image words hold the
+//    zero point;
+//  * then, per 32 channels and per shift, the wave reads its 4 pixel
+//    fragments from LDS once (the A operand; the next shift's fragments are
+//    requested before the current shift's products) and multiplies them with the
+//    weight fragment of every tap that reads that shift (the B operand, lane
+//    l: row l % 32 of the [OC, ldw] weight, K bytes 16 * (l / 32) .. +15,
+//    straight from global memory / L2); each tap's register is refilled with
+//    the next step's fragment right after its last product;
+//  * v_dot4 against 0x01010101 over the weight fragments gives the phase
+//    weight sums.
+#include <type_traits>
+
+#include "q8ta_internal.h"
+
+namespace q8ta {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;   // 4 waves x 32 output channels
+constexpr int kTR = 2;          // phase rows per workgroup
+constexpr int kTJ = 64;         // phase columns per workgroup
+constexpr int kOCB = 128;       // output channels per workgroup
+constexpr int kStageSlots = 4;  // halo staging units per thread
+
+template <int B, int E>
+struct Static {
+  template <class F>
+  __device__ __forceinline__ static void each(F&& f) {
+    if constexpr (B < E) {
+      f(std::integral_constant<int, B>{});
+      Static<B + 1, E>::each(f);
+    }
+  }
+};
+
+constexpr int fdiv(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+constexpr int fmod_(int a, int b) { return ((a % b) + b) % b; }
+
+// Compile-time tap table of a (K, stride, pad mod stride) pattern.  Tap t:
+// phase ph = rh*S + rw, kernel position (kh, kw), and input shift index.
+// Shift (dh, dw) is relative: the input row of phase row i is
+// i + dh + base_h, base_h = (pad_h - PM) / S for the transposed conv
+// (-pad_h for the forward one), so only PM = pad mod S enters the table.
+template <int S, int K, int PM, bool FWD>
+struct Pattern {
+  int T = 0;                 // taps
+  int ph[64] = {}, kh[64] = {}, kw[64] = {}, sh[64] = {};
+  int NS = 0;                // distinct shifts
+  int sdh[64] = {}, sdw[64] = {};
+  int dhmin = 0, dhmax = 0, dwmin = 0, dwmax = 0;
+  constexpr Pattern() {
+    int rk[8][8] = {}, rd[8][8] = {}, rn[8] = {};
+    for (int r = 0; r < S; ++r)
+      for (int k = 0; k < K; ++k) {
+        if (!FWD && fmod_(r + PM - k, S) != 0) continue;
+        rk[r][rn[r]] = k;
+        rd[r][rn[r]] = FWD ? k : fdiv(r + PM - k, S);
+        ++rn[r];
+      }
+    dhmin = dwmin = 1 << 20;
+    dhmax = dwmax = -(1 << 20);
+    for (int rh = 0; rh < S; ++rh)
+      for (int rw = 0; rw < S; ++rw)
+        for (int a = 0; a < rn[rh]; ++a)
+          for (int b = 0; b < rn[rw]; ++b) {
+            const int dh = rd[rh][a], dw = rd[rw][b];
+            int s = 0;
+            while (s < NS && !(sdh[s] == dh && sdw[s] == dw)) ++s;
+            if (s == NS) {
+              sdh[NS] = dh;
+              sdw[NS] = dw;
+              ++NS;
+            }
+            ph[T] = rh * S + rw;
+            kh[T] = rk[rh][a];
+            kw[T] = rk[rw][b];
+            sh[T] = s;
+            ++T;
+            dhmin = dh < dhmin ? dh : dhmin;
+            dhmax = dh > dhmax ? dh : dhmax;
+            dwmin = dw < dwmin ? dw : dwmin;
+            dwmax = dw > dwmax ? dw : dwmax;
+          }
+  }
+};
+
+// Runtime geometry (host-built).
+struct FxPlan {
+  int base_h, base_w;    // input row / column of phase (0, 0) shift (0, 0)
+  int HR, HC, coff;      // halo rows, columns (multiple of 8), column offset in the first word
+  int Hp, Wp, tiles_i, tiles_j, tiles_oc;
+  int xcd;
+  int out_vec;           // 16-byte output stores allowed
+};
+
+// LDS column slot (see the 32-pixel fragment reads): chunk c at c ^ 4 when
+// bit 4 of c is set; rows are padded to a multiple of 8 chunks.
+__device__ __forceinline__ int pos(int c) { return c ^ (((c >> 4) & 1) << 2); }
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int e) { return (w >> (8 * e)) & 0xffu; }
+
+template <int S, int K, int PM, bool FWD>
+__global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPlan p) {
+  constexpr Pattern<S, K, PM, FWD> P{};
+  constexpr int NPH = S * S;
+  constexpr int OROWS = kTR * S;                // output rows of the tile
+  constexpr int OCOLS = kTJ * S;                // output columns of the tile
+  constexpr int OPITCH = OCOLS + 16;            // LDS bytes per (channel, row) of the output copy
+
+  extern __shared__ __attribute__((aligned(16))) v4i smem[];
+  const int HR = p.HR, HC = p.HC;
+  const int NQ = (int)a.IC / 16;               // 16-channel blocks
+  v4i* xs = smem;                               // the halo: HR x NQ x HC chunks
+  int8_t* os = reinterpret_cast<int8_t*>(smem + HR * NQ * HC);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lo = lane & 31;
+  const int hi = lane >> 5;
+
+  int b = blockIdx.x;
+  if (p.xcd) {
+    const int per = (int)(gridDim.x >> 3);
+    b = (b & 7) * per + (b >> 3);
+  }
+  const int tj = b % p.tiles_j;   b /= p.tiles_j;
+  const int ti = b % p.tiles_i;   b /= p.tiles_i;
+  const int toc = b % p.tiles_oc; b /= p.tiles_oc;
+  const int n = b;
+  const int i0 = ti * kTR, j0 = tj * kTJ, oc0 = toc * kOCB;
+
+  const int H_in = (int)a.H_in, W_in = (int)a.W_in, IC = (int)a.IC, OC = (int)a.OC;
+  const int64_t plane = (int64_t)H_in * W_in;
+  const int8_t* xn = a.x + (int64_t)n * IC * plane;
+  const uint32_t zp4 = 0x01010101u * ((uint32_t)a.izp & 0xffu);
+  const int row0 = i0 + P.dhmin + p.base_h;        // input row of halo row 0
+  const int col0 = j0 + P.dwmin + p.base_w - p.coff;   // input column of halo column 0 (multiple of 4)
+
+  // ---- halo staging: unit u = (halo row, 16-channel block, 4 columns) ----
+  // All units are loaded before any is transposed and stored, at most
+  // kStageSlots per thread (the host checks the count).
+  {
+    const int CG = HC >> 2;
+    const int units = HR * NQ * CG;
+    uint32_t stg[kStageSlots][16];
+#pragma unroll
+    for (int sl = 0; sl < kStageSlots; ++sl) {
+      if (sl * kThreads >= units) break;   // wave-uniform
+      const int u = tid + sl * kThreads;
+      const int uu = u < units ? u : units - 1;
+      const int cg = uu % CG;
+      const int q = (uu / CG) % NQ;
+      const int r = uu / (CG * NQ);
+      const int ih = row0 + r, iw = col0 + 4 * cg;
+      const int ihc = ih < 0 ? 0 : (ih >= H_in ? H_in - 1 : ih);
+      const int iwc = iw < 0 ? 0 : (iw > W_in - 4 ? W_in - 4 : iw);
+      const int8_t* src = xn + (int64_t)(16 * q) * plane + (int64_t)ihc * W_in + iwc;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) stg[sl][t] = *reinterpret_cast<const uint32_t*>(src + t * plane);
+    }
+#pragma unroll
+    for (int sl = 0; sl < kStageSlots; ++sl) {
+      if (sl * kThreads >= units) break;
+      const int u = tid + sl * kThreads;
+      if (u < units) {
+        const int cg = u % CG;
+        const int q = (u / CG) % NQ;
+        const int r = u / (CG * NQ);
+        const int ih = row0 + r, iw = col0 + 4 * cg;
+        // W_in % 4 == 0, iw % 4 == 0: a word is wholly inside or outside
+        const bool in_img = ih >= 0 && ih < H_in && iw >= 0 && iw < W_in;
+        uint32_t d[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) d[t] = in_img ? stg[sl][t] : zp4;
+        // 4x4 byte transposes: chunk e, dword g = byte e of channels 4g .. 4g+3
+        v4i chunk[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t t0 = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x05010400u);
+          const uint32_t t1 = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x07030602u);
+          const uint32_t t2 = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x05010400u);
+          const uint32_t t3 = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x07030602u);
+          chunk[0][g] = (int)__builtin_amdgcn_perm(t2, t0, 0x05040100u);
+          chunk[1][g] = (int)__builtin_amdgcn_perm(t2, t0, 0x07060302u);
+          chunk[2][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x05040100u);
+          chunk[3][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x07060302u);
+        }
+        v4i* dst = xs + (r * NQ + q) * HC;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[pos(4 * cg + e)] = chunk[e];
+      }
+    }
+  }
+
+  // ---- weights: one fragment per (tap, 32 channels) ----------------------
+  const int oc = oc0 + 32 * wave + lo;
+  const int occ = oc < OC ? oc : OC - 1;    // rows past OC read row OC - 1 (never stored)
+  const int8_t* wrow = a.w + (int64_t)occ * a.ldw + 16 * hi;
+  const int Kw = __builtin_amdgcn_readfirstlane((int)a.Kw);
+  // tap offsets are wave-uniform (scalar); only wrow differs between lanes
+  auto wfrag = [&](int t, int off) {
+    return *reinterpret_cast<const v4i*>(wrow + ((P.kh[t] * Kw + P.kw[t]) * IC + off));
+  };
+
+  constexpr int NF = 2 * kTR;   // pixel fragments: kTR rows x 2 column halves
+  v16i acc[NPH][NF];
+  int32_t wsum[NPH];
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph) {
+    wsum[ph] = 0;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[ph][f] = v16i{};
+  }
+
+  // weight fragments of one step; tap t's register is refilled with the next
+  // step's fragment right after its last product
+  const int nk = IC / 32;
+  v4i bw[P.T];
+#pragma unroll
+  for (int t = 0; t < P.T; ++t) bw[t] = wfrag(t, 0);
+  __syncthreads();
+
+  // A fragments of shift s, step k
+  auto aload = [&](v4i (&dst)[NF], int s_dh, int s_dw, int k) {
+    const int q = 2 * k + hi;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int r = (f >> 1) + s_dh - P.dhmin;
+      const int cidx = (f & 1) * 32 + lo + s_dw - P.dwmin + p.coff;
+      dst[f] = xs[(r * NQ + q) * HC + pos(cidx)];
+    }
+  };
+  v4i acur[NF], anext[NF];
+  aload(acur, P.sdh[0], P.sdw[0], 0);
+  auto step = [&](int k, v4i (&cur)[P.T]) {
+    const int knext = k + 1 < nk ? k + 1 : k;   // past the end: re-read (unused)
+    Static<0, P.NS>::each([&](auto SI) {
+      constexpr int s = decltype(SI)::value;
+      // the next shift's (or the next step's first shift's) fragments first
+      if constexpr (s + 1 < P.NS) aload(anext, P.sdh[s + 1], P.sdw[s + 1], k);
+      else aload(anext, P.sdh[0], P.sdw[0], knext);
+      Static<0, P.T>::each([&](auto TI) {
+        constexpr int t = decltype(TI)::value;
+        if constexpr (P.sh[t] == s) {
+          constexpr int ph = P.ph[t];
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            acc[ph][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[f], cur[t], acc[ph][f], 0, 0, 0);
+          int32_t w4 = __builtin_amdgcn_sdot4(cur[t][0], 0x01010101, 0, false);
+          w4 = __builtin_amdgcn_sdot4(cur[t][1], 0x01010101, w4, false);
+          w4 = __builtin_amdgcn_sdot4(cur[t][2], 0x01010101, w4, false);
+          w4 = __builtin_amdgcn_sdot4(cur[t][3], 0x01010101, w4, false);
+          wsum[ph] += w4;
+          cur[t] = wfrag(t, 32 * knext);
+        }
+      });
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acur[f] = anext[f];
+    });
+  };
+  for (int k = 0; k < nk; ++k) step(k, bw);
+
+  // ---- epilogue: requantize into the LDS output block ----------------------
+  // lanes l and l + 32 hold the two 16-channel halves of each weight
+  // fragment; zw = input zero point x the phase's weight sum, once per phase
+  int32_t zw[NPH];
+#pragma unroll
+  for (int ph = 0; ph < NPH; ++ph) zw[ph] = a.izp * (wsum[ph] + __shfl_xor(wsum[ph], 32, 64));
+  const int ocl = 32 * wave + lo;
+  const bool oc_ok = oc < OC;
+  float sc = 0.0f, bi = 0.0f;
+  if (oc_ok && !a.acc) {
+    sc = a.wscale[oc];
+    bi = a.bias ? a.bias[oc] : 0.0f;
+  }
+  const int H_out = (int)a.H_out, W_out = (int)a.W_out;
+  if (a.acc) {
+    // accumulator output (verification entry point): direct int32 stores
+    if (oc_ok) {
+      Static<0, NPH>::each([&](auto PI) {
+        constexpr int ph = decltype(PI)::value;
+        constexpr int rh = ph / S, rw = ph % S;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ii = i0 + (f >> 1);
+            const int j = j0 + (f & 1) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const int oh = S * ii + rh, ow = S * j + rw;
+            if (oh < H_out && ow < W_out)
+              a.acc[(((int64_t)n * OC + oc) * H_out + oh) * W_out + ow] = acc[ph][f][r] - zw[ph];
+          }
+      });
+    }
+    return;
+  }
+  // lane: 4 consecutive phase columns x S column residues = 4*S consecutive
+  // output columns of one output row per (row residue, fragment, group)
+#pragma unroll
+  for (int rh = 0; rh < S; ++rh)
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        int qv[4 * S];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int rw = 0; rw < S; ++rw) {
+            const int ph = rh * S + rw;
+            qv[S * e + rw] = requant(acc[ph][f][4 * g + e] - zw[ph], sc, bi, a.rq);
+          }
+        const int orow = (f >> 1) * S + rh;
+        const int col = S * ((f & 1) * 32 + 8 * g + 4 * hi);
+        int8_t* d = os + (ocl * OROWS + orow) * OPITCH + col;
+        if constexpr (S == 2) {
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<v2u*>(d) =
+              v2u{pack4(qv[0], qv[1], qv[2], qv[3]), pack4(qv[4], qv[5], qv[6], qv[7])};
+        } else {
+          *reinterpret_cast<uint32_t*>(d) = pack4(qv[0], qv[1], qv[2], qv[3]);
+        }
+      }
+  __syncthreads();
+
+  // ---- copy the output block out: 16-byte pieces, whole rows ---------------
+  constexpr int PIECES = OCOLS / 16;
+  const int oh0 = S * i0, ow0 = S * j0;
+  for (int u = tid; u < kOCB * OROWS * PIECES; u += kThreads) {
+    const int pc = u % PIECES;
+    const int rr = u / PIECES;
+    const int orow = rr % OROWS;
+    const int ocq = rr / OROWS;
+    const int occ2 = oc0 + ocq, oh = oh0 + orow, ow = ow0 + 16 * pc;
+    if (occ2 >= OC || oh >= H_out || ow >= W_out) continue;
+    const int8_t* s_ = os + (ocq * OROWS + orow) * OPITCH + 16 * pc;
+    int8_t* g_ = a.out + (((int64_t)n * OC + occ2) * H_out + oh) * W_out + ow;
+    if (p.out_vec && ow + 16 <= W_out) {
+      *reinterpret_cast<v4i*>(g_) = *reinterpret_cast<const v4i*>(s_);
+    } else {
+      for (int e = 0; e < 16 && ow + e < W_out; ++e) g_[e] = s_[e];
+    }
+  }
+}
+
+template <int S, int K, int PM, bool FWD>
+bool plan_t(const DeconvArgs& a, FxPlan& p, size_t& lds) {
+  constexpr Pattern<S, K, PM, FWD> P{};
+  p = FxPlan{};
+  p.base_h = FWD ? -(int)a.ph : (int)(a.ph - PM) / S;
+  p.base_w = FWD ? -(int)a.pw : (int)(a.pw - PM) / S;
+  const int dwmin = P.dwmin + p.base_w;
+  p.coff = ((dwmin % 4) + 4) % 4;
+  p.HR = P.dhmax - P.dhmin + kTR;
+  p.HC = (p.coff + kTJ + P.dwmax - P.dwmin + 7) / 8 * 8;
+  const int64_t NQ = a.IC / 16;
+  if (p.HR * NQ * (p.HC / 4) > (int64_t)kStageSlots * kThreads) return false;
+  p.Hp = (int)((a.H_out + S - 1) / S);
+  p.Wp = (int)((a.W_out + S - 1) / S);
+  p.tiles_i = (p.Hp + kTR - 1) / kTR;
+  p.tiles_j = (p.Wp + kTJ - 1) / kTJ;
+  p.tiles_oc = (int)((a.OC + kOCB - 1) / kOCB);
+  p.out_vec = (a.W_out % 16 == 0) && (((uintptr_t)a.out & 15) == 0);
+  const int64_t blocks = (int64_t)a.N * p.tiles_i * p.tiles_j * p.tiles_oc;
+  p.xcd = blocks % 8 == 0;
+  lds = (size_t)p.HR * NQ * p.HC * 16 + (size_t)kOCB * kTR * S * (kTJ * S + 16);
+  return blocks < ((int64_t)1 << 31) && lds <= 160 * 1024;
+}
+
+template <int S, int K, int PM, bool FWD>
+hipError_t launch_t(const DeconvArgs& a, hipStream_t s) {
+  FxPlan p;
+  size_t lds = 0;
+  if (!plan_t<S, K, PM, FWD>(a, p, lds)) return hipErrorInvalidValue;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_deconv_fixed<S, K, PM, FWD>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t blocks = (int64_t)a.N * p.tiles_i * p.tiles_j * p.tiles_oc;
+  hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD>), dim3((unsigned)blocks), dim3(kThreads),
+                     lds, s, a, p);
+  return hipGetLastError();
+}
+
+// Which instance takes a shape: 0 = none.
+int pick(const DeconvArgs& a, bool fwd) {
+  if (a.groups != 1 || a.dil_h != 1 || a.dil_w != 1 || a.Kh != a.Kw) return 0;
+  if (a.IC % 64 != 0 || a.IC > 4096 || a.ldw % 16 != 0 || ((uintptr_t)a.w & 15) != 0) return 0;
+  if (a.W_in % 4 != 0 || ((uintptr_t)a.x & 3) != 0) return 0;
+  if (a.OC > (1 << 20) || a.H_out > (1 << 20) || a.W_out > (1 << 20) || a.H_in > (1 << 20) ||
+      a.W_in > (1 << 20) || a.N > (1 << 20) || a.ph > 4096 || a.pw > 4096)
+    return 0;
+  if (fwd) {
+    if (a.sh != 1 || a.sw != 1 || a.Kh != 3) return 0;
+    return 1;
+  }
+  if (a.sh != 2 || a.sw != 2 || (a.ph % 2) != (a.pw % 2)) return 0;
+  if (a.Kh == 3) return a.ph % 2 ? 2 : 3;
+  if (a.Kh == 4) return a.ph % 2 ? 4 : 5;
+  return 0;
+}
+
+hipError_t launch_pick(const DeconvArgs& a, int k, hipStream_t s) {
+  switch (k) {
+    case 1: return launch_t<1, 3, 0, true>(a, s);
+    case 2: return launch_t<2, 3, 1, false>(a, s);
+    case 3: return launch_t<2, 3, 0, false>(a, s);
+    case 4: return launch_t<2, 4, 1, false>(a, s);
+    case 5: return launch_t<2, 4, 0, false>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool fits(const DeconvArgs& a, int k) {
+  FxPlan p;
+  size_t lds;
+  switch (k) {
+    case 1: return plan_t<1, 3, 0, true>(a, p, lds);
+    case 2: return plan_t<2, 3, 1, false>(a, p, lds);
+    case 3: return plan_t<2, 3, 0, false>(a, p, lds);
+    case 4: return plan_t<2, 4, 1, false>(a, p, lds);
+    case 5: return plan_t<2, 4, 0, false>(a, p, lds);
+    default: return false;
+  }
+}
+
+}  // namespace
+
+bool deconv_fixed_supported(const DeconvArgs& a) {
+  const int k = pick(a, false);
+  return k && fits(a, k);
+}
+
+// The default choice for shapes with at least one workgroup per CU (256 tiles
+// of two phase rows x 64 columns x 128 channels); smaller problems are
+// latency-bound and run faster on the tiled 16x16x64 kernel.
+bool deconv_fixed_preferred(const DeconvArgs& a) {
+  if (!deconv_fixed_supported(a)) return false;
+  const int64_t Hp = (a.H_out + 1) / 2, Wp = (a.W_out + 1) / 2;
+  const int64_t tiles = a.N * ((Hp + kTR - 1) / kTR) * ((Wp + kTJ - 1) / kTJ) * ((a.OC + kOCB - 1) / kOCB);
+  return tiles >= 256;
+}
+
+bool conv_fixed_supported(const DeconvArgs& a) {
+  const int k = pick(a, true);
+  return k && fits(a, k);
+}
+
+hipError_t launch_deconv_fixed(const DeconvArgs& a, hipStream_t s) {
+  return launch_pick(a, pick(a, false), s);
+}
+
+hipError_t launch_conv_fixed(const DeconvArgs& a, hipStream_t s) {
+  return launch_pick(a, pick(a, true), s);
+}
+
+}  // namespace q8ta

@@ -72,8 +72,7 @@ __device__ __forceinline__ float requant_code(int32_t acc, float wscale, float b
   float t = v * r.inv_out;
   float q = __builtin_rintf(t);
   q = q + r.ozp;
-  q = __builtin_fmaxf(q, r.qmin);
-  q = __builtin_fminf(q, 127.0f);
+  q = __builtin_amdgcn_fmed3f(q, r.qmin, 127.0f);
   return q;
 }
 

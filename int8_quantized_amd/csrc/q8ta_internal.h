@@ -37,8 +37,7 @@ __device__ __forceinline__ int requant(int32_t acc, float wscale, float b, const
   float t = v * r.inv_out;
   float q = __builtin_rintf(t);
   q = q + r.ozp;
-  q = __builtin_fmaxf(q, r.qmin);
-  q = __builtin_fminf(q, 127.0f);
+  q = __builtin_amdgcn_fmed3f(q, r.qmin, 127.0f);   // clamp to [qmin, 127] in one instruction
   return (int)q;
 }
 
@@ -49,8 +48,7 @@ __device__ __forceinline__ int quantize1(float x, float inv, float zp) {
   float t = x * inv;
   float r = __builtin_rintf(t);
   float u = r + zp;
-  u = __builtin_fmaxf(u, -128.0f);
-  u = __builtin_fminf(u, 127.0f);
+  u = __builtin_amdgcn_fmed3f(u, -128.0f, 127.0f);
   return (int)u;
 }
 
@@ -59,9 +57,11 @@ __device__ __forceinline__ float dequant1(int q, int zp, float scale) {
   return (float)(q - zp) * scale;
 }
 
+// Low bytes of a, b, c, d as one little-endian word (three byte permutes).
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-         ((uint32_t)(d & 0xff) << 24);
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Lane moves inside a row of 16 lanes (DPP controls of the gfx9 encoding).
@@ -242,6 +242,16 @@ hipError_t launch_row_sums(const int8_t* w, int64_t N, int64_t K, int32_t* out, 
 hipError_t launch_row_sums_generic(const int8_t* w, int64_t N, int64_t K, int64_t ldw, int32_t* out,
                                    hipStream_t s);
 hipError_t launch_deconv_generic(const DeconvArgs& a, hipStream_t s);
+hipError_t launch_deconv_fixed(const DeconvArgs& a, hipStream_t s);
+bool deconv_fixed_supported(const DeconvArgs& a);
+bool deconv_fixed_preferred(const DeconvArgs& a);
+hipError_t launch_conv_fixed(const DeconvArgs& a, hipStream_t s);
+bool conv_fixed_supported(const DeconvArgs& a);
+hipError_t launch_deconv_mx(const DeconvArgs& a, hipStream_t s);
+bool deconv_mx_supported(const DeconvArgs& a);
+hipError_t launch_conv_mx(const DeconvArgs& a, hipStream_t s);
+bool conv_mx_supported(const DeconvArgs& a);
+bool conv_mx_preferred(const DeconvArgs& a);
 hipError_t launch_deconv_mfma(const DeconvArgs& a, hipStream_t s);
 bool deconv_mfma_supported(const DeconvArgs& a);
 hipError_t launch_conv_mfma(const DeconvArgs& a, hipStream_t s);

@@ -378,8 +378,9 @@ def test_select_kernel_names():
     others (leaving the choice unchanged) and makes no HIP call."""
     lib = q8.lib()
     for op, kernels in (("linear", ("generic",)),
-                        ("conv2d_transposed", ("mfma", "igemm", "tiled", "generic")),
-                        ("conv2d", ("mfma", "igemm", "generic"))):
+                        ("conv2d_transposed", ("fixed", "mfma32", "mfma", "igemm", "tiled",
+                                               "generic")),
+                        ("conv2d", ("fixed", "mfma32", "mfma", "igemm", "generic"))):
         for k in kernels + ("default",):
             _st(lib.q8ta_select_kernel(op.encode(), k.encode()), q8.Q8TA_OK)
         _st(lib.q8ta_select_kernel(op.encode(), b"dot4"), q8.Q8TA_ERR_UNSUPPORTED, "unknown kernel")

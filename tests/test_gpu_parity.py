@@ -431,6 +431,122 @@ def test_deconv_tiled_kernel(case):
         np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
 
 
+# Shapes the 32x32x32 matrix-core transposed conv takes (IC % 32 == 0,
+# W_in % 4 == 0, strides up to 2): several channel tiles and a partly empty
+# last one, ragged column tiles, one-sided strides, dilation, phases without
+# taps, padding beyond the kernel, cropped and enlarged outputs, IC not a
+# multiple of 64, and a padded weight row.
+DECONV_MX_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, stride, pad, out_pad, dilation, H_out, W_out, ldw_extra
+    (2, 64, 12, 20, 160, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), None, None, 0),
+    (1, 96, 9, 36, 33, 4, 4, (2, 2), (1, 1), (0, 0), (1, 1), None, None, 32),
+    (1, 32, 7, 16, 40, 3, 3, (1, 2), (1, 1), (0, 1), (1, 1), None, None, 0),
+    (1, 64, 6, 16, 48, 3, 4, (2, 1), (0, 2), (1, 0), (1, 1), None, None, 0),
+    (1, 64, 5, 136, 48, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), None, None, 0),
+    (1, 64, 8, 12, 32, 3, 3, (2, 2), (2, 2), (1, 1), (2, 2), None, None, 0),
+    (1, 32, 5, 8, 32, 1, 1, (2, 2), (0, 0), (1, 1), (1, 1), None, None, 0),
+    (2, 128, 6, 8, 64, 5, 5, (2, 2), (4, 4), (1, 1), (1, 1), None, None, 0),
+    (1, 64, 8, 8, 32, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), 9, 21, 0),
+    (1, 32, 4, 12, 24, 4, 4, (2, 2), (1, 1), (0, 0), (1, 1), 12, 40, 0),
+    (2, 256, 5, 16, 128, 3, 3, (2, 2), (1, 1), (1, 1), (1, 1), None, None, 16),
+    (1, 64, 32, 32, 32, 4, 4, (2, 2), (1, 1), (0, 0), (1, 1), None, None, 0),
+]
+
+
+@pytest.mark.parametrize("case", DECONV_MX_CASES, ids=[str(i) for i in range(len(DECONV_MX_CASES))])
+@pytest.mark.parametrize("act", ["none", "relu"])
+def test_deconv_mfma32_parity(case, act):
+    N, IC, H, W, OC, Kh, Kw, s, p, op, d, Ho, Wo, extra = case
+    _say(f"deconv mfma32 case={case} act={act}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 31, N, IC, H, W, OC, Kh, Kw, s, p, op,
+                       H_out=Ho, W_out=Wo, ldw=Kh * Kw * IC + extra, dilation=d)
+    with kernel("conv2d_transposed", "mfma32"):
+        np.testing.assert_array_equal(_run_deconv(c, activation=act),
+                                      _oracle_deconv(c, activation=act))
+        if act == "none":
+            np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+            np.testing.assert_array_equal(_run_deconv(c, bias=False), _oracle_deconv(c, bias=False))
+
+
+CONV2D_MX_CASES = [
+    # N, IC, H, W, OC, Kh, Kw, pad, dil, ldw_extra
+    (2, 64, 10, 12, 40, 3, 3, (1, 1), (1, 1), 0),
+    (1, 32, 7, 16, 160, 5, 5, (2, 2), (1, 1), 16),
+    (1, 64, 9, 8, 48, 3, 3, (2, 2), (2, 2), 0),
+    (1, 128, 7, 40, 64, 1, 1, (0, 0), (1, 1), 0),
+    (1, 96, 6, 132, 32, 3, 3, (0, 1), (1, 1), 0),
+    (2, 256, 8, 8, 128, 3, 3, (1, 1), (1, 1), 0),
+]
+
+
+@pytest.mark.parametrize("case", CONV2D_MX_CASES, ids=[str(i) for i in range(len(CONV2D_MX_CASES))])
+def test_conv2d_mfma32_parity(case):
+    N, IC, H, W, OC, Kh, Kw, p, d, extra = case
+    _say(f"conv2d mfma32 case={case}")
+    c = qi.conv_case(sum([N, IC, H, W, OC, Kh, Kw]) + 41, N, IC, H, W, OC, Kh, Kw, (1, 1), p, d,
+                     ldw=Kh * Kw * IC + extra)
+    with kernel("conv2d", "mfma32"):
+        np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
+        np.testing.assert_array_equal(_acc_conv(c), oracle.conv2d_acc(
+            c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out))
+        np.testing.assert_array_equal(_run_conv(c, activation="relu"),
+                                      _oracle_conv(c, activation="relu"))
+
+
+# Shapes the compile-time-pattern transposed conv takes (3x3 and 4x4, stride
+# 2, IC % 64 == 0, W_in % 4 == 0): several channel tiles (the last partly
+# empty), OC not a multiple of 32, several and ragged column tiles with
+# byte-wise stores, both parities of the padding, odd output sizes, a padded
+# weight row.
+DECONV_FIXED_CASES = [
+    # N, IC, H, W, OC, K, pad, out_pad
+    (2, 64, 12, 20, 160, 3, (1, 1), (1, 1)),
+    (1, 128, 9, 36, 33, 4, (1, 1), (0, 0)),
+    (1, 64, 7, 136, 48, 3, (0, 0), (1, 1)),
+    (1, 64, 6, 16, 64, 4, (2, 2), (0, 0)),
+    (2, 192, 5, 12, 130, 3, (2, 2), (1, 1)),
+    (1, 64, 8, 8, 32, 4, (3, 3), (1, 1)),
+    (1, 64, 32, 32, 32, 4, (1, 1), (0, 0)),
+]
+
+
+@pytest.mark.parametrize("case", DECONV_FIXED_CASES, ids=[str(i) for i in range(len(DECONV_FIXED_CASES))])
+@pytest.mark.parametrize("act", ["none", "relu"])
+def test_deconv_fixed_parity(case, act):
+    N, IC, H, W, OC, K, p, op = case
+    _say(f"deconv fixed case={case} act={act}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, K]) + 61, N, IC, H, W, OC, K, K, (2, 2), p, op,
+                       ldw=K * K * IC + 16)
+    with kernel("conv2d_transposed", "fixed"):
+        np.testing.assert_array_equal(_run_deconv(c, activation=act),
+                                      _oracle_deconv(c, activation=act))
+        if act == "none":
+            np.testing.assert_array_equal(_acc_deconv(c), _oracle_deconv_acc(c))
+            np.testing.assert_array_equal(_run_deconv(c, bias=False), _oracle_deconv(c, bias=False))
+
+
+CONV2D_FIXED_CASES = [
+    # N, IC, H, W, OC, pad
+    (2, 64, 10, 12, 40, (1, 1)),
+    (1, 128, 7, 132, 160, (0, 1)),
+    (2, 256, 8, 8, 128, (1, 1)),
+    (1, 64, 9, 8, 48, (2, 2)),
+]
+
+
+@pytest.mark.parametrize("case", CONV2D_FIXED_CASES, ids=[str(i) for i in range(len(CONV2D_FIXED_CASES))])
+def test_conv2d_fixed_parity(case):
+    N, IC, H, W, OC, p = case
+    _say(f"conv2d fixed case={case}")
+    c = qi.conv_case(sum([N, IC, H, W, OC]) + 71, N, IC, H, W, OC, 3, 3, (1, 1), p, (1, 1))
+    with kernel("conv2d", "fixed"):
+        np.testing.assert_array_equal(_run_conv(c), _oracle_conv(c))
+        np.testing.assert_array_equal(_acc_conv(c), oracle.conv2d_acc(
+            c.x, c.w, c.in_zp, c.Kh, c.Kw, c.stride, c.padding, c.dilation, c.H_out, c.W_out))
+        np.testing.assert_array_equal(_run_conv(c, activation="relu"),
+                                      _oracle_conv(c, activation="relu"))
+
+
 def test_deconv_epilogue_on_rounding_ties():
     """x == input zero point everywhere: the accumulator is 0 and the bias (one
     value per output channel, on and beside rounding ties) is requantized."""
