@@ -366,6 +366,10 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   __syncthreads();
 
   constexpr int NWS = PRE ? 1 : C::WAVES_M;
+  // Interior tiles of an output with fewer than 2^31 elements take the store
+  // path without bounds checks: each lane's element offset is one 32-bit
+  // value per channel, and the row offsets c * N are wave-uniform (scalar).
+  const bool fast = bm0 + C::BM <= M && bn0 + C::BN <= N && M * N <= (int64_t)INT32_MAX;
   if constexpr (TR) {
     // lane l: channel n of tile row wn*WN + i*32 + l % 32; register r: output
     // row m of fragment j at 8 * (r / 4) + 4 * (l / 32) + r % 4
@@ -379,7 +383,19 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
       const int32_t zc = a.izp * ws;
       const float sc = epi_sc[sl], bi = epi_bi[sl];
       const int64_t n = bn0 + rr;
-      if (n < N) {
+      if (fast) {
+        const uint32_t lane_off = (uint32_t)((bm0 + wm * C::WM + 4 * kg) * N + n);
+        Static<0, C::FM>::each([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Static<0, 16>::each([&](auto R) {
+            constexpr int r = decltype(R)::value;
+            constexpr int c = j * 32 + 8 * (r / 4) + r % 4;
+            const float q = requant_code(acc[i][j][r] - zc, sc, bi, a.rq);
+            float* rb = a.outf + (int64_t)c * N;   // wave-uniform row base
+            rb[lane_off] = (q - dq_zpf) * a.dq_scale;
+          });
+        });
+      } else if (n < N) {
         Static<0, C::FM>::each([&](auto J) {
           constexpr int j = decltype(J)::value;
           Static<0, 16>::each([&](auto R) {
@@ -416,6 +432,18 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
       int32_t zc[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) zc[r] = a.izp * wsv[r];
+      if (fast && vec_out && !a.acc) {
+        const uint32_t lane_off = (uint32_t)((bm0 + wm * C::WM + lrow) * N + nb);
+        Static<0, C::FM>::each([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          float q[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) q[r] = requant_code(acc[i][j][4 * g + r] - zc[r], sc[r], bi[r], a.rq);
+          int8_t* rb = a.out + (int64_t)(j * 32) * N;   // wave-uniform row base
+          *reinterpret_cast<uint32_t*>(rb + lane_off) = pack4((int)q[0], (int)q[1], (int)q[2], (int)q[3]);
+        });
+        return;
+      }
       Static<0, C::FM>::each([&](auto J) {
         constexpr int j = decltype(J)::value;
         const int64_t m = bm0 + wm * C::WM + j * 32 + lrow;

@@ -259,6 +259,7 @@ __global__ __launch_bounds__(kNT, 2) void k_gemm_pk(LinearArgs a, int tiles_m, i
   epi_bi[cslot(tid)] = e_bi;
   __syncthreads();
 
+  const bool fast = bm0 + kBM <= M && bn0 + kBN <= N && M * N <= (int64_t)INT32_MAX;
   if constexpr (TR) {
     // lane l: channel of tile row wn*64 + i*32 + l % 32; register r: output
     // row m of fragment j at 8 * (r / 4) + 4 * (l / 32) + r % 4
@@ -270,7 +271,20 @@ __global__ __launch_bounds__(kNT, 2) void k_gemm_pk(LinearArgs a, int tiles_m, i
       const int32_t zc = a.izp * epi_ws[sl];
       const float sc = epi_sc[sl], bi = epi_bi[sl];
       const int64_t n = bn0 + rr;
-      if (n < N) {
+      if (fast) {
+        // interior tile: one 32-bit lane offset, wave-uniform row bases
+        const uint32_t lane_off = (uint32_t)((bm0 + 4 * kg) * N + n);
+        Static<0, kFM>::each([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Static<0, 16>::each([&](auto R) {
+            constexpr int r = decltype(R)::value;
+            constexpr int c = j * 32 + 8 * (r / 4) + r % 4;
+            const float q = requant_code(acc[i][j][r] - zc, sc, bi, a.rq);
+            float* rb = a.outf + (int64_t)c * N;
+            rb[lane_off] = (q - dq_zpf) * a.dq_scale;
+          });
+        });
+      } else if (n < N) {
         Static<0, kFM>::each([&](auto J) {
           constexpr int j = decltype(J)::value;
           Static<0, 16>::each([&](auto R) {
