@@ -113,7 +113,7 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
 
   const int H_in = (int)a.H_in, W_in = (int)a.W_in, IC = (int)a.IC;
   const int row0 = i0 + p.dhmin;                 // input row of LDS row 0
-  const int col0 = ((j0 + p.dwmin) >> 2) << 2;   // input column of LDS column 0 (floor to 4)
+  const int col0 = ((j0 + p.dwmin) >> 2) * 4;   // input column of LDS column 0 (floor to 4)
 
   // ---- 1. stage the input halo tile -------------------------------------
   {
@@ -483,7 +483,7 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
   if (p.WO > 2) p.WO = 2;
   p.OCB = p.WO * ocf;
   p.ICP = (int)((a.IC + 63) / 64 * 64);
-  const int c_lo = ((dwmin) >> 2) << 2;   // relative to j0, j0 is a multiple of 16
+  const int c_lo = (dwmin >> 2) * 4;   // relative to j0, j0 is a multiple of 16
   const int c_hi = p.TJ - 1 + dwmax + 1;
   p.HC = ((c_hi - c_lo) + 3) / 4 * 4;
   p.OCols = sw * p.TJ;
