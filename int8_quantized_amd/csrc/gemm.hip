@@ -305,9 +305,10 @@ bool gemm_mfma_supported(const LinearArgs& a) {
 // per CU, store-first K loop: 125.7-126.4 us on 2048 x 4096 x 11008 with the
 // fused dequantize, against 131-135 us for a 256 x 128 tile of this file);
 // the rest the 128 x 128 tile, or the 128 x 64 tile for few rows.
-hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s) {
+hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s, char kind) {
   const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
   const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (kind == 'x') return launch_gemm_mx(a, s);
   if (tv >= 256 && a.K >= 1024) return launch_gemm_mx(a, s);
   if (tm >= 256 || a.M > 64) return launch_cfg<CfgM>(a, s);
   return launch_cfg<CfgS>(a, s);

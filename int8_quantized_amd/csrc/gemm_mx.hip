@@ -9,25 +9,29 @@
 //    (3.7-3.9 with one or two waves per SIMD), one of v_mfma_i32_16x16x64_i8
 //    at ~2.4-3.0, so only the 32x32x32 form can approach the 5.0 POP/s dense
 //    int8 peak.
-//  * Each wave owns a WN x WM = 128 x 64 (or 64 x 128) sub-tile: 8
-//    accumulator fragments of 16 registers.  Every K byte then costs the wave
-//    WN + WM = 192 bytes of LDS fragment reads for 2 * WN * WM = 16384
-//    operations, 85 operations per LDS byte; the 64 x 64 wave tile of the
-//    16x16x64 kernel reads 128 bytes for 8192 (64 per byte), which puts the
-//    LDS port at the matrix cores' speed.
+//  * Each wave owns a 128 x 64 sub-tile (W rows x X rows): 8 accumulator
+//    fragments of 16 registers.  Every K byte then costs the wave 192 bytes
+//    of LDS fragment reads for 16384 operations.
 //  * Two workgroups of four waves share a CU (up to 256 registers per wave,
 //    two waves per SIMD, 2 x 24 KiB of LDS buffers): their barriers and
-//    epilogues are independent, so one workgroup's requantize and stores run
-//    while the other keeps the matrix cores busy.  (The one-workgroup
-//    variant keeps a whole SIMD per wave and 128-byte K steps.)
-//  * K advances BK bytes per step through two LDS buffers; the slabs are
+//    epilogues are independent.  A lone workgroup on a CU (the last partial
+//    wave of tiles) runs a tile in about half the time of a pair, so the CU's
+//    throughput is the same with one or two.
+//  * K advances 64 bytes per step through two LDS buffers.  The slabs are
 //    staged in registers (16 B per load; rows past M/N read the last row,
-//    chunks past K are zeroed) and written to the buffer the matrix cores are
-//    not reading; one barrier per step.  The default loop (PD = 3) writes
-//    step k + 1's registers to LDS at the top of step k and refills them with
-//    step k + 3 at once.  The 16-byte chunk c of LDS row r sits at chunk
-//    position c ^ f(r), f chosen so that the 16 lanes one ds_read_b128 cycle
-//    serves hit distinct banks.
+//    chunks past K are zeroed), loaded two steps ahead and written to the
+//    buffer the matrix cores are not reading; one barrier per step.  Within
+//    a step the issue order is fixed with scheduling barriers: slice 0's
+//    fragment reads, then the 16 products, the first six each followed by
+//    one LDS write of the next step's slab, the load refilling that register
+//    and one fragment read of slice 1.  (Measured on 2048 x 4096 x 11008:
+//    116-123 us against 124-131 us for the compiler's own order; loading
+//    the slabs straight into LDS with global_load_lds_dwordx4 over three
+//    stages measured 122-126 us, and 128-byte steps with one workgroup per
+//    CU 135 us.)
+//  * The 16-byte chunk c of LDS row r sits at chunk position c ^ f(r), f
+//    chosen so that the 16 lanes one ds_read_b128 cycle serves hit distinct
+//    banks.
 //  * Lane l supplies row l % 32 of each operand with K bytes 16 * (l / 32)
 //    .. +15 of each 32-byte slice; accumulator register r of lane l holds row
 //    8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the product.
@@ -36,9 +40,11 @@
 //    store); for fp32 output (fused dequantize) the operands swap, so lane l
 //    holds one channel and each half-wave store writes 32 consecutive floats
 //    of one row, a whole 128-byte line.
-//  * sum w comes from v_dot4 against 0x01010101 over the W fragments while
-//    they are in registers; the waves sharing a W strip split the K slices
-//    between them and add their partial sums through LDS after the loop.
+//  * sum w is taken in the loader: each thread sums the bytes of the W
+//    chunks it passes from global memory to LDS with v_dot4 against
+//    0x01010101 (steps past the last one, repeated fetches of the last slab,
+//    are masked out), and the four threads of a row add their partials after
+//    the loop.
 //  * Workgroups are dispatched round-robin over the 8 XCDs; the block index
 //    is remapped so that each XCD walks a contiguous run of tiles (M
 //    fastest), which share W and X slabs in that XCD's L2.
@@ -65,15 +71,11 @@ struct Static {
   }
 };
 
-template <int BN_, int BM_, int BK_, int WAVES_N_, int WAVES_M_, int BLOCKS_PER_CU_, int PD_ = 1>
-struct MxCfg {
-  // 1: one register set, loads one step ahead; 2: two sets, loads two steps
-  // ahead; 3: two sets, the LDS write of step k + 1 moved to the top of
-  // step k (see the K loop)
-  static constexpr int PD = PD_;
-  static constexpr int BN = BN_, BM = BM_, BK = BK_;
-  static constexpr int WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
-  static constexpr int BLOCKS_PER_CU = BLOCKS_PER_CU_;
+// 256 x 128 tiles (W rows x X rows), 2 x 2 waves of 128 x 64, 64-byte K
+// steps, two workgroups per CU.
+struct Cfg {
+  static constexpr int BN = 256, BM = 128, BK = 64;
+  static constexpr int WAVES_N = 2, WAVES_M = 2, BLOCKS_PER_CU = 2;
   static constexpr int NT = 64 * WAVES_N * WAVES_M;
   static constexpr int WN = BN / WAVES_N, WM = BM / WAVES_M;
   static constexpr int FN = WN / 32, FM = WM / 32;
@@ -82,13 +84,11 @@ struct MxCfg {
   static constexpr int A_LD = BN * CPR / NT;     // W chunks per thread per step
   static constexpr int B_LD = BM * CPR / NT;     // X chunks per thread per step
   static constexpr int STAGE = (BN + BM) * BK;   // bytes per LDS buffer
-  static_assert(BK == 64 || BK == 128, "BK");
-  static_assert(PD >= 1 && PD <= 3, "prefetch mode");
-  static_assert(WN % 32 == 0 && WM % 32 == 0, "wave tile");
+  static_assert(KS == 2, "two slices per step");
   static_assert((BN * CPR) % NT == 0 && (BM * CPR) % NT == 0, "loader");
   static_assert(NT % CPR == 0, "a thread keeps its chunk column");
   static_assert(BN <= NT, "one channel per thread in the epilogue staging");
-  static_assert(KS % WAVES_M == 0 || WAVES_M == 1, "row-sum split");
+  static_assert(A_LD + B_LD <= FN * FM && FN + FM <= A_LD + B_LD, "interleave slots");
 };
 
 // Chunk position of chunk c in LDS row r: c ^ f(r), f from row bits 1..4
@@ -132,6 +132,9 @@ __device__ __forceinline__ int cslot(int r) { return (r & 3) * (BN / 4) + (r >> 
 
 // PRE: the row sums of W come from a.wsum_pre (trusted, precomputed by the
 // caller) instead of v_dot4 over the W fragments.
+
+// PRE: the row sums of W come from a.wsum_pre (trusted, precomputed by the
+// caller) instead of the loader's v_dot4.
 // TR (fp32 output only): X is the A operand and W the B operand, so lane l
 // holds output channel l % 32 of its fragments and the 32 lanes of a
 // half-wave store 32 consecutive floats (one whole 128-byte line) of one
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   __shared__ __attribute__((aligned(16))) int8_t smem[2 * C::STAGE];
   __shared__ __attribute__((aligned(16))) float epi_sc[C::BN];
   __shared__ __attribute__((aligned(16))) float epi_bi[C::BN];
-  __shared__ __attribute__((aligned(16))) int32_t epi_ws[C::WAVES_M][C::BN];
+  __shared__ __attribute__((aligned(16))) int32_t epi_ws[C::BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,11 +188,9 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
     xrow[i] = a.x + (m < M ? m : M - 1) * K + lc * 16;
   });
 
-  // PD register sets of staged chunks: with PD = 2 the loads of step kt + 2
-  // are issued while step kt is computed and step kt + 1 waits in the other
-  // set, so each load has two steps to arrive.
-  constexpr int SETS = C::PD == 1 ? 1 : 2;
-  v4i ra[SETS][C::A_LD], rb[SETS][C::B_LD];
+  // Two register sets of staged chunks: while step kt is computed, the set
+  // holding step kt + 1 is written to LDS and refilled with step kt + 3.
+  v4i ra[2][C::A_LD], rb[2][C::B_LD];
   auto load_global = [&](int kt, auto SET) {
     constexpr int st = decltype(SET)::value;
     int64_t ko = (int64_t)kt * C::BK;
@@ -209,28 +210,16 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
       rb[st][i] = kin ? v : v4i{0, 0, 0, 0};
     });
   };
-  auto store_lds = [&](int buf, auto SET) {
-    constexpr int st = decltype(SET)::value;
-    int8_t* As = smem + buf * C::STAGE;
-    int8_t* Bs = As + C::BN * C::BK;
-    Static<0, C::A_LD>::each([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const int row = lr + i * RSTEP;
-      *reinterpret_cast<v4i*>(As + row * C::BK + 16 * swz<C::CPR>(row, lc)) = ra[st][i];
-    });
-    Static<0, C::B_LD>::each([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const int row = lr + i * RSTEP;
-      *reinterpret_cast<v4i*>(Bs + row * C::BK + 16 * swz<C::CPR>(row, lc)) = rb[st][i];
-    });
-  };
 
   v16i acc[C::FN][C::FM];
   Static<0, C::FN>::each([&](auto I) {
     Static<0, C::FM>::each([&](auto J) { acc[decltype(I)::value][decltype(J)::value] = v16i{}; });
   });
-  int32_t wsum[C::FN];
-  Static<0, C::FN>::each([&](auto I) { wsum[decltype(I)::value] = 0; });
+  // sum w in the loader: thread tid passes the W chunks of rows lr + i * RSTEP,
+  // chunk column lc, through its registers and sums their bytes with v_dot4
+  // as it writes them to LDS.
+  int32_t lsum[C::A_LD];
+  Static<0, C::A_LD>::each([&](auto I) { lsum[decltype(I)::value] = 0; });
 
   // Per-channel constants of tile row tid, fetched before the K loop so their
   // latency hides behind it.  Scales and bias exist only for the requantizing
@@ -247,117 +236,136 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   const int kg = lane >> 5;
   const int a_off = (wn * C::WN + lrow) * C::BK;
   const int b_off = C::BN * C::BK + (wm * C::WM + lrow) * C::BK;
-  auto compute = [&](int buf) {
-    const int8_t* S = smem + buf * C::STAGE;
-    Static<0, C::KS>::each([&](auto KSI) {
-      constexpr int ks = decltype(KSI)::value;
-      const int cpos = 16 * swz<C::CPR>(lrow, 2 * ks + kg);
-      v4i af[C::FN], bf[C::FM];
-      Static<0, C::FN>::each([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        af[i] = *reinterpret_cast<const v4i*>(S + a_off + i * 32 * C::BK + cpos);
-      });
-      Static<0, C::FM>::each([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        bf[j] = *reinterpret_cast<const v4i*>(S + b_off + j * 32 * C::BK + cpos);
-      });
+
+  // LDS write of staged chunk m of register set SET into buffer buf (W chunks
+  // first), with its row sums when it is a W chunk of a real step
+  auto write_chunk = [&](int8_t* As, auto SET, auto MI, int ones) {
+    constexpr int st = decltype(SET)::value, m = decltype(MI)::value;
+    int8_t* Bs = As + C::BN * C::BK;
+    if constexpr (m < C::A_LD) {
+      const int row = lr + m * RSTEP;
+      *reinterpret_cast<v4i*>(As + row * C::BK + 16 * swz<C::CPR>(row, lc)) = ra[st][m];
       if constexpr (!PRE) {
-        // the WAVES_M waves of one W strip take turns over the K slices
-        if (C::WAVES_M == 1 || ks % C::WAVES_M == wm) {
-          Static<0, C::FN>::each([&](auto I) {
-            constexpr int i = decltype(I)::value;
-            wsum[i] = __builtin_amdgcn_sdot4(af[i][0], 0x01010101, wsum[i], false);
-            wsum[i] = __builtin_amdgcn_sdot4(af[i][1], 0x01010101, wsum[i], false);
-            wsum[i] = __builtin_amdgcn_sdot4(af[i][2], 0x01010101, wsum[i], false);
-            wsum[i] = __builtin_amdgcn_sdot4(af[i][3], 0x01010101, wsum[i], false);
-          });
-        }
-      }
-      Static<0, C::FN>::each([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        Static<0, C::FM>::each([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          if constexpr (TR)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        Static<0, 4>::each([&](auto D) {
+          lsum[m] = __builtin_amdgcn_sdot4(ra[st][m][decltype(D)::value], ones, lsum[m], false);
         });
-      });
+      }
+    } else {
+      constexpr int q = m - C::A_LD;
+      const int row = lr + q * RSTEP;
+      *reinterpret_cast<v4i*>(Bs + row * C::BK + 16 * swz<C::CPR>(row, lc)) = rb[st][q];
+    }
+  };
+  auto load_chunk = [&](auto SET, auto MI, int64_t ko, bool kin) {
+    constexpr int st = decltype(SET)::value, m = decltype(MI)::value;
+    if constexpr (m < C::A_LD) {
+      const v4i v = *reinterpret_cast<const v4i*>(wrow[m] + ko);
+      ra[st][m] = kin ? v : v4i{0, 0, 0, 0};
+    } else {
+      constexpr int q = m - C::A_LD;
+      const v4i v = *reinterpret_cast<const v4i*>(xrow[q] + ko);
+      rb[st][q] = kin ? v : v4i{0, 0, 0, 0};
+    }
+  };
+  auto product = [&](const v4i (&af)[C::FN], const v4i (&bf)[C::FM], auto I, auto J) {
+    constexpr int i = decltype(I)::value, j = decltype(J)::value;
+    if constexpr (TR)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+  auto read_frag = [&](const int8_t* S, v4i (&af)[C::FN], v4i (&bf)[C::FM], auto KSI, auto R) {
+    constexpr int ks = decltype(KSI)::value, r = decltype(R)::value;
+    const int cpos = 16 * swz<C::CPR>(lrow, 2 * ks + kg);
+    if constexpr (r < C::FN)
+      af[r] = *reinterpret_cast<const v4i*>(S + a_off + r * 32 * C::BK + cpos);
+    else
+      bf[r - C::FN] = *reinterpret_cast<const v4i*>(S + b_off + (r - C::FN) * 32 * C::BK + cpos);
+  };
+  constexpr int NR = C::FN + C::FM;          // fragment reads per slice
+  constexpr int NW = C::A_LD + C::B_LD;      // staged chunks per step
+  constexpr int NP = C::FN * C::FM;          // products per slice
+  constexpr std::integral_constant<int, 0> K0{};
+  constexpr std::integral_constant<int, 1> K1{};
+
+  // Step on LDS buffer buf: its products, interleaved with writing register
+  // set SET (step st_step) into buffer nbuf and refilling SET with step
+  // ld_step.  The order is fixed with scheduling barriers (see the header).
+  auto step = [&](int buf, int nbuf, auto SET, int st_step, int ld_step) {
+    const int8_t* S = smem + buf * C::STAGE;
+    int8_t* As = smem + nbuf * C::STAGE;
+    v4i af[2][C::FN], bf[2][C::FM];
+    const int ones = st_step < KT ? 0x01010101 : 0;
+    int64_t ko = (int64_t)ld_step * C::BK;
+    bool kin = true;
+    if constexpr (!KFULL) {
+      kin = ko + lc * 16 < K;
+      if (!kin) ko = K - 16 - lc * 16;
+    }
+    Static<0, NR>::each([&](auto R) { read_frag(S, af[0], bf[0], K0, R); });
+    __builtin_amdgcn_sched_barrier(0);
+    Static<0, 2 * NP>::each([&](auto MI) {
+      constexpr int m = decltype(MI)::value;
+      constexpr int ks = m / NP, i = (m % NP) / C::FM, j = m % C::FM;
+      product(af[ks], bf[ks], std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
+      if constexpr (m < NW) {
+        write_chunk(As, SET, MI, ones);
+        load_chunk(SET, MI, ko, kin);
+      }
+      if constexpr (m < NR) read_frag(S, af[1], bf[1], K1, MI);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // a whole step from LDS buffer 0 without staging work (an odd last step)
+  auto step_last = [&]() {
+    v4i af[2][C::FN], bf[2][C::FM];
+    Static<0, NR>::each([&](auto R) {
+      read_frag(smem, af[0], bf[0], K0, R);
+      read_frag(smem, af[1], bf[1], K1, R);
+    });
+    Static<0, 2 * NP>::each([&](auto MI) {
+      constexpr int m = decltype(MI)::value;
+      constexpr int ks = m / NP, i = (m % NP) / C::FM, j = m % C::FM;
+      product(af[ks], bf[ks], std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
     });
   };
 
   // Loads and LDS writes are issued on every step, also past the last one
   // (the step index is clamped: a repeated fetch of the last slab, written to
   // the buffer no one reads any more), so the loop carries no branch around
-  // them.
+  // them.  Step kt reads LDS buffer kt % 2; at its top the register set
+  // holding step kt + 1 (loaded two steps earlier) goes to buffer (kt + 1) % 2
+  // -- read last in step kt - 1, before the barrier that ended it.
   constexpr std::integral_constant<int, 0> S0{};
+  constexpr std::integral_constant<int, 1> S1{};
   load_global(0, S0);
-  store_lds(0, S0);
-  if constexpr (C::PD == 1) {
+  Static<0, NW>::each([&](auto MI) { write_chunk(smem, S0, MI, 0x01010101); });
+  load_global(min(1, KT - 1), S1);
+  load_global(min(2, KT - 1), S0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    step(0, 1, S1, kt + 1, min(kt + 3, KT - 1));
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      load_global(min(kt + 1, KT - 1), S0);
-      compute(cur);
-      store_lds(cur ^ 1, S0);
-      __syncthreads();
-    }
-  } else if constexpr (C::PD == 2) {
-    constexpr std::integral_constant<int, 1> S1{};
-    load_global(min(1, KT - 1), S1);
+    step(1, 0, S0, kt + 2, min(kt + 4, KT - 1));
     __syncthreads();
-    // step kt reads LDS buffer kt % 2 and register set (kt + 1) % 2 holds
-    // step kt + 1; the body always runs both halves (a break between them
-    // would leave a path on which the wait counts turn conservative)
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-      load_global(min(kt + 2, KT - 1), S0);
-      compute(0);
-      store_lds(1, S1);
-      __syncthreads();
-      load_global(min(kt + 3, KT - 1), S1);
-      compute(1);
-      store_lds(0, S0);
-      __syncthreads();
-    }
-    if (kt < KT) compute(0);   // odd KT: the last step sits in buffer 0
-  } else {
-    // Store first: at the top of step kt the set holding step kt + 1 (loaded
-    // two steps earlier) is written to buffer (kt + 1) % 2 -- read last in
-    // step kt - 1, before the barrier that ended it -- and immediately
-    // refilled with step kt + 3; then step kt is computed from buffer
-    // kt % 2.  The LDS writes overlap the step's matrix-core work instead of
-    // delaying the barrier, and each load still has two steps to arrive.
-    constexpr std::integral_constant<int, 1> S1{};
-    load_global(min(1, KT - 1), S1);
-    load_global(min(2, KT - 1), S0);
-    __syncthreads();
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-      store_lds(1, S1);
-      load_global(min(kt + 3, KT - 1), S1);
-      compute(0);
-      __syncthreads();
-      store_lds(0, S0);
-      load_global(min(kt + 4, KT - 1), S0);
-      compute(1);
-      __syncthreads();
-    }
-    if (kt < KT) compute(0);   // odd KT: the last step sits in buffer 0
   }
+  if (kt < KT) step_last();   // odd KT: the last step sits in buffer 0
 
-  // Row sums: lane l holds a partial of row l % 32 of fragment i over its
-  // 16-byte halves (l / 32) of this wave's K slices; lanes l and l ^ 32 cover
-  // the row, the WAVES_M waves of the strip cover K.
+  // Row sums: the CPR threads of a row (consecutive lanes) add their chunk
+  // columns.
   if constexpr (!PRE) {
-    Static<0, C::FN>::each([&](auto I) {
+    Static<0, C::A_LD>::each([&](auto I) {
       constexpr int i = decltype(I)::value;
-      int32_t v = wsum[i];
-      v += __shfl_xor(v, 32, 64);
-      if (kg == 0) epi_ws[wm][cslot<C::BN>(wn * C::WN + i * 32 + lrow)] = v;
+      int32_t v = lsum[i];
+      Static<1, C::CPR>::each([&](auto B) {
+        constexpr int bit = decltype(B)::value;
+        if constexpr ((bit & (bit - 1)) == 0) v += __shfl_xor(v, bit, 64);
+      });
+      if (lc == 0) epi_ws[cslot<C::BN>(lr + i * RSTEP)] = v;
     });
   } else {
-    if (tid < C::BN) epi_ws[0][cslot<C::BN>(tid)] = e_ws;
+    if (tid < C::BN) epi_ws[cslot<C::BN>(tid)] = e_ws;
   }
   if (tid < C::BN) {
     epi_sc[cslot<C::BN>(tid)] = e_sc;
@@ -365,7 +373,6 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   }
   __syncthreads();
 
-  constexpr int NWS = PRE ? 1 : C::WAVES_M;
   // Interior tiles of an output with fewer than 2^31 elements take the store
   // path without bounds checks: each lane's element offset is one 32-bit
   // value per channel, and the row offsets c * N are wave-uniform (scalar).
@@ -378,9 +385,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
       constexpr int i = decltype(I)::value;
       const int rr = wn * C::WN + i * 32 + lrow;
       const int sl = cslot<C::BN>(rr);
-      int32_t ws = epi_ws[0][sl];
-      Static<1, NWS>::each([&](auto W) { ws += epi_ws[decltype(W)::value][sl]; });
-      const int32_t zc = a.izp * ws;
+      const int32_t zc = a.izp * epi_ws[sl];
       const float sc = epi_sc[sl], bi = epi_bi[sl];
       const int64_t n = bn0 + rr;
       if (fast) {
@@ -424,8 +429,7 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int sl = cslot<C::BN>(rr + r);
-        wsv[r] = epi_ws[0][sl];
-        Static<1, NWS>::each([&](auto W) { wsv[r] += epi_ws[decltype(W)::value][sl]; });
+        wsv[r] = epi_ws[sl];
         sc[r] = epi_sc[sl];
         bi[r] = epi_bi[sl];
       }
@@ -474,42 +478,37 @@ __global__ __launch_bounds__(C::NT, C::BLOCKS_PER_CU) void k_gemm_mx(LinearArgs 
   });
 }
 
-// Two workgroups per CU: 256 x 128 tiles, 128 x 64 per wave, 64-byte K steps,
-// store-first K loop (loads three steps ahead).
-using MxY3 = MxCfg<256, 128, 64, 2, 2, 2, 3>;
 
-template <class C, bool PRE>
+template <bool PRE>
 hipError_t launch_mx2(const LinearArgs& a, int tiles_m, int tiles_n, hipStream_t s) {
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   // fp32 output (fused dequantize): the transposed form, whole-line stores
   const bool tr = a.outf != nullptr && a.acc == nullptr;
-  if (a.K % C::BK == 0) {
+  if (a.K % Cfg::BK == 0) {
     if (tr)
-      hipLaunchKernelGGL((k_gemm_mx<C, PRE, true, true>), grid, dim3(C::NT), 0, s, a, tiles_m, tiles_n);
+      hipLaunchKernelGGL((k_gemm_mx<Cfg, PRE, true, true>), grid, dim3(Cfg::NT), 0, s, a, tiles_m,
+                         tiles_n);
     else
-      hipLaunchKernelGGL((k_gemm_mx<C, PRE, true, false>), grid, dim3(C::NT), 0, s, a, tiles_m,
+      hipLaunchKernelGGL((k_gemm_mx<Cfg, PRE, true, false>), grid, dim3(Cfg::NT), 0, s, a, tiles_m,
                          tiles_n);
   } else {
     if (tr)
-      hipLaunchKernelGGL((k_gemm_mx<C, PRE, false, true>), grid, dim3(C::NT), 0, s, a, tiles_m,
+      hipLaunchKernelGGL((k_gemm_mx<Cfg, PRE, false, true>), grid, dim3(Cfg::NT), 0, s, a, tiles_m,
                          tiles_n);
     else
-      hipLaunchKernelGGL((k_gemm_mx<C, PRE, false, false>), grid, dim3(C::NT), 0, s, a, tiles_m,
-                         tiles_n);
+      hipLaunchKernelGGL((k_gemm_mx<Cfg, PRE, false, false>), grid, dim3(Cfg::NT), 0, s, a,
+                         tiles_m, tiles_n);
   }
   return hipGetLastError();
 }
 
-template <class C>
-hipError_t launch_mx(const LinearArgs& a, hipStream_t s) {
-  const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
-  const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
-  if (a.wsum_pre) return launch_mx2<C, true>(a, tiles_m, tiles_n, s);
-  return launch_mx2<C, false>(a, tiles_m, tiles_n, s);
-}
-
 }  // namespace
 
-hipError_t launch_gemm_mx(const LinearArgs& a, hipStream_t s) { return launch_mx<MxY3>(a, s); }
+hipError_t launch_gemm_mx(const LinearArgs& a, hipStream_t s) {
+  const int tiles_m = (int)((a.M + Cfg::BM - 1) / Cfg::BM);
+  const int tiles_n = (int)((a.N + Cfg::BN - 1) / Cfg::BN);
+  if (a.wsum_pre) return launch_mx2<true>(a, tiles_m, tiles_n, s);
+  return launch_mx2<false>(a, tiles_m, tiles_n, s);
+}
 
 }  // namespace q8ta

@@ -228,7 +228,9 @@ bool make_phases(const DeconvArgs& a, Phases& p);
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 bool gemv_supported(const LinearArgs& a);
-hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s);
+// kind: 0 the default choice; 'x' the 32x32x32 kernel of gemm_mx.hip for any
+// shape.
+hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s, char kind = 0);
 bool gemm_mfma_supported(const LinearArgs& a);
 // 32x32x32 matrix-core GEMM for large problems (same operand requirements as
 // launch_gemm_mfma, which chooses it).

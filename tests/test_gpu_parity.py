@@ -188,7 +188,7 @@ GEMM_TILE_SHAPES = [(64, 128, 64), (70, 48, 300), (300, 1040, 257), (512, 4096, 
                     (1024, 1024, 8192), (1000, 1040, 8100), (33, 100, 70)]
 
 
-@pytest.mark.parametrize("path", ["default", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma32", "generic"])
 @pytest.mark.parametrize("M,K,N", GEMM_TILE_SHAPES)
 def test_linear_every_gemm_tile(path, M, K, N):
     _say(f"gemm {path} M={M} K={K} N={N}")
@@ -281,6 +281,38 @@ def test_gemv_workload():
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
     np.testing.assert_array_equal(_run_linear(c, fn=q8.q8ta_linear_gemv), _oracle_linear(c))
     np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+
+
+_gemm_reference = {}
+
+
+def _gemm_full_reference(c):
+    """The oracle's whole int8 output of the 2048 x 4096 x 11008 workload
+    (computed once per process)."""
+    if "q" not in _gemm_reference:
+        _gemm_reference["q"] = oracle.linear(c.x, c.w, c.weight_scales, c.bias, c.in_scale,
+                                             c.in_zp, c.out_scale, c.out_zp)
+    return _gemm_reference["q"]
+
+
+@pytest.mark.parametrize("path", ["default"])
+def test_gemm_workload_full(path):
+    """GEMM M=2048 K=4096 N=11008 in the benchmark's launch configuration,
+    every output element against the oracle, int8 (q8ta_linear) and fp32
+    (q8ta_linear_dq)."""
+    c = qi.make_gemm()
+    _say(f"gemm full {path} 2048x4096x11008")
+    ref = _gemm_full_reference(c)
+    out = torch.empty((c.M, c.N), dtype=torch.int8, device="cuda")
+    y = torch.empty((c.M, c.N), dtype=torch.float32, device="cuda")
+    with kernel("linear", path):
+        q8.q8ta_linear(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                       dev(c.bias), c.out_scale, c.out_zp, "none", out)
+        q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, dev(c.w), None, dev(c.weight_scales),
+                          dev(c.bias), c.out_scale, c.out_zp, "none", y)
+    np.testing.assert_array_equal(host(out), ref)
+    dq = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
+    np.testing.assert_array_equal(host(y).view(np.uint32), dq.view(np.uint32))
 
 
 def test_gemm_workload_sampled_rows_and_dequantize():
@@ -728,7 +760,7 @@ DQ_SHAPES = [(1, 4096, 4096), (3, 48, 17), (4, 64, 32), (65, 320, 97), (300, 104
 
 
 @pytest.mark.parametrize("M,K,N", DQ_SHAPES)
-@pytest.mark.parametrize("path", ["default", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma32", "generic"])
 def test_linear_dq_equals_linear_then_dequantize(M, K, N, path):
     """q8ta_linear_dq == dequantize_per_tensor(q8ta_linear(...)) bit for bit,
     against the oracle's two steps (default and shape-general kernels)."""
@@ -1074,7 +1106,7 @@ def test_weight_sums(N, K, offset):
     np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
 
 
-@pytest.mark.parametrize("path", ["default", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma32", "generic"])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
                                    (7, 33, 5), (40, 256, 64), (1024, 1024, 8192)])
 def test_linear_presummed_equals_linear(path, M, K, N):
@@ -1097,7 +1129,7 @@ def test_linear_presummed_equals_linear(path, M, K, N):
                                     dev(c.bias), c.out_scale, c.out_zp, "none", outf)
         dq = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
         np.testing.assert_array_equal(host(outf).view(np.uint32), dq.view(np.uint32))
-        if M > 4 and K % 16 == 0 and path == "default":
+        if M > 4 and K % 16 == 0 and path != "generic":
             # the matrix-core GEMM takes the sums (the shape-general kernel forms
             # (x - zp) * w directly): shifted sums shift the accumulator
             wrong = sums + 1000

@@ -47,7 +47,7 @@ NO_GPU = pytest.mark.skipif(_gpu_present(), reason="calls with fake device point
                                                    "meaningful without a GPU")
 
 KERNELS = {
-    "linear": ["default", "generic"],
+    "linear": ["default", "mfma32", "generic"],
     "conv2d_transposed": ["default", "fixed", "mfma32", "mfma", "igemm", "tiled", "generic"],
     "conv2d": ["default", "fixed", "mfma32", "mfma", "igemm", "generic"],
 }
