@@ -39,6 +39,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T]
                        [--profile-only gemm|gemm-and-copy|deconv|deconv-and-copy]
        python bench.py --summarize-counters FETCH.csv WRITE.csv --traffic-of gemm_mx|deconv_fixed
        python bench.py --summarize-trace TRACE.{db,csv} [--kernel SUBSTRING]
+                       [--window K --before SUBSTRING]
 """
 from __future__ import annotations
 
@@ -186,31 +187,43 @@ class Timer:
         return out
 
 
-def summarize_trace(path, kernel=None):
+def summarize_trace(path, kernel=None, window=0, before=None):
     """Per-kernel duration statistics of a rocprofv3 kernel trace (the rocpd
-    SQLite database or the kernel_trace CSV), as a text table."""
+    SQLite database or the kernel_trace CSV), as a text table.  With
+    `window` and `before`: also the statistics of the last `window` launches
+    of the kernels matching `kernel` that start before the first launch
+    matching `before` (the timed steps of a run, which the benchmark follows
+    with other kernels)."""
     rows = []
     if path.endswith(".db"):
         import sqlite3
         db = sqlite3.connect(path)
-        for name, dur in db.execute("select name, duration from kernels"):
-            rows.append((name, dur / 1e3))
+        for name, start, end in db.execute("select name, start, end from kernels"):
+            rows.append((name, int(start), int(end)))
     else:
         import csv
         with open(path) as f:
             for r in csv.DictReader(f):
-                rows.append((r["Kernel_Name"],
-                             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+                rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort(key=lambda r: r[1])
     by = {}
-    for name, us in rows:
+    for name, t0, t1 in rows:
         if kernel and kernel not in name:
             continue
-        by.setdefault(name, []).append(us)
+        by.setdefault(name, []).append((t1 - t0) / 1e3)
     out = [f"{'calls':>6} {'mean_us':>9} {'median_us':>9} {'p10_us':>9} {'p90_us':>9} "
            f"{'min_us':>9} {'max_us':>9}  kernel"]
     for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"{len(v):6d} {statistics.mean(v):9.2f} {pct(v, 0.5):9.2f} {pct(v, 0.1):9.2f} "
                    f"{pct(v, 0.9):9.2f} {min(v):9.2f} {max(v):9.2f}  {name[:160]}")
+    if window and before:
+        stop = next((t0 for name, t0, _ in rows if before in name), None)
+        sel = [(t1 - t0) / 1e3 for name, t0, t1 in rows
+               if (not kernel or kernel in name) and (stop is None or t0 < stop)][-window:]
+        if sel:
+            out.append(f"last {len(sel)} launches before the first '{before}': mean "
+                       f"{statistics.mean(sel):.2f}, median {pct(sel, 0.5):.2f}, p10 "
+                       f"{pct(sel, 0.1):.2f}, p90 {pct(sel, 0.9):.2f} us")
     return "\n".join(out)
 
 
@@ -302,6 +315,10 @@ def main():
     ap.add_argument("--summarize-trace", default=None,
                     help="print per-kernel duration statistics of a rocprofv3 kernel trace")
     ap.add_argument("--kernel", default=None, help="with --summarize-trace: kernel name filter")
+    ap.add_argument("--window", type=int, default=0,
+                    help="with --summarize-trace and --before: statistics of the last WINDOW "
+                         "matching launches before the first launch matching --before")
+    ap.add_argument("--before", default=None)
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     default=None, help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, "
                     "WRITE_SIZE) into profiles/traffic_<--traffic-of>.json")
@@ -311,7 +328,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.kernel))
+        print(summarize_trace(args.summarize_trace, args.kernel, args.window, args.before))
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.traffic_of, args.command))
