@@ -397,10 +397,13 @@ hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s) {
 }
 
 // quantize_per_tensor -> transposed conv with an fp32 input (a.xf): the
-// implicit GEMM quantizes while it copies the input; the other paths (the
-// matrix-core kernel first) quantize into a stream-ordered int8 workspace.
+// compile-time-pattern kernel and the implicit GEMM quantize while they stage
+// or copy the input; the other paths quantize into a stream-ordered int8
+// workspace.
 hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s) {
   const char k = deconv_family(a);
+  if ((k == 0 && deconv_fixed_preferred(a)) || (k == 'f' && deconv_fixed_supported(a)))
+    return launch_deconv_fixed(a, s);
   const bool mfma = ((k == 0 || k == 'm') && deconv_mfma_supported(a)) ||
                     (k == 0 && deconv_fixed_preferred(a)) ||
                     (k == 'x' && deconv_mx_supported(a)) ||

@@ -128,7 +128,10 @@ __device__ __forceinline__ int pos(int c) { return c ^ (((c >> 4) & 1) << 2); }
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int e) { return (w >> (8 * e)) & 0xffu; }
 
-template <int S, int K, int PM, bool FWD>
+// XF: the input is fp32 (a.xf; the fused quantize -> transposed conv) and is
+// quantized with the quantize_per_tensor formula as the halo is staged, so
+// the int8 input never goes to memory.
+template <int S, int K, int PM, bool FWD, bool XF>
 __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPlan p) {
   constexpr Pattern<S, K, PM, FWD> P{};
   constexpr int NPH = S * S;
@@ -161,63 +164,112 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
 
   const int H_in = (int)a.H_in, W_in = (int)a.W_in, IC = (int)a.IC, OC = (int)a.OC;
   const int64_t plane = (int64_t)H_in * W_in;
-  const int8_t* xn = a.x + (int64_t)n * IC * plane;
   const uint32_t zp4 = 0x01010101u * ((uint32_t)a.izp & 0xffu);
   const int row0 = i0 + P.dhmin + p.base_h;        // input row of halo row 0
   const int col0 = j0 + P.dwmin + p.base_w - p.coff;   // input column of halo column 0 (multiple of 4)
 
   // ---- halo staging: unit u = (halo row, 16-channel block, 4 columns) ----
   // All units are loaded before any is transposed and stored, at most
-  // kStageSlots per thread (the host checks the count).
+  // kStageSlots per thread (the host checks the count); from fp32 input two
+  // at a time (16-byte loads of 4 pixels per channel, quantized in registers).
   {
     const int CG = HC >> 2;
     const int units = HR * NQ * CG;
-    uint32_t stg[kStageSlots][16];
-#pragma unroll
-    for (int sl = 0; sl < kStageSlots; ++sl) {
-      if (sl * kThreads >= units) break;   // wave-uniform
-      const int u = tid + sl * kThreads;
-      const int uu = u < units ? u : units - 1;
+    auto unit_src = [&](int uu, int& ih, int& iw) {
       const int cg = uu % CG;
       const int q = (uu / CG) % NQ;
       const int r = uu / (CG * NQ);
-      const int ih = row0 + r, iw = col0 + 4 * cg;
+      ih = row0 + r;
+      iw = col0 + 4 * cg;
       const int ihc = ih < 0 ? 0 : (ih >= H_in ? H_in - 1 : ih);
       const int iwc = iw < 0 ? 0 : (iw > W_in - 4 ? W_in - 4 : iw);
-      const int8_t* src = xn + (int64_t)(16 * q) * plane + (int64_t)ihc * W_in + iwc;
+      return (int64_t)(16 * q) * plane + (int64_t)ihc * W_in + iwc;
+    };
+    // 4x4 byte transposes (chunk e, dword g = byte e of channels 4g .. 4g+3)
+    // and the LDS store of one unit
+    auto put = [&](int u, const uint32_t (&d)[16]) {
+      const int cg = u % CG;
+      const int q = (u / CG) % NQ;
+      const int r = u / (CG * NQ);
+      v4i chunk[4];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) stg[sl][t] = *reinterpret_cast<const uint32_t*>(src + t * plane);
-    }
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t t0 = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x05010400u);
+        const uint32_t t1 = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x07030602u);
+        const uint32_t t2 = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x05010400u);
+        const uint32_t t3 = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x07030602u);
+        chunk[0][g] = (int)__builtin_amdgcn_perm(t2, t0, 0x05040100u);
+        chunk[1][g] = (int)__builtin_amdgcn_perm(t2, t0, 0x07060302u);
+        chunk[2][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x05040100u);
+        chunk[3][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x07060302u);
+      }
+      v4i* dst = xs + (r * NQ + q) * HC;
 #pragma unroll
-    for (int sl = 0; sl < kStageSlots; ++sl) {
-      if (sl * kThreads >= units) break;
-      const int u = tid + sl * kThreads;
-      if (u < units) {
-        const int cg = u % CG;
-        const int q = (u / CG) % NQ;
-        const int r = u / (CG * NQ);
-        const int ih = row0 + r, iw = col0 + 4 * cg;
-        // W_in % 4 == 0, iw % 4 == 0: a word is wholly inside or outside
-        const bool in_img = ih >= 0 && ih < H_in && iw >= 0 && iw < W_in;
-        uint32_t d[16];
+      for (int e = 0; e < 4; ++e) dst[pos(4 * cg + e)] = chunk[e];
+    };
+    if constexpr (!XF) {
+      const int8_t* xn = a.x + (int64_t)n * IC * plane;
+      uint32_t stg[kStageSlots][16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) d[t] = in_img ? stg[sl][t] : zp4;
-        // 4x4 byte transposes: chunk e, dword g = byte e of channels 4g .. 4g+3
-        v4i chunk[4];
+      for (int sl = 0; sl < kStageSlots; ++sl) {
+        if (sl * kThreads >= units) break;   // wave-uniform
+        const int u = tid + sl * kThreads;
+        int ih, iw;
+        const int8_t* src = xn + unit_src(u < units ? u : units - 1, ih, iw);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t t0 = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x05010400u);
-          const uint32_t t1 = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x07030602u);
-          const uint32_t t2 = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x05010400u);
-          const uint32_t t3 = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x07030602u);
-          chunk[0][g] = (int)__builtin_amdgcn_perm(t2, t0, 0x05040100u);
-          chunk[1][g] = (int)__builtin_amdgcn_perm(t2, t0, 0x07060302u);
-          chunk[2][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x05040100u);
-          chunk[3][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x07060302u);
+        for (int t = 0; t < 16; ++t) stg[sl][t] = *reinterpret_cast<const uint32_t*>(src + t * plane);
+      }
+#pragma unroll
+      for (int sl = 0; sl < kStageSlots; ++sl) {
+        if (sl * kThreads >= units) break;
+        const int u = tid + sl * kThreads;
+        if (u < units) {
+          int ih, iw;
+          unit_src(u, ih, iw);
+          // W_in % 4 == 0, iw % 4 == 0: a word is wholly inside or outside
+          const bool in_img = ih >= 0 && ih < H_in && iw >= 0 && iw < W_in;
+          uint32_t d[16];
+#pragma unroll
+          for (int t = 0; t < 16; ++t) d[t] = in_img ? stg[sl][t] : zp4;
+          put(u, d);
         }
-        v4i* dst = xs + (r * NQ + q) * HC;
+      }
+    } else {
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      const float* xn = a.xf + (int64_t)n * IC * plane;
+      const float zpf = (float)a.izp;
+      constexpr int PAIR = 2;
+      static_assert(kStageSlots % PAIR == 0, "slot pairs");
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[pos(4 * cg + e)] = chunk[e];
+      for (int sl0 = 0; sl0 < kStageSlots; sl0 += PAIR) {
+        if (sl0 * kThreads >= units) break;   // wave-uniform
+        v4f raw[PAIR][16];
+#pragma unroll
+        for (int h = 0; h < PAIR; ++h) {
+          const int u = tid + (sl0 + h) * kThreads;
+          int ih, iw;
+          const float* src = xn + unit_src(u < units ? u : units - 1, ih, iw);
+#pragma unroll
+          for (int t = 0; t < 16; ++t) raw[h][t] = *reinterpret_cast<const v4f*>(src + t * plane);
+        }
+#pragma unroll
+        for (int h = 0; h < PAIR; ++h) {
+          const int u = tid + (sl0 + h) * kThreads;
+          if (u < units) {
+            int ih, iw;
+            unit_src(u, ih, iw);
+            const bool in_img = ih >= 0 && ih < H_in && iw >= 0 && iw < W_in;
+            uint32_t d[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+              d[t] = in_img ? pack4(quantize1(raw[h][t][0], a.inv_in, zpf),
+                                    quantize1(raw[h][t][1], a.inv_in, zpf),
+                                    quantize1(raw[h][t][2], a.inv_in, zpf),
+                                    quantize1(raw[h][t][3], a.inv_in, zpf))
+                            : zp4;
+            put(u, d);
+          }
+        }
       }
     }
   }
@@ -397,29 +449,40 @@ bool plan_t(const DeconvArgs& a, FxPlan& p, size_t& lds) {
   return blocks < ((int64_t)1 << 31) && lds <= 160 * 1024;
 }
 
-template <int S, int K, int PM, bool FWD>
-hipError_t launch_t(const DeconvArgs& a, hipStream_t s) {
-  FxPlan p;
-  size_t lds = 0;
-  if (!plan_t<S, K, PM, FWD>(a, p, lds)) return hipErrorInvalidValue;
+template <int S, int K, int PM, bool FWD, bool XF>
+hipError_t launch_x(const DeconvArgs& a, const FxPlan& p, size_t lds, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_deconv_fixed<S, K, PM, FWD>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_deconv_fixed<S, K, PM, FWD, XF>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int64_t blocks = (int64_t)a.N * p.tiles_i * p.tiles_j * p.tiles_oc;
-  hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD>), dim3((unsigned)blocks), dim3(kThreads),
+  hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF>), dim3((unsigned)blocks), dim3(kThreads),
                      lds, s, a, p);
   return hipGetLastError();
+}
+
+template <int S, int K, int PM, bool FWD>
+hipError_t launch_t(const DeconvArgs& a, hipStream_t s) {
+  FxPlan p;
+  size_t lds = 0;
+  if (!plan_t<S, K, PM, FWD>(a, p, lds)) return hipErrorInvalidValue;
+  if constexpr (!FWD) {
+    if (a.xf) return launch_x<S, K, PM, FWD, true>(a, p, lds, s);
+  }
+  return launch_x<S, K, PM, FWD, false>(a, p, lds, s);
 }
 
 // Which instance takes a shape: 0 = none.
 int pick(const DeconvArgs& a, bool fwd) {
   if (a.groups != 1 || a.dil_h != 1 || a.dil_w != 1 || a.Kh != a.Kw) return 0;
   if (a.IC % 64 != 0 || a.IC > 4096 || a.ldw % 16 != 0 || ((uintptr_t)a.w & 15) != 0) return 0;
-  if (a.W_in % 4 != 0 || ((uintptr_t)a.x & 3) != 0) return 0;
+  // int8 input: 4-byte words of 4 pixels; fp32 input (fused quantize, the
+  // transposed conv only): 16-byte loads of 4 pixels
+  if (a.W_in % 4 != 0) return 0;
+  if (a.xf ? (fwd || ((uintptr_t)a.xf & 15) != 0) : ((uintptr_t)a.x & 3) != 0) return 0;
   if (a.OC > (1 << 20) || a.H_out > (1 << 20) || a.W_out > (1 << 20) || a.H_in > (1 << 20) ||
       a.W_in > (1 << 20) || a.N > (1 << 20) || a.ph > 4096 || a.pw > 4096)
     return 0;

@@ -557,6 +557,28 @@ def test_deconv_fixed_parity(case, act):
             np.testing.assert_array_equal(_run_deconv(c, bias=False), _oracle_deconv(c, bias=False))
 
 
+@pytest.mark.parametrize("case", DECONV_FIXED_CASES, ids=[str(i) for i in range(len(DECONV_FIXED_CASES))])
+@pytest.mark.parametrize("act", ["none", "relu"])
+def test_quantize_deconv_fixed_parity(case, act):
+    """The fused quantize -> transposed conv on the compile-time-pattern
+    kernel, which quantizes the fp32 input while it stages the halo."""
+    N, IC, H, W, OC, K, p, op = case
+    _say(f"quantize+deconv fixed case={case} act={act}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, K]) + 67, N, IC, H, W, OC, K, K, (2, 2), p, op,
+                       ldw=K * K * IC + 16, x_from_fp32=True)
+    out = torch.empty((N, OC, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+    with kernel("conv2d_transposed", "fixed"):
+        q8.q8ta_quantize_conv2d_transposed(dev(c.x_fp32), c.in_scale, c.in_zp, dev(c.w), c.Kh,
+                                           c.Kw, None, dev(c.weight_scales), dev(c.bias),
+                                           c.out_scale, c.out_zp, c.stride, c.padding,
+                                           c.output_padding, (1, 1), 1, act, out)
+    xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    ref = oracle.conv2d_transposed(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                   c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding, (1, 1),
+                                   c.H_out, c.W_out, activation=act)
+    np.testing.assert_array_equal(host(out), ref)
+
+
 CONV2D_FIXED_CASES = [
     # N, IC, H, W, OC, pad
     (2, 64, 10, 12, 40, (1, 1)),
