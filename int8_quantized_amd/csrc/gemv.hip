@@ -69,16 +69,16 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
       // codes and a zero ones-vector in sum w.  The workgroup quantizes the
       // MR x 1024*CH activations once: slot i = (m, c, lane) of the register
       // layout, 16 values each.
-      static_assert((MR * CH * 64) % kThreads == 0, "whole slots per thread");
-      constexpr int SL = MR * CH * 64 / kThreads;
+      constexpr int SLOTS = MR * CH * 64;
+      constexpr int SL = (SLOTS + kThreads - 1) / kThreads;
       v4f xr[SL][4];
       bool xok[SL];
 #pragma unroll
       for (int j = 0; j < SL; ++j) {
         const int i = threadIdx.x + j * kThreads;
-        const int m = i / (CH * 64);
+        const int m = (i < SLOTS ? i : 0) / (CH * 64);
         const int64_t kk = k0 + (int64_t)(i % (CH * 64)) * 16;
-        xok[j] = kk < K;
+        xok[j] = i < SLOTS && kk < K;
         const v4f* p = reinterpret_cast<const v4f*>(a.xf + m * K + (xok[j] ? kk : 0));
 #pragma unroll
         for (int d = 0; d < 4; ++d) xr[j][d] = p[d];
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
                             quantize1(xr[j][d][1], a.inv_in, (float)a.izp),
                             quantize1(xr[j][d][2], a.inv_in, (float)a.izp),
                             quantize1(xr[j][d][3], a.inv_in, (float)a.izp));
-        xs[threadIdx.x + j * kThreads] = xok[j] ? q : v4i{0, 0, 0, 0};
+        if (SLOTS % kThreads == 0 || threadIdx.x + j * kThreads < SLOTS)
+          xs[threadIdx.x + j * kThreads] = xok[j] ? q : v4i{0, 0, 0, 0};
       }
       __syncthreads();
 #pragma unroll
@@ -171,14 +172,21 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   }
 }
 
+// CH: consecutive 1 KiB slices a wave reads per pass over K: 4, or 1 when
+// K <= 1024 (one pass either way; the single slice wastes no loads or
+// quantize work on slices past K).
 template <int MR, int ROWS>
 hipError_t launch_rows(const LinearArgs& a, hipStream_t s) {
   const int64_t waves = (a.N + ROWS - 1) / ROWS;
   const int64_t blocks = (waves + kWaves - 1) / kWaves;
-  if (a.xf)
-    hipLaunchKernelGGL((k_skinny<MR, ROWS, 4, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_skinny<MR, ROWS, 4, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  const dim3 g((unsigned)blocks), t(kThreads);
+  if (a.K <= 1024) {
+    if (a.xf) hipLaunchKernelGGL((k_skinny<MR, ROWS, 1, true>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((k_skinny<MR, ROWS, 1, false>), g, t, 0, s, a);
+  } else {
+    if (a.xf) hipLaunchKernelGGL((k_skinny<MR, ROWS, 4, true>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((k_skinny<MR, ROWS, 4, false>), g, t, 0, s, a);
+  }
   return hipGetLastError();
 }
 
