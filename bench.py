@@ -37,7 +37,7 @@ skips it (the flags are then null).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T]
                        [--no-cpu-baseline] [--no-extra] [--step fused|chain]
                        [--profile-only gemm|gemm-and-copy|deconv|deconv-and-copy]
-       python bench.py --summarize-counters FETCH.csv WRITE.csv --traffic-of gemm_mx|deconv_fixed
+       python bench.py --summarize-counters FETCH.csv WRITE.csv --traffic-of gemm_w8|deconv_fixed
        python bench.py --summarize-trace TRACE.{db,csv} [--kernel SUBSTRING]
                        [--window K --before SUBSTRING]
 """
@@ -230,7 +230,7 @@ def summarize_trace(path, kernel=None, window=0, before=None):
 # Kernels whose HBM traffic is taken from rocprofv3 counters: name ->
 # (kernel-name substring, source file, algorithmic bytes read, written).
 TRAFFIC = {
-    "gemm_mx": ("k_gemm_mx", "gemm_mx.hip",
+    "gemm_w8": ("k_gemm_w8", "gemm_w8.hip",
                 2048 * 4096 + 11008 * 4096 + 8 * 11008, 4 * 2048 * 11008),
     "deconv_fixed": ("k_deconv_fixed", "deconv_fixed.hip",
                      8 * 256 * 64 * 64 + 128 * 9 * 256 + 8 * 128, 8 * 128 * 128 * 128),
@@ -322,7 +322,7 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     default=None, help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, "
                     "WRITE_SIZE) into profiles/traffic_<--traffic-of>.json")
-    ap.add_argument("--traffic-of", choices=sorted(TRAFFIC), default="gemm_mx")
+    ap.add_argument("--traffic-of", choices=sorted(TRAFFIC), default="gemm_w8")
     ap.add_argument("--command", default="", help="with --summarize-counters: the profiling "
                     "command, recorded in the summary")
     args = ap.parse_args()
@@ -479,11 +479,12 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "k_gemm_mx<256x128x64 tile, 2x2 waves of 128x64, 2 workgroups/CU, "
-                  "store-first K loop, transposed fp32 stores> (v_mfma_i32_32x32x32_i8)",
+        "kernel": "k_gemm_w8<256x256x64 tile, 2x4 waves of 128x64, 1 workgroup/CU, slabs "
+                  "straight into LDS over 3 stages, mid-step barrier, transposed fp32 stores> "
+                  "(v_mfma_i32_32x32x32_i8)",
         "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_INT8_TOPS, 4),
-        "traffic": traffic_from_profile("gemm_mx", os.path.join(CSRC, "gemm_mx.hip")),
+        "traffic": traffic_from_profile("gemm_w8", os.path.join(CSRC, "gemm_w8.hip")),
         "per_launch_ops": ops, "avg_launch_us": dist["mean_us"],
         "launch_us": dist,
         "algorithmic_bytes_per_launch": int(M * K + N * K + 8 * N + 4 * M * N),
@@ -494,7 +495,7 @@ def main():
     if not args.no_extra:
         extra, captured = run_extra(args, torch, np, q8, qi, lib, stream, timer, check, c, x, w,
                                     ws, b, y, step)
-        extra["ceilings"] = run_ceilings(torch, stream, timer)
+        extra["ceilings"] = run_ceilings(torch, stream, timer, operands=(x, w))
         log(f"  ceilings: {extra['ceilings']}")
 
     # ------------------------------------------------------------ CPU leg: oracle baseline + checks
@@ -897,11 +898,13 @@ def profile_copy(torch, stream):
     torch.cuda.synchronize()
 
 
-def run_ceilings(torch, stream, timer):
+def run_ceilings(torch, stream, timer, operands=None):
     """Achieved ceilings on this GPU (libq8ta_calib.so), next to the published
     peaks: a plain 16-byte copy, a read-only stream of the GEMV's weight size
     from HBM, an empty launch of the GEMV's grid, and register-only loops of
-    independent int8 MFMAs."""
+    independent int8 MFMAs -- on near-constant operands, and (`operands`: the
+    GEMM's activations and weights) on operands taken from the GEMM's own
+    data, which the matrix cores run markedly slower."""
     path = os.path.join(ROOT, "int8_quantized_amd", "libq8ta_calib.so")
     if not os.path.exists(path):
         return None
@@ -913,6 +916,9 @@ def run_ceilings(torch, stream, timer):
     cl.q8ta_calib_empty.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     cl.q8ta_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p]
+    cl.q8ta_calib_mfma_data.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
     out = torch.empty(512 * 256, dtype=torch.int32, device="cuda")
 
     def run(fns, n):
@@ -938,6 +944,14 @@ def run_ceilings(torch, stream, timer):
         mb, mi = 512, 2000
         d = run([lambda k=kind: cl.q8ta_calib_mfma(out.data_ptr(), mb, mi, k, stream)], 5)
         mfma[name] = round(mb * 4 * mi * per / (d["median_us"] / 1e6) / 1e12, 1)
+    if operands is not None:
+        xa, wb = operands
+        mb, mi = 512, 2000
+        d = run([lambda: cl.q8ta_calib_mfma_data(xa.data_ptr(), xa.numel() // 16, wb.data_ptr(),
+                                                 wb.numel() // 16, out.data_ptr(), mb, mi,
+                                                 stream)], 5)
+        mfma["mfma_32x32x32_i8_loop_tops_on_gemm_operands"] = round(
+            mb * 4 * mi * 8 * 65536 / (d["median_us"] / 1e6) / 1e12, 1)
     return {**mfma, "int8_mfma_peak_tops": PEAK_INT8_TOPS,
             "copy_256MiB_gbs": round(2 * n / (cp["median_us"] / 1e6) / 1e9, 1),
             "hbm_peak_gbs": PEAK_HBM_GBS,

@@ -80,12 +80,14 @@ const char* q8ta_last_error(void);
  * it.  Forces one kernel family of an op where the shape allows it (shapes
  * that family cannot take keep the default choice); results are bit-identical
  * whichever kernel runs.  Process-wide: applies to calls made after it returns.
- *   op "linear":            kernel "default" | "mfma32" | "generic"
- *                           (mfma32: the 32x32x32 matrix-core GEMM for every
- *                           shape the matrix-core path takes, which by
- *                           default only large problems use; generic: the
- *                           shape-general kernel instead of the GEMV /
- *                           matrix-core GEMM)
+ *   op "linear":            kernel "default" | "mfma32" | "mfma32_8w" |
+ *                           "generic"
+ *                           (mfma32: the 32x32x32 matrix-core GEMM with two
+ *                           four-wave workgroups per CU for every shape the
+ *                           matrix-core path takes; mfma32_8w: the
+ *                           eight-wave 256 x 256-tile form where K is a
+ *                           multiple of 64; generic: the shape-general
+ *                           kernel instead of the GEMV / matrix-core GEMM)
  *   op "conv2d_transposed": "default" | "fixed" | "mfma32" | "mfma" | "igemm" |
  *                           "tiled" | "generic"
  *   op "conv2d":            "default" | "fixed" | "mfma32" | "mfma" | "igemm" |

@@ -2,11 +2,12 @@
 // on the two resources the q8ta kernels are bound by, next to the published
 // peaks.  Not part of the q8ta op family.
 //
-//  q8ta_calib_dot4: each thread runs `iters` rounds of 16 independent v_dot4
-//    accumulations on registers (no memory traffic inside the loop) and writes
-//    one int32; ops = threads * iters * 16 * 8.
 //  q8ta_calib_mfma: a register-only loop of independent int8 MFMAs per wave
 //    (the matrix-core issue ceiling).
+//  q8ta_calib_mfma_data: the same 32x32x32 loop with every lane's operands
+//    taken from given int8 data: the matrix cores draw more power, and the
+//    chip runs them slower, on operands with many toggling bits (quantized
+//    data) than on the near-constant ones of q8ta_calib_mfma.
 //  q8ta_calib_copy: 16-byte grid-stride copy of n16 chunks; bytes = 32 * n16.
 //  q8ta_calib_read: read-only stream of n16 16-byte chunks, 8 per thread in
 //    the access pattern of the GEMV's weight stream (each load instruction of
@@ -19,24 +20,6 @@
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-
-__global__ __launch_bounds__(256) void k_dot4_loop(int32_t* out, int iters, int seed) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  int a[16], acc[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    a[k] = (t * 0x9E3779B1u) ^ (k * 0x85EBCA6Bu) ^ seed;
-    acc[k] = k;
-  }
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = __builtin_amdgcn_sdot4(a[k], a[(k + 1) & 15], acc[k], false);
-  }
-  int s = 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) s ^= acc[k];
-  out[t] = s;
-}
 
 // MFMA issue ceiling: each wave runs `iters` rounds of 16 independent int8
 // matrix products into 16 accumulators held in registers.  kind 0:
@@ -73,6 +56,28 @@ __global__ __launch_bounds__(256) void k_mfma_loop(int32_t* out, int iters, int 
 #pragma unroll
     for (int k = 0; k < 8; ++k) s ^= acc[k][0] ^ acc[k][15];
   }
+  out[t] = s;
+}
+
+// kind 1's loop on operands from memory: lane t of the grid takes A = the
+// 16 bytes at 16 * (t % na16) of a and B = those at 16 * (t % nb16) of b.
+__global__ __launch_bounds__(256) void k_mfma_data(const v4i* __restrict__ a, int64_t na16,
+                                                   const v4i* __restrict__ b, int64_t nb16,
+                                                   int iters, int32_t* out) {
+  typedef int v16i __attribute__((ext_vector_type(16)));
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const v4i av = a[t % na16];
+  const v4i bv = b[t % nb16];
+  v16i acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = v16i{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[k], 0, 0, 0);
+  }
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s ^= acc[k][0] ^ acc[k][15];
   out[t] = s;
 }
 
@@ -116,9 +121,13 @@ int q8ta_calib_mfma(int32_t* out, int blocks, int iters, int kind, hipStream_t s
   return (int)hipGetLastError();
 }
 
-int q8ta_calib_dot4(int32_t* out, int blocks, int iters, hipStream_t s) {
-  if (!out || blocks < 1 || iters < 1) return 1;
-  hipLaunchKernelGGL(k_dot4_loop, dim3(blocks), dim3(256), 0, s, out, iters, 12345);
+// a, b: device buffers of na16 / nb16 16-byte chunks; out: int32 device
+// buffer of blocks * 256 entries.  ops = blocks * 4 waves * iters * 8 * 65536.
+int q8ta_calib_mfma_data(const void* a, int64_t na16, const void* b, int64_t nb16, int32_t* out,
+                         int blocks, int iters, hipStream_t s) {
+  if (!a || !b || !out || na16 < 1 || nb16 < 1 || blocks < 1 || iters < 1) return 1;
+  hipLaunchKernelGGL(k_mfma_data, dim3(blocks), dim3(256), 0, s, (const v4i*)a, na16,
+                     (const v4i*)b, nb16, iters, out);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -454,7 +454,7 @@ const char* q8ta_last_error(void) { return g_err; }
 q8ta_status q8ta_select_kernel(const char* op, const char* kernel) {
   if (!op || !kernel) return fail(Q8TA_ERR_NULL, "q8ta_select_kernel: op and kernel must not be NULL");
   struct Name { const char* name; char code; };
-  static const Name linear[] = {{"default", 0}, {"mfma32", 'x'}, {"generic", 'g'}};
+  static const Name linear[] = {{"default", 0}, {"mfma32", 'x'}, {"mfma32_8w", 'w'}, {"generic", 'g'}};
   static const Name deconv[] = {{"default", 0}, {"fixed", 'f'}, {"mfma32", 'x'}, {"mfma", 'm'},
                                 {"igemm", 'i'}, {"tiled", 't'}, {"generic", 'g'}};
   static const Name conv[] = {{"default", 0}, {"fixed", 'f'}, {"mfma32", 'x'}, {"mfma", 'm'},
@@ -462,7 +462,7 @@ q8ta_status q8ta_select_kernel(const char* op, const char* kernel) {
   const Name* tab = nullptr;
   size_t n = 0;
   std::atomic<char>* dst = nullptr;
-  if (strcmp(op, "linear") == 0) { tab = linear; n = 3; dst = &g_sel_linear; }
+  if (strcmp(op, "linear") == 0) { tab = linear; n = 4; dst = &g_sel_linear; }
   else if (strcmp(op, "conv2d_transposed") == 0) { tab = deconv; n = 7; dst = &g_sel_deconv; }
   else if (strcmp(op, "conv2d") == 0) { tab = conv; n = 6; dst = &g_sel_conv; }
   else return fail(Q8TA_ERR_UNSUPPORTED, "q8ta_select_kernel: unknown op \"%.64s\"", op);

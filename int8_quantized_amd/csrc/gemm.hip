@@ -300,15 +300,20 @@ bool gemm_mfma_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-// Tile choice: problems that fill the GPU at least once with 256 x 128 tiles
-// and have a long K take the 32x32x32 kernel of gemm_mx.hip (two workgroups
-// per CU, store-first K loop: 125.7-126.4 us on 2048 x 4096 x 11008 with the
-// fused dequantize, against 131-135 us for a 256 x 128 tile of this file);
-// the rest the 128 x 128 tile, or the 128 x 64 tile for few rows.
+// Tile choice for a long K (>= 1024): problems whose 256 x 256 tiles fill
+// the 256 CUs at least once take the eight-wave kernel of gemm_w8.hip (on
+// 2048 x 4096 x N with the fused dequantize: 68.6-70.9 us at N = 8192 against
+// 81.6-83.7 us for gemm_mx.hip, 111.9-117.6 us against 113.5-119.4 us at
+// N = 11008, same boxes); smaller ones that fill them with 256 x 128 tiles
+// the two-workgroup kernel of gemm_mx.hip (43.8-44.9 us at N = 4096 against
+// 49.2-51.4 us: 128 tiles of 256 x 256 leave half the CUs idle); the rest the
+// 128 x 128 tile of this file, or the 128 x 64 tile for few rows.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s, char kind) {
   const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
   const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (kind == 'x') return launch_gemm_mx(a, s);
+  if (gemm_w8_supported(a) && (kind == 'w' || (a.K >= 1024 && gemm_w8_tiles(a) >= 256)))
+    return launch_gemm_w8(a, s);
   if (tv >= 256 && a.K >= 1024) return launch_gemm_mx(a, s);
   if (tm >= 256 || a.M > 64) return launch_cfg<CfgM>(a, s);
   return launch_cfg<CfgS>(a, s);

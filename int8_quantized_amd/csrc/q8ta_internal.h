@@ -229,12 +229,18 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 bool gemv_supported(const LinearArgs& a);
 // kind: 0 the default choice; 'x' the 32x32x32 kernel of gemm_mx.hip for any
-// shape.
+// shape; 'w' the eight-wave kernel of gemm_w8.hip where it applies (else the
+// default choice).
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s, char kind = 0);
 bool gemm_mfma_supported(const LinearArgs& a);
 // 32x32x32 matrix-core GEMM for large problems (same operand requirements as
 // launch_gemm_mfma, which chooses it).
 hipError_t launch_gemm_mx(const LinearArgs& a, hipStream_t s);
+// Eight-wave 256 x 256-tile matrix-core GEMM with slab loads straight into
+// LDS (gemm_w8.hip): K a multiple of 64, x and w 16-byte aligned.
+bool gemm_w8_supported(const LinearArgs& a);
+int64_t gemm_w8_tiles(const LinearArgs& a);
+hipError_t launch_gemm_w8(const LinearArgs& a, hipStream_t s);
 int64_t prepacked_bytes(int64_t N, int64_t K);
 hipError_t launch_prepack(const int8_t* w, int64_t N, int64_t K, int8_t* packed, hipStream_t s);
 hipError_t launch_gemm_pk(const LinearArgs& a, hipStream_t s);

@@ -377,7 +377,7 @@ def test_select_kernel_names():
     """q8ta_select_kernel accepts the documented op and kernel names, rejects
     others (leaving the choice unchanged) and makes no HIP call."""
     lib = q8.lib()
-    for op, kernels in (("linear", ("mfma32", "generic")),
+    for op, kernels in (("linear", ("mfma32", "mfma32_8w", "generic")),
                         ("conv2d_transposed", ("fixed", "mfma32", "mfma", "igemm", "tiled",
                                                "generic")),
                         ("conv2d", ("fixed", "mfma32", "mfma", "igemm", "generic"))):

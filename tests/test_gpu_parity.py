@@ -188,7 +188,7 @@ GEMM_TILE_SHAPES = [(64, 128, 64), (70, 48, 300), (300, 1040, 257), (512, 4096, 
                     (1024, 1024, 8192), (1000, 1040, 8100), (33, 100, 70)]
 
 
-@pytest.mark.parametrize("path", ["default", "mfma32", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma32", "mfma32_8w", "generic"])
 @pytest.mark.parametrize("M,K,N", GEMM_TILE_SHAPES)
 def test_linear_every_gemm_tile(path, M, K, N):
     _say(f"gemm {path} M={M} K={K} N={N}")
@@ -206,6 +206,44 @@ def test_linear_every_gemm_tile(path, M, K, N):
         ref = oracle.dequantize_per_tensor(_oracle_linear(c, activation="relu"), c.out_scale,
                                            c.out_zp)
         np.testing.assert_array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+
+
+# The eight-wave kernel: one K step (64), two, three (one pass of its three
+# LDS stages), a tail of one and of two steps after whole passes, ragged M and
+# N in one and in several tiles, and a grid that is not a multiple of 8 (its
+# XCD remapping leaves the last tiles in place).
+W8_SHAPES = [(256, 64, 256), (257, 128, 255), (512, 192, 512), (300, 1088, 257),
+             (70, 256, 1000), (1000, 1024, 900), (769, 640, 2304)]
+
+
+@pytest.mark.parametrize("M,K,N", W8_SHAPES)
+def test_linear_w8_edges(M, K, N):
+    _say(f"gemm w8 M={M} K={K} N={N}")
+    c = qi.linear_case(M * 7 + K + N, M, K, N)
+    ref = _oracle_linear(c, activation="relu")
+    wd = dev(c.w)
+    sums = torch.empty(N, dtype=torch.int32, device="cuda")
+    q8.q8ta_weight_sums(wd, sums)
+    out = torch.empty((M, N), dtype=torch.int8, device="cuda")
+    outf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    dq = oracle.dequantize_per_tensor(ref, c.out_scale, c.out_zp)
+    with kernel("linear", "mfma32_8w"):
+        q8.q8ta_linear(dev(c.x), c.in_scale, c.in_zp, wd, None, dev(c.weight_scales),
+                       dev(c.bias), c.out_scale, c.out_zp, "relu", out)
+        np.testing.assert_array_equal(host(out), ref)
+        np.testing.assert_array_equal(_acc_linear(c), oracle.linear_acc(c.x, c.w, c.in_zp))
+        q8.q8ta_linear_dq(dev(c.x), c.in_scale, c.in_zp, wd, None, dev(c.weight_scales),
+                          dev(c.bias), c.out_scale, c.out_zp, "relu", outf)
+        np.testing.assert_array_equal(host(outf).view(np.uint32), dq.view(np.uint32))
+        out.zero_()
+        q8.q8ta_linear_presummed(dev(c.x), c.in_scale, c.in_zp, wd, sums, dev(c.weight_scales),
+                                 dev(c.bias), c.out_scale, c.out_zp, "relu", out)
+        np.testing.assert_array_equal(host(out), ref)
+        outf.zero_()
+        q8.q8ta_linear_dq_presummed(dev(c.x), c.in_scale, c.in_zp, wd, sums,
+                                    dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp,
+                                    "relu", outf)
+        np.testing.assert_array_equal(host(outf).view(np.uint32), dq.view(np.uint32))
 
 
 @pytest.mark.parametrize("M,K", [(1, 2048), (3, 4096), (1, 5136), (4, 48), (2, 16)])
@@ -782,7 +820,7 @@ DQ_SHAPES = [(1, 4096, 4096), (3, 48, 17), (4, 64, 32), (65, 320, 97), (300, 104
 
 
 @pytest.mark.parametrize("M,K,N", DQ_SHAPES)
-@pytest.mark.parametrize("path", ["default", "mfma32", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma32", "mfma32_8w", "generic"])
 def test_linear_dq_equals_linear_then_dequantize(M, K, N, path):
     """q8ta_linear_dq == dequantize_per_tensor(q8ta_linear(...)) bit for bit,
     against the oracle's two steps (default and shape-general kernels)."""
@@ -1128,7 +1166,7 @@ def test_weight_sums(N, K, offset):
     np.testing.assert_array_equal(host(sums), oracle.weight_sums(w))
 
 
-@pytest.mark.parametrize("path", ["default", "mfma32", "generic"])
+@pytest.mark.parametrize("path", ["default", "mfma32", "mfma32_8w", "generic"])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 512), (300, 1024, 257), (65, 320, 97), (512, 4096, 768),
                                    (7, 33, 5), (40, 256, 64), (1024, 1024, 8192)])
 def test_linear_presummed_equals_linear(path, M, K, N):

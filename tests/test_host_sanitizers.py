@@ -47,7 +47,7 @@ NO_GPU = pytest.mark.skipif(_gpu_present(), reason="calls with fake device point
                                                    "meaningful without a GPU")
 
 KERNELS = {
-    "linear": ["default", "mfma32", "generic"],
+    "linear": ["default", "mfma32", "mfma32_8w", "generic"],
     "conv2d_transposed": ["default", "fixed", "mfma32", "mfma", "igemm", "tiled", "generic"],
     "conv2d": ["default", "fixed", "mfma32", "mfma", "igemm", "generic"],
 }
