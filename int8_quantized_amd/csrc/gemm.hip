@@ -302,9 +302,9 @@ bool gemm_mfma_supported(const LinearArgs& a) {
 
 // Tile choice for a long K (>= 1024): problems whose 256 x 256 tiles fill
 // the 256 CUs at least once take the eight-wave kernel of gemm_w8.hip (on
-// 2048 x 4096 x N with the fused dequantize: 68.6-70.9 us at N = 8192 against
-// 81.6-83.7 us for gemm_mx.hip, 111.9-117.6 us against 113.5-119.4 us at
-// N = 11008, same boxes); smaller ones that fill them with 256 x 128 tiles
+// 2048 x 4096 x N with the fused dequantize: 68.6-73.8 us at N = 8192 against
+// 81.6-88.0 us for gemm_mx.hip, 113.8 us against 122.1 us at N = 11008, same
+// boxes); smaller ones that fill them with 256 x 128 tiles
 // the two-workgroup kernel of gemm_mx.hip (43.8-44.9 us at N = 4096 against
 // 49.2-51.4 us: 128 tiles of 256 x 256 leave half the CUs idle); the rest the
 // 128 x 128 tile of this file, or the 128 x 64 tile for few rows.

@@ -21,11 +21,14 @@
 //    fragment reads 63, the matrix-core work alone 39 us (2.75 POP/s, close
 //    to what a register-only v_mfma loop sustains on operands with the bit
 //    statistics of quantized data: 2.9-3.1 POP/s).
-//  * Problems whose tiles do not fill the CUs a whole number of times run a
-//    partial last round (2048 x 11008: 344 tiles).  Splitting those last
-//    tiles along K over two workgroups measured slower (132 us against 112
-//    us): each piece's int32 partial tile (256 KiB) has to go through memory
-//    to the other piece, as much traffic as the split saves in compute.
+//  * Problems whose tiles do not fill the CUs a whole number of times would
+//    run a partial last round (2048 x 11008: 344 tiles, 88 in the last).
+//    The whole rounds are one launch; the remaining tile columns, when they
+//    fit one round as 256 x 128 tiles, a second launch of those (176 half
+//    tiles on 176 CUs: 113.8 us against ~120 us as one launch).  Splitting
+//    the last tiles along K over two workgroups instead measured slower (132
+//    us against 112 us): each piece's int32 partial tile (256 KiB) has to go
+//    through memory to the other piece, as much traffic as the split saves.
 //  * The slabs go straight from global memory into LDS
 //    (global_load_lds_dwordx4: each instruction moves 16 rows x 64 bytes;
 //    lane l's 16 bytes land at LDS offset 16 * l of the instruction's base;
@@ -321,7 +324,11 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
   // straight from the accumulators, each store instruction would cover 32
   // rows with 8 bytes each.
   if (fast && !a.acc && (N % 16) == 0 && ((uintptr_t)a.out & 15) == 0) {
-    auto row = [&](int m) { return (m < 128 ? sm.st0 : sm.st1) + (m & 127) * 256; };
+    constexpr int RPS = T::STAGE / T::TN;   // tile rows per stage
+    static_assert(3 * RPS >= T::BM, "the int8 tile fits the three stages");
+    auto row = [&](int m) {
+      return (m < RPS ? sm.st0 : (m < 2 * RPS ? sm.st1 : sm.st2)) + (m % RPS) * T::TN;
+    };
     Static<0, FN>::each([&](auto I) {
       constexpr int i = decltype(I)::value;
       Static<0, 4>::each([&](auto G) {
@@ -343,7 +350,7 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             q[r] = requant_code(acc[i][j][4 * g + r] - zc[r], sc[r], bi[r], a.rq);
-          *reinterpret_cast<uint32_t*>(row(m) + 16 * ((rr >> 4) ^ (m & 15)) + (rr & 15)) =
+          *reinterpret_cast<uint32_t*>(row(m) + 16 * ((rr >> 4) ^ (m & (T::TN / 16 - 1))) + (rr & 15)) =
               pack4((int)q[0], (int)q[1], (int)q[2], (int)q[3]);
         });
       });
@@ -355,7 +362,7 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
     for (int u = 0; u < CH / T::NT; ++u) {
       const int id = tid + u * T::NT;
       const int m = id / (T::TN / 16), c = id % (T::TN / 16);
-      const v4i v = *reinterpret_cast<const v4i*>(row(m) + 16 * (c ^ (m & 15)));
+      const v4i v = *reinterpret_cast<const v4i*>(row(m) + 16 * (c ^ (m & (T::TN / 16 - 1))));
       *reinterpret_cast<v4i*>(a.out + (bm0 + m) * N + bn0 + 16 * c) = v;
     }
     return;
@@ -421,8 +428,10 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
   });
 }
 
+// Tiles cover output columns n0 .. (tile column tn at n0 + tn * TN).
 template <class T, bool PRE, bool TR>
-__global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m, int tiles_n,
+                                                       int64_t n0) {
   __shared__ __attribute__((aligned(16))) int8_t st0[T::STAGE];
   __shared__ __attribute__((aligned(16))) int8_t st1[T::STAGE];
   __shared__ __attribute__((aligned(16))) int8_t st2[T::STAGE];
@@ -445,7 +454,7 @@ __global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m,
   const int KT = (int)(a.K / T::BK);
   const int tm = t % tiles_m;
   const int tn = t / tiles_m;
-  const int64_t bn0 = (int64_t)tn * T::TN;
+  const int64_t bn0 = n0 + (int64_t)tn * T::TN;
   const int64_t bm0 = (int64_t)tm * T::BM;
   const int64_t M = a.M, N = a.N, K = a.K;
 
@@ -516,19 +525,40 @@ __global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m,
 }
 
 template <class T, bool PRE>
-hipError_t launch_t(const LinearArgs& a, hipStream_t s) {
+hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t n0, int tiles_n) {
   const int tiles_m = (int)((a.M + T::BM - 1) / T::BM);
-  const int tiles_n = (int)((a.N + T::TN - 1) / T::TN);
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   // fp32 output (fused dequantize): the transposed form, whole-line stores
   if (a.outf != nullptr && a.acc == nullptr)
-    hipLaunchKernelGGL((k_gemm_w8<T, PRE, true>), grid, dim3(T::NT), 0, s, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_w8<T, PRE, true>), grid, dim3(T::NT), 0, s, a, tiles_m, tiles_n, n0);
   else
-    hipLaunchKernelGGL((k_gemm_w8<T, PRE, false>), grid, dim3(T::NT), 0, s, a, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_w8<T, PRE, false>), grid, dim3(T::NT), 0, s, a, tiles_m, tiles_n, n0);
   return hipGetLastError();
 }
 
-using T256 = Tile<2, 4, 4, 2>;
+using T256 = Tile<2, 4, 4, 2>;   // 256 x 256, waves of 128 x 64
+using T128 = Tile<4, 2, 2, 2>;   // 256 W rows x 128 X rows, waves of 64 x 64
+
+template <bool PRE>
+hipError_t launch_plan(const LinearArgs& a, hipStream_t s) {
+  const int64_t tiles_m = (a.M + T256::BM - 1) / T256::BM;
+  const int64_t tiles_n = (a.N + T256::TN - 1) / T256::TN;
+  const int64_t tiles = tiles_m * tiles_n;
+  // Whole rounds of 256 x 256 tiles over the 256 CUs, then the remaining
+  // columns as 256 x 128 tiles when those fit one round: the last round then
+  // keeps twice as many CUs busy, each with half a tile.
+  if (tiles % 256 != 0 && 256 % tiles_m == 0 && tiles > 256) {
+    const int64_t cols = tiles / 256 * 256 / tiles_m;
+    const int64_t rest = tiles_n - cols;
+    const int64_t half_tiles = rest * ((a.M + T128::BM - 1) / T128::BM);
+    if (half_tiles <= 256) {
+      hipError_t e = launch_t<T256, PRE>(a, s, 0, (int)cols);
+      if (e != hipSuccess) return e;
+      return launch_t<T128, PRE>(a, s, cols * T256::TN, (int)rest);
+    }
+  }
+  return launch_t<T256, PRE>(a, s, 0, (int)tiles_n);
+}
 
 }  // namespace
 
@@ -544,7 +574,7 @@ int64_t gemm_w8_tiles(const LinearArgs& a) {
 
 hipError_t launch_gemm_w8(const LinearArgs& a, hipStream_t s) {
   if (!gemm_w8_supported(a)) return hipErrorInvalidValue;
-  return a.wsum_pre ? launch_t<T256, true>(a, s) : launch_t<T256, false>(a, s);
+  return a.wsum_pre ? launch_plan<true>(a, s) : launch_plan<false>(a, s);
 }
 
 }  // namespace q8ta

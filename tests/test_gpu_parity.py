@@ -210,10 +210,12 @@ def test_linear_every_gemm_tile(path, M, K, N):
 
 # The eight-wave kernel: one K step (64), two, three (one pass of its three
 # LDS stages), a tail of one and of two steps after whole passes, ragged M and
-# N in one and in several tiles, and a grid that is not a multiple of 8 (its
-# XCD remapping leaves the last tiles in place).
+# N in one and in several tiles, a grid that is not a multiple of 8 (its XCD
+# remapping leaves the last tiles in place), and 258 tiles of 256 x 256: one
+# launch of 256 of them, then the last column of tiles as 256 x 128 tiles
+# (ragged in M and N).
 W8_SHAPES = [(256, 64, 256), (257, 128, 255), (512, 192, 512), (300, 1088, 257),
-             (70, 256, 1000), (1000, 1024, 900), (769, 640, 2304)]
+             (70, 256, 1000), (1000, 1024, 900), (769, 640, 2304), (300, 1088, 33000)]
 
 
 @pytest.mark.parametrize("M,K,N", W8_SHAPES)
