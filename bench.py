@@ -239,33 +239,40 @@ COPY_BYTES = 256 * 1024 * 1024      # the calibration copy reads and writes this
 
 
 def summarize_counters(fetch_csv, write_csv, name, command):
-    """HBM bytes per launch of one kernel from two rocprofv3 --pmc runs
+    """HBM bytes per call of one kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
     same counter reads for the 256 MiB calibration copy (k_copy16) of the same
-    run.  Writes profiles/traffic_<name>.json (read by the benchmark while the
-    kernel source is unchanged) and returns a text summary."""
+    run.  A call that launches several instantiations of the kernel (the
+    GEMM's two tile shapes) counts the median dispatch of each once.  Writes
+    profiles/traffic_<name>.json (read by the benchmark while the kernel
+    source is unchanged) and returns a text summary."""
     import csv
     sub, src, alg_r, alg_w = TRAFFIC[name]
 
     def read(path, counter):
-        vals, copy = [], []
+        by, copy = {}, []
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
                 if sub in r["Kernel_Name"]:
-                    vals.append(float(r["Counter_Value"]))
+                    by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
                 elif "k_copy16" in r["Kernel_Name"]:
                     copy.append(float(r["Counter_Value"]))
-        if not vals or not copy:
+        if not by or not copy:
             raise SystemExit(f"{path}: no {counter} rows for {sub} and k_copy16")
-        return vals, statistics.median(copy)
+        return by, statistics.median(copy)
 
-    fv, fc = read(fetch_csv, "FETCH_SIZE")
-    wv, wc = read(write_csv, "WRITE_SIZE")
+    fb, fc = read(fetch_csv, "FETCH_SIZE")
+    wb, wc = read(write_csv, "WRITE_SIZE")
     f_scale, w_scale = COPY_BYTES / (fc * 1024), COPY_BYTES / (wc * 1024)
-    fetch = statistics.median(fv) * 1024 * f_scale
-    write = statistics.median(wv) * 1024 * w_scale
+    fetch = sum(statistics.median(v) for v in fb.values()) * 1024 * f_scale
+    write = sum(statistics.median(v) for v in wb.values()) * 1024 * w_scale
+    raw = []
+    for label, by in (("FETCH", fb), ("WRITE", wb)):
+        for kname, v in sorted(by.items()):
+            raw.append(f"#   {label} {min(v):.0f} / {statistics.median(v):.0f} / {max(v):.0f} "
+                       f"({len(v)})  {kname[:150]}")
     sha = file_hash(os.path.join(CSRC, src))
     d = {"kernel": sub, "source": src, "source_sha256_16": sha,
          "bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
@@ -276,14 +283,13 @@ def summarize_counters(fetch_csv, write_csv, name, command):
         json.dump(d, f, indent=1)
         f.write("\n")
     return "\n".join([
-        f"# HBM traffic per launch of {sub} ({src} sha256[:16] = {sha}) on one MI355X",
+        f"# HBM traffic per call of {sub} ({src} sha256[:16] = {sha}) on one MI355X",
         f"# commands (one run per counter): {command}",
         f"# reference: 16-byte copy of 256 MiB (reads and writes {COPY_BYTES} B per launch)",
         f"#   FETCH_SIZE reads {fc:.1f} KiB for it -> scale {f_scale:.4f}",
         f"#   WRITE_SIZE reads {wc:.1f} KiB for it -> scale {w_scale:.4f}",
-        f"# per-dispatch raw values (KiB; min / median / max over the dispatches): FETCH "
-        f"{min(fv):.0f} / {statistics.median(fv):.0f} / {max(fv):.0f} ({len(fv)}), WRITE "
-        f"{min(wv):.0f} / {statistics.median(wv):.0f} / {max(wv):.0f} ({len(wv)})",
+        "# per-dispatch raw values (KiB; min / median / max over the dispatches, per kernel):",
+        *raw,
         "",
         f"{'':24}{'measured':>14}{'algorithmic':>14}{'ratio':>8}",
         f"{'read (FETCH_SIZE)':24}{fetch:14.0f}{alg_r:14d}{fetch / alg_r:8.2f}",
@@ -479,9 +485,11 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "k_gemm_w8<256x256x64 tile, 2x4 waves of 128x64, 1 workgroup/CU, slabs "
-                  "straight into LDS over 3 stages, mid-step barrier, transposed fp32 stores> "
-                  "(v_mfma_i32_32x32x32_i8)",
+        "kernel": "k_gemm_w8 (v_mfma_i32_32x32x32_i8; 1 workgroup of 8 waves per CU, slabs "
+                  "straight into LDS over 3 stages, mid-step barrier, transposed fp32 stores): "
+                  "one launch of 256 tiles of 256x256 (waves of 128x64) for the first 8192 "
+                  "columns, one of 176 tiles of 256x128 (waves of 64x64) for the last 2816; "
+                  "avg_launch_us is the whole call",
         "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_INT8_TOPS, 4),
         "traffic": traffic_from_profile("gemm_w8", os.path.join(CSRC, "gemm_w8.hip")),
