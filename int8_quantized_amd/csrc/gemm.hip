@@ -300,19 +300,21 @@ bool gemm_mfma_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-// Tile choice for a long K (>= 1024): problems whose 256 x 256 tiles fill
-// the 256 CUs at least once take the eight-wave kernel of gemm_w8.hip (on
-// 2048 x 4096 x N with the fused dequantize: 68.6-73.8 us at N = 8192 against
-// 81.6-88.0 us for gemm_mx.hip, 113.8 us against 122.1 us at N = 11008, same
-// boxes); smaller ones that fill them with 256 x 128 tiles
-// the two-workgroup kernel of gemm_mx.hip (43.8-44.9 us at N = 4096 against
-// 49.2-51.4 us: 128 tiles of 256 x 256 leave half the CUs idle); the rest the
-// 128 x 128 tile of this file, or the 128 x 64 tile for few rows.
+// Tile choice for a long K (>= 1024): the eight-wave kernel of gemm_w8.hip
+// for problems whose 256 x 256 tiles fill the 256 CUs at least once (whole
+// rounds of them, the remaining columns as 256 x 128 tiles in the same
+// launch) or whose 256 x 128 tiles fill half to all of them in one round (on
+// 2048 x 4096 x N with the fused dequantize, same boxes: 100.6-104.9 us
+// against 119.8-120.7 us for gemm_mx.hip at N = 11008, 69.4-70.9 against
+// 83.4-84.3 at 8192, 42.8 against 45.8 at 4096, 32.9 against 38.3 at 2048);
+// the others that fill the CUs with 256 x 128 tiles the two-workgroup kernel
+// of gemm_mx.hip; the rest the 128 x 128 tile of this file, or the 128 x 64
+// tile for few rows.
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t s, char kind) {
   const int64_t tv = ((a.M + 127) / 128) * ((a.N + 255) / 256);
   const int64_t tm = ((a.M + 127) / 128) * ((a.N + 127) / 128);
   if (kind == 'x') return launch_gemm_mx(a, s);
-  if (gemm_w8_supported(a) && (kind == 'w' || (a.K >= 1024 && gemm_w8_tiles(a) >= 256)))
+  if ((kind == 'w' && gemm_w8_supported(a)) || (kind == 0 && gemm_w8_preferred(a)))
     return launch_gemm_w8(a, s);
   if (tv >= 256 && a.K >= 1024) return launch_gemm_mx(a, s);
   if (tm >= 256 || a.M > 64) return launch_cfg<CfgM>(a, s);

@@ -23,11 +23,15 @@
 //    statistics of quantized data: 2.9-3.1 POP/s).
 //  * Problems whose tiles do not fill the CUs a whole number of times would
 //    run a partial last round (2048 x 11008: 344 tiles, 88 in the last).
-//    The whole rounds are one launch; the remaining tile columns, when they
-//    fit one round as 256 x 128 tiles, a second launch of those (176 half
-//    tiles on 176 CUs: 113.8 us against ~120 us as one launch).  Splitting
-//    the last tiles along K over two workgroups instead measured slower (132
-//    us against 112 us): each piece's int32 partial tile (256 KiB) has to go
+//    Instead the columns left after whole rounds are covered by 256 x 128
+//    tiles (eight waves of 64 x 64) when those fit one round, in the same
+//    launch after the 256 x 256 ones, so that they start on the CUs the first
+//    whole tiles free (C3: 176 half tiles; 100.6-104.9 us, against ~120 us
+//    with 88 whole tiles in the last round and 109-114 us with the half
+//    tiles as a second launch).  Problems of at most 128 whole tiles run as
+//    256 x 128 tiles throughout when that fills more CUs.  Splitting the
+//    last tiles along K over two workgroups instead measured slower (132 us
+//    against 112 us): each piece's int32 partial tile (256 KiB) has to go
 //    through memory to the other piece, as much traffic as the split saves.
 //  * The slabs go straight from global memory into LDS
 //    (global_load_lds_dwordx4: each instruction moves 16 rows x 64 bytes;
@@ -428,29 +432,15 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
   });
 }
 
-// Tiles cover output columns n0 .. (tile column tn at n0 + tn * TN).
+// One tile of shape T: tile t of a grid of tiles_m x tiles_n tiles (M
+// fastest) covering output columns n0 .. (tile column tn at n0 + tn * TN).
 template <class T, bool PRE, bool TR>
-__global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m, int tiles_n,
-                                                       int64_t n0) {
-  __shared__ __attribute__((aligned(16))) int8_t st0[T::STAGE];
-  __shared__ __attribute__((aligned(16))) int8_t st1[T::STAGE];
-  __shared__ __attribute__((aligned(16))) int8_t st2[T::STAGE];
-  __shared__ __attribute__((aligned(16))) float epi_sc[T::TN];
-  __shared__ __attribute__((aligned(16))) float epi_bi[T::TN];
-  __shared__ __attribute__((aligned(16))) int32_t epi_ws[T::TN];
-
+__device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, int t, int tiles_m,
+                                          int64_t n0) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / T::WAVES_M, wm = wave % T::WAVES_M;
-
-  // Workgroups are dispatched round-robin over the 8 XCDs: XCD x walks a
-  // contiguous run of tiles (M fastest), which share slabs in its L2.
-  const int nt = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  const int per = nt / 8;
-  int t = b;
-  if (b < per * 8) t = (b % 8) * per + (b / 8);
   const int KT = (int)(a.K / T::BK);
   const int tm = t % tiles_m;
   const int tn = t / tiles_m;
@@ -497,10 +487,9 @@ __global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m,
       e_sc = a.wscale[n];
       e_bi = a.bias ? a.bias[n] : 0.0f;
     }
-    epi_ws[cslot<T::TN>(tid)] = PRE && n < N ? a.wsum_pre[n] : 0;
+    sm.ws[cslot<T::TN>(tid)] = PRE && n < N ? a.wsum_pre[n] : 0;
   }
 
-  const Smem sm{st0, st1, st2, epi_sc, epi_bi, epi_ws};
   const int xr0 = 32 * T::FM * wm;
   const int wr0 = 32 * T::FN * wn;
   // sum w: of the WAVES_M waves that read the same weight rows, wave wm sums
@@ -524,16 +513,36 @@ __global__ __launch_bounds__(T::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m,
   }
 }
 
-template <class T, bool PRE>
-hipError_t launch_t(const LinearArgs& a, hipStream_t s, int64_t n0, int tiles_n) {
-  const int tiles_m = (int)((a.M + T::BM - 1) / T::BM);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  // fp32 output (fused dequantize): the transposed form, whole-line stores
-  if (a.outf != nullptr && a.acc == nullptr)
-    hipLaunchKernelGGL((k_gemm_w8<T, PRE, true>), grid, dim3(T::NT), 0, s, a, tiles_m, tiles_n, n0);
+// Workgroups below nta take tiles of shape TA (tiles_ma x tiles_na, from
+// column 0), the rest tiles of shape TB (tiles_mb x tiles_nb from column
+// n0b): the columns left after whole rounds of TA tiles, in one launch, so
+// that TB tiles start on the CUs the first TA tiles free.  Within each part
+// the workgroups are dispatched round-robin over the 8 XCDs; they are
+// renumbered so that XCD x walks a contiguous run of tiles (M fastest),
+// which share slabs in its L2.
+template <class TA, class TB, bool PRE, bool TR>
+__global__ __launch_bounds__(TA::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_ma, int tiles_na,
+                                                        int tiles_mb, int tiles_nb, int64_t n0b) {
+  static_assert(TA::NT == TB::NT, "one block size");
+  constexpr int STAGE = TA::STAGE > TB::STAGE ? TA::STAGE : TB::STAGE;
+  constexpr int TN = TA::TN > TB::TN ? TA::TN : TB::TN;
+  __shared__ __attribute__((aligned(16))) int8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) int8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) int8_t st2[STAGE];
+  __shared__ __attribute__((aligned(16))) float epi_sc[TN];
+  __shared__ __attribute__((aligned(16))) float epi_bi[TN];
+  __shared__ __attribute__((aligned(16))) int32_t epi_ws[TN];
+  const Smem sm{st0, st1, st2, epi_sc, epi_bi, epi_ws};
+  auto remap = [](int b, int nt) {
+    const int per = nt / 8;
+    return b < per * 8 ? (b % 8) * per + (b / 8) : b;
+  };
+  const int nta = tiles_ma * tiles_na;
+  const int b = blockIdx.x;
+  if (b < nta)
+    gemm_tile<TA, PRE, TR>(a, sm, remap(b, nta), tiles_ma, 0);
   else
-    hipLaunchKernelGGL((k_gemm_w8<T, PRE, false>), grid, dim3(T::NT), 0, s, a, tiles_m, tiles_n, n0);
-  return hipGetLastError();
+    gemm_tile<TB, PRE, TR>(a, sm, remap(b - nta, tiles_mb * tiles_nb), tiles_mb, n0b);
 }
 
 using T256 = Tile<2, 4, 4, 2>;   // 256 x 256, waves of 128 x 64
@@ -547,17 +556,30 @@ hipError_t launch_plan(const LinearArgs& a, hipStream_t s) {
   // Whole rounds of 256 x 256 tiles over the 256 CUs, then the remaining
   // columns as 256 x 128 tiles when those fit one round: the last round then
   // keeps twice as many CUs busy, each with half a tile.
+  // Problems of at most 128 such tiles run as 256 x 128 tiles throughout
+  // when those fill more CUs within one round.
+  int64_t cols = tiles_n, rest = 0;
+  const int64_t tiles_mb = (a.M + T128::BM - 1) / T128::BM;
   if (tiles % 256 != 0 && 256 % tiles_m == 0 && tiles > 256) {
-    const int64_t cols = tiles / 256 * 256 / tiles_m;
-    const int64_t rest = tiles_n - cols;
-    const int64_t half_tiles = rest * ((a.M + T128::BM - 1) / T128::BM);
-    if (half_tiles <= 256) {
-      hipError_t e = launch_t<T256, PRE>(a, s, 0, (int)cols);
-      if (e != hipSuccess) return e;
-      return launch_t<T128, PRE>(a, s, cols * T256::TN, (int)rest);
+    const int64_t c = tiles / 256 * 256 / tiles_m;
+    if ((tiles_n - c) * tiles_mb <= 256) {
+      cols = c;
+      rest = tiles_n - c;
     }
+  } else if (tiles <= 128 && tiles_mb * tiles_n <= 256 && tiles_mb > tiles_m) {
+    cols = 0;
+    rest = tiles_n;
   }
-  return launch_t<T256, PRE>(a, s, 0, (int)tiles_n);
+  const dim3 grid((unsigned)(tiles_m * cols + tiles_mb * rest));
+  const int64_t n0b = cols * T256::TN;
+  // fp32 output (fused dequantize): the transposed form, whole-line stores
+  if (a.outf != nullptr && a.acc == nullptr)
+    hipLaunchKernelGGL((k_gemm_w8<T256, T128, PRE, true>), grid, dim3(T256::NT), 0, s, a,
+                       (int)tiles_m, (int)cols, (int)tiles_mb, (int)rest, n0b);
+  else
+    hipLaunchKernelGGL((k_gemm_w8<T256, T128, PRE, false>), grid, dim3(T256::NT), 0, s, a,
+                       (int)tiles_m, (int)cols, (int)tiles_mb, (int)rest, n0b);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -568,8 +590,12 @@ bool gemm_w8_supported(const LinearArgs& a) {
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
-int64_t gemm_w8_tiles(const LinearArgs& a) {
-  return ((a.M + T256::BM - 1) / T256::BM) * ((a.N + T256::TN - 1) / T256::TN);
+bool gemm_w8_preferred(const LinearArgs& a) {
+  if (!gemm_w8_supported(a) || a.K < 1024) return false;
+  const int64_t tiles_n = (a.N + T256::TN - 1) / T256::TN;
+  const int64_t tiles = ((a.M + T256::BM - 1) / T256::BM) * tiles_n;
+  const int64_t half = ((a.M + T128::BM - 1) / T128::BM) * tiles_n;
+  return tiles >= 256 || (tiles <= 128 && half >= 128 && half <= 256);
 }
 
 hipError_t launch_gemm_w8(const LinearArgs& a, hipStream_t s) {

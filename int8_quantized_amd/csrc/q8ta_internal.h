@@ -239,7 +239,8 @@ hipError_t launch_gemm_mx(const LinearArgs& a, hipStream_t s);
 // Eight-wave 256 x 256-tile matrix-core GEMM with slab loads straight into
 // LDS (gemm_w8.hip): K a multiple of 64, x and w 16-byte aligned.
 bool gemm_w8_supported(const LinearArgs& a);
-int64_t gemm_w8_tiles(const LinearArgs& a);
+// The default choice takes it (K >= 1024 and its tiles keep most CUs busy).
+bool gemm_w8_preferred(const LinearArgs& a);
 hipError_t launch_gemm_w8(const LinearArgs& a, hipStream_t s);
 int64_t prepacked_bytes(int64_t N, int64_t K);
 hipError_t launch_prepack(const int8_t* w, int64_t N, int64_t K, int8_t* packed, hipStream_t s);
