@@ -488,8 +488,7 @@ def main():
         "kernel": "k_gemm_w8 (v_mfma_i32_32x32x32_i8; 1 workgroup of 8 waves per CU, slabs "
                   "straight into LDS over 3 stages, mid-step barrier, transposed fp32 stores): "
                   "one launch of 256 tiles of 256x256 (waves of 128x64) for the first 8192 "
-                  "columns, one of 176 tiles of 256x128 (waves of 64x64) for the last 2816; "
-                  "avg_launch_us is the whole call",
+                  "columns, then 176 tiles of 256x128 (waves of 64x64) for the last 2816",
         "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_INT8_TOPS, 4),
         "traffic": traffic_from_profile("gemm_w8", os.path.join(CSRC, "gemm_w8.hip")),
