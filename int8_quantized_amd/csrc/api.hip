@@ -18,6 +18,11 @@
 
 #include "q8ta_internal.h"
 
+namespace q8ta {
+// Kernel-family choice forced through q8ta_select_kernel (0 = default).
+extern std::atomic<char> g_sel_linear, g_sel_deconv, g_sel_conv;
+}  // namespace q8ta
+
 using namespace q8ta;
 
 namespace {
@@ -164,8 +169,12 @@ q8ta_status linear_impl(const char* op, bool gemv_only, const int8_t* x, int64_t
   a.dq_zp = (int32_t)output_zero_point;
   a.wsum_pre = wsum_pre;
   if (packed) {
+    // the eight-wave kernel where the default choice (or the selection) takes
+    // it, else the 256 x 128-tile kernel of gemm_pk.hip
     a.wpk = weight;
-    return hip_status(launch_gemm_pk(a, stream), op);
+    const char k = g_sel_linear.load(std::memory_order_relaxed);
+    const bool w8 = k == 'w' ? gemm_w8_supported(a) : (k == 0 && gemm_w8_preferred(a));
+    return hip_status(w8 ? launch_gemm_w8(a, stream) : launch_gemm_pk(a, stream), op);
   }
   if (xf) {
     a.xf = xf;

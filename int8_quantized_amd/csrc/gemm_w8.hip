@@ -141,10 +141,10 @@ struct Smem {
 // K loop and epilogue of one wave with FN weight fragments (32 rows each)
 // starting at tile row wr0 and activation rows xr0 .. xr0 + 63.  SUMK: the W
 // slice this wave sums for sum w (-1: none; PRE: never).
-template <class T, int SUMK, int SPAR, bool PRE, bool TR>
+template <class T, int SUMK, int SPAR, bool PRE, bool TR, bool PK>
 __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
                                     const int8_t* const (&gb)[T::NQ], const uint32_t (&voff)[T::NQ],
-                                    const int (&ldo)[T::NQ],
+                                    const int (&ldo)[T::NQ], const int (&kst)[T::NQ],
                                     int wr0, int xr0, int lane, int tid, int KT, int64_t bm0,
                                     int64_t bn0, float e_sc, float e_bi) {
   constexpr int FN = T::FN, FM = T::FM;
@@ -163,11 +163,10 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
   };
   auto issue = [&](int k, auto SI) {
     int8_t* d = stage(SI);
-    const int64_t ko = (int64_t)k * T::BK;
     Static<0, T::NQ>::each([&](auto Q) {
       constexpr int q = decltype(Q)::value;
-      __builtin_amdgcn_global_load_lds((const void*)(gb[q] + ko + voff[q]), Q8TA_LDS(d + ldo[q]), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(gb[q] + (int64_t)k * kst[q] + voff[q]),
+                                       Q8TA_LDS(d + ldo[q]), 16, 0, 0);
     });
   };
 
@@ -181,7 +180,9 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
   auto read_frag = [&](const int8_t* S, v4i (&af)[FN], v4i (&bf)[FM], auto KSI, auto R) {
     constexpr int ks = decltype(KSI)::value, r = decltype(R)::value;
     const int cpos = 16 * swz4(lrow, 2 * ks + kg);
-    if constexpr (r < FN)
+    if constexpr (r < FN && PK)   // 1 KiB fragments (32-row block, slice) in lane order
+      af[r] = *reinterpret_cast<const v4i*>(S + ((wr0 / 32 + r) * 2 + ks) * 1024 + 16 * lane);
+    else if constexpr (r < FN)
       af[r] = *reinterpret_cast<const v4i*>(S + a_off + r * 32 * T::BK + cpos);
     else
       bf[r - FN] = *reinterpret_cast<const v4i*>(S + b_off + (r - FN) * 32 * T::BK + cpos);
@@ -434,7 +435,7 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
 
 // One tile of shape T: tile t of a grid of tiles_m x tiles_n tiles (M
 // fastest) covering output columns n0 .. (tile column tn at n0 + tn * TN).
-template <class T, bool PRE, bool TR>
+template <class T, bool PRE, bool TR, bool PK>
 __device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, int t, int tiles_m,
                                           int64_t n0) {
   const int tid = threadIdx.x;
@@ -455,9 +456,13 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, i
   // The block's base address is wave-uniform (scalar registers) and each
   // lane adds a 32-bit offset within the tile, so a load is one scalar base
   // plus one vector register and a step advances only the scalar base.
+  // With a prepacked weight (PK) the W blocks are its 1 KiB fragments
+  // instead: block 2j + s of a step is slice s of 32-row block j of the tile,
+  // fetched whole (lane l: bytes 16 l ..), two fragments per K step.
   const int8_t* gb[T::NQ];
   uint32_t voff[T::NQ];
   int ldo[T::NQ];
+  int kst[T::NQ];   // bytes a step advances the block's source
   {
     const int br = lane >> 2;
     const int chunk = swz4(br, lane & 3);
@@ -465,7 +470,14 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, i
       constexpr int q = decltype(Q)::value;
       const int blk = wave * T::NQ + q;
       ldo[q] = blk * 1024;
-      if (blk < T::NBW) {
+      kst[q] = T::BK;
+      if (blk < T::NBW && PK) {
+        const int64_t KS = 2 * (K / 64), NB = (N + 31) / 32;
+        const int64_t nb = bn0 / 32 + blk / 2;
+        gb[q] = a.wpk;
+        voff[q] = (uint32_t)(((nb < NB ? nb : NB - 1) * KS + (blk & 1)) * 1024 + 16 * lane);
+        kst[q] = 2048;
+      } else if (blk < T::NBW) {
         const int64_t n = bn0 + 16 * blk + br;
         gb[q] = a.w + bn0 * K;
         voff[q] = (uint32_t)(((n < N ? n : N - 1) - bn0) * K + 16 * chunk);
@@ -497,18 +509,18 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, i
   // there are two such waves), so the v_dot4 work is the same on every SIMD.
   static_assert(T::WAVES_M == 2 || T::WAVES_M == 4, "sum w split");
   if (PRE) {
-    run<T, -1, -1, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi);
+    run<T, -1, -1, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi);
   } else if constexpr (T::WAVES_M == 2) {
     if (wm == 0)
-      run<T, 0, -1, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi);
+      run<T, 0, -1, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi);
     else
-      run<T, 1, -1, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi);
+      run<T, 1, -1, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi);
   } else {
     switch (wm) {
-      case 0: run<T, 0, 0, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
-      case 1: run<T, 1, 0, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
-      case 2: run<T, 0, 1, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
-      default: run<T, 1, 1, PRE, TR>(a, sm, gb, voff, ldo, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
+      case 0: run<T, 0, 0, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
+      case 1: run<T, 1, 0, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
+      case 2: run<T, 0, 1, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
+      default: run<T, 1, 1, PRE, TR, PK>(a, sm, gb, voff, ldo, kst, wr0, xr0, lane, tid, KT, bm0, bn0, e_sc, e_bi); break;
     }
   }
 }
@@ -520,7 +532,7 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, i
 // the workgroups are dispatched round-robin over the 8 XCDs; they are
 // renumbered so that XCD x walks a contiguous run of tiles (M fastest),
 // which share slabs in its L2.
-template <class TA, class TB, bool PRE, bool TR>
+template <class TA, class TB, bool PRE, bool TR, bool PK>
 __global__ __launch_bounds__(TA::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_ma, int tiles_na,
                                                         int tiles_mb, int tiles_nb, int64_t n0b) {
   static_assert(TA::NT == TB::NT, "one block size");
@@ -540,15 +552,15 @@ __global__ __launch_bounds__(TA::NT, 1) void k_gemm_w8(LinearArgs a, int tiles_m
   const int nta = tiles_ma * tiles_na;
   const int b = blockIdx.x;
   if (b < nta)
-    gemm_tile<TA, PRE, TR>(a, sm, remap(b, nta), tiles_ma, 0);
+    gemm_tile<TA, PRE, TR, PK>(a, sm, remap(b, nta), tiles_ma, 0);
   else
-    gemm_tile<TB, PRE, TR>(a, sm, remap(b - nta, tiles_mb * tiles_nb), tiles_mb, n0b);
+    gemm_tile<TB, PRE, TR, PK>(a, sm, remap(b - nta, tiles_mb * tiles_nb), tiles_mb, n0b);
 }
 
 using T256 = Tile<2, 4, 4, 2>;   // 256 x 256, waves of 128 x 64
 using T128 = Tile<4, 2, 2, 2>;   // 256 W rows x 128 X rows, waves of 64 x 64
 
-template <bool PRE>
+template <bool PRE, bool PK>
 hipError_t launch_plan(const LinearArgs& a, hipStream_t s) {
   const int64_t tiles_m = (a.M + T256::BM - 1) / T256::BM;
   const int64_t tiles_n = (a.N + T256::TN - 1) / T256::TN;
@@ -574,10 +586,10 @@ hipError_t launch_plan(const LinearArgs& a, hipStream_t s) {
   const int64_t n0b = cols * T256::TN;
   // fp32 output (fused dequantize): the transposed form, whole-line stores
   if (a.outf != nullptr && a.acc == nullptr)
-    hipLaunchKernelGGL((k_gemm_w8<T256, T128, PRE, true>), grid, dim3(T256::NT), 0, s, a,
+    hipLaunchKernelGGL((k_gemm_w8<T256, T128, PRE, true, PK>), grid, dim3(T256::NT), 0, s, a,
                        (int)tiles_m, (int)cols, (int)tiles_mb, (int)rest, n0b);
   else
-    hipLaunchKernelGGL((k_gemm_w8<T256, T128, PRE, false>), grid, dim3(T256::NT), 0, s, a,
+    hipLaunchKernelGGL((k_gemm_w8<T256, T128, PRE, false, PK>), grid, dim3(T256::NT), 0, s, a,
                        (int)tiles_m, (int)cols, (int)tiles_mb, (int)rest, n0b);
   return hipGetLastError();
 }
@@ -585,8 +597,11 @@ hipError_t launch_plan(const LinearArgs& a, hipStream_t s) {
 }  // namespace
 
 bool gemm_w8_supported(const LinearArgs& a) {
-  const bool al = (((uintptr_t)a.x | (uintptr_t)a.w) & 15) == 0;
-  return a.K % 64 == 0 && a.K > 0 && al && a.M > 0 && a.N > 0 &&
+  const int8_t* w = a.wpk ? a.wpk : a.w;
+  const bool al = (((uintptr_t)a.x | (uintptr_t)w) & 15) == 0;
+  // a prepacked weight comes with its sums; its fragment offsets are 32-bit
+  const bool pk_ok = !a.wpk || (a.wsum_pre && (a.N + 31) / 32 * 32 * a.K < ((int64_t)1 << 32));
+  return a.K % 64 == 0 && a.K > 0 && al && pk_ok && a.M > 0 && a.N > 0 &&
          a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
@@ -600,7 +615,8 @@ bool gemm_w8_preferred(const LinearArgs& a) {
 
 hipError_t launch_gemm_w8(const LinearArgs& a, hipStream_t s) {
   if (!gemm_w8_supported(a)) return hipErrorInvalidValue;
-  return a.wsum_pre ? launch_plan<true>(a, s) : launch_plan<false>(a, s);
+  if (a.wpk) return launch_plan<true, true>(a, s);
+  return a.wsum_pre ? launch_plan<true, false>(a, s) : launch_plan<false, false>(a, s);
 }
 
 }  // namespace q8ta

@@ -1241,21 +1241,28 @@ PK_SHAPES = [(300, 1040, 257), (64, 128, 64), (512, 4096, 768), (5, 64, 32), (12
              (1, 4096, 512), (700, 256, 1100), (256, 192, 256)]
 
 
+@pytest.mark.parametrize("path", ["default", "mfma32", "mfma32_8w"])
 @pytest.mark.parametrize("M,K,N", PK_SHAPES)
-def test_linear_prepacked_parity(M, K, N):
+def test_linear_prepacked_parity(M, K, N, path):
     """q8ta_linear_prepacked / _dq_prepacked with the weight's own sums: equal
-    to the oracle (int8 codes, and their dequantized fp32 values bit for bit)."""
-    _say(f"linear prepacked M={M} K={K} N={N}")
+    to the oracle (int8 codes, and their dequantized fp32 values bit for bit),
+    on the 256 x 128-tile kernel of gemm_pk.hip ("mfma32") and the eight-wave
+    kernel's prepacked mode ("mfma32_8w", K % 64 == 0)."""
+    _say(f"linear prepacked {path} M={M} K={K} N={N}")
     c = qi.linear_case(M * 5 + K + N + 11, M, K, N)
     packed, sums = _prepack(c.w)
     out = torch.empty((M, N), dtype=torch.int8, device="cuda")
-    q8.q8ta_linear_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
-                             dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none", out)
+    with kernel("linear", path):
+        q8.q8ta_linear_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
+                                 dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp, "none",
+                                 out)
     ref = _oracle_linear(c)
     np.testing.assert_array_equal(host(out), ref)
     outf = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    q8.q8ta_linear_dq_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
-                                dev(c.weight_scales), None, c.out_scale, c.out_zp, "relu", outf)
+    with kernel("linear", path):
+        q8.q8ta_linear_dq_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, N, sums,
+                                    dev(c.weight_scales), None, c.out_scale, c.out_zp, "relu",
+                                    outf)
     refr = oracle.dequantize_per_tensor(_oracle_linear(c, bias=False, activation="relu"),
                                         c.out_scale, c.out_zp)
     np.testing.assert_array_equal(host(outf).view(np.uint32), refr.view(np.uint32))
