@@ -105,7 +105,7 @@ struct Tile {
   // bytes per stage: the blocks at 1 KiB each (W first, then X), then the
   // landing place of the padding loads that even out the waves' counts
   static constexpr int STAGE = WAVES * NQ * 1024;
-  static_assert(TN <= NT, "one channel per thread in the constant staging");
+  static constexpr int CR = (TN + NT - 1) / NT;   // per-channel constants per thread
 };
 
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }
@@ -146,7 +146,8 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
                                     const int8_t* const (&gb)[T::NQ], const uint32_t (&voff)[T::NQ],
                                     const int (&ldo)[T::NQ], const int (&kst)[T::NQ],
                                     int wr0, int xr0, int lane, int tid, int KT, int64_t bm0,
-                                    int64_t bn0, float e_sc, float e_bi) {
+                                    int64_t bn0, const float (&e_sc)[T::CR],
+                                    const float (&e_bi)[T::CR]) {
   constexpr int FN = T::FN, FM = T::FM;
   constexpr int NR = FN + FM;   // fragment reads per slice
   constexpr int NP = FN * FM;   // products per slice
@@ -273,10 +274,14 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
         atomicAdd(&sm.ws[cslot<T::TN>(wr0 + i * 32 + lrow)], wsum[i]);
     });
   }
-  if (tid < T::TN) {
-    sm.sc[cslot<T::TN>(tid)] = e_sc;
-    sm.bi[cslot<T::TN>(tid)] = e_bi;
-  }
+  Static<0, T::CR>::each([&](auto C) {
+    constexpr int c = decltype(C)::value;
+    const int row = tid + c * T::NT;
+    if (row < T::TN) {
+      sm.sc[cslot<T::TN>(row)] = e_sc[c];
+      sm.bi[cslot<T::TN>(row)] = e_bi[c];
+    }
+  });
   __syncthreads();
 
   // Interior tiles of an output with fewer than 2^31 elements store without
@@ -490,17 +495,24 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, const Smem& sm, i
     });
   }
 
-  // Per-channel constants of tile row tid, fetched before the K loop; sum w
-  // starts at zero (the summing waves add into it) or is the caller's.
-  float e_sc = 0.0f, e_bi = 0.0f;
-  if (tid < T::TN) {
-    const int64_t n = bn0 + tid;
-    if (!a.acc && n < N) {
-      e_sc = a.wscale[n];
-      e_bi = a.bias ? a.bias[n] : 0.0f;
+  // Per-channel constants of tile rows tid, tid + NT, .., fetched before the
+  // K loop; sum w starts at zero (the summing waves add into it) or is the
+  // caller's.
+  float e_sc[T::CR], e_bi[T::CR];
+  Static<0, T::CR>::each([&](auto C) {
+    constexpr int c = decltype(C)::value;
+    const int row = tid + c * T::NT;
+    e_sc[c] = 0.0f;
+    e_bi[c] = 0.0f;
+    if (row < T::TN) {
+      const int64_t n = bn0 + row;
+      if (!a.acc && n < N) {
+        e_sc[c] = a.wscale[n];
+        e_bi[c] = a.bias ? a.bias[n] : 0.0f;
+      }
+      sm.ws[cslot<T::TN>(row)] = PRE && n < N ? a.wsum_pre[n] : 0;
     }
-    sm.ws[cslot<T::TN>(tid)] = PRE && n < N ? a.wsum_pre[n] : 0;
-  }
+  });
 
   const int xr0 = 32 * T::FM * wm;
   const int wr0 = 32 * T::FN * wn;
