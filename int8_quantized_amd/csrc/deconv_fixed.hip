@@ -334,6 +334,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
           w4 = __builtin_amdgcn_sdot4(cur[t][3], 0x01010101, w4, false);
           wsum[ph] += w4;
           cur[t] = wfrag(t, 32 * knext);
+          // keep the refill here: left to itself the compiler sinks every
+          // refill to the end of the step, and the next step then starts
+          // with a wait for all of them
+          __builtin_amdgcn_sched_barrier(0);
         }
       });
 #pragma unroll
