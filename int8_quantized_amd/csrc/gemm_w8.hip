@@ -613,8 +613,9 @@ bool gemm_w8_supported(const LinearArgs& a) {
   const bool al = (((uintptr_t)a.x | (uintptr_t)w) & 15) == 0;
   // a prepacked weight comes with its sums; its fragment offsets are 32-bit
   const bool pk_ok = !a.wpk || (a.wsum_pre && (a.N + 31) / 32 * 32 * a.K < ((int64_t)1 << 32));
-  return a.K % 64 == 0 && a.K > 0 && al && pk_ok && a.M > 0 && a.N > 0 &&
-         a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
+  // the lane offsets within a tile (up to 256 rows of K bytes) are 32-bit
+  return a.K % 64 == 0 && a.K > 0 && a.K < ((int64_t)1 << 24) && al && pk_ok && a.M > 0 &&
+         a.N > 0 && a.M <= (int64_t)1 << 30 && a.N <= (int64_t)1 << 30;
 }
 
 bool gemm_w8_preferred(const LinearArgs& a) {
