@@ -25,7 +25,8 @@
 //     along the row -- transposes the 16x4 bytes in registers and writes four
 //     16-byte pixel chunks.  Out-of-image words hold the zero point.
 //  2. Each wave owns one phase row i and FO output-channel fragments and runs
-//     the phases one after another: for every tap of the phase and every 64
+//     its phases one after another (all of them, or every PS-th when PS waves
+//     split them): for every tap of the phase and every 64
 //     channels, FJ activation fragments come from LDS and FO weight fragments
 //     (16 channels x 64 input channels, K-contiguous rows of the [OC, ldw]
 //     weight) come straight from global memory / L2; v_mfma_i32_16x16x64_i8
@@ -73,6 +74,7 @@ struct Plan {
   int dhmin, dwmin;
   int Hp, Wp;                 // phase rows / columns: ceil(H_out/s_h), ceil(W_out/s_w)
   int WI, WO, TJ, OCB;        // workgroup tile
+  int PS;                     // waves splitting the phases (1: a wave runs them all)
   int HR, HC, ICP;            // staged input tile: rows, columns (multiple of 4), channels (x64)
   int ORows, OCols, OPlane;   // staged output tile
   int tiles_i, tiles_j, tiles_oc;
@@ -114,6 +116,75 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
   const int H_in = (int)a.H_in, W_in = (int)a.W_in, IC = (int)a.IC;
   const int row0 = i0 + p.dhmin;                 // input row of LDS row 0
   const int col0 = ((j0 + p.dwmin) >> 2) * 4;   // input column of LDS column 0 (floor to 4)
+
+  // Wave roles: phase row wi of the tile, output-channel group wo, and phase
+  // group ps (the wave runs phases ps, ps + PS, ... of the s_h * s_w).
+  const int waves_used = p.WI * p.WO * p.PS;
+  const bool active = wave < waves_used;
+  const int wi = wave % p.WI;
+  const int wo = (wave / p.WI) % p.WO;
+  const int ps = wave / (p.WI * p.WO);
+  const int i = i0 + wi;
+  const int ocw = oc0 + wo * 16 * FO;
+  const int sh = (int)a.sh, sw = (int)a.sw;
+  const int S = sh * sw;
+  const int NQ64 = p.ICP >> 6;
+  // first phase s' >= s of this wave whose output row exists
+  auto next_phase = [&](int s) {
+    while (s < S && s / sw + sh * i >= (int)a.H_out) s += p.PS;
+    return s;
+  };
+
+  // Per-phase iteration state.  A phase's (tap row, tap column, 64-channel
+  // slice) iterations run as one flat sequence; the weight fragments of
+  // iteration it + kDepth are requested while iteration it computes (ring of
+  // kDepth + 1 register buffers), so their global/L2 latency overlaps the
+  // MFMAs.  The first phase's first fragments are requested before the input
+  // staging, so that latency overlaps the staging's.
+  constexpr int R = kDepth + 1;
+  v4i bb[R][FO];
+  int rh = 0, rw = 0, nth = 0, ntw = 0, nit = 0;
+  int hk0 = 0, hks = 0, hd0 = 0, hds = 0, wk0 = 0, wks = 0, wd0 = 0, wds = 0;
+  int pth = 0, ptw = 0, pc = 0;   // prefetch cursor
+  int cth = 0, ctw = 0, cc = 0;   // compute cursor
+  // The loads are unconditional (an exec-masked load would make the
+  // compiler wait for every outstanding load before the next MFMA):
+  // rows past OC read row OC - 1 (their accumulators are never
+  // stored) and channel chunks past IC read the row's last chunk
+  // (their activations are zero in LDS; their weight sums are dropped
+  // in `compute`).  tapoff + icb + 16 <= Kh*Kw*IC <= ldw.
+  auto load_b = [&](v4i (&dst)[FO]) {
+    const int64_t tapoff = (int64_t)((hk0 + pth * hks) * (int)a.Kw + wk0 + ptw * wks) * IC;
+    const int icb = (pc * 4 + lgrp) * 16;
+    const int icc = icb < IC ? icb : IC - 16;
+#pragma unroll
+    for (int f = 0; f < FO; ++f) {
+      const int oc = ocw + f * 16 + lrow;
+      const int occ = oc < a.OC ? oc : (int)a.OC - 1;
+      dst[f] = *reinterpret_cast<const v4i*>(a.w + (int64_t)occ * a.ldw + tapoff + icc);
+    }
+    // advance, saturating at the phase's last iteration (prefetches
+    // past the end re-read it and are never consumed)
+    if (++pc == NQ64) {
+      pc = 0;
+      if (++ptw == ntw) { ptw = 0; ++pth; }
+    }
+    if (pth >= nth) { pth = nth - 1; ptw = ntw - 1; pc = NQ64 - 1; }
+  };
+  auto setup = [&](int s) {
+    rh = s / sw;
+    rw = s - rh * sw;
+    nth = p.nth[rh];
+    ntw = p.ntw[rw];
+    nit = nth * ntw * NQ64;
+    hk0 = p.hk0[rh]; hks = p.hks[rh]; hd0 = p.hd0[rh] - p.dhmin; hds = p.hds[rh];
+    wk0 = p.wk0[rw]; wks = p.wks[rw]; wd0 = p.wd0[rw]; wds = p.wds[rw];
+    pth = ptw = pc = 0;
+    cth = ctw = cc = 0;
+    if (nit > 0) Static<0, kDepth>::each([&](auto U) { load_b(bb[decltype(U)::value]); });
+  };
+  int s = active ? next_phase(ps) : S;
+  if (s < S) setup(s);
 
   // ---- 1. stage the input halo tile -------------------------------------
   {
@@ -191,15 +262,7 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
   __syncthreads();
 
   // ---- 2. per-wave phase loop --------------------------------------------
-  const int waves_used = p.WI * p.WO;
-  if (wave < waves_used) {
-    const int wi = wave % p.WI;
-    const int wo = wave / p.WI;
-    const int i = i0 + wi;
-    const int ocw = oc0 + wo * 16 * FO;
-    const int sh = (int)a.sh, sw = (int)a.sw;
-    const int NQ64 = p.ICP >> 6;
-
+  if (active) {
     // Scales and bias only for the requantizing call (the accumulator entry
     // point passes no weight_scales).
     float sc[FO], bi[FO];
@@ -211,132 +274,95 @@ __global__ __launch_bounds__(512) void k_deconv(DeconvArgs a, Plan p) {
       bi[f] = (ok && a.bias) ? a.bias[oc] : 0.0f;
     }
 
-    for (int rh = 0; rh < sh; ++rh) {
+    while (s < S) {
       const int oh = rh + sh * i;
-      if (oh >= a.H_out) continue;
-      for (int rw = 0; rw < sw; ++rw) {
-        v4i acc[FJ][FO];
-        int32_t wsum[FO];
+      v4i acc[FJ][FO];
+      int32_t wsum[FO];
+#pragma unroll
+      for (int f = 0; f < FO; ++f) {
+        wsum[f] = 0;
+#pragma unroll
+        for (int g = 0; g < FJ; ++g) acc[g][f] = v4i{0, 0, 0, 0};
+      }
+      auto compute = [&](const v4i (&bf)[FO]) {
+        const int lr = wi + hd0 + cth * hds;
+        const int dw = wd0 + ctw * wds;
+        const int q = cc * 4 + lgrp;
+        v4i af[FJ];
+#pragma unroll
+        for (int g = 0; g < FJ; ++g) {
+          const int c = j0 + g * 16 + lrow + dw - col0;
+          af[g] = *reinterpret_cast<const v4i*>(xs + ((int64_t)(lr * p.HC + c) * p.ICP) +
+                                                16 * xswz(c, q, p.ICP));
+        }
+        const bool in_ic = q * 16 < IC;
 #pragma unroll
         for (int f = 0; f < FO; ++f) {
-          wsum[f] = 0;
-#pragma unroll
-          for (int g = 0; g < FJ; ++g) acc[g][f] = v4i{0, 0, 0, 0};
+          int32_t t = __builtin_amdgcn_sdot4(bf[f][0], 0x01010101, 0, false);
+          t = __builtin_amdgcn_sdot4(bf[f][1], 0x01010101, t, false);
+          t = __builtin_amdgcn_sdot4(bf[f][2], 0x01010101, t, false);
+          t = __builtin_amdgcn_sdot4(bf[f][3], 0x01010101, t, false);
+          wsum[f] += in_ic ? t : 0;
         }
-        // The phase's (tap row, tap column, 64-channel slice) iterations in
-        // one flat sequence; the weight fragments of iteration it + kDepth
-        // are requested while iteration it computes (ring of kDepth + 1
-        // register buffers), so their global/L2 latency overlaps the MFMAs.
-        const int nth = p.nth[rh], ntw = p.ntw[rw];
-        const int nit = nth * ntw * NQ64;
-        const int hk0 = p.hk0[rh], hks = p.hks[rh], hd0 = p.hd0[rh] - p.dhmin, hds = p.hds[rh];
-        const int wk0 = p.wk0[rw], wks = p.wks[rw], wd0 = p.wd0[rw], wds = p.wds[rw];
-        constexpr int R = kDepth + 1;
-        v4i bb[R][FO];
-        int pth = 0, ptw = 0, pc = 0;   // prefetch cursor
-        // The loads are unconditional (an exec-masked load would make the
-        // compiler wait for every outstanding load before the next MFMA):
-        // rows past OC read row OC - 1 (their accumulators are never
-        // stored) and channel chunks past IC read the row's last chunk
-        // (their activations are zero in LDS; their weight sums are dropped
-        // in `compute`).  tapoff + icb + 16 <= Kh*Kw*IC <= ldw.
-        auto load_b = [&](v4i (&dst)[FO]) {
-          const int64_t tapoff = (int64_t)((hk0 + pth * hks) * (int)a.Kw + wk0 + ptw * wks) * IC;
-          const int icb = (pc * 4 + lgrp) * 16;
-          const int icc = icb < IC ? icb : IC - 16;
 #pragma unroll
-          for (int f = 0; f < FO; ++f) {
-            const int oc = ocw + f * 16 + lrow;
-            const int occ = oc < a.OC ? oc : (int)a.OC - 1;
-            dst[f] = *reinterpret_cast<const v4i*>(a.w + (int64_t)occ * a.ldw + tapoff + icc);
-          }
-          // advance, saturating at the phase's last iteration (prefetches
-          // past the end re-read it and are never consumed)
-          if (++pc == NQ64) {
-            pc = 0;
-            if (++ptw == ntw) { ptw = 0; ++pth; }
-          }
-          if (pth >= nth) { pth = nth - 1; ptw = ntw - 1; pc = NQ64 - 1; }
-        };
-        int cth = 0, ctw = 0, cc = 0;   // compute cursor
-        auto compute = [&](const v4i (&bf)[FO]) {
-          const int lr = wi + hd0 + cth * hds;
-          const int dw = wd0 + ctw * wds;
-          const int q = cc * 4 + lgrp;
-          v4i af[FJ];
+        for (int g = 0; g < FJ; ++g)
 #pragma unroll
-          for (int g = 0; g < FJ; ++g) {
-            const int c = j0 + g * 16 + lrow + dw - col0;
-            af[g] = *reinterpret_cast<const v4i*>(xs + ((int64_t)(lr * p.HC + c) * p.ICP) +
-                                                  16 * xswz(c, q, p.ICP));
-          }
-          const bool in_ic = q * 16 < IC;
-#pragma unroll
-          for (int f = 0; f < FO; ++f) {
-            int32_t t = __builtin_amdgcn_sdot4(bf[f][0], 0x01010101, 0, false);
-            t = __builtin_amdgcn_sdot4(bf[f][1], 0x01010101, t, false);
-            t = __builtin_amdgcn_sdot4(bf[f][2], 0x01010101, t, false);
-            t = __builtin_amdgcn_sdot4(bf[f][3], 0x01010101, t, false);
-            wsum[f] += in_ic ? t : 0;
-          }
-#pragma unroll
-          for (int g = 0; g < FJ; ++g)
-#pragma unroll
-            for (int f = 0; f < FO; ++f)
-              acc[g][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[g], bf[f], acc[g][f], 0, 0, 0);
-          if (++cc == NQ64) {
-            cc = 0;
-            if (++ctw == ntw) { ctw = 0; ++cth; }
-          }
-        };
-        // Whole groups of R iterations run without guards, so the compiler
-        // sees every load of the ring and waits only for the oldest; the
-        // remaining nit % R iterations follow.
-        if (nit > 0) {
-          Static<0, kDepth>::each([&](auto U) { load_b(bb[decltype(U)::value]); });
-          const int nfull = nit - nit % R;
-          for (int base = 0; base < nfull; base += R) {
-            Static<0, R>::each([&](auto U) {
-              constexpr int u = decltype(U)::value;
-              load_b(bb[(u + kDepth) % R]);
-              compute(bb[u]);
-            });
-          }
-          Static<0, R - 1>::each([&](auto U) {
+          for (int f = 0; f < FO; ++f)
+            acc[g][f] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[g], bf[f], acc[g][f], 0, 0, 0);
+        if (++cc == NQ64) {
+          cc = 0;
+          if (++ctw == ntw) { ctw = 0; ++cth; }
+        }
+      };
+      // Whole groups of R iterations run without guards, so the compiler
+      // sees every load of the ring and waits only for the oldest; the
+      // remaining nit % R iterations follow.  The ring's first kDepth
+      // fragments were requested by `setup`.
+      if (nit > 0) {
+        const int nfull = nit - nit % R;
+        for (int base = 0; base < nfull; base += R) {
+          Static<0, R>::each([&](auto U) {
             constexpr int u = decltype(U)::value;
-            if (nfull + u < nit) {
-              load_b(bb[(u + kDepth) % R]);
-              compute(bb[u]);
-            }
+            load_b(bb[(u + kDepth) % R]);
+            compute(bb[u]);
           });
         }
-        // epilogue of phase (rh, rw): lane holds pixels j = j0+16g+4*lgrp+e of
-        // output channel ocw + 16f + lrow.
+        Static<0, R - 1>::each([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          if (nfull + u < nit) {
+            load_b(bb[(u + kDepth) % R]);
+            compute(bb[u]);
+          }
+        });
+      }
+      // epilogue of phase (rh, rw): lane holds pixels j = j0+16g+4*lgrp+e of
+      // output channel ocw + 16f + lrow.
 #pragma unroll
-        for (int f = 0; f < FO; ++f) {
-          int32_t v = wsum[f];
-          v += __shfl_xor(v, 16, 64);
-          v += __shfl_xor(v, 32, 64);
-          const int oc = ocw + f * 16 + lrow;
-          const int ocl = oc - oc0;
+      for (int f = 0; f < FO; ++f) {
+        int32_t v = wsum[f];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        const int oc = ocw + f * 16 + lrow;
+        const int ocl = oc - oc0;
 #pragma unroll
-          for (int g = 0; g < FJ; ++g) {
+        for (int g = 0; g < FJ; ++g) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int jl = g * 16 + 4 * lgrp + e;       // phase column within the tile
-              const int ow = rw + sw * (j0 + jl);
-              const int32_t c = acc[g][f][e] - a.izp * v;
-              if (a.acc) {
-                if (oc < a.OC && ow < a.W_out)
-                  a.acc[(((int64_t)n * a.OC + oc) * a.H_out + oh) * a.W_out + ow] = c;
-              } else {
-                const int qv = requant(c, sc[f], bi[f], a.rq);
-                os[ocl * p.OPlane + (rh + sh * wi) * p.OCols + rw + sw * jl] = (int8_t)qv;
-              }
+          for (int e = 0; e < 4; ++e) {
+            const int jl = g * 16 + 4 * lgrp + e;       // phase column within the tile
+            const int ow = rw + sw * (j0 + jl);
+            const int32_t c = acc[g][f][e] - a.izp * v;
+            if (a.acc) {
+              if (oc < a.OC && ow < a.W_out)
+                a.acc[(((int64_t)n * a.OC + oc) * a.H_out + oh) * a.W_out + ow] = c;
+            } else {
+              const int qv = requant(c, sc[f], bi[f], a.rq);
+              os[ocl * p.OPlane + (rh + sh * wi) * p.OCols + rw + sw * jl] = (int8_t)qv;
             }
           }
         }
       }
+      s = next_phase(s + p.PS);
+      if (s < S) setup(s);
     }
   }
   if (a.acc) return;
@@ -501,6 +527,15 @@ bool make_plan(const DeconvArgs& a, Plan& p, int& FJ, int& FO, bool forward = fa
       p.tiles_i = (p.Hp + WI - 1) / WI;
       p.tiles_j = (p.Wp + p.TJ - 1) / p.TJ;
       p.tiles_oc = (int)((a.OC + p.OCB - 1) / p.OCB);
+      // Small problems also split the phases over up to 8 waves, so a wave's
+      // serial chain of weight-fetch latencies is shorter.
+      p.PS = 1;
+      if (small) {
+        const int S = sh * sw;
+        const int room = 8 / (p.WI * p.WO);
+        p.PS = S < room ? S : room;
+        if (p.PS < 1) p.PS = 1;
+      }
       p.x_dword = (a.W_in % 4 == 0) && (((uintptr_t)a.x & 3) == 0);
       p.out_vec = (a.W_out % 16 == 0) && (((uintptr_t)a.out & 15) == 0) && (p.OCols % 16 == 0);
       const int64_t blocks = (int64_t)p.tiles_j * p.tiles_i * p.tiles_oc * a.N;
@@ -521,7 +556,7 @@ hipError_t launch_t(const DeconvArgs& a, const Plan& p, hipStream_t s) {
     attr_set = true;
   }
   const int64_t blocks = (int64_t)p.tiles_j * p.tiles_i * p.tiles_oc * a.N;
-  const int threads = 64 * p.WI * p.WO;
+  const int threads = 64 * p.WI * p.WO * p.PS;
   hipLaunchKernelGGL((k_deconv<FJ, FO>), dim3((unsigned)blocks), dim3(threads), lds, s, a, p);
   return hipGetLastError();
 }
