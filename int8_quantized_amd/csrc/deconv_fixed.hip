@@ -295,11 +295,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
   }
 
   // weight fragments of one step; tap t's register is refilled with the next
-  // step's fragment right after its last product
+  // step's fragment right after its last product.  The 32-channel steps run
+  // in a rotated order, a different rotation for neighbouring workgroups of
+  // one XCD: all workgroups start together and would otherwise request the
+  // same weight lines from L2 at the same moment (the integer sums do not
+  // depend on the order).
   const int nk = IC / 32;
+  const int rot = (int)(blockIdx.x >> 3) % nk;
+  auto kidx = [&](int k) { return k + rot < nk ? k + rot : k + rot - nk; };
   v4i bw[P.T];
 #pragma unroll
-  for (int t = 0; t < P.T; ++t) bw[t] = wfrag(t, 0);
+  for (int t = 0; t < P.T; ++t) bw[t] = wfrag(t, 32 * kidx(0));
   __syncthreads();
 
   // A fragments of shift s, step k
@@ -313,13 +319,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
     }
   };
   v4i acur[NF], anext[NF];
-  aload(acur, P.sdh[0], P.sdw[0], 0);
+  aload(acur, P.sdh[0], P.sdw[0], kidx(0));
   auto step = [&](int k, v4i (&cur)[P.T]) {
-    const int knext = k + 1 < nk ? k + 1 : k;   // past the end: re-read (unused)
+    const int kc = kidx(k);
+    const int knext = k + 1 < nk ? kidx(k + 1) : kc;   // past the end: re-read (unused)
     Static<0, P.NS>::each([&](auto SI) {
       constexpr int s = decltype(SI)::value;
       // the next shift's (or the next step's first shift's) fragments first
-      if constexpr (s + 1 < P.NS) aload(anext, P.sdh[s + 1], P.sdw[s + 1], k);
+      if constexpr (s + 1 < P.NS) aload(anext, P.sdh[s + 1], P.sdw[s + 1], kc);
       else aload(anext, P.sdh[0], P.sdw[0], knext);
       Static<0, P.T>::each([&](auto TI) {
         constexpr int t = decltype(TI)::value;
