@@ -388,32 +388,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
     return;
   }
   // lane: 4 consecutive phase columns x S column residues = 4*S consecutive
-  // output columns of one output row per (row residue, fragment, group)
+  // output columns of one output row per (row residue, fragment, group); the
+  // codes are packed in offset form (code + 128) by the conversion itself
+  const float ozp128 = a.rq.ozp + 128.0f, qmin128 = a.rq.qmin + 128.0f;
+  auto epilogue = [&](auto relu_tag) {
+    constexpr bool RELU = decltype(relu_tag)::value;
 #pragma unroll
-  for (int rh = 0; rh < S; ++rh)
+    for (int rh = 0; rh < S; ++rh)
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        int qv[4 * S];
+        for (int g = 0; g < 4; ++g) {
+          uint32_t wd[S];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < S; ++e) wd[e] = 0;
 #pragma unroll
-          for (int rw = 0; rw < S; ++rw) {
-            const int ph = rh * S + rw;
-            qv[S * e + rw] = requant(acc[ph][f][4 * g + e] - zw[ph], sc, bi, a.rq);
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int rw = 0; rw < S; ++rw) {
+              const int ph = rh * S + rw;
+              const int idx = S * e + rw;
+              wd[idx >> 2] = requant_u8<RELU>(acc[ph][f][4 * g + e] - zw[ph], sc, bi, a.rq, ozp128,
+                                              qmin128, idx & 3, wd[idx >> 2]);
+            }
+          const int orow = (f >> 1) * S + rh;
+          const int col = S * ((f & 1) * 32 + 8 * g + 4 * hi);
+          int8_t* d = os + (ocl * OROWS + orow) * OPITCH + col;
+          if constexpr (S == 2) {
+            typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<v2u*>(d) = v2u{wd[0] ^ 0x80808080u, wd[1] ^ 0x80808080u};
+          } else {
+            *reinterpret_cast<uint32_t*>(d) = wd[0] ^ 0x80808080u;
           }
-        const int orow = (f >> 1) * S + rh;
-        const int col = S * ((f & 1) * 32 + 8 * g + 4 * hi);
-        int8_t* d = os + (ocl * OROWS + orow) * OPITCH + col;
-        if constexpr (S == 2) {
-          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-          *reinterpret_cast<v2u*>(d) =
-              v2u{pack4(qv[0], qv[1], qv[2], qv[3]), pack4(qv[4], qv[5], qv[6], qv[7])};
-        } else {
-          *reinterpret_cast<uint32_t*>(d) = pack4(qv[0], qv[1], qv[2], qv[3]);
         }
-      }
+  };
+  if (a.rq.qmin > -128.0f)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
   __syncthreads();
 
   // ---- copy the output block out: 16-byte pieces, whole rows ---------------

@@ -41,6 +41,30 @@ __device__ __forceinline__ int requant(int32_t acc, float wscale, float b, const
   return (int)q;
 }
 
+// requant() with the code written into byte `sel` of `old` in offset form
+// (code + 128, so byte b of the result XOR 0x80 is the int8 code).  The same
+// left-to-right float steps up to the rounding; then u = rint(t) + (zp + 128),
+// exact for |rint(t)| < 2^24 - 256 and beyond that saturating either way,
+// goes through v_cvt_pk_u8_f32, which saturates at 0 and 255 (u is integral,
+// so its round-to-nearest-even is exact) and inserts the byte: the code of
+// requant() for every finite v.  The lower clamp at -128 is that saturation;
+// RELU adds the clamp at qmin + 128 (qmin128) for the relu-fused epilogue.
+// ozp128 is r.ozp + 128.
+template <bool RELU>
+__device__ __forceinline__ uint32_t requant_u8(int32_t acc, float wscale, float b, const Requant& r,
+                                               float ozp128, float qmin128, uint32_t sel,
+                                               uint32_t old) {
+  float v = (float)acc;
+  v = v * r.s_in;
+  v = v * wscale;
+  v = v + b;
+  float t = v * r.inv_out;
+  float u = __builtin_rintf(t);
+  u = u + ozp128;
+  if constexpr (RELU) u = __builtin_fmaxf(u, qmin128);
+  return __builtin_amdgcn_cvt_pk_u8_f32(u, sel, old);
+}
+
 // quantize_per_tensor of one value ("Add quantize_per_tensor op (int8 buffer
 // path)", commit message): clamp(rint(x * inv) + zp, -128, 127), inv formed on
 // the host as (float)(1.0 / scale).
