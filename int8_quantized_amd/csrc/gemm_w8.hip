@@ -339,6 +339,10 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
     auto row = [&](int m) {
       return (m < RPS ? sm.st0 : (m < 2 * RPS ? sm.st1 : sm.st2)) + (m % RPS) * T::TN;
     };
+    // the four codes of a register group packed in offset form (code + 128)
+    // by the conversion itself (one instantiation with the lower clamp, which
+    // is 0 without relu: a second copy of this loop costs registers)
+    const float ozp128 = a.rq.ozp + 128.0f, qmin128 = a.rq.qmin + 128.0f;
     Static<0, FN>::each([&](auto I) {
       constexpr int i = decltype(I)::value;
       Static<0, 4>::each([&](auto G) {
@@ -356,12 +360,13 @@ __device__ __forceinline__ void run(const LinearArgs& a, const Smem& sm,
         Static<0, FM>::each([&](auto J) {
           constexpr int j = decltype(J)::value;
           const int m = xr0 + j * 32 + lrow;
-          float q[4];
+          uint32_t wd = 0;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            q[r] = requant_code(acc[i][j][4 * g + r] - zc[r], sc[r], bi[r], a.rq);
-          *reinterpret_cast<uint32_t*>(row(m) + 16 * ((rr >> 4) ^ (m & (T::TN / 16 - 1))) + (rr & 15)) =
-              pack4((int)q[0], (int)q[1], (int)q[2], (int)q[3]);
+            wd = requant_u8<true>(acc[i][j][4 * g + r] - zc[r], sc[r], bi[r], a.rq, ozp128,
+                                  qmin128, r, wd);
+          *reinterpret_cast<uint32_t*>(row(m) + 16 * ((rr >> 4) ^ (m & (T::TN / 16 - 1))) +
+                                       (rr & 15)) = wd ^ 0x80808080u;
         });
       });
     });
