@@ -17,10 +17,14 @@
 // Constraints (1), zero-point-filled form).
 //
 // Workgroup: one image, two phase rows, 64 phase columns and 128 output
-// channels (4 waves of 32 channels, one wave per SIMD).  Each wave computes
-// all phases of the tile for its channels: per phase 4 fragments of 32
-// pixels (2 rows x 2 column halves), the accumulators of every phase live
-// together in the accumulation registers.
+// channels.  With stride 2 the taps fall into two groups by output-row
+// residue (the phases (rh, 0) and (rh, 1) of each rh); eight waves, two per
+// SIMD: wave w takes channels 32 (w % 4) .. +31 of group w / 4, so the two
+// waves of a SIMD share its matrix cores and one wave's requantize (vector
+// ALU) runs beside the other's products.  (Within one wave a 32x32x32
+// product hides only about four independent vector instructions.)  A wave's
+// accumulators: 2 phases x 4 fragments of 32 pixels (2 rows x 2 column
+// halves).  With stride 1 (one phase) four waves take all taps.
 // Steps:
 //  * the whole input halo of the tile (all channels) is staged in LDS once,
 //    in the operand's K-contiguous order: 32-bit words of 16 channel planes,
@@ -29,10 +33,11 @@
 //  * then, per 32 channels and per shift, the wave reads its 4 pixel
 //    fragments from LDS once (the A operand; the next shift's fragments are
 //    requested before the current shift's products) and multiplies them with the
-//    weight fragment of every tap that reads that shift (the B operand, lane
-//    l: row l % 32 of the [OC, ldw] weight, K bytes 16 * (l / 32) .. +15,
-//    straight from global memory / L2); each tap's register is refilled with
-//    the next step's fragment right after its last product;
+//    weight fragment of every tap of its group that reads that shift (the B
+//    operand, lane l: row l % 32 of the [OC, ldw] weight, K bytes
+//    16 * (l / 32) .. +15, straight from global memory / L2); each tap's
+//    register is refilled right after its products, two steps ahead from
+//    two register sets where registers allow;
 //  * v_dot4 against 0x01010101 over the weight fragments gives the phase
 //    weight sums.
 #include <type_traits>
@@ -45,11 +50,14 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;   // 4 waves x 32 output channels
+// Threads per workgroup: 8 waves (two per SIMD) for stride 2, whose taps
+// split into two groups; 4 waves for stride 1.
+template <int S>
+constexpr int threads_of() { return S == 2 ? 512 : 256; }
 constexpr int kTR = 2;          // phase rows per workgroup
 constexpr int kTJ = 64;         // phase columns per workgroup
 constexpr int kOCB = 128;       // output channels per workgroup
-constexpr int kStageSlots = 4;  // halo staging units per thread
+constexpr int kStageUnits = 1024;  // halo staging units per workgroup (the host checks the count)
 
 template <int B, int E>
 struct Static {
@@ -113,6 +121,55 @@ struct Pattern {
   }
 };
 
+// Taps of one group: output-row residue g of the stride phases (-1: every
+// tap), in the order the K loop visits them (shift by shift, then by tap).
+struct ShiftList {
+  int n = 0;
+  int s[64] = {};
+};
+
+template <int S, int K, int PM, bool FWD>
+constexpr bool in_group(int t, int g) {
+  constexpr Pattern<S, K, PM, FWD> P{};
+  return g < 0 || P.ph[t] / S == g;
+}
+
+template <int S, int K, int PM, bool FWD>
+constexpr int group_taps(int g) {
+  constexpr Pattern<S, K, PM, FWD> P{};
+  int n = 0;
+  for (int t = 0; t < P.T; ++t) n += in_group<S, K, PM, FWD>(t, g) ? 1 : 0;
+  return n;
+}
+
+// distinct input shifts read by group g, in increasing shift index
+template <int S, int K, int PM, bool FWD>
+constexpr ShiftList group_shifts(int g) {
+  constexpr Pattern<S, K, PM, FWD> P{};
+  ShiftList L{};
+  for (int s = 0; s < P.NS; ++s) {
+    bool used = false;
+    for (int t = 0; t < P.T; ++t) used = used || (P.sh[t] == s && in_group<S, K, PM, FWD>(t, g));
+    if (used) L.s[L.n++] = s;
+  }
+  return L;
+}
+
+// position of tap t in group g's visiting order
+template <int S, int K, int PM, bool FWD>
+constexpr int tap_ord(int g, int t) {
+  constexpr Pattern<S, K, PM, FWD> P{};
+  const ShiftList L = group_shifts<S, K, PM, FWD>(g);
+  int o = 0;
+  for (int i = 0; i < L.n; ++i)
+    for (int u = 0; u < P.T; ++u)
+      if (P.sh[u] == L.s[i] && in_group<S, K, PM, FWD>(u, g)) {
+        if (u == t) return o;
+        ++o;
+      }
+  return -1;
+}
+
 // Runtime geometry (host-built).
 struct FxPlan {
   int base_h, base_w;    // input row / column of phase (0, 0) shift (0, 0)
@@ -131,8 +188,12 @@ __device__ __forceinline__ uint32_t byte_of(uint32_t w, int e) { return (w >> (8
 // XF: the input is fp32 (a.xf; the fused quantize -> transposed conv) and is
 // quantized with the quantize_per_tensor formula as the halo is staged, so
 // the int8 input never goes to memory.
-template <int S, int K, int PM, bool FWD, bool XF>
-__global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPlan p) {
+// RELU: the relu-fused epilogue (lower clamp at the output zero point).
+template <int S, int K, int PM, bool FWD, bool XF, bool RELU>
+__global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs a, FxPlan p) {
+  constexpr int kThreads = threads_of<S>();
+  constexpr int kStageSlots = kStageUnits / kThreads;
+  constexpr bool SPLIT = S == 2;
   constexpr Pattern<S, K, PM, FWD> P{};
   constexpr int NPH = S * S;
   constexpr int OROWS = kTR * S;                // output rows of the tile
@@ -274,8 +335,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
     }
   }
 
-  // ---- weights: one fragment per (tap, 32 channels) ----------------------
-  const int oc = oc0 + 32 * wave + lo;
+  // ---- per wave: 32 output channels of one tap group ------------------------
+  // With stride 2 the taps split by output-row residue rh: waves 0-3 take
+  // the phases of one residue, waves 4-7 (which share the SIMDs of 0-3) the
+  // other, so one wave's requantize (vector ALU) runs beside the other's
+  // products (matrix cores).  A wave owns whole output rows: it requantizes
+  // them into LDS and copies them out itself.
+  constexpr int NF = 2 * kTR;                   // pixel fragments: kTR rows x 2 column halves
+  constexpr int NG = SPLIT ? S : 1;             // phases per group
+  const int og = wave & 3;                      // 32-channel block
+  const int oc = oc0 + 32 * og + lo;
   const int occ = oc < OC ? oc : OC - 1;    // rows past OC read row OC - 1 (never stored)
   const int8_t* wrow = a.w + (int64_t)occ * a.ldw + 16 * hi;
   const int Kw = __builtin_amdgcn_readfirstlane((int)a.Kw);
@@ -283,83 +352,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
   auto wfrag = [&](int t, int off) {
     return *reinterpret_cast<const v4i*>(wrow + ((P.kh[t] * Kw + P.kw[t]) * IC + off));
   };
-
-  constexpr int NF = 2 * kTR;   // pixel fragments: kTR rows x 2 column halves
-  v16i acc[NPH][NF];
-  int32_t wsum[NPH];
-#pragma unroll
-  for (int ph = 0; ph < NPH; ++ph) {
-    wsum[ph] = 0;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) acc[ph][f] = v16i{};
-  }
-
-  // weight fragments of one step; tap t's register is refilled with the next
-  // step's fragment right after its last product.  The 32-channel steps run
-  // in a rotated order, a different rotation for neighbouring workgroups of
-  // one XCD: all workgroups start together and would otherwise request the
-  // same weight lines from L2 at the same moment (the integer sums do not
-  // depend on the order).
-  const int nk = IC / 32;
+  const int nk = IC / 32;   // even: IC % 64 == 0
+  // The 32-channel steps run in a rotated order, a different rotation for
+  // neighbouring workgroups of one XCD: all workgroups start together and
+  // would otherwise request the same weight lines from L2 at the same moment
+  // (the integer sums do not depend on the order).
   const int rot = (int)(blockIdx.x >> 3) % nk;
   auto kidx = [&](int k) { return k + rot < nk ? k + rot : k + rot - nk; };
-  v4i bw[P.T];
-#pragma unroll
-  for (int t = 0; t < P.T; ++t) bw[t] = wfrag(t, 32 * kidx(0));
-  __syncthreads();
 
-  // A fragments of shift s, step k
-  auto aload = [&](v4i (&dst)[NF], int s_dh, int s_dw, int k) {
-    const int q = 2 * k + hi;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int r = (f >> 1) + s_dh - P.dhmin;
-      const int cidx = (f & 1) * 32 + lo + s_dw - P.dwmin + p.coff;
-      dst[f] = xs[(r * NQ + q) * HC + pos(cidx)];
-    }
-  };
-  v4i acur[NF], anext[NF];
-  aload(acur, P.sdh[0], P.sdw[0], kidx(0));
-  auto step = [&](int k, v4i (&cur)[P.T]) {
-    const int kc = kidx(k);
-    const int knext = k + 1 < nk ? kidx(k + 1) : kc;   // past the end: re-read (unused)
-    Static<0, P.NS>::each([&](auto SI) {
-      constexpr int s = decltype(SI)::value;
-      // the next shift's (or the next step's first shift's) fragments first
-      if constexpr (s + 1 < P.NS) aload(anext, P.sdh[s + 1], P.sdw[s + 1], kc);
-      else aload(anext, P.sdh[0], P.sdw[0], knext);
-      Static<0, P.T>::each([&](auto TI) {
-        constexpr int t = decltype(TI)::value;
-        if constexpr (P.sh[t] == s) {
-          constexpr int ph = P.ph[t];
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            acc[ph][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[f], cur[t], acc[ph][f], 0, 0, 0);
-          int32_t w4 = __builtin_amdgcn_sdot4(cur[t][0], 0x01010101, 0, false);
-          w4 = __builtin_amdgcn_sdot4(cur[t][1], 0x01010101, w4, false);
-          w4 = __builtin_amdgcn_sdot4(cur[t][2], 0x01010101, w4, false);
-          w4 = __builtin_amdgcn_sdot4(cur[t][3], 0x01010101, w4, false);
-          wsum[ph] += w4;
-          cur[t] = wfrag(t, 32 * knext);
-          // keep the refill here: left to itself the compiler sinks every
-          // refill to the end of the step, and the next step then starts
-          // with a wait for all of them
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      });
-#pragma unroll
-      for (int f = 0; f < NF; ++f) acur[f] = anext[f];
-    });
-  };
-  for (int k = 0; k < nk; ++k) step(k, bw);
-
-  // ---- epilogue: requantize into the LDS output block ----------------------
-  // lanes l and l + 32 hold the two 16-channel halves of each weight
-  // fragment; zw = input zero point x the phase's weight sum, once per phase
-  int32_t zw[NPH];
-#pragma unroll
-  for (int ph = 0; ph < NPH; ++ph) zw[ph] = a.izp * (wsum[ph] + __shfl_xor(wsum[ph], 32, 64));
-  const int ocl = 32 * wave + lo;
+  const int ocl = 32 * og + lo;
   const bool oc_ok = oc < OC;
   float sc = 0.0f, bi = 0.0f;
   if (oc_ok && !a.acc) {
@@ -367,84 +368,174 @@ __global__ __launch_bounds__(kThreads, 1) void k_deconv_fixed(DeconvArgs a, FxPl
     bi = a.bias ? a.bias[oc] : 0.0f;
   }
   const int H_out = (int)a.H_out, W_out = (int)a.W_out;
-  if (a.acc) {
-    // accumulator output (verification entry point): direct int32 stores
-    if (oc_ok) {
-      Static<0, NPH>::each([&](auto PI) {
-        constexpr int ph = decltype(PI)::value;
-        constexpr int rh = ph / S, rw = ph % S;
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ii = i0 + (f >> 1);
-            const int j = j0 + (f & 1) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const int oh = S * ii + rh, ow = S * j + rw;
-            if (oh < H_out && ow < W_out)
-              a.acc[(((int64_t)n * OC + oc) * H_out + oh) * W_out + ow] = acc[ph][f][r] - zw[ph];
-          }
-      });
-    }
-    return;
-  }
-  // lane: 4 consecutive phase columns x S column residues = 4*S consecutive
-  // output columns of one output row per (row residue, fragment, group); the
-  // codes are packed in offset form (code + 128) by the conversion itself
   const float ozp128 = a.rq.ozp + 128.0f, qmin128 = a.rq.qmin + 128.0f;
-  auto epilogue = [&](auto relu_tag) {
-    constexpr bool RELU = decltype(relu_tag)::value;
-#pragma unroll
-    for (int rh = 0; rh < S; ++rh)
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint32_t wd[S];
-#pragma unroll
-          for (int e = 0; e < S; ++e) wd[e] = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int rw = 0; rw < S; ++rw) {
-              const int ph = rh * S + rw;
-              const int idx = S * e + rw;
-              wd[idx >> 2] = requant_u8<RELU>(acc[ph][f][4 * g + e] - zw[ph], sc, bi, a.rq, ozp128,
-                                              qmin128, idx & 3, wd[idx >> 2]);
-            }
-          const int orow = (f >> 1) * S + rh;
-          const int col = S * ((f & 1) * 32 + 8 * g + 4 * hi);
-          int8_t* d = os + (ocl * OROWS + orow) * OPITCH + col;
-          if constexpr (S == 2) {
-            typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<v2u*>(d) = v2u{wd[0] ^ 0x80808080u, wd[1] ^ 0x80808080u};
-          } else {
-            *reinterpret_cast<uint32_t*>(d) = wd[0] ^ 0x80808080u;
-          }
-        }
-  };
-  if (a.rq.qmin > -128.0f)
-    epilogue(std::true_type{});
-  else
-    epilogue(std::false_type{});
-  __syncthreads();
-
-  // ---- copy the output block out: 16-byte pieces, whole rows ---------------
   constexpr int PIECES = OCOLS / 16;
   const int oh0 = S * i0, ow0 = S * j0;
-  for (int u = tid; u < kOCB * OROWS * PIECES; u += kThreads) {
-    const int pc = u % PIECES;
-    const int rr = u / PIECES;
-    const int orow = rr % OROWS;
-    const int ocq = rr / OROWS;
-    const int occ2 = oc0 + ocq, oh = oh0 + orow, ow = ow0 + 16 * pc;
-    if (occ2 >= OC || oh >= H_out || ow >= W_out) continue;
-    const int8_t* s_ = os + (ocq * OROWS + orow) * OPITCH + 16 * pc;
-    int8_t* g_ = a.out + (((int64_t)n * OC + occ2) * H_out + oh) * W_out + ow;
-    if (p.out_vec && ow + 16 <= W_out) {
-      *reinterpret_cast<v4i*>(g_) = *reinterpret_cast<const v4i*>(s_);
-    } else {
-      for (int e = 0; e < 16 && ow + e < W_out; ++e) g_[e] = s_[e];
+
+  auto run = [&](auto gtag) {
+    constexpr int G = decltype(gtag)::value;        // row residue of the group, -1: every tap
+    constexpr int RH = G < 0 ? 0 : G;
+    constexpr ShiftList L = group_shifts<S, K, PM, FWD>(G);
+    // Each weight fragment is requested two steps ahead, into two
+    // alternating register sets (with one set the compiler's wait counts at
+    // the loop head leave about half a step of cover).
+    constexpr bool TWO = SPLIT && group_taps<S, K, PM, FWD>(G) <= 6;
+    v16i acc[NG][NF];
+    int32_t wsum[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      wsum[g] = 0;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[g][f] = v16i{};
     }
+    // first fragments, in the order the loop refills them (set 0, then set
+    // 1, each shift by shift): the compiler's wait counts at the loop head
+    // are then those of the steady state
+    v4i bw[P.T], bw1[P.T];
+    Static<0, TWO ? 2 : 1>::each([&](auto RI) {
+      constexpr int set = decltype(RI)::value;
+      Static<0, L.n>::each([&](auto SI) {
+        constexpr int s = L.s[decltype(SI)::value];
+        Static<0, P.T>::each([&](auto TI) {
+          constexpr int t = decltype(TI)::value;
+          if constexpr (P.sh[t] == s && in_group<S, K, PM, FWD>(t, G)) {
+            if constexpr (set == 0) bw[t] = wfrag(t, 32 * kidx(0));
+            else bw1[t] = wfrag(t, 32 * kidx(1));
+          }
+        });
+      });
+    });
+    __syncthreads();   // the halo is staged
+
+    // A fragments of input shift (s_dh, s_dw), step k
+    auto aload = [&](v4i (&dst)[NF], int s_dh, int s_dw, int k) {
+      const int q = 2 * k + hi;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int r = (f >> 1) + s_dh - P.dhmin;
+        const int cidx = (f & 1) * 32 + lo + s_dw - P.dwmin + p.coff;
+        dst[f] = xs[(r * NQ + q) * HC + pos(cidx)];
+      }
+    };
+    v4i acur[NF], anext[NF];
+    // Step k: the products of the group's taps, shift by shift (the next
+    // shift's fragments requested before the current shift's products;
+    // after the last shift, the first shift of step k + 1).  Tap t's register
+    // is refilled with step kref's fragment right after its products.
+    auto step = [&](int k, int kref, v4i (&cur)[P.T]) {
+      const int kc = kidx(k);
+      const int kr = kidx(kref);
+      const int knext = k + 1 < nk ? kidx(k + 1) : kc;   // past the end: re-read (unused)
+      Static<0, L.n>::each([&](auto SI) {
+        constexpr int si = decltype(SI)::value;
+        constexpr int s = L.s[si];
+        if constexpr (si + 1 < L.n) aload(anext, P.sdh[L.s[si + 1]], P.sdw[L.s[si + 1]], kc);
+        else aload(anext, P.sdh[L.s[0]], P.sdw[L.s[0]], knext);
+        Static<0, P.T>::each([&](auto TI) {
+          constexpr int t = decltype(TI)::value;
+          if constexpr (P.sh[t] == s && in_group<S, K, PM, FWD>(t, G)) {
+            constexpr int g = P.ph[t] % NG;
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+              acc[g][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(acur[f], cur[t], acc[g][f], 0, 0, 0);
+            int32_t w4 = __builtin_amdgcn_sdot4(cur[t][0], 0x01010101, 0, false);
+            w4 = __builtin_amdgcn_sdot4(cur[t][1], 0x01010101, w4, false);
+            w4 = __builtin_amdgcn_sdot4(cur[t][2], 0x01010101, w4, false);
+            w4 = __builtin_amdgcn_sdot4(cur[t][3], 0x01010101, w4, false);
+            wsum[g] += w4;
+            cur[t] = wfrag(t, 32 * kr);
+            // keep the refill here: left to itself the compiler sinks every
+            // refill to the end of the step, and the next step then starts
+            // with a wait for all of them
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acur[f] = anext[f];
+      });
+    };
+    aload(acur, P.sdh[L.s[0]], P.sdw[L.s[0]], kidx(0));
+    if constexpr (TWO) {
+      for (int k = 0; k < nk; k += 2) {
+        step(k, k + 2 < nk ? k + 2 : k, bw);
+        step(k + 1, k + 3 < nk ? k + 3 : k + 1, bw1);
+      }
+    } else {
+      for (int k = 0; k < nk; ++k) step(k, k + 1 < nk ? k + 1 : k, bw);
+    }
+    // zw = input zero point x the phase's weight sum (lanes l and l + 32 hold
+    // the two 16-channel halves of each weight fragment)
+    int32_t zw[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) zw[g] = a.izp * (wsum[g] + __shfl_xor(wsum[g], 32, 64));
+
+    if (a.acc) {
+      // accumulator output (verification entry point): direct int32 stores
+      if (oc_ok) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int ii = i0 + (f >> 1);
+              const int j = j0 + (f & 1) * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              const int oh = S * ii + RH, ow = S * j + g;
+              if (oh < H_out && ow < W_out)
+                a.acc[(((int64_t)n * OC + oc) * H_out + oh) * W_out + ow] = acc[g][f][r] - zw[g];
+            }
+      }
+      return;
+    }
+    // Requantize the group's rows into LDS.  Word (f, gr, h): 4 codes of one
+    // output row, packed in offset form (code + 128) by the conversion
+    // itself: fragment f, register group gr, and with S == 2 phase columns
+    // e = 2h, 2h + 1 at both column residues.
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int gr = 0; gr < 4; ++gr)
+#pragma unroll
+        for (int h = 0; h < S; ++h) {
+          uint32_t wd = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int e = S == 2 ? 2 * h + (b >> 1) : b;
+            const int g = S == 2 ? (b & 1) : 0;
+            wd = requant_u8<RELU>(acc[g][f][4 * gr + e] - zw[g], sc, bi, a.rq, ozp128, qmin128, b,
+                                  wd);
+          }
+          const int orow = (f >> 1) * S + RH;
+          const int col = S * ((f & 1) * 32 + 8 * gr + 4 * hi) + 4 * h;
+          *reinterpret_cast<uint32_t*>(os + (ocl * OROWS + orow) * OPITCH + col) =
+              wd ^ 0x80808080u;
+        }
+    // The wave reads back only rows it wrote: its LDS operations run in
+    // order, so no workgroup barrier is needed.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // copy the wave's rows out: 16-byte pieces of whole rows
+    for (int u = lane; u < 32 * kTR * PIECES; u += 64) {
+      const int pc = u % PIECES;
+      const int rr = u / PIECES;
+      const int orow = (rr % kTR) * S + RH;
+      const int ocq = 32 * og + rr / kTR;
+      const int occ2 = oc0 + ocq, oh = oh0 + orow, ow = ow0 + 16 * pc;
+      if (occ2 >= OC || oh >= H_out || ow >= W_out) continue;
+      const int8_t* s_ = os + (ocq * OROWS + orow) * OPITCH + 16 * pc;
+      int8_t* g_ = a.out + (((int64_t)n * OC + occ2) * H_out + oh) * W_out + ow;
+      if (p.out_vec && ow + 16 <= W_out) {
+        *reinterpret_cast<v4i*>(g_) = *reinterpret_cast<const v4i*>(s_);
+      } else {
+        for (int e = 0; e < 16 && ow + e < W_out; ++e) g_[e] = s_[e];
+      }
+    }
+  };
+  if constexpr (SPLIT) {
+    if (wave < 4) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, -1>{});
   }
 }
 
@@ -459,7 +550,7 @@ bool plan_t(const DeconvArgs& a, FxPlan& p, size_t& lds) {
   p.HR = P.dhmax - P.dhmin + kTR;
   p.HC = (p.coff + kTJ + P.dwmax - P.dwmin + 7) / 8 * 8;
   const int64_t NQ = a.IC / 16;
-  if (p.HR * NQ * (p.HC / 4) > (int64_t)kStageSlots * kThreads) return false;
+  if (p.HR * NQ * (p.HC / 4) > (int64_t)kStageUnits) return false;
   p.Hp = (int)((a.H_out + S - 1) / S);
   p.Wp = (int)((a.W_out + S - 1) / S);
   p.tiles_i = (p.Hp + kTR - 1) / kTR;
@@ -476,14 +567,20 @@ template <int S, int K, int PM, bool FWD, bool XF>
 hipError_t launch_x(const DeconvArgs& a, const FxPlan& p, size_t lds, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_deconv_fixed<S, K, PM, FWD, XF>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
+    for (const void* f : {(const void*)k_deconv_fixed<S, K, PM, FWD, XF, false>,
+                          (const void*)k_deconv_fixed<S, K, PM, FWD, XF, true>}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+    }
     attr = true;
   }
   const int64_t blocks = (int64_t)a.N * p.tiles_i * p.tiles_j * p.tiles_oc;
-  hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF>), dim3((unsigned)blocks), dim3(kThreads),
-                     lds, s, a, p);
+  if (a.rq.qmin > -128.0f)
+    hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF, true>), dim3((unsigned)blocks),
+                       dim3(threads_of<S>()), lds, s, a, p);
+  else
+    hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF, false>), dim3((unsigned)blocks),
+                       dim3(threads_of<S>()), lds, s, a, p);
   return hipGetLastError();
 }
 
