@@ -33,22 +33,12 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int64_t n0 = wave * ROWS;
-  // The fp32 form shares each chunk's codes through LDS and meets barriers,
-  // so there a wave past the last row stays (its loads are masked to zero
-  // and it stores nothing).
-  if (!XF && n0 >= a.N) return;
+  // No early exit: a wave past the last row reads row N - 1 and stores
+  // nothing (a branch ahead of the weight stream would put a second round of
+  // argument reads before its first load; the fp32 form also shares each
+  // chunk's codes through LDS and meets barriers).
   const int64_t K = a.K;
   __shared__ v4i xs[XF ? MR * CH * 64 : 1];
-  // The epilogue's per-channel scale and bias are fetched before the weight
-  // stream so that their latency overlaps it (lane i < ROWS holds row n0 + i).
-  float sc_pre = 0.0f, b_pre = 0.0f;
-  {
-    const int64_t n = n0 + (lane % ROWS);
-    if (lane < ROWS * MR && n < a.N && !a.acc) {
-      sc_pre = a.wscale[n];
-      b_pre = a.bias ? a.bias[n] : 0.0f;
-    }
-  }
   int32_t dot[MR][ROWS];
   int32_t sw[ROWS];
 #pragma unroll
@@ -57,7 +47,10 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) dot[m][r] = 0;
   }
-  for (int64_t k0 = 0; k0 < K; k0 += 1024 * CH) {
+  // K >= 1 (the entry points check it): the first pass runs unconditionally,
+  // so no branch sits ahead of its loads
+  int64_t k0 = 0;
+  do {
     v4i wv[ROWS][CH];
     v4i xv[MR][CH];
     int ones[CH];  // 0x01010101 where the lane's slice is inside K, else 0
@@ -115,21 +108,30 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
         for (int m = 0; m < MR; ++m) xv[m][c] = xs[(m * CH + c) * 64 + lane];
       }
     } else {
+      // every load unconditional (no branch between them): rows past N
+      // read row N - 1, slices past K read the row's first bytes; both are
+      // cancelled by zero activations and a zero ones-vector
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int64_t kk = k0 + c * 1024 + lane * 16;
         const bool ok = kk < K;
-        ones[c] = 0x01010101;
+        ones[c] = ok ? 0x01010101 : 0;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-          const bool rok = ok && (n0 + r < a.N);
-          wv[r][c] = rok ? __builtin_nontemporal_load(
-                               reinterpret_cast<const v4i*>(a.w + (n0 + r) * K + kk))
-                         : v4i{0, 0, 0, 0};
+          const int64_t n = n0 + r < a.N ? n0 + r : a.N - 1;
+          wv[r][c] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4i*>(a.w + n * K + (ok ? kk : 0)));
         }
+      }
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
-          xv[m][c] = ok ? *reinterpret_cast<const v4i*>(a.x + m * K + kk) : v4i{0, 0, 0, 0};
+      for (int c = 0; c < CH; ++c) {
+        const int64_t kk = k0 + c * 1024 + lane * 16;
+        const bool ok = kk < K;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          const v4i v = *reinterpret_cast<const v4i*>(a.x + m * K + (ok ? kk : 0));
+          xv[m][c] = ok ? v : v4i{0, 0, 0, 0};
+        }
       }
     }
 #pragma unroll
@@ -145,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
         }
       }
     }
-  }
+    k0 += 1024 * CH;
+  } while (k0 < K);
   int32_t mine = 0;
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
       if (a.acc) {
         a.acc[m * a.N + n] = mine;
       } else {
-        const int q = requant(mine, sc_pre, b_pre, a.rq);
+        const int q = requant(mine, a.wscale[n], a.bias ? a.bias[n] : 0.0f, a.rq);
         if (a.outf)
           a.outf[m * a.N + n] = dequant1(q, a.dq_zp, a.dq_scale);
         else

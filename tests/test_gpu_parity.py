@@ -248,10 +248,12 @@ def test_linear_w8_edges(M, K, N):
         np.testing.assert_array_equal(host(outf).view(np.uint32), dq.view(np.uint32))
 
 
-@pytest.mark.parametrize("M,K", [(1, 2048), (3, 4096), (1, 5136), (4, 48), (2, 16)])
+@pytest.mark.parametrize("M,K", [(1, 2048), (3, 4096), (1, 5136), (4, 48), (2, 16), (1, 4112),
+                                 (1, 11008)])
 def test_gemv_k_slices(M, K):
-    """The skinny GEMM (M <= 4); K spans partial 1 KiB slices and several
-    passes."""
+    """The skinny GEMM (M <= 4) and, for M == 1 from K = 2048, the kernel in
+    which a workgroup owns 8 weight rows; K spans partial slices and several
+    passes, N = 1001 leaves a partly filled last row group."""
     _say(f"gemv M={M} K={K}")
     c = qi.linear_case(78 + M + K, M, K, 1001)
     np.testing.assert_array_equal(_run_linear(c), _oracle_linear(c))
