@@ -170,6 +170,21 @@ constexpr int tap_ord(int g, int t) {
   return -1;
 }
 
+// The output block in LDS: row (channel o, output row) at OPITCH bytes.
+// With stride 2 the 16-byte chunk c of a row sits at slot c ^ out_swz(o) and
+// its two 8-byte halves are exchanged when bit 4 of o is set: then the
+// requantize's 64-bit stores (32 channels of one row position per cycle) and
+// the copy-out's 16-byte reads (two channels' rows per cycle) each cover all
+// 64 LDS banks once.
+template <int S>
+constexpr int out_pitch() { return S == 2 ? 160 : kTJ * S + 16; }
+template <int S>
+__device__ __forceinline__ int out_swz(int o) {
+  return S == 2 ? (((o >> 2) & 1) | (((o >> 3) & 1) << 1) | (((o >> 1) & 1) << 2)) : 0;
+}
+template <int S>
+__device__ __forceinline__ int out_half(int o) { return S == 2 ? ((o >> 4) & 1) : 0; }
+
 // Runtime geometry (host-built).
 struct FxPlan {
   int base_h, base_w;    // input row / column of phase (0, 0) shift (0, 0)
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
   constexpr int NPH = S * S;
   constexpr int OROWS = kTR * S;                // output rows of the tile
   constexpr int OCOLS = kTJ * S;                // output columns of the tile
-  constexpr int OPITCH = OCOLS + 16;            // LDS bytes per (channel, row) of the output copy
+  constexpr int OPITCH = out_pitch<S>();        // LDS bytes per (channel, row) of the output copy
 
   extern __shared__ __attribute__((aligned(16))) v4i smem[];
   const int HR = p.HR, HC = p.HC;
@@ -264,9 +279,16 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
         chunk[2][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x05040100u);
         chunk[3][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x07060302u);
       }
+      // lanes 4 apart start at different chunks, so that the 16 lanes of one
+      // store cycle (consecutive units, 64 bytes apart) cover all banks
       v4i* dst = xs + (r * NQ + q) * HC;
+      const int rsh = (threadIdx.x >> 2) & 3;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[pos(4 * cg + e)] = chunk[e];
+      for (int j = 0; j < 4; ++j) {
+        const int e = (j + rsh) & 3;
+        const v4i v = e == 0 ? chunk[0] : e == 1 ? chunk[1] : e == 2 ? chunk[2] : chunk[3];
+        dst[pos(4 * cg + e)] = v;
+      }
     };
     if constexpr (!XF) {
       const int8_t* xn = a.x + (int64_t)n * IC * plane;
@@ -491,43 +513,55 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
     // output row, packed in offset form (code + 128) by the conversion
     // itself: fragment f, register group gr, and with S == 2 phase columns
     // e = 2h, 2h + 1 at both column residues.
+    // With S == 2 the two words of (f, gr) are one 8-byte store: half hi of
+    // chunk 4 (f & 1) + gr.
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    const int swz = out_swz<S>(ocl), hsw = out_half<S>(ocl);
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int gr = 0; gr < 4; ++gr)
+      for (int gr = 0; gr < 4; ++gr) {
+        uint32_t wd[S];
 #pragma unroll
         for (int h = 0; h < S; ++h) {
-          uint32_t wd = 0;
+          wd[h] = 0;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int e = S == 2 ? 2 * h + (b >> 1) : b;
             const int g = S == 2 ? (b & 1) : 0;
-            wd = requant_u8<RELU>(acc[g][f][4 * gr + e] - zw[g], sc, bi, a.rq, ozp128, qmin128, b,
-                                  wd);
+            wd[h] = requant_u8<RELU>(acc[g][f][4 * gr + e] - zw[g], sc, bi, a.rq, ozp128, qmin128,
+                                     b, wd[h]);
           }
-          const int orow = (f >> 1) * S + RH;
-          const int col = S * ((f & 1) * 32 + 8 * gr + 4 * hi) + 4 * h;
-          *reinterpret_cast<uint32_t*>(os + (ocl * OROWS + orow) * OPITCH + col) =
-              wd ^ 0x80808080u;
+          wd[h] ^= 0x80808080u;
         }
+        int8_t* rowp = os + (ocl * OROWS + (f >> 1) * S + RH) * OPITCH;
+        if constexpr (S == 2) {
+          *reinterpret_cast<v2u*>(rowp + 16 * ((4 * (f & 1) + gr) ^ swz) + 8 * (hi ^ hsw)) =
+              v2u{wd[0], wd[1]};
+        } else {
+          *reinterpret_cast<uint32_t*>(rowp + (f & 1) * 32 + 8 * gr + 4 * hi) = wd[0];
+        }
+      }
     // The wave reads back only rows it wrote: its LDS operations run in
     // order, so no workgroup barrier is needed.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    // copy the wave's rows out: 16-byte pieces of whole rows
+    // copy the wave's rows out: 16-byte pieces of whole rows (piece, then
+    // channel, then row)
     for (int u = lane; u < 32 * kTR * PIECES; u += 64) {
       const int pc = u % PIECES;
-      const int rr = u / PIECES;
-      const int orow = (rr % kTR) * S + RH;
-      const int ocq = 32 * og + rr / kTR;
+      const int ocq = 32 * og + (u / PIECES) % 32;
+      const int orow = (u / (PIECES * 32)) * S + RH;
       const int occ2 = oc0 + ocq, oh = oh0 + orow, ow = ow0 + 16 * pc;
       if (occ2 >= OC || oh >= H_out || ow >= W_out) continue;
-      const int8_t* s_ = os + (ocq * OROWS + orow) * OPITCH + 16 * pc;
+      v4i v = *reinterpret_cast<const v4i*>(os + (ocq * OROWS + orow) * OPITCH +
+                                            16 * (pc ^ out_swz<S>(ocq)));
+      if (out_half<S>(ocq)) v = v4i{v[2], v[3], v[0], v[1]};
       int8_t* g_ = a.out + (((int64_t)n * OC + occ2) * H_out + oh) * W_out + ow;
       if (p.out_vec && ow + 16 <= W_out) {
-        *reinterpret_cast<v4i*>(g_) = *reinterpret_cast<const v4i*>(s_);
+        *reinterpret_cast<v4i*>(g_) = v;
       } else {
-        for (int e = 0; e < 16 && ow + e < W_out; ++e) g_[e] = s_[e];
+        for (int e = 0; e < 16 && ow + e < W_out; ++e) g_[e] = (int8_t)(v[e >> 2] >> (8 * (e & 3)));
       }
     }
   };
@@ -559,7 +593,7 @@ bool plan_t(const DeconvArgs& a, FxPlan& p, size_t& lds) {
   p.out_vec = (a.W_out % 16 == 0) && (((uintptr_t)a.out & 15) == 0);
   const int64_t blocks = (int64_t)a.N * p.tiles_i * p.tiles_j * p.tiles_oc;
   p.xcd = blocks % 8 == 0;
-  lds = (size_t)p.HR * NQ * p.HC * 16 + (size_t)kOCB * kTR * S * (kTJ * S + 16);
+  lds = (size_t)p.HR * NQ * p.HC * 16 + (size_t)kOCB * kTR * S * out_pitch<S>();
   return blocks < ((int64_t)1 << 31) && lds <= 160 * 1024;
 }
 
