@@ -279,16 +279,9 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
         chunk[2][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x05040100u);
         chunk[3][g] = (int)__builtin_amdgcn_perm(t3, t1, 0x07060302u);
       }
-      // lanes 4 apart start at different chunks, so that the 16 lanes of one
-      // store cycle (consecutive units, 64 bytes apart) cover all banks
       v4i* dst = xs + (r * NQ + q) * HC;
-      const int rsh = (threadIdx.x >> 2) & 3;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = (j + rsh) & 3;
-        const v4i v = e == 0 ? chunk[0] : e == 1 ? chunk[1] : e == 2 ? chunk[2] : chunk[3];
-        dst[pos(4 * cg + e)] = v;
-      }
+      for (int e = 0; e < 4; ++e) dst[pos(4 * cg + e)] = chunk[e];
     };
     if constexpr (!XF) {
       const int8_t* xn = a.x + (int64_t)n * IC * plane;
