@@ -688,7 +688,33 @@ def run_extra(args, torch, np, q8, qi, lib, stream, timer, check, c, x, w, ws, b
     dfns[-1]()
     torch.cuda.synchronize()
     cap["deconv_large"] = (d, dout.cpu().numpy())
-    del dfns, qs
+    # the same calls on a prepacked weight (packed once, outside the timed region)
+    Nb, ICb, Hb, Wb = d.x_fp32.shape
+    OCb = d.w.shape[0]
+    wdev = torch.from_numpy(d.w).cuda()
+    sdev = torch.from_numpy(d.weight_scales).cuda()
+    bdev = torch.from_numpy(d.bias).cuda()
+    pk = torch.empty(lib.q8ta_conv2d_transposed_weight_prepacked_bytes(OCb, ICb, d.Kh, d.Kw),
+                     dtype=torch.int8, device="cuda")
+
+    def prepack():
+        check(lib.q8ta_conv2d_transposed_weight_prepack(wdev.data_ptr(), OCb, ICb, d.Kh, d.Kw,
+                                                        d.w.shape[1], pk.data_ptr(), stream))
+    prepack()
+    pout = torch.empty_like(dout)
+    pfns = [(lambda i=i: check(lib.q8ta_conv2d_transposed_prepacked(
+        qs[i].data_ptr(), Nb, ICb, Hb, Wb, d.in_scale, d.in_zp, pk.data_ptr(), OCb, d.Kh, d.Kw,
+        None, sdev.data_ptr(), bdev.data_ptr(), d.out_scale, d.out_zp, d.stride[0], d.stride[1],
+        d.padding[0], d.padding[1], d.output_padding[0], d.output_padding[1], 1, 1, 1, b"none",
+        pout.data_ptr(), d.H_out, d.W_out, stream))) for i in range(copies)]
+    r = summary(timed(pfns, 4 * copies), dops, "TOPS", PEAK_INT8_TOPS)
+    r["weight_prepack_us"] = dist_us(*timed([prepack], 20))["median_us"]
+    pfns[-1]()
+    torch.cuda.synchronize()
+    r["output_equal_to_plain_call"] = bool(torch.equal(pout, dout))
+    r["note"] = "q8ta_conv2d_transposed_prepacked: weight rearranged once into 1 KiB fragments"
+    res["deconv_prepacked_8x256x64x64_k3s2p1_to_8x128x128x128"] = r
+    del dfns, qs, pfns, pk, pout
     # quantize -> transposed conv as one call
     ffns = []
     for i in range(copies):

@@ -340,8 +340,10 @@ q8ta_status q8ta_linear_dq_prepacked(const int8_t* x, int64_t M, int64_t K,
  * channels g*(IC/groups) + icg, with weight[oc, (kh*Kw + kw)*(IC/groups) + icg]
  * (weight_row_stride >= Kh*Kw*IC/groups) -- the page's reshape of the
  * original [IC, OC, Kh, Kw] weight applied to each group's block.
- * Kernels: groups 1 take the implicit GEMM or the tiled direct kernel;
- * grouped shapes take a one-output-per-thread kernel.
+ * Kernels: the 3x3 / 4x4 stride-2 shapes with at least 256 tiles take a
+ * compile-time-pattern matrix-core kernel; other groups-1 shapes a tiled
+ * matrix-core kernel, an implicit GEMM or a tiled direct kernel; grouped
+ * shapes a one-output-per-thread kernel.
  */
 q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
                                    int64_t H_in, int64_t W_in,
@@ -359,6 +361,58 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
                                    int64_t groups, const char* activation,
                                    int8_t* out, int64_t H_out, int64_t W_out,
                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Prepacked transposed-conv weight (opt-in; the prepacked-layout half of the
+ * weight preparation [DCV] Constraints (1) leaves to the caller, as for the
+ * GEMM above).  A weight reused across calls is rearranged once so that every
+ * matrix-core operand fragment the compile-time-pattern kernel reads is one
+ * contiguous KiB:
+ *   packed layout: byte 16*l + j of fragment (ob, kh, kw, kc) is
+ *     weight[32*ob + l % 32][(kh*Kw + kw)*IC + 32*kc + 16*(l / 32) + j]
+ *     (l = 0..63, j = 0..15), zero for rows past OC; the fragment starts at
+ *     byte (((ob*Kh + kh)*Kw + kw)*(IC/32) + kc) * 1024.
+ *   q8ta_conv2d_transposed_weight_prepacked_bytes: size of that buffer,
+ *     ceil(OC/32)*32 * Kh*Kw*IC bytes; -1 for sizes < 1, IC % 64 != 0 or sizes
+ *     past 2^40 elements.  Host-only, no HIP call.
+ *   q8ta_conv2d_transposed_weight_prepack: weight int8 [OC, weight_row_stride]
+ *     (as for q8ta_conv2d_transposed) -> packed (device, caller-allocated,
+ *     q8ta_conv2d_transposed_weight_prepacked_bytes(OC, IC, Kh, Kw) bytes).
+ *     Needs IC % 64 == 0, weight_row_stride % 16 == 0 and 16-byte aligned
+ *     weight and packed (else Q8TA_ERR_UNSUPPORTED).
+ *   q8ta_conv2d_transposed_prepacked: q8ta_conv2d_transposed with
+ *     packed_weight in place of weight and no weight_row_stride.  Takes only
+ *     the shapes of the compile-time-pattern kernel: Kh == Kw in {3, 4},
+ *     stride 2 x 2, pad_h % 2 == pad_w % 2, groups 1, dilation 1,
+ *     IC % 64 == 0 with the input halo of a tile within LDS (IC <= 256),
+ *     W_in % 4 == 0, 4-byte aligned x, 16-byte aligned packed_weight; other
+ *     shapes return Q8TA_ERR_UNSUPPORTED (use q8ta_conv2d_transposed).  The
+ *     results are bit-identical to q8ta_conv2d_transposed on the unpacked
+ *     weight.  Other arguments and errors as for q8ta_conv2d_transposed.
+ */
+int64_t q8ta_conv2d_transposed_weight_prepacked_bytes(int64_t OC, int64_t IC, int64_t Kh,
+                                                      int64_t Kw);
+
+q8ta_status q8ta_conv2d_transposed_weight_prepack(const int8_t* weight, int64_t OC, int64_t IC,
+                                                  int64_t Kh, int64_t Kw,
+                                                  int64_t weight_row_stride, int8_t* packed,
+                                                  hipStream_t stream);
+
+q8ta_status q8ta_conv2d_transposed_prepacked(const int8_t* x, int64_t N, int64_t IC,
+                                             int64_t H_in, int64_t W_in,
+                                             double input_scale, int64_t input_zero_point,
+                                             const int8_t* packed_weight, int64_t OC,
+                                             int64_t Kh, int64_t Kw,
+                                             const int32_t* weight_sums,
+                                             const float* weight_scales, const float* bias,
+                                             double output_scale, int64_t output_zero_point,
+                                             int64_t stride_h, int64_t stride_w,
+                                             int64_t pad_h, int64_t pad_w,
+                                             int64_t output_padding_h, int64_t output_padding_w,
+                                             int64_t dilation_h, int64_t dilation_w,
+                                             int64_t groups, const char* activation,
+                                             int8_t* out, int64_t H_out, int64_t W_out,
+                                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * quantize_per_tensor followed by q8ta_conv2d_transposed, in one call (the

@@ -67,6 +67,13 @@ SIGNATURES = {
     "q8ta_linear_dq_presummed": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64,
                                   _S, _P, _P], ctypes.c_int),
     "q8ta_weight_prepacked_bytes": ([_I64, _I64], ctypes.c_int64),
+    "q8ta_conv2d_transposed_weight_prepacked_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_int64),
+    "q8ta_conv2d_transposed_weight_prepack": ([_P, _I64, _I64, _I64, _I64, _I64, _P, _P],
+                                              ctypes.c_int),
+    "q8ta_conv2d_transposed_prepacked": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64, _I64,
+                                          _I64, _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64,
+                                          _I64, _I64, _I64, _I64, _I64, _S, _P, _I64, _I64, _P],
+                                         ctypes.c_int),
     "q8ta_weight_prepack": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "q8ta_linear_prepacked": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
                                _P, _P], ctypes.c_int),
@@ -404,6 +411,53 @@ def q8ta_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw, wei
     return out
 
 
+def q8ta_conv2d_transposed_weight_prepacked_bytes(OC: int, IC: int, Kh: int, Kw: int) -> int:
+    """Size in bytes of the prepacked transposed-conv weight (-1 if unsupported)."""
+    return int(lib().q8ta_conv2d_transposed_weight_prepacked_bytes(int(OC), int(IC), int(Kh),
+                                                                   int(Kw)))
+
+
+def q8ta_conv2d_transposed_weight_prepack(weight, IC, Kh, Kw, packed, stream=None):
+    """Rearrange the int8 [OC, ldw] transposed-conv weight into its fragment
+    layout (packed: int8 device tensor of the prepacked size)."""
+    torch = _torch()
+    if weight.dim() != 2:
+        raise ValueError("weight [OC, ldw] expected")
+    OC, ldw = weight.shape
+    nb = q8ta_conv2d_transposed_weight_prepacked_bytes(OC, IC, Kh, Kw)
+    if packed.numel() != nb:
+        raise ValueError(f"packed must hold {nb} bytes")
+    _check(lib().q8ta_conv2d_transposed_weight_prepack(
+        _dev(weight, torch.int8, "weight"), OC, int(IC), int(Kh), int(Kw), ldw,
+        _dev(packed, torch.int8, "packed"), _stream(stream)))
+    return packed
+
+
+def q8ta_conv2d_transposed_prepacked(x, input_scale, input_zero_point, packed, OC, Kh, Kw,
+                                     weight_sums, weight_scales, bias, output_scale,
+                                     output_zero_point, stride, padding, output_padding, dilation,
+                                     groups, activation, out, stream=None):
+    """q8ta_conv2d_transposed on a prepacked weight (H_out, W_out taken from out)."""
+    torch = _torch()
+    if x.dim() != 4 or out.dim() != 4:
+        raise ValueError("x [N,IC,H,W] and out [N,OC,H_out,W_out] expected")
+    N, IC, H_in, W_in = x.shape
+    if out.shape[0] != N or out.shape[1] != OC:
+        raise ValueError("out must be [N, OC, H_out, W_out]")
+    if packed.numel() != q8ta_conv2d_transposed_weight_prepacked_bytes(OC, IC, Kh, Kw):
+        raise ValueError("packed does not hold an [OC, Kh*Kw*IC] prepacked weight")
+    _check(lib().q8ta_conv2d_transposed_prepacked(
+        _dev(x, torch.int8, "x"), N, IC, H_in, W_in, float(input_scale), int(input_zero_point),
+        _dev(packed, torch.int8, "packed"), int(OC), int(Kh), int(Kw),
+        _opt(weight_sums, torch.int32, "weight_sums"),
+        _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
+        float(output_scale), int(output_zero_point), int(stride[0]), int(stride[1]),
+        int(padding[0]), int(padding[1]), int(output_padding[0]), int(output_padding[1]),
+        int(dilation[0]), int(dilation[1]), int(groups), _act(activation),
+        _dev(out, torch.int8, "out"), out.shape[2], out.shape[3], _stream(stream)))
+    return out
+
+
 def q8ta_quantize_conv2d_transposed(x, input_scale, input_zero_point, weight, Kh, Kw,
                                     weight_sums, weight_scales, bias, output_scale,
                                     output_zero_point, stride, padding, output_padding, dilation,
@@ -495,5 +549,6 @@ __all__ = [
     "q8ta_weight_prepacked_bytes", "q8ta_weight_prepack", "q8ta_linear_prepacked",
     "q8ta_linear_dq_prepacked",
     "q8ta_conv2d_transposed_acc", "q8ta_quantize_conv2d_transposed", "q8ta_conv2d",
-    "q8ta_conv2d_acc",
+    "q8ta_conv2d_acc", "q8ta_conv2d_transposed_weight_prepacked_bytes",
+    "q8ta_conv2d_transposed_weight_prepack", "q8ta_conv2d_transposed_prepacked",
 ]

@@ -204,7 +204,9 @@ __device__ __forceinline__ uint32_t byte_of(uint32_t w, int e) { return (w >> (8
 // quantized with the quantize_per_tensor formula as the halo is staged, so
 // the int8 input never goes to memory.
 // RELU: the relu-fused epilogue (lower clamp at the output zero point).
-template <int S, int K, int PM, bool FWD, bool XF, bool RELU>
+// PKW: the weight is prepacked (a.wpk): fragment (channel block ob, kh, kw,
+// 32-channel step kc) is one contiguous KiB, lane l's 16 bytes at 16 l.
+template <int S, int K, int PM, bool FWD, bool XF, bool RELU, bool PKW = false>
 __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs a, FxPlan p) {
   constexpr int kThreads = threads_of<S>();
   constexpr int kStageSlots = kStageUnits / kThreads;
@@ -363,11 +365,19 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
   const int occ = oc < OC ? oc : OC - 1;    // rows past OC read row OC - 1 (never stored)
   const int8_t* wrow = a.w + (int64_t)occ * a.ldw + 16 * hi;
   const int Kw = __builtin_amdgcn_readfirstlane((int)a.Kw);
+  const int nk = IC / 32;   // even: IC % 64 == 0
+  // prepacked: blocks past the last one (OC not a multiple of 128) read the
+  // last block (outputs never stored)
+  const int nob = (OC + 31) / 32;
+  const int ob = (oc0 >> 5) + og < nob ? (oc0 >> 5) + og : nob - 1;
+  const int8_t* wpkw = PKW ? a.wpk + (int64_t)ob * (K * K * nk * 1024) + 16 * lane : nullptr;
   // tap offsets are wave-uniform (scalar); only wrow differs between lanes
   auto wfrag = [&](int t, int off) {
-    return *reinterpret_cast<const v4i*>(wrow + ((P.kh[t] * Kw + P.kw[t]) * IC + off));
+    if constexpr (PKW)
+      return *reinterpret_cast<const v4i*>(wpkw + ((P.kh[t] * K + P.kw[t]) * nk + (off >> 5)) * 1024);
+    else
+      return *reinterpret_cast<const v4i*>(wrow + ((P.kh[t] * Kw + P.kw[t]) * IC + off));
   };
-  const int nk = IC / 32;   // even: IC % 64 == 0
   // The 32-channel steps run in a rotated order, a different rotation for
   // neighbouring workgroups of one XCD: all workgroups start together and
   // would otherwise request the same weight lines from L2 at the same moment
@@ -590,12 +600,12 @@ bool plan_t(const DeconvArgs& a, FxPlan& p, size_t& lds) {
   return blocks < ((int64_t)1 << 31) && lds <= 160 * 1024;
 }
 
-template <int S, int K, int PM, bool FWD, bool XF>
+template <int S, int K, int PM, bool FWD, bool XF, bool PKW = false>
 hipError_t launch_x(const DeconvArgs& a, const FxPlan& p, size_t lds, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    for (const void* f : {(const void*)k_deconv_fixed<S, K, PM, FWD, XF, false>,
-                          (const void*)k_deconv_fixed<S, K, PM, FWD, XF, true>}) {
+    for (const void* f : {(const void*)k_deconv_fixed<S, K, PM, FWD, XF, false, PKW>,
+                          (const void*)k_deconv_fixed<S, K, PM, FWD, XF, true, PKW>}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
     }
@@ -603,10 +613,10 @@ hipError_t launch_x(const DeconvArgs& a, const FxPlan& p, size_t lds, hipStream_
   }
   const int64_t blocks = (int64_t)a.N * p.tiles_i * p.tiles_j * p.tiles_oc;
   if (a.rq.qmin > -128.0f)
-    hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF, true>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF, true, PKW>), dim3((unsigned)blocks),
                        dim3(threads_of<S>()), lds, s, a, p);
   else
-    hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((k_deconv_fixed<S, K, PM, FWD, XF, false, PKW>), dim3((unsigned)blocks),
                        dim3(threads_of<S>()), lds, s, a, p);
   return hipGetLastError();
 }
@@ -617,6 +627,7 @@ hipError_t launch_t(const DeconvArgs& a, hipStream_t s) {
   size_t lds = 0;
   if (!plan_t<S, K, PM, FWD>(a, p, lds)) return hipErrorInvalidValue;
   if constexpr (!FWD) {
+    if (a.wpk) return launch_x<S, K, PM, FWD, false, true>(a, p, lds, s);
     if (a.xf) return launch_x<S, K, PM, FWD, true>(a, p, lds, s);
   }
   return launch_x<S, K, PM, FWD, false>(a, p, lds, s);
@@ -668,6 +679,44 @@ bool fits(const DeconvArgs& a, int k) {
 }
 
 }  // namespace
+
+namespace {
+
+// The prepacked transposed-conv weight: one 16-byte piece per thread;
+// fragment ((ob * Kh + kh) * Kw + kw) * (IC / 32) + kc, lane l: row
+// 32 ob + l % 32, bytes (kh * Kw + kw) * IC + 32 kc + 16 (l / 32) .. +15 of
+// that row; rows past OC are zero.
+__global__ __launch_bounds__(256) void k_deconv_wprepack(const int8_t* __restrict__ w, int64_t ldw,
+                                                         int OC, int IC, int taps, int64_t total,
+                                                         int8_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int nk = IC / 32;
+  const int l = (int)(t & 63);
+  const int64_t fi = t >> 6;
+  const int kc = (int)(fi % nk);
+  const int tap = (int)((fi / nk) % taps);
+  const int64_t row = 32 * (fi / ((int64_t)nk * taps)) + (l & 31);
+  v4i v = {0, 0, 0, 0};
+  if (row < OC)
+    v = *reinterpret_cast<const v4i*>(w + row * ldw + (int64_t)tap * IC + 32 * kc + 16 * (l >> 5));
+  *reinterpret_cast<v4i*>(out + 16 * t) = v;
+}
+
+}  // namespace
+
+int64_t deconv_prepacked_bytes(int64_t OC, int64_t IC, int64_t Kh, int64_t Kw) {
+  return (OC + 31) / 32 * 32 * Kh * Kw * IC;
+}
+
+hipError_t launch_deconv_wprepack(const int8_t* w, int64_t OC, int64_t IC, int64_t Kh, int64_t Kw,
+                                  int64_t ldw, int8_t* packed, hipStream_t s) {
+  const int64_t total = deconv_prepacked_bytes(OC, IC, Kh, Kw) / 16;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(k_deconv_wprepack, dim3((unsigned)blocks), dim3(256), 0, s, w, ldw, (int)OC,
+                     (int)IC, (int)(Kh * Kw), total, packed);
+  return hipGetLastError();
+}
 
 bool deconv_fixed_supported(const DeconvArgs& a) {
   const int k = pick(a, false);

@@ -38,7 +38,6 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
   // argument reads before its first load; the fp32 form also shares each
   // chunk's codes through LDS and meets barriers).
   const int64_t K = a.K;
-  __shared__ v4i xs[XF ? MR * CH * 64 : 1];
   int32_t dot[MR][ROWS];
   int32_t sw[ROWS];
 #pragma unroll
@@ -55,6 +54,8 @@ __global__ __launch_bounds__(kThreads) void k_skinny(LinearArgs a) {
     v4i xv[MR][CH];
     int ones[CH];  // 0x01010101 where the lane's slice is inside K, else 0
     if constexpr (XF) {
+      // the int8 form allocates no LDS
+      __shared__ v4i xs[MR * CH * 64];
       // The chunk's fp32 activations are loaded first (the quantize below
       // waits only for them), then the weight stream, with every load
       // unconditional: rows past N read row N - 1 (never stored), slices past

@@ -225,12 +225,21 @@ struct DeconvArgs {
   // zero point, exactly as quantize_per_tensor would.
   const float* xf = nullptr;
   float inv_in = 0.0f;
+  // Prepacked weight (the fragment layout of
+  // q8ta_conv2d_transposed_weight_prepack); set only by the prepacked entry
+  // point, which takes the compile-time-pattern kernel.
+  const int8_t* wpk = nullptr;
 };
 // The same arguments describe the forward q8ta_conv2d (stride, padding and
 // dilation of the forward index relation).
 hipError_t launch_deconv(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_conv2d(const DeconvArgs& a, hipStream_t s);
 hipError_t launch_quantize_deconv(DeconvArgs a, hipStream_t s);
+// Transposed-conv weight [OC, ldw] -> fragment layout (IC % 64 == 0, 16-byte
+// aligned weight and packed, ldw % 16 == 0); its size in bytes.
+hipError_t launch_deconv_wprepack(const int8_t* w, int64_t OC, int64_t IC, int64_t Kh, int64_t Kw,
+                                  int64_t ldw, int8_t* packed, hipStream_t s);
+int64_t deconv_prepacked_bytes(int64_t OC, int64_t IC, int64_t Kh, int64_t Kw);
 
 // Stride phases of a transposed conv, built on the host: for row residue r
 // (output rows oh = r + s_h*i) the nth[r] qualifying kernel rows thk[r][t] read

@@ -316,6 +316,52 @@ def test_prepacked_entry_points_errors():
             q8.Q8TA_ERR_QPARAM)
 
 
+def test_deconv_prepacked_size_formula():
+    """ceil(OC/32)*32 rows of Kh*Kw*IC bytes; -1 for IC % 64 != 0 or sizes < 1."""
+    l = q8.lib()
+    for OC, IC, K in [(32, 64, 3), (33, 64, 4), (128, 256, 3), (1, 128, 3), (160, 192, 4)]:
+        assert l.q8ta_conv2d_transposed_weight_prepacked_bytes(OC, IC, K, K) == \
+            -(-OC // 32) * 32 * K * K * IC
+    assert l.q8ta_conv2d_transposed_weight_prepacked_bytes(32, 48, 3, 3) == -1
+    assert l.q8ta_conv2d_transposed_weight_prepacked_bytes(0, 64, 3, 3) == -1
+    assert l.q8ta_conv2d_transposed_weight_prepacked_bytes(32, 64, 0, 3) == -1
+
+
+def test_deconv_prepacked_entry_points_errors():
+    l = q8.lib()
+    odd = ctypes.c_void_p(4096 + 8)   # not 16-byte aligned
+    pk = l.q8ta_conv2d_transposed_weight_prepack
+    _st(pk(None, 32, 64, 3, 3, 576, FAKE, None), q8.Q8TA_ERR_NULL)
+    _st(pk(FAKE, 32, 64, 3, 3, 576, None, None), q8.Q8TA_ERR_NULL)
+    _st(pk(FAKE, 0, 64, 3, 3, 576, FAKE, None), q8.Q8TA_ERR_SHAPE)
+    _st(pk(FAKE, 32, 48, 3, 3, 432, FAKE, None), q8.Q8TA_ERR_UNSUPPORTED, "IC % 64")
+    _st(pk(FAKE, 32, 64, 3, 3, 500, FAKE, None), q8.Q8TA_ERR_SHAPE, "weight_row_stride")
+    _st(pk(FAKE, 32, 64, 3, 3, 584, FAKE, None), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(pk(odd, 32, 64, 3, 3, 576, FAKE, None), q8.Q8TA_ERR_UNSUPPORTED)
+    _st(pk(FAKE, 32, 64, 3, 3, 576, odd, None), q8.Q8TA_ERR_UNSUPPORTED)
+
+    def call(**kw):
+        d = dict(x=FAKE, N=1, IC=64, H_in=32, W_in=32, s_in=0.02, izp=3, w=FAKE, OC=32, Kh=3,
+                 Kw=3, ws=None, scales=FAKE, bias=FAKE, s_out=0.54, ozp=-5, sh=2, sw=2, ph=1,
+                 pw=1, oph=1, opw=1, dh=1, dw=1, groups=1, act=b"none", out=FAKE, H_out=64,
+                 W_out=64)
+        d.update(kw)
+        return l.q8ta_conv2d_transposed_prepacked(*d.values(), None)
+
+    _st(call(x=None), q8.Q8TA_ERR_NULL)
+    _st(call(w=None), q8.Q8TA_ERR_NULL)
+    _st(call(out=None), q8.Q8TA_ERR_NULL)
+    _st(call(scales=None), q8.Q8TA_ERR_NULL)
+    _st(call(N=0), q8.Q8TA_ERR_SHAPE)
+    _st(call(izp=300), q8.Q8TA_ERR_QPARAM)
+    _st(call(act=b"gelu"), q8.Q8TA_ERR_UNSUPPORTED)
+    # shapes outside the compile-time-pattern kernel
+    for kw in (dict(Kh=5, Kw=5), dict(Kh=3, Kw=4), dict(sh=1, sw=1), dict(IC=48), dict(W_in=30),
+               dict(ph=1, pw=0), dict(groups=2), dict(dh=2, dw=2), dict(w=odd),
+               dict(x=ctypes.c_void_p(4096 + 2))):
+        _st(call(**kw), q8.Q8TA_ERR_UNSUPPORTED, "use q8ta_conv2d_transposed")
+
+
 def _gpu_present():
     try:
         import torch

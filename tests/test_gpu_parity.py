@@ -621,6 +621,65 @@ def test_quantize_deconv_fixed_parity(case, act):
     np.testing.assert_array_equal(host(out), ref)
 
 
+def _deconv_pack_reference(w, OC, IC, K):
+    """The prepacked transposed-conv weight written out from the header's
+    formula: byte 16 l + j of fragment (ob, kh, kw, kc) is
+    w[32 ob + l % 32, (kh K + kw) IC + 32 kc + 16 (l // 32) + j], zero past OC."""
+    nob, nk = -(-OC // 32), IC // 32
+    out = np.zeros((nob, K, K, nk, 64, 16), np.int8)
+    for ob in range(nob):
+        for kh in range(K):
+            for kw in range(K):
+                for kc in range(nk):
+                    for l in range(64):
+                        row = 32 * ob + l % 32
+                        if row < OC:
+                            s0 = (kh * K + kw) * IC + 32 * kc + 16 * (l // 32)
+                            out[ob, kh, kw, kc, l] = w[row, s0:s0 + 16]
+    return out.reshape(-1)
+
+
+def _deconv_prepack(c):
+    OC, IC, K = c.w.shape[0], c.x.shape[1], c.Kh
+    packed = torch.empty(q8.q8ta_conv2d_transposed_weight_prepacked_bytes(OC, IC, K, K),
+                         dtype=torch.int8, device="cuda")
+    q8.q8ta_conv2d_transposed_weight_prepack(dev(c.w), IC, K, K, packed)
+    return packed
+
+
+@pytest.mark.parametrize("case", DECONV_FIXED_CASES, ids=[str(i) for i in range(len(DECONV_FIXED_CASES))])
+@pytest.mark.parametrize("act", ["none", "relu"])
+def test_deconv_prepacked_parity(case, act):
+    """q8ta_conv2d_transposed_weight_prepack writes the header's layout, and
+    q8ta_conv2d_transposed_prepacked on it equals the oracle (padded weight
+    rows, OC not a multiple of 32 or 128, several column tiles)."""
+    N, IC, H, W, OC, K, p, op = case
+    _say(f"deconv prepacked case={case} act={act}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, K]) + 61, N, IC, H, W, OC, K, K, (2, 2), p, op,
+                       ldw=K * K * IC + 16)
+    packed = _deconv_prepack(c)
+    np.testing.assert_array_equal(host(packed), _deconv_pack_reference(c.w, OC, IC, K))
+    out = torch.empty((N, OC, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+    q8.q8ta_conv2d_transposed_prepacked(dev(c.x), c.in_scale, c.in_zp, packed, OC, K, K, None,
+                                        dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp,
+                                        c.stride, c.padding, c.output_padding, (1, 1), 1, act, out)
+    np.testing.assert_array_equal(host(out), _oracle_deconv(c, activation=act))
+
+
+def test_deconv_prepacked_large_workload_full():
+    """[8,256,64,64] -> [8,128,128,128] on the prepacked weight, every output
+    against the oracle."""
+    c, xq_ref, ref = _c5_reference()
+    _say("deconv prepacked [8,256,64,64] -> [8,128,128,128], full output")
+    packed = _deconv_prepack(c)
+    out = torch.empty((8, 128, 128, 128), dtype=torch.int8, device="cuda")
+    q8.q8ta_conv2d_transposed_prepacked(dev(xq_ref), c.in_scale, c.in_zp, packed, 128, c.Kh, c.Kw,
+                                        None, dev(c.weight_scales), dev(c.bias), c.out_scale,
+                                        c.out_zp, c.stride, c.padding, c.output_padding, (1, 1), 1,
+                                        "none", out)
+    np.testing.assert_array_equal(host(out), ref)
+
+
 CONV2D_FIXED_CASES = [
     # N, IC, H, W, OC, pad
     (2, 64, 10, 12, 40, (1, 1)),
