@@ -714,7 +714,7 @@ def run_extra(args, torch, np, q8, qi, lib, stream, timer, check, c, x, w, ws, b
     r["output_equal_to_plain_call"] = bool(torch.equal(pout, dout))
     r["note"] = "q8ta_conv2d_transposed_prepacked: weight rearranged once into 1 KiB fragments"
     res["deconv_prepacked_8x256x64x64_k3s2p1_to_8x128x128x128"] = r
-    del dfns, qs, pfns, pk, pout
+    del dfns, qs, pfns
     # quantize -> transposed conv as one call
     ffns = []
     for i in range(copies):
@@ -726,7 +726,19 @@ def run_extra(args, torch, np, q8, qi, lib, stream, timer, check, c, x, w, ws, b
     ffns[0]()
     torch.cuda.synchronize()
     cap["quantize_deconv_large"] = (d, fout.cpu().numpy())
-    del xs, ffns
+    # the fused form on the prepacked weight
+    qpfns = [(lambda i=i: check(lib.q8ta_quantize_conv2d_transposed_prepacked(
+        xs[i].data_ptr(), Nb, ICb, Hb, Wb, d.in_scale, d.in_zp, pk.data_ptr(), OCb, d.Kh, d.Kw,
+        None, sdev.data_ptr(), bdev.data_ptr(), d.out_scale, d.out_zp, d.stride[0], d.stride[1],
+        d.padding[0], d.padding[1], d.output_padding[0], d.output_padding[1], 1, 1, 1, b"none",
+        pout.data_ptr(), d.H_out, d.W_out, stream))) for i in range(copies)]
+    r = summary(timed(qpfns, 4 * copies), dops, "TOPS", PEAK_INT8_TOPS)
+    qpfns[0]()
+    torch.cuda.synchronize()
+    r["output_equal_to_fused_call"] = bool(torch.equal(pout, fout))
+    r["note"] = "one call on the prepacked weight: quantize [8,256,64,64] fp32 (cold) + conv"
+    res["quantize_deconv_fused_prepacked_8x256x64x64"] = r
+    del xs, ffns, qpfns, pk, pout
 
     # ---- dequantize [2048, 11008] (rotate 6 copies of 22.5 MB in / 90 MB out)
     log("extra: dequantize [2048,11008]")

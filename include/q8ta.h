@@ -389,6 +389,10 @@ q8ta_status q8ta_conv2d_transposed(const int8_t* x, int64_t N, int64_t IC,
  *     shapes return Q8TA_ERR_UNSUPPORTED (use q8ta_conv2d_transposed).  The
  *     results are bit-identical to q8ta_conv2d_transposed on the unpacked
  *     weight.  Other arguments and errors as for q8ta_conv2d_transposed.
+ *   q8ta_quantize_conv2d_transposed_prepacked: q8ta_quantize_conv2d_transposed
+ *     (fp32 input, quantized in the same call) on the packed weight; the same
+ *     shapes, with a 16-byte aligned x (else Q8TA_ERR_UNSUPPORTED: use
+ *     q8ta_quantize_conv2d_transposed).
  */
 int64_t q8ta_conv2d_transposed_weight_prepacked_bytes(int64_t OC, int64_t IC, int64_t Kh,
                                                       int64_t Kw);
@@ -397,6 +401,15 @@ q8ta_status q8ta_conv2d_transposed_weight_prepack(const int8_t* weight, int64_t 
                                                   int64_t Kh, int64_t Kw,
                                                   int64_t weight_row_stride, int8_t* packed,
                                                   hipStream_t stream);
+
+q8ta_status q8ta_quantize_conv2d_transposed_prepacked(
+    const float* x, int64_t N, int64_t IC, int64_t H_in, int64_t W_in, double input_scale,
+    int64_t input_zero_point, const int8_t* packed_weight, int64_t OC, int64_t Kh, int64_t Kw,
+    const int32_t* weight_sums, const float* weight_scales, const float* bias,
+    double output_scale, int64_t output_zero_point, int64_t stride_h, int64_t stride_w,
+    int64_t pad_h, int64_t pad_w, int64_t output_padding_h, int64_t output_padding_w,
+    int64_t dilation_h, int64_t dilation_w, int64_t groups, const char* activation,
+    int8_t* out, int64_t H_out, int64_t W_out, hipStream_t stream);
 
 q8ta_status q8ta_conv2d_transposed_prepacked(const int8_t* x, int64_t N, int64_t IC,
                                              int64_t H_in, int64_t W_in,

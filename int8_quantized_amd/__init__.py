@@ -74,6 +74,10 @@ SIGNATURES = {
                                           _I64, _P, _P, _P, _DBL, _I64, _I64, _I64, _I64, _I64,
                                           _I64, _I64, _I64, _I64, _I64, _S, _P, _I64, _I64, _P],
                                          ctypes.c_int),
+    "q8ta_quantize_conv2d_transposed_prepacked": ([_P, _I64, _I64, _I64, _I64, _DBL, _I64, _P, _I64,
+                                                   _I64, _I64, _P, _P, _P, _DBL, _I64, _I64, _I64,
+                                                   _I64, _I64, _I64, _I64, _I64, _I64, _I64, _S,
+                                                   _P, _I64, _I64, _P], ctypes.c_int),
     "q8ta_weight_prepack": ([_P, _I64, _I64, _P, _P], ctypes.c_int),
     "q8ta_linear_prepacked": ([_P, _I64, _I64, _DBL, _I64, _P, _I64, _P, _P, _P, _DBL, _I64, _S,
                                _P, _P], ctypes.c_int),
@@ -437,8 +441,12 @@ def q8ta_conv2d_transposed_prepacked(x, input_scale, input_zero_point, packed, O
                                      weight_sums, weight_scales, bias, output_scale,
                                      output_zero_point, stride, padding, output_padding, dilation,
                                      groups, activation, out, stream=None):
-    """q8ta_conv2d_transposed on a prepacked weight (H_out, W_out taken from out)."""
+    """q8ta_conv2d_transposed on a prepacked weight (H_out, W_out taken from out);
+    with an fp32 x, q8ta_quantize_conv2d_transposed_prepacked."""
     torch = _torch()
+    fp32 = x.dtype == torch.float32
+    fn = (lib().q8ta_quantize_conv2d_transposed_prepacked if fp32
+          else lib().q8ta_conv2d_transposed_prepacked)
     if x.dim() != 4 or out.dim() != 4:
         raise ValueError("x [N,IC,H,W] and out [N,OC,H_out,W_out] expected")
     N, IC, H_in, W_in = x.shape
@@ -446,8 +454,9 @@ def q8ta_conv2d_transposed_prepacked(x, input_scale, input_zero_point, packed, O
         raise ValueError("out must be [N, OC, H_out, W_out]")
     if packed.numel() != q8ta_conv2d_transposed_weight_prepacked_bytes(OC, IC, Kh, Kw):
         raise ValueError("packed does not hold an [OC, Kh*Kw*IC] prepacked weight")
-    _check(lib().q8ta_conv2d_transposed_prepacked(
-        _dev(x, torch.int8, "x"), N, IC, H_in, W_in, float(input_scale), int(input_zero_point),
+    _check(fn(
+        _dev(x, torch.float32 if fp32 else torch.int8, "x"), N, IC, H_in, W_in,
+        float(input_scale), int(input_zero_point),
         _dev(packed, torch.int8, "packed"), int(OC), int(Kh), int(Kw),
         _opt(weight_sums, torch.int32, "weight_sums"),
         _dev(weight_scales, torch.float32, "weight_scales"), _opt(bias, torch.float32, "bias"),
@@ -551,4 +560,5 @@ __all__ = [
     "q8ta_conv2d_transposed_acc", "q8ta_quantize_conv2d_transposed", "q8ta_conv2d",
     "q8ta_conv2d_acc", "q8ta_conv2d_transposed_weight_prepacked_bytes",
     "q8ta_conv2d_transposed_weight_prepack", "q8ta_conv2d_transposed_prepacked",
+    "q8ta_quantize_conv2d_transposed_prepacked",
 ]

@@ -918,4 +918,44 @@ q8ta_status q8ta_quantize_conv2d_transposed(
   return hip_status(launch_quantize_deconv(a, stream), op);
 }
 
+q8ta_status q8ta_quantize_conv2d_transposed_prepacked(
+    const float* x, int64_t N, int64_t IC, int64_t H_in, int64_t W_in, double input_scale,
+    int64_t input_zero_point, const int8_t* packed_weight, int64_t OC, int64_t Kh, int64_t Kw,
+    const int32_t* weight_sums, const float* weight_scales, const float* bias, double output_scale,
+    int64_t output_zero_point, int64_t stride_h, int64_t stride_w, int64_t pad_h, int64_t pad_w,
+    int64_t output_padding_h, int64_t output_padding_w, int64_t dilation_h, int64_t dilation_w,
+    int64_t groups, const char* activation, int8_t* out, int64_t H_out, int64_t W_out,
+    hipStream_t stream) {
+  const char* op = "q8ta_quantize_conv2d_transposed_prepacked";
+  (void)weight_sums;
+  (void)output_padding_h;
+  (void)output_padding_w;
+  q8ta_status st = check_dil_groups(op, IC, OC, dilation_h, dilation_w, groups);
+  if (st) return st;
+  st = deconv_checks(op, (const int8_t*)x, N, IC, H_in, W_in, packed_weight, OC, Kh, Kw,
+                     Kh * Kw * IC, stride_h, stride_w, pad_h, pad_w, out, H_out, W_out, IC / groups);
+  if (st) return st;
+  if (!weight_scales) return fail(Q8TA_ERR_NULL, "%s: weight_scales must not be NULL", op);
+  if ((st = check_qparams(op, input_scale, input_zero_point))) return st;
+  if ((st = check_qparams(op, output_scale, output_zero_point))) return st;
+  bool relu = false;
+  if ((st = check_activation(op, activation, &relu))) return st;
+  DeconvArgs a{};
+  a.x = nullptr; a.xf = x; a.inv_in = recip(input_scale);
+  a.w = packed_weight; a.wpk = packed_weight; a.wscale = weight_scales; a.bias = bias;
+  a.out = out; a.acc = nullptr;
+  a.N = N; a.IC = IC; a.H_in = H_in; a.W_in = W_in; a.OC = OC; a.Kh = Kh; a.Kw = Kw;
+  a.ldw = Kh * Kw * IC; a.sh = stride_h; a.sw = stride_w; a.ph = pad_h; a.pw = pad_w;
+  a.dil_h = dilation_h; a.dil_w = dilation_w; a.groups = groups;
+  a.H_out = H_out; a.W_out = W_out; a.izp = (int32_t)input_zero_point;
+  a.rq = make_requant(input_scale, output_scale, output_zero_point, relu);
+  if (!deconv_fixed_supported(a))
+    return fail(Q8TA_ERR_UNSUPPORTED,
+                "%s: takes the 3x3 / 4x4 stride-2 shapes of the compile-time-pattern kernel only "
+                "(groups 1, dilation 1, equal padding parities, IC %% 64 == 0 with the input halo "
+                "of a tile in LDS, W_in %% 4 == 0, 16-byte aligned x and packed_weight); use "
+                "q8ta_quantize_conv2d_transposed", op);
+  return hip_status(launch_deconv_fixed(a, stream), op);
+}
+
 }  // extern "C"

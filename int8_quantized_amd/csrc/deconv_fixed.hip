@@ -627,7 +627,9 @@ hipError_t launch_t(const DeconvArgs& a, hipStream_t s) {
   size_t lds = 0;
   if (!plan_t<S, K, PM, FWD>(a, p, lds)) return hipErrorInvalidValue;
   if constexpr (!FWD) {
-    if (a.wpk) return launch_x<S, K, PM, FWD, false, true>(a, p, lds, s);
+    if (a.wpk)
+      return a.xf ? launch_x<S, K, PM, FWD, true, true>(a, p, lds, s)
+                  : launch_x<S, K, PM, FWD, false, true>(a, p, lds, s);
     if (a.xf) return launch_x<S, K, PM, FWD, true>(a, p, lds, s);
   }
   return launch_x<S, K, PM, FWD, false>(a, p, lds, s);

@@ -360,6 +360,14 @@ def test_deconv_prepacked_entry_points_errors():
                dict(ph=1, pw=0), dict(groups=2), dict(dh=2, dw=2), dict(w=odd),
                dict(x=ctypes.c_void_p(4096 + 2))):
         _st(call(**kw), q8.Q8TA_ERR_UNSUPPORTED, "use q8ta_conv2d_transposed")
+    qf = l.q8ta_quantize_conv2d_transposed_prepacked
+    _st(qf(None, 1, 64, 32, 32, 0.02, 3, FAKE, 32, 3, 3, None, FAKE, FAKE, 0.54, -5, 2, 2, 1, 1, 1,
+           1, 1, 1, 1, b"none", FAKE, 64, 64, None), q8.Q8TA_ERR_NULL)
+    _st(qf(ctypes.c_void_p(4096 + 4), 1, 64, 32, 32, 0.02, 3, FAKE, 32, 3, 3, None, FAKE, FAKE,
+           0.54, -5, 2, 2, 1, 1, 1, 1, 1, 1, 1, b"none", FAKE, 64, 64, None),
+        q8.Q8TA_ERR_UNSUPPORTED, "use q8ta_quantize_conv2d_transposed")
+    _st(qf(FAKE, 1, 64, 32, 32, 0.02, 3, FAKE, 32, 5, 5, None, FAKE, FAKE, 0.54, -5, 2, 2, 1, 1, 1,
+           1, 1, 1, 1, b"none", FAKE, 64, 64, None), q8.Q8TA_ERR_UNSUPPORTED)
 
 
 def _gpu_present():

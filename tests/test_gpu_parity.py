@@ -666,6 +666,27 @@ def test_deconv_prepacked_parity(case, act):
     np.testing.assert_array_equal(host(out), _oracle_deconv(c, activation=act))
 
 
+@pytest.mark.parametrize("case", DECONV_FIXED_CASES, ids=[str(i) for i in range(len(DECONV_FIXED_CASES))])
+def test_quantize_deconv_prepacked_parity(case):
+    """q8ta_quantize_conv2d_transposed_prepacked: the fp32 input quantized in
+    the same call, on the packed weight, against the oracle's chain."""
+    N, IC, H, W, OC, K, p, op = case
+    _say(f"quantize+deconv prepacked case={case}")
+    c = qi.deconv_case(sum([N, IC, H, W, OC, K]) + 67, N, IC, H, W, OC, K, K, (2, 2), p, op,
+                       ldw=K * K * IC + 16, x_from_fp32=True)
+    packed = _deconv_prepack(c)
+    out = torch.empty((N, OC, c.H_out, c.W_out), dtype=torch.int8, device="cuda")
+    q8.q8ta_conv2d_transposed_prepacked(dev(c.x_fp32), c.in_scale, c.in_zp, packed, OC, K, K, None,
+                                        dev(c.weight_scales), dev(c.bias), c.out_scale, c.out_zp,
+                                        c.stride, c.padding, c.output_padding, (1, 1), 1, "relu",
+                                        out)
+    xq = oracle.quantize_per_tensor(c.x_fp32, c.in_scale, c.in_zp)
+    ref = oracle.conv2d_transposed(xq, c.w, c.weight_scales, c.bias, c.in_scale, c.in_zp,
+                                   c.out_scale, c.out_zp, c.Kh, c.Kw, c.stride, c.padding, (1, 1),
+                                   c.H_out, c.W_out, activation="relu")
+    np.testing.assert_array_equal(host(out), ref)
+
+
 def test_deconv_prepacked_large_workload_full():
     """[8,256,64,64] -> [8,128,128,128] on the prepacked weight, every output
     against the oracle."""
@@ -675,6 +696,12 @@ def test_deconv_prepacked_large_workload_full():
     out = torch.empty((8, 128, 128, 128), dtype=torch.int8, device="cuda")
     q8.q8ta_conv2d_transposed_prepacked(dev(xq_ref), c.in_scale, c.in_zp, packed, 128, c.Kh, c.Kw,
                                         None, dev(c.weight_scales), dev(c.bias), c.out_scale,
+                                        c.out_zp, c.stride, c.padding, c.output_padding, (1, 1), 1,
+                                        "none", out)
+    np.testing.assert_array_equal(host(out), ref)
+    out.zero_()
+    q8.q8ta_conv2d_transposed_prepacked(dev(c.x_fp32), c.in_scale, c.in_zp, packed, 128, c.Kh,
+                                        c.Kw, None, dev(c.weight_scales), dev(c.bias), c.out_scale,
                                         c.out_zp, c.stride, c.padding, c.output_padding, (1, 1), 1,
                                         "none", out)
     np.testing.assert_array_equal(host(out), ref)
