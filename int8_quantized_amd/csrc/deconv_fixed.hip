@@ -433,13 +433,20 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
     __syncthreads();   // the halo is staged
 
     // A fragments of input shift (s_dh, s_dw), step k
+    // chunk (r * NQ + 2k + hi) * HC + pos(c): the lane's part (hi, column c)
+    // is fixed for the whole loop, one offset per column half and column
+    // shift, so a step adds only the wave-uniform (r * NQ + 2k) * HC
+    constexpr int NDW = P.dwmax - P.dwmin + 1;
+    int loff[2][NDW];
+#pragma unroll
+    for (int fx = 0; fx < 2; ++fx)
+#pragma unroll
+      for (int j = 0; j < NDW; ++j) loff[fx][j] = hi * HC + pos(fx * 32 + lo + j + p.coff);
     auto aload = [&](v4i (&dst)[NF], int s_dh, int s_dw, int k) {
-      const int q = 2 * k + hi;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int r = (f >> 1) + s_dh - P.dhmin;
-        const int cidx = (f & 1) * 32 + lo + s_dw - P.dwmin + p.coff;
-        dst[f] = xs[(r * NQ + q) * HC + pos(cidx)];
+        dst[f] = xs[(r * NQ + 2 * k) * HC + loff[f & 1][s_dw - P.dwmin]];
       }
     };
     v4i acur[NF], anext[NF];
