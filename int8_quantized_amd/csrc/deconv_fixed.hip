@@ -401,9 +401,9 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
     constexpr int G = decltype(gtag)::value;        // row residue of the group, -1: every tap
     constexpr int RH = G < 0 ? 0 : G;
     constexpr ShiftList L = group_shifts<S, K, PM, FWD>(G);
-    // Each weight fragment is requested two steps ahead, into two
-    // alternating register sets (with one set the compiler's wait counts at
-    // the loop head leave about half a step of cover).
+    // Groups of up to 6 taps request each weight fragment two steps ahead,
+    // into two alternating register sets; the 8-tap groups of 4x4 (longer
+    // steps, no registers to spare) and stride 1 one step ahead.
     constexpr bool TWO = SPLIT && group_taps<S, K, PM, FWD>(G) <= 6;
     v16i acc[NG][NF];
     int32_t wsum[NG];
