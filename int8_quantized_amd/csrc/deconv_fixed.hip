@@ -495,6 +495,10 @@ __global__ __launch_bounds__(threads_of<S>(), 1) void k_deconv_fixed(DeconvArgs 
     } else {
       for (int k = 0; k < nk; ++k) step(k, k + 1 < nk ? k + 1 : k, bw);
     }
+    // The group with fewer taps waits here for the other's products: its
+    // requantize (a long run of vector instructions) would otherwise win
+    // the SIMD's issue and slow them down; the two requantize together.
+    if constexpr (SPLIT) __syncthreads();
     // zw = input zero point x the phase's weight sum (lanes l and l + 32 hold
     // the two 16-channel halves of each weight fragment)
     int32_t zw[NG];
